@@ -1,0 +1,20 @@
+"""Seeded synthetic inputs for the gated delta rule forward (KDA / Gated DeltaNet).
+
+This package is shared by the fp64 oracle's tests and by the GPU path's tests and
+benchmark. It only draws random numbers and shapes them (normal draws, L2
+normalisation of query/key vectors, sigmoid for the write strength, the clipped
+log-decay, bf16 rounding of values handed to a bf16 kernel). It contains none of
+the method's arithmetic: no decay, no state update, no chunking.
+"""
+
+from .generate import (  # noqa: F401
+    CONFIGS,
+    ChunkInputs,
+    DecodeInputs,
+    WorkloadConfig,
+    bf16_round,
+    decode_step_inputs,
+    decode_initial_state,
+    make_chunk_inputs,
+    varlen_lengths,
+)

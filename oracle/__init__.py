@@ -1,0 +1,148 @@
+"""fp64 CPU oracle for the gated delta rule forward (KDA / Gated DeltaNet).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package. It shares no code with the
+HIP library (``gated_delta_rule_13_amd``) and never imports it; the HIP library
+never imports this package.
+
+Two independent implementations live here:
+  * ``kda_oracle.c`` (through ``kda_chains`` / ``kda_forward`` / ``kda_decode_step``):
+    the token recurrence in plain C, fp64, parallel over chains. This is the oracle
+    the GPU path is compared with.
+  * ``reference.py``: the same recurrence written with numpy (for small cases), the
+    pages' chunked (WY / UT transform) form, the pages' WY recursions and brute-force
+    unrolled products. These exist to pin the oracle to the pages.
+
+Every function here has at least one pin in ``tests/test_oracle_pins.py``; none is
+"parity unpinned".
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Iterable, Optional, Tuple
+
+import numpy as np
+
+from .build import LIB, build_oracle
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = LIB if os.path.exists(LIB) else build_oracle(force=True)
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        lib.oracle_kda_chains.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
+                                          P, P, P, P, ctypes.c_int, P, P, P, P, P, P,
+                                          ctypes.c_int]
+        lib.oracle_kda_chains.restype = ctypes.c_int
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def kda_chains(q, k, v, g, beta, row_off, row_len, s0=None, erase=None, write=None,
+               threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Runs independent chains whose tokens are rows of flat arrays.
+
+    q, k: [rows, dk]; v: [rows, dv]; g: [rows, dk] (per channel) or [rows] (per head);
+    beta (and the optional erase / write gates of the pins): [rows].
+    Chain c covers rows row_off[c] .. row_off[c] + row_len[c] - 1. s0: [chains, dk, dv].
+    Returns (o [rows, dv], final states [chains, dk, dv]), both float64.
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    erase, write, s0 = _f64(erase), _f64(write), _f64(s0)
+    rows, dk = q.shape
+    dv = v.shape[1]
+    per_channel = 1 if g.ndim == 2 else 0
+    off = np.ascontiguousarray(row_off, dtype=np.int64)
+    ln = np.ascontiguousarray(row_len, dtype=np.int64)
+    n = len(off)
+    assert k.shape == (rows, dk) and v.shape[0] == rows and beta.shape == (rows,)
+    assert np.all(off >= 0) and np.all(ln >= 0) and np.all(off + ln <= rows)
+    if s0 is not None:
+        assert s0.shape == (n, dk, dv)
+    o = np.zeros((rows, dv), np.float64)
+    sf = np.zeros((n, dk, dv), np.float64)
+    rc = _load().oracle_kda_chains(n, dk, dv, _ptr(off), _ptr(ln), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(g), per_channel, _ptr(beta), _ptr(erase), _ptr(write),
+                                   _ptr(s0), _ptr(o), _ptr(sf), int(threads))
+    if rc != 0:
+        raise MemoryError("oracle_kda_chains could not allocate its work buffers")
+    return o, sf
+
+
+def kda_forward(q, k, v, g, beta, s0=None, cu_seqlens=None,
+                chains: Optional[Iterable[Tuple[int, int]]] = None,
+                threads: int = 0) -> Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]]:
+    """Forward over head-major inputs [B, H, T, ...] (B = 1 with ``cu_seqlens``).
+
+    Each (sequence n, head h) is an independent chain. ``chains`` selects a subset
+    (default: all). Returns {(n, h): (o [len, dv], final state [dk, dv])}, float64.
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        N = len(cu) - 1
+        spans = [(0, int(cu[n]), int(cu[n + 1] - cu[n])) for n in range(N)]
+    else:
+        N = B
+        spans = [(n, 0, T) for n in range(N)]
+    if chains is None:
+        chains = [(n, h) for n in range(N) for h in range(H)]
+    chains = list(chains)
+    per_channel = g.ndim == 4
+    qs, ks, vs, gs, bs, offs, lens, s0s = [], [], [], [], [], [], [], []
+    row = 0
+    for (n, h) in chains:
+        b, t0, ln = spans[n]
+        sl = slice(t0, t0 + ln)
+        qs.append(q[b, h, sl])
+        ks.append(k[b, h, sl])
+        vs.append(v[b, h, sl])
+        gs.append(g[b, h, sl])
+        bs.append(beta[b, h, sl])
+        offs.append(row)
+        lens.append(ln)
+        row += ln
+        if s0 is not None:
+            s0s.append(s0[n, h])
+    cat = lambda xs, shape: (np.concatenate(xs) if xs else np.zeros(shape))  # noqa: E731
+    o, sf = kda_chains(cat(qs, (0, dk)), cat(ks, (0, dk)), cat(vs, (0, dv)),
+                       cat(gs, (0, dk) if per_channel else (0,)), cat(bs, (0,)),
+                       offs, lens, np.stack(s0s) if s0 is not None else None,
+                       threads=threads)
+    out = {}
+    for c, (n, h) in enumerate(chains):
+        out[(n, h)] = (o[offs[c]:offs[c] + lens[c]], sf[c])
+    return out
+
+
+def kda_decode_step(state, q, k, v, g, beta, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """One single-token step for every (sequence, head): state [N, H, dk, dv];
+    q, k [N, H, dk]; v [N, H, dv]; g [N, H, dk] or [N, H]; beta [N, H].
+    Returns (o [N, H, dv], new state [N, H, dk, dv]) in float64."""
+    N, H, dk, dv = state.shape
+    rows = N * H
+    o, sf = kda_chains(q.reshape(rows, dk), k.reshape(rows, dk), v.reshape(rows, dv),
+                       g.reshape(rows, -1) if g.ndim == 3 else g.reshape(rows),
+                       beta.reshape(rows), np.arange(rows), np.ones(rows, np.int64),
+                       s0=state.reshape(rows, dk, dv), threads=threads)
+    return o.reshape(N, H, dv), sf.reshape(N, H, dk, dv)

@@ -1,0 +1,296 @@
+"""Pins of the oracle: checks against what the pages and the mathematics fix.
+
+Each pin takes an implementation ``impl(q, k, v, g, beta, s0=None, erase=None,
+write=None) -> (o [T, dv], S_T [dk, dv])`` of one chain and raises AssertionError
+if it disagrees. The pins are written independently of the oracle's own code:
+closed forms, other equations of the pages, brute-force products and invariants.
+``tests/test_oracle_pins.py`` runs them on the C oracle and on its numpy twin;
+``tests/test_oracle_mutants.py`` shows that plausible mistakes fail at least one.
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+from oracle import reference as ref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def case(T, dk, dv, seed, gate="channel", strong=False):
+    """Small random chain: unit q, k; v ~ N(0,1); beta in (0,1); g in [-5, 0]."""
+    rng = np.random.default_rng(seed)
+    q = _unit(rng.standard_normal((T, dk)))
+    k = _unit(rng.standard_normal((T, dk)))
+    v = rng.standard_normal((T, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    shape = (T, dk) if gate == "channel" else (T,)
+    if strong:
+        g = -5.0 * rng.random(shape)
+    else:
+        g = np.maximum(-5.0, -np.exp(rng.standard_normal(shape) - 2.0))
+    s0 = 0.3 * rng.standard_normal((dk, dv))
+    return q, k, v, g, beta, s0
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a), np.asarray(b)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    assert err <= tol * scale, f"{what}: max |diff| {err:.3e} > {tol:.1e} * {scale:.3g}"
+
+
+def states_by_steps(impl, q, k, v, g, beta, s0, erase=None, write=None):
+    """States after every token, by calling ``impl`` one token at a time."""
+    S = s0
+    out = []
+    for t in range(k.shape[0]):
+        sl = slice(t, t + 1)
+        _, S = impl(q[sl], k[sl], v[sl], g[sl], beta[sl], s0=S,
+                    erase=None if erase is None else erase[sl],
+                    write=None if write is None else write[sl])
+        out.append(S)
+    return out
+
+
+# ---------------------------------------------------------------------------------
+def pin_basis_key_overwrite(impl):
+    """Closed form for a basis key k = e_i (boxed KDA recurrence, "Token Mixer I",
+    section "Kimi Delta Attention"): (I - beta e_i e_i^T) Diag(alpha) S + beta e_i v^T
+    keeps every row j != i at alpha_j S[j] and sets row i to (1 - beta) alpha_i S[i] + beta v.
+    The read-out is o = S^T q."""
+    rng = np.random.default_rng(11)
+    dk, dv = 6, 5
+    for i, b in [(0, 0.3), (3, 1.0), (5, 0.0), (2, 0.75)]:
+        S0 = rng.standard_normal((dk, dv))
+        g = -rng.random(dk) * 3.0
+        k = np.zeros(dk)
+        k[i] = 1.0
+        v = rng.standard_normal(dv)
+        q = rng.standard_normal(dk)
+        o, S = impl(q[None], k[None], v[None], g[None], np.array([b]), s0=S0)
+        a = np.exp(g)
+        want = a[:, None] * S0
+        want[i] = (1.0 - b) * a[i] * S0[i] + b * v
+        _close(S, want, 1e-12, "basis-key state")
+        _close(o[0], want.T @ q, 1e-12, "basis-key read-out")
+
+
+def pin_chunked_equals_recurrence(impl):
+    """The pages' chunkwise form (WY representation + UT transform, "Token Mixer I",
+    section "Kimi Delta Attention") equals the recurrence, for several chunk sizes and
+    a partial last chunk, per-channel and per-head decay, with an initial state."""
+    for gate in ("channel", "head"):
+        q, k, v, g, beta, s0 = case(150, 12, 7, seed=3, gate=gate, strong=True)
+        o, S = impl(q, k, v, g, beta, s0=s0)
+        for C in (16, 37, 64):
+            oc, Sc = ref.chunked(q, k, v, g, beta, s0=s0, C=C)
+            _close(o, oc, 1e-10, f"chunked C={C} outputs ({gate})")
+            _close(S, Sc, 1e-10, f"chunked C={C} final state ({gate})")
+
+
+def pin_deltanet_alpha_one(impl):
+    """alpha = 1 (g = 0) gives DeltaNet. Compared with the DeltaNet chunk algorithm of
+    "Token Mixer I", section "Delta Networks" (UT transform, state in the transposed
+    R^{dv x dk} orientation):
+      T = [I + StrictLower(diag(beta) K K^T)]^-1 diag(beta), W = T K, U = T V,
+      O = Q S^T + (Q K^T ⊙ M)(U - W S^T),  S <- S + (U - W S^T)^T K,
+    and with one step of the SGD view of section "Linear Attention and the Gated Delta
+    Rule": S <- S - beta grad_S 1/2 ||S^T k - v||^2."""
+    q, k, v, _, beta, s0 = case(96, 10, 6, seed=5)
+    g = np.zeros((96, 10))
+    o, S = impl(q, k, v, g, beta, s0=s0)
+    St = s0.T.copy()   # dv x dk
+    C = 32
+    out = np.zeros_like(o)
+    for c0 in range(0, 96, C):
+        sl = slice(c0, c0 + C)
+        Q, K, V, b = q[sl], k[sl], v[sl], beta[sl]
+        n = K.shape[0]
+        Tm = np.linalg.inv(np.eye(n) + np.tril(np.diag(b) @ K @ K.T, -1)) @ np.diag(b)
+        W, U = Tm @ K, Tm @ V
+        Vp = U - W @ St.T
+        out[sl] = Q @ St.T + np.tril(Q @ K.T) @ Vp
+        St = St + Vp.T @ K
+    _close(o, out, 1e-10, "DeltaNet chunk outputs")
+    _close(S, St.T, 1e-10, "DeltaNet chunk final state")
+    # one SGD step on the online regression loss
+    S1 = s0.copy()
+    _, S_impl = impl(q[:1], k[:1], v[:1], g[:1], beta[:1], s0=S1)
+    grad = np.outer(k[0], S1.T @ k[0] - v[0])
+    _close(S_impl, S1 - beta[0] * grad, 1e-12, "SGD step")
+
+
+def pin_gdn_scalar_gate(impl):
+    """One decay per head gives Gated DeltaNet, "Token Mixer I", section "Linear
+    Attention and the Gated Delta Rule": S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1}
+    + beta_t k_t v_t^T (explicit dk x dk matrices here). A per-channel decay that is
+    the same on every channel must give the same result."""
+    q, k, v, g, beta, s0 = case(40, 8, 5, seed=7, gate="head", strong=True)
+    o, S = impl(q, k, v, g, beta, s0=s0)
+    St = s0.copy()
+    want = np.zeros_like(o)
+    for t in range(40):
+        St = np.exp(g[t]) * (np.eye(8) - beta[t] * np.outer(k[t], k[t])) @ St \
+            + beta[t] * np.outer(k[t], v[t])
+        want[t] = St.T @ q[t]
+    _close(o, want, 1e-11, "GDN outputs")
+    _close(S, St, 1e-11, "GDN final state")
+    ob, Sb = impl(q, k, v, np.repeat(g[:, None], 8, axis=1), beta, s0=s0)
+    _close(ob, o, 1e-12, "broadcast per-channel decay outputs")
+    _close(Sb, S, 1e-12, "broadcast per-channel decay state")
+
+
+def pin_linear_attention(impl):
+    """With erase 0, write 1 and alpha = 1 the update is plain linear attention,
+    "Token Mixer I", section "Mamba2: Linear Attention with Decay": O = (Q K^T ⊙ M) V
+    with M the inclusive causal mask (plus Q S_0 for an initial state). With the tied
+    gate beta = 0 the state is frozen (o_t = S_0^T q_t), and with a decay it only decays:
+    S_T = Diag(gamma_T) S_0."""
+    T, dk, dv = 30, 7, 4
+    q, k, v, _, beta, s0 = case(T, dk, dv, seed=9)
+    zero = np.zeros(T)
+    o, S = impl(q, k, v, np.zeros((T, dk)), beta, s0=s0, erase=zero, write=np.ones(T))
+    M = np.tril(np.ones((T, T)))
+    _close(o, (q @ k.T * M) @ v + q @ s0, 1e-11, "linear attention outputs")
+    _close(S, s0 + k.T @ v, 1e-11, "linear attention final state")
+    o0, S0 = impl(q, k, v, np.zeros((T, dk)), zero, s0=s0)
+    _close(o0, q @ s0, 1e-12, "frozen-state outputs")
+    _close(S0, s0, 1e-12, "frozen state")
+    g = -np.random.default_rng(1).random((T, dk))
+    _, Sd = impl(q, k, v, g, zero, s0=s0)
+    _close(Sd, np.exp(g.sum(0))[:, None] * s0, 1e-12, "pure decay")
+
+
+def pin_decayed_linear_attention(impl):
+    """Erase 0, write 1 with decay: "Token Mixer I", section "Mamba2": o_t = sum_{i<=t}
+    v_i (q_t^T Diag(gamma_t / gamma_i) k_i) + (Diag(gamma_t) S_0)^T q_t per channel, and
+    O = ((Q K^T) ⊙ Gamma) V with Gamma_ij = gamma_i / gamma_j (i >= j) for one decay per head."""
+    T, dk, dv = 24, 6, 5
+    q, k, v, g, beta, s0 = case(T, dk, dv, seed=13, strong=True)
+    e, w = np.zeros(T), np.ones(T)
+    o, _ = impl(q, k, v, g, beta, s0=s0, erase=e, write=w)
+    G = np.cumsum(g, axis=0)
+    want = np.zeros((T, dv))
+    for t in range(T):
+        for i in range(t + 1):
+            want[t] += v[i] * (q[t] @ (np.exp(G[t] - G[i]) * k[i]))
+        want[t] += (np.exp(G[t])[:, None] * s0).T @ q[t]
+    _close(o, want, 1e-11, "per-channel decayed linear attention")
+    gh = g[:, 0]
+    oh, _ = impl(q, k, v, gh, beta, erase=e, write=w)
+    Gh = np.cumsum(gh)
+    Gam = np.tril(np.exp(Gh[:, None] - Gh[None, :]))
+    _close(oh, ((q @ k.T) * Gam) @ v, 1e-11, "scalar-decay linear attention")
+
+
+def pin_exact_overwrite(impl):
+    """"Token Mixer I", section "Gated DeltaNet-2 / Preliminary": with ||k|| = 1 and
+    beta = 1 the write overwrites the association of k, so S_t^T k_t = v_t; in general
+    S_t^T k_t = (1 - beta) (Diag(alpha) S_{t-1})^T k_t + beta v_t."""
+    T, dk, dv = 12, 9, 4
+    q, k, v, g, beta, s0 = case(T, dk, dv, seed=17)
+    sts = states_by_steps(impl, q, k, v, g, np.ones(T), s0)
+    for t in range(T):
+        _close(sts[t].T @ k[t], v[t], 1e-12, "beta=1 overwrite")
+    sts = states_by_steps(impl, q, k, v, g, beta, s0)
+    prev = s0
+    for t in range(T):
+        dec = np.exp(g[t])[:, None] * prev
+        _close(sts[t].T @ k[t], (1 - beta[t]) * dec.T @ k[t] + beta[t] * v[t], 1e-12,
+               "partial overwrite")
+        prev = sts[t]
+
+
+def pin_brute_force_products(impl):
+    """Brute force on T <= 16: the states equal S^r = P^r S_0 + H^r with the explicit
+    unrolled products of "Token Mixer I", section "Kimi Delta Attention", and the WY
+    forms of the same section give the same P^r and H^r."""
+    T, dk, dv = 16, 5, 3
+    q, k, v, g, beta, s0 = case(T, dk, dv, seed=19, strong=True)
+    sts = states_by_steps(impl, q, k, v, g, beta, s0)
+    w, u, G = ref.wy_factors(k, v, g, beta)
+    for r in range(1, T + 1):
+        P, H = ref.brute_force_products(k, v, g, beta, r)
+        _close(sts[r - 1], P @ s0 + H, 1e-12, f"unrolled products r={r}")
+        Pw, Hw = ref.wy_products(k, w, u, G, r)
+        _close(Pw, P, 1e-12, f"WY P r={r}")
+        _close(Hw, H, 1e-12, f"WY H r={r}")
+
+
+def pin_split_resume(impl):
+    """The state is the whole context (page "【轻量化复刻大模型】线性注意力（Linear
+    Attention）", section 4.0.1: each step reads S, modifies S, returns the output):
+    running [0, T) equals running [0, T1) and then [T1, T) from the returned state."""
+    q, k, v, g, beta, s0 = case(70, 8, 6, seed=23)
+    o, S = impl(q, k, v, g, beta, s0=s0)
+    T1 = 29
+    o1, S1 = impl(q[:T1], k[:T1], v[:T1], g[:T1], beta[:T1], s0=s0)
+    o2, S2 = impl(q[T1:], k[T1:], v[T1:], g[T1:], beta[T1:], s0=S1)
+    _close(np.concatenate([o1, o2]), o, 1e-12, "split outputs")
+    _close(S2, S, 1e-12, "split final state")
+
+
+def pin_page4_capacity_demo(impl):
+    """Page "【轻量化复刻大模型】线性注意力（Linear Attention）", section 4.1.8: the printed
+    read-back of a 1-D state after five writes (fixture tests/golden/page4_capacity_demo.txt).
+    beta = 0.5 and (1 - beta) alpha = 0.076 are inferred from the table (smoke pin)."""
+    rows = np.loadtxt(os.path.join(GOLDEN, "page4_capacity_demo.txt"))
+    vals, printed = rows[:, 0], rows[:, 1]
+    n = len(vals)
+    q = np.ones((n, 1))
+    k = np.ones((n, 1))
+    g = np.full((n, 1), np.log(0.076 / 0.5))
+    o, _ = impl(q, k, vals[:, None], g, np.full(n, 0.5))
+    assert np.array_equal(np.round(o[:, 0], 3), printed), (o[:, 0], printed)
+
+
+def pin_invariants(impl):
+    """Properties of the boxed recurrence ("Token Mixer I", section "Kimi Delta
+    Attention"): linear in (V, S_0) jointly; permuting the key channels of q, k and g
+    together permutes the rows of S and leaves O unchanged; value columns are
+    independent; ||S_t||_F <= ||S_{t-1}||_F + beta_t ||v_t|| for unit keys."""
+    T, dk, dv = 20, 6, 5
+    q, k, v, g, beta, s0 = case(T, dk, dv, seed=29, strong=True)
+    rng = np.random.default_rng(31)
+    v2, s2 = rng.standard_normal(v.shape), rng.standard_normal(s0.shape)
+    o1, S1 = impl(q, k, v, g, beta, s0=s0)
+    o2, S2 = impl(q, k, v2, g, beta, s0=s2)
+    o3, S3 = impl(q, k, 2.0 * v - 0.5 * v2, g, beta, s0=2.0 * s0 - 0.5 * s2)
+    _close(o3, 2.0 * o1 - 0.5 * o2, 1e-12, "linearity outputs")
+    _close(S3, 2.0 * S1 - 0.5 * S2, 1e-12, "linearity state")
+    perm = rng.permutation(dk)
+    op, Sp = impl(q[:, perm], k[:, perm], v, g[:, perm], beta, s0=s0[perm])
+    _close(op, o1, 1e-12, "channel permutation outputs")
+    _close(Sp, S1[perm], 1e-12, "channel permutation state")
+    cols = [4, 1]
+    oc, Sc = impl(q, k, v[:, cols], g, beta, s0=s0[:, cols])
+    _close(oc, o1[:, cols], 1e-12, "value-column independence outputs")
+    _close(Sc, S1[:, cols], 1e-12, "value-column independence state")
+    sts = states_by_steps(impl, q, k, v, g, beta, s0)
+    prev = s0
+    for t in range(T):
+        assert np.linalg.norm(sts[t]) <= np.linalg.norm(prev) + beta[t] * np.linalg.norm(v[t]) \
+            + 1e-12
+        prev = sts[t]
+
+
+ALL_PINS = [
+    pin_basis_key_overwrite,
+    pin_chunked_equals_recurrence,
+    pin_deltanet_alpha_one,
+    pin_gdn_scalar_gate,
+    pin_linear_attention,
+    pin_decayed_linear_attention,
+    pin_exact_overwrite,
+    pin_brute_force_products,
+    pin_split_resume,
+    pin_page4_capacity_demo,
+    pin_invariants,
+]

@@ -1,0 +1,81 @@
+"""Plants plausible mistakes in a copy of the oracle's recurrence (on the CPU) and
+checks that every one of them fails at least one pin: the pins are sharp enough to
+catch a dropped term, a wrong sign, a wrong order or a transposed operand."""
+
+import numpy as np
+import pytest
+
+from tests import pins
+
+
+def _make(mut):
+    def impl(q, k, v, g, beta, s0=None, erase=None, write=None):
+        q, k, v = (np.asarray(x, float) for x in (q, k, v))
+        T, dk = k.shape
+        dv = v.shape[1]
+        gg = np.asarray(g, float)
+        gg = gg if gg.ndim == 2 else np.repeat(gg[:, None], dk, axis=1)
+        e = beta if erase is None else erase
+        w = beta if write is None else write
+        S = np.zeros((dk, dv)) if s0 is None else np.array(s0, float)
+        o = np.zeros((T, dv))
+        G = np.zeros(dk)
+        for t in range(T):
+            a = np.exp(gg[t])
+            G = G + gg[t]
+            if mut == "decay_after_update":
+                S = S + np.outer(k[t], w[t] * v[t] - e[t] * (S.T @ k[t]))
+                S = a[:, None] * S
+            elif mut == "predict_from_undecayed":
+                p = S.T @ k[t]
+                S = a[:, None] * S + np.outer(k[t], w[t] * v[t] - e[t] * p)
+            elif mut == "cumulative_decay":
+                S = np.exp(G)[:, None] * S
+                S = S + np.outer(k[t], w[t] * v[t] - e[t] * (S.T @ k[t]))
+            else:
+                S = a[:, None] * S if mut != "no_decay" else S
+                p = S.T @ k[t]
+                if mut == "erase_without_beta":
+                    S = S + np.outer(k[t], w[t] * v[t] - p)
+                elif mut == "erase_sign":
+                    S = S + np.outer(k[t], w[t] * v[t] + e[t] * p)
+                elif mut == "predict_with_query":
+                    S = S + np.outer(k[t], w[t] * v[t] - e[t] * (S.T @ q[t]))
+                elif mut == "write_without_beta":
+                    S = S + np.outer(k[t], v[t] - e[t] * p)
+                else:
+                    S = S + np.outer(k[t], w[t] * v[t] - e[t] * p)
+            if mut == "readout_before_update_order":
+                o[t] = (S - np.outer(k[t], w[t] * v[t])).T @ q[t]
+            elif mut == "readout_with_key":
+                o[t] = S.T @ k[t]
+            elif mut == "readout_transposed_gate":
+                o[t] = S.T @ (q[t] * np.exp(gg[t]))
+            else:
+                o[t] = S.T @ q[t]
+        return o, S
+    return impl
+
+
+MUTANTS = ["decay_after_update", "predict_from_undecayed", "cumulative_decay", "no_decay",
+           "erase_without_beta", "erase_sign", "predict_with_query", "write_without_beta",
+           "readout_before_update_order", "readout_with_key", "readout_transposed_gate"]
+
+
+def test_unmutated_copy_passes_all_pins():
+    impl = _make(None)
+    for pin in pins.ALL_PINS:
+        pin(impl)
+
+
+@pytest.mark.parametrize("mut", MUTANTS)
+def test_mutant_fails_a_pin(mut):
+    impl = _make(mut)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {mut} passed every pin"
