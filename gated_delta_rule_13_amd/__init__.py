@@ -1,0 +1,198 @@
+"""Python binding of libkda.so, the MI355X (gfx950) gated delta rule forward library.
+
+The binding only marshals arguments: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/kda.h``. PyTorch provides device memory and the
+current stream. There is no CPU fallback: if the library is not built, or a tensor is
+not on the GPU, the call raises.
+
+  chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+            output_final_state=True)               -> (o, final_state or None)
+  recurrent_step(q, k, v, g, beta, state)         -> o      (state updated in place)
+
+The raw entry points ``kda_chunk_fwd``, ``kda_recurrent_step``,
+``kda_chunk_fwd_workspace_size`` and ``kda_status_string`` are exposed with the C
+names and C argument order (pointers as integers).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_PER_CHANNEL, KDA_GATE_PER_HEAD = 0, 1
+
+EXPORTED_SYMBOLS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
+                    "kda_status_string")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kda_status_string(status)}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libkda.so (built by ``gated_delta_rule_13_amd/build.py``); raises if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkda.so is not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
+                                  ctypes.c_size_t, P]
+    lib.kda_chunk_fwd.restype = I
+    lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.kda_recurrent_step.restype = I
+    lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------- raw ABI
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, num_seqs,
+                  B, H, T, dk, dv, dt, gm, workspace, workspace_bytes, stream) -> int:
+    return int(load_library().kda_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o,
+                                            cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm,
+                                            workspace, workspace_bytes, stream))
+
+
+def kda_recurrent_step(q, k, v, g, beta, state, o, N, H, dk, dv, dt, gm, stream) -> int:
+    return int(load_library().kda_recurrent_step(q, k, v, g, beta, state, o, N, H, dk, dv,
+                                                 dt, gm, stream))
+
+
+# ----------------------------------------------------------------------- torch helpers
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked forward over [B, H, T, d] head-major tensors (see ``kda_chunk_fwd``).
+
+    g: float32 [B, H, T, dk] (per key channel, KDA) or [B, H, T] (per head, Gated
+    DeltaNet); beta: float32 [B, H, T]; initial_state: float32 [N, H, dk, dv] or None;
+    cu_seqlens: int32 [N + 1] on the GPU (B must be 1) or None. ``o`` and ``final_state``
+    may be given to reuse buffers; ``final_state`` may be ``initial_state``.
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(initial_state, "initial_state", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, H, T):
+        raise ValueError("inconsistent q/k/v/beta shapes")
+    if g.shape == (B, H, T, dk):
+        gm = KDA_GATE_PER_CHANNEL
+    elif g.shape == (B, H, T):
+        gm = KDA_GATE_PER_HEAD
+    else:
+        raise ValueError(f"g must be [B,H,T,dk] or [B,H,T], got {tuple(g.shape)}")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None and initial_state.shape != (N, H, dk, dv):
+        raise ValueError(f"initial_state must be {(N, H, dk, dv)}")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", torch.float32, dev)
+    num_seqs = 0 if cu_seqlens is None else N
+    ws_bytes = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                       _ptr(final_state), _ptr(o), _ptr(cu_seqlens), num_seqs, B, H, T, dk,
+                       dv, dt, gm, _ptr(ws), ws_bytes, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   beta: torch.Tensor, state: torch.Tensor,
+                   o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step (see ``kda_recurrent_step``): q, k [N, H, dk]; v [N, H, dv];
+    g float32 [N, H, dk] or [N, H]; beta float32 [N, H]; state float32 [N, H, dk, dv],
+    updated in place. Returns o [N, H, dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(state, "state", torch.float32, dev)
+    if k.shape != q.shape or v.shape[:2] != (N, H) or beta.shape != (N, H) \
+            or state.shape != (N, H, dk, dv):
+        raise ValueError("inconsistent decode shapes")
+    if g.shape == (N, H, dk):
+        gm = KDA_GATE_PER_CHANNEL
+    elif g.shape == (N, H):
+        gm = KDA_GATE_PER_HEAD
+    else:
+        raise ValueError(f"g must be [N,H,dk] or [N,H], got {tuple(g.shape)}")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, dev)
+    st = kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                            _ptr(o), N, H, dk, dv, dt, gm, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_step")
+    return o

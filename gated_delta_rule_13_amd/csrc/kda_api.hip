@@ -1,0 +1,78 @@
+// C ABI of libkda.so (declared in include/kda.h): argument validation on the host,
+// then dispatch to the kernels on the caller's stream. Nothing here allocates,
+// synchronises or keeps state between calls.
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported shape or mode";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+  }
+  return "KDA_ERR_UNKNOWN: unknown status code";
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt) {
+  (void)B; (void)H; (void)T; (void)dk; (void)dv; (void)num_seqs; (void)dt;
+  return 0;  // the fused kernels keep every intermediate on chip
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, float* final_state,
+                         void* o, const int32_t* cu_seqlens, int num_seqs, int B, int H,
+                         int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
+  if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
+  if (!cu_seqlens && num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_INVALID_ARG;
+  if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+  const long long N = cu_seqlens ? num_seqs : B;
+  if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
+
+  kda::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.s0 = initial_state; a.sT = final_state; a.o = o; a.cu = cu_seqlens;
+  a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
+  const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
+  hipError_t err;
+  if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv))
+    err = kda::launch_chunk_mfma(a, per_channel, stream);
+  else
+    err = kda::launch_chunk_f32(a, dt == KDA_BF16, per_channel, stream);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state, void* o, int N, int H, int dk,
+                              int dv, kda_dtype dt, kda_gate_mode gm, hipStream_t stream) {
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
+  if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+  if ((long long)N * H > 0x7fffffffll) return KDA_ERR_UNSUPPORTED;
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+  a.N = N; a.H = H;
+  const hipError_t err =
+      kda::launch_decode(a, dk, dv, dt == KDA_BF16, gm == KDA_GATE_PER_CHANNEL, stream);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// Chunked forward in plain fp32 arithmetic (the kda_chunk_fwd path for float32
+// inputs; it also accepts bf16 inputs and is then a slow cross-check path).
+//
+// The algorithm is the chunkwise form of "Token Mixer I", section "Kimi Delta
+// Attention" (WY representation, UT transform, inter-chunk state update and chunk
+// output). With G_r the chunk-local inclusive cumulative log-decay (per key channel):
+//   A_qk[i,j] = sum_c q_i[c] k_j[c] exp(G_i[c] - G_j[c])          (j <= i)
+//   A_kk[i,j] = beta_i sum_c k_i[c] k_j[c] exp(G_i[c] - G_j[c])    (j <  i)
+//   Tm = (I + A_kk)^-1                       (forward substitution, column by column)
+//   X  = Diag(beta) (V - (K ⊙ e^G) S)        V' = Tm X   (= U - W S of the pages)
+//   O  = (Q ⊙ e^G) S + A_qk V'
+//   S <- Diag(e^{G_C}) S + (K ⊙ e^{G_C - G})^T V'
+// Every exponent is a difference G_i - G_j with j <= i, or G itself, so no factor
+// exceeds 1 in magnitude and nothing is divided by a decay.
+//
+// One 256-thread workgroup per (chain, block of DVB value columns): value columns are
+// independent (the decay acts on the rows of S), so the state pass splits over them.
+// Chunk size 32 keeps the fp32 tiles of q, k and G in LDS.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kC = 32;    // chunk length of this path
+constexpr int kDVB = 32;  // value columns per workgroup
+
+template <int DK, typename TIn, bool PER_CHANNEL>
+__global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_dvb) {
+  __shared__ float sQ[kC][DK];
+  __shared__ float sK[kC][DK];
+  __shared__ float sG[kC][DK];   // cumulative log-decay, later K ⊙ e^{G_C - G}
+  __shared__ float sAqk[kC][kC + 1];
+  __shared__ float sAkk[kC][kC + 1];
+  __shared__ float sTm[kC][kC + 1];
+  __shared__ float sV[kC][kDVB];  // V, later V'
+  __shared__ float sX[kC][kDVB];
+  __shared__ float sS[DK][kDVB];
+  __shared__ float sBeta[kC];
+  __shared__ float sGC[DK];
+
+  const int tid = threadIdx.x;
+  const int chain = blockIdx.x / n_dvb;
+  const int dvb = blockIdx.x % n_dvb;
+  const int n = chain / a.H;
+  const int h = chain % a.H;
+  const int DV = a.dv;
+  const TokenRange tr = token_range(a.cu, n, a.T);
+  const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;  // row of the first token
+  const TIn* q = static_cast<const TIn*>(a.q);
+  const TIn* k = static_cast<const TIn*>(a.k);
+  const TIn* v = static_cast<const TIn*>(a.v);
+  TIn* o = static_cast<TIn*>(a.o);
+  const int col0 = dvb * kDVB;
+  const size_t state_off = ((size_t)n * a.H + h) * DK * DV;
+
+  for (int idx = tid; idx < DK * kDVB; idx += kThreads) {
+    const int c = idx / kDVB, j = idx % kDVB;
+    sS[c][j] = a.s0 ? a.s0[state_off + (size_t)c * DV + col0 + j] : 0.f;
+  }
+
+  for (int c0 = 0; c0 < tr.len; c0 += kC) {
+    const int nt = min(kC, tr.len - c0);
+    __syncthreads();  // previous chunk finished with every LDS tile
+    // -- load the chunk; positions past the sequence end are identity tokens
+    for (int idx = tid; idx < kC * DK; idx += kThreads) {
+      const int t = idx / DK, c = idx % DK;
+      const bool ok = t < nt;
+      const size_t r = row0 + c0 + t;
+      sQ[t][c] = ok ? to_f32(q[r * DK + c]) : 0.f;
+      sK[t][c] = ok ? to_f32(k[r * DK + c]) : 0.f;
+      sG[t][c] = ok ? (PER_CHANNEL ? a.g[r * DK + c] : a.g[r]) : 0.f;
+    }
+    for (int idx = tid; idx < kC * kDVB; idx += kThreads) {
+      const int t = idx / kDVB, j = idx % kDVB;
+      sV[t][j] = t < nt ? to_f32(v[(row0 + c0 + t) * DV + col0 + j]) : 0.f;
+    }
+    if (tid < kC) sBeta[tid] = tid < nt ? a.beta[row0 + c0 + tid] : 0.f;
+    __syncthreads();
+    // -- chunk-local inclusive cumulative log-decay
+    for (int c = tid; c < DK; c += kThreads) {
+      float run = 0.f;
+      for (int t = 0; t < kC; ++t) {
+        run += sG[t][c];
+        sG[t][c] = run;
+      }
+      sGC[c] = run;
+    }
+    __syncthreads();
+    // -- A_qk (inclusive lower) and A_kk (strict lower, rows scaled by beta)
+    for (int pidx = tid; pidx < kC * kC; pidx += kThreads) {
+      const int i = pidx / kC, j = pidx % kC;
+      float aq = 0.f, ak = 0.f;
+      if (j <= i) {
+        for (int c = 0; c < DK; ++c) {
+          const float e = __expf(sG[i][c] - sG[j][c]);
+          const float kj = sK[j][c] * e;
+          aq += sQ[i][c] * kj;
+          ak += sK[i][c] * kj;
+        }
+      }
+      sAqk[i][j] = aq;
+      sAkk[i][j] = j < i ? sBeta[i] * ak : 0.f;
+    }
+    __syncthreads();
+    // -- Tm = (I + A_kk)^-1 by forward substitution, one column per thread
+    if (tid < kC) {
+      const int j = tid;
+      for (int i = 0; i < kC; ++i) sTm[i][j] = i == j ? 1.f : 0.f;
+      for (int i = j + 1; i < kC; ++i) {
+        float acc = 0.f;
+        for (int m = j; m < i; ++m) acc += sAkk[i][m] * sTm[m][j];
+        sTm[i][j] = -acc;
+      }
+    }
+    // -- decayed operands, in place: Q <- Q e^G, K <- K e^G, G <- K e^{G_C - G}
+    for (int idx = tid; idx < kC * DK; idx += kThreads) {
+      const int t = idx / DK, c = idx % DK;
+      const float G = sG[t][c];
+      const float e = __expf(G);
+      const float kk = sK[t][c];
+      sG[t][c] = kk * __expf(sGC[c] - G);
+      sQ[t][c] *= e;
+      sK[t][c] = kk * e;
+    }
+    __syncthreads();
+    // -- X = Diag(beta) (V - (K e^G) S)
+    for (int idx = tid; idx < kC * kDVB; idx += kThreads) {
+      const int t = idx / kDVB, j = idx % kDVB;
+      float acc = sV[t][j];
+      for (int c = 0; c < DK; ++c) acc -= sK[t][c] * sS[c][j];
+      sX[t][j] = sBeta[t] * acc;
+    }
+    __syncthreads();
+    // -- V' = Tm X
+    for (int idx = tid; idx < kC * kDVB; idx += kThreads) {
+      const int t = idx / kDVB, j = idx % kDVB;
+      float acc = 0.f;
+      for (int m = 0; m <= t; ++m) acc += sTm[t][m] * sX[m][j];
+      sV[t][j] = acc;
+    }
+    __syncthreads();
+    // -- O = (Q e^G) S + A_qk V'
+    for (int idx = tid; idx < kC * kDVB; idx += kThreads) {
+      const int t = idx / kDVB, j = idx % kDVB;
+      if (t < nt) {
+        float acc = 0.f;
+        for (int c = 0; c < DK; ++c) acc += sQ[t][c] * sS[c][j];
+        for (int m = 0; m <= t; ++m) acc += sAqk[t][m] * sV[m][j];
+        o[(row0 + c0 + t) * DV + col0 + j] = from_f32<TIn>(acc);
+      }
+    }
+    __syncthreads();
+    // -- S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T V'
+    for (int idx = tid; idx < DK * kDVB; idx += kThreads) {
+      const int c = idx / kDVB, j = idx % kDVB;
+      float acc = __expf(sGC[c]) * sS[c][j];
+      for (int t = 0; t < kC; ++t) acc += sG[t][c] * sV[t][j];
+      sS[c][j] = acc;
+    }
+  }
+  __syncthreads();
+  if (a.sT) {
+    for (int idx = tid; idx < DK * kDVB; idx += kThreads) {
+      const int c = idx / kDVB, j = idx % kDVB;
+      a.sT[state_off + (size_t)c * DV + col0 + j] = sS[c][j];
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_dk(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream) {
+  const int n_dvb = a.dv / kDVB;
+  const dim3 grid(a.N * a.H * n_dvb), block(kThreads);
+  if (bf16) {
+    if (per_channel)
+      chunk_f32_kernel<DK, kda::bf16, true><<<grid, block, 0, stream>>>(a, n_dvb);
+    else
+      chunk_f32_kernel<DK, kda::bf16, false><<<grid, block, 0, stream>>>(a, n_dvb);
+  } else {
+    if (per_channel)
+      chunk_f32_kernel<DK, float, true><<<grid, block, 0, stream>>>(a, n_dvb);
+    else
+      chunk_f32_kernel<DK, float, false><<<grid, block, 0, stream>>>(a, n_dvb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_f32(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream) {
+  if (a.dv % kDVB != 0) return hipErrorInvalidValue;
+  if (a.dk == 128) return launch_dk<128>(a, bf16, per_channel, stream);
+  if (a.dk == 64) return launch_dk<64>(a, bf16, per_channel, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

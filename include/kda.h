@@ -1,0 +1,123 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) gated delta rule forward library, libkda.so.
+ *
+ * The operator is the gated delta rule with per-key-channel decay (Kimi Delta
+ * Attention, "KDA"), for every independent chain (one sequence of one head):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = S_t^T q_t,          S_t in R^{dk x dv},  alpha_t = exp(g_t),
+ *
+ * as boxed in "Token Mixer I", section "Kimi Delta Attention: Improving Delta Rule
+ * with Fine-grained Gating". Gated DeltaNet is the case of one decay per head
+ * (KDA_GATE_PER_HEAD: g_t is a scalar broadcast over the key channels; "Token
+ * Mixer I", section "Linear Attention and the Gated Delta Rule"). There is no query
+ * scale. The state is stored row-major with rows = key channels.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HBM of the current HIP device), the
+ *    tensors are contiguous and head-major: [B, H, T, d] for per-token data.
+ *  - The caller owns every buffer. The library allocates no memory, keeps no global
+ *    state, never synchronises, and enqueues all work on `stream` (NULL = the null
+ *    stream). Calls are asynchronous: a KDA_OK return means "enqueued".
+ *  - Argument errors are detected on the host before anything is launched and are
+ *    returned as a status; no exception crosses the ABI. A failed launch returns
+ *    KDA_ERR_HIP.
+ *  - Preconditions that the host cannot see without reading device memory are not
+ *    checked and are undefined if violated: g in [-5, 0] (the lower bound of the
+ *    log-decay; the kernels rely on it for the exponent ranges of their scaled
+ *    operands), beta in [0, 1], cu_seqlens non-decreasing from 0 to T. Out-of-range
+ *    cu_seqlens entries are clamped to [0, T] so that no access leaves the buffers.
+ *  - Buffers may not alias each other, except initial_state with final_state.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1,  /* NULL required pointer, non-positive size, inconsistent shape */
+  KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. dk = 96) */
+  KDA_ERR_HIP = 3           /* a HIP runtime error while launching */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;   /* element type of q, k, v and o */
+
+typedef enum {
+  KDA_GATE_PER_CHANNEL = 0,  /* KDA: g is [.., dk], one log-decay per key channel */
+  KDA_GATE_PER_HEAD = 1      /* Gated DeltaNet: g is [..], one log-decay per head and token */
+} kda_gate_mode;
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for this problem. The current
+ * kernels need none and return 0; callers should still query it and pass a buffer
+ * of at least this size (NULL is accepted when the size is 0).
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt);
+
+/*
+ * Chunked prefill / training forward over whole sequences.
+ *
+ * Computes, for every chain, all outputs o_t and optionally the state after the last
+ * token. Internally the sequence is cut into chunks and processed with the chunkwise
+ * form of "Token Mixer I", section "Kimi Delta Attention" (WY representation, UT
+ * transform, inter-chunk state update, chunk output), re-derived with exponent
+ * differences so that no factor is divided by a small decay; the result equals the
+ * token recurrence up to rounding and does not depend on the (internal) chunk size.
+ *
+ *   q, k          [B, H, T, dk], dtype dt
+ *   v             [B, H, T, dv], dtype dt
+ *   g             float32 log-decay per token (NOT cumulative), in [-5, 0]:
+ *                 [B, H, T, dk] (KDA_GATE_PER_CHANNEL) or [B, H, T] (KDA_GATE_PER_HEAD)
+ *   beta          float32 [B, H, T], in [0, 1]
+ *   initial_state float32 [N, H, dk, dv] or NULL (= zero state)
+ *   final_state   float32 [N, H, dk, dv] or NULL (= not written); may equal initial_state
+ *   o             [B, H, T, dv], dtype dt; written for every token of every sequence
+ *   cu_seqlens    NULL: N = B sequences of length T (batch row b is sequence b).
+ *                 Otherwise a DEVICE int32 array of num_seqs + 1 offsets into the T
+ *                 axis (packed variable-length sequences); B must be 1 and N = num_seqs.
+ *                 Tokens of o outside every sequence are left untouched.
+ *   dk, dv        each 64 or 128 (anything else: KDA_ERR_UNSUPPORTED)
+ *   workspace     device buffer of at least kda_chunk_fwd_workspace_size(...) bytes
+ *
+ * Arithmetic: state and accumulation in float32. With dt = KDA_BF16 the dense
+ * contractions take bf16 operands on the matrix cores (float32 accumulate); with
+ * dt = KDA_F32 every operation is float32.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, float* final_state,
+                         void* o, const int32_t* cu_seqlens, int num_seqs, int B, int H,
+                         int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One single-token decode step for N sequences x H heads on a resident state.
+ * Per chain: S~ = Diag(exp g) S; p = S~^T k; S = S~ + beta k (v - p)^T; o = S^T q —
+ * the decay-then-delta form of the page "KDA 与 Gated DeltaNet：线性注意力怎样读写有限状态",
+ * section 2, and the fused recurrent path of its section 4.
+ *
+ *   q, k   [N, H, dk], dtype dt        v, o  [N, H, dv], dtype dt
+ *   g      float32 [N, H, dk] (per channel) or [N, H] (per head), in [-5, 0]
+ *   beta   float32 [N, H]
+ *   state  float32 [N, H, dk, dv], read and overwritten IN PLACE with S_t
+ *   dk, dv each 64 or 128
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state, void* o, int N, int H, int dk,
+                              int dv, kda_dtype dt, kda_gate_mode gm, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/kda.h declares,
+and rejects invalid arguments with the documented status codes before launching
+anything (no compute call is made here: there is no GPU in this environment)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_13_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kda_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(kda.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for sym in declared_symbols():
+        assert sym in exported, sym
+        assert getattr(lib, sym) is not None
+
+
+def test_status_strings():
+    for code in range(4):
+        assert kda.kda_status_string(code).startswith("KDA_")
+    assert "UNKNOWN" in kda.kda_status_string(99)
+
+
+def test_workspace_size_is_zero():
+    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == 0
+
+
+DUMMY = 0x1000  # never dereferenced: every call below is rejected on the host
+
+
+def chunk_call(**over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, beta=DUMMY, initial_state=None,
+                final_state=None, o=DUMMY, cu_seqlens=None, num_seqs=0, B=1, H=2, T=64,
+                dk=128, dv=128, dt=kda.KDA_BF16, gm=kda.KDA_GATE_PER_CHANNEL, workspace=None,
+                workspace_bytes=0, stream=None)
+    args.update(over)
+    return kda.kda_chunk_fwd(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=-3), kda.KDA_ERR_INVALID_ARG),
+    (dict(dt=7), kda.KDA_ERR_INVALID_ARG),
+    (dict(gm=5), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=DUMMY, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=DUMMY, num_seqs=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(num_seqs=3), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=256, dv=256), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_rejects(over, code):
+    assert chunk_call(**over) == code
+
+
+def step_call(**over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, beta=DUMMY, state=DUMMY, o=DUMMY, N=4,
+                H=2, dk=128, dv=128, dt=kda.KDA_BF16, gm=kda.KDA_GATE_PER_CHANNEL,
+                stream=None)
+    args.update(over)
+    return kda.kda_recurrent_step(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(state=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(k=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(N=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(dt=2), kda.KDA_ERR_INVALID_ARG),
+    (dict(gm=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=100), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_recurrent_step_rejects(over, code):
+    assert step_call(**over) == code
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4))

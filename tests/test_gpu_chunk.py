@@ -1,0 +1,156 @@
+"""GPU parity of kda_chunk_fwd against the fp64 oracle (through the C ABI).
+
+Full-size workloads: the tiny fp32 case, KDA B2 H16 T4096, GDN B1 H16 T8192 are
+checked on every output and final state; the packed varlen T=65536 H32 case runs in
+full on the GPU (the launch configuration the benchmark times) and is checked on
+sampled chains, including the longest and the shortest sequence. Smaller cases
+cover several chunks with a ragged tail for every dtype, gate mode and head size,
+and the edge cases: empty and one-token sequences, lengths at and around the chunk
+size, the decay floor g = -5 everywhere, no decay, beta = 0 and beta = 1.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from kda_workloads import CONFIGS, make_chunk_inputs
+from tests.gpu_util import (TOL, assert_close, check_chains, note, oracle_chains, run_chunk,
+                            up)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_workload_full_parity(idx):
+    cfg = CONFIGS[idx]
+    note(f"chunk parity {cfg.name}")
+    x = make_chunk_inputs(cfg)
+    o, sT = run_chunk(x, cfg.dtype)
+    ref = oracle_chains(x)
+    eo, es = check_chains(x, o, sT, ref, TOL[cfg.dtype], cfg.name)
+    print(f"{cfg.name}: normwise err o={eo:.2e} S={es:.2e}")
+
+
+def test_varlen_t65536_sampled_chains():
+    cfg = CONFIGS[3]
+    note(f"chunk parity {cfg.name} (sampled chains)")
+    x = make_chunk_inputs(cfg)
+    o, sT = run_chunk(x, cfg.dtype, o_fill=float("nan"))
+    assert np.all(np.isfinite(o)), "some output position was not written"
+    lens = np.diff(x.cu_seqlens)
+    rng = np.random.default_rng(1234)
+    chains = {(int(np.argmax(lens)), 0), (int(np.argmin(lens)), cfg.H - 1)}
+    while len(chains) < 8:
+        chains.add((int(rng.integers(cfg.num_seqs)), int(rng.integers(cfg.H))))
+    ref = oracle_chains(x, sorted(chains))
+    eo, es = check_chains(x, o, sT, ref, TOL["bf16"], cfg.name)
+    print(f"{cfg.name}: sampled {len(chains)} chains, err o={eo:.2e} S={es:.2e}")
+
+
+SMALL = []
+for dtype in ("f32", "bf16"):
+    for gate in ("channel", "head"):
+        for dk, dv in ((64, 64), (128, 128), (64, 128), (128, 64)):
+            SMALL.append((dtype, gate, dk, dv))
+
+
+@pytest.mark.parametrize("dtype,gate,dk,dv", SMALL)
+def test_small_ragged(dtype, gate, dk, dv):
+    cfg = CONFIGS[1].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=77)
+    note(f"chunk small {dtype} {gate} dk={dk} dv={dv}")
+    x = make_chunk_inputs(cfg)
+    o, sT = run_chunk(x, dtype)
+    check_chains(x, o, sT, oracle_chains(x), TOL[dtype], f"small {dtype} {gate} {dk}x{dv}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_varlen_edge_lengths(dtype):
+    lens = [0, 1, 63, 64, 65, 130, 0, 7, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1]) + 5   # tokens past the last sequence must stay untouched
+    cfg = CONFIGS[3].replace(dtype=dtype, H=2, T=T, num_seqs=0, pin_frac=0.05, seed=5)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(3).standard_normal((len(lens), 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    note(f"chunk varlen edges {dtype}")
+    o, sT = run_chunk(x, dtype, o_fill=float("nan"))
+    assert np.all(np.isnan(o[0, :, cu[-1]:])), "tokens outside every sequence were written"
+    assert np.all(np.isfinite(o[0, :, :cu[-1]]))
+    ref = oracle_chains(x)
+    check_chains(x, o, sT, ref, TOL[dtype], f"varlen edges {dtype}")
+    for n, ln in enumerate(lens):
+        if ln == 0:   # an empty sequence returns its initial state
+            np.testing.assert_array_equal(sT[n], x.s0[n])
+
+
+@pytest.mark.parametrize("case", ["floor", "no_decay", "beta0", "beta1"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_gates(case, dtype):
+    cfg = CONFIGS[1].replace(dtype=dtype, B=1, H=2, T=300, seed=9)
+    x = make_chunk_inputs(cfg)
+    if case == "floor":
+        x.g[...] = -5.0
+    elif case == "no_decay":
+        x.g[...] = 0.0
+    elif case == "beta0":
+        x.beta[...] = 0.0
+    else:
+        x.beta[...] = 1.0
+    note(f"chunk degenerate {case} {dtype}")
+    o, sT = run_chunk(x, dtype)
+    check_chains(x, o, sT, oracle_chains(x), TOL[dtype], f"{case} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token(dtype):
+    cfg = CONFIGS[1].replace(dtype=dtype, B=3, H=2, T=1, seed=4)
+    x = make_chunk_inputs(cfg)
+    note(f"chunk T=1 {dtype}")
+    o, sT = run_chunk(x, dtype)
+    check_chains(x, o, sT, oracle_chains(x), TOL[dtype], f"T=1 {dtype}")
+
+
+def test_split_resume_and_aliasing():
+    """[0, T) in one call equals [0, T1) then [T1, T) resumed from the returned state;
+    the resumed call passes the same buffer as initial and final state."""
+    import gated_delta_rule_13_amd as kda
+    cfg = CONFIGS[1].replace(B=2, H=4, T=640, seed=21)
+    x = make_chunk_inputs(cfg)
+    dt = torch.bfloat16
+    q, k, v, g, beta, s0 = (up(x.q, dt), up(x.k, dt), up(x.v, dt), up(x.g), up(x.beta),
+                            up(x.s0))
+    note("chunk split/resume")
+    o_full, s_full = kda.chunk_fwd(q, k, v, g, beta, initial_state=s0)
+    T1 = 197
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()  # noqa: E731
+    state = s0.clone()
+    o1, _ = kda.chunk_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1),
+                          sl(beta, 0, T1), initial_state=state, final_state=state)
+    o2, _ = kda.chunk_fwd(sl(q, T1, 640), sl(k, T1, 640), sl(v, T1, 640), sl(g, T1, 640),
+                          sl(beta, T1, 640), initial_state=state, final_state=state)
+    torch.cuda.synchronize()
+    o_split = torch.cat([o1, o2], dim=2).float().cpu().numpy()
+    assert_close(o_split, o_full.float().cpu().numpy(), 1e-2, "split outputs")
+    assert_close(state.cpu().numpy(), s_full.cpu().numpy(), 1e-2, "split state")
+
+
+def test_deterministic():
+    cfg = CONFIGS[1].replace(B=2, H=4, T=1000, seed=8)
+    x = make_chunk_inputs(cfg)
+    note("chunk determinism")
+    o1, s1 = run_chunk(x, "bf16")
+    o2, s2 = run_chunk(x, "bf16")
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_gdn_equals_broadcast_kda():
+    cfg = CONFIGS[2].replace(H=4, T=700, seed=12)
+    x = make_chunk_inputs(cfg)
+    note("chunk GDN vs broadcast KDA")
+    o1, s1 = run_chunk(x, "bf16")
+    x.g = np.ascontiguousarray(np.repeat(x.g[..., None], cfg.dk, axis=-1))
+    o2, s2 = run_chunk(x, "bf16")
+    assert_close(o1, o2, 1e-2, "GDN vs KDA outputs")
+    assert_close(s1, s2, 1e-2, "GDN vs KDA states")
