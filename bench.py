@@ -1,0 +1,247 @@
+"""Benchmark of the gated delta rule forward (KDA) on one MI355X.
+
+A step is one kda_chunk_fwd call over the packed variable-length workload
+(H = 32, dk = dv = 128, T = 65536 tokens in 8 sequences, bf16 q/k/v/o, fp32
+per-channel log-decay and beta, chunk 64): cumulative decay, stability scaling, UT
+transform, sequential state pass and chunk output, all in one fused kernel launch.
+Inputs are seeded synthetic tensors resident in HBM before the timed region.
+
+Printed (one JSON line on stdout):
+  value          tokens/s of that step (65536 tokens per step)
+  roofline       the chunk kernel against the HBM roofline: algorithmic bytes per
+                 launch / average launch time (HIP events on the launch stream),
+                 and the HBM bytes measured by rocprofv3 counters when given
+  mfma           the same kernel's algorithmic flops against the bf16 MFMA peak
+  decode         kda_recurrent_step on 256 sequences x 32 heads, 512 consecutive
+                 steps on a resident fp32 state: tokens/s and HBM GB/s
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd tokens/s at H=32,dk=dv=128,T=64K; % MFMA peak; decode HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+CHUNK = 64
+
+# HBM traffic of the chunk kernel per launch, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# WRITE_SIZE, KiB per dispatch) each scaled by the counter/byte ratio measured on a
+# plain 1 GiB copy kernel. None until measured for the current kernel.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def chunk_alg_flops_per_head_token(dk: int, dv: int, C: int = CHUNK) -> float:
+    """Three C x dk x dv contractions (W S or K^ S, Q^ S, K_dec^T V'), A_kk, A_qk and the
+    beta-scaled key product at C dk each, T V and A_qk V' at C dv each, and the
+    triangular inverse, counted without the zero halves of triangular tiles."""
+    return 6 * dk * dv + 3 * C * dk + 2 * C * dv + C * C / 3
+
+
+def chunk_alg_bytes(x) -> float:
+    """Inputs read once and outputs written once: q, k, v (bf16), g (fp32 per channel),
+    beta (fp32), o (bf16), plus the initial / final state of every chain (fp32)."""
+    B, H, T, dk = x.q.shape
+    dv = x.v.shape[-1]
+    per_tok = 2 * (2 * dk + dv) + 4 * (dk if x.g.ndim == 4 else 1) + 4 + 2 * dv
+    n_chains = x.n_seqs * H
+    state = 4 * dk * dv * n_chains * (2 if x.s0 is not None else 1)
+    return float(per_tok * B * H * T + state)
+
+
+def decode_alg_bytes_per_step(N: int, H: int, dk: int, dv: int) -> float:
+    """State read and written once (fp32), q, k, v (bf16), g (fp32), beta, o (bf16)."""
+    per_chain = 2 * dk * dv * 4 + 2 * (2 * dk + dv) + 4 * dk + 4 + 2 * dv
+    return float(per_chain * N * H)
+
+
+def bench_chunk(torch, kda, x, steps: int, warmup: int):
+    dev = torch.device("cuda:0")
+    up = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)  # noqa
+    q, k, v = (up(a, torch.bfloat16) for a in (x.q, x.k, x.v))
+    g, beta = up(x.g), up(x.beta)
+    cu = up(x.cu_seqlens, torch.int32) if x.cu_seqlens is not None else None
+    s0 = up(x.s0) if x.s0 is not None else None
+    o = torch.empty(tuple(x.v.shape), dtype=torch.bfloat16, device=dev)
+    sT = torch.empty((x.n_seqs, x.q.shape[1], x.q.shape[3], x.v.shape[3]), dtype=torch.float32,
+                     device=dev)
+    call = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, o=o,  # noqa
+                                 final_state=sT)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def bench_decode(torch, kda, cfg, reps: int = 5):
+    from kda_workloads import decode_initial_state, decode_step_inputs
+    dev = torch.device("cuda:0")
+    N, H, dk, dv, S = cfg.B, cfg.H, cfg.dk, cfg.dv, cfg.T
+    t0 = time.time()
+    qs = torch.empty((S, N, H, dk), dtype=torch.bfloat16, device=dev)
+    ks = torch.empty_like(qs)
+    vs = torch.empty((S, N, H, dv), dtype=torch.bfloat16, device=dev)
+    gs = torch.empty((S, N, H, dk), dtype=torch.float32, device=dev)
+    bs = torch.empty((S, N, H), dtype=torch.float32, device=dev)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        for s, d in enumerate(ex.map(lambda i: decode_step_inputs(cfg, i), range(S))):
+            qs[s].copy_(torch.from_numpy(d.q))
+            ks[s].copy_(torch.from_numpy(d.k))
+            vs[s].copy_(torch.from_numpy(d.v))
+            gs[s].copy_(torch.from_numpy(d.g))
+            bs[s].copy_(torch.from_numpy(d.beta))
+    s_init = torch.from_numpy(decode_initial_state(cfg)).to(dev)
+    state = torch.empty_like(s_init)
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+    log(f"decode inputs generated and resident in {time.time() - t0:.1f}s")
+    stream = torch.cuda.current_stream(dev)
+    state.copy_(s_init)
+    for s in range(8):  # warm-up
+        kda.recurrent_step(qs[s], ks[s], vs[s], gs[s], bs[s], state, o=o)
+    times = []
+    for _ in range(reps):
+        state.copy_(s_init)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for s in range(S):
+            kda.recurrent_step(qs[s], ks[s], vs[s], gs[s], bs[s], state, o=o)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / 1e3)
+    return statistics.median(times)
+
+
+def cpu_baseline(x, max_chains: int):
+    """The fp64 oracle as it stands, on the host cores, over a seeded sample of chains of
+    the same workload (all tokens of each sampled chain). Reported in tokens/s of the
+    metric (head-tokens / H, i.e. positions carrying all heads)."""
+    import oracle
+    H = x.q.shape[1]
+    all_chains = [(n, h) for n in range(x.n_seqs) for h in range(H)]
+    rng = np.random.default_rng(2024)
+    idx = np.sort(rng.choice(len(all_chains), size=min(max_chains, len(all_chains)),
+                             replace=False))
+    chains = [all_chains[i] for i in idx]
+    head_tokens = sum(x.chain_rows(n, h)[2] for (n, h) in chains)
+    threads = oracle.max_threads()
+    chains, cargs, ckw = oracle.pack_chains(x.q, x.k, x.v, x.g, x.beta, x.s0, x.cu_seqlens,
+                                            chains)
+    t0 = time.perf_counter()
+    oracle.kda_chains(*cargs, **ckw, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": head_tokens / H / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(chains)} of {len(all_chains)} (sequence, head) chains of the "
+                      f"workload, all their tokens ({head_tokens} head-tokens), fp64 token "
+                      f"recurrence, {dt:.1f} s"}
+
+
+def copy_probe(torch):
+    """A plain 1 GiB device copy, run only to calibrate the HBM byte counters."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-chains", type=int, default=256)
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gated_delta_rule_13_amd as kda
+    from kda_workloads import CONFIGS, make_chunk_inputs
+
+    kda.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    cfg = CONFIGS[3]
+    t0 = time.time()
+    x = make_chunk_inputs(cfg)
+    log(f"generated {cfg.name} in {time.time() - t0:.1f}s; lengths {np.diff(x.cu_seqlens)}")
+    if args.copy_probe:
+        copy_probe(torch)
+    ms = bench_chunk(torch, kda, x, args.steps, args.warmup)
+    tokens = cfg.T
+    value = tokens / (ms / 1e3)
+    alg_bytes = chunk_alg_bytes(x)
+    alg_flops = chunk_alg_flops_per_head_token(cfg.dk, cfg.dv) * cfg.H * cfg.T
+    gbs = alg_bytes / (ms / 1e3) / 1e9
+    tflops = alg_flops / (ms / 1e3) / 1e12
+    log(f"chunk_fwd: {ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s, {gbs:.0f} GB/s, "
+        f"{tflops:.1f} TFLOP/s")
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "H": cfg.H, "dk": cfg.dk, "dv": cfg.dv,
+                   "T": cfg.T, "num_seqs": cfg.num_seqs, "gate": "per-key-channel",
+                   "chunk": CHUNK, "state": "fp32", "qkvo": "bf16", "g_beta": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": MEASURED_TRAFFIC_BYTES,
+                     "kernel": "kda chunk forward (fused)",
+                     "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
+    }
+    if not args.no_decode:
+        dcfg = CONFIGS[4]
+        sec = bench_decode(torch, kda, dcfg)
+        per_step = decode_alg_bytes_per_step(dcfg.B, dcfg.H, dcfg.dk, dcfg.dv)
+        dgbs = per_step * dcfg.T / sec / 1e9
+        result["decode"] = {
+            "workload": dcfg.name, "steps": dcfg.T, "us_per_step": sec / dcfg.T * 1e6,
+            "tokens_per_s": dcfg.B * dcfg.T / sec, "hbm_gbs": dgbs,
+            "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
+        log(f"decode: {sec / dcfg.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_chains)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -19,12 +19,17 @@ Distributions (the same for every workload unless stated):
   beta  = sigmoid(x), x ~ N(0, 1)
   g     = max(-5, -exp(x)), x ~ N(-3, 1)   (log of the decay alpha, per token)
   s0    ~ N(0, 0.02^2) where a workload has a random initial state
-Draw order: q, k, v, beta, g, s0, then sequence lengths and pinned rows.
+Every tensor is drawn in blocks of one (batch row, head) from its own counter-style
+seeded stream, numpy.random.default_rng([seed, tensor id, batch row, head]), so the
+values do not depend on how many threads fill the blocks; the sequence lengths and
+the pinned rows have streams of their own.
 """
 
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -73,16 +78,55 @@ CONFIGS = [
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 value (ties to even), kept as float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    """Round finite float32 values to the nearest bfloat16 value (ties to even), kept as
+    float32. (For finite inputs the 32-bit sum below cannot overflow.)"""
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 def _l2_normalise(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True, dtype=np.float32))
-    return (x / n).astype(np.float32)
+    n = np.sqrt(np.einsum("...i,...i->...", x, x))[..., None]
+    x /= n
+    return x
+
+
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _blocks(seed: int, tid: int, lead, tail, fill):
+    """Array of shape lead + tail; block (i, j) of the two leading axes is filled by
+    fill(rng, tail) with rng = default_rng([seed, tid, i, j])."""
+    out = np.empty(tuple(lead) + tuple(tail), np.float32)
+
+    def one(ij):
+        i, j = ij
+        out[i, j] = fill(np.random.default_rng([seed, tid, i, j]), tail)
+
+    jobs = [(i, j) for i in range(lead[0]) for j in range(lead[1])]
+    if len(jobs) == 1 or int(np.prod(tail)) < 65536:
+        for ij in jobs:
+            one(ij)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(one, jobs))
+    return out
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def _unit_normal(rng, shape):
+    return _l2_normalise(rng.standard_normal(shape, dtype=np.float32))
+
+
+def _sigmoid_normal(rng, shape):
+    return _sigmoid(rng.standard_normal(shape, dtype=np.float32))
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
@@ -90,8 +134,12 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
 
 
 def _log_decay(rng: np.random.Generator, shape) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32) - np.float32(3.0)
-    return np.maximum(np.float32(G_FLOOR), -np.exp(x)).astype(np.float32)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    x -= np.float32(3.0)
+    np.exp(x, out=x)
+    np.negative(x, out=x)
+    np.maximum(x, np.float32(G_FLOOR), out=x)
+    return x
 
 
 def varlen_lengths(rng: np.random.Generator, num_seqs: int, total: int,
@@ -143,27 +191,27 @@ class ChunkInputs:
 def make_chunk_inputs(cfg: WorkloadConfig) -> ChunkInputs:
     """Inputs of a prefill workload (or of a smaller case built with ``cfg.replace``)."""
     assert cfg.kind == "chunk"
-    rng = np.random.default_rng(cfg.seed)
-    B, H, T, dk, dv = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv
-    q = _l2_normalise(rng.standard_normal((B, H, T, dk), dtype=np.float32))
-    k = _l2_normalise(rng.standard_normal((B, H, T, dk), dtype=np.float32))
-    v = rng.standard_normal((B, H, T, dv), dtype=np.float32)
+    B, H, T, dk, dv, sd = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.seed
+    q = _blocks(sd, 0, (B, H), (T, dk), _unit_normal)
+    k = _blocks(sd, 1, (B, H), (T, dk), _unit_normal)
+    v = _blocks(sd, 2, (B, H), (T, dv), _normal)
     if cfg.dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
-    beta = _sigmoid(rng.standard_normal((B, H, T), dtype=np.float32))
-    g = _log_decay(rng, (B, H, T, dk) if cfg.gate == "channel" else (B, H, T))
+    beta = _blocks(sd, 3, (B, H), (T,), _sigmoid_normal)
+    g = _blocks(sd, 4, (B, H), (T, dk) if cfg.gate == "channel" else (T,), _log_decay)
     n_seqs = cfg.num_seqs if cfg.num_seqs else B
     s0 = None
     if cfg.random_s0:
-        s0 = (rng.standard_normal((n_seqs, H, dk, dv), dtype=np.float32) * np.float32(0.02))
+        s0 = _blocks(sd, 5, (n_seqs, H), (dk, dv), _normal)
+        s0 *= np.float32(0.02)
     cu = None
     if cfg.num_seqs:
         assert B == 1
-        lens = varlen_lengths(rng, cfg.num_seqs, T)
+        lens = varlen_lengths(np.random.default_rng([sd, 6]), cfg.num_seqs, T)
         cu = np.zeros(cfg.num_seqs + 1, dtype=np.int32)
         cu[1:] = np.cumsum(lens)
     if cfg.pin_frac > 0:
-        pin = rng.random((B, H, T)) < cfg.pin_frac
+        pin = np.random.default_rng([sd, 7]).random((B, H, T)) < cfg.pin_frac
         g[pin] = np.float32(G_FLOOR)
     return ChunkInputs(cfg, q, k, v, g, beta, s0, cu)
 
@@ -179,23 +227,24 @@ class DecodeInputs:
 
 def decode_initial_state(cfg: WorkloadConfig) -> np.ndarray:
     """Resident fp32 state [N, H, dk, dv] ~ N(0, 0.02^2) (zeros if the workload has none)."""
-    shape = (cfg.B, cfg.H, cfg.dk, cfg.dv)
+    N, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
     if not cfg.random_s0:
-        return np.zeros(shape, np.float32)
-    rng = np.random.default_rng([cfg.seed, 0])
-    return rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+        return np.zeros((N, H, dk, dv), np.float32)
+    s = _blocks(cfg.seed, 5, (N, H), (dk, dv), _normal)
+    s *= np.float32(0.02)
+    return s
 
 
 def decode_step_inputs(cfg: WorkloadConfig, step: int) -> DecodeInputs:
-    """Inputs of decode step ``step`` (0-based); each step has its own seeded stream."""
+    """Inputs of decode step ``step`` (0-based); each step has its own seeded streams."""
     assert cfg.kind == "decode"
-    rng = np.random.default_rng([cfg.seed, step + 1])
+    rng = lambda tid: np.random.default_rng([cfg.seed, 100 + tid, step])  # noqa: E731
     N, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
-    q = _l2_normalise(rng.standard_normal((N, H, dk), dtype=np.float32))
-    k = _l2_normalise(rng.standard_normal((N, H, dk), dtype=np.float32))
-    v = rng.standard_normal((N, H, dv), dtype=np.float32)
+    q = _unit_normal(rng(0), (N, H, dk))
+    k = _unit_normal(rng(1), (N, H, dk))
+    v = _normal(rng(2), (N, H, dv))
     if cfg.dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
-    beta = _sigmoid(rng.standard_normal((N, H), dtype=np.float32))
-    g = _log_decay(rng, (N, H, dk) if cfg.gate == "channel" else (N, H))
+    beta = _sigmoid_normal(rng(3), (N, H))
+    g = _log_decay(rng(4), (N, H, dk) if cfg.gate == "channel" else (N, H))
     return DecodeInputs(q, k, v, g, beta)

@@ -88,14 +88,11 @@ def kda_chains(q, k, v, g, beta, row_off, row_len, s0=None, erase=None, write=No
     return o, sf
 
 
-def kda_forward(q, k, v, g, beta, s0=None, cu_seqlens=None,
-                chains: Optional[Iterable[Tuple[int, int]]] = None,
-                threads: int = 0) -> Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]]:
-    """Forward over head-major inputs [B, H, T, ...] (B = 1 with ``cu_seqlens``).
-
-    Each (sequence n, head h) is an independent chain. ``chains`` selects a subset
-    (default: all). Returns {(n, h): (o [len, dv], final state [dk, dv])}, float64.
-    """
+def pack_chains(q, k, v, g, beta, s0=None, cu_seqlens=None,
+                chains: Optional[Iterable[Tuple[int, int]]] = None):
+    """Gathers the rows of the selected (sequence n, head h) chains of head-major inputs
+    [B, H, T, ...] (B = 1 with ``cu_seqlens``) into the flat float64 arrays of
+    ``kda_chains``. Returns (chains, args, kwargs) with ``kda_chains(*args, **kwargs)``."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if cu_seqlens is not None:
@@ -109,30 +106,38 @@ def kda_forward(q, k, v, g, beta, s0=None, cu_seqlens=None,
         chains = [(n, h) for n in range(N) for h in range(H)]
     chains = list(chains)
     per_channel = g.ndim == 4
-    qs, ks, vs, gs, bs, offs, lens, s0s = [], [], [], [], [], [], [], []
+    offs, lens = [], []
     row = 0
     for (n, h) in chains:
-        b, t0, ln = spans[n]
-        sl = slice(t0, t0 + ln)
-        qs.append(q[b, h, sl])
-        ks.append(k[b, h, sl])
-        vs.append(v[b, h, sl])
-        gs.append(g[b, h, sl])
-        bs.append(beta[b, h, sl])
         offs.append(row)
-        lens.append(ln)
-        row += ln
-        if s0 is not None:
-            s0s.append(s0[n, h])
-    cat = lambda xs, shape: (np.concatenate(xs) if xs else np.zeros(shape))  # noqa: E731
-    o, sf = kda_chains(cat(qs, (0, dk)), cat(ks, (0, dk)), cat(vs, (0, dv)),
-                       cat(gs, (0, dk) if per_channel else (0,)), cat(bs, (0,)),
-                       offs, lens, np.stack(s0s) if s0 is not None else None,
-                       threads=threads)
-    out = {}
-    for c, (n, h) in enumerate(chains):
-        out[(n, h)] = (o[offs[c]:offs[c] + lens[c]], sf[c])
-    return out
+        lens.append(spans[n][2])
+        row += spans[n][2]
+
+    def gather(x, width):
+        out = np.empty((row,) + ((width,) if width else ()), np.float64)
+        for c, (n, h) in enumerate(chains):
+            b, t0, ln = spans[n]
+            out[offs[c]:offs[c] + ln] = x[b, h, t0:t0 + ln]
+        return out
+
+    args = (gather(q, dk), gather(k, dk), gather(v, dv), gather(g, dk if per_channel else 0),
+            gather(beta, 0), offs, lens)
+    kwargs = {"s0": np.stack([s0[n, h] for (n, h) in chains]) if s0 is not None else None}
+    return chains, args, kwargs
+
+
+def kda_forward(q, k, v, g, beta, s0=None, cu_seqlens=None,
+                chains: Optional[Iterable[Tuple[int, int]]] = None,
+                threads: int = 0) -> Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]]:
+    """Forward over head-major inputs [B, H, T, ...] (B = 1 with ``cu_seqlens``).
+
+    Each (sequence n, head h) is an independent chain. ``chains`` selects a subset
+    (default: all). Returns {(n, h): (o [len, dv], final state [dk, dv])}, float64.
+    """
+    chains, args, kwargs = pack_chains(q, k, v, g, beta, s0, cu_seqlens, chains)
+    o, sf = kda_chains(*args, **kwargs, threads=threads)
+    offs, lens = args[5], args[6]
+    return {ch: (o[offs[c]:offs[c] + lens[c]], sf[c]) for c, ch in enumerate(chains)}
 
 
 def kda_decode_step(state, q, k, v, g, beta, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
