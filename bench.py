@@ -39,8 +39,22 @@ CHUNK = 64
 
 # HBM traffic of the chunk kernel per launch, from two rocprofv3 --pmc runs (FETCH_SIZE,
 # WRITE_SIZE, KiB per dispatch) each scaled by the counter/byte ratio measured on a
-# plain 1 GiB copy kernel. None until measured for the current kernel.
-MEASURED_TRAFFIC_BYTES = None
+# plain 1 GiB copy kernel in the same runs. It is reported only while the kernel source
+# is the one the counters were taken on (its SHA-256 below); otherwise traffic is null.
+MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
+    "bytes": 3246813788,
+    "kernel_sha256": "33159e42310271669d0de47753c1e7d3b7c5ac3e649a6a96e3ed5f498e36c5e0",
+}
+CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_13_amd", "csrc", "kda_chunk_mfma.hip")
+
+
+def measured_traffic():
+    import hashlib
+    if not MEASURED_TRAFFIC:
+        return None
+    with open(CHUNK_KERNEL_SRC, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return MEASURED_TRAFFIC["bytes"] if digest == MEASURED_TRAFFIC["kernel_sha256"] else None
 
 
 def log(msg: str) -> None:
@@ -220,7 +234,7 @@ def main() -> int:
                    "chunk": CHUNK, "state": "fp32", "qkvo": "bf16", "g_beta": "fp32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": MEASURED_TRAFFIC_BYTES,
+                     "traffic": measured_traffic(),
                      "kernel": "kda chunk forward (fused)",
                      "alg_bytes_per_launch": alg_bytes},
         "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
