@@ -8,41 +8,76 @@
 // step is a pure HBM stream: 2 * dk * dv * 4 bytes of state traffic per chain
 // against about 8 * dk * dv flops.
 //
-// Layout: one 256-thread workgroup per chain. Thread t owns the float4 column group
-// cq = t % (dv / 4) and the rows rg, rg + RG, rg + 2 RG, ... with rg = t / (dv / 4),
-// RG = 256 / (dv / 4). A wavefront therefore reads whole 512-byte state rows with
-// 16-byte loads. The column reductions over rows go through LDS.
+// Layout: a persistent grid of 1024-thread workgroups; each takes one chain at a time
+// (grid stride). Thread t owns the float4 column group cq = t % (dv / 4) and the rows
+// rg, rg + RG, ... with rg = t / (dv / 4), RG = 1024 / (dv / 4), so a wavefront reads
+// two whole 512-byte state rows per 16-byte load. The column reductions over rows go
+// through LDS. The state streams through HBM with non-temporal loads and stores; at
+// the 256 x 32 decode workload this runs at about 76% of the HBM peak, against 79% for
+// a plain read-modify-write of the same bytes.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;     // one workgroup = one chain's full dk x dv state
+constexpr int kPersistGrid = 1024;  // workgroups; each loops over chains (grid stride)
 
-template <int DK, int DV, typename TIn, bool PER_CHANNEL>
-__global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
-  constexpr int QUADS = DV / 4;
-  constexpr int RG = kThreads / QUADS;
+typedef float nf4 __attribute__((ext_vector_type(4)));
+
+// The state is streamed once per step (537 MB at the decode workload, twice the MALL),
+// so its loads and stores are non-temporal.
+__device__ __forceinline__ float4 ld_state(const float4* p) {
+  const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_state(float4* p, float4 v) {
+  const nf4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nf4*>(p));
+}
+
+// Workgroups of THREADS threads loop over the work items (chain, block of DVB value
+// columns) with a grid stride.
+template <int DK, int DV, int DVB, int THREADS, typename TIn, bool PER_CHANNEL>
+__global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
+  constexpr int QUADS = DVB / 4;
+  constexpr int RG = THREADS / QUADS;
   constexpr int RPT = DK / RG;
-  static_assert(RPT * RG == DK, "rows must split evenly over row groups");
+  constexpr int NB = DV / DVB;
+  static_assert(RPT * RG == DK && QUADS * RG == THREADS, "rows must split evenly");
 
   __shared__ float s_k[DK];
   __shared__ float s_q[DK];
   __shared__ float s_alpha[DK];
   __shared__ float4 s_red_p[RG][QUADS];
   __shared__ float4 s_red_y[RG][QUADS];
-  __shared__ float s_kq[kThreads / 64];
+  __shared__ float s_kq[THREADS / 64];
 
-  const int chain = blockIdx.x;  // n * H + h
   const int tid = threadIdx.x;
+  const int items = a.N * a.H * NB;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+  if (item != (int)blockIdx.x) __syncthreads();  // the previous item is done with LDS
+  const int chain = item / NB;  // n * H + h
+  const int col0 = (item % NB) * DVB;
   const TIn* qp = static_cast<const TIn*>(a.q) + (size_t)chain * DK;
   const TIn* kp = static_cast<const TIn*>(a.k) + (size_t)chain * DK;
-  const TIn* vp = static_cast<const TIn*>(a.v) + (size_t)chain * DV;
+  const TIn* vp = static_cast<const TIn*>(a.v) + (size_t)chain * DV + col0;
 
-  // key, query and decay of this token; k^T q by a wavefront reduction
+  const int cq = tid % QUADS;
+  const int rg = tid / QUADS;
+  float4* S = reinterpret_cast<float4*>(a.state + (size_t)chain * DK * DV + col0);
+  constexpr int ROWQ = DV / 4;  // float4 per state row
+
+  auto row_of = [&](int i) { return rg + RG * i; };
+
+  // issue the state loads first; the vectors and k^T q are computed while they fly
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) s[i] = ld_state(&S[row_of(i) * ROWQ + cq]);
+
   float kq = 0.f;
-  for (int i = tid; i < DK; i += kThreads) {
+  for (int i = tid; i < DK; i += THREADS) {
     const float kk = to_f32(kp[i]);
     const float qq = to_f32(qp[i]);
     s_k[i] = kk;
@@ -54,17 +89,12 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
   if ((tid & 63) == 0) s_kq[tid >> 6] = kq;
   __syncthreads();
 
-  const int cq = tid % QUADS;
-  const int rg = tid / QUADS;
-  float4* S = reinterpret_cast<float4*>(a.state + (size_t)chain * DK * DV);
-
-  float4 s[RPT];
   float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    float4 x = S[r * QUADS + cq];
+    const int r = row_of(i);
+    float4 x = s[i];
     const float al = s_alpha[r];
     x.x *= al; x.y *= al; x.z *= al; x.w *= al;
     s[i] = x;
@@ -85,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
   }
   float kqs = 0.f;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) kqs += s_kq[w];
+  for (int w = 0; w < THREADS / 64; ++w) kqs += s_kq[w];
 
   const float b = a.beta[chain];
   float4 d;
@@ -96,34 +126,38 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs a) {
 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
+    const int r = row_of(i);
     const float kr = s_k[r];
     float4 x = s[i];
     x.x += kr * d.x; x.y += kr * d.y; x.z += kr * d.z; x.w += kr * d.w;
-    S[r * QUADS + cq] = x;
+    st_state(&S[r * ROWQ + cq], x);
   }
   if (rg == 0) {
-    TIn* op = static_cast<TIn*>(a.o) + (size_t)chain * DV + 4 * cq;
+    TIn* op = static_cast<TIn*>(a.o) + (size_t)chain * DV + col0 + 4 * cq;
     op[0] = from_f32<TIn>(y.x + kqs * d.x);
     op[1] = from_f32<TIn>(y.y + kqs * d.y);
     op[2] = from_f32<TIn>(y.z + kqs * d.z);
     op[3] = from_f32<TIn>(y.w + kqs * d.w);
   }
+  }
 }
 
 template <int DK, int DV>
 hipError_t launch_dims(const DecodeArgs& a, bool bf16, bool per_channel, hipStream_t stream) {
-  const dim3 grid(a.N * a.H), block(kThreads);
+  constexpr int DVB = DV;
+  constexpr int THREADS = kThreads;
+  const int items = a.N * a.H * (DV / DVB);
+  const dim3 grid(items > kPersistGrid ? kPersistGrid : items), block(THREADS);
   if (bf16) {
     if (per_channel)
-      decode_step_kernel<DK, DV, kda::bf16, true><<<grid, block, 0, stream>>>(a);
+      decode_step_kernel<DK, DV, DVB, THREADS, kda::bf16, true><<<grid, block, 0, stream>>>(a);
     else
-      decode_step_kernel<DK, DV, kda::bf16, false><<<grid, block, 0, stream>>>(a);
+      decode_step_kernel<DK, DV, DVB, THREADS, kda::bf16, false><<<grid, block, 0, stream>>>(a);
   } else {
     if (per_channel)
-      decode_step_kernel<DK, DV, float, true><<<grid, block, 0, stream>>>(a);
+      decode_step_kernel<DK, DV, DVB, THREADS, float, true><<<grid, block, 0, stream>>>(a);
     else
-      decode_step_kernel<DK, DV, float, false><<<grid, block, 0, stream>>>(a);
+      decode_step_kernel<DK, DV, DVB, THREADS, float, false><<<grid, block, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
