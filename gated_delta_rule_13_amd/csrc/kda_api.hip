@@ -51,7 +51,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
-  if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv))
+  if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T))
     err = kda::launch_chunk_mfma(a, per_channel, stream);
   else
     err = kda::launch_chunk_f32(a, dt == KDA_BF16, per_channel, stream);

@@ -14,23 +14,32 @@
 // Every factor above is <= 1 except k / P (<= e^80 |k|), and every product of two of them
 // is the exact exp(G_i - G_j) weighting, so no quantity is divided by a small decay.
 //
-// Layout: one workgroup per chain (sequence, head) with NW = dv / 16 wavefronts (8 for
-// dv = 128, two per SIMD); wavefront w owns value columns [16 w, 16 w + 16) of the state
-// for the whole sequence, held in matrix-core accumulator registers. The sequence is
-// processed 64 tokens (four 16-token blocks) at a time: all wavefronts first compute the
-// decay products and the bf16 operands of the four blocks into LDS; wavefronts 0..3 then
-// compute the 16 x 16 A_qk / A_kk tile of one block each and invert its (I + A_kk) on the
-// fp32 matrix cores; finally every wavefront runs the four blocks' state steps for its
-// own columns. The next 64 tokens are loaded into registers during those state steps.
+// Layout: one workgroup per chain (sequence, head) with eight wavefronts in two roles.
+// The four "prep" wavefronts each own one 16-token block of the next 64 tokens: they
+// load its q, k, g, beta, compute the decay products and the bf16 operands into LDS, then
+// the block's A_qk / A_kk tile and the inverse of its (I + Diag(beta) A_kk) on the fp32
+// matrix cores -- no other wavefront is involved, so they need no barrier. The four
+// "state" wavefronts each own dv / 4 value columns of the state for the whole sequence,
+// held in matrix-core accumulator registers, and run the four blocks' state steps of the
+// current 64 tokens from the other LDS buffer; their outputs go through an LDS tile and
+// leave as 16-byte pieces of token rows. One workgroup barrier per 64 tokens swaps the
+// two buffers, so the vector-ALU work of preparing tokens t + 64 overlaps the
+// matrix-core chain of the state steps of tokens t.
 //
 // Matrix-core operand layouts used (lane l, r = l % 16, p = l / 16):
 //   16x16x32 bf16: A[r][8p + i], B[8p + i][r] (i < 8); D[4p + e][r] (e < 4)
 //   16x16x16 bf16: A[r][4p + i], B[4p + i][r] (i < 4); D[4p + e][r]
 //   16x16x4  fp32: A[r][p], B[p][r]; D[4p + e][r]
 // The D layout of one product is the B layout of a 16x16x16 product, which chains the
-// UT solve and the state update in registers. The contraction of the 16x16x32 products
-// over channels is permuted (k = 8p + i <-> channel 32s + 16(i/4) + 4p + i%4) so that two
-// D tiles of the state form one B operand without moving data between lanes.
+// UT solve and the state update in registers. A state wavefront keeps its dk x 16 slice of
+// S as eight accumulator tiles whose rows are a fixed permutation of the key channels:
+// tile m = 2 s + h, row 4 p + e holds channel 32 s + 8 p + 4 h + e. Then tiles 2 s and
+// 2 s + 1 together are the B operand of a 16x16x32 product over channels [32 s, 32 s + 32)
+// in natural order, and the matching A operand is 16 contiguous bytes of a token row.
+//
+// Global memory is read and written through buffer descriptors bounded by the chain's
+// rows: reads past the sequence's end return zero (q = k = 0, g = 0, beta = 0 is the
+// identity token) and writes past it are dropped, so partial chunks need no branches.
 #include <stddef.h>
 
 #include "kda_device.h"
@@ -43,35 +52,44 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-#ifndef KDA_NW128
-#define KDA_NW128 8  // wavefronts per workgroup for dv = 128 (each owns 128 / (16 NW) tiles)
-#endif
-
-constexpr int kC = 64;         // tokens loaded and prepared at a time (four blocks)
+constexpr int kC = 64;         // tokens prepared and consumed per step (four blocks)
 constexpr int kDK = 128;       // key head size of this kernel
 constexpr int kLDK = kDK + 8;  // padded LDS row (bf16) of [token][channel] tiles
 constexpr int kLDT = kC + 8;   // padded LDS row (bf16) of [channel][token] tiles
+constexpr int kPrepWaves = 4;  // one per 16-token block
 
-struct Smem {
+
+// Operands of 64 tokens, written by the prep wavefronts and read by the state wavefronts.
+struct Stage {
   bf16 qr[kC][kLDK];      // q * P
   bf16 kr[kC][kLDK];      // k * P
-  bf16 kd[kC][kLDK];      // k / P
   bf16 kcT[kDK][kLDT];    // (k * E)^T
-  bf16 vT[128][kLDT];     // V^T (value column, token)
   bf16 aqk[4][16][24];    // A_qk of each block (lower, diagonal included)
   bf16 tdiag[4][16][24];  // (I + Diag(beta) A_kk)^-1 of each block
   float tot[4][kDK];      // decay over each block
   float beta[kC];
 };
+struct Smem {
+  Stage st[2];            // double buffer
+  bf16 kd[kC][kLDK];      // k / P (prep wavefronts only; each reads back its own rows)
+  bf16 ost[kC][kLDK];     // outputs of the last 64 tokens (each state wavefront: its columns)
+};
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one CU");
-static_assert(offsetof(Smem, kcT) % 16 == 0 && offsetof(Smem, vT) % 16 == 0 &&
-                  offsetof(Smem, aqk) % 16 == 0 && offsetof(Smem, tdiag) % 16 == 0 &&
-                  offsetof(Smem, tot) % 16 == 0,
+static_assert(sizeof(Stage) % 16 == 0 && offsetof(Stage, kcT) % 16 == 0 &&
+                  offsetof(Stage, aqk) % 16 == 0 && offsetof(Stage, tdiag) % 16 == 0 &&
+                  offsetof(Stage, tot) % 16 == 0 && offsetof(Smem, kd) % 16 == 0 &&
+                  offsetof(Smem, ost) % 16 == 0,
               "vector LDS accesses need 16-byte aligned arrays");
 static_assert((kLDK * 2) % 16 == 0 && (kLDT * 2) % 16 == 0, "row pitch must keep alignment");
 
-// LDS-only barrier: waits for this wavefront's LDS operations, not for its global loads
-// (the prefetch of the next tokens stays in flight across it).
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes are done
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits for this wavefront's LDS operations, not for its global
+// loads (prefetches stay in flight across it).
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited on
@@ -109,217 +127,149 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
-// CPT consecutive bf16 values packed in registers (CPT = 2 or 4).
-template <int CPT>
-struct BfVec {
-  typedef __attribute__((__vector_size__(CPT * sizeof(__bf16)))) __bf16 type;
-};
-template <int CPT>
-struct F32Vec {
-  typedef __attribute__((__vector_size__(CPT * sizeof(float)))) float type;
-};
-template <int CPT>
-__device__ __forceinline__ typename BfVec<CPT>::type pack_bf(const float* v) {
-  typename F32Vec<CPT>::type f;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) f[j] = v[j];
-  return __builtin_convertvector(f, typename BfVec<CPT>::type);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes from p (stride 0: offsets are byte offsets and
+// an access at or past `bytes` reads zero / writes nothing).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
-template <int CPT>
-__device__ __forceinline__ void ld_f32(const float* src, float* dst) {
-  if constexpr (CPT == 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = v[j];
-  } else {
-    const float2 v = *reinterpret_cast<const float2*>(src);
-    dst[0] = v.x;
-    dst[1] = v.y;
-  }
+__device__ __forceinline__ bf16x4 ld_b64(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ f32x4 ld_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float ld_b32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ bf16 ld_b16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+__device__ __forceinline__ void st_b128(rsrc_t r, uint32_t off, bf16x8 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), r, off, 0, 0);
 }
 
-// Work split of a workgroup with NW wavefronts. In the decay phase, wavefront w covers
-// block I = w / (NW / 4) and channel segment w % (NW / 4); lane l covers the CPT channels
-// CPT * (l % 32) + j of that segment and tokens 8 * (l / 32) + u of the block.
-template <int NW, int NT = 1>
-struct Split {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int CPT = 16 / NW;   // channels per thread in the decay phase
-  static constexpr int SEGS = NW / 4;   // channel segments per block
-  static constexpr int DV = 16 * NW * NT;
-  __device__ static int block(int wave) { return wave / SEGS; }
-  __device__ static int channel0(int wave, int lane) {
-    return (wave % SEGS) * (kDK / SEGS) + CPT * (lane & 31);
-  }
-};
+// x from lane 4 (lane / 4) + E of this lane's quad (DPP quad permutation, no LDS access).
+template <int E>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), E * 0x55, 0xf, 0xf, true));
+}
 
-// Inputs of 64 tokens held in registers by one thread: q, k, g for 8 tokens x CPT
-// channels (decay-phase split), two 8-column segments of v (token-major over the lanes,
-// staged through LDS), and beta of one token (used by the first 64 threads).
-template <int NW, int NT>
-struct ChunkRegs {
-  typename BfVec<Split<NW>::CPT>::type q[8];
-  typename BfVec<Split<NW>::CPT>::type k[8];
-  float g[8][Split<NW>::CPT];
-  bf16x8 v[2 * NT];
+// Raw inputs of one 16-token block held by one prep lane: 8 tokens (half hf = lane / 32)
+// x 4 channels (4 * (lane % 32) + j); beta of token lane for lanes < 16.
+struct BlockRegs {
+  bf16x4 q[8];
+  bf16x4 k[8];
+  f32x4 g[8];
   float beta;
 };
 
-// Loads tokens c0 .. c0 + nt - 1 (1 <= nt <= 64); positions past nt get the identity
-// token (q = k = v = 0, g = 0, beta = 0).
-template <int NW, int NT, bool PER_CHANNEL>
-__device__ __forceinline__ void load_chunk(ChunkRegs<NW, NT>& r, const ChunkArgs& a,
-                                           size_t row0, int c0, int nt, int tid) {
-  using SP = Split<NW, NT>;
-  constexpr int CPT = SP::CPT;
-  typedef typename BfVec<CPT>::type bv;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int I = SP::block(wave), ch0 = SP::channel0(wave, lane), hf = lane >> 5;
-  const bf16* q = static_cast<const bf16*>(a.q);
-  const bf16* k = static_cast<const bf16*>(a.k);
-  const bf16* v = static_cast<const bf16*>(a.v);
-  const bf16 zb = static_cast<bf16>(0.f);
+// Bounded views of one chain's inputs, and this prep lane's byte offsets within a chunk.
+struct PrepSrc {
+  rsrc_t q, k, g, beta;
+  uint32_t qk_off, g_off, b_off;
+};
+
+template <bool PER_CHANNEL>
+__device__ __forceinline__ PrepSrc prep_src(const ChunkArgs& a, size_t row0, int len, int I,
+                                            int lane) {
+  const int cq = lane & 31, hf = lane >> 5;
+  PrepSrc s;
+  s.q = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, (uint32_t)len * kDK * 2);
+  s.k = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, (uint32_t)len * kDK * 2);
+  s.g = PER_CHANNEL ? make_rsrc(a.g + row0 * kDK, (uint32_t)len * kDK * 4)
+                    : make_rsrc(a.g + row0, (uint32_t)len * 4);
+  s.beta = make_rsrc(a.beta + row0, (uint32_t)len * 4);
+  s.qk_off = ((16 * I + 8 * hf) * kDK + 4 * cq) * 2;
+  s.g_off = PER_CHANNEL ? ((16 * I + 8 * hf) * kDK + 4 * cq) * 4 : (16 * I + 8 * hf) * 4;
+  s.b_off = (16 * I + (lane & 15)) * 4;
+  return s;
+}
+
+// Loads block I of the 64 tokens starting at c0 (rows past the chain read as zero).
+template <bool PER_CHANNEL>
+__device__ __forceinline__ void load_block(BlockRegs& r, const PrepSrc& s, int c0) {
+  const uint32_t qk = s.qk_off + (uint32_t)c0 * kDK * 2;
+  const uint32_t go = s.g_off + (uint32_t)c0 * (PER_CHANNEL ? kDK * 4 : 4);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    r.q[u] = ld_b64(s.q, qk + u * kDK * 2);
+    r.k[u] = ld_b64(s.k, qk + u * kDK * 2);
+    if (PER_CHANNEL) {
+      r.g[u] = ld_b128(s.g, go + u * kDK * 4);
+    } else {
+      const float gg = ld_b32(s.g, go + u * 4);
+      r.g[u] = f32x4{gg, gg, gg, gg};
+    }
+  }
+  r.beta = ld_b32(s.beta, s.b_off + (uint32_t)c0 * 4);
+}
+
+// Decay products of block I and its bf16 operands, written to LDS by one wavefront:
+// alpha = exp(g); P_t = exp(G_t - G_0) is the inclusive prefix product of alpha, E_t =
+// exp(G_16 - G_t) the product after t, tot = exp(G_16 - G_0), and k / P_t = k E_t / tot.
+// A lane holds 8 tokens of one half block; the halves exchange their products.
+__device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const BlockRegs& r,
+                                           int I, int lane) {
+  const int cq = lane & 31, hf = lane >> 5;
+  f32x4 al[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[u][j] = __expf(r.g[u][j]);
+  f32x4 half = al[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) half[j] *= al[u][j];
+  f32x4 tot, rtot, run, rs;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float other = __shfl_xor(half[j], 32, 64);  // the other half block's product
+    tot[j] = half[j] * other;
+    rtot[j] = __builtin_amdgcn_rcpf(tot[j]);
+    run[j] = hf ? other : 1.f;  // prefix entering this half
+    rs[j] = hf ? 1.f : other;   // product after this half
+  }
+  if (hf == 0) *reinterpret_cast<f32x4*>(&st.tot[I][4 * cq]) = tot;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int t = 16 * I + 8 * hf + u;
-    const size_t row = row0 + c0 + t;
-    if (t < nt) {
-      r.q[u] = *reinterpret_cast<const bv*>(q + row * kDK + ch0);
-      r.k[u] = *reinterpret_cast<const bv*>(k + row * kDK + ch0);
-      if (PER_CHANNEL) {
-        ld_f32<CPT>(a.g + row * kDK + ch0, r.g[u]);
-      } else {
-        const float gg = a.g[row];
+    f32x4 qr, kr;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) r.g[u][j] = gg;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        r.q[u][j] = zb;
-        r.k[u][j] = zb;
-        r.g[u][j] = 0.f;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
-    const int seg = tid + SP::kThreads * i;
-    const int t = seg & 63, c8 = seg >> 6;
-    if (t < nt) {
-      r.v[i] = *reinterpret_cast<const bf16x8*>(v + (row0 + c0 + t) * SP::DV + 8 * c8);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) r.v[i][j] = zb;
-    }
-  }
-  const int tb = tid & 63;
-  r.beta = tb < nt ? a.beta[row0 + c0 + tb] : 0.f;
-}
-
-// The bf16 operands of one thread's share of the 64 tokens, ready to be written to LDS:
-// q P, k P, k / P per token (CPT channels), k E per channel (8 tokens), the decay over
-// the block, and the staged v and beta.
-template <int NW, int NT>
-struct Prepped {
-  typename BfVec<Split<NW>::CPT>::type qr[8], kr[8], kd[8];
-  bf16x8 kc[Split<NW>::CPT];
-  float tot[Split<NW>::CPT];
-  bf16x8 v[2 * NT];
-  float beta;
-};
-
-// Decay products inside the thread's block (tokens 8 hf + u, channels ch0 + j):
-// P = exp(G_t - G_0) (prefix), E = exp(G_16 - G_t) (suffix after t), tot = P * E.
-template <int NW, int NT>
-__device__ __forceinline__ void prep(Prepped<NW, NT>& o, const ChunkRegs<NW, NT>& c, int hf) {
-  constexpr int CPT = Split<NW>::CPT;
-  float P[8][CPT], E[8][CPT], al[8][CPT], run[CPT], rs[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) run[j] = rs[j] = 1.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      al[u][j] = __expf(c.g[u][j]);
+    for (int j = 0; j < 4; ++j) {
       run[j] *= al[u][j];
-      P[u][j] = run[j];
+      qr[j] = static_cast<float>(r.q[u][j]) * run[j];
+      kr[j] = static_cast<float>(r.k[u][j]) * run[j];
     }
+    *reinterpret_cast<bf16x4*>(&st.qr[t][4 * cq]) = pack4(qr);
+    *reinterpret_cast<bf16x4*>(&st.kr[t][4 * cq]) = pack4(kr);
   }
 #pragma unroll
-  for (int u = 7; u >= 0; --u) {
+  for (int h4 = 1; h4 >= 0; --h4) {
+    float kcv[4][4];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      E[u][j] = rs[j];
-      rs[j] *= al[u][j];
+    for (int uu = 3; uu >= 0; --uu) {
+      const int u = 4 * h4 + uu;
+      const int t = 16 * I + 8 * hf + u;
+      f32x4 kdv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kcv[j][uu] = static_cast<float>(r.k[u][j]) * rs[j];
+        kdv[j] = kcv[j][uu] * rtot[j];
+        rs[j] *= al[u][j];
+      }
+      *reinterpret_cast<bf16x4*>(&kd[t][4 * cq]) = pack4(kdv);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<bf16x4*>(&st.kcT[4 * cq + j][16 * I + 8 * hf + 4 * h4]) =
+          pack4(kcv[j][0], kcv[j][1], kcv[j][2], kcv[j][3]);
   }
-  float other[CPT], rtot[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    other[j] = __shfl_xor(run[j], 32, 64);  // the other half block's product
-    o.tot[j] = run[j] * other[j];
-    rtot[j] = __builtin_amdgcn_rcpf(o.tot[j]);
-  }
-  float kcv[8][CPT];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    float qr[CPT], kr[CPT], kd[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      // upper half: prefix times the lower half's product; lower half: suffix times
-      // the upper half's product
-      const float pp = hf ? P[u][j] * other[j] : P[u][j];
-      const float ee = hf ? E[u][j] : E[u][j] * other[j];
-      const float qv = static_cast<float>(c.q[u][j]);
-      const float kv = static_cast<float>(c.k[u][j]);
-      qr[j] = qv * pp;
-      kr[j] = kv * pp;
-      kcv[u][j] = kv * ee;
-      kd[j] = kcv[u][j] * rtot[j];
-    }
-    o.qr[u] = pack_bf<CPT>(qr);
-    o.kr[u] = pack_bf<CPT>(kr);
-    o.kd[u] = pack_bf<CPT>(kd);
-  }
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const f32x4 lo = {kcv[0][j], kcv[1][j], kcv[2][j], kcv[3][j]};
-    const f32x4 hi = {kcv[4][j], kcv[5][j], kcv[6][j], kcv[7][j]};
-    o.kc[j] = cat8(pack4(lo), pack4(hi));
-  }
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) o.v[i] = c.v[i];
-  o.beta = c.beta;
-}
-
-template <int NW, int NT>
-__device__ __forceinline__ void write_prepped(Smem& sm, const Prepped<NW, NT>& o, int tid) {
-  using SP = Split<NW, NT>;
-  constexpr int CPT = SP::CPT;
-  typedef typename BfVec<CPT>::type bv;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int I = SP::block(wave), ch0 = SP::channel0(wave, lane), hf = lane >> 5;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int t = 16 * I + 8 * hf + u;
-    *reinterpret_cast<bv*>(&sm.qr[t][ch0]) = o.qr[u];
-    *reinterpret_cast<bv*>(&sm.kr[t][ch0]) = o.kr[u];
-    *reinterpret_cast<bv*>(&sm.kd[t][ch0]) = o.kd[u];
-  }
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    *reinterpret_cast<bf16x8*>(&sm.kcT[ch0 + j][16 * I + 8 * hf]) = o.kc[j];
-    if (hf == 0) sm.tot[I][ch0 + j] = o.tot[j];
-  }
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
-    const int seg = tid + SP::kThreads * i;
-    const int t = seg & 63, c8 = seg >> 6;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sm.vT[8 * c8 + j][t] = o.v[i][j];
-  }
-  if (tid < kC) sm.beta[tid] = o.beta;
+  if (lane < 16) st.beta[16 * I + lane] = r.beta;
 }
 
 // 16 x 16 fp32 products on the matrix cores with X in row layout (lane 16p + r holds
@@ -344,14 +294,15 @@ __device__ __forceinline__ f32x4 mm_row(const f32x4& xr, const f32x4& yc) {
 // strictly lower. N is nilpotent (N^16 = 0), so (I + N)^-1 = (I - N)(I + N^2)(I + N^4)
 // (I + N^8) exactly; the factors are polynomials in N and commute, which lets every
 // product take its left factor in row layout and its right factor in column layout.
-__device__ __forceinline__ void block_tiles(Smem& sm, int I, int rr, int p) {
+__device__ __forceinline__ void block_tiles(Stage& st, const bf16 (*kd)[kLDK], int I, int rr,
+                                            int p) {
   bf16x8 bq[4], bk[4], bc[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int ch = 32 * ks + 8 * p;
-    bq[ks] = *reinterpret_cast<const bf16x8*>(&sm.qr[16 * I + rr][ch]);
-    bk[ks] = *reinterpret_cast<const bf16x8*>(&sm.kr[16 * I + rr][ch]);
-    bc[ks] = *reinterpret_cast<const bf16x8*>(&sm.kd[16 * I + rr][ch]);
+    bq[ks] = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][ch]);
+    bk[ks] = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][ch]);
+    bc[ks] = *reinterpret_cast<const bf16x8*>(&kd[16 * I + rr][ch]);
   }
   f32x4 accq = zero4(), acck = zero4(), acct = zero4();
 #pragma unroll
@@ -361,12 +312,12 @@ __device__ __forceinline__ void block_tiles(Smem& sm, int I, int rr, int p) {
     acct = mfma32(bc[ks], bk[ks], acct);   // A_kk[j][i]: lane holds A_kk[rr][4p + e]
   }
   f32x4 nc, nr;
-  const float brr = sm.beta[16 * I + rr];
+  const float brr = st.beta[16 * I + rr];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 4 * p + e;
-    sm.aqk[I][i][rr] = static_cast<bf16>(rr <= i ? accq[e] : 0.f);
-    nc[e] = rr < i ? sm.beta[16 * I + i] * acck[e] : 0.f;   // N[i][rr]
+    st.aqk[I][i][rr] = static_cast<bf16>(rr <= i ? accq[e] : 0.f);
+    nc[e] = rr < i ? st.beta[16 * I + i] * acck[e] : 0.f;   // N[i][rr]
     nr[e] = i < rr ? brr * acct[e] : 0.f;                    // N[rr][i]
   }
   const f32x4 n2c = mm_col(nr, nc), n2r = mm_row(nr, nc);
@@ -382,20 +333,43 @@ __device__ __forceinline__ void block_tiles(Smem& sm, int I, int rr, int p) {
   for (int e = 0; e < 4; ++e) y2[e] = y1[e] + t1[e];
   const f32x4 t2 = mm_col(n8r, y2);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) sm.tdiag[I][4 * p + e][rr] = static_cast<bf16>(y2[e] + t2[e]);
+  for (int e = 0; e < 4; ++e) st.tdiag[I][4 * p + e][rr] = static_cast<bf16>(y2[e] + t2[e]);
 }
 
-template <int NW, int NT, bool PER_CHANNEL>
-__global__ __launch_bounds__(64 * NW) void chunk_mfma_kernel(ChunkArgs a) {
-  using SP = Split<NW, NT>;
-  constexpr int DV = SP::DV;
+// Values of one state column for the 16 tokens of block I, in the accumulator layout
+// (token 16 I + 4 p + e), kept as raw bf16 so that nothing waits for the loads before the
+// step that uses them. off is the byte offset of token 16 I + 4 p in this column.
+template <int DV>
+__device__ __forceinline__ void load_values(bf16 (&vv)[4], rsrc_t v, uint32_t off) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = ld_b16(v, off + e * DV * 2);
+}
+
+// Stores the outputs of chunk `step` that this state wavefront staged in LDS (its 16 NT
+// columns of 64 token rows) as 16-byte row pieces; rows past the chain are dropped.
+template <int NT, int DV>
+__device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int step, int j,
+                                              int lane) {
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) {
+    const int idx = lane + 64 * i;
+    const int t = idx / (2 * NT);
+    const int c0 = 16 * NT * j + 8 * (idx % (2 * NT));
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(&sm.ost[t][c0]);
+    st_b128(odst, (uint32_t)((step * kC + t) * DV + c0) * 2, x);
+  }
+}
+
+template <int NS, int NT, bool PER_CHANNEL>
+__global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(ChunkArgs a) {
+  constexpr int DV = 16 * NS * NT;
   __shared__ __align__(16) Smem sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int hf = lane >> 5;                 // decay phase: token half of the block
-  const int rr = lane & 15, p = lane >> 4;  // matrix-core phases
+  const int rr = lane & 15, p = lane >> 4;
+  const bool prep_wave = wave < kPrepWaves;
 
   const int chain = blockIdx.x;
   const int n = chain / a.H;
@@ -403,138 +377,159 @@ __global__ __launch_bounds__(64 * NW) void chunk_mfma_kernel(ChunkArgs a) {
   const TokenRange tr = token_range(a.cu, n, a.T);
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
   const size_t state_off = ((size_t)n * a.H + h) * kDK * DV;
+  const int nsteps = (tr.len + kC - 1) / kC;
 
-  // state S[channel][column] of this wavefront's NT column tiles, accumulator layout:
-  // S_acc[j][m][e] = S[16 m + 4 p + e][16 (NT wave + j) + rr]
-  f32x4 S_acc[NT][8];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int col = 16 * (NT * wave + j) + rr;
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S_acc[j][m][e] =
-            a.s0 ? a.s0[state_off + (size_t)(16 * m + 4 * p + e) * DV + col] : 0.f;
-  }
-
-  ChunkRegs<NW, NT> cur;
-  if (tr.len > 0) load_chunk<NW, NT, PER_CHANNEL>(cur, a, row0, 0, min(kC, tr.len), tid);
-
-  for (int c0 = 0; c0 < tr.len; c0 += kC) {
-    const int nt = min(kC, tr.len - c0);
-    lds_barrier();  // the previous tokens' state steps are done with LDS
-    {
-      Prepped<NW, NT> pre;
-      prep<NW, NT>(pre, cur, hf);
-      write_prepped<NW, NT>(sm, pre, tid);
+  if (prep_wave) {
+    // ---------------- prep wavefront: block I of every 64 tokens
+    const int I = wave;
+    const PrepSrc src = prep_src<PER_CHANNEL>(a, row0, tr.len, I, lane);
+    BlockRegs r;
+    if (nsteps > 0) {
+      load_block<PER_CHANNEL>(r, src, 0);
+      prep_block(sm.st[0], sm.kd, r, I, lane);
+      wave_lds_fence();
+      block_tiles(sm.st[0], sm.kd, I, rr, p);
+      if (nsteps > 1) load_block<PER_CHANNEL>(r, src, kC);
     }
     lds_barrier();
-
-    // ---- per block: A_qk and A_kk tiles, and the inverse of (I + Diag(beta) A_kk)
-    if (wave < 4) block_tiles(sm, wave, rr, p);
-    lds_barrier();
-
-    // every input of these tokens is in LDS now: fetch the next ones while computing
-    const bool has_next = c0 + kC < tr.len;
-    if (has_next)
-      load_chunk<NW, NT, PER_CHANNEL>(cur, a, row0, c0 + kC, min(kC, tr.len - c0 - kC), tid);
-
-    // ---- the four blocks' state steps for this wavefront's column tiles
-    bf16* o = static_cast<bf16*>(a.o);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      // B operands of S (bf16), contraction permuted over channels
-      bf16x8 sb[NT][4];
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          sb[j][ks] = cat8(pack4(S_acc[j][2 * ks]), pack4(S_acc[j][2 * ks + 1]));
-      // X = (K P) S and O = (Q P) S
-      f32x4 X[NT], Oc[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) X[j] = Oc[j] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16* kr_ = &sm.kr[16 * I + rr][32 * ks + 4 * p];
-        const bf16* qr_ = &sm.qr[16 * I + rr][32 * ks + 4 * p];
-        const bf16x8 ak = cat8(*reinterpret_cast<const bf16x4*>(kr_),
-                               *reinterpret_cast<const bf16x4*>(kr_ + 16));
-        const bf16x8 aq = cat8(*reinterpret_cast<const bf16x4*>(qr_),
-                               *reinterpret_cast<const bf16x4*>(qr_ + 16));
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          X[j] = mfma32(ak, sb[j][ks], X[j]);
-          Oc[j] = mfma32(aq, sb[j][ks], Oc[j]);
-        }
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + 1 < nsteps) {
+        Stage& st = sm.st[(s + 1) & 1];
+        prep_block(st, sm.kd, r, I, lane);
+        wave_lds_fence();
+        block_tiles(st, sm.kd, I, rr, p);
+        if (s + 2 < nsteps) load_block<PER_CHANNEL>(r, src, (s + 2) * kC);
       }
-      // V' = Tm Diag(beta) (V - X)
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * I + 4 * p]);
-      const bf16x4 tI = *reinterpret_cast<const bf16x4*>(&sm.tdiag[I][rr][4 * p]);
-      const bf16x4 aI = *reinterpret_cast<const bf16x4*>(&sm.aqk[I][rr][4 * p]);
-      bf16x4 vp[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int col = 16 * (NT * wave + j) + rr;
-        const bf16x4 vv = *reinterpret_cast<const bf16x4*>(&sm.vT[col][16 * I + 4 * p]);
-        f32x4 R;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) R[e] = bt[e] * (static_cast<float>(vv[e]) - X[j][e]);
-        vp[j] = pack4(mfma16(tI, pack4(R), zero4()));
-        // O += A_qk V'
-        const bf16x4 ob = pack4(mfma16(aI, vp[j], Oc[j]));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * I + 4 * p + e;
-          if (t < nt) o[(row0 + c0 + t) * DV + col] = ob[e];
-        }
-      }
-      // S <- Diag(tot) S + (K E)^T V'
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const f32x4 dc = *reinterpret_cast<const f32x4*>(&sm.tot[I][16 * m + 4 * p]);
-        const bf16x4 ac = *reinterpret_cast<const bf16x4*>(&sm.kcT[16 * m + rr][16 * I + 4 * p]);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          f32x4 s_ = S_acc[j][m];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s_[e] *= dc[e];
-          S_acc[j][m] = mfma16(ac, vp[j], s_);
-        }
-      }
+      lds_barrier();
     }
-  }
-
-  if (a.sT) {
+  } else {
+    // ---------------- state wavefront: value columns 16 (NT j + c) + rr, c < NT
+    const int j = wave - kPrepWaves;
+    const rsrc_t vsrc =
+        make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, (uint32_t)tr.len * DV * 2);
+    const rsrc_t odst = make_rsrc(static_cast<bf16*>(a.o) + row0 * DV, (uint32_t)tr.len * DV * 2);
+    int col[NT];
+    uint32_t voff[NT];  // byte offset of (token 4 p, column col) within a 64-token chunk
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int col = 16 * (NT * wave + j) + rr;
+    for (int c = 0; c < NT; ++c) {
+      col[c] = 16 * (NT * j + c) + rr;
+      voff[c] = (uint32_t)(4 * p * DV + col[c]) * 2;
+    }
+    // S_acc[c][m][e] = S[32 (m / 2) + 8 p + 4 (m % 2) + e][col[c]]
+    f32x4 S_acc[NT][8];
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a.sT[state_off + (size_t)(16 * m + 4 * p + e) * DV + col] = S_acc[j][m][e];
+        for (int e = 0; e < 4; ++e) {
+          const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
+          S_acc[c][m][e] = a.s0 ? a.s0[state_off + (size_t)ch * DV + col[c]] : 0.f;
+        }
+    bf16 vv[NT][4][4];
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int I = 0; I < 4; ++I) load_values<DV>(vv[c][I], vsrc, voff[c] + I * 16 * DV * 2);
+    // the initial state must be in registers before the loop, or the loop would wait
+    // for these loads on every pass
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    lds_barrier();
+    for (int s = 0; s < nsteps; ++s) {
+      const Stage& st = sm.st[s & 1];
+      const uint32_t cbyte = (uint32_t)s * kC * DV * 2;
+      // the barrier ending the previous step waited for this wavefront's staging writes
+      if (s > 0) flush_outputs<NT, DV>(sm, odst, s - 1, j, lane);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        // X = (K P) S and O = (Q P) S, S as the B operand (bf16)
+        f32x4 X[NT], Oc[NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) X[c] = Oc[c] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][32 * ks + 8 * p]);
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const bf16x8 sb = cat8(pack4(S_acc[c][2 * ks]), pack4(S_acc[c][2 * ks + 1]));
+            X[c] = mfma32(ak, sb, X[c]);
+            Oc[c] = mfma32(aq, sb, Oc[c]);
+          }
+        }
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&st.beta[16 * I + 4 * p]);
+        const bf16x4 tI = *reinterpret_cast<const bf16x4*>(&st.tdiag[I][rr][4 * p]);
+        const bf16x4 aI = *reinterpret_cast<const bf16x4*>(&st.aqk[I][rr][4 * p]);
+        bf16x4 vp[NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          // V' = Tm Diag(beta) (V - X);  O += A_qk V'
+          f32x4 R;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[e] = bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
+          const uint32_t boff = voff[c] + cbyte + I * 16 * DV * 2;
+          load_values<DV>(vv[c][I], vsrc, boff + kC * DV * 2);  // the next 64 tokens
+          vp[c] = pack4(mfma16(tI, pack4(R), zero4()));
+          const bf16x4 ob = pack4(mfma16(aI, vp[c], Oc[c]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.ost[16 * I + 4 * p + e][col[c]] = ob[e];
+        }
+        // S <- Diag(tot) S + (K E)^T V'
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int s2 = m >> 1, h2 = m & 1;
+          // tot of this lane's rows: one float per lane, spread over its quad
+          const float d1 = st.tot[I][32 * s2 + 8 * p + 4 * h2 + (rr & 3)];
+          const int cha = 32 * s2 + 8 * (rr >> 2) + 4 * h2 + (rr & 3);  // channel of A row rr
+          const bf16x4 ac = *reinterpret_cast<const bf16x4*>(&st.kcT[cha][16 * I + 4 * p]);
+          const f32x4 dc = {quad_bcast<0>(d1), quad_bcast<1>(d1), quad_bcast<2>(d1),
+                            quad_bcast<3>(d1)};
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            f32x4 s_ = S_acc[c][m];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_[e] *= dc[e];
+            S_acc[c][m] = mfma16(ac, vp[c], s_);
+          }
+        }
+      }
+      lds_barrier();
+    }
+    if (nsteps > 0) flush_outputs<NT, DV>(sm, odst, nsteps - 1, j, lane);
+    if (a.sT) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
+            a.sT[state_off + (size_t)ch * DV + col[c]] = S_acc[c][m][e];
+          }
     }
   }
 }
 
-template <int NW, int NT, bool PER_CHANNEL>
-hipError_t launch_nw(const ChunkArgs& a, hipStream_t stream) {
-  chunk_mfma_kernel<NW, NT, PER_CHANNEL><<<dim3(a.N * a.H), dim3(64 * NW), 0, stream>>>(a);
+template <int NS, int NT, bool PER_CHANNEL>
+hipError_t launch_ns(const ChunkArgs& a, hipStream_t stream) {
+  chunk_mfma_kernel<NS, NT, PER_CHANNEL>
+      <<<dim3(a.N * a.H), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool chunk_mfma_supports(int dk, int dv) { return dk == kDK && (dv == 64 || dv == 128); }
+// Buffer descriptors address at most 2^31 bytes: a chain's g rows (T x dk fp32) must fit.
+bool chunk_mfma_supports(int dk, int dv, int T) {
+  return dk == kDK && (dv == 64 || dv == 128) && (long long)T * kDK * 4 < (1ll << 31);
+}
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool per_channel, hipStream_t stream) {
-  if (!chunk_mfma_supports(a.dk, a.dv)) return hipErrorInvalidValue;
+  if (!chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
+  // four state wavefronts: two 16-column tiles each for dv = 128, one for dv = 64
   if (a.dv == 128)
-    return per_channel ? launch_nw<KDA_NW128, 8 / KDA_NW128, true>(a, stream)
-                       : launch_nw<KDA_NW128, 8 / KDA_NW128, false>(a, stream);
-  return per_channel ? launch_nw<4, 1, true>(a, stream) : launch_nw<4, 1, false>(a, stream);
+    return per_channel ? launch_ns<4, 2, true>(a, stream) : launch_ns<4, 2, false>(a, stream);
+  return per_channel ? launch_ns<4, 1, true>(a, stream) : launch_ns<4, 1, false>(a, stream);
 }
 
 }  // namespace kda

@@ -44,6 +44,6 @@ hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, bool pe
                          hipStream_t stream);
 hipError_t launch_chunk_f32(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool per_channel, hipStream_t stream);
-bool chunk_mfma_supports(int dk, int dv);
+bool chunk_mfma_supports(int dk, int dv, int T);
 
 }  // namespace kda
