@@ -58,6 +58,10 @@ constexpr int kLDK = kDK + 8;  // padded LDS row (bf16) of [token][channel] tile
 constexpr int kLDT = kC + 8;   // padded LDS row (bf16) of [channel][token] tiles
 constexpr int kPrepWaves = 4;  // one per 16-token block
 
+#ifndef KDA_STATE_PRIO
+#define KDA_STATE_PRIO 3
+#endif
+
 
 // Operands of 64 tokens, written by the prep wavefronts and read by the state wavefronts.
 struct Stage {
@@ -107,7 +111,18 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x4 pack4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Round to bf16 pairwise (one v_cvt_pk_bf16_f32 per pair; converting the 4-vector
+// directly is split into single-element conversions by the compiler).
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ bf16x4 pack4(f32x4 v) {
+  return __builtin_bit_cast(bf16x4, (u32x2){pack2(v[0], v[1]), pack2(v[2], v[3])});
+}
 __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
   return pack4(f32x4{a, b, c, d});
 }
@@ -404,6 +419,9 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     }
   } else {
     // ---------------- state wavefront: value columns 16 (NT j + c) + rr, c < NT
+    // The state steps are the sequential critical path; the prep wavefronts sharing a
+    // SIMD have slack, so the state wavefronts take issue priority.
+    __builtin_amdgcn_s_setprio(KDA_STATE_PRIO);
     const int j = wave - kPrepWaves;
     const rsrc_t vsrc =
         make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, (uint32_t)tr.len * DV * 2);
@@ -442,10 +460,12 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
       if (s > 0) flush_outputs<NT, DV>(sm, odst, s - 1, j, lane);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        // X = (K P) S and O = (Q P) S, S as the B operand (bf16)
-        f32x4 X[NT], Oc[NT];
+        // X = (K P) S, S as the B operand (bf16), and O^T = S^T (Q P)^T, S^T as the A
+        // operand (the same registers): O^T leaves each lane with four consecutive
+        // columns of one token
+        f32x4 X[NT], Ot[NT];
 #pragma unroll
-        for (int c = 0; c < NT; ++c) X[c] = Oc[c] = zero4();
+        for (int c = 0; c < NT; ++c) X[c] = Ot[c] = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][32 * ks + 8 * p]);
@@ -454,25 +474,34 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
           for (int c = 0; c < NT; ++c) {
             const bf16x8 sb = cat8(pack4(S_acc[c][2 * ks]), pack4(S_acc[c][2 * ks + 1]));
             X[c] = mfma32(ak, sb, X[c]);
-            Oc[c] = mfma32(aq, sb, Oc[c]);
+            Ot[c] = mfma32(sb, aq, Ot[c]);
           }
         }
         const f32x4 bt = *reinterpret_cast<const f32x4*>(&st.beta[16 * I + 4 * p]);
         const bf16x4 tI = *reinterpret_cast<const bf16x4*>(&st.tdiag[I][rr][4 * p]);
         const bf16x4 aI = *reinterpret_cast<const bf16x4*>(&st.aqk[I][rr][4 * p]);
+        // V' = Tm Diag(beta) (V - X)
         bf16x4 vp[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-          // V' = Tm Diag(beta) (V - X);  O += A_qk V'
           f32x4 R;
 #pragma unroll
           for (int e = 0; e < 4; ++e) R[e] = bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
-          const uint32_t boff = voff[c] + cbyte + I * 16 * DV * 2;
-          load_values<DV>(vv[c][I], vsrc, boff + kC * DV * 2);  // the next 64 tokens
-          vp[c] = pack4(mfma16(tI, pack4(R), zero4()));
-          const bf16x4 ob = pack4(mfma16(aI, vp[c], Oc[c]));
+          vp[c] = pack4(R);
+          // the next 64 tokens' values of this block
+          load_values<DV>(vv[c][I], vsrc, voff[c] + cbyte + (I * 16 + kC) * DV * 2);
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sm.ost[16 * I + 4 * p + e][col[c]] = ob[e];
+        for (int c = 0; c < NT; ++c) vp[c] = pack4(mfma16(tI, vp[c], zero4()));
+        // O^T += V'^T A_qk^T, staged as bf16 token rows. The product starts from zero
+        // and O^T is added on the vector ALU: accumulating a 16x16x16 product onto the
+        // result of a 16x16x32 product still in flight delays its completion beyond the
+        // wait states counted from its issue, and the conversion below then read stale
+        // registers.
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const bf16x4 ob = pack4(Ot[c] + mfma16(vp[c], aI, zero4()));
+          *reinterpret_cast<bf16x4*>(&sm.ost[16 * I + rr][16 * (NT * j + c) + 4 * p]) = ob;
         }
         // S <- Diag(tot) S + (K E)^T V'
 #pragma unroll
