@@ -118,13 +118,14 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
               o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              schedule: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked forward over [B, H, T, d] head-major tensors (see ``kda_chunk_fwd``).
 
     g: float32 [B, H, T, dk] (per key channel, KDA) or [B, H, T] (per head, Gated
     DeltaNet); beta: float32 [B, H, T]; initial_state: float32 [N, H, dk, dv] or None;
     cu_seqlens: int32 [N + 1] on the GPU (B must be 1) or None. ``o`` and ``final_state``
     may be given to reuse buffers; ``final_state`` may be ``initial_state``.
+    ``schedule=False`` passes no workspace (one workgroup per chain, no column split).
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -154,7 +155,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, dev)
     num_seqs = 0 if cu_seqlens is None else N
-    ws_bytes = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt)
+    ws_bytes = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt) if schedule else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                        _ptr(final_state), _ptr(o), _ptr(cu_seqlens), num_seqs, B, H, T, dk,

@@ -24,8 +24,26 @@ const char* kda_status_string(kda_status s) {
 
 size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
                                     kda_dtype dt) {
-  (void)B; (void)H; (void)T; (void)dk; (void)dv; (void)num_seqs; (void)dt;
-  return 0;  // the fused kernels keep every intermediate on chip
+  // only the matrix-core path uses a workspace: its work list (every intermediate of the
+  // method stays on chip)
+  if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return 0;
+  if (dt != KDA_BF16 || !kda::chunk_mfma_supports(dk, dv, T)) return 0;
+  // equal-length batches are scheduled on the host: only packed sequences need one
+  if (num_seqs == 0 || (long long)num_seqs * H > (1ll << 24)) return 0;
+  return kda::chunk_plan_bytes(num_seqs, H, dv);
+}
+
+// Compute units of the current device, cached per device (sizes the chunk schedule).
+static int device_compute_units() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -40,7 +58,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
   if (!cu_seqlens && num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARG;
   const size_t need = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt);
-  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_INVALID_ARG;
+  // workspace_bytes == 0: run without the schedule; otherwise it must hold the schedule
+  if (workspace_bytes > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_INVALID_ARG;
+  const bool scheduled = need > 0 && workspace_bytes > 0;
   if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
   const long long N = cu_seqlens ? num_seqs : B;
   if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
@@ -49,6 +69,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.s0 = initial_state; a.sT = final_state; a.o = o; a.cu = cu_seqlens;
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
+  a.plan = scheduled ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.cus = device_compute_units();
+  a.split_all = 0;
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
   if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T))

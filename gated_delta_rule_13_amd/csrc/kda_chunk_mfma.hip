@@ -360,18 +360,142 @@ __device__ __forceinline__ void load_values(bf16 (&vv)[4], rsrc_t v, uint32_t of
   for (int e = 0; e < 4; ++e) vv[e] = ld_b16(v, off + e * DV * 2);
 }
 
-// Stores the outputs of chunk `step` that this state wavefront staged in LDS (its 16 NT
-// columns of 64 token rows) as 16-byte row pieces; rows past the chain are dropped.
-template <int NT, int DV>
-__device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int step, int j,
-                                              int lane) {
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
+// Stores the outputs of chunk `step` that this state wavefront staged in LDS (its 16 nt
+// columns from cbase, 64 token rows) as 16-byte row pieces; rows past the chain are dropped.
+template <int DV>
+__device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int step, int cbase,
+                                              int nt, int lane) {
+  for (int i = 0; i < 2 * nt; ++i) {
     const int idx = lane + 64 * i;
-    const int t = idx / (2 * NT);
-    const int c0 = 16 * NT * j + 8 * (idx % (2 * NT));
+    const int t = idx / (2 * nt);
+    const int c0 = cbase + 8 * (idx % (2 * nt));
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(&sm.ost[t][c0]);
     st_b128(odst, (uint32_t)((step * kC + t) * DV + c0) * 2, x);
+  }
+}
+
+// State wavefront: NT 16-column tiles of S starting at column cbase, for the whole chain.
+// Whole chains use the kernel's tile count, half items half of it; each is its own
+// straight-line instantiation (a tile count chosen at run time inside the loops would let
+// branches remove instructions that the wait states after the matrix-core products were
+// counted on).
+template <int NT, int DV>
+__device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const TokenRange& tr,
+                                           size_t row0, size_t state_off, int nsteps, int cbase,
+                                           int lane, int rr, int p) {
+  const rsrc_t vsrc =
+      make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, (uint32_t)tr.len * DV * 2);
+  const rsrc_t odst = make_rsrc(static_cast<bf16*>(a.o) + row0 * DV, (uint32_t)tr.len * DV * 2);
+  int col[NT];
+  uint32_t voff[NT];  // byte offset of (token 4 p, column col) within a 64-token chunk
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    col[c] = cbase + 16 * c + rr;
+    voff[c] = (uint32_t)(4 * p * DV + col[c]) * 2;
+  }
+  // S_acc[c][m][e] = S[32 (m / 2) + 8 p + 4 (m % 2) + e][col[c]]
+  f32x4 S_acc[NT][8];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
+        S_acc[c][m][e] = a.s0 ? a.s0[state_off + (size_t)ch * DV + col[c]] : 0.f;
+      }
+  bf16 vv[NT][4][4];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      load_values<DV>(vv[c][I], vsrc, voff[c] + I * 16 * DV * 2);
+  // the initial state must be in registers before the loop, or the loop would wait
+  // for these loads on every pass
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  lds_barrier();
+  for (int s = 0; s < nsteps; ++s) {
+    const Stage& st = sm.st[s & 1];
+    const uint32_t cbyte = (uint32_t)s * kC * DV * 2;
+    // the barrier ending the previous step waited for this wavefront's staging writes
+    if (s > 0) flush_outputs<DV>(sm, odst, s - 1, cbase, NT, lane);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      // X = (K P) S, S as the B operand (bf16), and O^T = S^T (Q P)^T, S^T as the A
+      // operand (the same registers): O^T leaves each lane with four consecutive
+      // columns of one token
+      f32x4 X[NT], Ot[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) X[c] = Ot[c] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][32 * ks + 8 * p]);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const bf16x8 sb = cat8(pack4(S_acc[c][2 * ks]), pack4(S_acc[c][2 * ks + 1]));
+          X[c] = mfma32(ak, sb, X[c]);
+          Ot[c] = mfma32(sb, aq, Ot[c]);
+        }
+      }
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&st.beta[16 * I + 4 * p]);
+      const bf16x4 tI = *reinterpret_cast<const bf16x4*>(&st.tdiag[I][rr][4 * p]);
+      const bf16x4 aI = *reinterpret_cast<const bf16x4*>(&st.aqk[I][rr][4 * p]);
+      // V' = Tm Diag(beta) (V - X)
+      bf16x4 vp[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        f32x4 R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[e] = bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
+        vp[c] = pack4(R);
+        // the next 64 tokens' values of this block
+        load_values<DV>(vv[c][I], vsrc, voff[c] + cbyte + (I * 16 + kC) * DV * 2);
+      }
+#pragma unroll
+      for (int c = 0; c < NT; ++c) vp[c] = pack4(mfma16(tI, vp[c], zero4()));
+      // O^T += V'^T A_qk^T, staged as bf16 token rows. The product starts from zero
+      // and O^T is added on the vector ALU: accumulating a 16x16x16 product onto the
+      // result of a 16x16x32 product still in flight delays its completion beyond the
+      // wait states counted from its issue, and the conversion below then read stale
+      // registers.
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        const bf16x4 ob = pack4(Ot[c] + mfma16(vp[c], aI, zero4()));
+        *reinterpret_cast<bf16x4*>(&sm.ost[16 * I + rr][cbase + 16 * c + 4 * p]) = ob;
+      }
+      // S <- Diag(tot) S + (K E)^T V'
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int s2 = m >> 1, h2 = m & 1;
+        // tot of this lane's rows: one float per lane, spread over its quad
+        const float d1 = st.tot[I][32 * s2 + 8 * p + 4 * h2 + (rr & 3)];
+        const int cha = 32 * s2 + 8 * (rr >> 2) + 4 * h2 + (rr & 3);  // channel of A row rr
+        const bf16x4 ac = *reinterpret_cast<const bf16x4*>(&st.kcT[cha][16 * I + 4 * p]);
+        const f32x4 dc = {quad_bcast<0>(d1), quad_bcast<1>(d1), quad_bcast<2>(d1),
+                          quad_bcast<3>(d1)};
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          f32x4 s_ = S_acc[c][m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s_[e] *= dc[e];
+          S_acc[c][m] = mfma16(ac, vp[c], s_);
+        }
+      }
+    }
+    lds_barrier();
+  }
+  if (nsteps > 0) flush_outputs<DV>(sm, odst, nsteps - 1, cbase, NT, lane);
+  if (a.sT) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
+          a.sT[state_off + (size_t)ch * DV + col[c]] = S_acc[c][m][e];
+        }
   }
 }
 
@@ -386,7 +510,17 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
   const int rr = lane & 15, p = lane >> 4;
   const bool prep_wave = wave < kPrepWaves;
 
-  const int chain = blockIdx.x;
+  // work item: a chain, or one half of its value columns
+  int chain = blockIdx.x, part = 0;
+  if (a.plan) {
+    if (blockIdx.x >= a.plan[0]) return;  // the grid is sized for the largest schedule
+    const uint32_t item = a.plan[1 + blockIdx.x];
+    chain = (int)(item >> 2);
+    part = (int)(item & 3);
+  } else if (NT > 1 && a.split_all) {
+    chain = blockIdx.x >> 1;
+    part = 1 + (blockIdx.x & 1);
+  }
   const int n = chain / a.H;
   const int h = chain % a.H;
   const TokenRange tr = token_range(a.cu, n, a.T);
@@ -418,131 +552,117 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
       lds_barrier();
     }
   } else {
-    // ---------------- state wavefront: value columns 16 (NT j + c) + rr, c < NT
+    // ---------------- state wavefront
     // The state steps are the sequential critical path; the prep wavefronts sharing a
     // SIMD have slack, so the state wavefronts take issue priority.
     __builtin_amdgcn_s_setprio(KDA_STATE_PRIO);
     const int j = wave - kPrepWaves;
-    const rsrc_t vsrc =
-        make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, (uint32_t)tr.len * DV * 2);
-    const rsrc_t odst = make_rsrc(static_cast<bf16*>(a.o) + row0 * DV, (uint32_t)tr.len * DV * 2);
-    int col[NT];
-    uint32_t voff[NT];  // byte offset of (token 4 p, column col) within a 64-token chunk
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      col[c] = 16 * (NT * j + c) + rr;
-      voff[c] = (uint32_t)(4 * p * DV + col[c]) * 2;
+    if constexpr (NT > 1) {
+      if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
+        state_role<NT / 2, DV>(sm, a, tr, row0, state_off, nsteps,
+                               (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane, rr, p);
+        return;
+      }
     }
-    // S_acc[c][m][e] = S[32 (m / 2) + 8 p + 4 (m % 2) + e][col[c]]
-    f32x4 S_acc[NT][8];
-#pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
-          S_acc[c][m][e] = a.s0 ? a.s0[state_off + (size_t)ch * DV + col[c]] : 0.f;
-        }
-    bf16 vv[NT][4][4];
-#pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-      for (int I = 0; I < 4; ++I) load_values<DV>(vv[c][I], vsrc, voff[c] + I * 16 * DV * 2);
-    // the initial state must be in registers before the loop, or the loop would wait
-    // for these loads on every pass
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    lds_barrier();
-    for (int s = 0; s < nsteps; ++s) {
-      const Stage& st = sm.st[s & 1];
-      const uint32_t cbyte = (uint32_t)s * kC * DV * 2;
-      // the barrier ending the previous step waited for this wavefront's staging writes
-      if (s > 0) flush_outputs<NT, DV>(sm, odst, s - 1, j, lane);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        // X = (K P) S, S as the B operand (bf16), and O^T = S^T (Q P)^T, S^T as the A
-        // operand (the same registers): O^T leaves each lane with four consecutive
-        // columns of one token
-        f32x4 X[NT], Ot[NT];
-#pragma unroll
-        for (int c = 0; c < NT; ++c) X[c] = Ot[c] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][32 * ks + 8 * p]);
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);
-#pragma unroll
-          for (int c = 0; c < NT; ++c) {
-            const bf16x8 sb = cat8(pack4(S_acc[c][2 * ks]), pack4(S_acc[c][2 * ks + 1]));
-            X[c] = mfma32(ak, sb, X[c]);
-            Ot[c] = mfma32(sb, aq, Ot[c]);
-          }
-        }
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(&st.beta[16 * I + 4 * p]);
-        const bf16x4 tI = *reinterpret_cast<const bf16x4*>(&st.tdiag[I][rr][4 * p]);
-        const bf16x4 aI = *reinterpret_cast<const bf16x4*>(&st.aqk[I][rr][4 * p]);
-        // V' = Tm Diag(beta) (V - X)
-        bf16x4 vp[NT];
-#pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          f32x4 R;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) R[e] = bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
-          vp[c] = pack4(R);
-          // the next 64 tokens' values of this block
-          load_values<DV>(vv[c][I], vsrc, voff[c] + cbyte + (I * 16 + kC) * DV * 2);
-        }
-#pragma unroll
-        for (int c = 0; c < NT; ++c) vp[c] = pack4(mfma16(tI, vp[c], zero4()));
-        // O^T += V'^T A_qk^T, staged as bf16 token rows. The product starts from zero
-        // and O^T is added on the vector ALU: accumulating a 16x16x16 product onto the
-        // result of a 16x16x32 product still in flight delays its completion beyond the
-        // wait states counted from its issue, and the conversion below then read stale
-        // registers.
-#pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const bf16x4 ob = pack4(Ot[c] + mfma16(vp[c], aI, zero4()));
-          *reinterpret_cast<bf16x4*>(&sm.ost[16 * I + rr][16 * (NT * j + c) + 4 * p]) = ob;
-        }
-        // S <- Diag(tot) S + (K E)^T V'
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int s2 = m >> 1, h2 = m & 1;
-          // tot of this lane's rows: one float per lane, spread over its quad
-          const float d1 = st.tot[I][32 * s2 + 8 * p + 4 * h2 + (rr & 3)];
-          const int cha = 32 * s2 + 8 * (rr >> 2) + 4 * h2 + (rr & 3);  // channel of A row rr
-          const bf16x4 ac = *reinterpret_cast<const bf16x4*>(&st.kcT[cha][16 * I + 4 * p]);
-          const f32x4 dc = {quad_bcast<0>(d1), quad_bcast<1>(d1), quad_bcast<2>(d1),
-                            quad_bcast<3>(d1)};
-#pragma unroll
-          for (int c = 0; c < NT; ++c) {
-            f32x4 s_ = S_acc[c][m];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s_[e] *= dc[e];
-            S_acc[c][m] = mfma16(ac, vp[c], s_);
-          }
+    state_role<NT, DV>(sm, a, tr, row0, state_off, nsteps, 16 * NT * j, lane, rr, p);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Schedule. With one workgroup per chain the launch lasts as long as the longest chain, and
+// packed sequences of very different lengths leave most compute units idle for its second
+// half. The scheduler (one workgroup, on the device, so that the call stays asynchronous)
+// sorts the sequences by chunk count and splits the value columns of the longest ones over
+// two workgroups while that lowers the bound max(longest item, total work / compute units)
+// on the makespan; a half item re-does the prep work and half of the state work, costing
+// about kHalfCost of the whole chain. Items are listed longest first, which the in-order
+// workgroup dispatch turns into longest-processing-time-first list scheduling.
+
+constexpr int kMaxPlanSeqs = 1024;  // sequences one scheduling workgroup sorts
+constexpr double kHalfCost = 0.88;  // time of a half-column item relative to its whole chain
+
+__global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t* cu, int N, int H,
+                                                                  int T, int cus, int allow_split,
+                                                                  uint32_t* plan) {
+  __shared__ int key[kMaxPlanSeqs];       // chunks of the sequence
+  __shared__ int seq[kMaxPlanSeqs];       // sequence index
+  __shared__ int ent_seq[kMaxPlanSeqs];   // schedule entries (one per sequence), in order
+  __shared__ int ent_parts[kMaxPlanSeqs];
+  __shared__ uint32_t ent_off[kMaxPlanSeqs + 1];
+  __shared__ int n_ent;
+  const int t = threadIdx.x;
+  int c = -1;  // padding sorts last
+  if (t < N) c = (token_range(cu, t, T).len + kC - 1) / kC;
+  key[t] = c;
+  seq[t] = t;
+  __syncthreads();
+  // bitonic sort: more chunks first, then lower sequence index
+  for (int k = 2; k <= kMaxPlanSeqs; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int u = t ^ j;
+      if (u > t) {
+        const bool t_first = key[t] > key[u] || (key[t] == key[u] && seq[t] < seq[u]);
+        if (((t & k) == 0) != t_first) {
+          const int k0 = key[t], s0 = seq[t];
+          key[t] = key[u];
+          seq[t] = seq[u];
+          key[u] = k0;
+          seq[u] = s0;
         }
       }
-      lds_barrier();
+      __syncthreads();
     }
-    if (nsteps > 0) flush_outputs<NT, DV>(sm, odst, nsteps - 1, j, lane);
-    if (a.sT) {
-#pragma unroll
-      for (int c = 0; c < NT; ++c)
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
-            a.sT[state_off + (size_t)ch * DV + col[c]] = S_acc[c][m][e];
-          }
+  if (t == 0) {
+    double total = 0.0;  // work in chunk-times of one workgroup
+    for (int i = 0; i < N; ++i) total += (double)key[i] * H;
+    int ns = 0;  // the ns longest sequences are split
+    double maxhalf = 0.0;
+    while (allow_split && ns < N && key[ns] > 0) {
+      const double c0 = key[ns], next = ns + 1 < N ? key[ns + 1] : 0.0;
+      const double bound = fmax(fmax(c0, maxhalf), total / cus);
+      const double total2 = total + H * (2.0 * kHalfCost - 1.0) * c0;
+      const double maxhalf2 = fmax(maxhalf, kHalfCost * c0);
+      if (!(fmax(fmax(next, maxhalf2), total2 / cus) < 0.98 * bound)) break;
+      total = total2;
+      maxhalf = maxhalf2;
+      ++ns;
     }
+    // merge split sequences (item cost kHalfCost * chunks) and whole ones by cost
+    int a = 0, b = ns, e = 0;
+    uint32_t off = 0;
+    while (a < ns || b < N) {
+      const bool split = a < ns && (b >= N || kHalfCost * key[a] >= key[b]);
+      const int i = split ? a++ : b++;
+      ent_seq[e] = seq[i];
+      ent_parts[e] = split ? 2 : 1;
+      ent_off[e] = off;
+      off += (uint32_t)H * ent_parts[e];
+      ++e;
+    }
+    ent_off[e] = off;
+    n_ent = e;
+    plan[0] = off;
+  }
+  __syncthreads();
+  const uint32_t items = ent_off[n_ent];
+  for (uint32_t i = t; i < items; i += kMaxPlanSeqs) {
+    int lo = 0, hi = n_ent - 1;  // entry holding item i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ent_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t local = i - ent_off[lo];
+    const int parts = ent_parts[lo];
+    const uint32_t hh = local / parts;
+    const uint32_t part = parts == 2 ? 1 + local % 2 : 0;
+    plan[1 + i] = (((uint32_t)ent_seq[lo] * H + hh) << 2) | part;
   }
 }
 
 template <int NS, int NT, bool PER_CHANNEL>
-hipError_t launch_ns(const ChunkArgs& a, hipStream_t stream) {
+hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
   chunk_mfma_kernel<NS, NT, PER_CHANNEL>
-      <<<dim3(a.N * a.H), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
+      <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -553,12 +673,40 @@ bool chunk_mfma_supports(int dk, int dv, int T) {
   return dk == kDK && (dv == 64 || dv == 128) && (long long)T * kDK * 4 < (1ll << 31);
 }
 
-hipError_t launch_chunk_mfma(const ChunkArgs& a, bool per_channel, hipStream_t stream) {
+size_t chunk_plan_bytes(int N, int H, int dv) {
+  (void)dv;
+  if (N > kMaxPlanSeqs) return 0;  // too many sequences to sort in one workgroup: no schedule
+  const size_t words = 1 + 2 * (size_t)N * H;
+  return (words * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_chunk_mfma(const ChunkArgs& args, bool per_channel, hipStream_t stream) {
+  ChunkArgs a = args;
   if (!chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
+  const bool can_split = a.dv == 128;  // a half of dv = 128 is one 16-column tile per wavefront
+  unsigned grid = (unsigned)a.N * a.H;
+  a.split_all = 0;
+  if (a.plan && a.cu) {
+    // packed sequences: the work list is built on the device from cu_seqlens
+    chunk_plan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, can_split,
+                                                      a.plan);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (can_split) grid *= 2;  // the largest schedule; workgroups past its length exit at once
+  } else {
+    // equal lengths: split every chain when all the halves fit on the device at once
+    a.plan = nullptr;
+    if (can_split && a.cus > 0 && 2ll * a.N * a.H <= a.cus) {
+      a.split_all = 1;
+      grid *= 2;
+    }
+  }
   // four state wavefronts: two 16-column tiles each for dv = 128, one for dv = 64
   if (a.dv == 128)
-    return per_channel ? launch_ns<4, 2, true>(a, stream) : launch_ns<4, 2, false>(a, stream);
-  return per_channel ? launch_ns<4, 1, true>(a, stream) : launch_ns<4, 1, false>(a, stream);
+    return per_channel ? launch_ns<4, 2, true>(a, grid, stream)
+                       : launch_ns<4, 2, false>(a, grid, stream);
+  return per_channel ? launch_ns<4, 1, true>(a, grid, stream)
+                     : launch_ns<4, 1, false>(a, grid, stream);
 }
 
 }  // namespace kda

@@ -22,6 +22,14 @@ struct ChunkArgs {
   int T;               // length of the T axis of every [B, H, T, .] tensor
   int dk;
   int dv;
+  // Work list built on the device by the scheduler (see chunk_plan_bytes), or nullptr for
+  // one workgroup per chain in chain order. Entry 0 is the item count; item i is
+  // ((n * H + h) << 2) | part with part 0 = all value columns, 1 / 2 = first / second half.
+  uint32_t* plan;
+  int cus;             // compute units of the device (sizes the schedule)
+  // Without a work list: split every chain's value columns over two workgroups
+  // (item 2 c + i is half i + 1 of chain c). Chosen on the host for equal-length batches.
+  int split_all;
 };
 
 // Arguments of one kda_recurrent_step call.
@@ -45,5 +53,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, bool pe
 hipError_t launch_chunk_f32(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool per_channel, hipStream_t stream);
 bool chunk_mfma_supports(int dk, int dv, int T);
+// Bytes of workspace the matrix-core path uses for its schedule (0: no schedule).
+size_t chunk_plan_bytes(int N, int H, int dv);
 
 }  // namespace kda

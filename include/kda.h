@@ -55,9 +55,14 @@ typedef enum {
 } kda_gate_mode;
 
 /*
- * Bytes of device workspace kda_chunk_fwd needs for this problem. The current
- * kernels need none and return 0; callers should still query it and pass a buffer
- * of at least this size (NULL is accepted when the size is 0).
+ * Bytes of device workspace kda_chunk_fwd uses for this problem. For packed sequences
+ * (num_seqs > 0, at most 1024) on the bf16 matrix-core path (dk = 128) it keeps a work
+ * list there: 4 * (1 + 2 * num_seqs * H) bytes rounded up to 256. Every other case
+ * returns 0. A small scheduling kernel fills the list on the device: it splits the value
+ * columns of the longest sequences' chains over two workgroups and orders the work
+ * longest first, so that packed sequences of unequal length keep every compute unit
+ * busy. (Equal-length batches need no list: their split is decided on the host.) The
+ * results do not depend on the schedule: each value column is computed the same way.
  */
 size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
                                     kda_dtype dt);
@@ -85,7 +90,12 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  *                 axis (packed variable-length sequences); B must be 1 and N = num_seqs.
  *                 Tokens of o outside every sequence are left untouched.
  *   dk, dv        each 64 or 128 (anything else: KDA_ERR_UNSUPPORTED)
- *   workspace     device buffer of at least kda_chunk_fwd_workspace_size(...) bytes
+ *   workspace     device buffer of at least kda_chunk_fwd_workspace_size(...) bytes,
+ *                 owned by the caller and not read before this call writes it; or
+ *                 workspace_bytes = 0 (workspace ignored) to run one workgroup per chain
+ *                 in chain order. 0 < workspace_bytes < the size, or a NULL workspace
+ *                 with workspace_bytes > 0: KDA_ERR_INVALID_ARG. Calls that overlap on
+ *                 one workspace race.
  *
  * Arithmetic: state and accumulation in float32. With dt = KDA_BF16 the dense
  * contractions take bf16 operands on the matrix cores (float32 accumulate); with

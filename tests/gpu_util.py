@@ -45,7 +45,7 @@ def assert_close(got, want, tol, what):
     return e
 
 
-def run_chunk(x, dtype: str, initial_state=True, o_fill=None):
+def run_chunk(x, dtype: str, initial_state=True, o_fill=None, schedule=True):
     """Runs kda_chunk_fwd on inputs ``x`` (kda_workloads.ChunkInputs).
     Returns (o float32 numpy [B,H,T,dv], final state numpy [N,H,dk,dv])."""
     dt = DT[dtype]
@@ -56,7 +56,8 @@ def run_chunk(x, dtype: str, initial_state=True, o_fill=None):
     o = None
     if o_fill is not None:
         o = torch.full(tuple(x.v.shape), o_fill, dtype=dt, device=dev())
-    o, sT = kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, o=o)
+    o, sT = kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, o=o,
+                          schedule=schedule)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), sT.cpu().numpy()
 

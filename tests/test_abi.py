@@ -40,8 +40,17 @@ def test_status_strings():
     assert "UNKNOWN" in kda.kda_status_string(99)
 
 
-def test_workspace_size_is_zero():
-    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == 0
+def test_workspace_size():
+    # the matrix-core path keeps a work list of 1 + 2 N H words (rounded up to 256 bytes)
+    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == 2304
+    assert kda.kda_chunk_fwd_workspace_size(1, 16, 4096, 128, 64, 2, kda.KDA_BF16) == 512
+    # equal-length batches (num_seqs = 0) are scheduled on the host
+    assert kda.kda_chunk_fwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_BF16) == 0
+    # no schedule: fp32, dk = 64, more than 1024 sequences, invalid sizes
+    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_F32) == 0
+    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 64, 128, 8, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_fwd_workspace_size(1, 4, 65536, 128, 128, 1025, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_fwd_workspace_size(0, 4, 64, 128, 128, 0, kda.KDA_BF16) == 0
 
 
 DUMMY = 0x1000  # never dereferenced: every call below is rejected on the host
@@ -67,6 +76,11 @@ def chunk_call(**over):
     (dict(cu_seqlens=DUMMY, num_seqs=2, B=2), kda.KDA_ERR_INVALID_ARG),
     (dict(cu_seqlens=DUMMY, num_seqs=0), kda.KDA_ERR_INVALID_ARG),
     (dict(num_seqs=3), kda.KDA_ERR_INVALID_ARG),
+    # packed sequences need a work list: a buffer below its size, or a size without a buffer
+    (dict(cu_seqlens=DUMMY, num_seqs=2, workspace=DUMMY, workspace_bytes=16),
+     kda.KDA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=DUMMY, num_seqs=2, workspace=None, workspace_bytes=4096),
+     kda.KDA_ERR_INVALID_ARG),
     (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
     (dict(dv=32), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=256, dv=256), kda.KDA_ERR_UNSUPPORTED),

@@ -154,3 +154,23 @@ def test_gdn_equals_broadcast_kda():
     o2, s2 = run_chunk(x, "bf16")
     assert_close(o1, o2, 1e-2, "GDN vs KDA outputs")
     assert_close(s1, s2, 1e-2, "GDN vs KDA states")
+
+
+@pytest.mark.parametrize("dv", [128, 64])
+def test_schedule_is_bitwise_neutral(dv):
+    """The work list (longest sequences first, value columns of the longest chains split
+    over two workgroups) changes only where each column is computed, not how: outputs and
+    final states equal the one-workgroup-per-chain run bit for bit, and match the oracle."""
+    lens = [3000, 90, 700, 0, 1300, 33, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(H=4, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05, seed=21)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(8).standard_normal((len(lens), 4, 128, dv)).astype(
+        np.float32) * np.float32(0.02)
+    note(f"chunk schedule neutrality dv={dv}")
+    o1, s1 = run_chunk(x, "bf16", schedule=True)
+    o0, s0 = run_chunk(x, "bf16", schedule=False)
+    np.testing.assert_array_equal(o1, o0)
+    np.testing.assert_array_equal(s1, s0)
+    check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], f"scheduled dv={dv}")
