@@ -37,7 +37,7 @@ def _load():
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         lib.oracle_kda_chains.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
-                                          P, P, P, P, ctypes.c_int, P, P, P, P, P, P,
+                                          P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P, P,
                                           ctypes.c_int]
         lib.oracle_kda_chains.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -62,12 +62,17 @@ def kda_chains(q, k, v, g, beta, row_off, row_len, s0=None, erase=None, write=No
     """Runs independent chains whose tokens are rows of flat arrays.
 
     q, k: [rows, dk]; v: [rows, dv]; g: [rows, dk] (per channel) or [rows] (per head);
-    beta (and the optional erase / write gates of the pins): [rows].
+    beta: [rows]. The optional erase / write gates are scalars per row ([rows], used by
+    the pins) or the Gated Delta Rule-2 vectors (erase [rows, dk], write [rows, dv]).
     Chain c covers rows row_off[c] .. row_off[c] + row_len[c] - 1. s0: [chains, dk, dv].
     Returns (o [rows, dv], final states [chains, dk, dv]), both float64.
     """
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     erase, write, s0 = _f64(erase), _f64(write), _f64(s0)
+    erase_vec = erase if erase is not None and erase.ndim == 2 else None
+    write_vec = write if write is not None and write.ndim == 2 else None
+    erase = None if erase_vec is not None else erase
+    write = None if write_vec is not None else write
     rows, dk = q.shape
     dv = v.shape[1]
     per_channel = 1 if g.ndim == 2 else 0
@@ -75,6 +80,10 @@ def kda_chains(q, k, v, g, beta, row_off, row_len, s0=None, erase=None, write=No
     ln = np.ascontiguousarray(row_len, dtype=np.int64)
     n = len(off)
     assert k.shape == (rows, dk) and v.shape[0] == rows and beta.shape == (rows,)
+    assert erase_vec is None or erase_vec.shape == (rows, dk)
+    assert write_vec is None or write_vec.shape == (rows, dv)
+    assert erase is None or erase.shape == (rows,)
+    assert write is None or write.shape == (rows,)
     assert np.all(off >= 0) and np.all(ln >= 0) and np.all(off + ln <= rows)
     if s0 is not None:
         assert s0.shape == (n, dk, dv)
@@ -82,17 +91,19 @@ def kda_chains(q, k, v, g, beta, row_off, row_len, s0=None, erase=None, write=No
     sf = np.zeros((n, dk, dv), np.float64)
     rc = _load().oracle_kda_chains(n, dk, dv, _ptr(off), _ptr(ln), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(g), per_channel, _ptr(beta), _ptr(erase), _ptr(write),
-                                   _ptr(s0), _ptr(o), _ptr(sf), int(threads))
+                                   _ptr(erase_vec), _ptr(write_vec), _ptr(s0), _ptr(o),
+                                   _ptr(sf), int(threads))
     if rc != 0:
         raise MemoryError("oracle_kda_chains could not allocate its work buffers")
     return o, sf
 
 
 def pack_chains(q, k, v, g, beta, s0=None, cu_seqlens=None,
-                chains: Optional[Iterable[Tuple[int, int]]] = None):
+                chains: Optional[Iterable[Tuple[int, int]]] = None, erase=None, write=None):
     """Gathers the rows of the selected (sequence n, head h) chains of head-major inputs
     [B, H, T, ...] (B = 1 with ``cu_seqlens``) into the flat float64 arrays of
-    ``kda_chains``. Returns (chains, args, kwargs) with ``kda_chains(*args, **kwargs)``."""
+    ``kda_chains``; ``erase`` [B, H, T, dk] and ``write`` [B, H, T, dv] are the Gated
+    Delta Rule-2 gates. Returns (chains, args, kwargs) with ``kda_chains(*args, **kwargs)``."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if cu_seqlens is not None:
@@ -123,31 +134,42 @@ def pack_chains(q, k, v, g, beta, s0=None, cu_seqlens=None,
     args = (gather(q, dk), gather(k, dk), gather(v, dv), gather(g, dk if per_channel else 0),
             gather(beta, 0), offs, lens)
     kwargs = {"s0": np.stack([s0[n, h] for (n, h) in chains]) if s0 is not None else None}
+    if erase is not None:
+        kwargs["erase"] = gather(erase, dk)
+    if write is not None:
+        kwargs["write"] = gather(write, dv)
     return chains, args, kwargs
 
 
 def kda_forward(q, k, v, g, beta, s0=None, cu_seqlens=None,
                 chains: Optional[Iterable[Tuple[int, int]]] = None,
-                threads: int = 0) -> Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]]:
+                threads: int = 0, erase=None,
+                write=None) -> Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]]:
     """Forward over head-major inputs [B, H, T, ...] (B = 1 with ``cu_seqlens``).
 
     Each (sequence n, head h) is an independent chain. ``chains`` selects a subset
-    (default: all). Returns {(n, h): (o [len, dv], final state [dk, dv])}, float64.
+    (default: all). ``erase`` [B, H, T, dk] and ``write`` [B, H, T, dv] select Gated
+    Delta Rule-2 (beta is then unused). Returns {(n, h): (o [len, dv], final state
+    [dk, dv])}, float64.
     """
-    chains, args, kwargs = pack_chains(q, k, v, g, beta, s0, cu_seqlens, chains)
+    chains, args, kwargs = pack_chains(q, k, v, g, beta, s0, cu_seqlens, chains, erase, write)
     o, sf = kda_chains(*args, **kwargs, threads=threads)
     offs, lens = args[5], args[6]
     return {ch: (o[offs[c]:offs[c] + lens[c]], sf[c]) for c, ch in enumerate(chains)}
 
 
-def kda_decode_step(state, q, k, v, g, beta, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+def kda_decode_step(state, q, k, v, g, beta, threads: int = 0, erase=None,
+                    write=None) -> Tuple[np.ndarray, np.ndarray]:
     """One single-token step for every (sequence, head): state [N, H, dk, dv];
-    q, k [N, H, dk]; v [N, H, dv]; g [N, H, dk] or [N, H]; beta [N, H].
+    q, k [N, H, dk]; v [N, H, dv]; g [N, H, dk] or [N, H]; beta [N, H]; optional Gated
+    Delta Rule-2 gates erase [N, H, dk] and write [N, H, dv].
     Returns (o [N, H, dv], new state [N, H, dk, dv]) in float64."""
     N, H, dk, dv = state.shape
     rows = N * H
     o, sf = kda_chains(q.reshape(rows, dk), k.reshape(rows, dk), v.reshape(rows, dv),
                        g.reshape(rows, -1) if g.ndim == 3 else g.reshape(rows),
                        beta.reshape(rows), np.arange(rows), np.ones(rows, np.int64),
-                       s0=state.reshape(rows, dk, dv), threads=threads)
+                       s0=state.reshape(rows, dk, dv), threads=threads,
+                       erase=None if erase is None else np.reshape(erase, (rows, dk)),
+                       write=None if write is None else np.reshape(write, (rows, dv)))
     return o.reshape(N, H, dv), sf.reshape(N, H, dk, dv)

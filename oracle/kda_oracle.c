@@ -19,10 +19,16 @@
  *   3. p = S^T k_t             (the prediction of the value from the decayed state)
  *   4. S <- S + k_t (w v_t - e p)^T
  *   5. o_t = S^T q_t
- * With e = w = beta_t this is the method. Other (e, w) exist only for the pins of the
- * tests: they are the scalar form of the decoupled erase / write gates of "Token Mixer I",
- * section "Gated DeltaNet-2: Decoupling Erase and Write" (e = 0, w = 1 and alpha = 1 give
- * plain linear attention).
+ * With e = w = beta_t this is the method. Other scalar (e, w) exist for the pins of the
+ * tests (e = 0, w = 1 and alpha = 1 give plain linear attention).
+ *
+ * Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2: Decoupling Erase and
+ * Write", the residual of its fast-weight section) replaces the scalar gate by a
+ * per-key-channel erase gate b_t in [0,1]^dk and a per-value-channel write gate
+ * w_t in [0,1]^dv: with S~ = Diag(alpha) S,
+ *   S_t = S~ + k_t (w_t * v_t - S~^T (b_t * k_t))^T      (* elementwise)
+ * so steps 3-4 read p = S~^T (b_t * k_t) and write k_t (w_t * v_t - p)^T. b = beta 1 and
+ * w = beta 1 give the method again.
  */
 #include <math.h>
 #include <stdint.h>
@@ -45,8 +51,9 @@ static void oracle_chain(int dk, int dv, int64_t off, int64_t len,
                          const double* q, const double* k, const double* v,
                          const double* g, int gate_per_channel, const double* beta,
                          const double* erase, const double* write,
+                         const double* erase_vec, const double* write_vec,
                          const double* s0, double* o, double* s_final,
-                         double* S, double* a, double* p, double* d) {
+                         double* S, double* a, double* p, double* d, double* ek) {
   if (s0)
     memcpy(S, s0, sizeof(double) * (size_t)dk * dv);
   else
@@ -67,13 +74,14 @@ static void oracle_chain(int dk, int dv, int64_t off, int64_t len,
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a[i];
 
-    /* 3: prediction p = S^T k */
+    /* 3: prediction p = S^T (e k), e the erase gate of each key channel */
+    for (int i = 0; i < dk; ++i) ek[i] = (erase_vec ? erase_vec[row * dk + i] : et) * kt[i];
     for (int j = 0; j < dv; ++j) p[j] = 0.0;
     for (int i = 0; i < dk; ++i)
-      for (int j = 0; j < dv; ++j) p[j] += S[(size_t)i * dv + j] * kt[i];
+      for (int j = 0; j < dv; ++j) p[j] += S[(size_t)i * dv + j] * ek[i];
 
-    /* 4: rank-one correction along k */
-    for (int j = 0; j < dv; ++j) d[j] = wt * vt[j] - et * p[j];
+    /* 4: rank-one correction along k, w the write gate of each value channel */
+    for (int j = 0; j < dv; ++j) d[j] = (write_vec ? write_vec[row * dv + j] : wt) * vt[j] - p[j];
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += kt[i] * d[j];
 
@@ -91,6 +99,8 @@ static void oracle_chain(int dk, int dv, int64_t off, int64_t len,
  *   row_off[c], row_len[c] : first row and number of tokens of chain c
  *   q, k : [rows, dk]   v, o : [rows, dv]   g : [rows, dk] or [rows]   beta : [rows]
  *   erase, write : [rows] or NULL (NULL = beta, the method itself)
+ *   erase_vec    : [rows, dk] or NULL; write_vec : [rows, dv] or NULL (Gated Delta Rule-2
+ *                  gates; when given they replace erase / write)
  *   s0, s_final  : [n_chains, dk, dv] or NULL (s0 NULL = zero initial state)
  *   n_threads    : OpenMP threads (<= 0: the runtime default)
  * Returns 0, or -1 if a work buffer could not be allocated.
@@ -100,6 +110,7 @@ int oracle_kda_chains(int n_chains, int dk, int dv,
                       const double* q, const double* k, const double* v,
                       const double* g, int gate_per_channel, const double* beta,
                       const double* erase, const double* write,
+                      const double* erase_vec, const double* write_vec,
                       const double* s0, double* o, double* s_final, int n_threads) {
   int failed = 0;
 #ifdef _OPENMP
@@ -111,7 +122,8 @@ int oracle_kda_chains(int n_chains, int dk, int dv,
     double* a = (double*)malloc(sizeof(double) * (size_t)dk);
     double* p = (double*)malloc(sizeof(double) * (size_t)dv);
     double* d = (double*)malloc(sizeof(double) * (size_t)dv);
-    const int have_buffers = S && a && p && d;
+    double* ek = (double*)malloc(sizeof(double) * (size_t)dk);
+    const int have_buffers = S && a && p && d && ek;
     if (!have_buffers) failed = 1;
     /* every thread reaches the work-sharing loop; one without buffers computes nothing */
 #ifdef _OPENMP
@@ -120,13 +132,14 @@ int oracle_kda_chains(int n_chains, int dk, int dv,
     for (int c = 0; c < n_chains; ++c) {
       if (!have_buffers) continue;
       oracle_chain(dk, dv, row_off[c], row_len[c], q, k, v, g, gate_per_channel, beta,
-                   erase, write, s0 ? s0 + (size_t)c * dk * dv : NULL, o,
-                   s_final ? s_final + (size_t)c * dk * dv : NULL, S, a, p, d);
+                   erase, write, erase_vec, write_vec, s0 ? s0 + (size_t)c * dk * dv : NULL, o,
+                   s_final ? s_final + (size_t)c * dk * dv : NULL, S, a, p, d, ek);
     }
     free(S);
     free(a);
     free(p);
     free(d);
+    free(ek);
   }
   return failed ? -1 : 0;
 }

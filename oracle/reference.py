@@ -24,8 +24,10 @@ def recurrence(q, k, v, g, beta, s0=None, erase=None, write=None, states=False):
     Fine-grained Gating", boxed recurrence, evaluated in the decay-then-delta order of
     the page "KDA 与 Gated DeltaNet：线性注意力怎样读写有限状态", section 2:
       S~ = Diag(exp g_t) S;  S = S~ + k_t (w_t v_t - e_t S~^T k_t)^T;  o_t = S^T q_t,
-    with e_t = w_t = beta_t (None) for the method. Returns (o [T, dv], S_T) and, with
-    ``states``, also the list of states after every token.
+    with e_t = w_t = beta_t (None) for the method. ``erase`` [T, dk] and ``write``
+    [T, dv] are the per-channel gates of Gated Delta Rule-2 ("Token Mixer I", section
+    "Gated DeltaNet-2"): S = S~ + k_t (w_t * v_t - S~^T (e_t * k_t))^T. Returns
+    (o [T, dv], S_T) and, with ``states``, also the list of states after every token.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     T, dk = k.shape
@@ -39,8 +41,8 @@ def recurrence(q, k, v, g, beta, s0=None, erase=None, write=None, states=False):
     hist = []
     for t in range(T):
         S = a[t][:, None] * S
-        p = S.T @ k[t]
-        S = S + np.outer(k[t], w[t] * v[t] - e[t] * p)
+        p = S.T @ (e[t] * k[t])
+        S = S + np.outer(k[t], w[t] * v[t] - p)
         o[t] = S.T @ q[t]
         if states:
             hist.append(S.copy())

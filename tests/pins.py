@@ -281,6 +281,69 @@ def pin_invariants(impl):
         prev = sts[t]
 
 
+# ---------------------------------------------------------------------------------
+# Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2: Decoupling Erase and
+# Write"): erase gate b_t in [0,1]^dk on the key side, write gate w_t in [0,1]^dv on the
+# value side.
+
+def _gdr2_gates(T, dk, dv, seed):
+    rng = np.random.default_rng(seed)
+    return rng.random((T, dk)), rng.random((T, dv))
+
+
+def pin_gdr2_reduces_to_kda(impl):
+    """The section states that b_t = beta_t 1 and w_t = beta_t 1 give KDA exactly."""
+    q, k, v, g, beta, s0 = case(40, 12, 10, seed=61)
+    o1, S1 = impl(q, k, v, g, beta, s0=s0)
+    o2, S2 = impl(q, k, v, g, beta, s0=s0, erase=np.repeat(beta[:, None], 12, axis=1),
+                  write=np.repeat(beta[:, None], 10, axis=1))
+    _close(o2, o1, 1e-12, "b = w = beta 1 outputs")
+    _close(S2, S1, 1e-12, "b = w = beta 1 state")
+
+
+def pin_gdr2_write_only(impl):
+    """With b = 0 nothing is erased: S_t = Diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T, whose
+    unrolled (parallel) form is the decayed linear attention of "Token Mixer I", section
+    "Mamba2: Linear Attention with Decay", with per-channel decay and gated values:
+    o_t = (q_t * gamma_t)^T S_0 + sum_{j<=t} (sum_c q_t[c] k_j[c] gamma_t[c] / gamma_j[c]) w_j * v_j,
+    gamma_t = exp(sum_{s<=t} g_s)."""
+    T, dk, dv = 14, 9, 7
+    q, k, v, g, beta, s0 = case(T, dk, dv, seed=62)
+    _, w = _gdr2_gates(T, dk, dv, 63)
+    o, S = impl(q, k, v, g, beta, s0=s0, erase=np.zeros((T, dk)), write=w)
+    G = np.cumsum(g, axis=0)
+    z = w * v
+    want = np.zeros((T, dv))
+    for t in range(T):
+        want[t] = (q[t] * np.exp(G[t])) @ s0
+        for j in range(t + 1):
+            want[t] += np.sum(q[t] * k[j] * np.exp(G[t] - G[j])) * z[j]
+    _close(o, want, 1e-10, "write-only outputs")
+    S_want = np.exp(G[-1])[:, None] * s0 + sum(
+        np.outer(k[j] * np.exp(G[-1] - G[j]), z[j]) for j in range(T))
+    _close(S, S_want, 1e-10, "write-only state")
+
+
+def pin_gdr2_erase_direction(impl):
+    """One token, no decay, nothing written: the erase matrix keeps k_t as its left factor
+    and takes b_t * k_t as its right factor (the read direction), so
+    S_1 = (I - k (b * k)^T) S_0 and o = S_1^T q. Zeroing one channel of b leaves the
+    component of S_0 along that channel unread."""
+    dk, dv = 8, 6
+    q, k, v, g, beta, s0 = case(1, dk, dv, seed=64)
+    b, _ = _gdr2_gates(1, dk, dv, 65)
+    b[0, 3] = 0.0
+    o, S = impl(q, k, v, np.zeros_like(g), beta, s0=s0, erase=b, write=np.zeros((1, dv)))
+    S_want = (np.eye(dk) - np.outer(k[0], b[0] * k[0])) @ s0
+    _close(S, S_want, 1e-12, "erase state")
+    _close(o[0], S_want.T @ q[0], 1e-12, "erase output")
+    s_mod = s0.copy()
+    s_mod[3] += 1.0   # channel 3 is not read: changing its row moves S only along that row
+    _, S2 = impl(q, k, v, np.zeros_like(g), beta, s0=s_mod, erase=b, write=np.zeros((1, dv)))
+    d = S2 - S
+    _close(np.delete(d, 3, axis=0), np.zeros((dk - 1, dv)), 1e-12, "unread channel")
+
+
 ALL_PINS = [
     pin_basis_key_overwrite,
     pin_chunked_equals_recurrence,
@@ -293,4 +356,7 @@ ALL_PINS = [
     pin_split_resume,
     pin_page4_capacity_demo,
     pin_invariants,
+    pin_gdr2_reduces_to_kda,
+    pin_gdr2_write_only,
+    pin_gdr2_erase_direction,
 ]

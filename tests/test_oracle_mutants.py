@@ -24,27 +24,32 @@ def _make(mut):
             a = np.exp(gg[t])
             G = G + gg[t]
             if mut == "decay_after_update":
-                S = S + np.outer(k[t], w[t] * v[t] - e[t] * (S.T @ k[t]))
+                S = S + np.outer(k[t], w[t] * v[t] - S.T @ (e[t] * k[t]))
                 S = a[:, None] * S
             elif mut == "predict_from_undecayed":
-                p = S.T @ k[t]
-                S = a[:, None] * S + np.outer(k[t], w[t] * v[t] - e[t] * p)
+                p = S.T @ (e[t] * k[t])
+                S = a[:, None] * S + np.outer(k[t], w[t] * v[t] - p)
             elif mut == "cumulative_decay":
                 S = np.exp(G)[:, None] * S
-                S = S + np.outer(k[t], w[t] * v[t] - e[t] * (S.T @ k[t]))
+                S = S + np.outer(k[t], w[t] * v[t] - S.T @ (e[t] * k[t]))
             else:
                 S = a[:, None] * S if mut != "no_decay" else S
                 p = S.T @ k[t]
+                pe = S.T @ (e[t] * k[t])   # read along the erase-gated key
                 if mut == "erase_without_beta":
                     S = S + np.outer(k[t], w[t] * v[t] - p)
                 elif mut == "erase_sign":
-                    S = S + np.outer(k[t], w[t] * v[t] + e[t] * p)
+                    S = S + np.outer(k[t], w[t] * v[t] + pe)
                 elif mut == "predict_with_query":
-                    S = S + np.outer(k[t], w[t] * v[t] - e[t] * (S.T @ q[t]))
+                    S = S + np.outer(k[t], w[t] * v[t] - S.T @ (e[t] * q[t]))
                 elif mut == "write_without_beta":
-                    S = S + np.outer(k[t], v[t] - e[t] * p)
+                    S = S + np.outer(k[t], v[t] - pe)
+                elif mut == "erase_gate_on_write_factor":   # b on the left factor
+                    S = S + np.outer(e[t] * k[t], w[t] * v[t] - p)
+                elif mut == "write_gate_on_residual":       # w on the whole residual
+                    S = S + np.outer(k[t], w[t] * (v[t] - pe))
                 else:
-                    S = S + np.outer(k[t], w[t] * v[t] - e[t] * p)
+                    S = S + np.outer(k[t], w[t] * v[t] - pe)
             if mut == "readout_before_update_order":
                 o[t] = (S - np.outer(k[t], w[t] * v[t])).T @ q[t]
             elif mut == "readout_with_key":
@@ -59,7 +64,8 @@ def _make(mut):
 
 MUTANTS = ["decay_after_update", "predict_from_undecayed", "cumulative_decay", "no_decay",
            "erase_without_beta", "erase_sign", "predict_with_query", "write_without_beta",
-           "readout_before_update_order", "readout_with_key", "readout_transposed_gate"]
+           "readout_before_update_order", "readout_with_key", "readout_transposed_gate",
+           "erase_gate_on_write_factor", "write_gate_on_residual"]
 
 
 def test_unmutated_copy_passes_all_pins():

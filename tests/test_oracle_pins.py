@@ -35,7 +35,10 @@ def test_c_oracle_matches_numpy_twin(gate):
     q, k, v, g, beta, s0 = pins.case(200, 16, 12, seed=41, gate=gate, strong=True)
     e = np.random.default_rng(2).random(200)
     w = np.random.default_rng(3).random(200)
-    for kw in ({}, {"s0": s0}, {"s0": s0, "erase": e, "write": w}):
+    ev = np.random.default_rng(4).random((200, 16))   # Gated Delta Rule-2 vector gates
+    wv = np.random.default_rng(6).random((200, 12))
+    for kw in ({}, {"s0": s0}, {"s0": s0, "erase": e, "write": w},
+               {"s0": s0, "erase": ev, "write": wv}):
         o1, S1 = c_oracle(q, k, v, g, beta, **kw)
         o2, S2 = numpy_twin(q, k, v, g, beta, **kw)
         np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
