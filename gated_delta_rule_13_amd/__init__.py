@@ -30,7 +30,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_PER_CHANNEL, KDA_GATE_PER_HEAD = 0, 1
 
 EXPORTED_SYMBOLS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
-                    "kda_status_string")
+                    "kda_status_string", "kda_gdr2_chunk_fwd", "kda_gdr2_recurrent_step")
 
 _lib = None
 
@@ -55,6 +55,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = I
     lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.kda_recurrent_step.restype = I
+    lib.kda_gdr2_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                       I, P, ctypes.c_size_t, P]
+    lib.kda_gdr2_chunk_fwd.restype = I
+    lib.kda_gdr2_recurrent_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.kda_gdr2_recurrent_step.restype = I
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [I]
@@ -82,6 +87,21 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, n
 def kda_recurrent_step(q, k, v, g, beta, state, o, N, H, dk, dv, dt, gm, stream) -> int:
     return int(load_library().kda_recurrent_step(q, k, v, g, beta, state, o, N, H, dk, dv,
                                                  dt, gm, stream))
+
+
+def kda_gdr2_chunk_fwd(q, k, v, g, erase, write, initial_state, final_state, o, cu_seqlens,
+                       num_seqs, B, H, T, dk, dv, dt, gm, workspace, workspace_bytes,
+                       stream) -> int:
+    return int(load_library().kda_gdr2_chunk_fwd(q, k, v, g, erase, write, initial_state,
+                                                 final_state, o, cu_seqlens, num_seqs, B, H,
+                                                 T, dk, dv, dt, gm, workspace,
+                                                 workspace_bytes, stream))
+
+
+def kda_gdr2_recurrent_step(q, k, v, g, erase, write, state, o, N, H, dk, dv, dt, gm,
+                            stream) -> int:
+    return int(load_library().kda_gdr2_recurrent_step(q, k, v, g, erase, write, state, o, N,
+                                                      H, dk, dv, dt, gm, stream))
 
 
 # ----------------------------------------------------------------------- torch helpers
@@ -114,19 +134,10 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
-              cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
-              o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              schedule: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked forward over [B, H, T, d] head-major tensors (see ``kda_chunk_fwd``).
-
-    g: float32 [B, H, T, dk] (per key channel, KDA) or [B, H, T] (per head, Gated
-    DeltaNet); beta: float32 [B, H, T]; initial_state: float32 [N, H, dk, dv] or None;
-    cu_seqlens: int32 [N + 1] on the GPU (B must be 1) or None. ``o`` and ``final_state``
-    may be given to reuse buffers; ``final_state`` may be ``initial_state``.
-    ``schedule=False`` passes no workspace (one workgroup per chain, no column split).
-    """
+def _chunk(q, k, v, g, gates, initial_state, cu_seqlens, output_final_state, o, final_state,
+           schedule):
+    """Shared argument checks and call of kda_chunk_fwd / kda_gdr2_chunk_fwd.
+    ``gates`` is (beta,) or (erase, write)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -134,11 +145,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, q.dtype, dev)
     _check(g, "g", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
     _check(initial_state, "initial_state", torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, H, T):
-        raise ValueError("inconsistent q/k/v/beta shapes")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("inconsistent q/k/v shapes")
+    if len(gates) == 1:
+        _check(gates[0], "beta", torch.float32, dev)
+        if gates[0].shape != (B, H, T):
+            raise ValueError(f"beta must be {(B, H, T)}")
+    else:
+        _check(gates[0], "erase", torch.float32, dev)
+        _check(gates[1], "write", torch.float32, dev)
+        if gates[0].shape != (B, H, T, dk) or gates[1].shape != (B, H, T, dv):
+            raise ValueError(f"erase must be {(B, H, T, dk)} and write {(B, H, T, dv)}")
     if g.shape == (B, H, T, dk):
         gm = KDA_GATE_PER_CHANNEL
     elif g.shape == (B, H, T):
@@ -157,20 +176,50 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     num_seqs = 0 if cu_seqlens is None else N
     ws_bytes = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt) if schedule else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                       _ptr(final_state), _ptr(o), _ptr(cu_seqlens), num_seqs, B, H, T, dk,
-                       dv, dt, gm, _ptr(ws), ws_bytes, _stream(dev))
+    common = (_ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(cu_seqlens), num_seqs,
+              B, H, T, dk, dv, dt, gm, _ptr(ws), ws_bytes, _stream(dev))
+    if len(gates) == 1:
+        st = kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]), *common)
+        where = "kda_chunk_fwd"
+    else:
+        st = kda_gdr2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]),
+                                _ptr(gates[1]), *common)
+        where = "kda_gdr2_chunk_fwd"
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_fwd")
+        raise KDAError(st, where)
     return o, final_state
 
 
-def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                   beta: torch.Tensor, state: torch.Tensor,
-                   o: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One decode step (see ``kda_recurrent_step``): q, k [N, H, dk]; v [N, H, dv];
-    g float32 [N, H, dk] or [N, H]; beta float32 [N, H]; state float32 [N, H, dk, dv],
-    updated in place. Returns o [N, H, dv]."""
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              schedule: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked forward over [B, H, T, d] head-major tensors (see ``kda_chunk_fwd``).
+
+    g: float32 [B, H, T, dk] (per key channel, KDA) or [B, H, T] (per head, Gated
+    DeltaNet); beta: float32 [B, H, T]; initial_state: float32 [N, H, dk, dv] or None;
+    cu_seqlens: int32 [N + 1] on the GPU (B must be 1) or None. ``o`` and ``final_state``
+    may be given to reuse buffers; ``final_state`` may be ``initial_state``.
+    ``schedule=False`` passes no workspace (one workgroup per chain, no column split).
+    """
+    return _chunk(q, k, v, g, (beta,), initial_state, cu_seqlens, output_final_state, o,
+                  final_state, schedule)
+
+
+def gdr2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   erase: torch.Tensor, write: torch.Tensor,
+                   initial_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                   o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                   schedule: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated Delta Rule-2 chunked forward (see ``kda_gdr2_chunk_fwd``): ``chunk_fwd`` with
+    beta replaced by erase float32 [B, H, T, dk] and write float32 [B, H, T, dv]."""
+    return _chunk(q, k, v, g, (erase, write), initial_state, cu_seqlens, output_final_state,
+                  o, final_state, schedule)
+
+
+def _step(q, k, v, g, gates, state, o):
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -178,11 +227,18 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, q.dtype, dev)
     _check(g, "g", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
     _check(state, "state", torch.float32, dev)
-    if k.shape != q.shape or v.shape[:2] != (N, H) or beta.shape != (N, H) \
-            or state.shape != (N, H, dk, dv):
+    if k.shape != q.shape or v.shape[:2] != (N, H) or state.shape != (N, H, dk, dv):
         raise ValueError("inconsistent decode shapes")
+    if len(gates) == 1:
+        _check(gates[0], "beta", torch.float32, dev)
+        if gates[0].shape != (N, H):
+            raise ValueError("beta must be [N, H]")
+    else:
+        _check(gates[0], "erase", torch.float32, dev)
+        _check(gates[1], "write", torch.float32, dev)
+        if gates[0].shape != (N, H, dk) or gates[1].shape != (N, H, dv):
+            raise ValueError("erase must be [N, H, dk] and write [N, H, dv]")
     if g.shape == (N, H, dk):
         gm = KDA_GATE_PER_CHANNEL
     elif g.shape == (N, H):
@@ -192,8 +248,32 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _check(o, "o", q.dtype, dev)
-    st = kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                            _ptr(o), N, H, dk, dv, dt, gm, _stream(dev))
+    if len(gates) == 1:
+        st = kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]),
+                                _ptr(state), _ptr(o), N, H, dk, dv, dt, gm, _stream(dev))
+        where = "kda_recurrent_step"
+    else:
+        st = kda_gdr2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]),
+                                     _ptr(gates[1]), _ptr(state), _ptr(o), N, H, dk, dv, dt,
+                                     gm, _stream(dev))
+        where = "kda_gdr2_recurrent_step"
     if st != KDA_OK:
-        raise KDAError(st, "kda_recurrent_step")
+        raise KDAError(st, where)
     return o
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   beta: torch.Tensor, state: torch.Tensor,
+                   o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step (see ``kda_recurrent_step``): q, k [N, H, dk]; v [N, H, dv];
+    g float32 [N, H, dk] or [N, H]; beta float32 [N, H]; state float32 [N, H, dk, dv],
+    updated in place. Returns o [N, H, dv]."""
+    return _step(q, k, v, g, (beta,), state, o)
+
+
+def gdr2_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        erase: torch.Tensor, write: torch.Tensor, state: torch.Tensor,
+                        o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gated Delta Rule-2 decode step (see ``kda_gdr2_recurrent_step``): erase float32
+    [N, H, dk], write float32 [N, H, dv] in place of beta."""
+    return _step(q, k, v, g, (erase, write), state, o)

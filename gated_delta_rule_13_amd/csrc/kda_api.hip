@@ -46,12 +46,16 @@ static int device_compute_units() {
   return n;
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const float* initial_state, float* final_state,
-                         void* o, const int32_t* cu_seqlens, int num_seqs, int B, int H,
-                         int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+// The two forward paths differ only in their gates: beta (KDA, Gated DeltaNet) or the
+// erase / write vectors of Gated Delta Rule-2 (erase != nullptr).
+static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* erase, const float* write,
+                                 const float* initial_state, float* final_state, void* o,
+                                 const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                                 int dk, int dv, kda_dtype dt, kda_gate_mode gm, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !g || !o) return KDA_ERR_INVALID_ARG;
+  if (erase ? !write : !beta) return KDA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
@@ -66,7 +70,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
 
   kda::ChunkArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = erase; a.write = write;
   a.s0 = initial_state; a.sT = final_state; a.o = o; a.cu = cu_seqlens;
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
   a.plan = scheduled ? static_cast<uint32_t*>(workspace) : nullptr;
@@ -81,21 +85,65 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
-                              const float* beta, float* state, void* o, int N, int H, int dk,
-                              int dv, kda_dtype dt, kda_gate_mode gm, hipStream_t stream) {
-  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+static kda_status recurrent_step_impl(const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta, const float* erase,
+                                      const float* write, float* state, void* o, int N, int H,
+                                      int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                                      hipStream_t stream) {
+  if (!q || !k || !v || !g || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (erase ? !write : !beta) return KDA_ERR_INVALID_ARG;
   if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
   if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
   if ((long long)N * H > 0x7fffffffll) return KDA_ERR_UNSUPPORTED;
   kda::DecodeArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = erase; a.write = write;
+  a.state = state; a.o = o;
   a.N = N; a.H = H;
   const hipError_t err =
       kda::launch_decode(a, dk, dv, dt == KDA_BF16, gm == KDA_GATE_PER_CHANNEL, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, float* final_state,
+                         void* o, const int32_t* cu_seqlens, int num_seqs, int B, int H,
+                         int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!beta) return KDA_ERR_INVALID_ARG;
+  return chunk_fwd_impl(q, k, v, g, beta, nullptr, nullptr, initial_state, final_state, o,
+                        cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm, workspace,
+                        workspace_bytes, stream);
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state, void* o, int N, int H, int dk,
+                              int dv, kda_dtype dt, kda_gate_mode gm, hipStream_t stream) {
+  if (!beta) return KDA_ERR_INVALID_ARG;
+  return recurrent_step_impl(q, k, v, g, beta, nullptr, nullptr, state, o, N, H, dk, dv, dt,
+                             gm, stream);
+}
+
+kda_status kda_gdr2_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                              const float* erase, const float* write,
+                              const float* initial_state, float* final_state, void* o,
+                              const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                              int dk, int dv, kda_dtype dt, kda_gate_mode gm, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (!erase || !write) return KDA_ERR_INVALID_ARG;
+  return chunk_fwd_impl(q, k, v, g, nullptr, erase, write, initial_state, final_state, o,
+                        cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm, workspace,
+                        workspace_bytes, stream);
+}
+
+kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                                   const float* erase, const float* write, float* state,
+                                   void* o, int N, int H, int dk, int dv, kda_dtype dt,
+                                   kda_gate_mode gm, hipStream_t stream) {
+  if (!erase || !write) return KDA_ERR_INVALID_ARG;
+  return recurrent_step_impl(q, k, v, g, nullptr, erase, write, state, o, N, H, dk, dv, dt,
+                             gm, stream);
 }
 
 }  // extern "C"

@@ -13,6 +13,10 @@
 // Every exponent is a difference G_i - G_j with j <= i, or G itself, so no factor
 // exceeds 1 in magnitude and nothing is divided by a decay.
 //
+// Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2"): the read side uses
+// the erase-gated keys B * K in place of Diag(beta) K (in A_kk and in the prediction), and
+// the values are gated per channel, X = W * V - ((B * K) e^G) S; the rest is unchanged.
+//
 // One 256-thread workgroup per (chain, block of DVB value columns): value columns are
 // independent (the decay acts on the rows of S), so the state pass splits over them.
 // Chunk size 32 keeps the fp32 tiles of q, k and G in LDS.
@@ -26,7 +30,7 @@ constexpr int kThreads = 256;
 constexpr int kC = 32;    // chunk length of this path
 constexpr int kDVB = 32;  // value columns per workgroup
 
-template <int DK, typename TIn, bool PER_CHANNEL>
+template <int DK, typename TIn, bool PER_CHANNEL, bool GDR2>
 __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_dvb) {
   __shared__ float sQ[kC][DK];
   __shared__ float sK[kC][DK];
@@ -39,6 +43,9 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
   __shared__ float sS[DK][kDVB];
   __shared__ float sBeta[kC];
   __shared__ float sGC[DK];
+  // Gated Delta Rule-2: erase-gated keys b * k (the read side) and the write gates
+  __shared__ float sE[GDR2 ? kC : 1][GDR2 ? DK : 1];
+  __shared__ float sW[GDR2 ? kC : 1][GDR2 ? kDVB : 1];
 
   const int tid = threadIdx.x;
   const int chain = blockIdx.x / n_dvb;
@@ -71,12 +78,14 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
       sQ[t][c] = ok ? to_f32(q[r * DK + c]) : 0.f;
       sK[t][c] = ok ? to_f32(k[r * DK + c]) : 0.f;
       sG[t][c] = ok ? (PER_CHANNEL ? a.g[r * DK + c] : a.g[r]) : 0.f;
+      if (GDR2) sE[t][c] = ok ? a.erase[r * DK + c] * sK[t][c] : 0.f;
     }
     for (int idx = tid; idx < kC * kDVB; idx += kThreads) {
       const int t = idx / kDVB, j = idx % kDVB;
       sV[t][j] = t < nt ? to_f32(v[(row0 + c0 + t) * DV + col0 + j]) : 0.f;
+      if (GDR2) sW[t][j] = t < nt ? a.write[(row0 + c0 + t) * DV + col0 + j] : 0.f;
     }
-    if (tid < kC) sBeta[tid] = tid < nt ? a.beta[row0 + c0 + tid] : 0.f;
+    if (tid < kC) sBeta[tid] = tid < nt ? (GDR2 ? 1.f : a.beta[row0 + c0 + tid]) : 0.f;
     __syncthreads();
     // -- chunk-local inclusive cumulative log-decay
     for (int c = tid; c < DK; c += kThreads) {
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
           const float e = __expf(sG[i][c] - sG[j][c]);
           const float kj = sK[j][c] * e;
           aq += sQ[i][c] * kj;
-          ak += sK[i][c] * kj;
+          ak += (GDR2 ? sE[i][c] : sK[i][c]) * kj;
         }
       }
       sAqk[i][j] = aq;
@@ -123,14 +132,21 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
       sG[t][c] = kk * __expf(sGC[c] - G);
       sQ[t][c] *= e;
       sK[t][c] = kk * e;
+      if (GDR2) sE[t][c] *= e;
     }
     __syncthreads();
-    // -- X = Diag(beta) (V - (K e^G) S)
+    // -- X = Diag(beta) (V - (K e^G) S); Gated Delta Rule-2: X = W * V - ((B * K) e^G) S
     for (int idx = tid; idx < kC * kDVB; idx += kThreads) {
       const int t = idx / kDVB, j = idx % kDVB;
-      float acc = sV[t][j];
-      for (int c = 0; c < DK; ++c) acc -= sK[t][c] * sS[c][j];
-      sX[t][j] = sBeta[t] * acc;
+      if (GDR2) {
+        float acc = sW[t][j] * sV[t][j];
+        for (int c = 0; c < DK; ++c) acc -= sE[t][c] * sS[c][j];
+        sX[t][j] = acc;
+      } else {
+        float acc = sV[t][j];
+        for (int c = 0; c < DK; ++c) acc -= sK[t][c] * sS[c][j];
+        sX[t][j] = sBeta[t] * acc;
+      }
     }
     __syncthreads();
     // -- V' = Tm X
@@ -169,20 +185,24 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
   }
 }
 
+template <int DK, typename TIn, bool PER_CHANNEL>
+void launch_gates(const ChunkArgs& a, dim3 grid, int n_dvb, hipStream_t stream) {
+  if (a.erase)
+    chunk_f32_kernel<DK, TIn, PER_CHANNEL, true><<<grid, dim3(kThreads), 0, stream>>>(a, n_dvb);
+  else
+    chunk_f32_kernel<DK, TIn, PER_CHANNEL, false><<<grid, dim3(kThreads), 0, stream>>>(a, n_dvb);
+}
+
 template <int DK>
 hipError_t launch_dk(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream) {
   const int n_dvb = a.dv / kDVB;
-  const dim3 grid(a.N * a.H * n_dvb), block(kThreads);
+  const dim3 grid(a.N * a.H * n_dvb);
   if (bf16) {
-    if (per_channel)
-      chunk_f32_kernel<DK, kda::bf16, true><<<grid, block, 0, stream>>>(a, n_dvb);
-    else
-      chunk_f32_kernel<DK, kda::bf16, false><<<grid, block, 0, stream>>>(a, n_dvb);
+    if (per_channel) launch_gates<DK, kda::bf16, true>(a, grid, n_dvb, stream);
+    else launch_gates<DK, kda::bf16, false>(a, grid, n_dvb, stream);
   } else {
-    if (per_channel)
-      chunk_f32_kernel<DK, float, true><<<grid, block, 0, stream>>>(a, n_dvb);
-    else
-      chunk_f32_kernel<DK, float, false><<<grid, block, 0, stream>>>(a, n_dvb);
+    if (per_channel) launch_gates<DK, float, true>(a, grid, n_dvb, stream);
+    else launch_gates<DK, float, false>(a, grid, n_dvb, stream);
   }
   return hipGetLastError();
 }

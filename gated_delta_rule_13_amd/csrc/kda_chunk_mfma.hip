@@ -179,16 +179,17 @@ struct BlockRegs {
   bf16x4 q[8];
   bf16x4 k[8];
   f32x4 g[8];
+  f32x4 b[8];  // erase gate (Gated Delta Rule-2 only)
   float beta;
 };
 
 // Bounded views of one chain's inputs, and this prep lane's byte offsets within a chunk.
 struct PrepSrc {
-  rsrc_t q, k, g, beta;
-  uint32_t qk_off, g_off, b_off;
+  rsrc_t q, k, g, beta, erase;
+  uint32_t qk_off, g_off, b_off, e_off;
 };
 
-template <bool PER_CHANNEL>
+template <bool PER_CHANNEL, bool GDR2>
 __device__ __forceinline__ PrepSrc prep_src(const ChunkArgs& a, size_t row0, int len, int I,
                                             int lane) {
   const int cq = lane & 31, hf = lane >> 5;
@@ -201,11 +202,15 @@ __device__ __forceinline__ PrepSrc prep_src(const ChunkArgs& a, size_t row0, int
   s.qk_off = ((16 * I + 8 * hf) * kDK + 4 * cq) * 2;
   s.g_off = PER_CHANNEL ? ((16 * I + 8 * hf) * kDK + 4 * cq) * 4 : (16 * I + 8 * hf) * 4;
   s.b_off = (16 * I + (lane & 15)) * 4;
+  if (GDR2) {
+    s.erase = make_rsrc(a.erase + row0 * kDK, (uint32_t)len * kDK * 4);
+    s.e_off = ((16 * I + 8 * hf) * kDK + 4 * cq) * 4;
+  }
   return s;
 }
 
 // Loads block I of the 64 tokens starting at c0 (rows past the chain read as zero).
-template <bool PER_CHANNEL>
+template <bool PER_CHANNEL, bool GDR2>
 __device__ __forceinline__ void load_block(BlockRegs& r, const PrepSrc& s, int c0) {
   const uint32_t qk = s.qk_off + (uint32_t)c0 * kDK * 2;
   const uint32_t go = s.g_off + (uint32_t)c0 * (PER_CHANNEL ? kDK * 4 : 4);
@@ -219,14 +224,19 @@ __device__ __forceinline__ void load_block(BlockRegs& r, const PrepSrc& s, int c
       const float gg = ld_b32(s.g, go + u * 4);
       r.g[u] = f32x4{gg, gg, gg, gg};
     }
+    if (GDR2) r.b[u] = ld_b128(s.erase, s.e_off + (uint32_t)c0 * kDK * 4 + u * kDK * 4);
   }
-  r.beta = ld_b32(s.beta, s.b_off + (uint32_t)c0 * 4);
+  // Gated Delta Rule-2 has no scalar gate: its erase gate sits in the key operand
+  r.beta = GDR2 ? 1.f : ld_b32(s.beta, s.b_off + (uint32_t)c0 * 4);
 }
 
 // Decay products of block I and its bf16 operands, written to LDS by one wavefront:
 // alpha = exp(g); P_t = exp(G_t - G_0) is the inclusive prefix product of alpha, E_t =
 // exp(G_16 - G_t) the product after t, tot = exp(G_16 - G_0), and k / P_t = k E_t / tot.
 // A lane holds 8 tokens of one half block; the halves exchange their products.
+// For Gated Delta Rule-2 the read-side operand is (b * k) P, b the erase gate: it serves
+// both the prediction (b * k)^T S and the strictly lower (b * k) (k / P)^T of the solve.
+template <bool GDR2>
 __device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const BlockRegs& r,
                                            int I, int lane) {
   const int cq = lane & 31, hf = lane >> 5;
@@ -258,7 +268,7 @@ __device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const Bl
     for (int j = 0; j < 4; ++j) {
       run[j] *= al[u][j];
       qr[j] = static_cast<float>(r.q[u][j]) * run[j];
-      kr[j] = static_cast<float>(r.k[u][j]) * run[j];
+      kr[j] = static_cast<float>(r.k[u][j]) * (GDR2 ? r.b[u][j] * run[j] : run[j]);
     }
     *reinterpret_cast<bf16x4*>(&st.qr[t][4 * cq]) = pack4(qr);
     *reinterpret_cast<bf16x4*>(&st.kr[t][4 * cq]) = pack4(kr);
@@ -360,6 +370,14 @@ __device__ __forceinline__ void load_values(bf16 (&vv)[4], rsrc_t v, uint32_t of
   for (int e = 0; e < 4; ++e) vv[e] = ld_b16(v, off + e * DV * 2);
 }
 
+// Write gates of one value column for the 16 tokens of block I (fp32, same layout as
+// load_values; off is the byte offset of token 16 I + 4 p in this column of the gates).
+template <int DV>
+__device__ __forceinline__ void load_gates(float (&ww)[4], rsrc_t w, uint32_t off) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ww[e] = ld_b32(w, off + e * DV * 4);
+}
+
 // Stores the outputs of chunk `step` that this state wavefront staged in LDS (its 16 nt
 // columns from cbase, 64 token rows) as 16-byte row pieces; rows past the chain are dropped.
 template <int DV>
@@ -379,7 +397,7 @@ __device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int s
 // straight-line instantiation (a tile count chosen at run time inside the loops would let
 // branches remove instructions that the wait states after the matrix-core products were
 // counted on).
-template <int NT, int DV>
+template <int NT, int DV, bool GDR2>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const TokenRange& tr,
                                            size_t row0, size_t state_off, int nsteps, int cbase,
                                            int lane, int rr, int p) {
@@ -405,11 +423,15 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
         S_acc[c][m][e] = a.s0 ? a.s0[state_off + (size_t)ch * DV + col[c]] : 0.f;
       }
   bf16 vv[NT][4][4];
+  float ww[NT][4][4];  // write gate of the values (Gated Delta Rule-2 only)
+  const rsrc_t wsrc = GDR2 ? make_rsrc(a.write + row0 * DV, (uint32_t)tr.len * DV * 4) : vsrc;
 #pragma unroll
   for (int c = 0; c < NT; ++c)
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 4; ++I) {
       load_values<DV>(vv[c][I], vsrc, voff[c] + I * 16 * DV * 2);
+      if (GDR2) load_gates<DV>(ww[c][I], wsrc, 2 * (voff[c] + I * 16 * DV * 2));
+    }
   // the initial state must be in registers before the loop, or the loop would wait
   // for these loads on every pass
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -447,10 +469,13 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
       for (int c = 0; c < NT; ++c) {
         f32x4 R;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[e] = bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
+        for (int e = 0; e < 4; ++e)
+          R[e] = GDR2 ? ww[c][I][e] * static_cast<float>(vv[c][I][e]) - X[c][e]
+                      : bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
         vp[c] = pack4(R);
         // the next 64 tokens' values of this block
         load_values<DV>(vv[c][I], vsrc, voff[c] + cbyte + (I * 16 + kC) * DV * 2);
+        if (GDR2) load_gates<DV>(ww[c][I], wsrc, 2 * (voff[c] + cbyte + (I * 16 + kC) * DV * 2));
       }
 #pragma unroll
       for (int c = 0; c < NT; ++c) vp[c] = pack4(mfma16(tI, vp[c], zero4()));
@@ -499,7 +524,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
   }
 }
 
-template <int NS, int NT, bool PER_CHANNEL>
+template <int NS, int NT, bool PER_CHANNEL, bool GDR2>
 __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int DV = 16 * NS * NT;
   __shared__ __align__(16) Smem sm;
@@ -531,23 +556,23 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
   if (prep_wave) {
     // ---------------- prep wavefront: block I of every 64 tokens
     const int I = wave;
-    const PrepSrc src = prep_src<PER_CHANNEL>(a, row0, tr.len, I, lane);
+    const PrepSrc src = prep_src<PER_CHANNEL, GDR2>(a, row0, tr.len, I, lane);
     BlockRegs r;
     if (nsteps > 0) {
-      load_block<PER_CHANNEL>(r, src, 0);
-      prep_block(sm.st[0], sm.kd, r, I, lane);
+      load_block<PER_CHANNEL, GDR2>(r, src, 0);
+      prep_block<GDR2>(sm.st[0], sm.kd, r, I, lane);
       wave_lds_fence();
       block_tiles(sm.st[0], sm.kd, I, rr, p);
-      if (nsteps > 1) load_block<PER_CHANNEL>(r, src, kC);
+      if (nsteps > 1) load_block<PER_CHANNEL, GDR2>(r, src, kC);
     }
     lds_barrier();
     for (int s = 0; s < nsteps; ++s) {
       if (s + 1 < nsteps) {
         Stage& st = sm.st[(s + 1) & 1];
-        prep_block(st, sm.kd, r, I, lane);
+        prep_block<GDR2>(st, sm.kd, r, I, lane);
         wave_lds_fence();
         block_tiles(st, sm.kd, I, rr, p);
-        if (s + 2 < nsteps) load_block<PER_CHANNEL>(r, src, (s + 2) * kC);
+        if (s + 2 < nsteps) load_block<PER_CHANNEL, GDR2>(r, src, (s + 2) * kC);
       }
       lds_barrier();
     }
@@ -559,12 +584,12 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     const int j = wave - kPrepWaves;
     if constexpr (NT > 1) {
       if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
-        state_role<NT / 2, DV>(sm, a, tr, row0, state_off, nsteps,
+        state_role<NT / 2, DV, GDR2>(sm, a, tr, row0, state_off, nsteps,
                                (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane, rr, p);
         return;
       }
     }
-    state_role<NT, DV>(sm, a, tr, row0, state_off, nsteps, 16 * NT * j, lane, rr, p);
+    state_role<NT, DV, GDR2>(sm, a, tr, row0, state_off, nsteps, 16 * NT * j, lane, rr, p);
   }
 }
 
@@ -661,8 +686,12 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
 
 template <int NS, int NT, bool PER_CHANNEL>
 hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
-  chunk_mfma_kernel<NS, NT, PER_CHANNEL>
-      <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
+  if (a.erase)
+    chunk_mfma_kernel<NS, NT, PER_CHANNEL, true>
+        <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
+  else
+    chunk_mfma_kernel<NS, NT, PER_CHANNEL, false>
+        <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -3,6 +3,9 @@
 // Per chain (sequence, head), following the decay-then-delta form of the page
 // "KDA 与 Gated DeltaNet：线性注意力怎样读写有限状态", section 2:
 //   S~ = Diag(alpha) S,  p = S~^T k,  d = beta (v - p),  S = S~ + k d^T,  o = S^T q.
+// Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2") reads along the
+// erase-gated key and gates the written values per channel: p = S~^T (b * k),
+// d = w * v - p; the rest is the same.
 // Since S^T q = S~^T q + (k^T q) d, one read of S gives both reductions p and
 // y = S~^T q; the state is then updated in registers and written back once. The
 // step is a pure HBM stream: 2 * dk * dv * 4 bytes of state traffic per chain
@@ -39,7 +42,7 @@ __device__ __forceinline__ void st_state(float4* p, float4 v) {
 
 // Workgroups of THREADS threads loop over the work items (chain, block of DVB value
 // columns) with a grid stride.
-template <int DK, int DV, int DVB, int THREADS, typename TIn, bool PER_CHANNEL>
+template <int DK, int DV, int DVB, int THREADS, typename TIn, bool PER_CHANNEL, bool GDR2>
 __global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
   constexpr int QUADS = DVB / 4;
   constexpr int RG = THREADS / QUADS;
@@ -50,6 +53,7 @@ __global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
   __shared__ float s_k[DK];
   __shared__ float s_q[DK];
   __shared__ float s_alpha[DK];
+  __shared__ float s_e[GDR2 ? DK : 1];  // erase-gated key (Gated Delta Rule-2)
   __shared__ float4 s_red_p[RG][QUADS];
   __shared__ float4 s_red_y[RG][QUADS];
   __shared__ float s_kq[THREADS / 64];
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
     s_k[i] = kk;
     s_q[i] = qq;
     s_alpha[i] = __expf(PER_CHANNEL ? a.g[(size_t)chain * DK + i] : a.g[chain]);
+    if (GDR2) s_e[i] = a.erase[(size_t)chain * DK + i] * kk;
     kq += kk * qq;
   }
   for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
     const float al = s_alpha[r];
     x.x *= al; x.y *= al; x.z *= al; x.w *= al;
     s[i] = x;
-    const float kr = s_k[r], qr = s_q[r];
+    const float kr = GDR2 ? s_e[r] : s_k[r], qr = s_q[r];
     p.x += x.x * kr; p.y += x.y * kr; p.z += x.z * kr; p.w += x.w * kr;
     y.x += x.x * qr; y.y += x.y * qr; y.z += x.z * qr; y.w += x.w * qr;
   }
@@ -117,12 +122,20 @@ __global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
   for (int w = 0; w < THREADS / 64; ++w) kqs += s_kq[w];
 
-  const float b = a.beta[chain];
   float4 d;
-  d.x = b * (to_f32(vp[4 * cq + 0]) - p.x);
-  d.y = b * (to_f32(vp[4 * cq + 1]) - p.y);
-  d.z = b * (to_f32(vp[4 * cq + 2]) - p.z);
-  d.w = b * (to_f32(vp[4 * cq + 3]) - p.w);
+  if (GDR2) {
+    const float* wp = a.write + (size_t)chain * DV + col0 + 4 * cq;
+    d.x = wp[0] * to_f32(vp[4 * cq + 0]) - p.x;
+    d.y = wp[1] * to_f32(vp[4 * cq + 1]) - p.y;
+    d.z = wp[2] * to_f32(vp[4 * cq + 2]) - p.z;
+    d.w = wp[3] * to_f32(vp[4 * cq + 3]) - p.w;
+  } else {
+    const float b = a.beta[chain];
+    d.x = b * (to_f32(vp[4 * cq + 0]) - p.x);
+    d.y = b * (to_f32(vp[4 * cq + 1]) - p.y);
+    d.z = b * (to_f32(vp[4 * cq + 2]) - p.z);
+    d.w = b * (to_f32(vp[4 * cq + 3]) - p.w);
+  }
 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -142,22 +155,27 @@ __global__ __launch_bounds__(THREADS) void decode_step_kernel(DecodeArgs a) {
   }
 }
 
+template <int DK, int DV, typename TIn, bool PER_CHANNEL>
+void launch_gates(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  constexpr int DVB = DV;
+  if (a.erase)
+    decode_step_kernel<DK, DV, DVB, kThreads, TIn, PER_CHANNEL, true>
+        <<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    decode_step_kernel<DK, DV, DVB, kThreads, TIn, PER_CHANNEL, false>
+        <<<grid, dim3(kThreads), 0, stream>>>(a);
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const DecodeArgs& a, bool bf16, bool per_channel, hipStream_t stream) {
-  constexpr int DVB = DV;
-  constexpr int THREADS = kThreads;
-  const int items = a.N * a.H * (DV / DVB);
-  const dim3 grid(items > kPersistGrid ? kPersistGrid : items), block(THREADS);
+  const int items = a.N * a.H;
+  const dim3 grid(items > kPersistGrid ? kPersistGrid : items);
   if (bf16) {
-    if (per_channel)
-      decode_step_kernel<DK, DV, DVB, THREADS, kda::bf16, true><<<grid, block, 0, stream>>>(a);
-    else
-      decode_step_kernel<DK, DV, DVB, THREADS, kda::bf16, false><<<grid, block, 0, stream>>>(a);
+    if (per_channel) launch_gates<DK, DV, kda::bf16, true>(a, grid, stream);
+    else launch_gates<DK, DV, kda::bf16, false>(a, grid, stream);
   } else {
-    if (per_channel)
-      decode_step_kernel<DK, DV, DVB, THREADS, float, true><<<grid, block, 0, stream>>>(a);
-    else
-      decode_step_kernel<DK, DV, DVB, THREADS, float, false><<<grid, block, 0, stream>>>(a);
+    if (per_channel) launch_gates<DK, DV, float, true>(a, grid, stream);
+    else launch_gates<DK, DV, float, false>(a, grid, stream);
   }
   return hipGetLastError();
 }

@@ -12,7 +12,9 @@ struct ChunkArgs {
   const void* k;
   const void* v;
   const float* g;
-  const float* beta;
+  const float* beta;   // [B, H, T]; unused with the Gated Delta Rule-2 gates below
+  const float* erase;  // Gated Delta Rule-2 erase gate [B, H, T, dk], or nullptr (KDA)
+  const float* write;  // Gated Delta Rule-2 write gate [B, H, T, dv] (with erase)
   const float* s0;     // [N, H, dk, dv] or nullptr
   float* sT;           // [N, H, dk, dv] or nullptr
   void* o;
@@ -38,7 +40,9 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   const float* g;
-  const float* beta;
+  const float* beta;   // [N, H]; unused with the Gated Delta Rule-2 gates below
+  const float* erase;  // [N, H, dk] or nullptr (KDA)
+  const float* write;  // [N, H, dv] (with erase)
   float* state;
   void* o;
   int N;

@@ -123,6 +123,41 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               const float* beta, float* state, void* o, int N, int H, int dk,
                               int dv, kda_dtype dt, kda_gate_mode gm, hipStream_t stream);
 
+/*
+ * Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2: Decoupling Erase and
+ * Write"): the scalar gate beta is replaced by a per-key-channel erase gate b_t and a
+ * per-value-channel write gate w_t. Per chain, decay first, then
+ *   S_t = S~ + k_t (w_t * v_t - S~^T (b_t * k_t))^T,  S~ = Diag(exp g_t) S_{t-1},
+ *   o_t = S_t^T q_t            (* elementwise)
+ * which is the residual z_t - S~^T e_t of the section's fast-weight view with
+ * e_t = b_t * k_t and z_t = w_t * v_t. b = beta 1 and w = beta 1 give kda_chunk_fwd.
+ *
+ * kda_gdr2_chunk_fwd takes every argument of kda_chunk_fwd (same layouts, workspace,
+ * errors and arithmetic), with beta replaced by
+ *   erase  float32 [B, H, T, dk], in [0, 1]  (read side: which key channels are erased)
+ *   write  float32 [B, H, T, dv], in [0, 1]  (write side: which value channels are written)
+ * NULL erase or write: KDA_ERR_INVALID_ARG. The chunkwise form is the one of
+ * kda_chunk_fwd with the erase-gated keys b * k on the read side (the prediction and the
+ * strictly lower matrix of the UT transform) and w * v in place of beta v.
+ */
+kda_status kda_gdr2_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                              const float* erase, const float* write,
+                              const float* initial_state, float* final_state, void* o,
+                              const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                              int dk, int dv, kda_dtype dt, kda_gate_mode gm, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gated Delta Rule-2 decode step: kda_recurrent_step with beta replaced by
+ *   erase  float32 [N, H, dk], write  float32 [N, H, dv]
+ * per chain: S~ = Diag(exp g) S; p = S~^T (b * k); S = S~ + k (w * v - p)^T; o = S^T q.
+ * NULL erase or write: KDA_ERR_INVALID_ARG; everything else as kda_recurrent_step.
+ */
+kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                                   const float* erase, const float* write, float* state,
+                                   void* o, int N, int H, int dk, int dv, kda_dtype dt,
+                                   kda_gate_mode gm, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -19,6 +19,8 @@ Distributions (the same for every workload unless stated):
   beta  = sigmoid(x), x ~ N(0, 1)
   g     = max(-5, -exp(x)), x ~ N(-3, 1)   (log of the decay alpha, per token)
   s0    ~ N(0, 0.02^2) where a workload has a random initial state
+  erase, write (gates = "gdr2" only) = sigmoid(x), x ~ N(0, 1) per element:
+        the Gated Delta Rule-2 gates, erase [B, H, T, dk] and write [B, H, T, dv]
 Every tensor is drawn in blocks of one (batch row, head) from its own counter-style
 seeded stream, numpy.random.default_rng([seed, tensor id, batch row, head]), so the
 values do not depend on how many threads fill the blocks; the sequence lengths and
@@ -53,6 +55,7 @@ class WorkloadConfig:
     num_seqs: int = 0       # > 0: packed variable-length sequences (B must be 1)
     pin_frac: float = 0.0   # fraction of (head, token) rows whose log-decay is pinned at -5
     seed: int = 0
+    gates: str = "beta"     # "beta" (one gate per token) or "gdr2" (erase [.., dk], write [.., dv])
 
     @property
     def n_chains(self) -> int:
@@ -175,6 +178,8 @@ class ChunkInputs:
     beta: np.ndarray
     s0: Optional[np.ndarray]
     cu_seqlens: Optional[np.ndarray]
+    erase: Optional[np.ndarray] = None   # [B, H, T, dk] (Gated Delta Rule-2)
+    write: Optional[np.ndarray] = None   # [B, H, T, dv]
 
     @property
     def n_seqs(self) -> int:
@@ -213,7 +218,11 @@ def make_chunk_inputs(cfg: WorkloadConfig) -> ChunkInputs:
     if cfg.pin_frac > 0:
         pin = np.random.default_rng([sd, 7]).random((B, H, T)) < cfg.pin_frac
         g[pin] = np.float32(G_FLOOR)
-    return ChunkInputs(cfg, q, k, v, g, beta, s0, cu)
+    erase = write = None
+    if cfg.gates == "gdr2":
+        erase = _blocks(sd, 8, (B, H), (T, dk), _sigmoid_normal)
+        write = _blocks(sd, 9, (B, H), (T, dv), _sigmoid_normal)
+    return ChunkInputs(cfg, q, k, v, g, beta, s0, cu, erase, write)
 
 
 @dataclass
@@ -223,6 +232,8 @@ class DecodeInputs:
     v: np.ndarray      # [N, H, dv]
     g: np.ndarray      # [N, H, dk] or [N, H]
     beta: np.ndarray   # [N, H]
+    erase: Optional[np.ndarray] = None   # [N, H, dk] (Gated Delta Rule-2)
+    write: Optional[np.ndarray] = None   # [N, H, dv]
 
 
 def decode_initial_state(cfg: WorkloadConfig) -> np.ndarray:
@@ -247,4 +258,8 @@ def decode_step_inputs(cfg: WorkloadConfig, step: int) -> DecodeInputs:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     beta = _sigmoid_normal(rng(3), (N, H))
     g = _log_decay(rng(4), (N, H, dk) if cfg.gate == "channel" else (N, H))
-    return DecodeInputs(q, k, v, g, beta)
+    erase = write = None
+    if cfg.gates == "gdr2":
+        erase = _sigmoid_normal(rng(5), (N, H, dk))
+        write = _sigmoid_normal(rng(6), (N, H, dv))
+    return DecodeInputs(q, k, v, g, beta, erase, write)

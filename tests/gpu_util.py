@@ -56,8 +56,12 @@ def run_chunk(x, dtype: str, initial_state=True, o_fill=None, schedule=True):
     o = None
     if o_fill is not None:
         o = torch.full(tuple(x.v.shape), o_fill, dtype=dt, device=dev())
-    o, sT = kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, o=o,
-                          schedule=schedule)
+    if x.erase is not None:   # Gated Delta Rule-2 gates
+        o, sT = kda.gdr2_chunk_fwd(q, k, v, g, up(x.erase), up(x.write), initial_state=s0,
+                                   cu_seqlens=cu, o=o, schedule=schedule)
+    else:
+        o, sT = kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, o=o,
+                              schedule=schedule)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), sT.cpu().numpy()
 
@@ -65,7 +69,8 @@ def run_chunk(x, dtype: str, initial_state=True, o_fill=None, schedule=True):
 def oracle_chains(x, chains=None, initial_state=True):
     return oracle.kda_forward(x.q, x.k, x.v, x.g, x.beta,
                               s0=x.s0 if initial_state else None,
-                              cu_seqlens=x.cu_seqlens, chains=chains)
+                              cu_seqlens=x.cu_seqlens, chains=chains,
+                              erase=x.erase, write=x.write)
 
 
 def check_chains(x, o, sT, ref, tol, what):

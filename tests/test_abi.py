@@ -89,6 +89,44 @@ def test_chunk_fwd_rejects(over, code):
     assert chunk_call(**over) == code
 
 
+def gdr2_chunk_call(**over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, erase=DUMMY, write=DUMMY,
+                initial_state=None, final_state=None, o=DUMMY, cu_seqlens=None, num_seqs=0,
+                B=1, H=2, T=64, dk=128, dv=128, dt=kda.KDA_BF16, gm=kda.KDA_GATE_PER_CHANNEL,
+                workspace=None, workspace_bytes=0, stream=None)
+    args.update(over)
+    return kda.kda_gdr2_chunk_fwd(*args.values())
+
+
+def gdr2_step_call(**over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, erase=DUMMY, write=DUMMY, state=DUMMY,
+                o=DUMMY, N=4, H=2, dk=128, dv=128, dt=kda.KDA_BF16,
+                gm=kda.KDA_GATE_PER_CHANNEL, stream=None)
+    args.update(over)
+    return kda.kda_gdr2_recurrent_step(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(erase=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(write=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(dv=48), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_gdr2_chunk_fwd_rejects(over, code):
+    assert gdr2_chunk_call(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(erase=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(write=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(state=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=256), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_gdr2_recurrent_step_rejects(over, code):
+    assert gdr2_step_call(**over) == code
+
+
 def step_call(**over):
     args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, beta=DUMMY, state=DUMMY, o=DUMMY, N=4,
                 H=2, dk=128, dv=128, dt=kda.KDA_BF16, gm=kda.KDA_GATE_PER_CHANNEL,

@@ -1,0 +1,132 @@
+"""GPU parity of the Gated Delta Rule-2 entry points (kda_gdr2_chunk_fwd,
+kda_gdr2_recurrent_step) against the fp64 oracle, through the C ABI.
+
+The erase gate b [.., dk] and the write gate w [.., dv] are drawn as sigmoid(N(0, 1))
+per element. Checked: every dtype, gate mode and head size on ragged sequences; the
+B2 H16 T4096 workload in full; the packed varlen T=65536 workload (the benchmark's
+launch configuration) on sampled chains; edge lengths; b = w = beta 1 against the
+KDA entry point; decode steps against the oracle and against one chunked forward.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_13_amd as kda
+import oracle
+from kda_workloads import CONFIGS, decode_initial_state, decode_step_inputs, make_chunk_inputs
+from tests.gpu_util import (DT, TOL, assert_close, check_chains, note, oracle_chains, run_chunk,
+                            up)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [(dtype, gate, dk, dv) for dtype in ("f32", "bf16") for gate in ("channel", "head")
+         for dk, dv in ((64, 64), (128, 128), (64, 128), (128, 64))]
+
+
+@pytest.mark.parametrize("dtype,gate,dk,dv", SMALL)
+def test_gdr2_small_ragged(dtype, gate, dk, dv):
+    cfg = CONFIGS[1].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=78,
+                             gates="gdr2")
+    note(f"gdr2 small {dtype} {gate} dk={dk} dv={dv}")
+    x = make_chunk_inputs(cfg)
+    o, sT = run_chunk(x, dtype)
+    check_chains(x, o, sT, oracle_chains(x), TOL[dtype], f"gdr2 small {dtype} {gate} {dk}x{dv}")
+
+
+def test_gdr2_b2_h16_t4096_full():
+    cfg = CONFIGS[1].replace(name="gdr2_bf16_b2_h16_t4096", gates="gdr2")
+    note(f"gdr2 parity {cfg.name}")
+    x = make_chunk_inputs(cfg)
+    o, sT = run_chunk(x, "bf16")
+    eo, es = check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], cfg.name)
+    print(f"{cfg.name}: err o={eo:.2e} S={es:.2e}")
+
+
+def test_gdr2_varlen_t65536_sampled_chains():
+    cfg = CONFIGS[3].replace(name="gdr2_bf16_varlen_h32_t65536", gates="gdr2")
+    note(f"gdr2 parity {cfg.name} (sampled chains)")
+    x = make_chunk_inputs(cfg)
+    o, sT = run_chunk(x, "bf16", o_fill=float("nan"))
+    assert np.all(np.isfinite(o)), "some output position was not written"
+    lens = np.diff(x.cu_seqlens)
+    rng = np.random.default_rng(4321)
+    chains = {(int(np.argmax(lens)), 1), (int(np.argmin(lens)), cfg.H - 2)}
+    while len(chains) < 6:
+        chains.add((int(rng.integers(cfg.num_seqs)), int(rng.integers(cfg.H))))
+    eo, es = check_chains(x, o, sT, oracle_chains(x, sorted(chains)), TOL["bf16"], cfg.name)
+    print(f"{cfg.name}: sampled {len(chains)} chains, err o={eo:.2e} S={es:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gdr2_varlen_edge_lengths(dtype):
+    lens = [0, 1, 63, 64, 65, 130, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(dtype=dtype, H=2, T=int(cu[-1]) + 3, num_seqs=0, pin_frac=0.05,
+                             seed=6, gates="gdr2")
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(4).standard_normal((len(lens), 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    note(f"gdr2 varlen edges {dtype}")
+    o, sT = run_chunk(x, dtype, o_fill=float("nan"))
+    assert np.all(np.isnan(o[0, :, cu[-1]:])), "tokens outside every sequence were written"
+    check_chains(x, o, sT, oracle_chains(x), TOL[dtype], f"gdr2 varlen edges {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gdr2_with_beta_gates_matches_kda(dtype):
+    """b = beta 1 and w = beta 1 reduce Gated Delta Rule-2 to KDA: both entry points agree
+    (to the rounding of the bf16 operands, which the two paths form differently)."""
+    cfg = CONFIGS[1].replace(dtype=dtype, B=1, H=4, T=333, seed=13, random_s0=True)
+    note(f"gdr2 = kda with beta gates {dtype}")
+    x = make_chunk_inputs(cfg)
+    o_kda, s_kda = run_chunk(x, dtype)
+    x.erase = np.repeat(x.beta[..., None], cfg.dk, axis=-1)
+    x.write = np.repeat(x.beta[..., None], cfg.dv, axis=-1)
+    o_g, s_g = run_chunk(x, dtype)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert_close(o_g, o_kda, tol, f"outputs {dtype}")
+    assert_close(s_g, s_kda, tol, f"states {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
+def test_gdr2_decode_small(dtype, gate, dk, dv):
+    cfg = CONFIGS[4].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=5, H=3, T=6, seed=31,
+                             gates="gdr2")
+    note(f"gdr2 decode {dtype} {gate} dk={dk} dv={dv}")
+    S0 = decode_initial_state(cfg)
+    state = up(S0)
+    ref = S0.astype(np.float64)
+    for step in range(cfg.T):
+        d = decode_step_inputs(cfg, step)
+        o = kda.gdr2_recurrent_step(up(d.q, DT[dtype]), up(d.k, DT[dtype]), up(d.v, DT[dtype]),
+                                    up(d.g), up(d.erase), up(d.write), state)
+        ro, ref = oracle.kda_decode_step(ref, d.q, d.k, d.v, d.g, d.beta, erase=d.erase,
+                                         write=d.write)
+        assert_close(o.float().cpu().numpy(), ro, TOL[dtype], f"decode o step {step}")
+    torch.cuda.synchronize()
+    assert_close(state.cpu().numpy(), ref, TOL[dtype], "decode state")
+
+
+def test_gdr2_decode_steps_equal_chunk_forward():
+    """T decode steps on the same tokens equal one chunked forward (the state is the
+    whole context), for the bf16 matrix-core chunk path."""
+    B, H, T, dk, dv = 2, 4, 70, 128, 128
+    cfg = CONFIGS[1].replace(B=B, H=H, T=T, seed=55, random_s0=True, gates="gdr2")
+    note("gdr2 decode steps vs chunk forward")
+    x = make_chunk_inputs(cfg)
+    o_chunk, s_chunk = run_chunk(x, "bf16")
+    bf = torch.bfloat16
+    state = up(x.s0)
+    outs = []
+    for t in range(T):
+        sl = (slice(None), slice(None), t)
+        outs.append(kda.gdr2_recurrent_step(
+            up(x.q[sl], bf), up(x.k[sl], bf), up(x.v[sl], bf), up(x.g[sl]),
+            up(x.erase[sl]), up(x.write[sl]), state).float().cpu().numpy())
+    o_steps = np.stack(outs, axis=2)
+    assert_close(o_steps, o_chunk, TOL["bf16"], "outputs")
+    assert_close(state.cpu().numpy(), s_chunk, TOL["bf16"], "state")
