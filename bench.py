@@ -42,19 +42,26 @@ CHUNK = 64
 # plain 1 GiB copy kernel in the same runs. It is reported only while the kernel source
 # is the one the counters were taken on (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3247025923,
-    "kernel_sha256": "3abea36dabd0e878220693ecd0fed13e0787e2370656cadf93c9d093c9120992",
+    "bytes": 3247135685,
+    "kernel_sha256": "8539ba78417a1033b40190864444042086c7b00b1556e48bf5b035fcc1687722",
+}
+MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
+    "bytes": 5386500000,
+    "kernel_sha256": "8539ba78417a1033b40190864444042086c7b00b1556e48bf5b035fcc1687722",
 }
 CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_13_amd", "csrc", "kda_chunk_mfma.hip")
 
 
-def measured_traffic():
+def measured_traffic(record=None):
+    """HBM bytes per launch from the committed rocprofv3 counters, or None once the chunk
+    kernel source differs from the one they were taken on."""
     import hashlib
-    if not MEASURED_TRAFFIC:
+    record = MEASURED_TRAFFIC if record is None else record
+    if not record:
         return None
     with open(CHUNK_KERNEL_SRC, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
-    return MEASURED_TRAFFIC["bytes"] if digest == MEASURED_TRAFFIC["kernel_sha256"] else None
+    return record["bytes"] if digest == record["kernel_sha256"] else None
 
 
 def log(msg: str) -> None:
@@ -70,18 +77,22 @@ def chunk_alg_flops_per_head_token(dk: int, dv: int, C: int = CHUNK) -> float:
 
 def chunk_alg_bytes(x) -> float:
     """Inputs read once and outputs written once: q, k, v (bf16), g (fp32 per channel),
-    beta (fp32), o (bf16), plus the initial / final state of every chain (fp32)."""
+    beta (fp32) or the Gated Delta Rule-2 gates (erase fp32 [dk], write fp32 [dv]),
+    o (bf16), plus the initial / final state of every chain (fp32)."""
     B, H, T, dk = x.q.shape
     dv = x.v.shape[-1]
-    per_tok = 2 * (2 * dk + dv) + 4 * (dk if x.g.ndim == 4 else 1) + 4 + 2 * dv
+    gates = 4 * (dk + dv) if x.erase is not None else 4
+    per_tok = 2 * (2 * dk + dv) + 4 * (dk if x.g.ndim == 4 else 1) + gates + 2 * dv
     n_chains = x.n_seqs * H
     state = 4 * dk * dv * n_chains * (2 if x.s0 is not None else 1)
     return float(per_tok * B * H * T + state)
 
 
-def decode_alg_bytes_per_step(N: int, H: int, dk: int, dv: int) -> float:
-    """State read and written once (fp32), q, k, v (bf16), g (fp32), beta, o (bf16)."""
-    per_chain = 2 * dk * dv * 4 + 2 * (2 * dk + dv) + 4 * dk + 4 + 2 * dv
+def decode_alg_bytes_per_step(N: int, H: int, dk: int, dv: int, gdr2: bool = False) -> float:
+    """State read and written once (fp32), q, k, v (bf16), g (fp32), beta or the Gated
+    Delta Rule-2 gates (erase [dk], write [dv], fp32), o (bf16)."""
+    gates = 4 * (dk + dv) if gdr2 else 4
+    per_chain = 2 * dk * dv * 4 + 2 * (2 * dk + dv) + 4 * dk + gates + 2 * dv
     return float(per_chain * N * H)
 
 
@@ -95,8 +106,13 @@ def bench_chunk(torch, kda, x, steps: int, warmup: int):
     o = torch.empty(tuple(x.v.shape), dtype=torch.bfloat16, device=dev)
     sT = torch.empty((x.n_seqs, x.q.shape[1], x.q.shape[3], x.v.shape[3]), dtype=torch.float32,
                      device=dev)
-    call = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, o=o,  # noqa
-                                 final_state=sT)
+    if x.erase is not None:
+        erase, write = up(x.erase), up(x.write)
+        call = lambda: kda.gdr2_chunk_fwd(q, k, v, g, erase, write, initial_state=s0,  # noqa
+                                          cu_seqlens=cu, o=o, final_state=sT)
+    else:
+        call = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu,  # noqa
+                                     o=o, final_state=sT)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -120,6 +136,10 @@ def bench_decode(torch, kda, cfg, reps: int = 5):
     vs = torch.empty((S, N, H, dv), dtype=torch.bfloat16, device=dev)
     gs = torch.empty((S, N, H, dk), dtype=torch.float32, device=dev)
     bs = torch.empty((S, N, H), dtype=torch.float32, device=dev)
+    gdr2 = cfg.gates == "gdr2"
+    if gdr2:
+        es = torch.empty((S, N, H, dk), dtype=torch.float32, device=dev)
+        ws = torch.empty((S, N, H, dv), dtype=torch.float32, device=dev)
     from concurrent.futures import ThreadPoolExecutor
     with ThreadPoolExecutor(8) as ex:
         for s, d in enumerate(ex.map(lambda i: decode_step_inputs(cfg, i), range(S))):
@@ -128,14 +148,23 @@ def bench_decode(torch, kda, cfg, reps: int = 5):
             vs[s].copy_(torch.from_numpy(d.v))
             gs[s].copy_(torch.from_numpy(d.g))
             bs[s].copy_(torch.from_numpy(d.beta))
+            if gdr2:
+                es[s].copy_(torch.from_numpy(d.erase))
+                ws[s].copy_(torch.from_numpy(d.write))
+
+    def step(s):
+        if gdr2:
+            kda.gdr2_recurrent_step(qs[s], ks[s], vs[s], gs[s], es[s], ws[s], state, o=o)
+        else:
+            kda.recurrent_step(qs[s], ks[s], vs[s], gs[s], bs[s], state, o=o)
     s_init = torch.from_numpy(decode_initial_state(cfg)).to(dev)
     state = torch.empty_like(s_init)
     o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
     log(f"decode inputs generated and resident in {time.time() - t0:.1f}s")
     stream = torch.cuda.current_stream(dev)
     state.copy_(s_init)
-    for s in range(8):  # warm-up
-        kda.recurrent_step(qs[s], ks[s], vs[s], gs[s], bs[s], state, o=o)
+    for s in range(min(8, S)):  # warm-up
+        step(s)
     times = []
     for _ in range(reps):
         state.copy_(s_init)
@@ -143,7 +172,7 @@ def bench_decode(torch, kda, cfg, reps: int = 5):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         for s in range(S):
-            kda.recurrent_step(qs[s], ks[s], vs[s], gs[s], bs[s], state, o=o)
+            step(s)
         ev1.record(stream)
         torch.cuda.synchronize()
         times.append(ev0.elapsed_time(ev1) / 1e3)
@@ -194,6 +223,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-gdr2", action="store_true",
+                    help="skip the Gated Delta Rule-2 measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -250,6 +281,33 @@ def main() -> int:
             "tokens_per_s": dcfg.B * dcfg.T / sec, "hbm_gbs": dgbs,
             "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
         log(f"decode: {sec / dcfg.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
+    if not args.no_gdr2:
+        # Gated Delta Rule-2 on the same workloads: vector erase / write gates
+        gcfg = cfg.replace(name="gdr2_bf16_varlen_h32_t65536", gates="gdr2")
+        t0 = time.time()
+        gx = make_chunk_inputs(gcfg)
+        log(f"generated {gcfg.name} in {time.time() - t0:.1f}s")
+        gms = bench_chunk(torch, kda, gx, args.steps, args.warmup)
+        gbytes = chunk_alg_bytes(gx)
+        ggbs = gbytes / (gms / 1e3) / 1e9
+        result["gdr2"] = {
+            "workload": gcfg.name, "ms_per_step": gms, "tokens_per_s": gcfg.T / (gms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(MEASURED_TRAFFIC_GDR2),
+                         "alg_bytes_per_launch": gbytes}}
+        log(f"gdr2 chunk_fwd: {gms:.3f} ms/step, {gcfg.T / gms / 1e3:.2f} M tokens/s, "
+            f"{ggbs:.0f} GB/s")
+        del gx
+        if not args.no_decode:
+            gd = CONFIGS[4].replace(name="gdr2_decode_n256_h32", T=64, gates="gdr2")
+            sec = bench_decode(torch, kda, gd)
+            per_step = decode_alg_bytes_per_step(gd.B, gd.H, gd.dk, gd.dv, gdr2=True)
+            dgbs = per_step * gd.T / sec / 1e9
+            result["gdr2"]["decode"] = {
+                "workload": gd.name, "steps": gd.T, "us_per_step": sec / gd.T * 1e6,
+                "hbm_gbs": dgbs, "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
+            log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_chains)
         log(f"cpu baseline: {result['cpu_baseline']}")

@@ -524,6 +524,18 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
   }
 }
 
+// Position `local` among the 2 n items of n split chains: groups of (up to) 8 chains list
+// their first halves, then their second halves, so the two halves of a chain are 8 items
+// apart. Workgroups are dispatched round-robin over the 8 XCDs, so both halves run on one
+// XCD and the second reads the chain's q, k, g through that XCD's L2.
+__host__ __device__ inline void split_item(uint32_t local, uint32_t n, uint32_t& chain,
+                                           uint32_t& part) {
+  const uint32_t group = local / 16, within = local % 16;
+  const uint32_t gsize = n - 8 * group < 8 ? n - 8 * group : 8;
+  chain = 8 * group + within % gsize;
+  part = 1 + within / gsize;
+}
+
 template <int NS, int NT, bool PER_CHANNEL, bool GDR2>
 __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int DV = 16 * NS * NT;
@@ -543,8 +555,10 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     chain = (int)(item >> 2);
     part = (int)(item & 3);
   } else if (NT > 1 && a.split_all) {
-    chain = blockIdx.x >> 1;
-    part = 1 + (blockIdx.x & 1);
+    uint32_t c, pt;
+    split_item(blockIdx.x, (uint32_t)(a.N * a.H), c, pt);
+    chain = (int)c;
+    part = (int)pt;
   }
   const int n = chain / a.H;
   const int h = chain % a.H;
@@ -604,6 +618,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
 // workgroup dispatch turns into longest-processing-time-first list scheduling.
 
 constexpr int kMaxPlanSeqs = 1024;  // sequences one scheduling workgroup sorts
+
 constexpr double kHalfCost = 0.88;  // time of a half-column item relative to its whole chain
 
 __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t* cu, int N, int H,
@@ -621,11 +636,13 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
   key[t] = c;
   seq[t] = t;
   __syncthreads();
-  // bitonic sort: more chunks first, then lower sequence index
-  for (int k = 2; k <= kMaxPlanSeqs; k <<= 1)
+  // bitonic sort of the first n2 >= N entries: more chunks first, then lower index
+  int n2 = 1;
+  while (n2 < N) n2 <<= 1;
+  for (int k = 2; k <= n2; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
       const int u = t ^ j;
-      if (u > t) {
+      if (t < n2 && u > t) {
         const bool t_first = key[t] > key[u] || (key[t] == key[u] && seq[t] < seq[u]);
         if (((t & k) == 0) != t_first) {
           const int k0 = key[t], s0 = seq[t];
@@ -677,9 +694,8 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
       if (ent_off[mid] <= i) lo = mid; else hi = mid - 1;
     }
     const uint32_t local = i - ent_off[lo];
-    const int parts = ent_parts[lo];
-    const uint32_t hh = local / parts;
-    const uint32_t part = parts == 2 ? 1 + local % 2 : 0;
+    uint32_t hh = local, part = 0;
+    if (ent_parts[lo] == 2) split_item(local, (uint32_t)H, hh, part);
     plan[1 + i] = (((uint32_t)ent_seq[lo] * H + hh) << 2) | part;
   }
 }

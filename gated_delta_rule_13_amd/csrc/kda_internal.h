@@ -29,8 +29,8 @@ struct ChunkArgs {
   // ((n * H + h) << 2) | part with part 0 = all value columns, 1 / 2 = first / second half.
   uint32_t* plan;
   int cus;             // compute units of the device (sizes the schedule)
-  // Without a work list: split every chain's value columns over two workgroups
-  // (item 2 c + i is half i + 1 of chain c). Chosen on the host for equal-length batches.
+  // Without a work list: split every chain's value columns over two workgroups (the two
+  // halves of a chain 8 items apart). Chosen on the host for equal-length batches.
   int split_all;
 };
 
