@@ -344,6 +344,49 @@ def pin_gdr2_erase_direction(impl):
     _close(np.delete(d, 3, axis=0), np.zeros((dk - 1, dv)), 1e-12, "unread channel")
 
 
+# ---------------------------------------------------------------------------------
+# Prologue / epilogue (oracle/gates.py): closed forms and special cases.
+
+def pins_gates():
+    """Pins of oracle/gates.py (raises AssertionError)."""
+    from oracle import gates as G
+    # L2Norm: a 3-4-5 triangle, unit length, scale invariance, the zero vector stays 0
+    _close(G.l2norm(np.array([3.0, 4.0])), np.array([0.6, 0.8]), 1e-7, "l2norm 3-4-5")
+    x = np.random.default_rng(71).standard_normal((5, 128)) * 7.0
+    _close(np.linalg.norm(G.l2norm(x), axis=-1), np.ones(5), 1e-9, "l2norm unit")
+    _close(G.l2norm(3.5 * x), G.l2norm(x), 1e-9, "l2norm scale")
+    assert np.all(G.l2norm(np.zeros(8)) == 0.0)
+    # softplus: log 2 at 0, -> x for large x, -> exp(x) for very negative x, odd part x
+    _close(G.softplus(0.0), np.log(2.0), 1e-15, "softplus(0)")
+    _close(G.softplus(60.0), 60.0, 1e-15, "softplus(60)")
+    _close(G.softplus(-40.0), np.exp(-40.0), 1e-15, "softplus(-40)")
+    t = np.linspace(-30, 30, 61)
+    _close(G.softplus(t) - G.softplus(-t), t, 1e-12, "softplus(x) - softplus(-x) = x")
+    # decay gate: -exp(A_log) softplus(dt_bias) at u = 0; never positive; head scaling
+    A_log = np.log(np.array([0.5, 2.0]))
+    dt_bias = np.linspace(-3, 3, 2 * 4)
+    g = G.decay_gate(np.zeros((1, 2, 3, 4)), A_log, dt_bias)
+    want = -np.array([0.5, 2.0])[:, None] * np.log1p(np.exp(dt_bias.reshape(2, 4)))
+    _close(g[0, :, 0, :], want, 1e-12, "decay gate at u = 0")
+    u = np.random.default_rng(72).standard_normal((2, 2, 5, 4)) * 10
+    assert np.all(G.decay_gate(u, A_log, dt_bias) <= 0.0)
+    # sigmoid: 1/2 at 0, symmetry, the logistic function
+    _close(G.sigmoid(0.0), 0.5, 1e-15, "sigmoid(0)")
+    _close(G.sigmoid(t) + G.sigmoid(-t), np.ones_like(t), 1e-12, "sigmoid symmetry")
+    _close(G.sigmoid(1.3), 1.0 / (1.0 + np.exp(-1.3)), 1e-15, "sigmoid(1.3)")
+    # epilogue: a constant row c gives sign(c) w / sqrt(1 + eps / c^2) * sigmoid(z);
+    # z = 0 halves; invariant to the scale of o (up to eps); RMS of the result = weight
+    w = np.linspace(0.5, 1.5, 16)
+    o = np.full((1, 16), -3.0)
+    _close(G.epilogue(o, np.zeros((1, 16)), w, 1e-6), -0.5 * w / np.sqrt(1 + 1e-6 / 9),
+           1e-12, "epilogue constant row")
+    o = np.random.default_rng(73).standard_normal((4, 16))
+    z = np.random.default_rng(74).standard_normal((4, 16))
+    _close(G.epilogue(o * 40.0, z, w, 0.0), G.epilogue(o, z, w, 0.0), 1e-12, "epilogue scale")
+    y = G.epilogue(o, np.full_like(z, 50.0), np.ones(16), 0.0)
+    _close(np.sqrt(np.mean(y * y, axis=-1)), np.ones(4), 1e-12, "epilogue unit RMS")
+
+
 ALL_PINS = [
     pin_basis_key_overwrite,
     pin_chunked_equals_recurrence,

@@ -85,3 +85,24 @@ def test_mutant_fails_a_pin(mut):
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"mutant {mut} passed every pin"
+
+
+GATE_MUTANTS = {
+    "l2norm_without_sqrt": ("l2norm", lambda G: lambda x: np.asarray(x, float) / (
+        np.sum(np.asarray(x, float) ** 2, axis=-1, keepdims=True) + G.EPS_L2)),
+    "softplus_as_relu": ("softplus", lambda G: lambda x: np.maximum(np.asarray(x, float), 0.0)),
+    "rms_as_sum": ("epilogue", lambda G: lambda o, z, w, eps: G.sigmoid(z) * np.asarray(o) / np.sqrt(
+        np.sum(np.asarray(o) ** 2, axis=-1, keepdims=True) + eps) * w),
+    "gate_on_input": ("epilogue", lambda G: lambda o, z, w, eps: G.sigmoid(o) * np.asarray(z) / np.sqrt(
+        np.mean(np.asarray(z) ** 2, axis=-1, keepdims=True) + eps) * w),
+}
+
+
+@pytest.mark.parametrize("mut", sorted(GATE_MUTANTS))
+def test_gate_mutant_fails_a_pin(mut, monkeypatch):
+    from oracle import gates as G
+    name, make = GATE_MUTANTS[mut]
+    monkeypatch.setattr(G, name, make(G))
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            pins.pins_gates()

@@ -85,3 +85,7 @@ def test_decode_step_equals_one_token_forward():
                                     g[n, h][None], beta[n, h][None], s0=S[n, h])
             np.testing.assert_allclose(o[n, h], oo[0], rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(S1[n, h], SS, rtol=1e-12, atol=1e-12)
+
+
+def test_gates_pins():
+    pins.pins_gates()
