@@ -14,6 +14,9 @@ Printed (one JSON line on stdout):
   mfma           the same kernel's algorithmic flops against the bf16 MFMA peak
   decode         kda_recurrent_step on 256 sequences x 32 heads, 512 consecutive
                  steps on a resident fp32 state: tokens/s and HBM GB/s
+  gdr2           the Gated Delta Rule-2 forward and decode step on the same workloads
+  gates          the fused prologue (L2Norm, decay gate, sigmoid) and epilogue (gated
+                 RMSNorm) on the chunk workload's rows, against the HBM roofline
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
 """
 
@@ -94,6 +97,78 @@ def decode_alg_bytes_per_step(N: int, H: int, dk: int, dv: int, gdr2: bool = Fal
     gates = 4 * (dk + dv) if gdr2 else 4
     per_chain = 2 * dk * dv * 4 + 2 * (2 * dk + dv) + 4 * dk + gates + 2 * dv
     return float(per_chain * N * H)
+
+
+def prologue_alg_bytes(B: int, H: int, T: int, dk: int, qk_bytes: int = 2) -> float:
+    """q, k read and written (bf16), u read and g written (fp32 per channel), the beta
+    pre-activation read and beta written (fp32), plus A_log and dt_bias once."""
+    per_row = 4 * dk * qk_bytes + 2 * 4 * dk + 2 * 4
+    return float(per_row * B * H * T + 4 * H * (1 + dk))
+
+
+def epilogue_alg_bytes(B: int, H: int, T: int, dv: int, o_bytes: int = 2) -> float:
+    """o and z read, the gated output written (bf16), plus the RMSNorm weight once."""
+    return float(3 * o_bytes * dv * B * H * T + 4 * dv)
+
+
+def time_calls(torch, call, steps: int, warmup: int) -> float:
+    """Average milliseconds per call, HIP events on the launch stream."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def bench_gates(torch, kda, cfg, steps: int, warmup: int):
+    """The fused prologue and epilogue around the operator on the workload's B, H, T."""
+    from kda_workloads import make_gate_inputs
+    dev = torch.device("cuda:0")
+    up = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)  # noqa
+    t0 = time.time()
+    x = make_gate_inputs(cfg)
+    bf = torch.bfloat16
+    q_in, k_in, z = up(x.q_in, bf), up(x.k_in, bf), up(x.z, bf)
+    u, A_log, dt_bias, beta_in, w = (up(a) for a in (x.u, x.A_log, x.dt_bias, x.beta_in,
+                                                      x.weight))
+    del x
+    log(f"gate inputs generated and resident in {time.time() - t0:.1f}s")
+    q, k = torch.empty_like(q_in), torch.empty_like(k_in)
+    g, beta = torch.empty_like(u), torch.empty_like(beta_in)
+    o = torch.empty_like(z)
+    st = kda.load_library()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    B, H, T, dk = q_in.shape
+    dv = z.shape[-1]
+
+    def prologue():
+        rc = st.kda_prologue(q_in.data_ptr(), k_in.data_ptr(), u.data_ptr(), A_log.data_ptr(),
+                             dt_bias.data_ptr(), beta_in.data_ptr(), q.data_ptr(), k.data_ptr(),
+                             g.data_ptr(), beta.data_ptr(), B, H, T, dk, kda.KDA_BF16, stream)
+        if rc != kda.KDA_OK:
+            raise RuntimeError(f"kda_prologue returned {rc}")
+
+    def epilogue():
+        rc = st.kda_epilogue(q.data_ptr(), z.data_ptr(), w.data_ptr(), 1e-6, o.data_ptr(),
+                             B, H, T, dv, kda.KDA_BF16, stream)
+        if rc != kda.KDA_OK:
+            raise RuntimeError(f"kda_epilogue returned {rc}")
+    out = {}
+    for name, call, nbytes in (("prologue", prologue, prologue_alg_bytes(B, H, T, dk)),
+                               ("epilogue", epilogue, epilogue_alg_bytes(B, H, T, dv))):
+        ms = time_calls(torch, call, steps, warmup)
+        gbs = nbytes / (ms / 1e3) / 1e9
+        out[name] = {"us_per_launch": ms * 1e3, "roofline": {
+            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "alg_bytes_per_launch": nbytes}}
+        log(f"{name}: {ms * 1e3:.1f} us/launch, {gbs:.0f} GB/s")
+    return out
 
 
 def bench_chunk(torch, kda, x, steps: int, warmup: int):
@@ -225,6 +300,8 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-gdr2", action="store_true",
                     help="skip the Gated Delta Rule-2 measurements")
+    ap.add_argument("--no-gates", action="store_true",
+                    help="skip the prologue / epilogue measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -308,6 +385,9 @@ def main() -> int:
                 "workload": gd.name, "steps": gd.T, "us_per_step": sec / gd.T * 1e6,
                 "hbm_gbs": dgbs, "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
+    if not args.no_gates:
+        result["gates"] = dict(workload=cfg.name, **bench_gates(torch, kda, cfg, args.steps,
+                                                                 args.warmup))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_chains)
         log(f"cpu baseline: {result['cpu_baseline']}")

@@ -30,7 +30,8 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_PER_CHANNEL, KDA_GATE_PER_HEAD = 0, 1
 
 EXPORTED_SYMBOLS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
-                    "kda_status_string", "kda_gdr2_chunk_fwd", "kda_gdr2_recurrent_step")
+                    "kda_status_string", "kda_gdr2_chunk_fwd", "kda_gdr2_recurrent_step",
+                    "kda_prologue", "kda_epilogue")
 
 _lib = None
 
@@ -60,6 +61,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_gdr2_chunk_fwd.restype = I
     lib.kda_gdr2_recurrent_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.kda_gdr2_recurrent_step.restype = I
+    lib.kda_prologue.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.kda_prologue.restype = I
+    lib.kda_epilogue.argtypes = [P, P, P, ctypes.c_float, P, I, I, I, I, I, P]
+    lib.kda_epilogue.restype = I
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [I]
@@ -102,6 +107,17 @@ def kda_gdr2_recurrent_step(q, k, v, g, erase, write, state, o, N, H, dk, dv, dt
                             stream) -> int:
     return int(load_library().kda_gdr2_recurrent_step(q, k, v, g, erase, write, state, o, N,
                                                       H, dk, dv, dt, gm, stream))
+
+
+def kda_prologue(q_in, k_in, u, A_log, dt_bias, beta_in, q_out, k_out, g_out, beta_out, B, H, T,
+                 dk, dt, stream) -> int:
+    return int(load_library().kda_prologue(q_in, k_in, u, A_log, dt_bias, beta_in, q_out,
+                                           k_out, g_out, beta_out, B, H, T, dk, dt, stream))
+
+
+def kda_epilogue(o_in, z, weight, eps, o_out, B, H, T, dv, dt, stream) -> int:
+    return int(load_library().kda_epilogue(o_in, z, weight, float(eps), o_out, B, H, T, dv, dt,
+                                           stream))
 
 
 # ----------------------------------------------------------------------- torch helpers
@@ -277,3 +293,52 @@ def gdr2_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     """Gated Delta Rule-2 decode step (see ``kda_gdr2_recurrent_step``): erase float32
     [N, H, dk], write float32 [N, H, dv] in place of beta."""
     return _step(q, k, v, g, (erase, write), state, o)
+
+
+def prologue(q_in: torch.Tensor, k_in: torch.Tensor, u: torch.Tensor, A_log: torch.Tensor,
+             dt_bias: torch.Tensor, beta_in: Optional[torch.Tensor] = None,
+             inplace: bool = False):
+    """Fused prologue (see ``kda_prologue``): q_in, k_in [B, H, T, dk] (bf16 or fp32),
+    u float32 [B, H, T, dk], A_log float32 [H], dt_bias float32 [H, dk] (or [H * dk]),
+    beta_in float32 [B, H, T] or None. Returns (q, k, g, beta); with ``inplace`` q, k, g
+    and beta overwrite q_in, k_in, u and beta_in."""
+    B, H, T, dk = q_in.shape
+    dev = q_in.device
+    dt = _dtype_code(q_in)
+    _check(q_in, "q_in", q_in.dtype, dev)
+    _check(k_in, "k_in", q_in.dtype, dev)
+    for t, n in ((u, "u"), (A_log, "A_log"), (dt_bias, "dt_bias")):
+        _check(t, n, torch.float32, dev)
+    _check(beta_in, "beta_in", torch.float32, dev)
+    if k_in.shape != q_in.shape or u.shape != q_in.shape or A_log.numel() != H \
+            or dt_bias.numel() != H * dk or (beta_in is not None and beta_in.shape != (B, H, T)):
+        raise ValueError("inconsistent prologue shapes")
+    q = q_in if inplace else torch.empty_like(q_in)
+    k = k_in if inplace else torch.empty_like(k_in)
+    g = u if inplace else torch.empty_like(u)
+    beta = None if beta_in is None else (beta_in if inplace else torch.empty_like(beta_in))
+    st = kda_prologue(_ptr(q_in), _ptr(k_in), _ptr(u), _ptr(A_log), _ptr(dt_bias), _ptr(beta_in),
+                      _ptr(q), _ptr(k), _ptr(g), _ptr(beta), B, H, T, dk, dt, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_prologue")
+    return q, k, g, beta
+
+
+def epilogue(o_in: torch.Tensor, z: torch.Tensor, weight: Optional[torch.Tensor] = None,
+             eps: float = 1e-6, inplace: bool = False) -> torch.Tensor:
+    """Fused epilogue (see ``kda_epilogue``): Sigmoid(z) * RMSNorm(o_in) * weight per head
+    over dv. o_in, z [B, H, T, dv] (same dtype); weight float32 [dv] or None."""
+    B, H, T, dv = o_in.shape
+    dev = o_in.device
+    dt = _dtype_code(o_in)
+    _check(o_in, "o_in", o_in.dtype, dev)
+    _check(z, "z", o_in.dtype, dev)
+    _check(weight, "weight", torch.float32, dev)
+    if z.shape != o_in.shape or (weight is not None and weight.numel() != dv):
+        raise ValueError("inconsistent epilogue shapes")
+    out = o_in if inplace else torch.empty_like(o_in)
+    st = kda_epilogue(_ptr(o_in), _ptr(z), _ptr(weight), eps, _ptr(out), B, H, T, dv, dt,
+                      _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_epilogue")
+    return out

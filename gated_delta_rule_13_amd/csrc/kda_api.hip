@@ -146,4 +146,39 @@ kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, 
                              gm, stream);
 }
 
+kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, const float* A_log,
+                        const float* dt_bias, const float* beta_in, void* q_out, void* k_out,
+                        float* g_out, float* beta_out, int B, int H, int T, int dk,
+                        kda_dtype dt, hipStream_t stream) {
+  if (!q_in || !k_in || !u || !A_log || !dt_bias || !q_out || !k_out || !g_out)
+    return KDA_ERR_INVALID_ARG;
+  if (!beta_in != !beta_out) return KDA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || T <= 0 || dk <= 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (!supported_dim(dk)) return KDA_ERR_UNSUPPORTED;
+  if ((long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
+  kda::PrologueArgs a;
+  a.q_in = q_in; a.k_in = k_in; a.u = u; a.A_log = A_log; a.dt_bias = dt_bias;
+  a.beta_in = beta_in; a.q_out = q_out; a.k_out = k_out; a.g_out = g_out; a.beta_out = beta_out;
+  a.B = B; a.H = H; a.T = T;
+  const hipError_t err = kda::launch_prologue(a, dk, dt == KDA_BF16, stream);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, float eps,
+                        void* o_out, int B, int H, int T, int dv, kda_dtype dt,
+                        hipStream_t stream) {
+  if (!o_in || !z || !o_out) return KDA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !(eps < 1e30f)) return KDA_ERR_INVALID_ARG;  // also rejects NaN
+  if (B <= 0 || H <= 0 || T <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (!supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+  if ((long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
+  kda::EpilogueArgs a;
+  a.o_in = o_in; a.z = z; a.weight = weight; a.eps = eps; a.o_out = o_out;
+  a.B = B; a.H = H; a.T = T;
+  const hipError_t err = kda::launch_epilogue(a, dv, dt == KDA_BF16, stream);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

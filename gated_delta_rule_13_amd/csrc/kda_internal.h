@@ -49,6 +49,31 @@ struct DecodeArgs {
   int H;
 };
 
+// Arguments of one kda_prologue call (every pointer a device array, head-major).
+struct PrologueArgs {
+  const void* q_in;       // [B, H, T, dk]
+  const void* k_in;
+  const float* u;         // [B, H, T, dk] decay pre-activation
+  const float* A_log;     // [H]
+  const float* dt_bias;   // [H, dk]
+  const float* beta_in;   // [B, H, T] or nullptr
+  void* q_out;
+  void* k_out;
+  float* g_out;           // [B, H, T, dk]
+  float* beta_out;        // [B, H, T] (with beta_in)
+  int B, H, T;
+};
+
+// Arguments of one kda_epilogue call.
+struct EpilogueArgs {
+  const void* o_in;       // [B, H, T, dv]
+  const void* z;          // [B, H, T, dv] output-gate pre-activation
+  const float* weight;    // [dv] or nullptr (= 1)
+  float eps;
+  void* o_out;
+  int B, H, T;
+};
+
 // Each launcher returns the launch's hipError_t; `bf16` selects the element type of
 // q, k, v, o, `per_channel` the gate layout. Unsupported (dk, dv) return
 // hipErrorInvalidValue (the host validates before calling).
@@ -57,6 +82,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, bool pe
 hipError_t launch_chunk_f32(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool per_channel, hipStream_t stream);
 bool chunk_mfma_supports(int dk, int dv, int T);
+hipError_t launch_prologue(const PrologueArgs& a, int dk, bool bf16, hipStream_t stream);
+hipError_t launch_epilogue(const EpilogueArgs& a, int dv, bool bf16, hipStream_t stream);
 // Bytes of workspace the matrix-core path uses for its schedule (0: no schedule).
 size_t chunk_plan_bytes(int N, int H, int dv);
 

@@ -158,6 +158,44 @@ kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, 
                                    void* o, int N, int H, int dk, int dv, kda_dtype dt,
                                    kda_gate_mode gm, hipStream_t stream);
 
+/*
+ * Prologue: the steps that turn per-token pre-activations into the operator's inputs,
+ * fused into one pass ("Token Mixer I", section "The Kimi Linear Model Architecture",
+ * neural parameterization; the decay function of the page "阅读笔记: Kimi Delta
+ * Attention", section 6). Per head h and token:
+ *   q_out = q_in / sqrt(sum q_in^2 + 1e-6), k_out likewise      (L2Norm over dk)
+ *   g_out = max(-exp(A_log[h]) * softplus(u + dt_bias[h, :]), -5)  (fp32 log-decay, the
+ *           g of kda_chunk_fwd; -5 is KDA's lower bound g_min, page "【轻量化复刻大模型】
+ *           线性注意力（Linear Attention）", section 3.1)
+ *   beta_out = Sigmoid(beta_in)                                 (optional)
+ *
+ *   q_in, k_in, q_out, k_out  [B, H, T, dk], dtype dt; q_out / k_out may equal q_in / k_in
+ *   u, g_out   float32 [B, H, T, dk] (may be the same buffer)
+ *   A_log      float32 [H]        dt_bias  float32 [H, dk]
+ *   beta_in, beta_out  float32 [B, H, T], both NULL or both set (may be the same buffer)
+ *   dk         64 or 128 (else KDA_ERR_UNSUPPORTED)
+ * Any other NULL array: KDA_ERR_INVALID_ARG. With cu_seqlens packing, pass B = 1 and the
+ * packed T. fp32 arithmetic throughout; bf16 outputs are rounded once.
+ */
+kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, const float* A_log,
+                        const float* dt_bias, const float* beta_in, void* q_out, void* k_out,
+                        float* g_out, float* beta_out, int B, int H, int T, int dk,
+                        kda_dtype dt, hipStream_t stream);
+
+/*
+ * Epilogue: the per-head RMSNorm and output gate applied to the operator's output before
+ * the output projection (same section), fused into one pass. Per head and token:
+ *   o_out = Sigmoid(z) * o_in / sqrt(mean(o_in^2) + eps) * weight     (over dv)
+ *
+ *   o_in, z, o_out  [B, H, T, dv], dtype dt; o_out may equal o_in
+ *   weight          float32 [dv] (shared by the heads), or NULL for 1
+ *   eps             finite, >= 0 (else KDA_ERR_INVALID_ARG)
+ *   dv              64 or 128 (else KDA_ERR_UNSUPPORTED)
+ */
+kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, float eps,
+                        void* o_out, int B, int H, int T, int dv, kda_dtype dt,
+                        hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -11,10 +11,12 @@ from .generate import (  # noqa: F401
     CONFIGS,
     ChunkInputs,
     DecodeInputs,
+    GateInputs,
     WorkloadConfig,
     bf16_round,
     decode_step_inputs,
     decode_initial_state,
     make_chunk_inputs,
+    make_gate_inputs,
     varlen_lengths,
 )

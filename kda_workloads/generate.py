@@ -21,6 +21,7 @@ Distributions (the same for every workload unless stated):
   s0    ~ N(0, 0.02^2) where a workload has a random initial state
   erase, write (gates = "gdr2" only) = sigmoid(x), x ~ N(0, 1) per element:
         the Gated Delta Rule-2 gates, erase [B, H, T, dk] and write [B, H, T, dv]
+  prologue / epilogue pre-activations: see make_gate_inputs
 Every tensor is drawn in blocks of one (batch row, head) from its own counter-style
 seeded stream, numpy.random.default_rng([seed, tensor id, batch row, head]), so the
 values do not depend on how many threads fill the blocks; the sequence lengths and
@@ -263,3 +264,39 @@ def decode_step_inputs(cfg: WorkloadConfig, step: int) -> DecodeInputs:
         erase = _sigmoid_normal(rng(5), (N, H, dk))
         write = _sigmoid_normal(rng(6), (N, H, dv))
     return DecodeInputs(q, k, v, g, beta, erase, write)
+
+
+@dataclass
+class GateInputs:
+    """Pre-activations of the prologue and the epilogue (head-major, float32; the q / k /
+    z values are bf16-rounded for bf16 workloads)."""
+    q_in: np.ndarray      # [B, H, T, dk] before L2Norm
+    k_in: np.ndarray
+    u: np.ndarray         # [B, H, T, dk] decay pre-activation
+    A_log: np.ndarray     # [H]
+    dt_bias: np.ndarray   # [H, dk]
+    beta_in: np.ndarray   # [B, H, T]
+    z: np.ndarray         # [B, H, T, dv] output-gate pre-activation
+    weight: np.ndarray    # [dv] RMSNorm weight
+
+
+def make_gate_inputs(cfg: WorkloadConfig) -> GateInputs:
+    """Synthetic pre-activations in the ranges of a Mamba-style parameterization: raw q, k,
+    u, z and the beta pre-activation ~ N(0, 1); dt_bias = log(expm1(dt)) with dt
+    log-uniform in [1e-3, 1e-1]; A_log = log U[1, 16]; weight = 1 + N(0, 0.1^2). With these
+    the prologue's log-decay has median about -0.09, 95% of it in [-1.6, 0], and about
+    0.5% of it on the lower bound -5."""
+    B, H, T, dk, dv, sd = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.seed
+    q_in = _blocks(sd, 10, (B, H), (T, dk), _normal)
+    k_in = _blocks(sd, 11, (B, H), (T, dk), _normal)
+    z = _blocks(sd, 12, (B, H), (T, dv), _normal)
+    if cfg.dtype == "bf16":
+        q_in, k_in, z = bf16_round(q_in), bf16_round(k_in), bf16_round(z)
+    u = _blocks(sd, 13, (B, H), (T, dk), _normal)
+    beta_in = _blocks(sd, 14, (B, H), (T,), _normal)
+    rng = np.random.default_rng([sd, 15])
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(H, dk)))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    A_log = np.log(rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    weight = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    return GateInputs(q_in, k_in, u, A_log, dt_bias, beta_in, z, weight)

@@ -9,9 +9,11 @@ Sources ("Token Mixer I", section "The Kimi Linear Model Architecture", neural
 parameterization; page "阅读笔记: Kimi Delta Attention", section 6, model architecture):
   q, k   = L2Norm(.) of the (short-convolved, Swish-activated) projections, per head and
            token, over the key channels;
-  log a  = -exp(A_log) * softplus(u + dt_bias), u the low-rank projection of the token,
-           A_log [H], dt_bias [H * dk]; computed in fp32 before the operator ("Token Mixer
-           I", section "Gated DeltaNet-2", decay parameterization);
+  log a  = max(-exp(A_log) * softplus(u + dt_bias), g_min), u the low-rank projection of
+           the token, A_log [H], dt_bias [H * dk]; computed in fp32 before the operator
+           ("Token Mixer I", section "Gated DeltaNet-2", decay parameterization), with the
+           lower bound g_min = -5 of KDA's decay (page "【轻量化复刻大模型】线性注意力（Linear
+           Attention）", knowledge map of section 3.1, item 7a);
   beta   = Sigmoid(.) of its projection;
   out    = Sigmoid(z) * RMSNorm(o), per head over the value channels, z the low-rank
            projection of the output gate.
@@ -25,6 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 EPS_L2 = 1e-6
+G_MIN = -5.0
 
 
 def l2norm(x):
@@ -45,13 +48,13 @@ def sigmoid(x):
 
 
 def decay_gate(u, A_log, dt_bias):
-    """log-decay g = -exp(A_log[h]) * softplus(u + dt_bias[h, c]) for u [B, H, T, dk],
-    A_log [H], dt_bias [H * dk] (head-major)."""
+    """log-decay g = max(-exp(A_log[h]) * softplus(u + dt_bias[h, c]), G_MIN) for
+    u [B, H, T, dk], A_log [H], dt_bias [H * dk] (head-major)."""
     u = np.asarray(u, dtype=np.float64)
     B, H, T, dk = u.shape
     a = np.exp(np.asarray(A_log, dtype=np.float64)).reshape(1, H, 1, 1)
     b = np.asarray(dt_bias, dtype=np.float64).reshape(1, H, 1, dk)
-    return -a * softplus(u + b)
+    return np.maximum(-a * softplus(u + b), G_MIN)
 
 
 def prologue(q_in, k_in, u, A_log, dt_bias, beta_in):

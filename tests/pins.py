@@ -364,12 +364,16 @@ def pins_gates():
     _close(G.softplus(t) - G.softplus(-t), t, 1e-12, "softplus(x) - softplus(-x) = x")
     # decay gate: -exp(A_log) softplus(dt_bias) at u = 0; never positive; head scaling
     A_log = np.log(np.array([0.5, 2.0]))
-    dt_bias = np.linspace(-3, 3, 2 * 4)
+    dt_bias = np.linspace(-3, 1.5, 2 * 4)  # keeps every g at u = 0 above the bound
     g = G.decay_gate(np.zeros((1, 2, 3, 4)), A_log, dt_bias)
     want = -np.array([0.5, 2.0])[:, None] * np.log1p(np.exp(dt_bias.reshape(2, 4)))
     _close(g[0, :, 0, :], want, 1e-12, "decay gate at u = 0")
     u = np.random.default_rng(72).standard_normal((2, 2, 5, 4)) * 10
-    assert np.all(G.decay_gate(u, A_log, dt_bias) <= 0.0)
+    gu = G.decay_gate(u, A_log, dt_bias)
+    assert np.all(gu <= 0.0) and np.all(gu >= -5.0)
+    # the lower bound g_min = -5: a large pre-activation saturates at exactly -5
+    _close(G.decay_gate(np.full((1, 2, 1, 4), 50.0), A_log, dt_bias), np.full((1, 2, 1, 4), -5.0),
+           0.0, "decay gate lower bound")
     # sigmoid: 1/2 at 0, symmetry, the logistic function
     _close(G.sigmoid(0.0), 0.5, 1e-15, "sigmoid(0)")
     _close(G.sigmoid(t) + G.sigmoid(-t), np.ones_like(t), 1e-12, "sigmoid symmetry")

@@ -154,3 +154,45 @@ def test_python_wrapper_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         kda.chunk_fwd(x, x, x, torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4))
+
+
+def prologue_call(**over):
+    args = dict(q_in=DUMMY, k_in=DUMMY, u=DUMMY, A_log=DUMMY, dt_bias=DUMMY, beta_in=None,
+                q_out=DUMMY, k_out=DUMMY, g_out=DUMMY, beta_out=None, B=1, H=2, T=8, dk=128,
+                dt=kda.KDA_BF16, stream=None)
+    args.update(over)
+    return kda.kda_prologue(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(u=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(A_log=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(g_out=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta_in=DUMMY), kda.KDA_ERR_INVALID_ARG),        # beta_in without beta_out
+    (dict(beta_out=DUMMY), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(dt=3), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_prologue_rejects(over, code):
+    assert prologue_call(**over) == code
+
+
+def epilogue_call(**over):
+    args = dict(o_in=DUMMY, z=DUMMY, weight=None, eps=1e-6, o_out=DUMMY, B=1, H=2, T=8, dv=128,
+                dt=kda.KDA_BF16, stream=None)
+    args.update(over)
+    return kda.kda_epilogue(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(z=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o_out=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(dv=200), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_epilogue_rejects(over, code):
+    assert epilogue_call(**over) == code

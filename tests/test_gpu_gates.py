@@ -1,0 +1,215 @@
+"""GPU parity of the fused prologue and epilogue (kda_prologue, kda_epilogue) against the
+fp64 definitions of oracle/gates.py, through the C ABI.
+
+Both are elementwise up to one reduction per row, so the check is per element: the
+kernels compute in fp32 and round once to the output type, giving
+|got - want| <= 2^-8 |want| + 1e-6 max |want| for bf16 outputs and
+|got - want| <= 2e-6 |want| + 1e-6 max |want| for fp32 ones (a few fp32 roundings of the
+exponential, the logarithm and the square root), which is tighter than the normwise
+bf16 / fp32 bounds of the operator and implies them. Checked: every dtype and head size
+on a ragged row count; without beta; in place; zero rows and saturating pre-activations;
+the B2 H16 T4096 workload in full; the packed H32 T65536 workload the benchmark times, on
+sampled rows; and prologue -> kda_chunk_fwd -> epilogue against the oracle's composition.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_13_amd as kda
+import oracle
+from oracle import gates as G
+from kda_workloads import CONFIGS, bf16_round, make_chunk_inputs, make_gate_inputs
+from tests.gpu_util import DT, TOL, assert_close, note, up
+
+pytestmark = pytest.mark.gpu
+
+REL = {"bf16": 2.0 ** -8, "f32": 2e-6}
+
+
+def assert_elementwise(got, want, dtype, what):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    scale = float(np.max(np.abs(want))) if want.size else 0.0
+    bound = REL[dtype] * np.abs(want) + 1e-6 * scale
+    bad = np.abs(got - want) > bound
+    if np.any(bad):
+        i = np.unravel_index(np.argmax(np.abs(got - want) - bound), got.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound; worst at {i}: "
+                             f"got {got[i]!r} want {want[i]!r}")
+
+
+def down(t):
+    return t.float().cpu().numpy()
+
+
+def run_prologue(x, dtype, with_beta=True, inplace=False):
+    dt = DT[dtype]
+    args = (up(x.q_in, dt), up(x.k_in, dt), up(x.u), up(x.A_log), up(x.dt_bias),
+            up(x.beta_in) if with_beta else None)
+    q, k, g, beta = kda.prologue(*args, inplace=inplace)
+    torch.cuda.synchronize()
+    if inplace:
+        assert q.data_ptr() == args[0].data_ptr() and g.data_ptr() == args[2].data_ptr()
+    return down(q), down(k), down(g), None if beta is None else down(beta)
+
+
+def check_prologue(x, dtype, got, what):
+    q, k, g, beta = got
+    rq, rk, rg, rb = G.prologue(x.q_in, x.k_in, x.u, x.A_log, x.dt_bias, x.beta_in)
+    assert_elementwise(q, rq, dtype, f"{what} q")
+    assert_elementwise(k, rk, dtype, f"{what} k")
+    assert_elementwise(g, rg, "f32", f"{what} g")   # the log-decay is fp32 for every dtype
+    assert np.all(g <= 0.0) and np.all(g >= G.G_MIN), f"{what}: g outside [g_min, 0]"
+    if beta is not None:
+        assert_elementwise(beta, rb, "f32", f"{what} beta")
+
+
+def small_gates(dtype, dk, dv, B=2, H=3, T=77, seed=91):
+    cfg = CONFIGS[1].replace(dtype=dtype, dk=dk, dv=dv, B=B, H=H, T=T, seed=seed)
+    return cfg, make_gate_inputs(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_prologue_small(dtype, dk):
+    # 2 * 3 * 77 = 462 rows: several blocks of 8 or 16 rows and a ragged last block
+    _, x = small_gates(dtype, dk, 64)
+    note(f"prologue {dtype} dk={dk}")
+    check_prologue(x, dtype, run_prologue(x, dtype), f"prologue {dtype} dk={dk}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prologue_without_beta_and_in_place(dtype):
+    _, x = small_gates(dtype, 128, 128, B=1, H=2, T=33, seed=5)
+    note(f"prologue without beta / in place {dtype}")
+    q, k, g, beta = run_prologue(x, dtype, with_beta=False)
+    assert beta is None
+    check_prologue(x, dtype, (q, k, g, None), f"no beta {dtype}")
+    check_prologue(x, dtype, run_prologue(x, dtype, inplace=True), f"in place {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prologue_extremes(dtype):
+    """Zero rows (L2Norm of 0 is 0), large and tiny magnitudes, and pre-activations that
+    saturate softplus, the g_min bound and the sigmoid."""
+    _, x = small_gates(dtype, 128, 128, B=1, H=2, T=40, seed=8)
+    x.q_in[0, 0, 3] = 0.0
+    x.k_in[0, 1, 7] = 0.0
+    x.q_in[0, 1, 5] *= np.float32(1e4)
+    x.k_in[0, 0, 9] *= np.float32(1e-3)
+    x.u[0, 0, 0] = 60.0            # g on the lower bound
+    x.u[0, 1, 1] = -60.0           # softplus ~ exp(-60): g ~ 0
+    x.u[0, 0, 2, :64] = 3.0
+    x.beta_in[0, 0, :4] = [60.0, -60.0, 0.0, 1e-3]
+    if dtype == "bf16":   # the scaled rows must stay bf16 values
+        x.q_in, x.k_in = bf16_round(x.q_in), bf16_round(x.k_in)
+    note(f"prologue extremes {dtype}")
+    got = run_prologue(x, dtype)
+    check_prologue(x, dtype, got, f"extremes {dtype}")
+    assert np.all(got[0][0, 0, 3] == 0.0) and np.all(got[1][0, 1, 7] == 0.0)
+    assert np.all(got[2][0, 0, 0] == G.G_MIN)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("with_weight", [True, False])
+def test_epilogue_small(dtype, dv, with_weight):
+    _, x = small_gates(dtype, 128, dv)
+    o = np.random.default_rng(17).standard_normal(x.z.shape).astype(np.float32) * 0.3
+    if dtype == "bf16":
+        o = bf16_round(o)
+    w = x.weight if with_weight else None
+    note(f"epilogue {dtype} dv={dv} weight={with_weight}")
+    y = kda.epilogue(up(o, DT[dtype]), up(x.z, DT[dtype]), None if w is None else up(w), eps=1e-5)
+    want = G.epilogue(o, x.z, np.ones(dv) if w is None else w, 1e-5)
+    assert_elementwise(down(y), want, dtype, f"epilogue {dtype} dv={dv}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_epilogue_zero_rows_and_in_place(dtype):
+    _, x = small_gates(dtype, 128, 128, B=1, H=2, T=21, seed=12)
+    o = np.random.default_rng(3).standard_normal(x.z.shape).astype(np.float32)
+    o[0, 1, 4] = 0.0                       # a zero row stays zero for any eps
+    o[0, 0, 6] *= np.float32(1e-3)         # eps matters: sqrt(mean o^2 + eps)
+    if dtype == "bf16":
+        o = bf16_round(o)
+    x.z[0, 0, 0, :8] = [60.0, -60.0, 0.0, 1.0, -1.0, 20.0, -20.0, 0.5]
+    note(f"epilogue zero rows / in place {dtype}")
+    ot = up(o, DT[dtype])
+    y = kda.epilogue(ot, up(x.z, DT[dtype]), up(x.weight), eps=1e-6, inplace=True)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == ot.data_ptr()
+    got = down(y)
+    assert_elementwise(got, G.epilogue(o, x.z, x.weight, 1e-6), dtype, f"in place {dtype}")
+    assert np.all(got[0, 1, 4] == 0.0)
+
+
+def test_gates_b2_h16_t4096_full():
+    cfg = CONFIGS[1]
+    x = make_gate_inputs(cfg)
+    note(f"prologue / epilogue in full on {cfg.name}")
+    check_prologue(x, "bf16", run_prologue(x, "bf16"), cfg.name)
+    y = kda.epilogue(up(x.q_in, torch.bfloat16), up(x.z, torch.bfloat16), up(x.weight), eps=1e-6)
+    assert_elementwise(down(y), G.epilogue(x.q_in, x.z, x.weight, 1e-6), "bf16",
+                       f"{cfg.name} epilogue")
+
+
+def test_gates_varlen_t65536_sampled_rows():
+    """The benchmark's launch: H32 T65536 packed tokens (B = 1), dk = dv = 128, on 4096
+    sampled rows (the grid strides over 2M rows, so every block runs many passes)."""
+    cfg = CONFIGS[3]
+    x = make_gate_inputs(cfg)
+    note(f"prologue / epilogue on {cfg.name} (sampled rows)")
+    bf = torch.bfloat16
+    q, k, g, beta = kda.prologue(up(x.q_in, bf), up(x.k_in, bf), up(x.u), up(x.A_log),
+                                 up(x.dt_bias), up(x.beta_in))
+    y = kda.epilogue(q, up(x.z, bf), up(x.weight), eps=1e-6)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    rows = np.concatenate([[0, cfg.H * cfg.T - 1], rng.integers(0, cfg.H * cfg.T, 4094)])
+    h, t = rows // cfg.T, rows % cfg.T
+    idx = (torch.zeros(len(rows), dtype=torch.long), torch.from_numpy(h), torch.from_numpy(t))
+    dev_idx = tuple(i.to(q.device) for i in idx)
+    rg = np.empty((len(rows), cfg.dk))
+    for hh in np.unique(h):   # the oracle's gate, one head at a time
+        m = h == hh
+        rg[m] = G.decay_gate(x.u[0, hh, t[m]][None, None], x.A_log[hh:hh + 1],
+                             x.dt_bias[hh])[0, 0]
+    assert_elementwise(down(q[dev_idx]), G.l2norm(x.q_in[0, h, t]), "bf16", "sampled q")
+    assert_elementwise(down(k[dev_idx]), G.l2norm(x.k_in[0, h, t]), "bf16", "sampled k")
+    assert_elementwise(down(g[dev_idx]), rg, "f32", "sampled g")
+    assert_elementwise(down(beta[dev_idx]), G.sigmoid(x.beta_in[0, h, t]), "f32",
+                       "sampled beta")
+    qb = down(q[dev_idx])   # the epilogue read the bf16 q the prologue wrote
+    assert_elementwise(down(y[dev_idx]), G.epilogue(qb, x.z[0, h, t], x.weight, 1e-6), "bf16",
+                       "sampled epilogue")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prologue_operator_epilogue_end_to_end(dtype):
+    """prologue -> kda_chunk_fwd -> epilogue on the device, each step checked against the
+    oracle on the values the previous step handed over: the prologue's outputs against
+    its definition, the operator on those (rounded) outputs against the recurrence, the
+    epilogue on the operator's output against its definition. (The composition is not
+    compared in one piece: RMSNorm rescales every row to unit size, so a row with a
+    small output would turn the bf16 rounding of q and k into a large relative error.)"""
+    cfg = CONFIGS[1].replace(dtype=dtype, B=1, H=2, T=150, seed=44)
+    x = make_gate_inputs(cfg)
+    v = make_chunk_inputs(cfg).v
+    note(f"prologue -> chunk_fwd -> epilogue {dtype}")
+    dt = DT[dtype]
+    q, k, g, beta = kda.prologue(up(x.q_in, dt), up(x.k_in, dt), up(x.u), up(x.A_log),
+                                 up(x.dt_bias), up(x.beta_in))
+    o, sT = kda.chunk_fwd(q, k, up(v, dt), g, beta)
+    y = kda.epilogue(o, up(x.z, dt), up(x.weight), eps=1e-6)
+    torch.cuda.synchronize()
+    check_prologue(x, dtype, (down(q), down(k), down(g), down(beta)), f"end to end {dtype}")
+    ref = oracle.kda_forward(down(q), down(k), v, down(g), down(beta))
+    ro = np.stack([ref[(0, h)][0] for h in range(cfg.H)])[None]
+    rs = np.stack([ref[(0, h)][1] for h in range(cfg.H)])[None]
+    assert_close(down(sT), rs, TOL[dtype], "final state")
+    assert_close(down(o), ro, TOL[dtype], "operator output")
+    assert_elementwise(down(y), G.epilogue(down(o), x.z, x.weight, 1e-6), dtype, "epilogue")

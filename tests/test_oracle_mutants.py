@@ -91,6 +91,9 @@ GATE_MUTANTS = {
     "l2norm_without_sqrt": ("l2norm", lambda G: lambda x: np.asarray(x, float) / (
         np.sum(np.asarray(x, float) ** 2, axis=-1, keepdims=True) + G.EPS_L2)),
     "softplus_as_relu": ("softplus", lambda G: lambda x: np.maximum(np.asarray(x, float), 0.0)),
+    "decay_without_lower_bound": ("decay_gate", lambda G: lambda u, A_log, dt_bias: -np.exp(
+        np.asarray(A_log, float)).reshape(1, -1, 1, 1) * G.softplus(np.asarray(u, float) + np.asarray(
+            dt_bias, float).reshape(1, len(A_log), 1, -1))),
     "rms_as_sum": ("epilogue", lambda G: lambda o, z, w, eps: G.sigmoid(z) * np.asarray(o) / np.sqrt(
         np.sum(np.asarray(o) ** 2, axis=-1, keepdims=True) + eps) * w),
     "gate_on_input": ("epilogue", lambda G: lambda o, z, w, eps: G.sigmoid(o) * np.asarray(z) / np.sqrt(
