@@ -1,12 +1,17 @@
 // C ABI of libkda.so (declared in include/kda.h): argument validation on the host,
 // then dispatch to the kernels on the caller's stream. Nothing here allocates,
 // synchronises or keeps state between calls.
+#include <cstdint>
+
 #include "kda.h"
 #include "kda_internal.h"
 
 namespace {
 
 bool supported_dim(int d) { return d == 64 || d == 128; }
+
+// The row-streaming kernels access eight channels at a time (16 bytes in bf16).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -153,6 +158,9 @@ kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, cons
   if (!q_in || !k_in || !u || !A_log || !dt_bias || !q_out || !k_out || !g_out)
     return KDA_ERR_INVALID_ARG;
   if (!beta_in != !beta_out) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(u) || !aligned16(dt_bias) ||
+      !aligned16(q_out) || !aligned16(k_out) || !aligned16(g_out))
+    return KDA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || dk <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (!supported_dim(dk)) return KDA_ERR_UNSUPPORTED;
@@ -169,6 +177,8 @@ kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, fl
                         void* o_out, int B, int H, int T, int dv, kda_dtype dt,
                         hipStream_t stream) {
   if (!o_in || !z || !o_out) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(o_in) || !aligned16(z) || !aligned16(o_out) || !aligned16(weight))
+    return KDA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || !(eps < 1e30f)) return KDA_ERR_INVALID_ARG;  // also rejects NaN
   if (B <= 0 || H <= 0 || T <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;

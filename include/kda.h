@@ -174,8 +174,9 @@ kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, 
  *   A_log      float32 [H]        dt_bias  float32 [H, dk]
  *   beta_in, beta_out  float32 [B, H, T], both NULL or both set (may be the same buffer)
  *   dk         64 or 128 (else KDA_ERR_UNSUPPORTED)
- * Any other NULL array: KDA_ERR_INVALID_ARG. With cu_seqlens packing, pass B = 1 and the
- * packed T. fp32 arithmetic throughout; bf16 outputs are rounded once.
+ * Any other NULL array, or any [.., dk] array or dt_bias not 16-byte aligned:
+ * KDA_ERR_INVALID_ARG. With cu_seqlens packing, pass B = 1 and the packed T. fp32
+ * arithmetic throughout; bf16 outputs are rounded once.
  */
 kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, const float* A_log,
                         const float* dt_bias, const float* beta_in, void* q_out, void* k_out,
@@ -191,6 +192,7 @@ kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, cons
  *   weight          float32 [dv] (shared by the heads), or NULL for 1
  *   eps             finite, >= 0 (else KDA_ERR_INVALID_ARG)
  *   dv              64 or 128 (else KDA_ERR_UNSUPPORTED)
+ * A NULL o_in, z or o_out, or any array not 16-byte aligned: KDA_ERR_INVALID_ARG.
  */
 kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, float eps,
                         void* o_out, int B, int H, int T, int dv, kda_dtype dt,

@@ -173,6 +173,9 @@ def prologue_call(**over):
     (dict(T=0), kda.KDA_ERR_INVALID_ARG),
     (dict(dt=3), kda.KDA_ERR_INVALID_ARG),
     (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(q_in=DUMMY + 8), kda.KDA_ERR_INVALID_ARG),     # not 16-byte aligned
+    (dict(g_out=DUMMY + 4), kda.KDA_ERR_INVALID_ARG),
+    (dict(dt_bias=DUMMY + 4), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_prologue_rejects(over, code):
     assert prologue_call(**over) == code
@@ -193,6 +196,8 @@ def epilogue_call(**over):
     (dict(eps=float("inf")), kda.KDA_ERR_INVALID_ARG),
     (dict(B=-1), kda.KDA_ERR_INVALID_ARG),
     (dict(dv=200), kda.KDA_ERR_UNSUPPORTED),
+    (dict(z=DUMMY + 8), kda.KDA_ERR_INVALID_ARG),        # not 16-byte aligned
+    (dict(weight=DUMMY + 4), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_epilogue_rejects(over, code):
     assert epilogue_call(**over) == code
