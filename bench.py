@@ -52,17 +52,27 @@ MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
     "bytes": 5386500000,
     "kernel_sha256": "8539ba78417a1033b40190864444042086c7b00b1556e48bf5b035fcc1687722",
 }
-CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_13_amd", "csrc", "kda_chunk_mfma.hip")
+MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
+    "bytes": 4320464550,
+    "kernel_sha256": "7b71bd805a0b3f8716f80570bf27cba8d0b6c9ff81b3b572063d4f27f5b0b336",
+}
+MEASURED_TRAFFIC_EPILOGUE = {  # profiles/kda_epilogue_h32_t65536.md
+    "bytes": 1610632255,
+    "kernel_sha256": "7b71bd805a0b3f8716f80570bf27cba8d0b6c9ff81b3b572063d4f27f5b0b336",
+}
+CSRC = os.path.join(ROOT, "gated_delta_rule_13_amd", "csrc")
+CHUNK_KERNEL_SRC = os.path.join(CSRC, "kda_chunk_mfma.hip")
+GATES_KERNEL_SRC = os.path.join(CSRC, "kda_gates.hip")
 
 
-def measured_traffic(record=None):
-    """HBM bytes per launch from the committed rocprofv3 counters, or None once the chunk
-    kernel source differs from the one they were taken on."""
+def measured_traffic(record=None, src=CHUNK_KERNEL_SRC):
+    """HBM bytes per launch from the committed rocprofv3 counters, or None once the
+    kernel source ``src`` differs from the one they were taken on."""
     import hashlib
     record = MEASURED_TRAFFIC if record is None else record
     if not record:
         return None
-    with open(CHUNK_KERNEL_SRC, "rb") as f:
+    with open(src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
     return record["bytes"] if digest == record["kernel_sha256"] else None
 
@@ -160,13 +170,15 @@ def bench_gates(torch, kda, cfg, steps: int, warmup: int):
         if rc != kda.KDA_OK:
             raise RuntimeError(f"kda_epilogue returned {rc}")
     out = {}
-    for name, call, nbytes in (("prologue", prologue, prologue_alg_bytes(B, H, T, dk)),
-                               ("epilogue", epilogue, epilogue_alg_bytes(B, H, T, dv))):
+    for name, call, nbytes, rec in (
+            ("prologue", prologue, prologue_alg_bytes(B, H, T, dk), MEASURED_TRAFFIC_PROLOGUE),
+            ("epilogue", epilogue, epilogue_alg_bytes(B, H, T, dv), MEASURED_TRAFFIC_EPILOGUE)):
         ms = time_calls(torch, call, steps, warmup)
         gbs = nbytes / (ms / 1e3) / 1e9
         out[name] = {"us_per_launch": ms * 1e3, "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbs / HBM_PEAK_GBS, "alg_bytes_per_launch": nbytes}}
+            "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(rec, GATES_KERNEL_SRC),
+            "alg_bytes_per_launch": nbytes}}
         log(f"{name}: {ms * 1e3:.1f} us/launch, {gbs:.0f} GB/s")
     return out
 
