@@ -8,10 +8,13 @@ never imports this package.
 Two independent implementations live here:
   * ``kda_oracle.c`` (through ``kda_chains`` / ``kda_forward`` / ``kda_decode_step``):
     the token recurrence in plain C, fp64, parallel over chains. This is the oracle
-    the GPU path is compared with.
+    the GPU path is compared with. ``kda_oracle_bwd.c`` (``kda_chains_bwd`` /
+    ``kda_backward``) is its backward pass: the chain rule through the same token
+    step in reverse order.
   * ``reference.py``: the same recurrence written with numpy (for small cases), the
     pages' chunked (WY / UT transform) form, the pages' WY recursions and brute-force
-    unrolled products. These exist to pin the oracle to the pages.
+    unrolled products, and the backward twin ``recurrence_bwd``. These exist to pin the
+    oracle to the pages (the backward to finite differences of the forward).
 
 Every function here has at least one pin in ``tests/test_oracle_pins.py``; none is
 "parity unpinned".
@@ -40,6 +43,10 @@ def _load():
                                           P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P, P,
                                           ctypes.c_int]
         lib.oracle_kda_chains.restype = ctypes.c_int
+        lib.oracle_kda_chains_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
+                                              P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P,
+                                              P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_kda_chains_bwd.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -96,6 +103,45 @@ def kda_chains(q, k, v, g, beta, row_off, row_len, s0=None, erase=None, write=No
     if rc != 0:
         raise MemoryError("oracle_kda_chains could not allocate its work buffers")
     return o, sf
+
+
+def kda_chains_bwd(q, k, v, g, beta, row_off, row_len, do, s0=None, dsT=None, erase=None,
+                   write=None, threads: int = 0) -> Dict[str, np.ndarray]:
+    """Gradients of ``kda_chains`` (kda_oracle_bwd.c): given do [rows, dv] and dsT
+    [chains, dk, dv] (None = 0), the gradients of sum(do * o) + sum(dsT * S_T) with respect
+    to q, k, v, g, beta (or the Gated Delta Rule-2 gates erase [rows, dk] / write
+    [rows, dv]) and s0. Returns a dict of float64 arrays: dq, dk, dv, dg, ds0 and dbeta or
+    derase / dwrite."""
+    q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    erase, write, s0, dsT = _f64(erase), _f64(write), _f64(s0), _f64(dsT)
+    rows, dk = q.shape
+    dv = v.shape[1]
+    off = np.ascontiguousarray(row_off, dtype=np.int64)
+    ln = np.ascontiguousarray(row_len, dtype=np.int64)
+    n = len(off)
+    gdr2 = erase is not None
+    assert (write is not None) == gdr2
+    assert k.shape == (rows, dk) and v.shape == (rows, dv) and do.shape == (rows, dv)
+    assert beta.shape == (rows,) and g.shape in ((rows, dk), (rows,))
+    assert not gdr2 or (erase.shape == (rows, dk) and write.shape == (rows, dv))
+    assert np.all(off >= 0) and np.all(ln >= 0) and np.all(off + ln <= rows)
+    for x in (s0, dsT):
+        assert x is None or x.shape == (n, dk, dv)
+    out = {"dq": np.zeros((rows, dk)), "dk": np.zeros((rows, dk)), "dv": np.zeros((rows, dv)),
+           "dg": np.zeros(g.shape), "ds0": np.zeros((n, dk, dv))}
+    if gdr2:
+        out["derase"], out["dwrite"] = np.zeros((rows, dk)), np.zeros((rows, dv))
+    else:
+        out["dbeta"] = np.zeros(rows)
+    rc = _load().oracle_kda_chains_bwd(
+        n, dk, dv, _ptr(off), _ptr(ln), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        1 if g.ndim == 2 else 0, _ptr(beta), _ptr(erase), _ptr(write), _ptr(s0), _ptr(do),
+        _ptr(dsT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+        _ptr(out.get("dbeta")), _ptr(out.get("derase")), _ptr(out.get("dwrite")),
+        _ptr(out["ds0"]), int(threads))
+    if rc != 0:
+        raise MemoryError("oracle_kda_chains_bwd could not allocate its work buffers")
+    return out
 
 
 def pack_chains(q, k, v, g, beta, s0=None, cu_seqlens=None,
@@ -156,6 +202,28 @@ def kda_forward(q, k, v, g, beta, s0=None, cu_seqlens=None,
     o, sf = kda_chains(*args, **kwargs, threads=threads)
     offs, lens = args[5], args[6]
     return {ch: (o[offs[c]:offs[c] + lens[c]], sf[c]) for c, ch in enumerate(chains)}
+
+
+def kda_backward(q, k, v, g, beta, do, s0=None, dsT=None, cu_seqlens=None,
+                 chains: Optional[Iterable[Tuple[int, int]]] = None, threads: int = 0,
+                 erase=None, write=None) -> Dict[Tuple[int, int], Dict[str, np.ndarray]]:
+    """Backward over head-major inputs [B, H, T, ...] (B = 1 with ``cu_seqlens``): do
+    [B, H, T, dv] and dsT [N, H, dk, dv] (None = 0) are the loss's gradients with respect
+    to o and the final states. Returns {(n, h): {name: gradient}} with dq, dk [len, dk],
+    dv [len, dv], dg [len, dk] or [len], ds0 [dk, dv] and dbeta [len] (or derase [len, dk]
+    / dwrite [len, dv] for Gated Delta Rule-2), float64."""
+    chains, args, kwargs = pack_chains(q, k, v, g, beta, s0, cu_seqlens, chains, erase, write)
+    # the rows of do, in the packed order of the chains
+    _, dargs, _ = pack_chains(q, k, do, g, beta, None, cu_seqlens, chains)
+    dsT_c = np.stack([dsT[n, h] for (n, h) in chains]) if dsT is not None else None
+    offs, lens = args[5], args[6]
+    out = kda_chains_bwd(*args[:5], offs, lens, dargs[2], s0=kwargs["s0"], dsT=dsT_c,
+                         erase=kwargs.get("erase"), write=kwargs.get("write"), threads=threads)
+    res = {}
+    for c, ch in enumerate(chains):
+        sl = slice(offs[c], offs[c] + lens[c])
+        res[ch] = {name: (a[c] if name == "ds0" else a[sl]) for name, a in out.items()}
+    return res
 
 
 def kda_decode_step(state, q, k, v, g, beta, threads: int = 0, erase=None,

@@ -1,4 +1,5 @@
-"""Builds the C oracle (``kda_oracle.c``) into ``oracle/libkda_oracle.so`` with gcc and OpenMP.
+"""Builds the C oracle (``kda_oracle.c``, ``kda_oracle_bwd.c``) into ``oracle/libkda_oracle.so``
+with gcc and OpenMP.
 
 Test infrastructure: the HIP library neither builds nor loads this file.
 """
@@ -10,16 +11,17 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "kda_oracle.c")
+SRCS = [os.path.join(HERE, "kda_oracle.c"), os.path.join(HERE, "kda_oracle_bwd.c")]
 LIB = os.path.join(HERE, "libkda_oracle.so")
 
 
 def build_oracle(force: bool = True) -> str:
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+    if not force and os.path.exists(LIB) and all(
+            os.path.getmtime(LIB) >= os.path.getmtime(src) for src in SRCS):
         return LIB
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           SRC, "-o", tmp, "-lm"]
+           *SRCS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

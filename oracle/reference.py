@@ -143,3 +143,54 @@ def wy_products(k, w, u, G, r):
         P -= np.outer(d * k[i], w[i])
         H += np.outer(d * k[i], u[i])
     return P, H
+
+
+def recurrence_bwd(q, k, v, g, beta, do, s0=None, dsT=None, erase=None, write=None):
+    """Gradients of sum(do * o) + sum(dsT * S_T) for ``recurrence``, the numpy twin of
+    ``kda_oracle_bwd.c``: the chain rule through the token step S~ = Diag(a) S,
+    p = S~^T (e * k), d = w * v - p, S' = S~ + k d^T, o = S'^T q, in reverse token order
+    (every state kept). Returns a dict with dq, dk, dv, dg (shaped like g), ds0 and
+    dbeta (e = w = beta) or derase [T, dk] / dwrite [T, dv] (Gated Delta Rule-2)."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    T, dk = k.shape
+    dv = v.shape[1]
+    g = np.asarray(g, dtype=np.float64)
+    a = np.exp(_gate(g, dk))
+    beta = np.asarray(beta, dtype=np.float64)
+    gdr2 = erase is not None
+    E = np.asarray(erase, np.float64) if gdr2 else np.repeat(beta[:, None], dk, axis=1)
+    W = np.asarray(write, np.float64) if gdr2 else np.repeat(beta[:, None], dv, axis=1)
+    S = np.zeros((dk, dv)) if s0 is None else np.array(s0, dtype=np.float64)
+    St, D = [], []
+    for t in range(T):                       # forward, keeping S~ and d of every token
+        S = a[t][:, None] * S
+        St.append(S.copy())
+        d = W[t] * v[t] - S.T @ (E[t] * k[t])
+        D.append(d)
+        S = S + np.outer(k[t], d)
+    out = {"dq": np.zeros((T, dk)), "dk": np.zeros((T, dk)), "dv": np.zeros((T, dv)),
+           "dg": np.zeros((T, dk))}
+    de, dw = np.zeros((T, dk)), np.zeros((T, dv))
+    dS = np.zeros((dk, dv)) if dsT is None else np.array(dsT, dtype=np.float64)
+    for t in reversed(range(T)):
+        Sp = St[t] + np.outer(k[t], D[t])    # S' of token t
+        dS = dS + np.outer(q[t], do[t])
+        out["dq"][t] = Sp @ do[t]
+        dd = dS.T @ k[t]
+        out["dk"][t] = dS @ D[t]
+        dw[t] = dd * v[t]
+        out["dv"][t] = dd * W[t]
+        dS = dS - np.outer(E[t] * k[t], dd)  # dS~
+        r = -St[t] @ dd
+        out["dk"][t] += E[t] * r
+        de[t] = k[t] * r
+        out["dg"][t] = np.sum(dS * St[t], axis=1)
+        dS = a[t][:, None] * dS
+    if g.ndim == 1:
+        out["dg"] = out["dg"].sum(axis=1)
+    out["ds0"] = dS
+    if gdr2:
+        out["derase"], out["dwrite"] = de, dw
+    else:
+        out["dbeta"] = de.sum(axis=1) + dw.sum(axis=1)
+    return out

@@ -407,3 +407,116 @@ ALL_PINS = [
     pin_gdr2_write_only,
     pin_gdr2_erase_direction,
 ]
+
+
+# ------------------------------------------------------------------ backward pass
+# Each backward pin takes ``bwd(q, k, v, g, beta, do, s0=None, dsT=None, erase=None,
+# write=None) -> dict`` (the gradients of sum(do * o) + sum(dsT * S_T); see
+# oracle.reference.recurrence_bwd) and checks it against the definition of a derivative
+# or against closed forms, using only the forward recurrence (pinned above).
+
+def _loss(q, k, v, g, beta, do, s0, dsT, erase=None, write=None):
+    o, S = ref.recurrence(q, k, v, g, beta, s0=s0, erase=erase, write=write)
+    return float(np.sum(do * o) + np.sum(dsT * S))
+
+
+def pin_bwd_finite_differences(bwd):
+    """Central differences of the loss with respect to every input element (fp64, step
+    1e-6: truncation and cancellation both below 1e-9 of the gradient's scale), for
+    per-channel and per-head decay, with an initial state, and for the Gated Delta
+    Rule-2 gates."""
+    h = 1e-6
+    for mode in ("channel", "head", "gdr2"):
+        T, dk, dv = 9, 5, 4
+        q, k, v, g, beta, s0 = case(T, dk, dv, seed=61, gate="head" if mode == "head" else
+                                    "channel", strong=True)
+        rng = np.random.default_rng(62)
+        do = rng.standard_normal((T, dv))
+        dsT = rng.standard_normal((dk, dv))
+        gates = {}
+        if mode == "gdr2":
+            gates = {"erase": rng.random((T, dk)), "write": rng.random((T, dv))}
+        got = bwd(q, k, v, g, beta, do, s0=s0, dsT=dsT, **gates)
+        inputs = {"dq": q, "dk": k, "dv": v, "dg": g, "ds0": s0}
+        if mode == "gdr2":
+            inputs.update(derase=gates["erase"], dwrite=gates["write"])
+        else:
+            inputs["dbeta"] = beta
+        for name, x in inputs.items():
+            fd = np.zeros(x.shape)
+            for idx in np.ndindex(x.shape):
+                keep = x[idx]
+                x[idx] = keep + h
+                lp = _loss(q, k, v, g, beta, do, s0, dsT, **gates)
+                x[idx] = keep - h
+                lm = _loss(q, k, v, g, beta, do, s0, dsT, **gates)
+                x[idx] = keep
+                fd[idx] = (lp - lm) / (2 * h)
+            _close(got[name], fd, 1e-7, f"finite differences {name} ({mode})")
+
+
+def pin_bwd_linear_attention(bwd):
+    """Erase 0, write 1, alpha = 1 is linear attention, o_t = sum_{s<=t} (q_t.k_s) v_s +
+    S0^T q_t and S_T = S0 + K^T V ("Token Mixer I", section "Mamba2"); its gradients in
+    closed form: dQ = (dO V^T ⊙ M) K + dO S0^T, dK = (dO V^T ⊙ M)^T Q + V dS_T^T,
+    dV = (Q K^T ⊙ M)^T dO + K dS_T, dS0 = Q^T dO + dS_T, M the inclusive causal mask,
+    and the write gate's gradient dW = dV ⊙ V (since dV = dd * 1)."""
+    T, dk, dv = 14, 6, 5
+    q, k, v, _, beta, s0 = case(T, dk, dv, seed=63)
+    rng = np.random.default_rng(64)
+    do = rng.standard_normal((T, dv))
+    dsT = rng.standard_normal((dk, dv))
+    M = np.tril(np.ones((T, T)))
+    got = bwd(q, k, v, np.zeros((T, dk)), beta, do, s0=s0, dsT=dsT,
+              erase=np.zeros((T, dk)), write=np.ones((T, dv)))
+    _close(got["dq"], (do @ v.T * M) @ k + do @ s0.T, 1e-12, "linear attention dq")
+    _close(got["dk"], (do @ v.T * M).T @ q + v @ dsT.T, 1e-12, "linear attention dk")
+    dV = (q @ k.T * M).T @ do + k @ dsT
+    _close(got["dv"], dV, 1e-12, "linear attention dv")
+    _close(got["ds0"], q.T @ do + dsT, 1e-12, "linear attention ds0")
+    _close(got["dwrite"], dV * v, 1e-12, "linear attention dwrite")
+
+
+def pin_bwd_pure_decay(bwd):
+    """With the tied gate beta = 0 and do = 0 the state only decays, S_T = Diag(exp sum_t
+    g_t) S0: dS0 = Diag(exp sum_t g_t) dS_T, every token's dg_t = rowsum(dS_T ⊙ S_T) (the
+    sum over channels for one decay per head), and dq = dv = 0."""
+    T, dk, dv = 11, 6, 4
+    for gate in ("channel", "head"):
+        q, k, v, g, _, s0 = case(T, dk, dv, seed=65, gate=gate, strong=True)
+        dsT = np.random.default_rng(66).standard_normal((dk, dv))
+        got = bwd(q, k, v, g, np.zeros(T), np.zeros((T, dv)), s0=s0, dsT=dsT)
+        gs = g.sum(axis=0) if gate == "channel" else np.full(dk, g.sum())
+        ST = np.exp(gs)[:, None] * s0
+        _close(got["ds0"], np.exp(gs)[:, None] * dsT, 1e-12, f"pure decay ds0 ({gate})")
+        row = np.sum(dsT * ST, axis=1)
+        want = np.tile(row, (T, 1)) if gate == "channel" else np.full(T, row.sum())
+        _close(got["dg"], want, 1e-12, f"pure decay dg ({gate})")
+        _close(got["dq"], np.zeros((T, dk)), 0.0, "pure decay dq")
+        _close(got["dv"], np.zeros((T, dv)), 0.0, "pure decay dv")
+
+
+def pin_bwd_linear_in_cotangents(bwd):
+    """The gradients are linear in (do, dS_T): bwd(a do1 + b do2, a ds1 + b ds2) =
+    a bwd(do1, ds1) + b bwd(do2, ds2), and zero cotangents give zero gradients."""
+    T, dk, dv = 70, 8, 6   # crosses the oracle's 64-token checkpoint segments
+    q, k, v, g, beta, s0 = case(T, dk, dv, seed=67, strong=True)
+    rng = np.random.default_rng(68)
+    do1, do2 = rng.standard_normal((2, T, dv))
+    ds1, ds2 = rng.standard_normal((2, dk, dv))
+    r1 = bwd(q, k, v, g, beta, do1, s0=s0, dsT=ds1)
+    r2 = bwd(q, k, v, g, beta, do2, s0=s0, dsT=ds2)
+    r3 = bwd(q, k, v, g, beta, 2.0 * do1 - 0.5 * do2, s0=s0, dsT=2.0 * ds1 - 0.5 * ds2)
+    for name in r1:
+        _close(r3[name], 2.0 * r1[name] - 0.5 * r2[name], 1e-12, f"linearity {name}")
+    r0 = bwd(q, k, v, g, beta, np.zeros((T, dv)), s0=s0, dsT=np.zeros((dk, dv)))
+    for name in r0:
+        assert np.all(r0[name] == 0.0), f"zero cotangents give nonzero {name}"
+
+
+BWD_PINS = [
+    pin_bwd_finite_differences,
+    pin_bwd_linear_attention,
+    pin_bwd_pure_decay,
+    pin_bwd_linear_in_cotangents,
+]
