@@ -81,6 +81,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   a.plan = scheduled ? static_cast<uint32_t*>(workspace) : nullptr;
   a.cus = device_compute_units();
   a.split_all = 0;
+  a.hist = nullptr;
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
   if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T))
@@ -149,6 +150,51 @@ kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, 
   if (!erase || !write) return KDA_ERR_INVALID_ARG;
   return recurrent_step_impl(q, k, v, g, nullptr, erase, write, state, o, N, H, dk, dv, dt,
                              gm, stream);
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt) {
+  if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0 || dt != KDA_BF16) return 0;
+  if (!kda::chunk_bwd_supports(dk, dv, T)) return 0;
+  const int N = num_seqs > 0 ? num_seqs : B;
+  const size_t one = kda::chunk_bwd_hist_bytes(N, H, T, dv, num_seqs > 0);
+  return 2 * ((one + 255) / 256 * 256);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, const void* grad_o,
+                         const float* grad_final_state, void* grad_q, void* grad_k,
+                         void* grad_v, float* grad_g, float* grad_beta,
+                         float* grad_initial_state, const int32_t* cu_seqlens, int num_seqs,
+                         int B, int H, int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !g || !beta || !grad_o) return KDA_ERR_INVALID_ARG;
+  if (!grad_q || !grad_k || !grad_v || !grad_g || !grad_beta) return KDA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
+  if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
+  if (!cu_seqlens && num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_BF16 || !kda::chunk_bwd_supports(dk, dv, T)) return KDA_ERR_UNSUPPORTED;
+  const long long N = cu_seqlens ? num_seqs : B;
+  if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
+  const size_t need =
+      kda_chunk_bwd_workspace_size(B, H, T, dk, dv, cu_seqlens ? num_seqs : 0, dt);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+
+  kda::BwdArgs b;
+  kda::ChunkArgs& a = b.f;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = nullptr; a.write = nullptr;
+  a.s0 = initial_state; a.sT = nullptr; a.o = nullptr; a.cu = cu_seqlens;
+  a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
+  a.plan = nullptr; a.cus = device_compute_units(); a.split_all = 0; a.hist = nullptr;
+  b.dout = grad_o; b.dsT = grad_final_state;
+  b.dq = grad_q; b.dk = grad_k; b.dv = grad_v; b.dg = grad_g; b.dbeta = grad_beta;
+  b.ds0 = grad_initial_state;
+  b.hist_s = workspace;
+  b.hist_ds = static_cast<char*>(workspace) + need / 2;
+  const hipError_t err = kda::launch_chunk_bwd(b, gm == KDA_GATE_PER_CHANNEL, stream);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, const float* A_log,

@@ -1,0 +1,785 @@
+// Backward pass of the chunked forward on the CDNA4 matrix cores (bf16 operands, fp32
+// accumulate, dk = 128): the gradients of a loss with respect to q, k, v, g, beta and the
+// initial state, given its gradients dO with respect to the outputs and dS_T with respect
+// to the final state.
+//
+// The pages give the forward only (their chunkwise-training section states that the
+// backward pass has the forward's shapes), so the steps below are the chain rule applied
+// to the forward's 16-token block ("Token Mixer I", section "Kimi Delta Attention",
+// chunkwise form, with the block of the forward kernel). With S the state entering a block
+// and, per key channel, P_t the decay from the block start through token t, E_t the decay
+// after t, Gam = P_16, the block computes
+//   Qh = q P, Kh = k P, Kb = k / P, Kt = k E,  A = StrictTril(Kh Kb^T), M = Tril(Qh Kb^T),
+//   Tm = (I + Diag(beta) A)^-1,  R = V - Kh S,  U = Tm Diag(beta) R,
+//   O = Qh S + M U,  S' = Diag(Gam) S + Kt^T U.
+// Given dS' (the gradient reaching S') and dO, reverse mode gives
+//   dU = M^T dO + Kt dS',  dY = Tm^T dU,  dV = Diag(beta) dY,
+//   dS = Diag(Gam) dS' + Qh^T dO - Kh^T Diag(beta) dY                 (the carry)
+//   dQh = dO S^T + dM Kb,  dKh = -Diag(beta) dY S^T + dA Kb,  dKb = dA^T Kh + dM^T Qh,
+//   dKt = U dS'^T,  with dM = Tril(dO U^T), dA = -StrictTril(Diag(beta) dY U^T),
+//   dbeta_t = sum_j dY_tj R_tj - sum_s A_ts (dY U^T)_ts,
+//   d log P_t = dQh_t Qh_t + dKh_t Kh_t - dKb_t Kb_t - dKt_t Kt_t   (per channel),
+//   d log Gam = sum_t dKt_t Kt_t + Gam * rowsum(dS' * S),
+//   dg_s = sum_{t >= s} d log P_t + d log Gam,   dq = dQh P,   dk = dKh P + dKb / P + dKt E.
+//
+// Three launches:
+//   1. the forward state pass with the state history (kda_chunk_mfma.hip): S at every
+//      block start, bf16, in the layout of hist_chain_offset;
+//   2. chunk_bwd_state_kernel: the carry above, one workgroup per chain, from the last
+//      block to the first; it records dS' of every block (same layout) and writes dS_0;
+//   3. chunk_bwd_grad_kernel: every block independently from (S, dS'), one workgroup per
+//      block: dq, dk, dv, dg, dbeta.
+// Launch 2 has the forward's structure: four "prep" wavefronts prepare the operands of
+// the next 64 tokens (in reverse) while four "state" wavefronts, holding dS in matrix-core
+// accumulators, run the carry of the current 64 tokens; one barrier per 64 tokens.
+#include <stddef.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_mfma.h"
+
+namespace kda {
+namespace {
+
+constexpr int kC = 64;          // tokens per step (four blocks)
+constexpr int kLDK = kDK + 8;   // padded LDS row (bf16) of [token][channel] tiles
+constexpr int kLDB = kC + 4;    // padded LDS row (bf16) of [channel][token] tiles (8-byte rows)
+constexpr int kPrepWaves = 4;
+
+#ifndef KDA_STATE_PRIO
+#define KDA_STATE_PRIO 3
+#endif
+
+// ------------------------------------------------------------------ launch 2: the carry
+
+// Operands of 64 tokens for the carry, written by the prep wavefronts.
+struct RStage {
+  bf16 kc[kC][kLDK];      // Kt = k * E (row-major: A operand of Kt dS')
+  bf16 qrT[kDK][kLDB];    // Qh^T (A operand of Qh^T dO)
+  bf16 krT[kDK][kLDB];    // Kh^T
+  bf16 aqkT[4][16][24];   // M^T of each block
+  bf16 tdT[4][16][24];    // Tm^T of each block
+  float tot[4][kDK];      // Gam of each block
+  float beta[kC];
+};
+struct RSmem {
+  RStage st[2];
+  bf16 qg[kC][kLDK];      // Qh / Gam (prep wavefronts only; each reads back its own rows)
+  bf16 kg[kC][kLDK];      // Kh / Gam
+};
+static_assert(sizeof(RSmem) <= 160 * 1024, "LDS budget of one CU");
+static_assert(sizeof(RStage) % 16 == 0 && offsetof(RStage, qrT) % 16 == 0 &&
+                  offsetof(RStage, krT) % 16 == 0 && offsetof(RStage, aqkT) % 16 == 0 &&
+                  offsetof(RStage, tdT) % 16 == 0 && offsetof(RStage, tot) % 16 == 0 &&
+                  offsetof(RSmem, qg) % 16 == 0 && offsetof(RSmem, kg) % 16 == 0,
+              "vector LDS accesses need aligned arrays");
+static_assert((kLDB * 2) % 8 == 0, "transposed rows must keep 8-byte alignment");
+
+// Decay products of block I and its operands for the carry (one wavefront; a lane holds
+// 8 tokens x 4 channels as in the forward's prep).
+__device__ __forceinline__ void prep_block_rev(RStage& st, bf16 (*qg)[kLDK], bf16 (*kg)[kLDK],
+                                               const BlockRegs& r, int I, int lane) {
+  const int cq = lane & 31, hf = lane >> 5;
+  f32x4 al[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[u][j] = __expf(r.g[u][j]);
+  f32x4 half = al[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) half[j] *= al[u][j];
+  f32x4 tot, rtot, run, rs;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float other = __shfl_xor(half[j], 32, 64);
+    tot[j] = half[j] * other;
+    rtot[j] = __builtin_amdgcn_rcpf(tot[j]);
+    run[j] = hf ? other : 1.f;
+    rs[j] = hf ? 1.f : other;
+  }
+  if (hf == 0) *reinterpret_cast<f32x4*>(&st.tot[I][4 * cq]) = tot;
+  float qp[4][8], kp[4][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int t = 16 * I + 8 * hf + u;
+    f32x4 qs, ks;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      run[j] *= al[u][j];
+      qp[j][u] = static_cast<float>(r.q[u][j]) * run[j];
+      kp[j][u] = static_cast<float>(r.k[u][j]) * run[j];
+      qs[j] = qp[j][u] * rtot[j];
+      ks[j] = kp[j][u] * rtot[j];
+    }
+    *reinterpret_cast<bf16x4*>(&qg[t][4 * cq]) = pack4(qs);
+    *reinterpret_cast<bf16x4*>(&kg[t][4 * cq]) = pack4(ks);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t0 = 16 * I + 8 * hf;
+    *reinterpret_cast<bf16x4*>(&st.qrT[4 * cq + j][t0]) =
+        pack4(qp[j][0], qp[j][1], qp[j][2], qp[j][3]);
+    *reinterpret_cast<bf16x4*>(&st.qrT[4 * cq + j][t0 + 4]) =
+        pack4(qp[j][4], qp[j][5], qp[j][6], qp[j][7]);
+    *reinterpret_cast<bf16x4*>(&st.krT[4 * cq + j][t0]) =
+        pack4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
+    *reinterpret_cast<bf16x4*>(&st.krT[4 * cq + j][t0 + 4]) =
+        pack4(kp[j][4], kp[j][5], kp[j][6], kp[j][7]);
+  }
+#pragma unroll
+  for (int u = 7; u >= 0; --u) {
+    const int t = 16 * I + 8 * hf + u;
+    f32x4 ke;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ke[j] = static_cast<float>(r.k[u][j]) * rs[j];
+      rs[j] *= al[u][j];
+    }
+    *reinterpret_cast<bf16x4*>(&st.kc[t][4 * cq]) = pack4(ke);
+  }
+  if (lane < 16) st.beta[16 * I + lane] = r.beta;
+}
+
+// M^T and Tm^T of block I: A_qk = (Qh / Gam) Kt^T and A_kk = (Kh / Gam) Kt^T are the
+// forward's Qh Kb^T and Kh Kb^T (Kb = Kt / Gam).
+__device__ __forceinline__ void block_tiles_rev(RStage& st, const bf16 (*qg)[kLDK],
+                                                const bf16 (*kg)[kLDK], int I, int rr, int p) {
+  bf16x8 bq[4], bk[4], bc[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = 32 * ks + 8 * p;
+    bq[ks] = *reinterpret_cast<const bf16x8*>(&qg[16 * I + rr][ch]);
+    bk[ks] = *reinterpret_cast<const bf16x8*>(&kg[16 * I + rr][ch]);
+    bc[ks] = *reinterpret_cast<const bf16x8*>(&st.kc[16 * I + rr][ch]);
+  }
+  f32x4 accq = zero4(), acck = zero4(), acct = zero4();
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    accq = mfma32(bq[ks], bc[ks], accq);   // A_qk[4p + e][rr]
+    acck = mfma32(bk[ks], bc[ks], acck);   // A_kk[4p + e][rr]
+    acct = mfma32(bc[ks], bk[ks], acct);   // A_kk[rr][4p + e]
+  }
+  f32x4 m, nc, nr;
+  const float brr = st.beta[16 * I + rr];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * p + e;
+    m[e] = rr <= i ? accq[e] : 0.f;                           // M[i][rr] = M^T[rr][i]
+    nc[e] = rr < i ? st.beta[16 * I + i] * acck[e] : 0.f;     // N[i][rr]
+    nr[e] = i < rr ? brr * acct[e] : 0.f;                     // N[rr][i]
+  }
+  *reinterpret_cast<bf16x4*>(&st.aqkT[I][rr][4 * p]) = pack4(m);
+  const f32x4 inv = unit_lower_inverse(nc, nr, rr, p);        // Tm[4p + e][rr]
+  *reinterpret_cast<bf16x4*>(&st.tdT[I][rr][4 * p]) = pack4(inv);
+}
+
+// dO of one value column for the 16 tokens of block I (token 16 I + 4 p + e), raw bf16.
+template <int DV>
+__device__ __forceinline__ void load_col(bf16 (&x)[4], rsrc_t src, uint32_t off) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = ld_b16(src, off + e * DV * 2);
+}
+
+// State wavefront of the carry: NT 16-column tiles of dS from column cbase, whole chain,
+// from the last block to the first.
+template <int NT, int DV>
+__device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const TokenRange& tr,
+                                           size_t row0, size_t state_off, size_t hist_off,
+                                           int nsteps, int cbase, int lane, int rr, int p) {
+  const rsrc_t dosrc =
+      make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, (uint32_t)tr.len * DV * 2);
+  const rsrc_t hdst = make_rsrc(static_cast<char*>(b.hist_ds) + hist_off,
+                                (uint32_t)nsteps * 4 * kDK * DV * 2);
+  int col[NT];
+  uint32_t coff[NT];  // byte offset of (token 4 p, column col) within a 64-token step
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    col[c] = cbase + 16 * c + rr;
+    coff[c] = (uint32_t)(4 * p * DV + col[c]) * 2;
+  }
+  // D_acc[c][m][e] = dS[32 (m / 2) + 8 p + 4 (m % 2) + e][col[c]] (the forward's S layout)
+  f32x4 D_acc[NT][8];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
+        D_acc[c][m][e] = b.dsT ? b.dsT[state_off + (size_t)ch * DV + col[c]] : 0.f;
+      }
+  bf16 dd[NT][4][4];
+  if (nsteps > 0) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        load_col<DV>(dd[c][I], dosrc, coff[c] + ((nsteps - 1) * kC + 16 * I) * DV * 2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  lds_barrier();
+  for (int s = nsteps - 1; s >= 0; --s) {
+    const RStage& st = sm.st[s & 1];
+#pragma unroll
+    for (int I = 3; I >= 0; --I) {
+      const uint32_t blk = 4 * (uint32_t)s + I;
+      // dS' of this block: record it, and Kt dS' (dS' as the B operand, bf16)
+      f32x4 dU[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) dU[c] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kc[16 * I + rr][32 * ks + 8 * p]);
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const bf16x8 db = cat8(pack4(D_acc[c][2 * ks]), pack4(D_acc[c][2 * ks + 1]));
+          const uint32_t tile = blk * (DV / 16) + (cbase + 16 * c) / 16;
+          st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, db);
+          dU[c] = mfma32(ak, db, dU[c]);
+        }
+      }
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&st.beta[16 * I + 4 * p]);
+      const bf16x4 aT = *reinterpret_cast<const bf16x4*>(&st.aqkT[I][rr][4 * p]);
+      const bf16x4 tT = *reinterpret_cast<const bf16x4*>(&st.tdT[I][rr][4 * p]);
+      bf16x4 dob[NT], nby[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dob[c][e] = dd[c][I][e];
+        if (s > 0) load_col<DV>(dd[c][I], dosrc, coff[c] + ((s - 1) * kC + 16 * I) * DV * 2);
+        // dU = M^T dO + Kt dS' (the 16x16x16 product starts from zero: accumulating it
+        // onto a 16x16x32 result still in flight is not covered by the wait states)
+        const f32x4 u = dU[c] + mfma16(aT, dob[c], zero4());
+        const f32x4 dy = mfma16(tT, pack4(u), zero4());        // dY = Tm^T dU
+        nby[c] = pack4(-bt[0] * dy[0], -bt[1] * dy[1], -bt[2] * dy[2], -bt[3] * dy[3]);
+      }
+      // dS = Diag(Gam) dS' + Qh^T dO - Kh^T Diag(beta) dY
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int s2 = m >> 1, h2 = m & 1;
+        const float d1 = st.tot[I][32 * s2 + 8 * p + 4 * h2 + (rr & 3)];
+        const int cha = 32 * s2 + 8 * (rr >> 2) + 4 * h2 + (rr & 3);
+        const bf16x4 aq = *reinterpret_cast<const bf16x4*>(&st.qrT[cha][16 * I + 4 * p]);
+        const bf16x4 ak = *reinterpret_cast<const bf16x4*>(&st.krT[cha][16 * I + 4 * p]);
+        const f32x4 dc = {quad_bcast<0>(d1), quad_bcast<1>(d1), quad_bcast<2>(d1),
+                          quad_bcast<3>(d1)};
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          f32x4 t_ = D_acc[c][m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t_[e] *= dc[e];
+          t_ = mfma16(aq, dob[c], t_);
+          D_acc[c][m] = mfma16(ak, nby[c], t_);
+        }
+      }
+    }
+    lds_barrier();
+  }
+  if (b.ds0) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
+          b.ds0[state_off + (size_t)ch * DV + col[c]] = D_acc[c][m][e];
+        }
+  }
+}
+
+template <int NS, int NT, bool PER_CHANNEL>
+__global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel(BwdArgs b) {
+  constexpr int DV = 16 * NS * NT;
+  __shared__ __align__(16) RSmem sm;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rr = lane & 15, p = lane >> 4;
+  const ChunkArgs& a = b.f;
+  const int chain = blockIdx.x;
+  const int n = chain / a.H, h = chain % a.H;
+  const TokenRange tr = token_range(a.cu, n, a.T);
+  const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
+  const size_t state_off = ((size_t)n * a.H + h) * kDK * DV;
+  const size_t hist_off = hist_chain_offset(a, n, h, tr);
+  const int nsteps = (tr.len + kC - 1) / kC;
+  if (wave < kPrepWaves) {
+    const int I = wave;
+    const PrepSrc src = prep_src<PER_CHANNEL, false>(a, row0, tr.len, I, lane);
+    BlockRegs r;
+    if (nsteps > 0) {
+      load_block<PER_CHANNEL, false>(r, src, (nsteps - 1) * kC);
+      prep_block_rev(sm.st[(nsteps - 1) & 1], sm.qg, sm.kg, r, I, lane);
+      wave_lds_fence();
+      block_tiles_rev(sm.st[(nsteps - 1) & 1], sm.qg, sm.kg, I, rr, p);
+      if (nsteps > 1) load_block<PER_CHANNEL, false>(r, src, (nsteps - 2) * kC);
+    }
+    lds_barrier();
+    for (int s = nsteps - 1; s >= 0; --s) {
+      if (s > 0) {
+        RStage& st = sm.st[(s - 1) & 1];
+        prep_block_rev(st, sm.qg, sm.kg, r, I, lane);
+        wave_lds_fence();
+        block_tiles_rev(st, sm.qg, sm.kg, I, rr, p);
+        if (s > 1) load_block<PER_CHANNEL, false>(r, src, (s - 2) * kC);
+      }
+      lds_barrier();
+    }
+  } else {
+    __builtin_amdgcn_s_setprio(KDA_STATE_PRIO);
+    const int j = wave - kPrepWaves;
+    carry_role<NT, DV>(sm, b, tr, row0, state_off, hist_off, nsteps, 16 * NT * j, lane, rr, p);
+  }
+}
+
+// ------------------------------------------------------------ launch 3: the gradients
+
+constexpr int kGThreads = 256;  // four wavefronts per 16-token block
+
+template <int DV>
+struct GSmem {
+  float P[16][kDK];        // decay from the block start through token t
+  float E[16][kDK];        // decay after token t
+  float gam[kDK];
+  bf16 qraw[16][kLDK];     // the bf16 inputs
+  bf16 kraw[16][kLDK];
+  bf16 qh[16][kLDK];       // Qh, Kh, Kb, Kt as bf16 operands
+  bf16 kh[16][kLDK];
+  bf16 kb[16][kLDK];
+  bf16 kt[16][kLDK];
+  bf16 srow[kDK][DV + 8];  // S and dS' of the block, row-major
+  bf16 dsrow[kDK][DV + 8];
+  bf16 vr[16][DV + 8];     // token rows of V, dO, U, dY, Diag(beta) dY
+  bf16 dor[16][DV + 8];
+  bf16 ur[16][DV + 8];
+  bf16 dyr[16][DV + 8];
+  bf16 bdyr[16][DV + 8];
+  float A[16][17];         // StrictTril(Kh Kb^T)
+  float M[16][17];         // Tril(Qh Kb^T)
+  float Tm[16][17];
+  float G1[16][17];        // dO U^T
+  float G2[16][17];        // dY U^T
+  float beta[16];
+  float r1[16];            // sum_j dY_tj R_tj
+  float dlgam[kDK];        // d log Gam
+  float dlp[16][kDK];      // d log P_t
+  bf16 dqr[16][kLDK];      // dq, dk staged as token rows
+  bf16 dkr[16][kLDK];
+};
+
+// Position of work item (16-token block) `slot` of head h: sequence n and block blk, or
+// false when the slot holds no block. Sequence n's blocks take slots from
+// floor(cu[n] / 16) + n on (consecutive sequences never overlap).
+__device__ __forceinline__ bool grad_item(const ChunkArgs& a, int slot, int& n, int& blk,
+                                          TokenRange& tr) {
+  if (!a.cu) {
+    const int per = (a.T + 15) / 16;
+    n = slot / per;
+    blk = slot % per;
+    if (n >= a.N) return false;
+    tr = token_range(nullptr, n, a.T);
+    return true;
+  }
+  int lo = 0, hi = a.N - 1;  // last sequence whose first slot is <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int first = min(max(a.cu[mid], 0), a.T) / 16 + mid;
+    if (first <= slot) lo = mid; else hi = mid - 1;
+  }
+  n = lo;
+  tr = token_range(a.cu, n, a.T);
+  blk = slot - (tr.t0 / 16 + n);
+  return blk >= 0 && blk * 16 < tr.len;
+}
+
+template <int DV, bool PER_CHANNEL>
+__global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, int slots) {
+  constexpr int NTW = DV / 64;     // value tiles per wavefront
+  constexpr int LDV = DV + 8;
+  __shared__ __align__(16) GSmem<DV> sm;
+  const ChunkArgs& a = b.f;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rr = lane & 15, p = lane >> 4;
+  const int h = blockIdx.x / slots, slot = blockIdx.x % slots;
+  int n, blk;
+  TokenRange tr;
+  if (!grad_item(a, slot, n, blk, tr)) return;
+  const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + 16 * (size_t)blk;
+  const int len = min(16, tr.len - 16 * blk);  // tokens of this block in the sequence
+  const size_t hoff = hist_chain_offset(a, n, h, tr) + (size_t)blk * kDK * DV * 2;
+
+  // ---- 1. inputs: q, k rows; v, dO rows; S and dS' tiles; the decay of every channel
+  {
+    const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, len * kDK * 2);
+    const rsrc_t ks = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, len * kDK * 2);
+    const int t = tid >> 4, c8 = 8 * (tid & 15);
+    const uint32_t off = (uint32_t)(t * kDK + c8) * 2;
+    *reinterpret_cast<f32x4*>(&sm.qraw[t][c8]) = ld_b128(qs, off);
+    *reinterpret_cast<f32x4*>(&sm.kraw[t][c8]) = ld_b128(ks, off);
+    const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
+    const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
+    for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
+      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+      const uint32_t o2 = (uint32_t)(tt * DV + cc) * 2;
+      *reinterpret_cast<f32x4*>(&sm.vr[tt][cc]) = ld_b128(vs, o2);
+      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, o2);
+    }
+  }
+  // S and dS' tiles of this wavefront's value columns, in registers (B operands) and
+  // as rows in LDS
+  bf16x8 sb[NTW][4], db[NTW][4];
+  {
+    const rsrc_t hs = make_rsrc(static_cast<const char*>(b.hist_s) + hoff, kDK * DV * 2);
+    const rsrc_t hd = make_rsrc(static_cast<const char*>(b.hist_ds) + hoff, kDK * DV * 2);
+#pragma unroll
+    for (int c = 0; c < NTW; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ct = wave * NTW + c;
+        const uint32_t off = (uint32_t)(((ct * 4 + ks) * 64 + lane) * 16);
+        sb[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
+        db[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
+        const int col = 16 * ct + rr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sm.srow[32 * ks + 8 * p + i][col] = sb[c][ks][i];
+          sm.dsrow[32 * ks + 8 * p + i][col] = db[c][ks][i];
+        }
+      }
+  }
+  if (tid < kDK) {
+    // channel tid: prefix and suffix products of alpha over the block
+    const int c = tid;
+    float al[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float gv = t < len ? (PER_CHANNEL ? a.g[(row0 + t) * kDK + c] : a.g[row0 + t]) : 0.f;
+      al[t] = __expf(gv);
+    }
+    float run = 1.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      run *= al[t];
+      sm.P[t][c] = run;
+    }
+    sm.gam[c] = run;
+    float suf = 1.f;
+#pragma unroll
+    for (int t = 15; t >= 0; --t) {
+      sm.E[t][c] = suf;
+      suf *= al[t];
+    }
+  } else if (tid < kDK + 16) {
+    const int t = tid - kDK;
+    sm.beta[t] = t < len ? a.beta[row0 + t] : 0.f;
+    sm.r1[t] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- 2. the decayed operands (bf16) for the matrix cores
+  {
+    const int t = tid >> 4, c8 = 8 * (tid & 15);
+    bf16x8 q8 = *reinterpret_cast<const bf16x8*>(&sm.qraw[t][c8]);
+    bf16x8 k8 = *reinterpret_cast<const bf16x8*>(&sm.kraw[t][c8]);
+    float qh[8], kh[8], kb[8], kt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float P = sm.P[t][c8 + i], E = sm.E[t][c8 + i];
+      const float rg = __builtin_amdgcn_rcpf(sm.gam[c8 + i]);
+      const float qf = static_cast<float>(q8[i]), kf = static_cast<float>(k8[i]);
+      qh[i] = qf * P;
+      kh[i] = kf * P;
+      kt[i] = kf * E;
+      kb[i] = kt[i] * rg;
+    }
+    *reinterpret_cast<bf16x8*>(&sm.qh[t][c8]) = cat8(pack4(qh[0], qh[1], qh[2], qh[3]),
+                                                      pack4(qh[4], qh[5], qh[6], qh[7]));
+    *reinterpret_cast<bf16x8*>(&sm.kh[t][c8]) = cat8(pack4(kh[0], kh[1], kh[2], kh[3]),
+                                                      pack4(kh[4], kh[5], kh[6], kh[7]));
+    *reinterpret_cast<bf16x8*>(&sm.kb[t][c8]) = cat8(pack4(kb[0], kb[1], kb[2], kb[3]),
+                                                      pack4(kb[4], kb[5], kb[6], kb[7]));
+    *reinterpret_cast<bf16x8*>(&sm.kt[t][c8]) = cat8(pack4(kt[0], kt[1], kt[2], kt[3]),
+                                                      pack4(kt[4], kt[5], kt[6], kt[7]));
+  }
+  __syncthreads();
+
+  // ---- 3. A, M and Tm of the block (one wavefront)
+  if (wave == 0) {
+    f32x4 accq = zero4(), acck = zero4(), acct = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 32 * ks + 8 * p;
+      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.qh[rr][ch]);
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm.kh[rr][ch]);
+      const bf16x8 bc = *reinterpret_cast<const bf16x8*>(&sm.kb[rr][ch]);
+      accq = mfma32(bq, bc, accq);   // (Qh Kb^T)[4p + e][rr]
+      acck = mfma32(bk, bc, acck);   // (Kh Kb^T)[4p + e][rr]
+      acct = mfma32(bc, bk, acct);   // (Kh Kb^T)[rr][4p + e]
+    }
+    f32x4 nc, nr;
+    const float brr = sm.beta[rr];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * p + e;
+      sm.M[i][rr] = rr <= i ? accq[e] : 0.f;
+      sm.A[i][rr] = rr < i ? acck[e] : 0.f;
+      nc[e] = rr < i ? sm.beta[i] * acck[e] : 0.f;
+      nr[e] = i < rr ? brr * acct[e] : 0.f;
+    }
+    const f32x4 inv = unit_lower_inverse(nc, nr, rr, p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Tm[4 * p + e][rr] = inv[e];
+  }
+  __syncthreads();
+
+  // ---- 4. per value tile: R, U, dU, dY (token 4p + e, column 16 ct + rr)
+  {
+    bf16x4 tA, tT, mT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tA[i] = static_cast<bf16>(sm.Tm[rr][4 * p + i]);   // Tm row rr
+      tT[i] = static_cast<bf16>(sm.Tm[4 * p + i][rr]);   // Tm^T row rr
+      mT[i] = static_cast<bf16>(sm.M[4 * p + i][rr]);    // M^T row rr
+    }
+    f32x4 bt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bt[e] = sm.beta[4 * p + e];
+    f32x4 r1 = zero4();
+#pragma unroll
+    for (int c = 0; c < NTW; ++c) {
+      const int col = 16 * (wave * NTW + c) + rr;
+      f32x4 X = zero4(), dU2 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.kh[rr][32 * ks + 8 * p]);
+        const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sm.kt[rr][32 * ks + 8 * p]);
+        X = mfma32(ah, sb[c][ks], X);       // (Kh S)[4p + e][col]
+        dU2 = mfma32(at, db[c][ks], dU2);   // (Kt dS')[4p + e][col]
+      }
+      f32x4 R, x;
+      bf16x4 dob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        R[e] = static_cast<float>(sm.vr[4 * p + e][col]) - X[e];
+        x[e] = bt[e] * R[e];
+        dob[e] = sm.dor[4 * p + e][col];
+      }
+      const f32x4 U = mfma16(tA, pack4(x), zero4());
+      const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
+      const f32x4 dY = mfma16(tT, pack4(dU), zero4());
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.ur[4 * p + e][col] = static_cast<bf16>(U[e]);
+        sm.dyr[4 * p + e][col] = static_cast<bf16>(dY[e]);
+        sm.bdyr[4 * p + e][col] = static_cast<bf16>(bt[e] * dY[e]);
+        r1[e] += dY[e] * R[e];
+      }
+    }
+    // sum r1 over the 16 columns of each lane group, then over the wavefronts
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = r1[e];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      v += __shfl_xor(v, 8, 64);
+      if (rr == 0) atomicAdd(&sm.r1[4 * p + e], v);
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. contractions over the value columns; wavefront w: channel tiles 2w, 2w + 1
+  f32x4 C1[2], C2[2], C3[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    C1[mt] = C2[mt] = C3[mt] = zero4();
+    const int ch = 16 * (2 * wave + mt) + rr;
+#pragma unroll
+    for (int kk = 0; kk < DV / 32; ++kk) {
+      const int j = 32 * kk + 8 * p;
+      const bf16x8 s8 = *reinterpret_cast<const bf16x8*>(&sm.srow[ch][j]);
+      const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(&sm.dsrow[ch][j]);
+      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dor[rr][j]);
+      const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&sm.bdyr[rr][j]);
+      const bf16x8 au = *reinterpret_cast<const bf16x8*>(&sm.ur[rr][j]);
+      C1[mt] = mfma32(ao, s8, C1[mt]);   // (dO S^T)[4p + e][ch]
+      C2[mt] = mfma32(ay, s8, C2[mt]);   // (Diag(beta) dY S^T)[4p + e][ch]
+      C3[mt] = mfma32(au, d8, C3[mt]);   // (U dS'^T)[4p + e][ch]
+    }
+  }
+  if (wave == 0) {
+    f32x4 g1 = zero4(), g2 = zero4();
+#pragma unroll
+    for (int kk = 0; kk < DV / 32; ++kk) {
+      const int j = 32 * kk + 8 * p;
+      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dor[rr][j]);
+      const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&sm.dyr[rr][j]);
+      const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&sm.ur[rr][j]);
+      g1 = mfma32(ao, bu, g1);   // (dO U^T)[4p + e][rr]
+      g2 = mfma32(ay, bu, g2);   // (dY U^T)[4p + e][rr]
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.G1[4 * p + e][rr] = g1[e];
+      sm.G2[4 * p + e][rr] = g2[e];
+    }
+  } else if (wave == 1) {
+    // Gam * rowsum(dS' * S): lane pair per channel
+    for (int c = lane; c < kDK; c += 64) {
+      float acc = 0.f;
+      for (int j = 0; j < DV; j += 8) {
+        const bf16x8 s8 = *reinterpret_cast<const bf16x8*>(&sm.srow[c][j]);
+        const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(&sm.dsrow[c][j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += static_cast<float>(s8[i]) * static_cast<float>(d8[i]);
+      }
+      sm.dlgam[c] = sm.gam[c] * acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- 6. the 16 x 16 corrections and the chain rule through the decay
+  {
+    bf16x4 dmr, dar, dmT, daT;   // dM, dA rows rr and columns rr
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s_ = 4 * p + i;
+      dmr[i] = static_cast<bf16>(s_ <= rr ? sm.G1[rr][s_] : 0.f);
+      dar[i] = static_cast<bf16>(s_ < rr ? -sm.beta[rr] * sm.G2[rr][s_] : 0.f);
+      dmT[i] = static_cast<bf16>(rr <= s_ ? sm.G1[s_][rr] : 0.f);
+      daT[i] = static_cast<bf16>(rr < s_ ? -sm.beta[s_] * sm.G2[s_][rr] : 0.f);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int ch = 16 * (2 * wave + mt) + rr;
+      bf16x4 bkb, bkh, bqh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bkb[i] = sm.kb[4 * p + i][ch];
+        bkh[i] = sm.kh[4 * p + i][ch];
+        bqh[i] = sm.qh[4 * p + i][ch];
+      }
+      const f32x4 dQh = C1[mt] + mfma16(dmr, bkb, zero4());
+      const f32x4 dKh = mfma16(dar, bkb, zero4()) - C2[mt];
+      const f32x4 dKb = mfma16(daT, bkh, zero4()) + mfma16(dmT, bqh, zero4());
+      const f32x4 dKt = C3[mt];
+      const float rg = __builtin_amdgcn_rcpf(sm.gam[ch]);
+      float lg = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * p + e;
+        const float P = sm.P[t][ch], E = sm.E[t][ch];
+        const float qf = static_cast<float>(sm.qraw[t][ch]);
+        const float kf = static_cast<float>(sm.kraw[t][ch]);
+        const float qh = qf * P, kh = kf * P, kt = kf * E, kb = kt * rg;
+        sm.dqr[t][ch] = static_cast<bf16>(dQh[e] * P);
+        sm.dkr[t][ch] = static_cast<bf16>(dKh[e] * P + dKb[e] * E * rg + dKt[e] * E);
+        sm.dlp[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;
+        lg += dKt[e] * kt;
+      }
+      lg += __shfl_xor(lg, 16, 64);
+      lg += __shfl_xor(lg, 32, 64);
+      if (p == 0) sm.dlgam[ch] += lg;
+    }
+  }
+  __syncthreads();
+
+  // ---- 7. outputs: dq, dk, dv rows; dg (suffix sums); dbeta
+  {
+    const rsrc_t qd = make_rsrc(static_cast<bf16*>(b.dq) + row0 * kDK, len * kDK * 2);
+    const rsrc_t kd = make_rsrc(static_cast<bf16*>(b.dk) + row0 * kDK, len * kDK * 2);
+    const int t = tid >> 4, c8 = 8 * (tid & 15);
+    const uint32_t off = (uint32_t)(t * kDK + c8) * 2;
+    st_b128(qd, off, *reinterpret_cast<const bf16x8*>(&sm.dqr[t][c8]));
+    st_b128(kd, off, *reinterpret_cast<const bf16x8*>(&sm.dkr[t][c8]));
+    const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
+    for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
+      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+      st_b128(vd, (uint32_t)(tt * DV + cc) * 2, *reinterpret_cast<const bf16x8*>(&sm.bdyr[tt][cc]));
+    }
+  }
+  if (PER_CHANNEL) {
+    if (tid < kDK) {
+      const int c = tid;
+      float acc = sm.dlgam[c];
+      for (int t = 15; t >= 0; --t) {
+        acc += sm.dlp[t][c];
+        if (t < len) b.dg[(row0 + t) * kDK + c] = acc;
+      }
+    }
+  } else {
+    // one decay per head: the sum over channels of the per-channel gradients
+    if (tid < kDK) {
+      const int c = tid;
+      float acc = sm.dlgam[c];
+      for (int t = 15; t >= 0; --t) {
+        acc += sm.dlp[t][c];
+        sm.dlp[t][c] = acc;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int t = 0; t < 16; ++t) {
+        float v = sm.dlp[t][lane] + sm.dlp[t][lane + 64];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0 && t < len) b.dg[row0 + t] = v;
+      }
+    }
+  }
+  if (tid >= 192 && tid < 208) {
+    const int t = tid - 192;
+    float acc = sm.r1[t];
+    for (int s_ = 0; s_ < t; ++s_) acc -= sm.A[t][s_] * sm.G2[t][s_];
+    if (t < len) b.dbeta[row0 + t] = acc;
+  }
+}
+
+}  // namespace
+
+bool chunk_bwd_supports(int dk, int dv, int T) {
+  // the forward's bounds, and one chain's state history addressable by a buffer descriptor
+  return chunk_mfma_supports(dk, dv, T) && ((long long)T + 64) * 16 * dv < (1ll << 31);
+}
+
+size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed) {
+  const size_t tokens = packed ? (size_t)T + 64 * (size_t)N : (size_t)N * (((size_t)T + 63) / 64 * 64);
+  return (size_t)H * tokens * (kDK / 16) * 2 * (size_t)dv;  // hist_chain_offset's layout
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t stream) {
+  BwdArgs b = args;
+  ChunkArgs& a = b.f;
+  if (!chunk_bwd_supports(a.dk, a.dv, a.T) || a.erase) return hipErrorInvalidValue;
+  // 1. states at every block start
+  a.hist = b.hist_s;
+  a.sT = nullptr;
+  hipError_t e = launch_chunk_mfma_hist(a, per_channel, stream);
+  if (e != hipSuccess) return e;
+  a.hist = nullptr;
+  // 2. the carry, one workgroup per chain
+  const unsigned chains = (unsigned)a.N * a.H;
+  if (a.dv == 128) {
+    if (per_channel) chunk_bwd_state_kernel<4, 2, true><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
+    else chunk_bwd_state_kernel<4, 2, false><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
+  } else {
+    if (per_channel) chunk_bwd_state_kernel<4, 1, true><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
+    else chunk_bwd_state_kernel<4, 1, false><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 3. the gradients of every block
+  const int slots = a.cu ? a.T / 16 + a.N + 1 : a.N * ((a.T + 15) / 16);
+  const unsigned grid = (unsigned)slots * a.H;
+  if (a.dv == 128) {
+    if (per_channel) chunk_bwd_grad_kernel<128, true><<<grid, kGThreads, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<128, false><<<grid, kGThreads, 0, stream>>>(b, slots);
+  } else {
+    if (per_channel) chunk_bwd_grad_kernel<64, true><<<grid, kGThreads, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<64, false><<<grid, kGThreads, 0, stream>>>(b, slots);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -44,16 +44,13 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kC = 64;         // tokens prepared and consumed per step (four blocks)
-constexpr int kDK = 128;       // key head size of this kernel
 constexpr int kLDK = kDK + 8;  // padded LDS row (bf16) of [token][channel] tiles
 constexpr int kLDT = kC + 8;   // padded LDS row (bf16) of [channel][token] tiles
 constexpr int kPrepWaves = 4;  // one per 16-token block
@@ -86,149 +83,7 @@ static_assert(sizeof(Stage) % 16 == 0 && offsetof(Stage, kcT) % 16 == 0 &&
               "vector LDS accesses need 16-byte aligned arrays");
 static_assert((kLDK * 2) % 16 == 0 && (kLDT * 2) % 16 == 0, "row pitch must keep alignment");
 
-__device__ __forceinline__ void wave_lds_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes are done
-  asm volatile("" ::: "memory");
-}
 
-// Workgroup barrier that waits for this wavefront's LDS operations, not for its global
-// loads (prefetches stay in flight across it).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited on
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// Round to bf16 pairwise (one v_cvt_pk_bf16_f32 per pair; converting the 4-vector
-// directly is split into single-element conversions by the compiler).
-__device__ __forceinline__ unsigned pack2(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
-__device__ __forceinline__ bf16x4 pack4(f32x4 v) {
-  return __builtin_bit_cast(bf16x4, (u32x2){pack2(v[0], v[1]), pack2(v[2], v[3])});
-}
-__device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
-  return pack4(f32x4{a, b, c, d});
-}
-
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = a[i];
-    r[4 + i] = b[i];
-  }
-  return r;
-}
-
-__device__ __forceinline__ f32x4 zero4() {
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  return z;
-}
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor over `bytes` bytes from p (stride 0: offsets are byte offsets and
-// an access at or past `bytes` reads zero / writes nothing).
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ bf16x4 ld_b64(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ __forceinline__ f32x4 ld_b128(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ float ld_b32(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ bf16 ld_b16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-}
-__device__ __forceinline__ void st_b128(rsrc_t r, uint32_t off, bf16x8 x) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), r, off, 0, 0);
-}
-
-// x from lane 4 (lane / 4) + E of this lane's quad (DPP quad permutation, no LDS access).
-template <int E>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), E * 0x55, 0xf, 0xf, true));
-}
-
-// Raw inputs of one 16-token block held by one prep lane: 8 tokens (half hf = lane / 32)
-// x 4 channels (4 * (lane % 32) + j); beta of token lane for lanes < 16.
-struct BlockRegs {
-  bf16x4 q[8];
-  bf16x4 k[8];
-  f32x4 g[8];
-  f32x4 b[8];  // erase gate (Gated Delta Rule-2 only)
-  float beta;
-};
-
-// Bounded views of one chain's inputs, and this prep lane's byte offsets within a chunk.
-struct PrepSrc {
-  rsrc_t q, k, g, beta, erase;
-  uint32_t qk_off, g_off, b_off, e_off;
-};
-
-template <bool PER_CHANNEL, bool GDR2>
-__device__ __forceinline__ PrepSrc prep_src(const ChunkArgs& a, size_t row0, int len, int I,
-                                            int lane) {
-  const int cq = lane & 31, hf = lane >> 5;
-  PrepSrc s;
-  s.q = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, (uint32_t)len * kDK * 2);
-  s.k = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, (uint32_t)len * kDK * 2);
-  s.g = PER_CHANNEL ? make_rsrc(a.g + row0 * kDK, (uint32_t)len * kDK * 4)
-                    : make_rsrc(a.g + row0, (uint32_t)len * 4);
-  s.beta = make_rsrc(a.beta + row0, (uint32_t)len * 4);
-  s.qk_off = ((16 * I + 8 * hf) * kDK + 4 * cq) * 2;
-  s.g_off = PER_CHANNEL ? ((16 * I + 8 * hf) * kDK + 4 * cq) * 4 : (16 * I + 8 * hf) * 4;
-  s.b_off = (16 * I + (lane & 15)) * 4;
-  if (GDR2) {
-    s.erase = make_rsrc(a.erase + row0 * kDK, (uint32_t)len * kDK * 4);
-    s.e_off = ((16 * I + 8 * hf) * kDK + 4 * cq) * 4;
-  }
-  return s;
-}
-
-// Loads block I of the 64 tokens starting at c0 (rows past the chain read as zero).
-template <bool PER_CHANNEL, bool GDR2>
-__device__ __forceinline__ void load_block(BlockRegs& r, const PrepSrc& s, int c0) {
-  const uint32_t qk = s.qk_off + (uint32_t)c0 * kDK * 2;
-  const uint32_t go = s.g_off + (uint32_t)c0 * (PER_CHANNEL ? kDK * 4 : 4);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    r.q[u] = ld_b64(s.q, qk + u * kDK * 2);
-    r.k[u] = ld_b64(s.k, qk + u * kDK * 2);
-    if (PER_CHANNEL) {
-      r.g[u] = ld_b128(s.g, go + u * kDK * 4);
-    } else {
-      const float gg = ld_b32(s.g, go + u * 4);
-      r.g[u] = f32x4{gg, gg, gg, gg};
-    }
-    if (GDR2) r.b[u] = ld_b128(s.erase, s.e_off + (uint32_t)c0 * kDK * 4 + u * kDK * 4);
-  }
-  // Gated Delta Rule-2 has no scalar gate: its erase gate sits in the key operand
-  r.beta = GDR2 ? 1.f : ld_b32(s.beta, s.b_off + (uint32_t)c0 * 4);
-}
 
 // Decay products of block I and its bf16 operands, written to LDS by one wavefront:
 // alpha = exp(g); P_t = exp(G_t - G_0) is the inclusive prefix product of alpha, E_t =
@@ -297,28 +152,9 @@ __device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const Bl
   if (lane < 16) st.beta[16 * I + lane] = r.beta;
 }
 
-// 16 x 16 fp32 products on the matrix cores with X in row layout (lane 16p + r holds
-// X[r][4p + e]) and Y in column layout (holds Y[4p + e][r], the accumulator layout); the
-// contraction index of step s is 4p + s, which both layouts hold as element s.
-// mm_col returns X Y in column layout; mm_row returns X Y in row layout, computed as the
-// column layout of Y^T X^T.
-__device__ __forceinline__ f32x4 mm_col(const f32x4& xr, const f32x4& yc) {
-  f32x4 acc = zero4();
-#pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mfma_f32(xr[s], yc[s], acc);
-  return acc;
-}
-__device__ __forceinline__ f32x4 mm_row(const f32x4& xr, const f32x4& yc) {
-  f32x4 acc = zero4();
-#pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mfma_f32(yc[s], xr[s], acc);
-  return acc;
-}
 
 // The A_qk / A_kk tile of block I and the inverse of its (I + N), N = Diag(beta) A_kk
-// strictly lower. N is nilpotent (N^16 = 0), so (I + N)^-1 = (I - N)(I + N^2)(I + N^4)
-// (I + N^8) exactly; the factors are polynomials in N and commute, which lets every
-// product take its left factor in row layout and its right factor in column layout.
+// strictly lower (unit_lower_inverse).
 __device__ __forceinline__ void block_tiles(Stage& st, const bf16 (*kd)[kLDK], int I, int rr,
                                             int p) {
   bf16x8 bq[4], bk[4], bc[4];
@@ -345,20 +181,9 @@ __device__ __forceinline__ void block_tiles(Stage& st, const bf16 (*kd)[kLDK], i
     nc[e] = rr < i ? st.beta[16 * I + i] * acck[e] : 0.f;   // N[i][rr]
     nr[e] = i < rr ? brr * acct[e] : 0.f;                    // N[rr][i]
   }
-  const f32x4 n2c = mm_col(nr, nc), n2r = mm_row(nr, nc);
-  const f32x4 n4c = mm_col(n2r, n2c), n4r = mm_row(n2r, n2c);
-  const f32x4 n8r = mm_row(n4r, n4c);
-  const f32x4 nn2c = mm_col(nr, n2c);
-  f32x4 y1;
+  const f32x4 inv = unit_lower_inverse(nc, nr, rr, p);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) y1[e] = (4 * p + e == rr ? 1.f : 0.f) - nc[e] + n2c[e] - nn2c[e];
-  const f32x4 t1 = mm_col(n4r, y1);
-  f32x4 y2;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) y2[e] = y1[e] + t1[e];
-  const f32x4 t2 = mm_col(n8r, y2);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) st.tdiag[I][4 * p + e][rr] = static_cast<bf16>(y2[e] + t2[e]);
+  for (int e = 0; e < 4; ++e) st.tdiag[I][4 * p + e][rr] = static_cast<bf16>(inv[e]);
 }
 
 // Values of one state column for the 16 tokens of block I, in the accumulator layout
@@ -397,13 +222,18 @@ __device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int s
 // straight-line instantiation (a tile count chosen at run time inside the loops would let
 // branches remove instructions that the wait states after the matrix-core products were
 // counted on).
-template <int NT, int DV, bool GDR2>
+// With HIST (the backward pass's state pass) the wavefront records the state at every
+// block start in a.hist (at byte hist_off, the layout of hist_chain_offset) and computes
+// no outputs.
+template <int NT, int DV, bool GDR2, bool HIST>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const TokenRange& tr,
-                                           size_t row0, size_t state_off, int nsteps, int cbase,
-                                           int lane, int rr, int p) {
+                                           size_t row0, size_t state_off, size_t hist_off,
+                                           int nsteps, int cbase, int lane, int rr, int p) {
   const rsrc_t vsrc =
       make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, (uint32_t)tr.len * DV * 2);
   const rsrc_t odst = make_rsrc(static_cast<bf16*>(a.o) + row0 * DV, (uint32_t)tr.len * DV * 2);
+  const rsrc_t hdst = make_rsrc(static_cast<char*>(a.hist) + (HIST ? hist_off : 0),
+                                HIST ? (uint32_t)nsteps * 4 * kDK * DV * 2 : 0);
   int col[NT];
   uint32_t voff[NT];  // byte offset of (token 4 p, column col) within a 64-token chunk
 #pragma unroll
@@ -440,7 +270,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
     const Stage& st = sm.st[s & 1];
     const uint32_t cbyte = (uint32_t)s * kC * DV * 2;
     // the barrier ending the previous step waited for this wavefront's staging writes
-    if (s > 0) flush_outputs<DV>(sm, odst, s - 1, cbase, NT, lane);
+    if (!HIST && s > 0) flush_outputs<DV>(sm, odst, s - 1, cbase, NT, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       // X = (K P) S, S as the B operand (bf16), and O^T = S^T (Q P)^T, S^T as the A
@@ -452,12 +282,18 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][32 * ks + 8 * p]);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           const bf16x8 sb = cat8(pack4(S_acc[c][2 * ks]), pack4(S_acc[c][2 * ks + 1]));
           X[c] = mfma32(ak, sb, X[c]);
-          Ot[c] = mfma32(sb, aq, Ot[c]);
+          if constexpr (HIST) {
+            const uint32_t tile = (uint32_t)(4 * s + I) * (DV / 16) + (cbase + 16 * c) / 16;
+            st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, sb);
+          } else {
+            const bf16x8 aq =
+                *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);
+            Ot[c] = mfma32(sb, aq, Ot[c]);
+          }
         }
       }
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&st.beta[16 * I + 4 * p]);
@@ -484,10 +320,12 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
       // result of a 16x16x32 product still in flight delays its completion beyond the
       // wait states counted from its issue, and the conversion below then read stale
       // registers.
+      if constexpr (!HIST) {
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const bf16x4 ob = pack4(Ot[c] + mfma16(vp[c], aI, zero4()));
-        *reinterpret_cast<bf16x4*>(&sm.ost[16 * I + rr][cbase + 16 * c + 4 * p]) = ob;
+        for (int c = 0; c < NT; ++c) {
+          const bf16x4 ob = pack4(Ot[c] + mfma16(vp[c], aI, zero4()));
+          *reinterpret_cast<bf16x4*>(&sm.ost[16 * I + rr][cbase + 16 * c + 4 * p]) = ob;
+        }
       }
       // S <- Diag(tot) S + (K E)^T V'
 #pragma unroll
@@ -510,7 +348,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
     }
     lds_barrier();
   }
-  if (nsteps > 0) flush_outputs<DV>(sm, odst, nsteps - 1, cbase, NT, lane);
+  if (!HIST && nsteps > 0) flush_outputs<DV>(sm, odst, nsteps - 1, cbase, NT, lane);
   if (a.sT) {
 #pragma unroll
     for (int c = 0; c < NT; ++c)
@@ -536,7 +374,7 @@ __host__ __device__ inline void split_item(uint32_t local, uint32_t n, uint32_t&
   part = 1 + within / gsize;
 }
 
-template <int NS, int NT, bool PER_CHANNEL, bool GDR2>
+template <int NS, int NT, bool PER_CHANNEL, bool GDR2, bool HIST>
 __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int DV = 16 * NS * NT;
   __shared__ __align__(16) Smem sm;
@@ -565,6 +403,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
   const TokenRange tr = token_range(a.cu, n, a.T);
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
   const size_t state_off = ((size_t)n * a.H + h) * kDK * DV;
+  const size_t hist_off = HIST ? hist_chain_offset(a, n, h, tr) : 0;
   const int nsteps = (tr.len + kC - 1) / kC;
 
   if (prep_wave) {
@@ -598,12 +437,14 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     const int j = wave - kPrepWaves;
     if constexpr (NT > 1) {
       if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
-        state_role<NT / 2, DV, GDR2>(sm, a, tr, row0, state_off, nsteps,
-                               (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane, rr, p);
+        state_role<NT / 2, DV, GDR2, HIST>(sm, a, tr, row0, state_off, hist_off, nsteps,
+                                           (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane,
+                                           rr, p);
         return;
       }
     }
-    state_role<NT, DV, GDR2>(sm, a, tr, row0, state_off, nsteps, 16 * NT * j, lane, rr, p);
+    state_role<NT, DV, GDR2, HIST>(sm, a, tr, row0, state_off, hist_off, nsteps, 16 * NT * j,
+                                   lane, rr, p);
   }
 }
 
@@ -702,11 +543,14 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
 
 template <int NS, int NT, bool PER_CHANNEL>
 hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
-  if (a.erase)
-    chunk_mfma_kernel<NS, NT, PER_CHANNEL, true>
+  if (a.hist)
+    chunk_mfma_kernel<NS, NT, PER_CHANNEL, false, true>
+        <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
+  else if (a.erase)
+    chunk_mfma_kernel<NS, NT, PER_CHANNEL, true, false>
         <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
   else
-    chunk_mfma_kernel<NS, NT, PER_CHANNEL, false>
+    chunk_mfma_kernel<NS, NT, PER_CHANNEL, false, false>
         <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -723,6 +567,14 @@ size_t chunk_plan_bytes(int N, int H, int dv) {
   if (N > kMaxPlanSeqs) return 0;  // too many sequences to sort in one workgroup: no schedule
   const size_t words = 1 + 2 * (size_t)N * H;
   return (words * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipStream_t stream) {
+  ChunkArgs a = args;
+  if (!a.hist || a.erase) return hipErrorInvalidValue;
+  a.o = nullptr;
+  a.plan = nullptr;  // one workgroup per chain, or per half of its columns (launch_chunk_mfma)
+  return launch_chunk_mfma(a, per_channel, stream);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& args, bool per_channel, hipStream_t stream) {

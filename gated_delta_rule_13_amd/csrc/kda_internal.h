@@ -32,6 +32,23 @@ struct ChunkArgs {
   // Without a work list: split every chain's value columns over two workgroups (the two
   // halves of a chain 8 items apart). Chosen on the host for equal-length batches.
   int split_all;
+  // Backward pass only: the state history (see hist_chain_offset), or nullptr.
+  void* hist;
+};
+
+// Arguments of one kda_chunk_bwd call (shapes and validation as kda_chunk_fwd).
+struct BwdArgs {
+  ChunkArgs f;             // the forward's inputs (o, sT, plan unused)
+  const void* dout;        // [B, H, T, dv] gradient of the loss with respect to o
+  const float* dsT;        // [N, H, dk, dv] gradient with respect to the final states, or nullptr
+  void* dq;                // [B, H, T, dk]
+  void* dk;                // [B, H, T, dk]
+  void* dv;                // [B, H, T, dv]
+  float* dg;               // like g
+  float* dbeta;            // [B, H, T]
+  float* ds0;              // [N, H, dk, dv] or nullptr
+  void* hist_s;            // workspace: states at every 16-token block start
+  void* hist_ds;           // workspace: state gradients at every 16-token block end
 };
 
 // Arguments of one kda_recurrent_step call.
@@ -86,5 +103,13 @@ hipError_t launch_prologue(const PrologueArgs& a, int dk, bool bf16, hipStream_t
 hipError_t launch_epilogue(const EpilogueArgs& a, int dv, bool bf16, hipStream_t stream);
 // Bytes of workspace the matrix-core path uses for its schedule (0: no schedule).
 size_t chunk_plan_bytes(int N, int H, int dv);
+
+// Backward pass (bf16, dk = 128, dv in {64, 128}, one decay per channel or per head).
+bool chunk_bwd_supports(int dk, int dv, int T);
+// Bytes of one of the two state histories of the backward pass.
+size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed);
+// Forward state pass that records the history (kda_chunk_mfma.hip).
+hipError_t launch_chunk_mfma_hist(const ChunkArgs& a, bool per_channel, hipStream_t stream);
+hipError_t launch_chunk_bwd(const BwdArgs& a, bool per_channel, hipStream_t stream);
 
 }  // namespace kda

@@ -198,6 +198,45 @@ kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, fl
                         void* o_out, int B, int H, int T, int dv, kda_dtype dt,
                         hipStream_t stream);
 
+/*
+ * Bytes of device workspace that kda_chunk_bwd needs for these shapes (0 when the call
+ * would be rejected as unsupported): two bf16 state histories of dk * dv / 8 bytes per
+ * token, sequences padded to whole 64-token steps.
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt);
+
+/*
+ * Backward pass of kda_chunk_fwd: the gradients of a scalar loss L with respect to every
+ * input, given dL/do and dL/dS_T. The pages describe the forward only; these are its
+ * derivatives (the chain rule through the chunkwise form of "Token Mixer I", section
+ * "Kimi Delta Attention", recomputing the forward states; exact up to rounding).
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv, gm:
+ *                    the forward's inputs, as in kda_chunk_fwd
+ *   grad_o           [B, H, T, dv], dtype dt: dL/do
+ *   grad_final_state float32 [N, H, dk, dv] or NULL (= 0): dL/dS_T
+ *   grad_q, grad_k   [B, H, T, dk], dtype dt        grad_v  [B, H, T, dv], dtype dt
+ *   grad_g           float32, shaped like g          grad_beta  float32 [B, H, T]
+ *   grad_initial_state float32 [N, H, dk, dv], or NULL (not written)
+ *   workspace        device buffer of at least kda_chunk_bwd_workspace_size(...) bytes,
+ *                    owned by the caller (contents on entry ignored; calls that overlap
+ *                    on one workspace race)
+ * Gradients are written for every token of every sequence; tokens outside every
+ * sequence are left untouched. Supported: dt = KDA_BF16, dk = 128, dv = 64 or 128, either
+ * gate mode (anything else: KDA_ERR_UNSUPPORTED). A NULL required array, a workspace
+ * smaller than the size above, or the forward's argument errors: KDA_ERR_INVALID_ARG.
+ * Arithmetic: bf16 operands on the matrix cores with float32 accumulation and float32
+ * state gradients; the stored forward states are bf16.
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, const void* grad_o,
+                         const float* grad_final_state, void* grad_q, void* grad_k,
+                         void* grad_v, float* grad_g, float* grad_beta,
+                         float* grad_initial_state, const int32_t* cu_seqlens, int num_seqs,
+                         int B, int H, int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -10,6 +10,7 @@ the method's arithmetic: no decay, no state update, no chunking.
 from .generate import (  # noqa: F401
     CONFIGS,
     ChunkInputs,
+    Cotangents,
     DecodeInputs,
     GateInputs,
     WorkloadConfig,
@@ -17,6 +18,7 @@ from .generate import (  # noqa: F401
     decode_step_inputs,
     decode_initial_state,
     make_chunk_inputs,
+    make_cotangents,
     make_gate_inputs,
     varlen_lengths,
 )

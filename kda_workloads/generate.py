@@ -300,3 +300,20 @@ def make_gate_inputs(cfg: WorkloadConfig) -> GateInputs:
     A_log = np.log(rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
     weight = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
     return GateInputs(q_in, k_in, u, A_log, dt_bias, beta_in, z, weight)
+
+
+@dataclass
+class Cotangents:
+    """Gradients of a loss with respect to the forward's outputs, for the backward pass."""
+    do: np.ndarray      # [B, H, T, dv], ~ N(0, 1) (bf16-rounded for bf16 workloads)
+    dsT: np.ndarray     # [N, H, dk, dv], ~ N(0, 0.1^2)
+
+
+def make_cotangents(cfg: WorkloadConfig, n_seqs: int) -> Cotangents:
+    """Seeded cotangents of a prefill workload (tensor ids 16 and 17)."""
+    B, H, T, dk, dv, sd = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.seed
+    do = _blocks(sd, 16, (B, H), (T, dv), _normal)
+    if cfg.dtype == "bf16":
+        do = bf16_round(do)
+    dsT = (np.float32(0.1) * _blocks(sd, 17, (n_seqs, H), (dk, dv), _normal)).astype(np.float32)
+    return Cotangents(do, dsT)

@@ -201,3 +201,44 @@ def epilogue_call(**over):
 ])
 def test_epilogue_rejects(over, code):
     assert epilogue_call(**over) == code
+
+
+def test_bwd_workspace_size():
+    # two bf16 histories of dk * dv / 8 bytes per padded token: 2 x 32 x (4096 + 64 * 2) x 2048
+    one = 32 * (4096 + 64 * 2) * 2048
+    assert kda.kda_chunk_bwd_workspace_size(1, 32, 4096, 128, 128, 2, kda.KDA_BF16) == 2 * one
+    # equal lengths: B sequences padded to 64 tokens each
+    one = 16 * 2 * 4096 * 1024
+    assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 64, 0, kda.KDA_BF16) == 2 * one
+    assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_F32) == 0
+    assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 64, 128, 0, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_bwd_workspace_size(0, 16, 4096, 128, 128, 0, kda.KDA_BF16) == 0
+
+
+def bwd_call(**over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, beta=DUMMY, initial_state=None,
+                grad_o=DUMMY, grad_final_state=None, grad_q=DUMMY, grad_k=DUMMY, grad_v=DUMMY,
+                grad_g=DUMMY, grad_beta=DUMMY, grad_initial_state=None, cu_seqlens=None,
+                num_seqs=0, B=1, H=2, T=64, dk=128, dv=128, dt=kda.KDA_BF16,
+                gm=kda.KDA_GATE_PER_CHANNEL, workspace=DUMMY, workspace_bytes=0, stream=None)
+    args.update(over)
+    return kda.kda_chunk_bwd(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(grad_o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(grad_q=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(grad_g=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(grad_beta=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(gm=7), kda.KDA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=DUMMY, num_seqs=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(workspace_bytes=100), kda.KDA_ERR_INVALID_ARG),     # smaller than the size
+    (dict(workspace=None, workspace_bytes=1 << 30), kda.KDA_ERR_INVALID_ARG),
+    (dict(dt=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=96), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects(over, code):
+    assert bwd_call(**over) == code

@@ -1,0 +1,156 @@
+"""GPU parity of the backward pass (kda_chunk_bwd) against the fp64 backward oracle
+(oracle/kda_oracle_bwd.c, itself pinned to finite differences of the forward), through
+the C ABI.
+
+Every gradient (dq, dk, dv, dg, dbeta, dS0) is compared chain by chain with the normwise
+bound max |got - want| <= 2e-2 max |want| of bf16 inputs with fp32 accumulation, each
+tensor separately. Checked: both gate modes and value head sizes on ragged sequences with
+and without an initial state and a final-state cotangent; sequence lengths around the
+16- and 64-token block edges (packed); the B2 H16 T4096 workload in full; the packed
+H32 T65536 workload on sampled chains; tokens outside every sequence left untouched.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_13_amd as kda
+import oracle
+from kda_workloads import CONFIGS, make_chunk_inputs, make_cotangents
+from tests.gpu_util import TOL, assert_close, note, up
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta")
+
+
+def run_bwd(x, ct, initial_state=True, final_cotangent=True, fill=None):
+    bf = torch.bfloat16
+    q, k, v, do = up(x.q, bf), up(x.k, bf), up(x.v, bf), up(ct.do, bf)
+    s0 = up(x.s0) if (initial_state and x.s0 is not None) else None
+    dsT = up(ct.dsT) if final_cotangent else None
+    cu = up(x.cu_seqlens, torch.int32) if x.cu_seqlens is not None else None
+    if fill is None:
+        out = kda.chunk_bwd(q, k, v, up(x.g), up(x.beta), do, initial_state=s0,
+                            grad_final_state=dsT, cu_seqlens=cu)
+    else:   # pre-filled outputs through the raw entry point (untouched-token check)
+        B, H, T, dk = x.q.shape
+        dv = x.v.shape[-1]
+        outs = [torch.full(x.q.shape, fill, dtype=bf, device=q.device) for _ in range(2)]
+        outs.append(torch.full(x.v.shape, fill, dtype=bf, device=q.device))
+        outs.append(torch.full(x.g.shape, fill, dtype=torch.float32, device=q.device))
+        outs.append(torch.full(x.beta.shape, fill, dtype=torch.float32, device=q.device))
+        N = x.n_seqs
+        ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+        ns = 0 if cu is None else N
+        gm = kda.KDA_GATE_PER_CHANNEL if x.g.ndim == 4 else kda.KDA_GATE_PER_HEAD
+        wsb = kda.kda_chunk_bwd_workspace_size(B, H, T, dk, dv, ns, kda.KDA_BF16)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        g, beta = up(x.g), up(x.beta)
+        st = kda.kda_chunk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                               beta.data_ptr(), s0.data_ptr() if s0 is not None else None,
+                               do.data_ptr(), dsT.data_ptr() if dsT is not None else None,
+                               *[o.data_ptr() for o in outs], ds0.data_ptr(),
+                               cu.data_ptr() if cu is not None else None, ns, B, H, T, dk, dv,
+                               kda.KDA_BF16, gm, ws.data_ptr(), wsb,
+                               torch.cuda.current_stream().cuda_stream)
+        assert st == kda.KDA_OK, kda.kda_status_string(st)
+        out = (*outs, ds0)
+    torch.cuda.synchronize()
+    return {name: t.float().cpu().numpy() for name, t in zip(NAMES + ("ds0",), out)}
+
+
+def oracle_grads(x, ct, chains=None, initial_state=True, final_cotangent=True):
+    return oracle.kda_backward(x.q, x.k, x.v, x.g, x.beta, ct.do,
+                               s0=x.s0 if initial_state else None,
+                               dsT=ct.dsT if final_cotangent else None,
+                               cu_seqlens=x.cu_seqlens, chains=chains)
+
+
+def check(x, got, ref, what, tol=TOL["bf16"]):
+    errs = {}
+    for name in NAMES + ("ds0",):
+        g_parts, w_parts = [], []
+        for (n, h), r in ref.items():
+            if name == "ds0":
+                g_parts.append(got["ds0"][n, h])
+            else:
+                b, t0, ln = x.chain_rows(n, h)
+                g_parts.append(got[name][b, h, t0:t0 + ln])
+            w_parts.append(r[name])
+        gg = np.concatenate([a.ravel() for a in g_parts])
+        ww = np.concatenate([a.ravel() for a in w_parts])
+        errs[name] = assert_close(gg, ww, tol, f"{what}: {name}")
+    return errs
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("dv", [128, 64])
+def test_bwd_small_ragged(gate, dv):
+    cfg = CONFIGS[1].replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=81, random_s0=True)
+    note(f"bwd small {gate} dv={dv}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct), f"bwd {gate} dv={dv}")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("initial_state,final_cotangent", [(False, False), (True, False),
+                                                            (False, True)])
+def test_bwd_optional_states(initial_state, final_cotangent):
+    cfg = CONFIGS[1].replace(B=1, H=2, T=150, seed=82, random_s0=True)
+    note(f"bwd s0={initial_state} dsT={final_cotangent}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    got = run_bwd(x, ct, initial_state, final_cotangent)
+    check(x, got, oracle_grads(x, ct, initial_state=initial_state,
+                               final_cotangent=final_cotangent), "bwd optional states")
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+def test_bwd_varlen_edge_lengths(gate):
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(gate=gate, H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05,
+                             seed=83)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(8).standard_normal((len(lens), 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    ct = make_cotangents(cfg, len(lens))
+    note(f"bwd varlen edges {gate}")
+    got = run_bwd(x, ct, fill=float("nan"))
+    for name in NAMES:
+        tail = got[name][0, :, cu[-1]:]
+        assert np.all(np.isnan(tail)), f"{name}: tokens outside every sequence were written"
+    check(x, got, oracle_grads(x, ct), f"bwd varlen edges {gate}")
+
+
+def test_bwd_b2_h16_t4096_full():
+    cfg = CONFIGS[1]
+    note(f"bwd parity {cfg.name}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct), cfg.name)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_bwd_gdn_b1_h16_t8192_sampled_chains():
+    cfg = CONFIGS[2]
+    note(f"bwd parity {cfg.name} (sampled chains)")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    chains = [(0, 0), (0, 7), (0, 15)]
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct, chains), cfg.name)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_bwd_varlen_t65536_sampled_chains():
+    cfg = CONFIGS[3]
+    note(f"bwd parity {cfg.name} (sampled chains)")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    lens = np.diff(x.cu_seqlens)
+    chains = sorted({(int(np.argmax(lens)), 3), (int(np.argmin(lens)), 30), (2, 17)})
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct, chains), cfg.name)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
