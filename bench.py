@@ -17,6 +17,7 @@ Printed (one JSON line on stdout):
   gdr2           the Gated Delta Rule-2 forward and decode step on the same workloads
   gates          the fused prologue (L2Norm, decay gate, sigmoid) and epilogue (gated
                  RMSNorm) on the chunk workload's rows, against the HBM roofline
+  bwd            kda_chunk_bwd (all gradients) on the chunk workload
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
 """
 
@@ -183,6 +184,52 @@ def bench_gates(torch, kda, cfg, steps: int, warmup: int):
     return out
 
 
+def bwd_alg_bytes(x) -> float:
+    """Inputs read once and outputs written once: q, k, v, dO (bf16), g (fp32 per channel),
+    beta (fp32); dq, dk, dv (bf16), dg, dbeta (fp32); plus the initial state, the final
+    state's gradient and the initial state's gradient of every chain (fp32)."""
+    B, H, T, dk = x.q.shape
+    dv = x.v.shape[-1]
+    g = 4 * (dk if x.g.ndim == 4 else 1)
+    per_tok = 2 * 2 * (2 * dk + dv) + 2 * dv + 2 * (g + 4)
+    n_chains = x.n_seqs * H
+    state = 4 * dk * dv * n_chains * (3 if x.s0 is not None else 2)
+    return float(per_tok * B * H * T + state)
+
+
+def bench_bwd(torch, kda, x, steps: int, warmup: int):
+    """kda_chunk_bwd on the workload (all gradients, with the final-state cotangent)."""
+    from kda_workloads import make_cotangents
+    dev = torch.device("cuda:0")
+    up = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)  # noqa
+    bf = torch.bfloat16
+    ct = make_cotangents(x.cfg, x.n_seqs)
+    q, k, v, do = up(x.q, bf), up(x.k, bf), up(x.v, bf), up(ct.do, bf)
+    g, beta, dsT = up(x.g), up(x.beta), up(ct.dsT)
+    s0 = up(x.s0) if x.s0 is not None else None
+    cu = up(x.cu_seqlens, torch.int32) if x.cu_seqlens is not None else None
+    B, H, T, dk = x.q.shape
+    dv = x.v.shape[-1]
+    outs = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+            torch.empty_like(beta)]
+    ds0 = torch.empty((x.n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    ns = x.n_seqs if cu is not None else 0
+    gm = kda.KDA_GATE_PER_CHANNEL if x.g.ndim == 4 else kda.KDA_GATE_PER_HEAD
+    wsb = kda.kda_chunk_bwd_workspace_size(B, H, T, dk, dv, ns, kda.KDA_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+
+    def call():
+        rc = kda.kda_chunk_bwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(s0), ptr(do),
+                               ptr(dsT), *[o.data_ptr() for o in outs], ds0.data_ptr(), ptr(cu),
+                               ns, B, H, T, dk, dv, kda.KDA_BF16, gm, ws.data_ptr(), wsb, stream)
+        if rc != kda.KDA_OK:
+            raise RuntimeError(f"kda_chunk_bwd returned {rc}")
+    ms = time_calls(torch, call, steps, warmup)
+    return ms, wsb
+
+
 def bench_chunk(torch, kda, x, steps: int, warmup: int):
     dev = torch.device("cuda:0")
     up = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)  # noqa
@@ -314,6 +361,7 @@ def main() -> int:
                     help="skip the Gated Delta Rule-2 measurements")
     ap.add_argument("--no-gates", action="store_true",
                     help="skip the prologue / epilogue measurements")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -397,6 +445,16 @@ def main() -> int:
                 "workload": gd.name, "steps": gd.T, "us_per_step": sec / gd.T * 1e6,
                 "hbm_gbs": dgbs, "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
+    if not args.no_bwd:
+        bms, wsb = bench_bwd(torch, kda, x, args.steps, args.warmup)
+        bbytes = bwd_alg_bytes(x)
+        bgbs = bbytes / (bms / 1e3) / 1e9
+        result["bwd"] = {
+            "workload": cfg.name, "ms_per_step": bms, "tokens_per_s": cfg.T / (bms / 1e3),
+            "workspace_bytes": wsb,
+            "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bgbs / HBM_PEAK_GBS, "alg_bytes_per_launch": bbytes}}
+        log(f"chunk_bwd: {bms:.3f} ms/step, {cfg.T / bms / 1e3:.2f} M tokens/s, {bgbs:.0f} GB/s")
     if not args.no_gates:
         result["gates"] = dict(workload=cfg.name, **bench_gates(torch, kda, cfg, args.steps,
                                                                  args.warmup))

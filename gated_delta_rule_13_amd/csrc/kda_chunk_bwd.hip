@@ -337,21 +337,16 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
 
 constexpr int kGThreads = 256;  // four wavefronts per 16-token block
 
+// LDS of one block (about 50 KB for dv = 128, so that three blocks share a CU).
 template <int DV>
 struct GSmem {
-  float P[16][kDK];        // decay from the block start through token t
-  float E[16][kDK];        // decay after token t
+  float P[16][kDK];        // decay from the block start through token t; later d log P_t
   float gam[kDK];
-  bf16 qraw[16][kLDK];     // the bf16 inputs
-  bf16 kraw[16][kLDK];
-  bf16 qh[16][kLDK];       // Qh, Kh, Kb, Kt as bf16 operands
+  bf16 qh[16][kLDK];       // Qh, Kh, Kb, Kt as bf16 operands (qh, kh later hold dq, dk)
   bf16 kh[16][kLDK];
   bf16 kb[16][kLDK];
   bf16 kt[16][kLDK];
-  bf16 srow[kDK][DV + 8];  // S and dS' of the block, row-major
-  bf16 dsrow[kDK][DV + 8];
-  bf16 vr[16][DV + 8];     // token rows of V, dO, U, dY, Diag(beta) dY
-  bf16 dor[16][DV + 8];
+  bf16 dor[16][DV + 8];    // token rows of dO, U, dY and Diag(beta) dY
   bf16 ur[16][DV + 8];
   bf16 dyr[16][DV + 8];
   bf16 bdyr[16][DV + 8];
@@ -363,9 +358,6 @@ struct GSmem {
   float beta[16];
   float r1[16];            // sum_j dY_tj R_tj
   float dlgam[kDK];        // d log Gam
-  float dlp[16][kDK];      // d log P_t
-  bf16 dqr[16][kLDK];      // dq, dk staged as token rows
-  bf16 dkr[16][kLDK];
 };
 
 // Position of work item (16-token block) `slot` of head h: sequence n and block blk, or
@@ -393,10 +385,21 @@ __device__ __forceinline__ bool grad_item(const ChunkArgs& a, int slot, int& n, 
   return blk >= 0 && blk * 16 < tr.len;
 }
 
+// Selector of channels 16 hh + n out of a 32-channel slab, as the B operand of a
+// 16x16x32 product: with an S tile as the A operand (lane 16 p + r holds channels
+// 8 p + i of column r) the product is the tile transposed, D[4p + e][n] = S[16 hh + n]
+// [column 4 p + e], exactly (one nonzero term per entry).
+__device__ __forceinline__ bf16x8 selector(int hh, int rr, int p) {
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = static_cast<bf16>(8 * p + i == 16 * hh + rr ? 1.f : 0.f);
+  return b;
+}
+
 template <int DV, bool PER_CHANNEL>
 __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, int slots) {
-  constexpr int NTW = DV / 64;     // value tiles per wavefront
-  constexpr int LDV = DV + 8;
+  constexpr int NTW = DV / 64;     // value tiles per wavefront in phase A
+  constexpr int NCT = DV / 16;     // value tiles of the block
   __shared__ __align__(16) GSmem<DV> sm;
   const ChunkArgs& a = b.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -408,103 +411,91 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + 16 * (size_t)blk;
   const int len = min(16, tr.len - 16 * blk);  // tokens of this block in the sequence
   const size_t hoff = hist_chain_offset(a, n, h, tr) + (size_t)blk * kDK * DV * 2;
+  const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, len * kDK * 2);
+  const rsrc_t ks_ = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, len * kDK * 2);
+  const rsrc_t hs = make_rsrc(static_cast<const char*>(b.hist_s) + hoff, kDK * DV * 2);
+  const rsrc_t hd = make_rsrc(static_cast<const char*>(b.hist_ds) + hoff, kDK * DV * 2);
 
-  // ---- 1. inputs: q, k rows; v, dO rows; S and dS' tiles; the decay of every channel
-  {
-    const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, len * kDK * 2);
-    const rsrc_t ks = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, len * kDK * 2);
-    const int t = tid >> 4, c8 = 8 * (tid & 15);
-    const uint32_t off = (uint32_t)(t * kDK + c8) * 2;
-    *reinterpret_cast<f32x4*>(&sm.qraw[t][c8]) = ld_b128(qs, off);
-    *reinterpret_cast<f32x4*>(&sm.kraw[t][c8]) = ld_b128(ks, off);
-    const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
-    const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
-    for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
-      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
-      const uint32_t o2 = (uint32_t)(tt * DV + cc) * 2;
-      *reinterpret_cast<f32x4*>(&sm.vr[tt][cc]) = ld_b128(vs, o2);
-      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, o2);
-    }
-  }
-  // S and dS' tiles of this wavefront's value columns, in registers (B operands) and
-  // as rows in LDS
-  bf16x8 sb[NTW][4], db[NTW][4];
-  {
-    const rsrc_t hs = make_rsrc(static_cast<const char*>(b.hist_s) + hoff, kDK * DV * 2);
-    const rsrc_t hd = make_rsrc(static_cast<const char*>(b.hist_ds) + hoff, kDK * DV * 2);
-#pragma unroll
-    for (int c = 0; c < NTW; ++c)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ct = wave * NTW + c;
-        const uint32_t off = (uint32_t)(((ct * 4 + ks) * 64 + lane) * 16);
-        sb[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
-        db[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
-        const int col = 16 * ct + rr;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          sm.srow[32 * ks + 8 * p + i][col] = sb[c][ks][i];
-          sm.dsrow[32 * ks + 8 * p + i][col] = db[c][ks][i];
-        }
-      }
-  }
+  // ---- 0. decay of every channel; dO rows and beta
   if (tid < kDK) {
-    // channel tid: prefix and suffix products of alpha over the block
     const int c = tid;
-    float al[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float gv = t < len ? (PER_CHANNEL ? a.g[(row0 + t) * kDK + c] : a.g[row0 + t]) : 0.f;
-      al[t] = __expf(gv);
-    }
     float run = 1.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      run *= al[t];
+      const float gv = t < len ? (PER_CHANNEL ? a.g[(row0 + t) * kDK + c] : a.g[row0 + t]) : 0.f;
+      run *= __expf(gv);
       sm.P[t][c] = run;
     }
     sm.gam[c] = run;
-    float suf = 1.f;
-#pragma unroll
-    for (int t = 15; t >= 0; --t) {
-      sm.E[t][c] = suf;
-      suf *= al[t];
-    }
   } else if (tid < kDK + 16) {
     const int t = tid - kDK;
     sm.beta[t] = t < len ? a.beta[row0 + t] : 0.f;
     sm.r1[t] = 0.f;
   }
+  {
+    const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
+    for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
+      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
+    }
+  }
+  const int t8 = tid >> 4, c8 = 8 * (tid & 15);
+  const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld_b128(qs, (uint32_t)(t8 * kDK + c8) * 2));
+  const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld_b128(ks_, (uint32_t)(t8 * kDK + c8) * 2));
   __syncthreads();
 
-  // ---- 2. the decayed operands (bf16) for the matrix cores
+  // ---- 1. the decayed operands (bf16) for the matrix cores
   {
-    const int t = tid >> 4, c8 = 8 * (tid & 15);
-    bf16x8 q8 = *reinterpret_cast<const bf16x8*>(&sm.qraw[t][c8]);
-    bf16x8 k8 = *reinterpret_cast<const bf16x8*>(&sm.kraw[t][c8]);
     float qh[8], kh[8], kb[8], kt[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float P = sm.P[t][c8 + i], E = sm.E[t][c8 + i];
-      const float rg = __builtin_amdgcn_rcpf(sm.gam[c8 + i]);
+      const float P = sm.P[t8][c8 + i], G = sm.gam[c8 + i];
+      const float rp = __builtin_amdgcn_rcpf(P);
       const float qf = static_cast<float>(q8[i]), kf = static_cast<float>(k8[i]);
       qh[i] = qf * P;
       kh[i] = kf * P;
-      kt[i] = kf * E;
-      kb[i] = kt[i] * rg;
+      kb[i] = kf * rp;       // k / P
+      kt[i] = kb[i] * G;     // k E = k Gam / P
     }
-    *reinterpret_cast<bf16x8*>(&sm.qh[t][c8]) = cat8(pack4(qh[0], qh[1], qh[2], qh[3]),
-                                                      pack4(qh[4], qh[5], qh[6], qh[7]));
-    *reinterpret_cast<bf16x8*>(&sm.kh[t][c8]) = cat8(pack4(kh[0], kh[1], kh[2], kh[3]),
-                                                      pack4(kh[4], kh[5], kh[6], kh[7]));
-    *reinterpret_cast<bf16x8*>(&sm.kb[t][c8]) = cat8(pack4(kb[0], kb[1], kb[2], kb[3]),
-                                                      pack4(kb[4], kb[5], kb[6], kb[7]));
-    *reinterpret_cast<bf16x8*>(&sm.kt[t][c8]) = cat8(pack4(kt[0], kt[1], kt[2], kt[3]),
-                                                      pack4(kt[4], kt[5], kt[6], kt[7]));
+    *reinterpret_cast<bf16x8*>(&sm.qh[t8][c8]) = cat8(pack4(qh[0], qh[1], qh[2], qh[3]),
+                                                       pack4(qh[4], qh[5], qh[6], qh[7]));
+    *reinterpret_cast<bf16x8*>(&sm.kh[t8][c8]) = cat8(pack4(kh[0], kh[1], kh[2], kh[3]),
+                                                       pack4(kh[4], kh[5], kh[6], kh[7]));
+    *reinterpret_cast<bf16x8*>(&sm.kb[t8][c8]) = cat8(pack4(kb[0], kb[1], kb[2], kb[3]),
+                                                       pack4(kb[4], kb[5], kb[6], kb[7]));
+    *reinterpret_cast<bf16x8*>(&sm.kt[t8][c8]) = cat8(pack4(kt[0], kt[1], kt[2], kt[3]),
+                                                       pack4(kt[4], kt[5], kt[6], kt[7]));
+  }
+  // S and dS' tiles: this wavefront's value tiles (all channels, phase 2) and its
+  // 32-channel slab (all value tiles, phase 3), as stored (lane-native 16-byte pieces)
+  bf16x8 sa[NTW][4], da[NTW][4], sl[NCT], dl[NCT];
+#pragma unroll
+  for (int c = 0; c < NTW; ++c)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t off = (uint32_t)((((wave * NTW + c) * 4 + ks) * 64 + lane) * 16);
+      sa[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
+      da[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
+    }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const uint32_t off = (uint32_t)(((ct * 4 + wave) * 64 + lane) * 16);
+    sl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
+    dl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
+  }
+  // V of this wavefront's columns (token 4 p + e)
+  bf16 vv[NTW][4];
+  {
+    const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
+#pragma unroll
+    for (int c = 0; c < NTW; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[c][e] = ld_b16(vs, (uint32_t)((4 * p + e) * DV + 16 * (wave * NTW + c) + rr) * 2);
   }
   __syncthreads();
 
-  // ---- 3. A, M and Tm of the block (one wavefront)
+  // ---- 1b. A, M and Tm of the block (one wavefront)
   if (wave == 0) {
     f32x4 accq = zero4(), acck = zero4(), acct = zero4();
 #pragma unroll
@@ -533,7 +524,7 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
   }
   __syncthreads();
 
-  // ---- 4. per value tile: R, U, dU, dY (token 4p + e, column 16 ct + rr)
+  // ---- 2. this wavefront's value tiles: R, U, dU, dY (token 4p + e, column 16 ct + rr)
   {
     bf16x4 tA, tT, mT;
 #pragma unroll
@@ -554,14 +545,14 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.kh[rr][32 * ks + 8 * p]);
         const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sm.kt[rr][32 * ks + 8 * p]);
-        X = mfma32(ah, sb[c][ks], X);       // (Kh S)[4p + e][col]
-        dU2 = mfma32(at, db[c][ks], dU2);   // (Kt dS')[4p + e][col]
+        X = mfma32(ah, sa[c][ks], X);       // (Kh S)[4p + e][col]
+        dU2 = mfma32(at, da[c][ks], dU2);   // (Kt dS')[4p + e][col]
       }
       f32x4 R, x;
       bf16x4 dob;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        R[e] = static_cast<float>(sm.vr[4 * p + e][col]) - X[e];
+        R[e] = static_cast<float>(vv[c][e]) - X[e];
         x[e] = bt[e] * R[e];
         dob[e] = sm.dor[4 * p + e][col];
       }
@@ -576,7 +567,6 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
         r1[e] += dY[e] * R[e];
       }
     }
-    // sum r1 over the 16 columns of each lane group, then over the wavefronts
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float v = r1[e];
@@ -589,57 +579,63 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
   }
   __syncthreads();
 
-  // ---- 5. contractions over the value columns; wavefront w: channel tiles 2w, 2w + 1
+  // ---- 3. contractions over the value columns for this wavefront's channel slab
+  // (channels 32 w + 16 hh + rr), with S and dS' transposed by selector products
   f32x4 C1[2], C2[2], C3[2];
+  float r2[2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    C1[mt] = C2[mt] = C3[mt] = zero4();
-    const int ch = 16 * (2 * wave + mt) + rr;
+  for (int hh = 0; hh < 2; ++hh) {
+    const bf16x8 sel = selector(hh, rr, p);
+    C1[hh] = C2[hh] = C3[hh] = zero4();
+    r2[hh] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < DV / 32; ++kk) {
-      const int j = 32 * kk + 8 * p;
-      const bf16x8 s8 = *reinterpret_cast<const bf16x8*>(&sm.srow[ch][j]);
-      const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(&sm.dsrow[ch][j]);
-      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dor[rr][j]);
-      const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&sm.bdyr[rr][j]);
-      const bf16x8 au = *reinterpret_cast<const bf16x8*>(&sm.ur[rr][j]);
-      C1[mt] = mfma32(ao, s8, C1[mt]);   // (dO S^T)[4p + e][ch]
-      C2[mt] = mfma32(ay, s8, C2[mt]);   // (Diag(beta) dY S^T)[4p + e][ch]
-      C3[mt] = mfma32(au, d8, C3[mt]);   // (U dS'^T)[4p + e][ch]
+    for (int ct = 0; ct < NCT; ++ct) {
+      const f32x4 st = mfma32(sl[ct], sel, zero4());   // S[ch][16 ct + 4p + e]
+      const f32x4 dt = mfma32(dl[ct], sel, zero4());   // dS'[ch][16 ct + 4p + e]
+      const int j = 16 * ct + 4 * p;
+      const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][j]);
+      const bf16x4 ay = *reinterpret_cast<const bf16x4*>(&sm.bdyr[rr][j]);
+      const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.ur[rr][j]);
+      const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
+      C1[hh] = mfma16(ao, sb4, C1[hh]);   // (dO S^T)[4p + e][ch]
+      C2[hh] = mfma16(ay, sb4, C2[hh]);   // (Diag(beta) dY S^T)[4p + e][ch]
+      C3[hh] = mfma16(au, db4, C3[hh]);   // (U dS'^T)[4p + e][ch]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r2[hh] += st[e] * dt[e];
     }
+    r2[hh] += __shfl_xor(r2[hh], 16, 64);
+    r2[hh] += __shfl_xor(r2[hh], 32, 64);
   }
-  if (wave == 0) {
-    f32x4 g1 = zero4(), g2 = zero4();
+  if (wave == 0 || wave == 1) {
+    // G1 = dO U^T (wavefront 0), G2 = dY U^T (wavefront 1)
+    f32x4 gg = zero4();
 #pragma unroll
     for (int kk = 0; kk < DV / 32; ++kk) {
       const int j = 32 * kk + 8 * p;
-      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dor[rr][j]);
-      const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&sm.dyr[rr][j]);
+      const bf16x8 aa = wave == 0 ? *reinterpret_cast<const bf16x8*>(&sm.dor[rr][j])
+                                  : *reinterpret_cast<const bf16x8*>(&sm.dyr[rr][j]);
       const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&sm.ur[rr][j]);
-      g1 = mfma32(ao, bu, g1);   // (dO U^T)[4p + e][rr]
-      g2 = mfma32(ay, bu, g2);   // (dY U^T)[4p + e][rr]
+      gg = mfma32(aa, bu, gg);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sm.G1[4 * p + e][rr] = g1[e];
-      sm.G2[4 * p + e][rr] = g2[e];
-    }
-  } else if (wave == 1) {
-    // Gam * rowsum(dS' * S): lane pair per channel
-    for (int c = lane; c < kDK; c += 64) {
-      float acc = 0.f;
-      for (int j = 0; j < DV; j += 8) {
-        const bf16x8 s8 = *reinterpret_cast<const bf16x8*>(&sm.srow[c][j]);
-        const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(&sm.dsrow[c][j]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc += static_cast<float>(s8[i]) * static_cast<float>(d8[i]);
-      }
-      sm.dlgam[c] = sm.gam[c] * acc;
+      if (wave == 0) sm.G1[4 * p + e][rr] = gg[e];
+      else sm.G2[4 * p + e][rr] = gg[e];
     }
   }
+  // q and k of this lane's elements (token 4p + e, channel 32 w + 16 hh + rr)
+  bf16 qe[2][4], ke[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t off = (uint32_t)((4 * p + e) * kDK + 32 * wave + 16 * hh + rr) * 2;
+      qe[hh][e] = ld_b16(qs, off);
+      ke[hh][e] = ld_b16(ks_, off);
+    }
   __syncthreads();
 
-  // ---- 6. the 16 x 16 corrections and the chain rule through the decay
+  // ---- 4. the 16 x 16 corrections and the chain rule through the decay
   {
     bf16x4 dmr, dar, dmT, daT;   // dM, dA rows rr and columns rr
 #pragma unroll
@@ -651,8 +647,8 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
       daT[i] = static_cast<bf16>(rr < s_ ? -sm.beta[s_] * sm.G2[s_][rr] : 0.f);
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int ch = 16 * (2 * wave + mt) + rr;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ch = 32 * wave + 16 * hh + rr;
       bf16x4 bkb, bkh, bqh;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -660,39 +656,38 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
         bkh[i] = sm.kh[4 * p + i][ch];
         bqh[i] = sm.qh[4 * p + i][ch];
       }
-      const f32x4 dQh = C1[mt] + mfma16(dmr, bkb, zero4());
-      const f32x4 dKh = mfma16(dar, bkb, zero4()) - C2[mt];
+      const f32x4 dQh = C1[hh] + mfma16(dmr, bkb, zero4());
+      const f32x4 dKh = mfma16(dar, bkb, zero4()) - C2[hh];
       const f32x4 dKb = mfma16(daT, bkh, zero4()) + mfma16(dmT, bqh, zero4());
-      const f32x4 dKt = C3[mt];
-      const float rg = __builtin_amdgcn_rcpf(sm.gam[ch]);
+      const f32x4 dKt = C3[hh];
+      const float G = sm.gam[ch];
       float lg = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 4 * p + e;
-        const float P = sm.P[t][ch], E = sm.E[t][ch];
-        const float qf = static_cast<float>(sm.qraw[t][ch]);
-        const float kf = static_cast<float>(sm.kraw[t][ch]);
-        const float qh = qf * P, kh = kf * P, kt = kf * E, kb = kt * rg;
-        sm.dqr[t][ch] = static_cast<bf16>(dQh[e] * P);
-        sm.dkr[t][ch] = static_cast<bf16>(dKh[e] * P + dKb[e] * E * rg + dKt[e] * E);
-        sm.dlp[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;
+        const float P = sm.P[t][ch], rp = __builtin_amdgcn_rcpf(P);
+        const float qf = static_cast<float>(qe[hh][e]), kf = static_cast<float>(ke[hh][e]);
+        const float qh = qf * P, kh = kf * P, kb = kf * rp, kt = kb * G;
+        // this wavefront's own channel columns: qh / kh / P are read above, then reused
+        sm.qh[t][ch] = static_cast<bf16>(dQh[e] * P);                                // dq
+        sm.kh[t][ch] = static_cast<bf16>(dKh[e] * P + (dKb[e] + dKt[e] * G) * rp);  // dk
+        sm.P[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;        // d log P
         lg += dKt[e] * kt;
       }
       lg += __shfl_xor(lg, 16, 64);
       lg += __shfl_xor(lg, 32, 64);
-      if (p == 0) sm.dlgam[ch] += lg;
+      if (p == 0) sm.dlgam[ch] = lg + G * r2[hh];
     }
   }
   __syncthreads();
 
-  // ---- 7. outputs: dq, dk, dv rows; dg (suffix sums); dbeta
+  // ---- 5. outputs: dq, dk, dv rows; dg (suffix sums); dbeta
   {
     const rsrc_t qd = make_rsrc(static_cast<bf16*>(b.dq) + row0 * kDK, len * kDK * 2);
     const rsrc_t kd = make_rsrc(static_cast<bf16*>(b.dk) + row0 * kDK, len * kDK * 2);
-    const int t = tid >> 4, c8 = 8 * (tid & 15);
-    const uint32_t off = (uint32_t)(t * kDK + c8) * 2;
-    st_b128(qd, off, *reinterpret_cast<const bf16x8*>(&sm.dqr[t][c8]));
-    st_b128(kd, off, *reinterpret_cast<const bf16x8*>(&sm.dkr[t][c8]));
+    const uint32_t off = (uint32_t)(t8 * kDK + c8) * 2;
+    st_b128(qd, off, *reinterpret_cast<const bf16x8*>(&sm.qh[t8][c8]));
+    st_b128(kd, off, *reinterpret_cast<const bf16x8*>(&sm.kh[t8][c8]));
     const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
     for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
       const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
@@ -704,7 +699,7 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
       const int c = tid;
       float acc = sm.dlgam[c];
       for (int t = 15; t >= 0; --t) {
-        acc += sm.dlp[t][c];
+        acc += sm.P[t][c];
         if (t < len) b.dg[(row0 + t) * kDK + c] = acc;
       }
     }
@@ -714,14 +709,14 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
       const int c = tid;
       float acc = sm.dlgam[c];
       for (int t = 15; t >= 0; --t) {
-        acc += sm.dlp[t][c];
-        sm.dlp[t][c] = acc;
+        acc += sm.P[t][c];
+        sm.P[t][c] = acc;
       }
     }
     __syncthreads();
     if (wave == 0) {
       for (int t = 0; t < 16; ++t) {
-        float v = sm.dlp[t][lane] + sm.dlp[t][lane + 64];
+        float v = sm.P[t][lane] + sm.P[t][lane + 64];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
         if (lane == 0 && t < len) b.dg[row0 + t] = v;
