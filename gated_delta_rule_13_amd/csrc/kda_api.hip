@@ -158,7 +158,9 @@ size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num
   if (!kda::chunk_bwd_supports(dk, dv, T)) return 0;
   const int N = num_seqs > 0 ? num_seqs : B;
   const size_t one = kda::chunk_bwd_hist_bytes(N, H, T, dv, num_seqs > 0);
-  return 2 * ((one + 255) / 256 * 256);
+  // the two histories, then the work list of packed sequences
+  const size_t plan = num_seqs > 0 ? kda::chunk_plan_bytes(num_seqs, H, dv) : 0;
+  return 2 * ((one + 255) / 256 * 256) + plan;
 }
 
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -191,8 +193,12 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
   b.dout = grad_o; b.dsT = grad_final_state;
   b.dq = grad_q; b.dk = grad_k; b.dv = grad_v; b.dg = grad_g; b.dbeta = grad_beta;
   b.ds0 = grad_initial_state;
+  const size_t one = (kda::chunk_bwd_hist_bytes((int)N, H, T, dv, cu_seqlens != nullptr) + 255) /
+                    256 * 256;
   b.hist_s = workspace;
-  b.hist_ds = static_cast<char*>(workspace) + need / 2;
+  b.hist_ds = static_cast<char*>(workspace) + one;
+  b.plan = need > 2 * one ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * one)
+                          : nullptr;
   const hipError_t err = kda::launch_chunk_bwd(b, gm == KDA_GATE_PER_CHANNEL, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -297,7 +297,19 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rr = lane & 15, p = lane >> 4;
   const ChunkArgs& a = b.f;
-  const int chain = blockIdx.x;
+  // work item: a chain, or one half of its value columns (the forward's schedule)
+  int chain = blockIdx.x, part = 0;
+  if (b.plan) {
+    if (blockIdx.x >= b.plan[0]) return;
+    const uint32_t item = b.plan[1 + blockIdx.x];
+    chain = (int)(item >> 2);
+    part = (int)(item & 3);
+  } else if (NT > 1 && a.split_all) {
+    uint32_t c, pt;
+    split_item(blockIdx.x, (uint32_t)(a.N * a.H), c, pt);
+    chain = (int)c;
+    part = (int)pt;
+  }
   const int n = chain / a.H, h = chain % a.H;
   const TokenRange tr = token_range(a.cu, n, a.T);
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
@@ -329,6 +341,13 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
   } else {
     __builtin_amdgcn_s_setprio(KDA_STATE_PRIO);
     const int j = wave - kPrepWaves;
+    if constexpr (NT > 1) {
+      if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
+        carry_role<NT / 2, DV>(sm, b, tr, row0, state_off, hist_off, nsteps,
+                               (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane, rr, p);
+        return;
+      }
+    }
     carry_role<NT, DV>(sm, b, tr, row0, state_off, hist_off, nsteps, 16 * NT * j, lane, rr, p);
   }
 }
@@ -337,7 +356,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
 
 constexpr int kGThreads = 256;  // four wavefronts per 16-token block
 
-// LDS of one block (about 50 KB for dv = 128, so that three blocks share a CU).
+// LDS of one block (about 50 KB for dv = 128).
 template <int DV>
 struct GSmem {
   float P[16][kDK];        // decay from the block start through token t; later d log P_t
@@ -396,8 +415,11 @@ __device__ __forceinline__ bf16x8 selector(int hh, int rr, int p) {
   return b;
 }
 
+// Three wavefronts per SIMD (at most 170 registers): three blocks share a CU (the LDS of
+// one is about 50 KB), measured 7% faster than the two that 205 registers allow.
 template <int DV, bool PER_CHANNEL>
-__global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, int slots) {
+__global__ __attribute__((amdgpu_waves_per_eu(3))) __launch_bounds__(kGThreads) void
+chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   constexpr int NTW = DV / 64;     // value tiles per wavefront in phase A
   constexpr int NCT = DV / 16;     // value tiles of the block
   __shared__ __align__(16) GSmem<DV> sm;
@@ -415,6 +437,31 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
   const rsrc_t ks_ = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, len * kDK * 2);
   const rsrc_t hs = make_rsrc(static_cast<const char*>(b.hist_s) + hoff, kDK * DV * 2);
   const rsrc_t hd = make_rsrc(static_cast<const char*>(b.hist_ds) + hoff, kDK * DV * 2);
+
+  // global loads first, so that their latency overlaps the first phases: q and k of this
+  // thread's 8 channels, the S and dS' tiles of this wavefront's value columns (all
+  // channels, as stored: lane-native 16-byte pieces) and V of those columns
+  const int t8 = tid >> 4, c8 = 8 * (tid & 15);
+  const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld_b128(qs, (uint32_t)(t8 * kDK + c8) * 2));
+  const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld_b128(ks_, (uint32_t)(t8 * kDK + c8) * 2));
+  bf16x8 sa[NTW][4], da[NTW][4];
+#pragma unroll
+  for (int c = 0; c < NTW; ++c)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t off = (uint32_t)((((wave * NTW + c) * 4 + ks) * 64 + lane) * 16);
+      sa[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
+      da[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
+    }
+  bf16 vv[NTW][4];
+  {
+    const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
+#pragma unroll
+    for (int c = 0; c < NTW; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[c][e] = ld_b16(vs, (uint32_t)((4 * p + e) * DV + 16 * (wave * NTW + c) + rr) * 2);
+  }
 
   // ---- 0. decay of every channel; dO rows and beta
   if (tid < kDK) {
@@ -439,9 +486,6 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
       *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
     }
   }
-  const int t8 = tid >> 4, c8 = 8 * (tid & 15);
-  const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld_b128(qs, (uint32_t)(t8 * kDK + c8) * 2));
-  const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld_b128(ks_, (uint32_t)(t8 * kDK + c8) * 2));
   __syncthreads();
 
   // ---- 1. the decayed operands (bf16) for the matrix cores
@@ -465,33 +509,6 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
                                                        pack4(kb[4], kb[5], kb[6], kb[7]));
     *reinterpret_cast<bf16x8*>(&sm.kt[t8][c8]) = cat8(pack4(kt[0], kt[1], kt[2], kt[3]),
                                                        pack4(kt[4], kt[5], kt[6], kt[7]));
-  }
-  // S and dS' tiles: this wavefront's value tiles (all channels, phase 2) and its
-  // 32-channel slab (all value tiles, phase 3), as stored (lane-native 16-byte pieces)
-  bf16x8 sa[NTW][4], da[NTW][4], sl[NCT], dl[NCT];
-#pragma unroll
-  for (int c = 0; c < NTW; ++c)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t off = (uint32_t)((((wave * NTW + c) * 4 + ks) * 64 + lane) * 16);
-      sa[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
-      da[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
-    }
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const uint32_t off = (uint32_t)(((ct * 4 + wave) * 64 + lane) * 16);
-    sl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
-    dl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
-  }
-  // V of this wavefront's columns (token 4 p + e)
-  bf16 vv[NTW][4];
-  {
-    const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
-#pragma unroll
-    for (int c = 0; c < NTW; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vv[c][e] = ld_b16(vs, (uint32_t)((4 * p + e) * DV + 16 * (wave * NTW + c) + rr) * 2);
   }
   __syncthreads();
 
@@ -525,6 +542,7 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
   __syncthreads();
 
   // ---- 2. this wavefront's value tiles: R, U, dU, dY (token 4p + e, column 16 ct + rr)
+  bf16x8 sl[NCT], dl[NCT];
   {
     bf16x4 tA, tT, mT;
 #pragma unroll
@@ -566,6 +584,13 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(BwdArgs b, in
         sm.bdyr[4 * p + e][col] = static_cast<bf16>(bt[e] * dY[e]);
         r1[e] += dY[e] * R[e];
       }
+    }
+    // S and dS' of this wavefront's 32-channel slab (all value tiles), for phase 3
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint32_t off = (uint32_t)(((ct * 4 + wave) * 64 + lane) * 16);
+      sl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
+      dl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -747,14 +772,24 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
   BwdArgs b = args;
   ChunkArgs& a = b.f;
   if (!chunk_bwd_supports(a.dk, a.dv, a.T) || a.erase) return hipErrorInvalidValue;
-  // 1. states at every block start
+  // 1. states at every block start (builds the work list of packed sequences)
   a.hist = b.hist_s;
   a.sT = nullptr;
+  a.plan = a.cu ? b.plan : nullptr;
   hipError_t e = launch_chunk_mfma_hist(a, per_channel, stream);
   if (e != hipSuccess) return e;
   a.hist = nullptr;
-  // 2. the carry, one workgroup per chain
-  const unsigned chains = (unsigned)a.N * a.H;
+  // 2. the carry, over the same work list (or every chain split when all halves fit)
+  b.plan = a.plan;
+  const bool can_split = a.dv == 128;
+  unsigned chains = (unsigned)a.N * a.H;
+  a.split_all = 0;
+  if (can_split && b.plan) {
+    chains *= 2;
+  } else if (can_split && a.cus > 0 && 2ll * a.N * a.H <= a.cus) {
+    a.split_all = 1;
+    chains *= 2;
+  }
   if (a.dv == 128) {
     if (per_channel) chunk_bwd_state_kernel<4, 2, true><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
     else chunk_bwd_state_kernel<4, 2, false><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);

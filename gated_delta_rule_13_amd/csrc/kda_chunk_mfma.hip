@@ -362,18 +362,6 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
   }
 }
 
-// Position `local` among the 2 n items of n split chains: groups of (up to) 8 chains list
-// their first halves, then their second halves, so the two halves of a chain are 8 items
-// apart. Workgroups are dispatched round-robin over the 8 XCDs, so both halves run on one
-// XCD and the second reads the chain's q, k, g through that XCD's L2.
-__host__ __device__ inline void split_item(uint32_t local, uint32_t n, uint32_t& chain,
-                                           uint32_t& part) {
-  const uint32_t group = local / 16, within = local % 16;
-  const uint32_t gsize = n - 8 * group < 8 ? n - 8 * group : 8;
-  chain = 8 * group + within % gsize;
-  part = 1 + within / gsize;
-}
-
 template <int NS, int NT, bool PER_CHANNEL, bool GDR2, bool HIST>
 __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(ChunkArgs a) {
   constexpr int DV = 16 * NS * NT;
@@ -573,8 +561,7 @@ hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipSt
   ChunkArgs a = args;
   if (!a.hist || a.erase) return hipErrorInvalidValue;
   a.o = nullptr;
-  a.plan = nullptr;  // one workgroup per chain, or per half of its columns (launch_chunk_mfma)
-  return launch_chunk_mfma(a, per_channel, stream);
+  return launch_chunk_mfma(a, per_channel, stream);  // builds the work list when a.plan is set
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& args, bool per_channel, hipStream_t stream) {

@@ -49,6 +49,7 @@ struct BwdArgs {
   float* ds0;              // [N, H, dk, dv] or nullptr
   void* hist_s;            // workspace: states at every 16-token block start
   void* hist_ds;           // workspace: state gradients at every 16-token block end
+  uint32_t* plan;          // workspace: the work list of the two sequential launches, or nullptr
 };
 
 // Arguments of one kda_recurrent_step call.

@@ -208,6 +208,18 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& nc, const f32x4
   return inv;
 }
 
+// Position `local` among the 2 n items of n split chains: groups of (up to) 8 chains list
+// their first halves, then their second halves, so the two halves of a chain are 8 items
+// apart. Workgroups are dispatched round-robin over the 8 XCDs, so both halves run on one
+// XCD and the second reads the chain's q, k, g through that XCD's L2.
+__host__ __device__ inline void split_item(uint32_t local, uint32_t n, uint32_t& chain,
+                                           uint32_t& part) {
+  const uint32_t group = local / 16, within = local % 16;
+  const uint32_t gsize = n - 8 * group < 8 ? n - 8 * group : 8;
+  chain = 8 * group + within % gsize;
+  part = 1 + within / gsize;
+}
+
 // State history of the backward pass. For every chain (sequence n, head h) the kernels
 // keep one dk x dv bf16 matrix per 16-token block of the chain (its 64-token steps
 // padded with identity tokens), stored as the 16x16x32 B operands of the state tiles:

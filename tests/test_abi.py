@@ -205,8 +205,10 @@ def test_epilogue_rejects(over, code):
 
 def test_bwd_workspace_size():
     # two bf16 histories of dk * dv / 8 bytes per padded token: 2 x 32 x (4096 + 64 * 2) x 2048
+    # (packed sequences: plus the 768-byte work list of 2 x 32 chains)
     one = 32 * (4096 + 64 * 2) * 2048
-    assert kda.kda_chunk_bwd_workspace_size(1, 32, 4096, 128, 128, 2, kda.KDA_BF16) == 2 * one
+    assert kda.kda_chunk_bwd_workspace_size(1, 32, 4096, 128, 128, 2, kda.KDA_BF16) == \
+        2 * one + 768
     # equal lengths: B sequences padded to 64 tokens each
     one = 16 * 2 * 4096 * 1024
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 64, 0, kda.KDA_BF16) == 2 * one
