@@ -27,17 +27,6 @@ const char* kda_status_string(kda_status s) {
   return "KDA_ERR_UNKNOWN: unknown status code";
 }
 
-size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
-                                    kda_dtype dt) {
-  // only the matrix-core path uses a workspace: its work list (every intermediate of the
-  // method stays on chip)
-  if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return 0;
-  if (dt != KDA_BF16 || !kda::chunk_mfma_supports(dk, dv, T)) return 0;
-  // equal-length batches are scheduled on the host: only packed sequences need one
-  if (num_seqs == 0 || (long long)num_seqs * H > (1ll << 24)) return 0;
-  return kda::chunk_plan_bytes(num_seqs, H, dv);
-}
-
 // Compute units of the current device, cached per device (sizes the chunk schedule).
 static int device_compute_units() {
   static int cached[64];
@@ -49,6 +38,22 @@ static int device_compute_units() {
     n = 256;
   if (dev >= 0 && dev < 64) cached[dev] = n;
   return n;
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt) {
+  // only the matrix-core path uses a workspace: its work list (every intermediate of the
+  // method stays on chip)
+  if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return 0;
+  if (dt != KDA_BF16 || !kda::chunk_mfma_supports(dk, dv, T)) return 0;
+  const long long N = num_seqs > 0 ? num_seqs : B;
+  if (N * H > (1ll << 24)) return 0;
+  // few chains for the device: segments and their states (this also covers the work list)
+  const size_t seg = kda::chunk_seg_bytes((int)N, H, T, dv, device_compute_units());
+  if (seg > 0) return seg;
+  // equal-length batches are scheduled on the host: only packed sequences need a work list
+  if (num_seqs == 0) return 0;
+  return kda::chunk_plan_bytes(num_seqs, H, dv);
 }
 
 // The two forward paths differ only in their gates: beta (KDA, Gated DeltaNet) or the
@@ -82,11 +87,16 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   a.cus = device_compute_units();
   a.split_all = 0;
   a.hist = nullptr;
+  a.seg_len = 0;
+  a.nseg = 1;
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
-  if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T))
-    err = kda::launch_chunk_mfma(a, per_channel, stream);
-  else
+  if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T)) {
+    if (scheduled && !erase && kda::chunk_seg_bytes(a.N, H, T, dv, a.cus) > 0)
+      err = kda::launch_chunk_mfma_segmented(a, per_channel, workspace, stream);
+    else
+      err = kda::launch_chunk_mfma(a, per_channel, stream);
+  } else
     err = kda::launch_chunk_f32(a, dt == KDA_BF16, per_channel, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -190,6 +200,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
   a.s0 = initial_state; a.sT = nullptr; a.o = nullptr; a.cu = cu_seqlens;
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
   a.plan = nullptr; a.cus = device_compute_units(); a.split_all = 0; a.hist = nullptr;
+  a.seg_len = 0; a.nseg = 1;
   b.dout = grad_o; b.dsT = grad_final_state;
   b.dq = grad_q; b.dk = grad_k; b.dv = grad_v; b.dg = grad_g; b.dbeta = grad_beta;
   b.ds0 = grad_initial_state;

@@ -54,6 +54,8 @@ constexpr int kC = 64;         // tokens prepared and consumed per step (four bl
 constexpr int kLDK = kDK + 8;  // padded LDS row (bf16) of [token][channel] tiles
 constexpr int kLDT = kC + 8;   // padded LDS row (bf16) of [channel][token] tiles
 constexpr int kPrepWaves = 4;  // one per 16-token block
+constexpr int kModeOut = 0, kModeHist = 1, kModeState = 2, kModeTrans = 3;  // see state_role
+constexpr int kModePair = 4;  // launch of both kModeState and kModeTrans items (see the kernel)
 
 #ifndef KDA_STATE_PRIO
 #define KDA_STATE_PRIO 3
@@ -222,15 +224,23 @@ __device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int s
 // straight-line instantiation (a tile count chosen at run time inside the loops would let
 // branches remove instructions that the wait states after the matrix-core products were
 // counted on).
-// With HIST (the backward pass's state pass) the wavefront records the state at every
-// block start in a.hist (at byte hist_off, the layout of hist_chain_offset) and computes
-// no outputs.
-template <int NT, int DV, bool GDR2, bool HIST>
+// MODE selects what the wavefront produces besides the final state (written to sTp, the
+// dk x dv row-major matrix of this item, when not null; s0p likewise for the initial state):
+//   kModeOut   the outputs o (the forward itself);
+//   kModeHist  the state at every block start in a.hist (at byte hist_off, the layout of
+//              hist_chain_offset), for the backward pass; no outputs;
+//   kModeState nothing else (the end state of a segment started from zero);
+//   kModeTrans the transition of the segment: the identity as initial state and zero values,
+//              so that the final state is the dk x dk product of the segment's token maps.
+template <int NT, int DV, bool GDR2, int MODE>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const TokenRange& tr,
-                                           size_t row0, size_t state_off, size_t hist_off,
-                                           int nsteps, int cbase, int lane, int rr, int p) {
-  const rsrc_t vsrc =
-      make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, (uint32_t)tr.len * DV * 2);
+                                           size_t row0, const float* s0p, float* sTp,
+                                           size_t hist_off, int nsteps, int cbase, int lane,
+                                           int rr, int p) {
+  constexpr bool HIST = MODE == kModeHist, OUT = MODE == kModeOut, TRANS = MODE == kModeTrans;
+  // (the transition reads no values: a zero-sized view returns zeros)
+  const rsrc_t vsrc = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV,
+                                TRANS ? 0u : (uint32_t)tr.len * DV * 2);
   const rsrc_t odst = make_rsrc(static_cast<bf16*>(a.o) + row0 * DV, (uint32_t)tr.len * DV * 2);
   const rsrc_t hdst = make_rsrc(static_cast<char*>(a.hist) + (HIST ? hist_off : 0),
                                 HIST ? (uint32_t)nsteps * 4 * kDK * DV * 2 : 0);
@@ -250,7 +260,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
-        S_acc[c][m][e] = a.s0 ? a.s0[state_off + (size_t)ch * DV + col[c]] : 0.f;
+        S_acc[c][m][e] = TRANS ? (ch == col[c] ? 1.f : 0.f)
+                               : (s0p ? s0p[(size_t)ch * DV + col[c]] : 0.f);
       }
   bf16 vv[NT][4][4];
   float ww[NT][4][4];  // write gate of the values (Gated Delta Rule-2 only)
@@ -270,7 +281,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
     const Stage& st = sm.st[s & 1];
     const uint32_t cbyte = (uint32_t)s * kC * DV * 2;
     // the barrier ending the previous step waited for this wavefront's staging writes
-    if (!HIST && s > 0) flush_outputs<DV>(sm, odst, s - 1, cbase, NT, lane);
+    if (OUT && s > 0) flush_outputs<DV>(sm, odst, s - 1, cbase, NT, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       // X = (K P) S, S as the B operand (bf16), and O^T = S^T (Q P)^T, S^T as the A
@@ -289,7 +300,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
           if constexpr (HIST) {
             const uint32_t tile = (uint32_t)(4 * s + I) * (DV / 16) + (cbase + 16 * c) / 16;
             st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, sb);
-          } else {
+          } else if constexpr (OUT) {
             const bf16x8 aq =
                 *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);
             Ot[c] = mfma32(sb, aq, Ot[c]);
@@ -320,7 +331,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
       // result of a 16x16x32 product still in flight delays its completion beyond the
       // wait states counted from its issue, and the conversion below then read stale
       // registers.
-      if constexpr (!HIST) {
+      if constexpr (OUT) {
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           const bf16x4 ob = pack4(Ot[c] + mfma16(vp[c], aI, zero4()));
@@ -348,8 +359,8 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
     }
     lds_barrier();
   }
-  if (!HIST && nsteps > 0) flush_outputs<DV>(sm, odst, nsteps - 1, cbase, NT, lane);
-  if (a.sT) {
+  if (OUT && nsteps > 0) flush_outputs<DV>(sm, odst, nsteps - 1, cbase, NT, lane);
+  if (sTp) {
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -357,13 +368,14 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
-          a.sT[state_off + (size_t)ch * DV + col[c]] = S_acc[c][m][e];
+          sTp[(size_t)ch * DV + col[c]] = S_acc[c][m][e];
         }
   }
 }
 
-template <int NS, int NT, bool PER_CHANNEL, bool GDR2, bool HIST>
+template <int NS, int NT, bool PER_CHANNEL, bool GDR2, int MODE>
 __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(ChunkArgs a) {
+  constexpr bool HIST = MODE == kModeHist;
   constexpr int DV = 16 * NS * NT;
   __shared__ __align__(16) Smem sm;
 
@@ -382,15 +394,47 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     part = (int)(item & 3);
   } else if (NT > 1 && a.split_all) {
     uint32_t c, pt;
-    split_item(blockIdx.x, (uint32_t)(a.N * a.H), c, pt);
+    split_item(blockIdx.x, (uint32_t)(a.N * a.H * (a.seg_len > 0 ? a.nseg : 1)), c, pt);
     chain = (int)c;
     part = (int)pt;
   }
+  // kModePair: even items compute segment end states, odd items their transitions (the
+  // transitions in a.hist as fp32 dk x dk matrices; DV = dk)
+  int kind = MODE;
+  if constexpr (MODE == kModePair) {
+    kind = chain & 1 ? kModeTrans : kModeState;
+    chain >>= 1;
+  }
+  // with segments, an item is segment `seg` of its chain (segments of seg_len tokens)
+  int seg = 0;
+  if (a.seg_len > 0) {
+    seg = chain % a.nseg;
+    chain /= a.nseg;
+  }
   const int n = chain / a.H;
   const int h = chain % a.H;
-  const TokenRange tr = token_range(a.cu, n, a.T);
+  TokenRange tr = token_range(a.cu, n, a.T);
+  const size_t mat = (size_t)n * a.H + h;  // the chain's state matrix
+  const float* s0p = a.s0 ? a.s0 + mat * kDK * DV : nullptr;
+  float* sTp = a.sT ? a.sT + mat * kDK * DV : nullptr;
+  if (a.seg_len > 0) {
+    const int nseg_n = tr.len > 0 ? (tr.len + a.seg_len - 1) / a.seg_len : 1;
+    // the outputs pass runs every segment; the state and transition passes all but the last
+    if (MODE == kModeOut ? seg >= nseg_n : seg >= nseg_n - 1) return;
+    const int first = seg * a.seg_len;
+    tr.t0 += first;
+    tr.len = min(a.seg_len, tr.len - first);
+    const size_t item = mat * a.nseg + seg;
+    if (MODE == kModeOut) {   // start states of the segments in s0; the chain's in sT
+      s0p = a.s0 + item * kDK * DV;
+      sTp = (seg == nseg_n - 1 && a.sT) ? a.sT + mat * kDK * DV : nullptr;
+    } else {                  // per-segment end states (transitions: dk x dk, DV = dk)
+      s0p = nullptr;
+      sTp = (kind == kModeTrans && MODE == kModePair ? static_cast<float*>(a.hist) : a.sT) +
+            item * kDK * DV;
+    }
+  }
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
-  const size_t state_off = ((size_t)n * a.H + h) * kDK * DV;
   const size_t hist_off = HIST ? hist_chain_offset(a, n, h, tr) : 0;
   const int nsteps = (tr.len + kC - 1) / kC;
 
@@ -423,15 +467,24 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     // SIMD have slack, so the state wavefronts take issue priority.
     __builtin_amdgcn_s_setprio(KDA_STATE_PRIO);
     const int j = wave - kPrepWaves;
+    if constexpr (MODE == kModePair) {  // whole items only
+      if (kind == kModeTrans)
+        state_role<NT, DV, GDR2, kModeTrans>(sm, a, tr, row0, s0p, sTp, 0, nsteps, 16 * NT * j,
+                                             lane, rr, p);
+      else
+        state_role<NT, DV, GDR2, kModeState>(sm, a, tr, row0, s0p, sTp, 0, nsteps, 16 * NT * j,
+                                             lane, rr, p);
+      return;
+    }
     if constexpr (NT > 1) {
       if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
-        state_role<NT / 2, DV, GDR2, HIST>(sm, a, tr, row0, state_off, hist_off, nsteps,
+        state_role<NT / 2, DV, GDR2, MODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps,
                                            (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane,
                                            rr, p);
         return;
       }
     }
-    state_role<NT, DV, GDR2, HIST>(sm, a, tr, row0, state_off, hist_off, nsteps, 16 * NT * j,
+    state_role<NT, DV, GDR2, MODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps, 16 * NT * j,
                                    lane, rr, p);
   }
 }
@@ -529,18 +582,93 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
   }
 }
 
-template <int NS, int NT, bool PER_CHANNEL>
+template <int NS, int NT, bool PER_CHANNEL, int MODE>
 hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
-  if (a.hist)
-    chunk_mfma_kernel<NS, NT, PER_CHANNEL, false, true>
-        <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
-  else if (a.erase)
-    chunk_mfma_kernel<NS, NT, PER_CHANNEL, true, false>
-        <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
-  else
-    chunk_mfma_kernel<NS, NT, PER_CHANNEL, false, false>
-        <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
+  if constexpr (MODE == kModeOut) {
+    if (a.erase) {
+      chunk_mfma_kernel<NS, NT, PER_CHANNEL, true, MODE>
+          <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
+  chunk_mfma_kernel<NS, NT, PER_CHANNEL, false, MODE>
+      <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+// One launch of mode MODE over a.N * a.H chains (times a.nseg segments when a.seg_len > 0):
+// value columns split over two workgroups when every half fits on the device at once, or
+// the work list of packed sequences (built here) when a.plan is set.
+template <int MODE>
+hipError_t launch_mode(const ChunkArgs& args, bool per_channel, int dv, hipStream_t stream) {
+  ChunkArgs a = args;
+  const bool can_split = dv == 128;  // a half of dv = 128 is one 16-column tile per wavefront
+  const long long items =
+      (long long)a.N * a.H * (a.seg_len > 0 ? a.nseg : 1) * (MODE == kModePair ? 2 : 1);
+  unsigned grid = (unsigned)items;
+  a.split_all = 0;
+  if (a.plan && a.cu && a.seg_len == 0) {
+    // packed sequences: the work list is built on the device from cu_seqlens
+    chunk_plan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, can_split,
+                                                      a.plan);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (can_split) grid *= 2;  // the largest schedule; workgroups past its length exit at once
+  } else {
+    a.plan = nullptr;
+    if (MODE != kModePair && can_split && a.cus > 0 && 2 * items <= a.cus) {
+      a.split_all = 1;
+      grid *= 2;
+    }
+  }
+  // four state wavefronts: two 16-column tiles each for dv = 128, one for dv = 64
+  if (dv == 128)
+    return per_channel ? launch_ns<4, 2, true, MODE>(a, grid, stream)
+                       : launch_ns<4, 2, false, MODE>(a, grid, stream);
+  return per_channel ? launch_ns<4, 1, true, MODE>(a, grid, stream)
+                     : launch_ns<4, 1, false, MODE>(a, grid, stream);
+}
+
+// S_{s+1} = A_s S_s + B_s over the segments of every chain (fp32), from the chain's initial
+// state: writes the start state of every segment. One workgroup per (chain, 32 value
+// columns); thread (row, half) owns 16 columns of one state row.
+__global__ __launch_bounds__(256) void seg_combine_kernel(const int32_t* cu, int N, int H, int T,
+                                                          int dv, int seg_len, int nseg,
+                                                          const float* s0, const float* Am,
+                                                          const float* Bm, float* start) {
+  __shared__ float S[kDK][33];
+  const int chain = blockIdx.x, cb = 32 * blockIdx.y;
+  const int row = threadIdx.x >> 1, c0 = 16 * (threadIdx.x & 1);
+  const int len = token_range(cu, chain / H, T).len;
+  const int nseg_n = len > 0 ? (len + seg_len - 1) / seg_len : 1;
+  const size_t sz = (size_t)kDK * dv;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[i] = s0 ? s0[chain * sz + (size_t)row * dv + cb + c0 + i] : 0.f;
+    S[row][c0 + i] = acc[i];
+    start[((size_t)chain * nseg) * sz + (size_t)row * dv + cb + c0 + i] = acc[i];
+  }
+  for (int sg = 0; sg + 1 < nseg_n; ++sg) {
+    __syncthreads();
+    const size_t item = (size_t)chain * nseg + sg;
+    const float* Arow = Am + item * kDK * kDK + (size_t)row * kDK;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = Bm[item * sz + (size_t)row * dv + cb + c0 + i];
+    for (int k4 = 0; k4 < kDK; k4 += 4) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(Arow + k4);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += av[kk] * S[k4 + kk][c0 + i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[row][c0 + i] = acc[i];
+      start[(item + 1) * sz + (size_t)row * dv + cb + c0 + i] = acc[i];
+    }
+  }
 }
 
 }  // namespace
@@ -557,40 +685,88 @@ size_t chunk_plan_bytes(int N, int H, int dv) {
   return (words * 4 + 255) / 256 * 256;
 }
 
+void chunk_seg_config(int N, int H, int T, int dv, int cus, int& seg_len, int& nseg) {
+  seg_len = 0;
+  nseg = 1;
+  if (cus <= 0 || N <= 0 || H <= 0) return;
+  // enough segments for about one workgroup per compute unit in the outputs pass (two per
+  // chain segment with split value columns), each at least 512 tokens long (measured on the
+  // B2 H16 T4096 and B1 H16 T8192 workloads: twice or four times as many segments, or
+  // 256-token segments, are slower: the extra rounds of workgroups cost more than the
+  // shorter critical path saves)
+  constexpr int kSegMinTokens = 512;
+  const long long per = (dv == 128 ? 2ll : 1ll) * N * H;
+  long long P = cus / per;
+  P = P < T / kSegMinTokens ? P : T / kSegMinTokens;
+  if (P < 2) return;
+  const int L = (int)(((T + P - 1) / P + 63) / 64 * 64);
+  seg_len = L;
+  nseg = (T + L - 1) / L;
+}
+
+size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus) {
+  int L, P;
+  chunk_seg_config(N, H, T, dv, cus, L, P);
+  if (L == 0) return 0;
+  // start states and end states (dk x dv) and transitions (dk x dk) of every segment, fp32
+  return (size_t)N * H * P * ((size_t)2 * kDK * dv + (size_t)kDK * kDK) * 4;
+}
+
 hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipStream_t stream) {
   ChunkArgs a = args;
-  if (!a.hist || a.erase) return hipErrorInvalidValue;
+  if (!a.hist || a.erase || !chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
   a.o = nullptr;
-  return launch_chunk_mfma(a, per_channel, stream);  // builds the work list when a.plan is set
+  a.seg_len = 0;
+  return launch_mode<kModeHist>(a, per_channel, a.dv, stream);  // builds the work list
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& args, bool per_channel, hipStream_t stream) {
   ChunkArgs a = args;
   if (!chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
-  const bool can_split = a.dv == 128;  // a half of dv = 128 is one 16-column tile per wavefront
-  unsigned grid = (unsigned)a.N * a.H;
-  a.split_all = 0;
-  if (a.plan && a.cu) {
-    // packed sequences: the work list is built on the device from cu_seqlens
-    chunk_plan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, can_split,
-                                                      a.plan);
-    const hipError_t e = hipGetLastError();
+  a.seg_len = 0;
+  return launch_mode<kModeOut>(a, per_channel, a.dv, stream);
+}
+
+hipError_t launch_chunk_mfma_segmented(const ChunkArgs& args, bool per_channel, void* ws,
+                                       hipStream_t stream) {
+  ChunkArgs a = args;
+  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.erase) return hipErrorInvalidValue;
+  int L, P;
+  chunk_seg_config(a.N, a.H, a.T, a.dv, a.cus, L, P);
+  if (L == 0) return hipErrorInvalidValue;
+  a.plan = nullptr;
+  a.seg_len = L;
+  a.nseg = P;
+  const size_t items = (size_t)a.N * a.H * P;
+  float* start = static_cast<float*>(ws);
+  float* Bm = start + items * kDK * a.dv;
+  float* Am = Bm + items * kDK * a.dv;
+  // 1. end state of every segment but the last, started from zero, and 2. its transition
+  // (dk x dk: the identity's dk columns as the state); one launch when dv = dk
+  ChunkArgs b = a;
+  b.s0 = nullptr;
+  b.sT = Bm;
+  b.o = nullptr;
+  hipError_t e;
+  if (a.dv == kDK) {
+    b.hist = Am;
+    e = launch_mode<kModePair>(b, per_channel, kDK, stream);
     if (e != hipSuccess) return e;
-    if (can_split) grid *= 2;  // the largest schedule; workgroups past its length exit at once
   } else {
-    // equal lengths: split every chain when all the halves fit on the device at once
-    a.plan = nullptr;
-    if (can_split && a.cus > 0 && 2ll * a.N * a.H <= a.cus) {
-      a.split_all = 1;
-      grid *= 2;
-    }
+    e = launch_mode<kModeState>(b, per_channel, a.dv, stream);
+    if (e != hipSuccess) return e;
+    b.sT = Am;
+    e = launch_mode<kModeTrans>(b, per_channel, kDK, stream);
+    if (e != hipSuccess) return e;
   }
-  // four state wavefronts: two 16-column tiles each for dv = 128, one for dv = 64
-  if (a.dv == 128)
-    return per_channel ? launch_ns<4, 2, true>(a, grid, stream)
-                       : launch_ns<4, 2, false>(a, grid, stream);
-  return per_channel ? launch_ns<4, 1, true>(a, grid, stream)
-                     : launch_ns<4, 1, false>(a, grid, stream);
+  // 3. the start state of every segment
+  seg_combine_kernel<<<dim3((unsigned)(a.N * a.H), (unsigned)(a.dv / 32)), 256, 0, stream>>>(
+      a.cu, a.N, a.H, a.T, a.dv, L, P, a.s0, Am, Bm, start);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 4. every segment's outputs from its start state; the last one writes the final state
+  a.s0 = start;
+  return launch_mode<kModeOut>(a, per_channel, a.dv, stream);
 }
 
 }  // namespace kda

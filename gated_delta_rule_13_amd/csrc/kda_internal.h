@@ -34,6 +34,10 @@ struct ChunkArgs {
   int split_all;
   // Backward pass only: the state history (see hist_chain_offset), or nullptr.
   void* hist;
+  // Segments (chunk_seg_config): items are segments of seg_len tokens, nseg per chain at
+  // most; seg_len = 0 for whole chains.
+  int seg_len;
+  int nseg;
 };
 
 // Arguments of one kda_chunk_bwd call (shapes and validation as kda_chunk_fwd).
@@ -104,6 +108,14 @@ hipError_t launch_prologue(const PrologueArgs& a, int dk, bool bf16, hipStream_t
 hipError_t launch_epilogue(const EpilogueArgs& a, int dv, bool bf16, hipStream_t stream);
 // Bytes of workspace the matrix-core path uses for its schedule (0: no schedule).
 size_t chunk_plan_bytes(int N, int H, int dv);
+
+// Chains cut into segments (few chains, long sequences): seg_len tokens each, nseg per
+// chain at most; seg_len = 0 when whole chains fill the device. chunk_seg_bytes is the
+// workspace of launch_chunk_mfma_segmented (0 when not segmented).
+void chunk_seg_config(int N, int H, int T, int dv, int cus, int& seg_len, int& nseg);
+size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus);
+hipError_t launch_chunk_mfma_segmented(const ChunkArgs& a, bool per_channel, void* ws,
+                                       hipStream_t stream);
 
 // Backward pass (bf16, dk = 128, dv in {64, 128}, one decay per channel or per head).
 bool chunk_bwd_supports(int dk, int dv, int T);

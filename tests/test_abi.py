@@ -41,11 +41,20 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    # the matrix-core path keeps a work list of 1 + 2 N H words (rounded up to 256 bytes)
+    # (sizes for a 256-CU device; without a GPU the library assumes 256 compute units)
+    # enough chains for the device: a work list of 1 + 2 N H words (rounded up to 256 bytes)
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == 2304
-    assert kda.kda_chunk_fwd_workspace_size(1, 16, 4096, 128, 64, 2, kda.KDA_BF16) == 512
-    # equal-length batches (num_seqs = 0) are scheduled on the host
-    assert kda.kda_chunk_fwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_BF16) == 0
+    # few chains: segments; per segment two dk x dv states and one dk x dk transition (fp32)
+    # 2 sequences x 16 heads, dv = 64: 8 segments of 512 tokens
+    assert kda.kda_chunk_fwd_workspace_size(1, 16, 4096, 128, 64, 2, kda.KDA_BF16) == \
+        32 * 8 * (2 * 128 * 64 + 128 * 128) * 4
+    # 2 x 16 equal-length chains, dv = 128 (two workgroups per segment): 4 segments
+    assert kda.kda_chunk_fwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_BF16) == \
+        32 * 4 * (2 * 128 * 128 + 128 * 128) * 4
+    # equal lengths with enough chains: scheduled on the host, no workspace
+    assert kda.kda_chunk_fwd_workspace_size(8, 32, 4096, 128, 128, 0, kda.KDA_BF16) == 0
+    # segments are at least 512 tokens: a short sequence is never cut
+    assert kda.kda_chunk_fwd_workspace_size(1, 2, 1000, 128, 128, 0, kda.KDA_BF16) == 0
     # no schedule: fp32, dk = 64, more than 1024 sequences, invalid sizes
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_F32) == 0
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 64, 128, 8, kda.KDA_BF16) == 0

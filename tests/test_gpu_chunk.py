@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import gated_delta_rule_13_amd as kda
 from kda_workloads import CONFIGS, make_chunk_inputs
 from tests.gpu_util import (TOL, assert_close, check_chains, note, oracle_chains, run_chunk,
                             up)
@@ -161,12 +162,13 @@ def test_schedule_is_bitwise_neutral(dv):
     """The work list (longest sequences first, value columns of the longest chains split
     over two workgroups) changes only where each column is computed, not how: outputs and
     final states equal the one-workgroup-per-chain run bit for bit, and match the oracle."""
+    # 7 sequences x 20 heads: enough chains that the work list is used, not segments
     lens = [3000, 90, 700, 0, 1300, 33, 64]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=4, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05, seed=21)
+    cfg = CONFIGS[3].replace(H=20, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05, seed=21)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
-    x.s0 = np.random.default_rng(8).standard_normal((len(lens), 4, 128, dv)).astype(
+    x.s0 = np.random.default_rng(8).standard_normal((len(lens), 20, 128, dv)).astype(
         np.float32) * np.float32(0.02)
     note(f"chunk schedule neutrality dv={dv}")
     o1, s1 = run_chunk(x, "bf16", schedule=True)
@@ -174,3 +176,39 @@ def test_schedule_is_bitwise_neutral(dv):
     np.testing.assert_array_equal(o1, o0)
     np.testing.assert_array_equal(s1, s0)
     check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], f"scheduled dv={dv}")
+
+
+SEG_CASES = [  # (name, lens or None for equal lengths, B, H, T, dv, gate)
+    ("varlen_dv128", [3000, 90, 700, 0, 1300, 33, 64], 1, 4, None, 128, "channel"),
+    ("varlen_dv64_head", [2500, 513, 511, 1700], 1, 3, None, 64, "head"),
+    ("equal_b2_h2", None, 2, 2, 2100, 128, "channel"),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: c[0])
+def test_segmented_matches_oracle_and_whole_chains(case):
+    """Few chains for the device: each chain is cut into segments, the segments' end states
+    and transitions are combined, and every segment restarts from its exact start state.
+    Outputs and final states match the oracle, and the whole-chain run to rounding."""
+    name, lens, B, H, T, dv, gate = case
+    if lens is not None:
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
+                                 pin_frac=0.05, seed=23)
+    else:
+        cfg = CONFIGS[1].replace(B=B, H=H, T=T, dv=dv, gate=gate, seed=23, random_s0=True)
+    x = make_chunk_inputs(cfg)
+    if lens is not None:
+        x.cu_seqlens = cu
+        x.s0 = np.random.default_rng(9).standard_normal((len(lens), H, 128, dv)).astype(
+            np.float32) * np.float32(0.02)
+    ns = x.n_seqs if lens is not None else 0
+    ws = kda.kda_chunk_fwd_workspace_size(x.q.shape[0], H, x.q.shape[2], 128, dv, ns,
+                                          kda.KDA_BF16)
+    assert ws > 128 * 128 * 4, f"{name}: expected the segmented path"
+    note(f"segmented chunk {name}")
+    o1, s1 = run_chunk(x, "bf16", schedule=True)
+    o0, s0 = run_chunk(x, "bf16", schedule=False)
+    check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], f"segmented {name}")
+    assert_close(o1, o0, TOL["bf16"], f"{name}: segmented vs whole outputs")
+    assert_close(s1, s0, TOL["bf16"], f"{name}: segmented vs whole states")
