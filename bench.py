@@ -18,6 +18,7 @@ Printed (one JSON line on stdout):
   gates          the fused prologue (L2Norm, decay gate, sigmoid) and epilogue (gated
                  RMSNorm) on the chunk workload's rows, against the HBM roofline
   bwd            kda_chunk_bwd (all gradients) on the chunk workload
+  small_configs  kda_chunk_fwd on the B2 H16 T4096 and GDN B1 H16 T8192 workloads
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
 """
 
@@ -445,6 +446,17 @@ def main() -> int:
                 "workload": gd.name, "steps": gd.T, "us_per_step": sec / gd.T * 1e6,
                 "hbm_gbs": dgbs, "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
+    # the two smaller prefill workloads (parity-test shapes), scheduled as a caller would
+    small = {}
+    for ci in (1, 2):
+        c = CONFIGS[ci]
+        sx = make_chunk_inputs(c)
+        sms = bench_chunk(torch, kda, sx, args.steps, args.warmup)
+        sb = chunk_alg_bytes(sx)
+        small[c.name] = {"ms_per_step": sms, "tokens_per_s": c.B * c.T / (sms / 1e3),
+                         "hbm_gbs": sb / (sms / 1e3) / 1e9}
+        log(f"{c.name}: {sms:.3f} ms/step, {c.B * c.T / sms / 1e3:.2f} M tokens/s")
+    result["small_configs"] = small
     if not args.no_bwd:
         bms, wsb = bench_bwd(torch, kda, x, args.steps, args.warmup)
         bbytes = bwd_alg_bytes(x)

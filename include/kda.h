@@ -55,14 +55,27 @@ typedef enum {
 } kda_gate_mode;
 
 /*
- * Bytes of device workspace kda_chunk_fwd uses for this problem. For packed sequences
- * (num_seqs > 0, at most 1024) on the bf16 matrix-core path (dk = 128) it keeps a work
- * list there: 4 * (1 + 2 * num_seqs * H) bytes rounded up to 256. Every other case
- * returns 0. A small scheduling kernel fills the list on the device: it splits the value
- * columns of the longest sequences' chains over two workgroups and orders the work
- * longest first, so that packed sequences of unequal length keep every compute unit
- * busy. (Equal-length batches need no list: their split is decided on the host.) The
- * results do not depend on the schedule: each value column is computed the same way.
+ * Bytes of device workspace kda_chunk_fwd uses for this problem on the current device
+ * (bf16 matrix-core path, dk = 128; every other case returns 0). Two uses:
+ *
+ *  - Few chains for the device (N * H chains, two workgroups each at dv = 128, fewer than
+ *    the compute units) and sequences of at least 1024 tokens: every sequence is cut into
+ *    P segments of L tokens (P = CUs / (2 N H) or CUs / (N H) at dv = 64, L >= 512 a
+ *    multiple of 64), and the state is passed between segments as an affine scan. Each
+ *    segment but the last gets its end state from a zero start, B, and its transition, A,
+ *    the dk x dk product of its token maps (the recurrence is affine in the state:
+ *    S_end = A S_start + B); S_{s+1} = A_s S_s + B_s gives every start state; then all
+ *    segments compute their outputs in parallel. Workspace: N H P (2 dk dv + dk^2) * 4
+ *    bytes. Results equal the whole-chain computation up to rounding (the state crosses a
+ *    segment boundary as A S + B instead of token by token). Not used by
+ *    kda_gdr2_chunk_fwd.
+ *  - Otherwise, packed sequences (num_seqs > 0, at most 1024): a work list of
+ *    4 * (1 + 2 * num_seqs * H) bytes rounded up to 256, filled on the device by a small
+ *    scheduling kernel: it splits the value columns of the longest sequences' chains over
+ *    two workgroups and orders the work longest first, so that packed sequences of unequal
+ *    length keep every compute unit busy. These results do not depend on the schedule bit
+ *    for bit: each value column is computed the same way. (Equal-length batches with
+ *    enough chains need no workspace: their split is decided on the host.)
  */
 size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
                                     kda_dtype dt);
