@@ -220,11 +220,22 @@ def bench_bwd(torch, kda, x, steps: int, warmup: int):
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    if x.erase is not None:   # Gated Delta Rule-2: erase / write gates and their gradients
+        erase, write = up(x.erase), up(x.write)
+        outs = outs[:4] + [torch.empty_like(erase), torch.empty_like(write)]
 
     def call():
-        rc = kda.kda_chunk_bwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(s0), ptr(do),
-                               ptr(dsT), *[o.data_ptr() for o in outs], ds0.data_ptr(), ptr(cu),
-                               ns, B, H, T, dk, dv, kda.KDA_BF16, gm, ws.data_ptr(), wsb, stream)
+        if x.erase is not None:
+            rc = kda.kda_gdr2_chunk_bwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(erase), ptr(write),
+                                        ptr(s0), ptr(do), ptr(dsT),
+                                        *[o.data_ptr() for o in outs], ds0.data_ptr(),
+                                        ptr(cu), ns, B, H, T, dk, dv, kda.KDA_BF16, gm,
+                                        ws.data_ptr(), wsb, stream)
+        else:
+            rc = kda.kda_chunk_bwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(s0), ptr(do),
+                                   ptr(dsT), *[o.data_ptr() for o in outs], ds0.data_ptr(),
+                                   ptr(cu), ns, B, H, T, dk, dv, kda.KDA_BF16, gm,
+                                   ws.data_ptr(), wsb, stream)
         if rc != kda.KDA_OK:
             raise RuntimeError(f"kda_chunk_bwd returned {rc}")
     ms = time_calls(torch, call, steps, warmup)
@@ -436,6 +447,10 @@ def main() -> int:
                          "alg_bytes_per_launch": gbytes}}
         log(f"gdr2 chunk_fwd: {gms:.3f} ms/step, {gcfg.T / gms / 1e3:.2f} M tokens/s, "
             f"{ggbs:.0f} GB/s")
+        if not args.no_bwd:
+            gbms, _ = bench_bwd(torch, kda, gx, args.steps, args.warmup)
+            result["gdr2"]["bwd"] = {"ms_per_step": gbms, "tokens_per_s": gcfg.T / (gbms / 1e3)}
+            log(f"gdr2 chunk_bwd: {gbms:.3f} ms/step")
         del gx
         if not args.no_decode:
             gd = CONFIGS[4].replace(name="gdr2_decode_n256_h32", T=64, gates="gdr2")

@@ -32,7 +32,7 @@ KDA_GATE_PER_CHANNEL, KDA_GATE_PER_HEAD = 0, 1
 EXPORTED_SYMBOLS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
                     "kda_status_string", "kda_gdr2_chunk_fwd", "kda_gdr2_recurrent_step",
                     "kda_prologue", "kda_epilogue", "kda_chunk_bwd",
-                    "kda_chunk_bwd_workspace_size")
+                    "kda_chunk_bwd_workspace_size", "kda_gdr2_chunk_bwd")
 
 _lib = None
 
@@ -69,6 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I,
                                   I, I, I, I, P, ctypes.c_size_t, P]
     lib.kda_chunk_bwd.restype = I
+    lib.kda_gdr2_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I,
+                                       I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
+    lib.kda_gdr2_chunk_bwd.restype = I
     lib.kda_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
@@ -126,6 +129,16 @@ def kda_chunk_bwd(q, k, v, g, beta, initial_state, grad_o, grad_final_state, gra
         q, k, v, g, beta, initial_state, grad_o, grad_final_state, grad_q, grad_k, grad_v,
         grad_g, grad_beta, grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm,
         workspace, workspace_bytes, stream))
+
+
+def kda_gdr2_chunk_bwd(q, k, v, g, erase, write, initial_state, grad_o, grad_final_state,
+                       grad_q, grad_k, grad_v, grad_g, grad_erase, grad_write,
+                       grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm,
+                       workspace, workspace_bytes, stream) -> int:
+    return int(load_library().kda_gdr2_chunk_bwd(
+        q, k, v, g, erase, write, initial_state, grad_o, grad_final_state, grad_q, grad_k,
+        grad_v, grad_g, grad_erase, grad_write, grad_initial_state, cu_seqlens, num_seqs, B, H,
+        T, dk, dv, dt, gm, workspace, workspace_bytes, stream))
 
 
 def kda_prologue(q_in, k_in, u, A_log, dt_bias, beta_in, q_out, k_out, g_out, beta_out, B, H, T,
@@ -322,19 +335,41 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     """Backward of ``chunk_fwd`` (see ``kda_chunk_bwd``): returns (dq, dk, dv, dg, dbeta,
     dS0 or None) for the loss gradients grad_o [B, H, T, dv] and grad_final_state
     [N, H, dk, dv] (None = 0). bf16 q/k/v/grad_o, dk = 128, dv in {64, 128}."""
+    return _bwd(q, k, v, g, (beta,), grad_o, initial_state, grad_final_state, cu_seqlens,
+                grad_initial_state)
+
+
+def gdr2_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   erase: torch.Tensor, write: torch.Tensor, grad_o: torch.Tensor,
+                   initial_state: Optional[torch.Tensor] = None,
+                   grad_final_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, grad_initial_state: bool = True):
+    """Backward of ``gdr2_chunk_fwd`` (see ``kda_gdr2_chunk_bwd``): returns (dq, dk, dv, dg,
+    d_erase, d_write, dS0 or None)."""
+    return _bwd(q, k, v, g, (erase, write), grad_o, initial_state, grad_final_state,
+                cu_seqlens, grad_initial_state)
+
+
+def _bwd(q, k, v, g, gates, grad_o, initial_state, grad_final_state, cu_seqlens,
+         grad_initial_state):
+    """Shared checks and call of kda_chunk_bwd / kda_gdr2_chunk_bwd; ``gates`` is (beta,)
+    or (erase, write)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     dt = _dtype_code(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (grad_o, "grad_o")):
         _check(t, n, q.dtype, dev)
-    for t, n in ((g, "g"), (beta, "beta"), (initial_state, "initial_state"),
-                 (grad_final_state, "grad_final_state")):
+    for t, n in ((g, "g"), (initial_state, "initial_state"),
+                 (grad_final_state, "grad_final_state")) + tuple((x, "gate") for x in gates):
         _check(t, n, torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or grad_o.shape != v.shape \
-            or beta.shape != (B, H, T):
-        raise ValueError("inconsistent q/k/v/beta/grad_o shapes")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or grad_o.shape != v.shape:
+        raise ValueError("inconsistent q/k/v/grad_o shapes")
+    if len(gates) == 1 and gates[0].shape != (B, H, T):
+        raise ValueError(f"beta must be {(B, H, T)}")
+    if len(gates) == 2 and (gates[0].shape != (B, H, T, dk) or gates[1].shape != (B, H, T, dv)):
+        raise ValueError(f"erase must be {(B, H, T, dk)} and write {(B, H, T, dv)}")
     if g.shape == (B, H, T, dk):
         gm = KDA_GATE_PER_CHANNEL
     elif g.shape == (B, H, T):
@@ -349,16 +384,26 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     ws_bytes = kda_chunk_bwd_workspace_size(B, H, T, dk, dv, num_seqs, dt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    dg = torch.empty_like(g)
+    dgates = tuple(torch.empty_like(x) for x in gates)
     ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) \
         if grad_initial_state else None
-    st = kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                       _ptr(grad_o), _ptr(grad_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_),
-                       _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(cu_seqlens), num_seqs, B, H, T,
-                       dk, dv, dt, gm, _ptr(ws), ws_bytes, _stream(dev))
+    common = (_ptr(cu_seqlens), num_seqs, B, H, T, dk, dv, dt, gm, _ptr(ws), ws_bytes,
+              _stream(dev))
+    if len(gates) == 1:
+        st = kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]),
+                           _ptr(initial_state), _ptr(grad_o), _ptr(grad_final_state), _ptr(dq),
+                           _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dgates[0]), _ptr(ds0), *common)
+        where = "kda_chunk_bwd"
+    else:
+        st = kda_gdr2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]),
+                                _ptr(gates[1]), _ptr(initial_state), _ptr(grad_o),
+                                _ptr(grad_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                                _ptr(dg), _ptr(dgates[0]), _ptr(dgates[1]), _ptr(ds0), *common)
+        where = "kda_gdr2_chunk_bwd"
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_bwd")
-    return dq, dk_, dv_, dg, dbeta, ds0
+        raise KDAError(st, where)
+    return (dq, dk_, dv_, dg) + dgates + (ds0,)
 
 
 def prologue(q_in: torch.Tensor, k_in: torch.Tensor, u: torch.Tensor, A_log: torch.Tensor,

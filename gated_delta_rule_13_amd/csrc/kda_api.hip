@@ -173,15 +173,22 @@ size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num
   return 2 * ((one + 255) / 256 * 256) + plan;
 }
 
-kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const float* initial_state, const void* grad_o,
-                         const float* grad_final_state, void* grad_q, void* grad_k,
-                         void* grad_v, float* grad_g, float* grad_beta,
-                         float* grad_initial_state, const int32_t* cu_seqlens, int num_seqs,
-                         int B, int H, int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !g || !beta || !grad_o) return KDA_ERR_INVALID_ARG;
-  if (!grad_q || !grad_k || !grad_v || !grad_g || !grad_beta) return KDA_ERR_INVALID_ARG;
+// The two backward paths differ only in their gates: beta (KDA, Gated DeltaNet) or the
+// erase / write vectors of Gated Delta Rule-2 (erase != nullptr).
+static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* erase, const float* write,
+                                 const float* initial_state, const void* grad_o,
+                                 const float* grad_final_state, void* grad_q, void* grad_k,
+                                 void* grad_v, float* grad_g, float* grad_beta,
+                                 float* grad_erase, float* grad_write,
+                                 float* grad_initial_state, const int32_t* cu_seqlens,
+                                 int num_seqs, int B, int H, int T, int dk, int dv,
+                                 kda_dtype dt, kda_gate_mode gm, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !g || !grad_o) return KDA_ERR_INVALID_ARG;
+  if (erase ? (!write || !grad_erase || !grad_write) : (!beta || !grad_beta))
+    return KDA_ERR_INVALID_ARG;
+  if (!grad_q || !grad_k || !grad_v || !grad_g) return KDA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
@@ -196,13 +203,14 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
 
   kda::BwdArgs b;
   kda::ChunkArgs& a = b.f;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = nullptr; a.write = nullptr;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = erase; a.write = write;
   a.s0 = initial_state; a.sT = nullptr; a.o = nullptr; a.cu = cu_seqlens;
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
   a.plan = nullptr; a.cus = device_compute_units(); a.split_all = 0; a.hist = nullptr;
   a.seg_len = 0; a.nseg = 1;
   b.dout = grad_o; b.dsT = grad_final_state;
   b.dq = grad_q; b.dk = grad_k; b.dv = grad_v; b.dg = grad_g; b.dbeta = grad_beta;
+  b.derase = grad_erase; b.dwrite = grad_write;
   b.ds0 = grad_initial_state;
   const size_t one = (kda::chunk_bwd_hist_bytes((int)N, H, T, dv, cu_seqlens != nullptr) + 255) /
                     256 * 256;
@@ -212,6 +220,36 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
                           : nullptr;
   const hipError_t err = kda::launch_chunk_bwd(b, gm == KDA_GATE_PER_CHANNEL, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, const void* grad_o,
+                         const float* grad_final_state, void* grad_q, void* grad_k,
+                         void* grad_v, float* grad_g, float* grad_beta,
+                         float* grad_initial_state, const int32_t* cu_seqlens, int num_seqs,
+                         int B, int H, int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!beta) return KDA_ERR_INVALID_ARG;
+  return chunk_bwd_impl(q, k, v, g, beta, nullptr, nullptr, initial_state, grad_o,
+                        grad_final_state, grad_q, grad_k, grad_v, grad_g, grad_beta, nullptr,
+                        nullptr, grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv, dt,
+                        gm, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_gdr2_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                              const float* erase, const float* write,
+                              const float* initial_state, const void* grad_o,
+                              const float* grad_final_state, void* grad_q, void* grad_k,
+                              void* grad_v, float* grad_g, float* grad_erase,
+                              float* grad_write, float* grad_initial_state,
+                              const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                              int dk, int dv, kda_dtype dt, kda_gate_mode gm, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (!erase || !write) return KDA_ERR_INVALID_ARG;
+  return chunk_bwd_impl(q, k, v, g, nullptr, erase, write, initial_state, grad_o,
+                        grad_final_state, grad_q, grad_k, grad_v, grad_g, nullptr, grad_erase,
+                        grad_write, grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv,
+                        dt, gm, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, const float* A_log,

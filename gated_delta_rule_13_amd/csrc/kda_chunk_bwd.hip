@@ -76,7 +76,9 @@ static_assert(sizeof(RStage) % 16 == 0 && offsetof(RStage, qrT) % 16 == 0 &&
 static_assert((kLDB * 2) % 8 == 0, "transposed rows must keep 8-byte alignment");
 
 // Decay products of block I and its operands for the carry (one wavefront; a lane holds
-// 8 tokens x 4 channels as in the forward's prep).
+// 8 tokens x 4 channels as in the forward's prep). With the Gated Delta Rule-2 gates the
+// read-side key Kh is (b * k) P and beta is 1 (the write gate acts on the values).
+template <bool GDR2>
 __device__ __forceinline__ void prep_block_rev(RStage& st, bf16 (*qg)[kLDK], bf16 (*kg)[kLDK],
                                                const BlockRegs& r, int I, int lane) {
   const int cq = lane & 31, hf = lane >> 5;
@@ -109,7 +111,8 @@ __device__ __forceinline__ void prep_block_rev(RStage& st, bf16 (*qg)[kLDK], bf1
     for (int j = 0; j < 4; ++j) {
       run[j] *= al[u][j];
       qp[j][u] = static_cast<float>(r.q[u][j]) * run[j];
-      kp[j][u] = static_cast<float>(r.k[u][j]) * run[j];
+      // Gated Delta Rule-2: the read side takes the erase-gated key (b * k) P
+      kp[j][u] = static_cast<float>(r.k[u][j]) * (GDR2 ? r.b[u][j] * run[j] : run[j]);
       qs[j] = qp[j][u] * rtot[j];
       ks[j] = kp[j][u] * rtot[j];
     }
@@ -290,7 +293,7 @@ __device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const To
   }
 }
 
-template <int NS, int NT, bool PER_CHANNEL>
+template <int NS, int NT, bool PER_CHANNEL, bool GDR2>
 __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel(BwdArgs b) {
   constexpr int DV = 16 * NS * NT;
   __shared__ __align__(16) RSmem sm;
@@ -318,23 +321,23 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
   const int nsteps = (tr.len + kC - 1) / kC;
   if (wave < kPrepWaves) {
     const int I = wave;
-    const PrepSrc src = prep_src<PER_CHANNEL, false>(a, row0, tr.len, I, lane);
+    const PrepSrc src = prep_src<PER_CHANNEL, GDR2>(a, row0, tr.len, I, lane);
     BlockRegs r;
     if (nsteps > 0) {
-      load_block<PER_CHANNEL, false>(r, src, (nsteps - 1) * kC);
-      prep_block_rev(sm.st[(nsteps - 1) & 1], sm.qg, sm.kg, r, I, lane);
+      load_block<PER_CHANNEL, GDR2>(r, src, (nsteps - 1) * kC);
+      prep_block_rev<GDR2>(sm.st[(nsteps - 1) & 1], sm.qg, sm.kg, r, I, lane);
       wave_lds_fence();
       block_tiles_rev(sm.st[(nsteps - 1) & 1], sm.qg, sm.kg, I, rr, p);
-      if (nsteps > 1) load_block<PER_CHANNEL, false>(r, src, (nsteps - 2) * kC);
+      if (nsteps > 1) load_block<PER_CHANNEL, GDR2>(r, src, (nsteps - 2) * kC);
     }
     lds_barrier();
     for (int s = nsteps - 1; s >= 0; --s) {
       if (s > 0) {
         RStage& st = sm.st[(s - 1) & 1];
-        prep_block_rev(st, sm.qg, sm.kg, r, I, lane);
+        prep_block_rev<GDR2>(st, sm.qg, sm.kg, r, I, lane);
         wave_lds_fence();
         block_tiles_rev(st, sm.qg, sm.kg, I, rr, p);
-        if (s > 1) load_block<PER_CHANNEL, false>(r, src, (s - 2) * kC);
+        if (s > 1) load_block<PER_CHANNEL, GDR2>(r, src, (s - 2) * kC);
       }
       lds_barrier();
     }
@@ -417,7 +420,10 @@ __device__ __forceinline__ bf16x8 selector(int hh, int rr, int p) {
 
 // Three wavefronts per SIMD (at most 170 registers): three blocks share a CU (the LDS of
 // one is about 50 KB), measured 7% faster than the two that 205 registers allow.
-template <int DV, bool PER_CHANNEL>
+// GDR2: the Gated Delta Rule-2 gates. The read-side key Kh is then (b * k) P, beta is 1,
+// R = w * V - Kh S, dV = w * dY, and the gradients of the gates are d erase = k P * dKh and
+// d write = V * dY (instead of dbeta).
+template <int DV, bool PER_CHANNEL, bool GDR2>
 __global__ __attribute__((amdgpu_waves_per_eu(3))) __launch_bounds__(kGThreads) void
 chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   constexpr int NTW = DV / 64;     // value tiles per wavefront in phase A
@@ -454,13 +460,24 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       da[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
     }
   bf16 vv[NTW][4];
+  float wv[NTW][4];   // write gates (Gated Delta Rule-2)
+  const rsrc_t es = make_rsrc(a.erase + (GDR2 ? row0 * kDK : 0), GDR2 ? len * kDK * 4 : 0);
   {
     const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
+    const rsrc_t ws_ = make_rsrc(a.write + (GDR2 ? row0 * DV : 0), GDR2 ? len * DV * 4 : 0);
 #pragma unroll
     for (int c = 0; c < NTW; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vv[c][e] = ld_b16(vs, (uint32_t)((4 * p + e) * DV + 16 * (wave * NTW + c) + rr) * 2);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t o = (uint32_t)((4 * p + e) * DV + 16 * (wave * NTW + c) + rr);
+        vv[c][e] = ld_b16(vs, o * 2);
+        wv[c][e] = GDR2 ? ld_b32(ws_, o * 4) : 1.f;
+      }
+  }
+  f32x4 eb0 = zero4(), eb1 = zero4();   // erase gates of this thread's 8 channels
+  if (GDR2) {
+    eb0 = ld_b128(es, (uint32_t)(t8 * kDK + c8) * 4);
+    eb1 = ld_b128(es, (uint32_t)(t8 * kDK + c8 + 4) * 4);
   }
 
   // ---- 0. decay of every channel; dO rows and beta
@@ -476,7 +493,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     sm.gam[c] = run;
   } else if (tid < kDK + 16) {
     const int t = tid - kDK;
-    sm.beta[t] = t < len ? a.beta[row0 + t] : 0.f;
+    sm.beta[t] = GDR2 ? 1.f : (t < len ? a.beta[row0 + t] : 0.f);
     sm.r1[t] = 0.f;
   }
   {
@@ -497,7 +514,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       const float rp = __builtin_amdgcn_rcpf(P);
       const float qf = static_cast<float>(q8[i]), kf = static_cast<float>(k8[i]);
       qh[i] = qf * P;
-      kh[i] = kf * P;
+      kh[i] = kf * P * (GDR2 ? (i < 4 ? eb0[i] : eb1[i - 4]) : 1.f);   // the read-side key
       kb[i] = kf * rp;       // k / P
       kt[i] = kb[i] * G;     // k E = k Gam / P
     }
@@ -570,7 +587,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       bf16x4 dob;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        R[e] = static_cast<float>(vv[c][e]) - X[e];
+        R[e] = wv[c][e] * static_cast<float>(vv[c][e]) - X[e];
         x[e] = bt[e] * R[e];
         dob[e] = sm.dor[4 * p + e][col];
       }
@@ -581,8 +598,15 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       for (int e = 0; e < 4; ++e) {
         sm.ur[4 * p + e][col] = static_cast<bf16>(U[e]);
         sm.dyr[4 * p + e][col] = static_cast<bf16>(dY[e]);
-        sm.bdyr[4 * p + e][col] = static_cast<bf16>(bt[e] * dY[e]);
+        // dV = Diag(beta) dY, or w * dY with the write gate
+        sm.bdyr[4 * p + e][col] = static_cast<bf16>((GDR2 ? wv[c][e] : bt[e]) * dY[e]);
         r1[e] += dY[e] * R[e];
+      }
+      if (GDR2) {   // d write = V * dY
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * p + e < len)
+            b.dwrite[(row0 + 4 * p + e) * DV + col] = static_cast<float>(vv[c][e]) * dY[e];
       }
     }
     // S and dS' of this wavefront's 32-channel slab (all value tiles), for phase 3
@@ -619,7 +643,8 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       const f32x4 dt = mfma32(dl[ct], sel, zero4());   // dS'[ch][16 ct + 4p + e]
       const int j = 16 * ct + 4 * p;
       const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][j]);
-      const bf16x4 ay = *reinterpret_cast<const bf16x4*>(&sm.bdyr[rr][j]);
+      // Diag(beta) dY (beta = 1 with the Gated Delta Rule-2 gates: dY itself)
+      const bf16x4 ay = *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.dyr[rr][j] : &sm.bdyr[rr][j]);
       const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.ur[rr][j]);
       const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
       C1[hh] = mfma16(ao, sb4, C1[hh]);   // (dO S^T)[4p + e][ch]
@@ -648,15 +673,18 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       else sm.G2[4 * p + e][rr] = gg[e];
     }
   }
-  // q and k of this lane's elements (token 4p + e, channel 32 w + 16 hh + rr)
+  // q, k (and the erase gate) of this lane's elements (token 4p + e, channel
+  // 32 w + 16 hh + rr)
   bf16 qe[2][4], ke[2][4];
+  float be[2][4];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t off = (uint32_t)((4 * p + e) * kDK + 32 * wave + 16 * hh + rr) * 2;
-      qe[hh][e] = ld_b16(qs, off);
-      ke[hh][e] = ld_b16(ks_, off);
+      const uint32_t off = (uint32_t)((4 * p + e) * kDK + 32 * wave + 16 * hh + rr);
+      qe[hh][e] = ld_b16(qs, off * 2);
+      ke[hh][e] = ld_b16(ks_, off * 2);
+      be[hh][e] = GDR2 ? ld_b32(es, off * 4) : 1.f;
     }
   __syncthreads();
 
@@ -692,11 +720,13 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
         const int t = 4 * p + e;
         const float P = sm.P[t][ch], rp = __builtin_amdgcn_rcpf(P);
         const float qf = static_cast<float>(qe[hh][e]), kf = static_cast<float>(ke[hh][e]);
-        const float qh = qf * P, kh = kf * P, kb = kf * rp, kt = kb * G;
+        // (with the erase gate be, the read-side key is kh = be k P)
+        const float qh = qf * P, kh = kf * P * be[hh][e], kb = kf * rp, kt = kb * G;
         // this wavefront's own channel columns: qh / kh / P are read above, then reused
-        sm.qh[t][ch] = static_cast<bf16>(dQh[e] * P);                                // dq
-        sm.kh[t][ch] = static_cast<bf16>(dKh[e] * P + (dKb[e] + dKt[e] * G) * rp);  // dk
-        sm.P[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;        // d log P
+        sm.qh[t][ch] = static_cast<bf16>(dQh[e] * P);                                  // dq
+        sm.kh[t][ch] = static_cast<bf16>(dKh[e] * P * be[hh][e] + (dKb[e] + dKt[e] * G) * rp);
+        sm.P[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;          // d log P
+        if (GDR2 && t < len) b.derase[(row0 + t) * kDK + ch] = dKh[e] * kf * P;      // d erase
         lg += dKt[e] * kt;
       }
       lg += __shfl_xor(lg, 16, 64);
@@ -748,7 +778,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       }
     }
   }
-  if (tid >= 192 && tid < 208) {
+  if (!GDR2 && tid >= 192 && tid < 208) {
     const int t = tid - 192;
     float acc = sm.r1[t];
     for (int s_ = 0; s_ < t; ++s_) acc -= sm.A[t][s_] * sm.G2[t][s_];
@@ -768,10 +798,35 @@ size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed) {
   return (size_t)H * tokens * (kDK / 16) * 2 * (size_t)dv;  // hist_chain_offset's layout
 }
 
+template <bool GDR2>
+hipError_t launch_bwd_kernels(BwdArgs& b, bool per_channel, unsigned chains, int slots,
+                              hipStream_t stream) {
+  const ChunkArgs& a = b.f;
+  const unsigned threads = 64 * (kPrepWaves + 4);
+  if (a.dv == 128) {
+    if (per_channel) chunk_bwd_state_kernel<4, 2, true, GDR2><<<chains, threads, 0, stream>>>(b);
+    else chunk_bwd_state_kernel<4, 2, false, GDR2><<<chains, threads, 0, stream>>>(b);
+  } else {
+    if (per_channel) chunk_bwd_state_kernel<4, 1, true, GDR2><<<chains, threads, 0, stream>>>(b);
+    else chunk_bwd_state_kernel<4, 1, false, GDR2><<<chains, threads, 0, stream>>>(b);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)slots * a.H;
+  if (a.dv == 128) {
+    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
+  } else {
+    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t stream) {
   BwdArgs b = args;
   ChunkArgs& a = b.f;
-  if (!chunk_bwd_supports(a.dk, a.dv, a.T) || a.erase) return hipErrorInvalidValue;
+  if (!chunk_bwd_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
   // 1. states at every block start (builds the work list of packed sequences)
   a.hist = b.hist_s;
   a.sT = nullptr;
@@ -779,7 +834,8 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
   hipError_t e = launch_chunk_mfma_hist(a, per_channel, stream);
   if (e != hipSuccess) return e;
   a.hist = nullptr;
-  // 2. the carry, over the same work list (or every chain split when all halves fit)
+  // 2. the carry, over the same work list (or every chain split when all halves fit), and
+  // 3. the gradients of every block
   b.plan = a.plan;
   const bool can_split = a.dv == 128;
   unsigned chains = (unsigned)a.N * a.H;
@@ -790,26 +846,9 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
     a.split_all = 1;
     chains *= 2;
   }
-  if (a.dv == 128) {
-    if (per_channel) chunk_bwd_state_kernel<4, 2, true><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
-    else chunk_bwd_state_kernel<4, 2, false><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
-  } else {
-    if (per_channel) chunk_bwd_state_kernel<4, 1, true><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
-    else chunk_bwd_state_kernel<4, 1, false><<<chains, 64 * (kPrepWaves + 4), 0, stream>>>(b);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // 3. the gradients of every block
   const int slots = a.cu ? a.T / 16 + a.N + 1 : a.N * ((a.T + 15) / 16);
-  const unsigned grid = (unsigned)slots * a.H;
-  if (a.dv == 128) {
-    if (per_channel) chunk_bwd_grad_kernel<128, true><<<grid, kGThreads, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<128, false><<<grid, kGThreads, 0, stream>>>(b, slots);
-  } else {
-    if (per_channel) chunk_bwd_grad_kernel<64, true><<<grid, kGThreads, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<64, false><<<grid, kGThreads, 0, stream>>>(b, slots);
-  }
-  return hipGetLastError();
+  return a.erase ? launch_bwd_kernels<true>(b, per_channel, chains, slots, stream)
+                 : launch_bwd_kernels<false>(b, per_channel, chains, slots, stream);
 }
 
 }  // namespace kda

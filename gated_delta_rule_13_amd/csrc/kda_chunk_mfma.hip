@@ -584,7 +584,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
 
 template <int NS, int NT, bool PER_CHANNEL, int MODE>
 hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
-  if constexpr (MODE == kModeOut) {
+  if constexpr (MODE == kModeOut || MODE == kModeHist) {
     if (a.erase) {
       chunk_mfma_kernel<NS, NT, PER_CHANNEL, true, MODE>
           <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
@@ -714,7 +714,7 @@ size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus) {
 
 hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipStream_t stream) {
   ChunkArgs a = args;
-  if (!a.hist || a.erase || !chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
+  if (!a.hist || !chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
   a.o = nullptr;
   a.seg_len = 0;
   return launch_mode<kModeHist>(a, per_channel, a.dv, stream);  // builds the work list

@@ -49,7 +49,9 @@ struct BwdArgs {
   void* dk;                // [B, H, T, dk]
   void* dv;                // [B, H, T, dv]
   float* dg;               // like g
-  float* dbeta;            // [B, H, T]
+  float* dbeta;            // [B, H, T] (KDA / Gated DeltaNet)
+  float* derase;           // [B, H, T, dk] (Gated Delta Rule-2: f.erase set)
+  float* dwrite;           // [B, H, T, dv]
   float* ds0;              // [N, H, dk, dv] or nullptr
   void* hist_s;            // workspace: states at every 16-token block start
   void* hist_ds;           // workspace: state gradients at every 16-token block end

@@ -250,6 +250,23 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          int B, int H, int T, int dk, int dv, kda_dtype dt, kda_gate_mode gm,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Backward pass of kda_gdr2_chunk_fwd: kda_chunk_bwd with beta replaced by the Gated Delta
+ * Rule-2 gates erase float32 [B, H, T, dk] and write float32 [B, H, T, dv], whose gradients
+ * grad_erase [B, H, T, dk] and grad_write [B, H, T, dv] (float32) replace grad_beta.
+ * Workspace: kda_chunk_bwd_workspace_size. A NULL erase, write, grad_erase or grad_write:
+ * KDA_ERR_INVALID_ARG; everything else as kda_chunk_bwd.
+ */
+kda_status kda_gdr2_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                              const float* erase, const float* write,
+                              const float* initial_state, const void* grad_o,
+                              const float* grad_final_state, void* grad_q, void* grad_k,
+                              void* grad_v, float* grad_g, float* grad_erase,
+                              float* grad_write, float* grad_initial_state,
+                              const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                              int dk, int dv, kda_dtype dt, kda_gate_mode gm, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 

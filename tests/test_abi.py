@@ -253,3 +253,28 @@ def bwd_call(**over):
 ])
 def test_bwd_rejects(over, code):
     assert bwd_call(**over) == code
+
+
+def gdr2_bwd_call(**over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, erase=DUMMY, write=DUMMY,
+                initial_state=None, grad_o=DUMMY, grad_final_state=None, grad_q=DUMMY,
+                grad_k=DUMMY, grad_v=DUMMY, grad_g=DUMMY, grad_erase=DUMMY, grad_write=DUMMY,
+                grad_initial_state=None, cu_seqlens=None, num_seqs=0, B=1, H=2, T=64, dk=128,
+                dv=128, dt=kda.KDA_BF16, gm=kda.KDA_GATE_PER_CHANNEL, workspace=DUMMY,
+                workspace_bytes=0, stream=None)
+    args.update(over)
+    return kda.kda_gdr2_chunk_bwd(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(erase=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(write=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(grad_erase=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(grad_write=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(grad_g=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(workspace_bytes=100), kda.KDA_ERR_INVALID_ARG),
+    (dict(dt=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=32), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_gdr2_bwd_rejects(over, code):
+    assert gdr2_bwd_call(**over) == code

@@ -7,7 +7,8 @@ bound max |got - want| <= 2e-2 max |want| of bf16 inputs with fp32 accumulation,
 tensor separately. Checked: both gate modes and value head sizes on ragged sequences with
 and without an initial state and a final-state cotangent; sequence lengths around the
 16- and 64-token block edges (packed); the B2 H16 T4096 workload in full; the packed
-H32 T65536 workload on sampled chains; tokens outside every sequence left untouched.
+H32 T65536 workload on sampled chains; tokens outside every sequence left untouched; and
+the Gated Delta Rule-2 backward (erase and write gates: their gradients replace dbeta).
 """
 
 import numpy as np
@@ -153,4 +154,76 @@ def test_bwd_varlen_t65536_sampled_chains():
     lens = np.diff(x.cu_seqlens)
     chains = sorted({(int(np.argmax(lens)), 3), (int(np.argmin(lens)), 30), (2, 17)})
     errs = check(x, run_bwd(x, ct), oracle_grads(x, ct, chains), cfg.name)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+GDR2_NAMES = ("dq", "dk", "dv", "dg", "derase", "dwrite", "ds0")
+
+
+def run_gdr2_bwd(x, ct):
+    bf = torch.bfloat16
+    cu = up(x.cu_seqlens, torch.int32) if x.cu_seqlens is not None else None
+    out = kda.gdr2_chunk_bwd(up(x.q, bf), up(x.k, bf), up(x.v, bf), up(x.g), up(x.erase),
+                             up(x.write), up(ct.do, bf),
+                             initial_state=up(x.s0) if x.s0 is not None else None,
+                             grad_final_state=up(ct.dsT), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return {name: t.float().cpu().numpy() for name, t in zip(GDR2_NAMES, out)}
+
+
+def check_gdr2(x, got, ref, what):
+    errs = {}
+    for name in GDR2_NAMES:
+        g_parts, w_parts = [], []
+        for (n, h), r in ref.items():
+            if name == "ds0":
+                g_parts.append(got["ds0"][n, h])
+            else:
+                b, t0, ln = x.chain_rows(n, h)
+                g_parts.append(got[name][b, h, t0:t0 + ln])
+            w_parts.append(r[name])
+        errs[name] = assert_close(np.concatenate([a.ravel() for a in g_parts]),
+                                  np.concatenate([a.ravel() for a in w_parts]), TOL["bf16"],
+                                  f"{what}: {name}")
+    return errs
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("dv", [128, 64])
+def test_gdr2_bwd_small_ragged(gate, dv):
+    cfg = CONFIGS[1].replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=84, random_s0=True,
+                             gates="gdr2")
+    note(f"gdr2 bwd small {gate} dv={dv}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    ref = oracle.kda_backward(x.q, x.k, x.v, x.g, x.beta, ct.do, s0=x.s0, dsT=ct.dsT,
+                              erase=x.erase, write=x.write)
+    errs = check_gdr2(x, run_gdr2_bwd(x, ct), ref, f"gdr2 bwd {gate} dv={dv}")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_gdr2_bwd_varlen_edges():
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05, seed=85,
+                             gates="gdr2")
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(10).standard_normal((len(lens), 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    ct = make_cotangents(cfg, len(lens))
+    note("gdr2 bwd varlen edges")
+    ref = oracle.kda_backward(x.q, x.k, x.v, x.g, x.beta, ct.do, s0=x.s0, dsT=ct.dsT,
+                              cu_seqlens=cu, erase=x.erase, write=x.write)
+    check_gdr2(x, run_gdr2_bwd(x, ct), ref, "gdr2 bwd varlen edges")
+
+
+def test_gdr2_bwd_b2_h16_t4096_full():
+    cfg = CONFIGS[1].replace(name="gdr2_bf16_b2_h16_t4096", gates="gdr2")
+    note(f"gdr2 bwd parity {cfg.name}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    ref = oracle.kda_backward(x.q, x.k, x.v, x.g, x.beta, ct.do, s0=x.s0, dsT=ct.dsT,
+                              erase=x.erase, write=x.write)
+    errs = check_gdr2(x, run_gdr2_bwd(x, ct), ref, cfg.name)
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
