@@ -27,7 +27,7 @@
 //      block start, bf16, in the layout of hist_chain_offset;
 //   2. chunk_bwd_state_kernel: the carry above, one workgroup per chain, from the last
 //      block to the first; it records dS' of every block (same layout) and writes dS_0;
-//   3. chunk_bwd_grad_kernel: every block independently from (S, dS'), one workgroup per
+//   3. chunk_bwd_grad_kernel: every block independently from (S, dS'), one wavefront per
 //      block: dq, dk, dv, dg, dbeta.
 // Launch 2 has the forward's structure: four "prep" wavefronts prepare the operands of
 // the next 64 tokens (in reverse) while four "state" wavefronts, holding dS in matrix-core
@@ -357,28 +357,32 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
 
 // ------------------------------------------------------------ launch 3: the gradients
 
-constexpr int kGThreads = 256;  // four wavefronts per 16-token block
+// One wavefront per 16-token block, no barriers. The block's S and dS' are read once, one
+// 16-column value tile at a time, as stored (lane-native B operands over 32-channel
+// slabs); for each tile the wavefront forms its columns of Kh S, U, dU, dY and adds the
+// tile's share of every contraction over the value columns (dO S^T, Diag(beta) dY S^T,
+// U dS'^T, dO U^T, dY U^T and rowsum(dS' * S)) for all channels, taking S and dS'
+// transposed by products with a 0/1 selector (exact in bf16).
 
-// LDS of one block (about 50 KB for dv = 128).
 template <int DV>
 struct GSmem {
   float P[16][kDK];        // decay from the block start through token t; later d log P_t
   float gam[kDK];
-  bf16 qh[16][kLDK];       // Qh, Kh, Kb, Kt as bf16 operands (qh, kh later hold dq, dk)
-  bf16 kh[16][kLDK];
-  bf16 kb[16][kLDK];
-  bf16 kt[16][kLDK];
-  bf16 dor[16][DV + 8];    // token rows of dO, U, dY and Diag(beta) dY
-  bf16 ur[16][DV + 8];
-  bf16 dyr[16][DV + 8];
-  bf16 bdyr[16][DV + 8];
+  bf16 dor[16][kLDK];      // token rows of dO (dv <= dk columns); later of dq (dk columns)
+  union {
+    struct {               // phases 2-4
+      bf16 ut[16][24];     // U, dY, Diag(beta) dY of the current value tile (token rows)
+      bf16 yt[16][24];
+      bf16 bt[16][24];
+      float M[16][17];     // Tril(Qh Kb^T)
+      float Tm[16][17];
+      float G1[16][17];    // dO U^T
+    } w;
+    bf16 dkr[16][kLDK];    // phase 4-5: token rows of dk (written after the above are read)
+  } u;
   float A[16][17];         // StrictTril(Kh Kb^T)
-  float M[16][17];         // Tril(Qh Kb^T)
-  float Tm[16][17];
-  float G1[16][17];        // dO U^T
   float G2[16][17];        // dY U^T
   float beta[16];
-  float r1[16];            // sum_j dY_tj R_tj
   float dlgam[kDK];        // d log Gam
 };
 
@@ -418,19 +422,22 @@ __device__ __forceinline__ bf16x8 selector(int hh, int rr, int p) {
   return b;
 }
 
-// Three wavefronts per SIMD (at most 170 registers): three blocks share a CU (the LDS of
-// one is about 50 KB), measured 7% faster than the two that 205 registers allow.
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
+  return cat8(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
+}
+
 // GDR2: the Gated Delta Rule-2 gates. The read-side key Kh is then (b * k) P, beta is 1,
 // R = w * V - Kh S, dV = w * dY, and the gradients of the gates are d erase = k P * dKh and
 // d write = V * dY (instead of dbeta).
+// Two wavefronts per SIMD (at most 256 registers; about 21 KB of LDS each): measured 10%
+// faster than the one that 300 registers would allow.
 template <int DV, bool PER_CHANNEL, bool GDR2>
-__global__ __attribute__((amdgpu_waves_per_eu(3))) __launch_bounds__(kGThreads) void
+__global__ __attribute__((amdgpu_waves_per_eu(2))) __launch_bounds__(64) void
 chunk_bwd_grad_kernel(BwdArgs b, int slots) {
-  constexpr int NTW = DV / 64;     // value tiles per wavefront in phase A
-  constexpr int NCT = DV / 16;     // value tiles of the block
+  constexpr int NCT = DV / 16;   // value tiles of the block
   __shared__ __align__(16) GSmem<DV> sm;
   const ChunkArgs& a = b.f;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x;
   const int rr = lane & 15, p = lane >> 4;
   const int h = blockIdx.x / slots, slot = blockIdx.x % slots;
   int n, blk;
@@ -441,48 +448,44 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   const size_t hoff = hist_chain_offset(a, n, h, tr) + (size_t)blk * kDK * DV * 2;
   const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, len * kDK * 2);
   const rsrc_t ks_ = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, len * kDK * 2);
+  const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
   const rsrc_t hs = make_rsrc(static_cast<const char*>(b.hist_s) + hoff, kDK * DV * 2);
   const rsrc_t hd = make_rsrc(static_cast<const char*>(b.hist_ds) + hoff, kDK * DV * 2);
-
-  // global loads first, so that their latency overlaps the first phases: q and k of this
-  // thread's 8 channels, the S and dS' tiles of this wavefront's value columns (all
-  // channels, as stored: lane-native 16-byte pieces) and V of those columns
-  const int t8 = tid >> 4, c8 = 8 * (tid & 15);
-  const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld_b128(qs, (uint32_t)(t8 * kDK + c8) * 2));
-  const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld_b128(ks_, (uint32_t)(t8 * kDK + c8) * 2));
-  bf16x8 sa[NTW][4], da[NTW][4];
-#pragma unroll
-  for (int c = 0; c < NTW; ++c)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t off = (uint32_t)((((wave * NTW + c) * 4 + ks) * 64 + lane) * 16);
-      sa[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
-      da[c][ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
-    }
-  bf16 vv[NTW][4];
-  float wv[NTW][4];   // write gates (Gated Delta Rule-2)
   const rsrc_t es = make_rsrc(a.erase + (GDR2 ? row0 * kDK : 0), GDR2 ? len * kDK * 4 : 0);
-  {
-    const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
-    const rsrc_t ws_ = make_rsrc(a.write + (GDR2 ? row0 * DV : 0), GDR2 ? len * DV * 4 : 0);
+  const rsrc_t ws_ = make_rsrc(a.write + (GDR2 ? row0 * DV : 0), GDR2 ? len * DV * 4 : 0);
+
+  // S and dS' of value tile 0 (prefetched one tile ahead in the loop below)
+  bf16x8 sb[4], db[4];
 #pragma unroll
-    for (int c = 0; c < NTW; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t o = (uint32_t)((4 * p + e) * DV + 16 * (wave * NTW + c) + rr);
-        vv[c][e] = ld_b16(vs, o * 2);
-        wv[c][e] = GDR2 ? ld_b32(ws_, o * 4) : 1.f;
-      }
+  for (int ks = 0; ks < 4; ++ks) {
+    sb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, (uint32_t)((ks * 64 + lane) * 16)));
+    db[ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, (uint32_t)((ks * 64 + lane) * 16)));
   }
-  f32x4 eb0 = zero4(), eb1 = zero4();   // erase gates of this thread's 8 channels
-  if (GDR2) {
-    eb0 = ld_b128(es, (uint32_t)(t8 * kDK + c8) * 4);
-    eb1 = ld_b128(es, (uint32_t)(t8 * kDK + c8 + 4) * 4);
+  // q and k of token rr, channels 32 ks + 8 p + i: the row operands
+  bf16x8 q8[4], k8[4];
+  f32x4 e8[4][2];   // erase gates of the same elements (Gated Delta Rule-2)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t off = (uint32_t)(rr * kDK + 32 * ks + 8 * p);
+    q8[ks] = __builtin_bit_cast(bf16x8, ld_b128(qs, off * 2));
+    k8[ks] = __builtin_bit_cast(bf16x8, ld_b128(ks_, off * 2));
+    if (GDR2) {
+      e8[ks][0] = ld_b128(es, off * 4);
+      e8[ks][1] = ld_b128(es, off * 4 + 16);
+    }
   }
 
-  // ---- 0. decay of every channel; dO rows and beta
-  if (tid < kDK) {
-    const int c = tid;
+  // ---- 0. decay of every channel (two per lane), dO rows, beta
+  {
+    const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
+    for (int i = lane; i < 16 * DV / 8; i += 64) {
+      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
+    }
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int c = lane + 64 * half;
     float run = 1.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -491,298 +494,279 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       sm.P[t][c] = run;
     }
     sm.gam[c] = run;
-  } else if (tid < kDK + 16) {
-    const int t = tid - kDK;
-    sm.beta[t] = GDR2 ? 1.f : (t < len ? a.beta[row0 + t] : 0.f);
-    sm.r1[t] = 0.f;
   }
-  {
-    const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
-    for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
-      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
-      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
-    }
-  }
-  __syncthreads();
+  if (lane < 16) sm.beta[lane] = GDR2 ? 1.f : (lane < len ? a.beta[row0 + lane] : 0.f);
+  wave_lds_fence();
 
-  // ---- 1. the decayed operands (bf16) for the matrix cores
-  {
+  // ---- 1. row operands of token rr (bf16): Qh, Kh (the read-side key), Kb = k / P, Kt
+  bf16x8 ah[4], at[4];
+  f32x4 accq = zero4(), acck = zero4(), acct = zero4();
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c0 = 32 * ks + 8 * p;
     float qh[8], kh[8], kb[8], kt[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float P = sm.P[t8][c8 + i], G = sm.gam[c8 + i];
+      const float P = sm.P[rr][c0 + i], G = sm.gam[c0 + i];
       const float rp = __builtin_amdgcn_rcpf(P);
-      const float qf = static_cast<float>(q8[i]), kf = static_cast<float>(k8[i]);
-      qh[i] = qf * P;
-      kh[i] = kf * P * (GDR2 ? (i < 4 ? eb0[i] : eb1[i - 4]) : 1.f);   // the read-side key
-      kb[i] = kf * rp;       // k / P
-      kt[i] = kb[i] * G;     // k E = k Gam / P
+      const float kf = static_cast<float>(k8[ks][i]);
+      qh[i] = static_cast<float>(q8[ks][i]) * P;
+      kh[i] = kf * P * (GDR2 ? e8[ks][i >> 2][i & 3] : 1.f);
+      kb[i] = kf * rp;
+      kt[i] = kb[i] * G;
     }
-    *reinterpret_cast<bf16x8*>(&sm.qh[t8][c8]) = cat8(pack4(qh[0], qh[1], qh[2], qh[3]),
-                                                       pack4(qh[4], qh[5], qh[6], qh[7]));
-    *reinterpret_cast<bf16x8*>(&sm.kh[t8][c8]) = cat8(pack4(kh[0], kh[1], kh[2], kh[3]),
-                                                       pack4(kh[4], kh[5], kh[6], kh[7]));
-    *reinterpret_cast<bf16x8*>(&sm.kb[t8][c8]) = cat8(pack4(kb[0], kb[1], kb[2], kb[3]),
-                                                       pack4(kb[4], kb[5], kb[6], kb[7]));
-    *reinterpret_cast<bf16x8*>(&sm.kt[t8][c8]) = cat8(pack4(kt[0], kt[1], kt[2], kt[3]),
-                                                       pack4(kt[4], kt[5], kt[6], kt[7]));
+    const bf16x8 bq = to_bf16x8(qh), bc = to_bf16x8(kb);
+    ah[ks] = to_bf16x8(kh);
+    at[ks] = to_bf16x8(kt);
+    accq = mfma32(bq, bc, accq);        // (Qh Kb^T)[4p + e][rr]
+    acck = mfma32(ah[ks], bc, acck);    // (Kh Kb^T)[4p + e][rr]
+    acct = mfma32(bc, ah[ks], acct);    // (Kh Kb^T)[rr][4p + e]
   }
-  __syncthreads();
-
-  // ---- 1b. A, M and Tm of the block (one wavefront)
-  if (wave == 0) {
-    f32x4 accq = zero4(), acck = zero4(), acct = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 32 * ks + 8 * p;
-      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.qh[rr][ch]);
-      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm.kh[rr][ch]);
-      const bf16x8 bc = *reinterpret_cast<const bf16x8*>(&sm.kb[rr][ch]);
-      accq = mfma32(bq, bc, accq);   // (Qh Kb^T)[4p + e][rr]
-      acck = mfma32(bk, bc, acck);   // (Kh Kb^T)[4p + e][rr]
-      acct = mfma32(bc, bk, acct);   // (Kh Kb^T)[rr][4p + e]
-    }
+  // ---- 2. M, A and Tm of the block
+  {
     f32x4 nc, nr;
     const float brr = sm.beta[rr];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * p + e;
-      sm.M[i][rr] = rr <= i ? accq[e] : 0.f;
+      sm.u.w.M[i][rr] = rr <= i ? accq[e] : 0.f;
       sm.A[i][rr] = rr < i ? acck[e] : 0.f;
       nc[e] = rr < i ? sm.beta[i] * acck[e] : 0.f;
       nr[e] = i < rr ? brr * acct[e] : 0.f;
     }
     const f32x4 inv = unit_lower_inverse(nc, nr, rr, p);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Tm[4 * p + e][rr] = inv[e];
+    for (int e = 0; e < 4; ++e) sm.u.w.Tm[4 * p + e][rr] = inv[e];
   }
-  __syncthreads();
+  wave_lds_fence();
+  bf16x4 tA, tT, mT;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tA[i] = static_cast<bf16>(sm.u.w.Tm[rr][4 * p + i]);   // Tm row rr
+    tT[i] = static_cast<bf16>(sm.u.w.Tm[4 * p + i][rr]);   // Tm^T row rr
+    mT[i] = static_cast<bf16>(sm.u.w.M[4 * p + i][rr]);    // M^T row rr
+  }
+  f32x4 btv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) btv[e] = sm.beta[4 * p + e];
 
-  // ---- 2. this wavefront's value tiles: R, U, dU, dY (token 4p + e, column 16 ct + rr)
-  bf16x8 sl[NCT], dl[NCT];
-  {
-    bf16x4 tA, tT, mT;
+  // ---- 3. the value tiles
+  f32x4 C1[8], C2[8], C3[8], g1 = zero4(), g2 = zero4();
+  float r2[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tA[i] = static_cast<bf16>(sm.Tm[rr][4 * p + i]);   // Tm row rr
-      tT[i] = static_cast<bf16>(sm.Tm[4 * p + i][rr]);   // Tm^T row rr
-      mT[i] = static_cast<bf16>(sm.M[4 * p + i][rr]);    // M^T row rr
+  for (int m = 0; m < 8; ++m) {
+    C1[m] = C2[m] = C3[m] = zero4();
+    r2[m] = 0.f;
+  }
+  f32x4 r1 = zero4();
+  const bf16x8 sel0 = selector(0, rr, p), sel1 = selector(1, rr, p);
+  const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
+#pragma unroll 1
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + rr;
+    // V (and the write gates) of this tile (token 4p + e, column col)
+    f32x4 vcol, wcol;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t o = (uint32_t)((4 * p + e) * DV + col);
+      vcol[e] = static_cast<float>(ld_b16(vs, o * 2));
+      wcol[e] = GDR2 ? ld_b32(ws_, o * 4) : 1.f;
     }
-    f32x4 bt;
+    // X = Kh S and dU2 = Kt dS' for this tile
+    f32x4 X = zero4(), dU2 = zero4();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bt[e] = sm.beta[4 * p + e];
-    f32x4 r1 = zero4();
+    for (int ks = 0; ks < 4; ++ks) {
+      X = mfma32(ah[ks], sb[ks], X);
+      dU2 = mfma32(at[ks], db[ks], dU2);
+    }
+    f32x4 R, x;
+    bf16x4 dob;
 #pragma unroll
-    for (int c = 0; c < NTW; ++c) {
-      const int col = 16 * (wave * NTW + c) + rr;
-      f32x4 X = zero4(), dU2 = zero4();
+    for (int e = 0; e < 4; ++e) {
+      R[e] = wcol[e] * vcol[e] - X[e];
+      x[e] = btv[e] * R[e];
+      dob[e] = sm.dor[4 * p + e][col];
+    }
+    const f32x4 U = mfma16(tA, pack4(x), zero4());
+    const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
+    const f32x4 dY = mfma16(tT, pack4(dU), zero4());
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.u.w.ut[4 * p + e][rr] = static_cast<bf16>(U[e]);
+      sm.u.w.yt[4 * p + e][rr] = static_cast<bf16>(dY[e]);
+      sm.u.w.bt[4 * p + e][rr] = static_cast<bf16>((GDR2 ? wcol[e] : btv[e]) * dY[e]);
+      r1[e] += dY[e] * R[e];
+      if (GDR2 && 4 * p + e < len)   // d write = V * dY
+        b.dwrite[(row0 + 4 * p + e) * DV + col] = vcol[e] * dY[e];
+    }
+    // this tile's S and dS' as they arrived; then prefetch the next tile's
+    bf16x8 sc[4], dc[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      sc[ks] = sb[ks];
+      dc[ks] = db[ks];
+    }
+    if (ct + 1 < NCT) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.kh[rr][32 * ks + 8 * p]);
-        const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sm.kt[rr][32 * ks + 8 * p]);
-        X = mfma32(ah, sa[c][ks], X);       // (Kh S)[4p + e][col]
-        dU2 = mfma32(at, da[c][ks], dU2);   // (Kt dS')[4p + e][col]
-      }
-      f32x4 R, x;
-      bf16x4 dob;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        R[e] = wv[c][e] * static_cast<float>(vv[c][e]) - X[e];
-        x[e] = bt[e] * R[e];
-        dob[e] = sm.dor[4 * p + e][col];
-      }
-      const f32x4 U = mfma16(tA, pack4(x), zero4());
-      const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
-      const f32x4 dY = mfma16(tT, pack4(dU), zero4());
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.ur[4 * p + e][col] = static_cast<bf16>(U[e]);
-        sm.dyr[4 * p + e][col] = static_cast<bf16>(dY[e]);
-        // dV = Diag(beta) dY, or w * dY with the write gate
-        sm.bdyr[4 * p + e][col] = static_cast<bf16>((GDR2 ? wv[c][e] : bt[e]) * dY[e]);
-        r1[e] += dY[e] * R[e];
-      }
-      if (GDR2) {   // d write = V * dY
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * p + e < len)
-            b.dwrite[(row0 + 4 * p + e) * DV + col] = static_cast<float>(vv[c][e]) * dY[e];
+        const uint32_t off = (uint32_t)((((ct + 1) * 4 + ks) * 64 + lane) * 16);
+        sb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
+        db[ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
       }
     }
-    // S and dS' of this wavefront's 32-channel slab (all value tiles), for phase 3
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const uint32_t off = (uint32_t)(((ct * 4 + wave) * 64 + lane) * 16);
-      sl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
-      dl[ct] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
+    wave_lds_fence();
+    // dV = Diag(beta) dY (w * dY): this tile's 16 token rows of 16 columns
+    if (lane < 32) {
+      const int t = lane >> 1, c8 = 8 * (lane & 1);
+      st_b128(vd, (uint32_t)(t * DV + 16 * ct + c8) * 2,
+              *reinterpret_cast<const bf16x8*>(&sm.u.w.bt[t][c8]));
     }
+    // the tile's share of the contractions over the value columns (k = column 16 ct + 4p + i)
+    const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][16 * ct + 4 * p]);
+    // beta = 1 with the Gated Delta Rule-2 gates: Diag(beta) dY is dY itself
+    const bf16x4 ay = *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.u.w.yt[rr][4 * p] : &sm.u.w.bt[rr][4 * p]);
+    const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.u.w.ut[rr][4 * p]);
+    const bf16x4 ayy = *reinterpret_cast<const bf16x4*>(&sm.u.w.yt[rr][4 * p]);
+    g1 = mfma16(ao, au, g1);     // (dO U^T)[4p + e][rr]
+    g2 = mfma16(ayy, au, g2);    // (dY U^T)[4p + e][rr]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v = r1[e];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      v += __shfl_xor(v, 8, 64);
-      if (rr == 0) atomicAdd(&sm.r1[4 * p + e], v);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int m = 2 * ks + hh;   // channel tile: channels 16 m + n
+        const f32x4 st = mfma32(sc[ks], hh ? sel1 : sel0, zero4());   // S[16 m + rr][16 ct + 4p + e]
+        const f32x4 dt = mfma32(dc[ks], hh ? sel1 : sel0, zero4());
+        const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
+        C1[m] = mfma16(ao, sb4, C1[m]);   // (dO S^T)[4p + e][16 m + rr]
+        C2[m] = mfma16(ay, sb4, C2[m]);   // (Diag(beta) dY S^T)
+        C3[m] = mfma16(au, db4, C3[m]);   // (U dS'^T)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r2[m] += st[e] * dt[e];
+      }
+    wave_lds_fence();   // the tile rows are rewritten by the next tile
   }
-  __syncthreads();
+  // reductions: r1 over the 16 columns of each lane group, r2 over the lane groups
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = r1[e];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    r1[e] = v;   // lane 16 p + r: token 4 p + e
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    r2[m] += __shfl_xor(r2[m], 16, 64);
+    r2[m] += __shfl_xor(r2[m], 32, 64);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sm.u.w.G1[4 * p + e][rr] = g1[e];
+    sm.G2[4 * p + e][rr] = g2[e];
+  }
+  wave_lds_fence();
 
-  // ---- 3. contractions over the value columns for this wavefront's channel slab
-  // (channels 32 w + 16 hh + rr), with S and dS' transposed by selector products
-  f32x4 C1[2], C2[2], C3[2];
-  float r2[2];
+  // ---- 4. the 16 x 16 corrections and the chain rule through the decay, per channel tile
+  bf16x4 dmr, dar, dmT, daT;   // dM, dA rows rr and columns rr
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const bf16x8 sel = selector(hh, rr, p);
-    C1[hh] = C2[hh] = C3[hh] = zero4();
-    r2[hh] = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const f32x4 st = mfma32(sl[ct], sel, zero4());   // S[ch][16 ct + 4p + e]
-      const f32x4 dt = mfma32(dl[ct], sel, zero4());   // dS'[ch][16 ct + 4p + e]
-      const int j = 16 * ct + 4 * p;
-      const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][j]);
-      // Diag(beta) dY (beta = 1 with the Gated Delta Rule-2 gates: dY itself)
-      const bf16x4 ay = *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.dyr[rr][j] : &sm.bdyr[rr][j]);
-      const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.ur[rr][j]);
-      const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
-      C1[hh] = mfma16(ao, sb4, C1[hh]);   // (dO S^T)[4p + e][ch]
-      C2[hh] = mfma16(ay, sb4, C2[hh]);   // (Diag(beta) dY S^T)[4p + e][ch]
-      C3[hh] = mfma16(au, db4, C3[hh]);   // (U dS'^T)[4p + e][ch]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r2[hh] += st[e] * dt[e];
-    }
-    r2[hh] += __shfl_xor(r2[hh], 16, 64);
-    r2[hh] += __shfl_xor(r2[hh], 32, 64);
+  for (int i = 0; i < 4; ++i) {
+    const int s_ = 4 * p + i;
+    dmr[i] = static_cast<bf16>(s_ <= rr ? sm.u.w.G1[rr][s_] : 0.f);
+    dar[i] = static_cast<bf16>(s_ < rr ? -sm.beta[rr] * sm.G2[rr][s_] : 0.f);
+    dmT[i] = static_cast<bf16>(rr <= s_ ? sm.u.w.G1[s_][rr] : 0.f);
+    daT[i] = static_cast<bf16>(rr < s_ ? -sm.beta[s_] * sm.G2[s_][rr] : 0.f);
   }
-  if (wave == 0 || wave == 1) {
-    // G1 = dO U^T (wavefront 0), G2 = dY U^T (wavefront 1)
-    f32x4 gg = zero4();
+  wave_lds_fence();   // G1 is read before dk overwrites it (same storage)
 #pragma unroll
-    for (int kk = 0; kk < DV / 32; ++kk) {
-      const int j = 32 * kk + 8 * p;
-      const bf16x8 aa = wave == 0 ? *reinterpret_cast<const bf16x8*>(&sm.dor[rr][j])
-                                  : *reinterpret_cast<const bf16x8*>(&sm.dyr[rr][j]);
-      const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&sm.ur[rr][j]);
-      gg = mfma32(aa, bu, gg);
-    }
+  for (int m = 0; m < 8; ++m) {
+    const int ch = 16 * m + rr;
+    const float G = sm.gam[ch];
+    float P[4], qf[4], kf[4], bf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (wave == 0) sm.G1[4 * p + e][rr] = gg[e];
-      else sm.G2[4 * p + e][rr] = gg[e];
+      const uint32_t off = (uint32_t)((4 * p + e) * kDK + ch);
+      P[e] = sm.P[4 * p + e][ch];
+      qf[e] = static_cast<float>(ld_b16(qs, off * 2));
+      kf[e] = static_cast<float>(ld_b16(ks_, off * 2));
+      bf[e] = GDR2 ? ld_b32(es, off * 4) : 1.f;
     }
-  }
-  // q, k (and the erase gate) of this lane's elements (token 4p + e, channel
-  // 32 w + 16 hh + rr)
-  bf16 qe[2][4], ke[2][4];
-  float be[2][4];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t off = (uint32_t)((4 * p + e) * kDK + 32 * wave + 16 * hh + rr);
-      qe[hh][e] = ld_b16(qs, off * 2);
-      ke[hh][e] = ld_b16(ks_, off * 2);
-      be[hh][e] = GDR2 ? ld_b32(es, off * 4) : 1.f;
-    }
-  __syncthreads();
-
-  // ---- 4. the 16 x 16 corrections and the chain rule through the decay
-  {
-    bf16x4 dmr, dar, dmT, daT;   // dM, dA rows rr and columns rr
+    // operands with k = token (4p + i) and n = this channel
+    bf16x4 bkb, bkh, bqh;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s_ = 4 * p + i;
-      dmr[i] = static_cast<bf16>(s_ <= rr ? sm.G1[rr][s_] : 0.f);
-      dar[i] = static_cast<bf16>(s_ < rr ? -sm.beta[rr] * sm.G2[rr][s_] : 0.f);
-      dmT[i] = static_cast<bf16>(rr <= s_ ? sm.G1[s_][rr] : 0.f);
-      daT[i] = static_cast<bf16>(rr < s_ ? -sm.beta[s_] * sm.G2[s_][rr] : 0.f);
+      const float rp = __builtin_amdgcn_rcpf(P[i]);
+      bkb[i] = static_cast<bf16>(kf[i] * rp);
+      bkh[i] = static_cast<bf16>(kf[i] * P[i] * bf[i]);
+      bqh[i] = static_cast<bf16>(qf[i] * P[i]);
     }
+    const f32x4 dQh = C1[m] + mfma16(dmr, bkb, zero4());
+    const f32x4 dKh = mfma16(dar, bkb, zero4()) - C2[m];
+    const f32x4 dKb = mfma16(daT, bkh, zero4()) + mfma16(dmT, bqh, zero4());
+    const f32x4 dKt = C3[m];
+    float lg = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int ch = 32 * wave + 16 * hh + rr;
-      bf16x4 bkb, bkh, bqh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bkb[i] = sm.kb[4 * p + i][ch];
-        bkh[i] = sm.kh[4 * p + i][ch];
-        bqh[i] = sm.qh[4 * p + i][ch];
-      }
-      const f32x4 dQh = C1[hh] + mfma16(dmr, bkb, zero4());
-      const f32x4 dKh = mfma16(dar, bkb, zero4()) - C2[hh];
-      const f32x4 dKb = mfma16(daT, bkh, zero4()) + mfma16(dmT, bqh, zero4());
-      const f32x4 dKt = C3[hh];
-      const float G = sm.gam[ch];
-      float lg = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * p + e;
-        const float P = sm.P[t][ch], rp = __builtin_amdgcn_rcpf(P);
-        const float qf = static_cast<float>(qe[hh][e]), kf = static_cast<float>(ke[hh][e]);
-        // (with the erase gate be, the read-side key is kh = be k P)
-        const float qh = qf * P, kh = kf * P * be[hh][e], kb = kf * rp, kt = kb * G;
-        // this wavefront's own channel columns: qh / kh / P are read above, then reused
-        sm.qh[t][ch] = static_cast<bf16>(dQh[e] * P);                                  // dq
-        sm.kh[t][ch] = static_cast<bf16>(dKh[e] * P * be[hh][e] + (dKb[e] + dKt[e] * G) * rp);
-        sm.P[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;          // d log P
-        if (GDR2 && t < len) b.derase[(row0 + t) * kDK + ch] = dKh[e] * kf * P;      // d erase
-        lg += dKt[e] * kt;
-      }
-      lg += __shfl_xor(lg, 16, 64);
-      lg += __shfl_xor(lg, 32, 64);
-      if (p == 0) sm.dlgam[ch] = lg + G * r2[hh];
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * p + e;
+      const float rp = __builtin_amdgcn_rcpf(P[e]);
+      const float qh = qf[e] * P[e], kh = kf[e] * P[e] * bf[e], kb = kf[e] * rp, kt = kb * G;
+      sm.dor[t][ch] = static_cast<bf16>(dQh[e] * P[e]);                                 // dq
+      sm.u.dkr[t][ch] = static_cast<bf16>(dKh[e] * P[e] * bf[e] + (dKb[e] + dKt[e] * G) * rp);
+      sm.P[t][ch] = dQh[e] * qh + dKh[e] * kh - dKb[e] * kb - dKt[e] * kt;             // d log P
+      if (GDR2 && t < len) b.derase[(row0 + t) * kDK + ch] = dKh[e] * kf[e] * P[e];  // d erase
+      lg += dKt[e] * kt;
     }
+    lg += __shfl_xor(lg, 16, 64);
+    lg += __shfl_xor(lg, 32, 64);
+    if (p == 0) sm.dlgam[ch] = lg + G * r2[m];
   }
-  __syncthreads();
+  wave_lds_fence();
 
-  // ---- 5. outputs: dq, dk, dv rows; dg (suffix sums); dbeta
+  // ---- 5. outputs: dq, dk rows; dg (suffix sums); dbeta
   {
     const rsrc_t qd = make_rsrc(static_cast<bf16*>(b.dq) + row0 * kDK, len * kDK * 2);
     const rsrc_t kd = make_rsrc(static_cast<bf16*>(b.dk) + row0 * kDK, len * kDK * 2);
-    const uint32_t off = (uint32_t)(t8 * kDK + c8) * 2;
-    st_b128(qd, off, *reinterpret_cast<const bf16x8*>(&sm.qh[t8][c8]));
-    st_b128(kd, off, *reinterpret_cast<const bf16x8*>(&sm.kh[t8][c8]));
-    const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
-    for (int i = tid; i < 16 * DV / 8; i += kGThreads) {
-      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
-      st_b128(vd, (uint32_t)(tt * DV + cc) * 2, *reinterpret_cast<const bf16x8*>(&sm.bdyr[tt][cc]));
-    }
-  }
-  if (PER_CHANNEL) {
-    if (tid < kDK) {
-      const int c = tid;
-      float acc = sm.dlgam[c];
-      for (int t = 15; t >= 0; --t) {
-        acc += sm.P[t][c];
-        if (t < len) b.dg[(row0 + t) * kDK + c] = acc;
-      }
-    }
-  } else {
-    // one decay per head: the sum over channels of the per-channel gradients
-    if (tid < kDK) {
-      const int c = tid;
-      float acc = sm.dlgam[c];
-      for (int t = 15; t >= 0; --t) {
-        acc += sm.P[t][c];
-        sm.P[t][c] = acc;
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      for (int t = 0; t < 16; ++t) {
-        float v = sm.P[t][lane] + sm.P[t][lane + 64];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-        if (lane == 0 && t < len) b.dg[row0 + t] = v;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane + 64 * i;   // 256 pieces of 8 channels
+      const int t = idx >> 4, c8 = 8 * (idx & 15);
+      const uint32_t off = (uint32_t)(t * kDK + c8) * 2;
+      st_b128(qd, off, *reinterpret_cast<const bf16x8*>(&sm.dor[t][c8]));
+      st_b128(kd, off, *reinterpret_cast<const bf16x8*>(&sm.u.dkr[t][c8]));
     }
   }
-  if (!GDR2 && tid >= 192 && tid < 208) {
-    const int t = tid - 192;
-    float acc = sm.r1[t];
-    for (int s_ = 0; s_ < t; ++s_) acc -= sm.A[t][s_] * sm.G2[t][s_];
-    if (t < len) b.dbeta[row0 + t] = acc;
+  float dgs[2][16];   // per-channel suffix sums (lane's two channels)
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int c = lane + 64 * half;
+    float acc = sm.dlgam[c];
+#pragma unroll
+    for (int t = 15; t >= 0; --t) {
+      acc += sm.P[t][c];
+      dgs[half][t] = acc;
+      if (PER_CHANNEL && t < len) b.dg[(row0 + t) * kDK + c] = acc;
+    }
+  }
+  if (!PER_CHANNEL) {   // one decay per head: the sum over the channels
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float v = dgs[0][t] + dgs[1][t];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0 && t < len) b.dg[row0 + t] = v;
+    }
+  }
+  if (!GDR2) {
+    // dbeta_t = sum_j dY_tj R_tj - sum_s A_ts (dY U^T)_ts; lane 16 p holds token 4 p + e
+    if (rr == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * p + e;
+        float acc = r1[e];
+        for (int s_ = 0; s_ < t; ++s_) acc -= sm.A[t][s_] * sm.G2[t][s_];
+        if (t < len) b.dbeta[row0 + t] = acc;
+      }
+    }
   }
 }
 
@@ -814,11 +798,11 @@ hipError_t launch_bwd_kernels(BwdArgs& b, bool per_channel, unsigned chains, int
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)slots * a.H;
   if (a.dv == 128) {
-    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
+    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, 64, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, 64, 0, stream>>>(b, slots);
   } else {
-    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, kGThreads, 0, stream>>>(b, slots);
+    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, 64, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, 64, 0, stream>>>(b, slots);
   }
   return hipGetLastError();
 }
