@@ -47,12 +47,12 @@ CHUNK = 64
 # plain 1 GiB copy kernel in the same runs. It is reported only while the kernel source
 # is the one the counters were taken on (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3247139225,
-    "kernel_sha256": "1523fa23de3f004a8259c48e64df7a14d12f4376e4f2b297a0d4f161f12ca55e",
+    "bytes": 3247121264,
+    "kernel_sha256": "00bae921076522de8f1dc0e6eb723be29e1a0a92c81ba241d2ce8b93bb2c27fe",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5386471247,
-    "kernel_sha256": "1523fa23de3f004a8259c48e64df7a14d12f4376e4f2b297a0d4f161f12ca55e",
+    "bytes": 5386412111,
+    "kernel_sha256": "00bae921076522de8f1dc0e6eb723be29e1a0a92c81ba241d2ce8b93bb2c27fe",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,
