@@ -475,27 +475,43 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     }
   }
 
-  // ---- 0. decay of every channel (two per lane), dO rows, beta
+  // ---- 0. decay of every channel (two per lane), dO rows, beta. Every load is issued
+  // before the first use: bounded reads past the block's last token return g = 0.
   {
     const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
-    for (int i = lane; i < 16 * DV / 8; i += 64) {
-      const int tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
-      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
-    }
-  }
+    const rsrc_t gs = make_rsrc(a.g + row0 * (PER_CHANNEL ? kDK : 1),
+                                len * (PER_CHANNEL ? kDK : 1) * 4);
+    f32x4 dov[16 * DV / 8 / 64];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int c = lane + 64 * half;
-    float run = 1.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float gv = t < len ? (PER_CHANNEL ? a.g[(row0 + t) * kDK + c] : a.g[row0 + t]) : 0.f;
-      run *= __expf(gv);
-      sm.P[t][c] = run;
+    for (int j = 0; j < 16 * DV / 8 / 64; ++j) {
+      const int i = lane + 64 * j, tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+      dov[j] = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
     }
-    sm.gam[c] = run;
+    const float bv = GDR2 ? 1.f : ld_b32(make_rsrc(a.beta + row0, len * 4), (lane & 15) * 4);
+    float gv[2][16];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        gv[half][t] = ld_b32(gs, (uint32_t)(PER_CHANNEL ? t * kDK + lane + 64 * half : t) * 4);
+#pragma unroll
+    for (int j = 0; j < 16 * DV / 8 / 64; ++j) {
+      const int i = lane + 64 * j, tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+      *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = dov[j];
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = lane + 64 * half;
+      float run = 1.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        run *= __expf(gv[half][t]);
+        sm.P[t][c] = run;
+      }
+      sm.gam[c] = run;
+    }
+    if (lane < 16) sm.beta[lane] = bv;
   }
-  if (lane < 16) sm.beta[lane] = GDR2 ? 1.f : (lane < len ? a.beta[row0 + lane] : 0.f);
   wave_lds_fence();
 
   // ---- 1. row operands of token rr (bf16): Qh, Kh (the read-side key), Kb = k / P, Kt
@@ -645,6 +661,14 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       }
     wave_lds_fence();   // the tile rows are rewritten by the next tile
   }
+  // q and k rows again (token rr, channels 32 ks + 8 p + i) for the per-channel step below,
+  // loaded now so that the reductions cover their latency
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t off = (uint32_t)(rr * kDK + 32 * ks + 8 * p);
+    q8[ks] = __builtin_bit_cast(bf16x8, ld_b128(qs, off * 2));
+    k8[ks] = __builtin_bit_cast(bf16x8, ld_b128(ks_, off * 2));
+  }
   // reductions: r1 over the 16 columns of each lane group, r2 over the lane groups
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -682,13 +706,17 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   for (int m = 0; m < 8; ++m) {
     const int ch = 16 * m + rr;
     const float G = sm.gam[ch];
+    // q and k of token 4 p + e, channel ch: the rows transposed by the selector (exact)
+    const bf16x8 sel = (m & 1) ? sel1 : sel0;
+    const f32x4 qT = mfma32(q8[m >> 1], sel, zero4());
+    const f32x4 kT = mfma32(k8[m >> 1], sel, zero4());
     float P[4], qf[4], kf[4], bf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t off = (uint32_t)((4 * p + e) * kDK + ch);
       P[e] = sm.P[4 * p + e][ch];
-      qf[e] = static_cast<float>(ld_b16(qs, off * 2));
-      kf[e] = static_cast<float>(ld_b16(ks_, off * 2));
+      qf[e] = qT[e];
+      kf[e] = kT[e];
       bf[e] = GDR2 ? ld_b32(es, off * 4) : 1.f;
     }
     // operands with k = token (4p + i) and n = this channel
