@@ -180,7 +180,7 @@ __device__ __forceinline__ void block_tiles_rev(RStage& st, const bf16 (*qg)[kLD
 
 // dO of one value column for the 16 tokens of block I (token 16 I + 4 p + e), raw bf16.
 template <int DV>
-__device__ __forceinline__ void load_col(bf16 (&x)[4], rsrc_t src, uint32_t off) {
+__device__ __forceinline__ void load_col(bf16x4& x, rsrc_t src, uint32_t off) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) x[e] = ld_b16(src, off + e * DV * 2);
 }
@@ -213,7 +213,7 @@ __device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const To
         const int ch = 32 * (m >> 1) + 8 * p + 4 * (m & 1) + e;
         D_acc[c][m][e] = b.dsT ? b.dsT[state_off + (size_t)ch * DV + col[c]] : 0.f;
       }
-  bf16 dd[NT][4][4];
+  bf16x4 dd[NT][4];
   if (nsteps > 0) {
 #pragma unroll
     for (int c = 0; c < NT; ++c)
@@ -247,11 +247,13 @@ __device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const To
       const bf16x4 aT = *reinterpret_cast<const bf16x4*>(&st.aqkT[I][rr][4 * p]);
       const bf16x4 tT = *reinterpret_cast<const bf16x4*>(&st.tdT[I][rr][4 * p]);
       bf16x4 dob[NT], nby[NT];
+      // the next step's dO of this block (without a branch, which would make the compiler
+      // wait for the load there; at s = 0 it reloads this step's, unused)
+      const int sn = s > 0 ? s - 1 : 0;
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dob[c][e] = dd[c][I][e];
-        if (s > 0) load_col<DV>(dd[c][I], dosrc, coff[c] + ((s - 1) * kC + 16 * I) * DV * 2);
+        dob[c] = dd[c][I];
+        load_col<DV>(dd[c][I], dosrc, coff[c] + (sn * kC + 16 * I) * DV * 2);
         // dU = M^T dO + Kt dS' (the 16x16x16 product starts from zero: accumulating it
         // onto a 16x16x32 result still in flight is not covered by the wait states)
         const f32x4 u = dU[c] + mfma16(aT, dob[c], zero4());
