@@ -3,6 +3,8 @@
 // synchronises or keeps state between calls.
 #include <cstdint>
 
+#include <algorithm>
+
 #include "kda.h"
 #include "kda_internal.h"
 
@@ -48,8 +50,15 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
   if (dt != KDA_BF16 || !kda::chunk_mfma_supports(dk, dv, T)) return 0;
   const long long N = num_seqs > 0 ? num_seqs : B;
   if (N * H > (1ll << 24)) return 0;
+  const int cus = device_compute_units();
+  // dv = dk: the segment plan (packed sequences, or fewer equal-length chains than compute
+  // units); it also holds the work list that the Gated Delta Rule-2 gates use
+  if (dv == dk && (num_seqs > 0 || N * H < cus)) {
+    const size_t sp = kda::chunk_segplan_bytes((int)N, H, T, dv, num_seqs > 0);
+    if (sp > 0) return std::max(sp, num_seqs > 0 ? kda::chunk_plan_bytes(num_seqs, H, dv) : 0);
+  }
   // few chains for the device: segments and their states (this also covers the work list)
-  const size_t seg = kda::chunk_seg_bytes((int)N, H, T, dv, device_compute_units());
+  const size_t seg = kda::chunk_seg_bytes((int)N, H, T, dv, cus);
   if (seg > 0) return seg;
   // equal-length batches are scheduled on the host: only packed sequences need a work list
   if (num_seqs == 0) return 0;
@@ -89,10 +98,16 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   a.hist = nullptr;
   a.seg_len = 0;
   a.nseg = 1;
+  a.seg_slots = 0;
+  a.seg_mats = nullptr;
+  a.qt = nullptr;
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
   if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T)) {
-    if (scheduled && !erase && kda::chunk_seg_bytes(a.N, H, T, dv, a.cus) > 0)
+    const size_t sp = kda::chunk_segplan_bytes(a.N, H, T, dv, cu_seqlens != nullptr);
+    if (scheduled && !erase && sp > 0 && workspace_bytes >= sp)
+      err = kda::launch_chunk_mfma_segplan(a, per_channel, workspace, stream);
+    else if (scheduled && !erase && kda::chunk_seg_bytes(a.N, H, T, dv, a.cus) > 0)
       err = kda::launch_chunk_mfma_segmented(a, per_channel, workspace, stream);
     else
       err = kda::launch_chunk_mfma(a, per_channel, stream);
@@ -208,6 +223,7 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
   a.plan = nullptr; a.cus = device_compute_units(); a.split_all = 0; a.hist = nullptr;
   a.seg_len = 0; a.nseg = 1;
+  a.seg_slots = 0; a.seg_mats = nullptr; a.qt = nullptr;
   b.dout = grad_o; b.dsT = grad_final_state;
   b.dq = grad_q; b.dk = grad_k; b.dv = grad_v; b.dg = grad_g; b.dbeta = grad_beta;
   b.derase = grad_erase; b.dwrite = grad_write;

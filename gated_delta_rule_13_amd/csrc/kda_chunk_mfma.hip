@@ -42,6 +42,8 @@
 // identity token) and writes past it are dropped, so partial chunks need no branches.
 #include <stddef.h>
 
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -55,7 +57,21 @@ constexpr int kLDK = kDK + 8;  // padded LDS row (bf16) of [token][channel] tile
 constexpr int kLDT = kC + 8;   // padded LDS row (bf16) of [channel][token] tiles
 constexpr int kPrepWaves = 4;  // one per 16-token block
 constexpr int kModeOut = 0, kModeHist = 1, kModeState = 2, kModeTrans = 3;  // see state_role
+constexpr int kModeTransOut = 5;  // see state_role
 constexpr int kModePair = 4;  // launch of both kModeState and kModeTrans items (see the kernel)
+constexpr int kModeSeg = 6;   // launch of a segment plan (see chunk_segplan_kernel)
+// Segment plan (chunk_segplan_kernel) in the workspace, as 32-bit words: a header of kSegHdr
+// words ([0] items, [1] segment length X in 64-token chunks or 0 without segments, [2]
+// segments over all sequences, [3] correction units per head), then segbase[N + 1] (the
+// first segment of sequence n: its segments are slots segbase[n] .. segbase[n + 1] - 1),
+// corr_off[slots + 1] (the first correction unit of slot s) and two words per item:
+// ((n * H + h) << 2) | part, and (segment << 2) | kind.
+constexpr int kSegWhole = 0, kSegFirst = 1, kSegZero = 2, kSegTrans = 3;  // item kinds
+constexpr int kSegHdr = 8;
+__host__ __device__ inline size_t segplan_corr_off(int N) { return kSegHdr + (size_t)N + 1; }
+__host__ __device__ inline size_t segplan_items_off(int N, int slots) {
+  return segplan_corr_off(N) + (size_t)slots + 1;
+}
 
 #ifndef KDA_STATE_PRIO
 #define KDA_STATE_PRIO 3
@@ -231,17 +247,25 @@ __device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int s
 //              hist_chain_offset), for the backward pass; no outputs;
 //   kModeState nothing else (the end state of a segment started from zero);
 //   kModeTrans the transition of the segment: the identity as initial state and zero values,
-//              so that the final state is the dk x dk product of the segment's token maps.
+//              so that the final state is the dk x dk product of the segment's token maps;
+//   kModeTransOut  the same, and its outputs: with the identity as state the output of token t
+//              is the query carried back to the segment start (M_t^T q_t, M_t the product of
+//              the token maps up to t), dk values per token, so that the output from any start
+//              state S is S^T M_t^T q_t plus the output from the zero state.
+// Outputs go to obase (rows of DV values laid out as o).
 template <int NT, int DV, bool GDR2, int MODE>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const TokenRange& tr,
                                            size_t row0, const float* s0p, float* sTp,
                                            size_t hist_off, int nsteps, int cbase, int lane,
-                                           int rr, int p) {
-  constexpr bool HIST = MODE == kModeHist, OUT = MODE == kModeOut, TRANS = MODE == kModeTrans;
+                                           int rr, int p, void* obase) {
+  constexpr bool HIST = MODE == kModeHist;
+  constexpr bool OUT = MODE == kModeOut || MODE == kModeTransOut;
+  constexpr bool TRANS = MODE == kModeTrans || MODE == kModeTransOut;
   // (the transition reads no values: a zero-sized view returns zeros)
   const rsrc_t vsrc = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV,
                                 TRANS ? 0u : (uint32_t)tr.len * DV * 2);
-  const rsrc_t odst = make_rsrc(static_cast<bf16*>(a.o) + row0 * DV, (uint32_t)tr.len * DV * 2);
+  const rsrc_t odst = make_rsrc(static_cast<bf16*>(obase) + (OUT ? row0 * DV : 0),
+                                OUT ? (uint32_t)tr.len * DV * 2 : 0u);
   const rsrc_t hdst = make_rsrc(static_cast<char*>(a.hist) + (HIST ? hist_off : 0),
                                 HIST ? (uint32_t)nsteps * 4 * kDK * DV * 2 : 0);
   int col[NT];
@@ -387,7 +411,16 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
 
   // work item: a chain, or one half of its value columns
   int chain = blockIdx.x, part = 0;
-  if (a.plan) {
+  int kseg = 0, skind = kSegWhole;  // segment plans: segment index and item kind
+  if constexpr (MODE == kModeSeg) {
+    if (blockIdx.x >= a.plan[0]) return;  // the grid is sized for the largest plan
+    const uint32_t* it = a.plan + segplan_items_off(a.N, a.seg_slots) + 2 * blockIdx.x;
+    chain = (int)(it[0] >> 2);
+    part = (int)(it[0] & 3);
+    kseg = (int)(it[1] >> 2);
+    skind = (int)(it[1] & 3);
+    if (chain >= a.N * a.H) return;
+  } else if (a.plan) {
     if (blockIdx.x >= a.plan[0]) return;  // the grid is sized for the largest schedule
     const uint32_t item = a.plan[1 + blockIdx.x];
     chain = (int)(item >> 2);
@@ -434,6 +467,33 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
             item * kDK * DV;
     }
   }
+  // segment plans: segment kseg of X tokens of its sequence. The first segment runs from the
+  // chain's initial state and leaves the start state of the second; every later one runs
+  // twice, from the zero state (outputs and end state) and as its transition (carried-back
+  // queries and the dk x dk transition), and its outputs are completed afterwards.
+  void* obase = a.o;
+  if constexpr (MODE == kModeSeg) {
+    if (skind != kSegWhole) {
+      const int xt = (int)a.plan[1] * kC;
+      const int first = kseg * xt;
+      if (xt <= 0 || first >= tr.len) return;
+      tr.t0 += first;
+      tr.len = min(xt, tr.len - first);
+      const size_t slot = a.plan[kSegHdr + n] + (size_t)kseg;
+      if (slot + 1 >= (size_t)a.seg_slots + (skind == kSegFirst ? 0 : 1)) return;
+      const size_t msz = (size_t)kDK * DV, per = (size_t)a.seg_slots * a.H * msz;
+      if (skind == kSegFirst) {
+        sTp = a.seg_mats + ((slot + 1) * a.H + h) * msz;         // start of segment 1
+      } else if (skind == kSegZero) {
+        s0p = nullptr;
+        sTp = a.seg_mats + 2 * per + (slot * a.H + h) * msz;     // B: end state from zero
+      } else {
+        s0p = nullptr;
+        sTp = a.seg_mats + per + (slot * a.H + h) * msz;         // A: the transition
+        obase = a.qt;
+      }
+    }
+  }
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
   const size_t hist_off = HIST ? hist_chain_offset(a, n, h, tr) : 0;
   const int nsteps = (tr.len + kC - 1) / kC;
@@ -470,22 +530,31 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     if constexpr (MODE == kModePair) {  // whole items only
       if (kind == kModeTrans)
         state_role<NT, DV, GDR2, kModeTrans>(sm, a, tr, row0, s0p, sTp, 0, nsteps, 16 * NT * j,
-                                             lane, rr, p);
+                                             lane, rr, p, nullptr);
       else
         state_role<NT, DV, GDR2, kModeState>(sm, a, tr, row0, s0p, sTp, 0, nsteps, 16 * NT * j,
-                                             lane, rr, p);
+                                             lane, rr, p, nullptr);
       return;
     }
-    if constexpr (NT > 1) {
-      if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
-        state_role<NT / 2, DV, GDR2, MODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps,
-                                           (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane,
-                                           rr, p);
+    // segment plans: the transition items, then whole or half output items
+    constexpr int RMODE = MODE == kModeSeg ? kModeOut : MODE;
+    if constexpr (MODE == kModeSeg) {
+      if (skind == kSegTrans) {
+        state_role<NT, DV, GDR2, kModeTransOut>(sm, a, tr, row0, s0p, sTp, 0, nsteps,
+                                                16 * NT * j, lane, rr, p, obase);
         return;
       }
     }
-    state_role<NT, DV, GDR2, MODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps, 16 * NT * j,
-                                   lane, rr, p);
+    if constexpr (NT > 1) {
+      if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
+        state_role<NT / 2, DV, GDR2, RMODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps,
+                                            (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane,
+                                            rr, p, obase);
+        return;
+      }
+    }
+    state_role<NT, DV, GDR2, RMODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps, 16 * NT * j,
+                                    lane, rr, p, obase);
   }
 }
 
@@ -582,6 +651,283 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_plan_kernel(const int32_t*
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Segment plan. The schedule above cannot shorten a chain below kHalfCost of its length; when
+// the longest sequences still bound the launch, they are cut into segments of X tokens
+// instead. The first segment runs as usual from the initial state and hands its end state to
+// the second; every later segment k runs twice at the same time as the others, from the zero
+// state (outputs O0 and end state B_k) and from the identity (its dk x dk transition A_k and
+// the carried-back queries Qt). By linearity in the start state S_k, the segment's outputs
+// are O0 + Qt S_k and its end state A_k S_k + B_k: a short chain over the segments gives
+// every S_k (seg_chain_kernel) and a matrix-core pass adds Qt S_k (seg_correct_kernel).
+// The planner picks X (a multiple of 64 tokens, at least xc_min chunks) to minimise
+// max(longest item, total work / compute units) plus the cost of the corrections; without a
+// gain of kSegMinGain it keeps the halves schedule. Chunk counts stand for item times.
+
+constexpr int kSegGroup = 256;           // tokens per correction unit
+// (measured on MI355X, one chunk-time = 64 tokens of one item, about 4.5 us)
+constexpr float kSegCorrCost = 0.4f;     // correction of one chunk, in chunk-times of one item
+constexpr float kSegFixedCost = 8.f;     // the planner's extra time and the two extra launches
+constexpr float kSegChainCost = 0.5f;    // one step of the chain over the segments
+constexpr float kSegPacking = 1.1f;      // list scheduling of items shorter than the longest
+constexpr float kSegMinGain = 0.95f;
+
+// bitonic sort of entries 0 .. n2 - 1 (n2 a power of two, at most the block size): larger
+// key first, then lower (a, b)
+__device__ __forceinline__ void sort_entries(int* key, int* ea, int* eb, int n2) {
+  const int t = threadIdx.x;
+  for (int k = 2; k <= n2; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int u = t ^ j;
+      if (t < n2 && u > t) {
+        const bool t_first =
+            key[t] > key[u] ||
+            (key[t] == key[u] && (ea[t] < ea[u] || (ea[t] == ea[u] && eb[t] < eb[u])));
+        if (((t & k) == 0) != t_first) {
+          const int k0 = key[t], a0 = ea[t], b0 = eb[t];
+          key[t] = key[u];
+          ea[t] = ea[u];
+          eb[t] = eb[u];
+          key[u] = k0;
+          ea[u] = a0;
+          eb[u] = b0;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// Exclusive prefix sum of v over the kMaxPlanSeqs threads (every thread calls it with its
+// value; x is kMaxPlanSeqs + 1 words of scratch): returns the sum over lower threads and
+// leaves the total in x[kMaxPlanSeqs]. Wavefront scans by lane shifts, then the wavefront
+// totals.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* x) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  __syncthreads();  // earlier readers of x are done
+  if (lane == 63) x[wv] = incl;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+  for (int i = 0; i < kMaxPlanSeqs / 64; ++i) {
+    const uint32_t wt = x[i];
+    if (i < wv) before += wt;
+    total += wt;
+  }
+  __syncthreads();
+  if (t == 0) x[kMaxPlanSeqs] = total;
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
+    const int32_t* cu, int N, int H, int T, int cus, int slots_max, int xc_min, uint32_t* plan) {
+  __shared__ int cl[kMaxPlanSeqs];     // chunks of sequence n
+  __shared__ int ln[kMaxPlanSeqs];     // tokens of sequence n
+  __shared__ int key[kMaxPlanSeqs];    // entries: chunks
+  __shared__ int ea[kMaxPlanSeqs];     //          sequence
+  __shared__ int eb[kMaxPlanSeqs];     //          segment
+  __shared__ float bnd[kMaxPlanSeqs];  // bound of candidate segment length j
+  __shared__ int bix[kMaxPlanSeqs];
+  __shared__ int ent_parts[kMaxPlanSeqs];
+  __shared__ uint32_t ent_off[kMaxPlanSeqs + 1];
+  __shared__ int n_ent, xc_sel;
+  const int t = threadIdx.x;
+  uint32_t* segbase = plan + kSegHdr;
+  uint32_t* corr_off = plan + segplan_corr_off(N);
+  uint32_t* items = plan + segplan_items_off(N, slots_max);
+  int c = -1;
+  if (t < N) {
+    const int len = token_range(cu, t, T).len;
+    c = (len + kC - 1) / kC;
+    cl[t] = c;
+    ln[t] = len;
+  }
+  key[t] = c;
+  ea[t] = t;
+  eb[t] = 0;
+  __syncthreads();
+  int n2 = 1;
+  while (n2 < N) n2 <<= 1;
+  sort_entries(key, ea, eb, n2);
+  const int maxc = key[0] > 0 ? key[0] : 0;
+  // candidate segment lengths xc_min + j * step (chunks), shorter than the longest sequence
+  const int step = maxc > xc_min ? (maxc - xc_min + kMaxPlanSeqs - 1) / kMaxPlanSeqs : 1;
+  {
+    const int xc = xc_min + t * step;
+    float b = 3.0e38f;
+    if (xc < maxc) {
+      long long total = 0, corr = 0, slots = 0;
+      int longest = 0, most = 1;
+      for (int i = 0; i < N; ++i) {
+        const int ci = cl[i];
+        const int extra = ci > xc ? ci - xc : 0;
+        const int ns_i = ci > xc ? (ci + xc - 1) / xc : 1;
+        slots += ns_i;
+        most = max(most, ns_i);
+        total += ci + extra;
+        corr += extra;
+        longest = max(longest, min(ci, xc));
+      }
+      if (slots <= slots_max && slots <= kMaxPlanSeqs)
+        b = fmaxf((float)longest, kSegPacking * H * total / cus) +
+            kSegCorrCost * H * corr / cus + kSegFixedCost + kSegChainCost * (most - 1);
+    }
+    bnd[t] = b;
+    bix[t] = t;
+  }
+  __syncthreads();
+  {  // the best candidate (lowest index on ties): within each wavefront, then across them
+    float bv = bnd[t];
+    int bi = t;
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+      const float ov = __shfl_xor(bv, d, 64);
+      const int oi = __shfl_xor(bi, d, 64);
+      if (ov < bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    __syncthreads();
+    if ((t & 63) == 0) {
+      bnd[t >> 6] = bv;
+      bix[t >> 6] = bi;
+    }
+    __syncthreads();
+    if (t == 0) {
+      for (int i = 1; i < kMaxPlanSeqs / 64; ++i)
+        if (bnd[i] < bnd[0] || (bnd[i] == bnd[0] && bix[i] < bix[0])) {
+          bnd[0] = bnd[i];
+          bix[0] = bix[i];
+        }
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    // the halves schedule (as chunk_plan_kernel) and its bound
+    double total = 0.0;
+    for (int i = 0; i < N; ++i) total += (double)key[i] * H;
+    int ns = 0;
+    double maxhalf = 0.0;
+    while (ns < N && key[ns] > 0) {
+      const double c0 = key[ns], next = ns + 1 < N ? key[ns + 1] : 0.0;
+      const double bound = fmax(fmax(c0, maxhalf), total / cus);
+      const double total2 = total + H * (2.0 * kHalfCost - 1.0) * c0;
+      const double maxhalf2 = fmax(maxhalf, kHalfCost * c0);
+      if (!(fmax(fmax(next, maxhalf2), total2 / cus) < 0.98 * bound)) break;
+      total = total2;
+      maxhalf = maxhalf2;
+      ++ns;
+    }
+    const double half_bound = fmax(fmax(ns < N ? key[ns] : 0.0, maxhalf), total / cus);
+    xc_sel = bnd[0] < kSegMinGain * half_bound ? xc_min + bix[0] * step : 0;
+    plan[1] = (uint32_t)xc_sel;
+    if (xc_sel == 0) {
+      // the halves schedule: sequences by chunk count, halves of the ns longest
+      int a = 0, b = ns, e = 0;
+      uint32_t off = 0;
+      while (a < ns || b < N) {
+        const bool split = a < ns && (b >= N || kHalfCost * key[a] >= key[b]);
+        const int i = split ? a++ : b++;
+        eb[e] = ea[i];  // the merge reads key and ea only
+        ent_parts[e] = split ? 2 : 1;
+        ent_off[e] = off;
+        off += (uint32_t)H * ent_parts[e];
+        ++e;
+      }
+      ent_off[e] = off;
+      n_ent = e;
+      plan[0] = off;
+      plan[2] = 0;
+      plan[3] = 0;
+    }
+  }
+  __syncthreads();
+  const int xc = xc_sel;
+  if (xc == 0) {
+    if (t < n_ent) ea[t] = eb[t];
+    __syncthreads();
+  } else {
+    // segments of every sequence, in sequence order (slot = segbase[n] + k)
+    const int ns_t = t < N ? (cl[t] > xc ? (cl[t] + xc - 1) / xc : 1) : 0;
+    const uint32_t base = block_exclusive_scan((uint32_t)ns_t, ent_off);
+    const int slots = (int)ent_off[kMaxPlanSeqs];
+    if (t < N) {
+      segbase[t] = base;
+      for (int k = 0; k < ns_t; ++k) {
+        key[base + k] = ns_t == 1 ? cl[t] : min(xc, cl[t] - k * xc);
+        ea[base + k] = t;
+        eb[base + k] = k;
+      }
+    }
+    if (t == 0) segbase[N] = (uint32_t)slots;
+    if (t >= slots) key[t] = -1;  // padding sorts last
+    __syncthreads();
+    // correction units of every slot (later segments only), in slot order
+    uint32_t units = 0;
+    if (t < slots && eb[t] > 0) {
+      const int len = ln[ea[t]], k = eb[t];
+      units = (uint32_t)(min(xc * kC, len - k * xc * kC) + kSegGroup - 1) / kSegGroup;
+    }
+    const uint32_t uoff = block_exclusive_scan(units, ent_off);
+    if (t < slots) corr_off[t] = uoff;
+    if (t == 0) {
+      corr_off[slots] = ent_off[kMaxPlanSeqs];
+      plan[2] = (uint32_t)slots;
+      plan[3] = ent_off[kMaxPlanSeqs];
+    }
+    __syncthreads();
+    int m2 = 1;
+    while (m2 < slots) m2 <<= 1;
+    sort_entries(key, ea, eb, m2);
+    // items of every entry: whole sequences and first segments H, later segments 2 H
+    int parts = 0;
+    if (t < slots) {
+      const int n = ea[t];
+      const bool split = cl[n] > xc;
+      parts = !split ? 0 : eb[t] == 0 ? 1 : 2;
+      ent_parts[t] = parts;
+    }
+    const uint32_t eoff = block_exclusive_scan(t < slots ? (uint32_t)H * (parts == 2 ? 2 : 1) : 0u,
+                                               ent_off);
+    const uint32_t tot = ent_off[kMaxPlanSeqs];
+    __syncthreads();
+    if (t < slots) ent_off[t] = eoff;
+    if (t == 0) {
+      ent_off[slots] = tot;
+      n_ent = slots;
+      plan[0] = tot;
+    }
+    __syncthreads();
+  }
+  const uint32_t n_items = ent_off[n_ent];
+  for (uint32_t i = t; i < n_items; i += kMaxPlanSeqs) {
+    int lo = 0, hi = n_ent - 1;  // entry holding item i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ent_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t local = i - ent_off[lo];
+    uint32_t hh = local, part = 0, w1 = 0;
+    if (xc == 0) {
+      if (ent_parts[lo] == 2) split_item(local, (uint32_t)H, hh, part);
+    } else {
+      const int kind = ent_parts[lo] == 0 ? kSegWhole
+                       : ent_parts[lo] == 1 ? kSegFirst
+                       : (local < (uint32_t)H ? kSegZero : kSegTrans);
+      hh = local % (uint32_t)H;
+      w1 = ((uint32_t)eb[lo] << 2) | (uint32_t)kind;
+    }
+    items[2 * i] = (((uint32_t)ea[lo] * H + hh) << 2) | part;
+    items[2 * i + 1] = w1;
+  }
+}
+
 template <int NS, int NT, bool PER_CHANNEL, int MODE>
 hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (MODE == kModeOut || MODE == kModeHist) {
@@ -671,6 +1017,186 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const int32_t* cu, int
   }
 }
 
+// Start states of the later segments of a segment plan and the chain's final state:
+// S_{k+1} = A_k S_k + B_k from S_1 (left by the first segment), on the fp32 matrix cores,
+// dv = dk. One workgroup per (chain, 16 value columns): S's 16 columns in LDS; wavefront w
+// owns row tiles 2 w and 2 w + 1 and prefetches the next step's A rows and B tile.
+__global__ __launch_bounds__(256) void seg_chain_kernel(ChunkArgs a) {
+  __shared__ float S[kDK][17];
+  const uint32_t* plan = a.plan;
+  if (plan[1] == 0) return;
+  const int chain = blockIdx.x, cb = 16 * blockIdx.y;
+  const int n = chain / a.H, h = chain % a.H;
+  const uint32_t s0 = plan[kSegHdr + n], ns = plan[kSegHdr + n + 1] - s0;
+  if (ns < 2 || s0 + ns > (uint32_t)a.seg_slots) return;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, rr = lane & 15, p = lane >> 4;
+  const size_t msz = (size_t)kDK * kDK, per = (size_t)a.seg_slots * a.H * msz;
+  const float* first = a.seg_mats + ((size_t)(s0 + 1) * a.H + h) * msz;
+  for (int i = threadIdx.x; i < kDK * 16; i += 256) S[i >> 4][i & 15] = first[(size_t)(i >> 4) * kDK + cb + (i & 15)];
+  // operands of step k: A[16 (2 wv + ti) + rr][4 p + 16 j .. + 3] (16-byte loads) and
+  // B[16 (2 wv + ti) + 4 p + e][cb + rr]; product (j, e) contracts channel 4 p + 16 j + e of
+  // lane group p
+  f32x4 av[2][8], an[2][8];
+  f32x4 bv[2], bn[2];
+  auto load = [&](uint32_t k, f32x4 (&x)[2][8], f32x4 (&y)[2]) {
+    const size_t m = ((size_t)(s0 + k) * a.H + h) * msz;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int r0 = 16 * (2 * wv + ti);
+      const float* Ar = a.seg_mats + per + m + (size_t)(r0 + rr) * kDK + 4 * p;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[ti][j] = *reinterpret_cast<const f32x4*>(Ar + 16 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[ti][e] = a.seg_mats[2 * per + m + (size_t)(r0 + 4 * p + e) * kDK + cb + rr];
+    }
+  };
+  load(1, av, bv);
+  for (uint32_t k = 1; k < ns; ++k) {
+    __syncthreads();  // S of step k is in LDS
+    if (k + 1 < ns) load(k + 1, an, bn);
+    f32x4 acc[2] = {bv[0], bv[1]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b = S[4 * p + 16 * j + e][rr];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) acc[ti] = mfma_f32(av[ti][j][e], b, acc[ti]);
+      }
+    __syncthreads();  // every read of S is done
+    float* dst = k + 1 < ns ? a.seg_mats + ((size_t)(s0 + k + 1) * a.H + h) * msz
+                            : (a.sT ? a.sT + (size_t)chain * msz : nullptr);
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * (2 * wv + ti) + 4 * p + e;
+        S[row][rr] = acc[ti][e];
+        if (dst) dst[(size_t)row * kDK + cb + rr] = acc[ti][e];
+      }
+    if (k + 1 < ns) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        bv[ti] = bn[ti];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[ti][j] = an[ti][j];
+      }
+    }
+  }
+}
+
+// Outputs of the later segments of a segment plan: O += Qt S_k, one unit of kSegGroup tokens
+// of one segment and head per pass of a workgroup. S_k^T is staged in LDS as the bf16 A
+// operands of its eight 16-column tiles; wavefront w takes 16-token blocks w, w + 4, ...,
+// with the queries as the B operand, so that each product is a tile of O^T. The fp32 sums
+// go through a wavefront-private LDS tile, and O is read and written as whole 256-byte
+// rows (16 bytes per lane). The next block's loads are issued before the current block's
+// products.
+constexpr int kCorrLd = kDK + 4;  // padded row (floats) of the correction tile
+__device__ __forceinline__ bf16x8 to_bf16x8_(const float (&x)[8]) {
+  return cat8(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
+}
+__global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
+  __shared__ bf16x8 sa[8][4][64];            // [column tile][32-channel slab][lane]
+  __shared__ float ct_[4][16][kCorrLd];      // per wavefront: 16 tokens x 128 columns
+  __shared__ uint32_t segbase[kMaxPlanSeqs + 1], corr_off[kMaxPlanSeqs + 1];
+  const uint32_t* plan = a.plan;
+  const uint32_t units = plan[3], slots = plan[2];
+  if (plan[1] == 0 || units == 0 || slots == 0 || slots > (uint32_t)a.seg_slots ||
+      slots > (uint32_t)kMaxPlanSeqs || a.N > kMaxPlanSeqs)
+    return;
+  for (int i = threadIdx.x; i <= a.N; i += 256) segbase[i] = plan[kSegHdr + i];
+  for (uint32_t i = threadIdx.x; i <= slots; i += 256) corr_off[i] = plan[segplan_corr_off(a.N) + i];
+  __syncthreads();
+  const int xt = (int)plan[1] * kC;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rr = lane & 15, p = lane >> 4;
+  const size_t msz = (size_t)kDK * kDK;
+  float (*cw)[kCorrLd] = ct_[wv];
+  for (uint32_t w = blockIdx.x; w < units * (uint32_t)a.H; w += gridDim.x) {
+    const int h = (int)(w % (uint32_t)a.H);
+    const uint32_t u = w / (uint32_t)a.H;
+    uint32_t lo = 0, hi = slots - 1;  // the last slot whose first unit is <= u
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      if (corr_off[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t sl = lo;
+    int nlo = 0, nhi = a.N - 1;  // the sequence of slot sl
+    while (nlo < nhi) {
+      const int mid = (nlo + nhi + 1) >> 1;
+      if (segbase[mid] <= sl) nlo = mid; else nhi = mid - 1;
+    }
+    const int n = nlo;
+    const int k = (int)(sl - segbase[n]);
+    const TokenRange tr = token_range(a.cu, n, a.T);
+    const int g0 = k * xt + (int)(u - corr_off[sl]) * kSegGroup;  // first token of the unit
+    const int seg_end = min((k + 1) * xt, tr.len);
+    if (k < 1 || g0 >= seg_end) continue;  // uniform over the workgroup
+    const int len = min(kSegGroup, seg_end - g0);
+    const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + g0;
+    const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.qt) + row0 * kDK, (uint32_t)len * kDK * 2);
+    const rsrc_t os = make_rsrc(static_cast<bf16*>(a.o) + row0 * kDK, (uint32_t)len * kDK * 2);
+    const float* S = a.seg_mats + ((size_t)sl * a.H + h) * msz;
+    __syncthreads();  // the previous unit's reads of sa are done
+    for (int i = threadIdx.x; i < 8 * 4 * 64; i += 256) {
+      const int ct = i >> 8, ks = (i >> 6) & 3, l = i & 63, r = l & 15, q = l >> 4;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = S[(size_t)(32 * ks + 8 * q + j) * kDK + 16 * ct + r];
+      sa[ct][ks][l] = cat8(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
+    }
+    __syncthreads();
+    // block b0: queries of token b0 + rr (B operands), O rows as 16-byte pieces
+    // (piece lane + 64 i: token b0 + piece / 16, columns 8 (piece % 16) ..)
+    bf16x8 qb[4], ob[4];
+    auto load = [&](int b0) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qb[ks] = __builtin_bit_cast(bf16x8, ld_b128(qs, (uint32_t)((b0 + rr) * kDK + 32 * ks + 8 * p) * 2));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = lane + 64 * i;
+        ob[i] = __builtin_bit_cast(bf16x8, ld_b128(os, (uint32_t)((b0 + (pc >> 4)) * kDK + 8 * (pc & 15)) * 2));
+      }
+    };
+    int b0 = 16 * wv;
+    if (b0 < len) load(b0);
+    for (; b0 < len; b0 += 64) {
+      bf16x8 q_[4], o_[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q_[i] = qb[i];
+        o_[i] = ob[i];
+      }
+      if (b0 + 64 < len) load(b0 + 64);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        f32x4 d = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) d = mfma32(sa[ct][ks][lane], q_[ks], d);
+        // d[e] = correction of token b0 + rr, column 16 ct + 4 p + e
+        *reinterpret_cast<f32x4*>(&cw[rr][16 * ct + 4 * p]) = d;
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = lane + 64 * i, t = pc >> 4, c8 = 8 * (pc & 15);
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(&cw[t][c8]);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(&cw[t][c8 + 4]);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = static_cast<float>(o_[i][e]) + c0[e];
+          y[4 + e] = static_cast<float>(o_[i][4 + e]) + c1[e];
+        }
+        st_b128(os, (uint32_t)((b0 + t) * kDK + c8) * 2, to_bf16x8_(y));
+      }
+      wave_lds_fence();  // the tile is rewritten by the next block
+    }
+  }
+}
+
 }  // namespace
 
 // Buffer descriptors address at most 2^31 bytes: a chain's g rows (T x dk fp32) must fit.
@@ -710,6 +1236,61 @@ size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus) {
   if (L == 0) return 0;
   // start states and end states (dk x dv) and transitions (dk x dk) of every segment, fp32
   return (size_t)N * H * P * ((size_t)2 * kDK * dv + (size_t)kDK * kDK) * 4;
+}
+
+// Segment plans: the shortest segment (64-token chunks), at least 512 tokens and at most 64
+// segments per T tokens, and the capacity in segments that covers every candidate length
+// of the planner for packed sequences (equal-length batches take only those that fit).
+static int segplan_xc_min(int T) {
+  const int ct = (T + kC - 1) / kC;
+  return std::max(8, (ct + 63) / 64);
+}
+static int segplan_slots(int N, int T) {
+  const int ct = (T + kC - 1) / kC;
+  return N + N / 8 + (ct + segplan_xc_min(T) - 1) / segplan_xc_min(T) + 1;
+}
+static size_t segplan_plan_bytes(int N, int H, int T) {
+  const int sm = segplan_slots(N, T);
+  return (4 * (segplan_items_off(N, sm) + 4 * (size_t)H * sm) + 255) / 256 * 256;
+}
+
+size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed) {
+  if (dv != kDK || N <= 0 || N > kMaxPlanSeqs || H <= 0) return 0;
+  const size_t sm = (size_t)segplan_slots(N, T);
+  return segplan_plan_bytes(N, H, T) + 3 * sm * H * kDK * kDK * 4 +
+         (packed ? (size_t)1 : (size_t)N) * H * T * kDK * 2;
+}
+
+hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, void* ws,
+                                     hipStream_t stream) {
+  ChunkArgs a = args;
+  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.dv != kDK || a.erase || !ws ||
+      a.N > kMaxPlanSeqs)
+    return hipErrorInvalidValue;
+  const int sm = segplan_slots(a.N, a.T);
+  a.plan = static_cast<uint32_t*>(ws);
+  a.seg_slots = sm;
+  a.seg_mats = reinterpret_cast<float*>(static_cast<char*>(ws) + segplan_plan_bytes(a.N, a.H, a.T));
+  a.qt = a.seg_mats + (size_t)3 * sm * a.H * kDK * kDK;
+  a.seg_len = 0;
+  a.nseg = 1;
+  a.split_all = 0;
+  chunk_segplan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, sm,
+                                                       segplan_xc_min(a.T), a.plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)(2 * (size_t)a.H * sm);  // the largest plan
+  if (per_channel)
+    chunk_mfma_kernel<4, 2, true, false, kModeSeg><<<grid, 64 * (kPrepWaves + 4), 0, stream>>>(a);
+  else
+    chunk_mfma_kernel<4, 2, false, false, kModeSeg><<<grid, 64 * (kPrepWaves + 4), 0, stream>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  seg_chain_kernel<<<dim3((unsigned)(a.N * a.H), kDK / 16), 256, 0, stream>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  seg_correct_kernel<<<dim3(1024), 256, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipStream_t stream) {

@@ -38,6 +38,12 @@ struct ChunkArgs {
   // most; seg_len = 0 for whole chains.
   int seg_len;
   int nseg;
+  // Segment plans (launch_chunk_mfma_segplan): capacity in segments, the start states,
+  // transitions and zero-start end states of the segments (fp32, seg_slots x H matrices
+  // each), and the carried-back queries (bf16, laid out as q).
+  int seg_slots;
+  float* seg_mats;
+  void* qt;
 };
 
 // Arguments of one kda_chunk_bwd call (shapes and validation as kda_chunk_fwd).
@@ -118,6 +124,11 @@ void chunk_seg_config(int N, int H, int T, int dv, int cus, int& seg_len, int& n
 size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus);
 hipError_t launch_chunk_mfma_segmented(const ChunkArgs& a, bool per_channel, void* ws,
                                        hipStream_t stream);
+// Segment plan of the forward (dv = dk = 128, KDA / Gated DeltaNet gates): its workspace
+// bytes (0 when not available) and the launches (planner, items, segment chain, corrections).
+size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed);
+hipError_t launch_chunk_mfma_segplan(const ChunkArgs& a, bool per_channel, void* ws,
+                                     hipStream_t stream);
 
 // Backward pass (bf16, dk = 128, dv in {64, 128}, one decay per channel or per head).
 bool chunk_bwd_supports(int dk, int dv, int T);

@@ -78,6 +78,7 @@ __device__ __forceinline__ f32x4 zero4() {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 
 // Raw buffer descriptor over `bytes` bytes from p (stride 0: offsets are byte offsets and
 // an access at or past `bytes` reads zero / writes nothing).
@@ -98,6 +99,9 @@ __device__ __forceinline__ bf16 ld_b16(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void st_b128(rsrc_t r, uint32_t off, bf16x8 x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void st_b64(rsrc_t r, uint32_t off, bf16x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, x), r, off, 0, 0);
 }
 
 // x from lane 4 (lane / 4) + E of this lane's quad (DPP quad permutation, no LDS access).

@@ -56,26 +56,40 @@ typedef enum {
 
 /*
  * Bytes of device workspace kda_chunk_fwd uses for this problem on the current device
- * (bf16 matrix-core path, dk = 128; every other case returns 0). Two uses:
+ * (bf16 matrix-core path, dk = 128; every other case returns 0). Three uses:
  *
- *  - Few chains for the device (N * H chains, two workgroups each at dv = 128, fewer than
- *    the compute units) and sequences of at least 1024 tokens: every sequence is cut into
- *    P segments of L tokens (P = CUs / (2 N H) or CUs / (N H) at dv = 64, L >= 512 a
- *    multiple of 64), and the state is passed between segments as an affine scan. Each
- *    segment but the last gets its end state from a zero start, B, and its transition, A,
- *    the dk x dk product of its token maps (the recurrence is affine in the state:
- *    S_end = A S_start + B); S_{s+1} = A_s S_s + B_s gives every start state; then all
- *    segments compute their outputs in parallel. Workspace: N H P (2 dk dv + dk^2) * 4
- *    bytes. Results equal the whole-chain computation up to rounding (the state crosses a
- *    segment boundary as A S + B instead of token by token). Not used by
+ *  - dv = dk = 128 with packed sequences (num_seqs in 1 .. 1024), or equal-length batches
+ *    with fewer chains (B * H) than compute units: the segment plan. A planning kernel
+ *    reads the sequence lengths on the device and picks a segment length X (a multiple of
+ *    64 tokens, at least max(512, 64 * ceil(T / 4096)) tokens) when cutting the longest
+ *    sequences lowers the launch's critical path; otherwise it builds the work list
+ *    described below. The first segment of a cut sequence runs from the initial state;
+ *    every later segment runs twice at the same time, from the zero state (outputs O0, end
+ *    state B) and from the identity (the dk x dk transition A of the segment, the product
+ *    of its token maps, and the queries carried back to the segment start, Qt). The
+ *    recurrence is linear in the state, so with S the segment's start state its outputs
+ *    are O0 + Qt S and its end state A S + B: a chain over the segments gives every S and a
+ *    correction pass adds Qt S. Results equal the whole-chain computation up to rounding.
+ *    With C = ceil(T / 64), Xmin = max(8, ceil(C / 64)) and
+ *    M = N + floor(N / 8) + ceil(C / Xmin) + 1 segments of capacity, the size is
+ *    R(4 (N + M + 10 + 4 H M)) + 3 M H dk^2 * 4 + Q H T dk * 2 bytes, where R rounds up
+ *    to a multiple of 256 and Q = 1 for packed sequences, B otherwise (the plan, the
+ *    states and transitions, and Qt laid out as q). kda_gdr2_chunk_fwd uses only the
+ *    work list at its start.
+ *  - Otherwise, few chains for the device (N * H chains, two workgroups each at dv = 128,
+ *    fewer than the compute units) and sequences of at least 1024 tokens: every sequence
+ *    is cut into P segments of L tokens (P = CUs / (2 N H) or CUs / (N H) at dv = 64,
+ *    L >= 512 a multiple of 64); each segment but the last gets B and A as above,
+ *    S_{s+1} = A_s S_s + B_s gives every start state, then all segments compute their
+ *    outputs in parallel. Workspace: N H P (2 dk dv + dk^2) * 4 bytes. Not used by
  *    kda_gdr2_chunk_fwd.
  *  - Otherwise, packed sequences (num_seqs > 0, at most 1024): a work list of
  *    4 * (1 + 2 * num_seqs * H) bytes rounded up to 256, filled on the device by a small
  *    scheduling kernel: it splits the value columns of the longest sequences' chains over
  *    two workgroups and orders the work longest first, so that packed sequences of unequal
- *    length keep every compute unit busy. These results do not depend on the schedule bit
- *    for bit: each value column is computed the same way. (Equal-length batches with
- *    enough chains need no workspace: their split is decided on the host.)
+ *    length keep every compute unit busy. Work lists do not change results bit for bit:
+ *    each value column is computed the same way. (Equal-length batches with enough chains
+ *    need no workspace: their split is decided on the host.)
  */
 size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
                                     kda_dtype dt);

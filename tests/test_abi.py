@@ -40,21 +40,37 @@ def test_status_strings():
     assert "UNKNOWN" in kda.kda_status_string(99)
 
 
+def segment_plan_bytes(B, H, T, N, packed, dk=128):
+    """The segment plan's workspace as kda.h states it: plan words, the states and
+    transitions of M segments per head, and the carried-back queries laid out as q."""
+    C = -(-T // 64)
+    xmin = max(8, -(-C // 64))
+    M = N + N // 8 + -(-C // xmin) + 1
+    plan = -(-4 * (N + M + 10 + 4 * H * M) // 256) * 256
+    return plan + 3 * M * H * dk * dk * 4 + (1 if packed else B) * H * T * dk * 2
+
+
 def test_workspace_size():
     # (sizes for a 256-CU device; without a GPU the library assumes 256 compute units)
-    # enough chains for the device: a work list of 1 + 2 N H words (rounded up to 256 bytes)
-    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == 2304
-    # few chains: segments; per segment two dk x dv states and one dk x dk transition (fp32)
-    # 2 sequences x 16 heads, dv = 64: 8 segments of 512 tokens
+    # dv = dk, packed sequences: the segment plan
+    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == \
+        segment_plan_bytes(1, 32, 65536, 8, True) == 1002477056
+    assert kda.kda_chunk_fwd_workspace_size(1, 4, 5000, 128, 128, 7, kda.KDA_BF16) == \
+        segment_plan_bytes(1, 4, 5000, 7, True)
+    # dv = dk, equal lengths with fewer chains than compute units: the segment plan
+    assert kda.kda_chunk_fwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_BF16) == \
+        segment_plan_bytes(2, 16, 4096, 2, False)
+    assert kda.kda_chunk_fwd_workspace_size(1, 2, 1000, 128, 128, 0, kda.KDA_BF16) == \
+        segment_plan_bytes(1, 2, 1000, 1, False)
+    # dv = 64, few chains: segments; per segment two dk x dv states and one dk x dk
+    # transition (fp32); 2 sequences x 16 heads: 8 segments of 512 tokens
     assert kda.kda_chunk_fwd_workspace_size(1, 16, 4096, 128, 64, 2, kda.KDA_BF16) == \
         32 * 8 * (2 * 128 * 64 + 128 * 128) * 4
-    # 2 x 16 equal-length chains, dv = 128 (two workgroups per segment): 4 segments
-    assert kda.kda_chunk_fwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_BF16) == \
-        32 * 4 * (2 * 128 * 128 + 128 * 128) * 4
+    # dv = 64, packed sequences with enough chains: a work list of 1 + 2 N H words
+    # (rounded up to 256 bytes)
+    assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 64, 8, kda.KDA_BF16) == 2304
     # equal lengths with enough chains: scheduled on the host, no workspace
     assert kda.kda_chunk_fwd_workspace_size(8, 32, 4096, 128, 128, 0, kda.KDA_BF16) == 0
-    # segments are at least 512 tokens: a short sequence is never cut
-    assert kda.kda_chunk_fwd_workspace_size(1, 2, 1000, 128, 128, 0, kda.KDA_BF16) == 0
     # no schedule: fp32, dk = 64, more than 1024 sequences, invalid sizes
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_F32) == 0
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 64, 128, 8, kda.KDA_BF16) == 0
