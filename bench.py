@@ -42,17 +42,19 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 CHUNK = 64
 
-# HBM traffic of the chunk kernel per launch, from two rocprofv3 --pmc runs (FETCH_SIZE,
-# WRITE_SIZE, KiB per dispatch) each scaled by the counter/byte ratio measured on a
-# plain 1 GiB copy kernel in the same runs. It is reported only while the kernel source
-# is the one the counters were taken on (its SHA-256 below); otherwise traffic is null.
+# HBM traffic of one chunk-forward call (for the packed KDA workload: the segment planner,
+# the items, the segment chain and the output corrections; for Gated Delta Rule-2 the one
+# chunk launch), from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch)
+# each scaled by the counter/byte ratio measured on a plain 1 GiB copy kernel in the same
+# runs. It is reported only while the kernel source is the one the counters were taken on
+# (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3247121264,
-    "kernel_sha256": "00bae921076522de8f1dc0e6eb723be29e1a0a92c81ba241d2ce8b93bb2c27fe",
+    "bytes": 3697867624,
+    "kernel_sha256": "c0708e11a60dd076e46078f201ca4a0afbe0dff99f891478fe9783938ad15f0f",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5386412111,
-    "kernel_sha256": "00bae921076522de8f1dc0e6eb723be29e1a0a92c81ba241d2ce8b93bb2c27fe",
+    "bytes": 5386446112,
+    "kernel_sha256": "c0708e11a60dd076e46078f201ca4a0afbe0dff99f891478fe9783938ad15f0f",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,
@@ -415,7 +417,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
-                     "kernel": "kda chunk forward (fused)",
+                     "kernel": "kda chunk forward (segment plan: planner, items, segment chain, corrections)",
                      "alg_bytes_per_launch": alg_bytes},
         "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
