@@ -184,13 +184,18 @@ SEG_CASES = [  # (name, lens or None for equal lengths, B, H, T, dv, gate)
     ("varlen_dv128", [3000, 90, 700, 0, 1300, 33, 64], 1, 4, None, 128, "channel"),
     ("varlen_dv64_head", [2500, 513, 511, 1700], 1, 3, None, 64, "head"),
     ("equal_b2_h2", None, 2, 2, 2100, 128, "channel"),
+    # one chain: about twenty segments, a chain of that many steps and many correction units
+    ("one_long_h1", [20000], 1, 1, None, 128, "channel"),
+    # one decay per head; sequences of 1 and 0 tokens among cut ones
+    ("varlen_head_gate", [5000, 4000, 64, 1, 0, 2500], 1, 2, None, 128, "head"),
 ]
 
 
 @pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: c[0])
 def test_segmented_matches_oracle_and_whole_chains(case):
-    """Few chains for the device: each chain is cut into segments, the segments' end states
-    and transitions are combined, and every segment restarts from its exact start state.
+    """Few chains for the device: long sequences are cut into segments. dv = 128: the later
+    segments run from the zero state and as transitions, the start states are chained and
+    the outputs corrected; dv = 64: every segment is re-run from its exact start state.
     Outputs and final states match the oracle, and the whole-chain run to rounding."""
     name, lens, B, H, T, dv, gate = case
     if lens is not None:
@@ -214,3 +219,27 @@ def test_segmented_matches_oracle_and_whole_chains(case):
     check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], f"segmented {name}")
     assert_close(o1, o0, TOL["bf16"], f"{name}: segmented vs whole outputs")
     assert_close(s1, s0, TOL["bf16"], f"{name}: segmented vs whole states")
+
+
+def test_segmented_without_initial_or_final_state():
+    """The segment plan with no initial state (the first segment starts from zero) and no
+    final state requested (the segment chain writes none): outputs match the oracle."""
+    lens = [6000, 2500, 700]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=31)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = None
+    note("segmented chunk without initial / final state")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+               for a in (x.q, x.k, x.v))
+    g, beta = (torch.from_numpy(np.ascontiguousarray(a)).to("cuda") for a in (x.g, x.beta))
+    o, sT = kda.chunk_fwd(q, k, v, g, beta, cu_seqlens=torch.from_numpy(cu).to("cuda"),
+                          output_final_state=False)
+    torch.cuda.synchronize()
+    assert sT is None
+    ref = oracle_chains(x, initial_state=False)
+    on = o.float().cpu().numpy()
+    got = [on[b, h, t0:t0 + ln] for (n, h) in ref for (b, t0, ln) in [x.chain_rows(n, h)]]
+    assert_close(np.concatenate(got), np.concatenate([ro for ro, _ in ref.values()]),
+                 TOL["bf16"], "segmented, no states: outputs")
