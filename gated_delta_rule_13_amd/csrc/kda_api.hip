@@ -105,7 +105,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   hipError_t err;
   if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T)) {
     const size_t sp = kda::chunk_segplan_bytes(a.N, H, T, dv, cu_seqlens != nullptr);
-    if (scheduled && !erase && sp > 0 && workspace_bytes >= sp)
+    if (scheduled && sp > 0 && workspace_bytes >= sp)
       err = kda::launch_chunk_mfma_segplan(a, per_channel, workspace, stream);
     else if (scheduled && !erase && kda::chunk_seg_bytes(a.N, H, T, dv, a.cus) > 0)
       err = kda::launch_chunk_mfma_segmented(a, per_channel, workspace, stream);

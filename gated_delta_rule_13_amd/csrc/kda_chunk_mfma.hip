@@ -1264,8 +1264,7 @@ size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed) {
 hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, void* ws,
                                      hipStream_t stream) {
   ChunkArgs a = args;
-  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.dv != kDK || a.erase || !ws ||
-      a.N > kMaxPlanSeqs)
+  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.dv != kDK || !ws || a.N > kMaxPlanSeqs)
     return hipErrorInvalidValue;
   const int sm = segplan_slots(a.N, a.T);
   a.plan = static_cast<uint32_t*>(ws);
@@ -1280,10 +1279,14 @@ hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, vo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(2 * (size_t)a.H * sm);  // the largest plan
-  if (per_channel)
-    chunk_mfma_kernel<4, 2, true, false, kModeSeg><<<grid, 64 * (kPrepWaves + 4), 0, stream>>>(a);
-  else
-    chunk_mfma_kernel<4, 2, false, false, kModeSeg><<<grid, 64 * (kPrepWaves + 4), 0, stream>>>(a);
+  const dim3 block(64 * (kPrepWaves + 4));
+  if (a.erase) {  // Gated Delta Rule-2 gates
+    if (per_channel) chunk_mfma_kernel<4, 2, true, true, kModeSeg><<<grid, block, 0, stream>>>(a);
+    else chunk_mfma_kernel<4, 2, false, true, kModeSeg><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (per_channel) chunk_mfma_kernel<4, 2, true, false, kModeSeg><<<grid, block, 0, stream>>>(a);
+    else chunk_mfma_kernel<4, 2, false, false, kModeSeg><<<grid, block, 0, stream>>>(a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   seg_chain_kernel<<<dim3((unsigned)(a.N * a.H), kDK / 16), 256, 0, stream>>>(a);

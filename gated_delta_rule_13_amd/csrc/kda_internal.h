@@ -124,7 +124,7 @@ void chunk_seg_config(int N, int H, int T, int dv, int cus, int& seg_len, int& n
 size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus);
 hipError_t launch_chunk_mfma_segmented(const ChunkArgs& a, bool per_channel, void* ws,
                                        hipStream_t stream);
-// Segment plan of the forward (dv = dk = 128, KDA / Gated DeltaNet gates): its workspace
+// Segment plan of the forward (dv = dk = 128, any gates): its workspace
 // bytes (0 when not available) and the launches (planner, items, segment chain, corrections).
 size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed);
 hipError_t launch_chunk_mfma_segplan(const ChunkArgs& a, bool per_channel, void* ws,

@@ -74,8 +74,8 @@ typedef enum {
  *    M = N + floor(N / 8) + ceil(C / Xmin) + 1 segments of capacity, the size is
  *    R(4 (N + M + 10 + 4 H M)) + 3 M H dk^2 * 4 + Q H T dk * 2 bytes, where R rounds up
  *    to a multiple of 256 and Q = 1 for packed sequences, B otherwise (the plan, the
- *    states and transitions, and Qt laid out as q). kda_gdr2_chunk_fwd uses only the
- *    work list at its start.
+ *    states and transitions, and Qt laid out as q). kda_gdr2_chunk_fwd takes the same
+ *    plan (its recurrence is linear in the state too).
  *  - Otherwise, few chains for the device (N * H chains, two workgroups each at dv = 128,
  *    fewer than the compute units) and sequences of at least 1024 tokens: every sequence
  *    is cut into P segments of L tokens (P = CUs / (2 N H) or CUs / (N H) at dv = 64,

@@ -58,6 +58,26 @@ def test_gdr2_varlen_t65536_sampled_chains():
     print(f"{cfg.name}: sampled {len(chains)} chains, err o={eo:.2e} S={es:.2e}")
 
 
+def test_gdr2_segmented_matches_oracle_and_whole_chains():
+    """Few chains for the device: the segment plan cuts the long sequences; the later
+    segments run from the zero state and as transitions (zero values, so the write gate
+    leaves them untouched) and their outputs are corrected."""
+    lens = [5000, 3000, 800, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=57,
+                             gates="gdr2")
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(5).standard_normal((len(lens), 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    note("gdr2 segmented")
+    o1, s1 = run_chunk(x, "bf16", schedule=True)
+    o0, s0 = run_chunk(x, "bf16", schedule=False)
+    check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], "gdr2 segmented")
+    assert_close(o1, o0, TOL["bf16"], "gdr2 segmented vs whole outputs")
+    assert_close(s1, s0, TOL["bf16"], "gdr2 segmented vs whole states")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_gdr2_varlen_edge_lengths(dtype):
     lens = [0, 1, 63, 64, 65, 130, 7]
