@@ -34,6 +34,8 @@
 // accumulators, run the carry of the current 64 tokens; one barrier per 64 tokens.
 #include <stddef.h>
 
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -812,9 +814,10 @@ size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed) {
   return (size_t)H * tokens * (kDK / 16) * 2 * (size_t)dv;  // hist_chain_offset's layout
 }
 
+namespace {
+
 template <bool GDR2>
-hipError_t launch_bwd_kernels(BwdArgs& b, bool per_channel, unsigned chains, int slots,
-                              hipStream_t stream) {
+hipError_t launch_carry(BwdArgs& b, bool per_channel, unsigned chains, hipStream_t stream) {
   const ChunkArgs& a = b.f;
   const unsigned threads = 64 * (kPrepWaves + 4);
   if (a.dv == 128) {
@@ -824,8 +827,12 @@ hipError_t launch_bwd_kernels(BwdArgs& b, bool per_channel, unsigned chains, int
     if (per_channel) chunk_bwd_state_kernel<4, 1, true, GDR2><<<chains, threads, 0, stream>>>(b);
     else chunk_bwd_state_kernel<4, 1, false, GDR2><<<chains, threads, 0, stream>>>(b);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <bool GDR2>
+hipError_t launch_grad(BwdArgs& b, bool per_channel, int slots, hipStream_t stream) {
+  const ChunkArgs& a = b.f;
   const unsigned grid = (unsigned)slots * a.H;
   if (a.dv == 128) {
     if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, 64, 0, stream>>>(b, slots);
@@ -837,20 +844,31 @@ hipError_t launch_bwd_kernels(BwdArgs& b, bool per_channel, unsigned chains, int
   return hipGetLastError();
 }
 
+// A second stream per device (default priority, created once) for the state history, which
+// runs at the same time as the reverse carry: the carry does not read the states.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev] && hipStreamCreateWithFlags(&cache[dev], hipStreamNonBlocking) != hipSuccess)
+    cache[dev] = nullptr;
+  return cache[dev];
+}
+
+}  // namespace
+
 hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t stream) {
   BwdArgs b = args;
   ChunkArgs& a = b.f;
   if (!chunk_bwd_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
-  // 1. states at every block start (builds the work list of packed sequences)
-  a.hist = b.hist_s;
   a.sT = nullptr;
   a.plan = a.cu ? b.plan : nullptr;
-  hipError_t e = launch_chunk_mfma_hist(a, per_channel, stream);
-  if (e != hipSuccess) return e;
-  a.hist = nullptr;
-  // 2. the carry, over the same work list (or every chain split when all halves fit), and
-  // 3. the gradients of every block
   b.plan = a.plan;
+  // the work list of packed sequences, shared by the history and the carry
+  hipError_t e = launch_chunk_plan(a, stream);
+  if (e != hipSuccess) return e;
   const bool can_split = a.dv == 128;
   unsigned chains = (unsigned)a.N * a.H;
   a.split_all = 0;
@@ -861,8 +879,34 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
     chains *= 2;
   }
   const int slots = a.cu ? a.T / 16 + a.N + 1 : a.N * ((a.T + 15) / 16);
-  return a.erase ? launch_bwd_kernels<true>(b, per_channel, chains, slots, stream)
-                 : launch_bwd_kernels<false>(b, per_channel, chains, slots, stream);
+  // 1. the states at every block start, on the side stream, and 2. the carry, recording dS'
+  // of every block; then 3. the gradients of every block, after both
+  ChunkArgs h = b.f;
+  h.hist = b.hist_s;
+  h.split_all = 0;  // the history launch decides its own split
+  hipStream_t side = side_stream();
+  hipEvent_t forked = nullptr, joined = nullptr;
+  if (side && (hipEventCreateWithFlags(&forked, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&joined, hipEventDisableTiming) != hipSuccess))
+    side = nullptr;
+  if (side) {
+    if ((e = hipEventRecord(forked, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side, forked, 0)) != hipSuccess) return e;
+  }
+  e = launch_chunk_mfma_hist(h, per_channel, side ? side : stream, false);
+  if (e == hipSuccess)
+    e = a.erase ? launch_carry<true>(b, per_channel, chains, stream)
+                : launch_carry<false>(b, per_channel, chains, stream);
+  if (side) {
+    hipError_t e2 = hipEventRecord(joined, side);
+    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, joined, 0);
+    hipEventDestroy(forked);
+    hipEventDestroy(joined);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return e;
+  return a.erase ? launch_grad<true>(b, per_channel, slots, stream)
+                 : launch_grad<false>(b, per_channel, slots, stream);
 }
 
 }  // namespace kda

@@ -946,7 +946,8 @@ hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
 // value columns split over two workgroups when every half fits on the device at once, or
 // the work list of packed sequences (built here) when a.plan is set.
 template <int MODE>
-hipError_t launch_mode(const ChunkArgs& args, bool per_channel, int dv, hipStream_t stream) {
+hipError_t launch_mode(const ChunkArgs& args, bool per_channel, int dv, hipStream_t stream,
+                       bool build_plan = true) {
   ChunkArgs a = args;
   const bool can_split = dv == 128;  // a half of dv = 128 is one 16-column tile per wavefront
   const long long items =
@@ -955,10 +956,12 @@ hipError_t launch_mode(const ChunkArgs& args, bool per_channel, int dv, hipStrea
   a.split_all = 0;
   if (a.plan && a.cu && a.seg_len == 0) {
     // packed sequences: the work list is built on the device from cu_seqlens
-    chunk_plan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, can_split,
-                                                      a.plan);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (build_plan) {
+      chunk_plan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, can_split,
+                                                        a.plan);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     if (can_split) grid *= 2;  // the largest schedule; workgroups past its length exit at once
   } else {
     a.plan = nullptr;
@@ -1296,12 +1299,20 @@ hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, vo
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipStream_t stream) {
+hipError_t launch_chunk_plan(const ChunkArgs& a, hipStream_t stream) {
+  if (!a.plan || !a.cu) return hipSuccess;  // equal-length batches need no work list
+  chunk_plan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, a.dv == 128,
+                                                    a.plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_mfma_hist(const ChunkArgs& args, bool per_channel, hipStream_t stream,
+                                  bool build_plan) {
   ChunkArgs a = args;
   if (!a.hist || !chunk_mfma_supports(a.dk, a.dv, a.T)) return hipErrorInvalidValue;
   a.o = nullptr;
   a.seg_len = 0;
-  return launch_mode<kModeHist>(a, per_channel, a.dv, stream);  // builds the work list
+  return launch_mode<kModeHist>(a, per_channel, a.dv, stream, build_plan);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& args, bool per_channel, hipStream_t stream) {

@@ -135,7 +135,10 @@ bool chunk_bwd_supports(int dk, int dv, int T);
 // Bytes of one of the two state histories of the backward pass.
 size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed);
 // Forward state pass that records the history (kda_chunk_mfma.hip).
-hipError_t launch_chunk_mfma_hist(const ChunkArgs& a, bool per_channel, hipStream_t stream);
+hipError_t launch_chunk_mfma_hist(const ChunkArgs& a, bool per_channel, hipStream_t stream,
+                                  bool build_plan = true);
+// The work list of packed sequences alone (a.plan, a.cu set), as the launches above build it.
+hipError_t launch_chunk_plan(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool per_channel, hipStream_t stream);
 
 }  // namespace kda
