@@ -872,9 +872,7 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
   const bool can_split = a.dv == 128;
   unsigned chains = (unsigned)a.N * a.H;
   a.split_all = 0;
-  if (can_split && b.plan) {
-    chains *= 2;
-  } else if (can_split && a.cus > 0 && 2ll * a.N * a.H <= a.cus) {
+  if (!b.plan && can_split && a.cus > 0 && 2ll * a.N * a.H <= a.cus) {
     a.split_all = 1;
     chains *= 2;
   }

@@ -137,7 +137,8 @@ size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed);
 // Forward state pass that records the history (kda_chunk_mfma.hip).
 hipError_t launch_chunk_mfma_hist(const ChunkArgs& a, bool per_channel, hipStream_t stream,
                                   bool build_plan = true);
-// The work list of packed sequences alone (a.plan, a.cu set), as the launches above build it.
+// The work list of packed sequences for the backward's chain passes (whole chains, longest
+// first; a.plan, a.cu set).
 hipError_t launch_chunk_plan(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool per_channel, hipStream_t stream);
 
