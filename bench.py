@@ -49,12 +49,12 @@ CHUNK = 64
 # runs. It is reported only while the kernel source is the one the counters were taken on
 # (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3697867624,
-    "kernel_sha256": "c0708e11a60dd076e46078f201ca4a0afbe0dff99f891478fe9783938ad15f0f",
+    "bytes": 3700158839,
+    "kernel_sha256": "f7462983eeaf7d00b1c3fe63be99e14e3269313b33e5708064e7e56fff0ca5e7",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5386446112,
-    "kernel_sha256": "c0708e11a60dd076e46078f201ca4a0afbe0dff99f891478fe9783938ad15f0f",
+    "bytes": 5957684230,
+    "kernel_sha256": "f7462983eeaf7d00b1c3fe63be99e14e3269313b33e5708064e7e56fff0ca5e7",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,
