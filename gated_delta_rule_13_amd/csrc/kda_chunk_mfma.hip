@@ -1038,9 +1038,10 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(ChunkArgs a) {
   for (int i = threadIdx.x; i < kDK * 16; i += 256) S[i >> 4][i & 15] = first[(size_t)(i >> 4) * kDK + cb + (i & 15)];
   // operands of step k: A[16 (2 wv + ti) + rr][4 p + 16 j .. + 3] (16-byte loads) and
   // B[16 (2 wv + ti) + 4 p + e][cb + rr]; product (j, e) contracts channel 4 p + 16 j + e of
-  // lane group p
-  f32x4 av[2][8], an[2][8];
-  f32x4 bv[2], bn[2];
+  // lane group p. Three steps' operands are in flight (a ring of three register buffers),
+  // so that a step waits for loads issued three steps earlier.
+  f32x4 a0[2][8], a1[2][8], a2[2][8];
+  f32x4 b0[2], b1[2], b2[2];
   auto load = [&](uint32_t k, f32x4 (&x)[2][8], f32x4 (&y)[2]) {
     const size_t m = ((size_t)(s0 + k) * a.H + h) * msz;
 #pragma unroll
@@ -1053,18 +1054,16 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) y[ti][e] = a.seg_mats[2 * per + m + (size_t)(r0 + 4 * p + e) * kDK + cb + rr];
     }
   };
-  load(1, av, bv);
-  for (uint32_t k = 1; k < ns; ++k) {
+  auto step = [&](uint32_t k, const f32x4 (&x)[2][8], const f32x4 (&y)[2]) {
     __syncthreads();  // S of step k is in LDS
-    if (k + 1 < ns) load(k + 1, an, bn);
-    f32x4 acc[2] = {bv[0], bv[1]};
+    f32x4 acc[2] = {y[0], y[1]};
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float b = S[4 * p + 16 * j + e][rr];
+        const float bs = S[4 * p + 16 * j + e][rr];
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) acc[ti] = mfma_f32(av[ti][j][e], b, acc[ti]);
+        for (int ti = 0; ti < 2; ++ti) acc[ti] = mfma_f32(x[ti][j][e], bs, acc[ti]);
       }
     __syncthreads();  // every read of S is done
     float* dst = k + 1 < ns ? a.seg_mats + ((size_t)(s0 + k + 1) * a.H + h) * msz
@@ -1077,13 +1076,20 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(ChunkArgs a) {
         S[row][rr] = acc[ti][e];
         if (dst) dst[(size_t)row * kDK + cb + rr] = acc[ti][e];
       }
+  };
+  load(1, a0, b0);
+  if (2 < ns) load(2, a1, b1);
+  if (3 < ns) load(3, a2, b2);
+  for (uint32_t k = 1; k < ns; k += 3) {
+    step(k, a0, b0);
+    if (k + 3 < ns) load(k + 3, a0, b0);
     if (k + 1 < ns) {
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-        bv[ti] = bn[ti];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) av[ti][j] = an[ti][j];
-      }
+      step(k + 1, a1, b1);
+      if (k + 4 < ns) load(k + 4, a1, b1);
+    }
+    if (k + 2 < ns) {
+      step(k + 2, a2, b2);
+      if (k + 5 < ns) load(k + 5, a2, b2);
     }
   }
 }
