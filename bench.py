@@ -345,11 +345,33 @@ def cpu_baseline(x, max_chains: int):
     t0 = time.perf_counter()
     oracle.kda_chains(*cargs, **ckw, threads=threads)
     dt = time.perf_counter() - t0
+    # the same recurrence on one thread, over the 8 sampled chains of one head
+    one = [(n, 0) for n in range(x.n_seqs)]
+    one_tokens = sum(x.chain_rows(n, h)[2] for (n, h) in one)
+    _, oargs, okw = oracle.pack_chains(x.q, x.k, x.v, x.g, x.beta, x.s0, x.cu_seqlens, one)
+    t1 = time.perf_counter()
+    oracle.kda_chains(*oargs, **okw, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": head_tokens / H / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{len(chains)} of {len(all_chains)} (sequence, head) chains of the "
                       f"workload, all their tokens ({head_tokens} head-tokens), fp64 token "
-                      f"recurrence, {dt:.1f} s"}
+                      f"recurrence, {dt:.1f} s",
+            "cpu_model": cpu_model(),
+            "one_thread": {"value": one_tokens / H / dt1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"the {len(one)} chains of head 0 ({one_tokens} "
+                                     f"head-tokens), {dt1:.1f} s"}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_probe(torch):
