@@ -324,7 +324,24 @@ def bench_decode(torch, kda, cfg, reps: int = 5):
         ev1.record(stream)
         torch.cuda.synchronize()
         times.append(ev0.elapsed_time(ev1) / 1e3)
-    return statistics.median(times)
+    # the same steps captured once in a HIP graph and replayed (state re-initialised outside)
+    g = torch.cuda.CUDAGraph()
+    state.copy_(s_init)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for s in range(S):
+            step(s)
+    gtimes = []
+    for _ in range(reps):
+        state.copy_(s_init)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        gtimes.append(ev0.elapsed_time(ev1) / 1e3)
+    return statistics.median(times), statistics.median(gtimes)
 
 
 def cpu_baseline(x, max_chains: int):
@@ -446,13 +463,14 @@ def main() -> int:
     }
     if not args.no_decode:
         dcfg = CONFIGS[4]
-        sec = bench_decode(torch, kda, dcfg)
+        sec, gsec = bench_decode(torch, kda, dcfg)
         per_step = decode_alg_bytes_per_step(dcfg.B, dcfg.H, dcfg.dk, dcfg.dv)
         dgbs = per_step * dcfg.T / sec / 1e9
         result["decode"] = {
             "workload": dcfg.name, "steps": dcfg.T, "us_per_step": sec / dcfg.T * 1e6,
             "tokens_per_s": dcfg.B * dcfg.T / sec, "hbm_gbs": dgbs,
-            "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
+            "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step,
+            "graph_us_per_step": gsec / dcfg.T * 1e6}
         log(f"decode: {sec / dcfg.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
     if not args.no_gdr2:
         # Gated Delta Rule-2 on the same workloads: vector erase / write gates
@@ -478,7 +496,7 @@ def main() -> int:
         del gx
         if not args.no_decode:
             gd = CONFIGS[4].replace(name="gdr2_decode_n256_h32", T=64, gates="gdr2")
-            sec = bench_decode(torch, kda, gd)
+            sec, _ = bench_decode(torch, kda, gd)
             per_step = decode_alg_bytes_per_step(gd.B, gd.H, gd.dk, gd.dv, gdr2=True)
             dgbs = per_step * gd.T / sec / 1e9
             result["gdr2"]["decode"] = {

@@ -93,3 +93,39 @@ def test_steps_equal_chunk_forward(dtype):
     tol = TOL[dtype]
     assert_close(o_steps, o_chunk.float().cpu().numpy(), tol, "steps vs chunk outputs")
     assert_close(state.cpu().numpy(), s_chunk.cpu().numpy(), tol, "steps vs chunk states")
+
+
+def test_decode_steps_in_a_replayed_graph():
+    """Eight decode steps captured once in a HIP graph and replayed three times, with eager
+    work and synchronisations between the replays: every replay gives the eager outputs
+    and final state bit for bit."""
+    cfg = CONFIGS[4].replace(B=16, H=4, T=8, seed=61)
+    note("decode steps in a HIP graph")
+    N, H, T = cfg.B, cfg.H, cfg.T
+    S0 = up(decode_initial_state(cfg))
+    steps = [decode_step_inputs(cfg, s) for s in range(T)]
+    ins = [(up(d.q, torch.bfloat16), up(d.k, torch.bfloat16), up(d.v, torch.bfloat16),
+            up(d.g), up(d.beta)) for d in steps]
+    outs = [torch.empty((N, H, cfg.dv), dtype=torch.bfloat16, device=S0.device) for _ in range(T)]
+    state = S0.clone()
+    for s in range(T):
+        kda.recurrent_step(*ins[s], state, o=outs[s])
+    torch.cuda.synchronize()
+    want_o = [o.clone() for o in outs]
+    want_s = state.clone()
+    state.copy_(S0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(T):
+            kda.recurrent_step(*ins[s], state, o=outs[s])
+    for rep in range(3):
+        state.copy_(S0)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(T):
+            assert torch.equal(outs[s], want_o[s]), f"replay {rep}, step {s}: outputs differ"
+        assert torch.equal(state, want_s), f"replay {rep}: final state differs"
