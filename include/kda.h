@@ -16,9 +16,14 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers (HBM of the current HIP device), the
  *    tensors are contiguous and head-major: [B, H, T, d] for per-token data.
- *  - The caller owns every buffer. The library allocates no memory, keeps no global
- *    state, never synchronises, and enqueues all work on `stream` (NULL = the null
- *    stream). Calls are asynchronous: a KDA_OK return means "enqueued".
+ *  - The caller owns every buffer. The library allocates no device memory and never
+ *    synchronises the host; work is enqueued on `stream` (NULL = the null stream), and
+ *    calls are asynchronous: a KDA_OK return means "enqueued". Its only global state is a
+ *    per-device cache of the compute-unit count and, from the first kda_chunk_bwd /
+ *    kda_gdr2_chunk_bwd call on a device, one more stream of that device (default
+ *    priority, kept until the process ends): the backward forks part of its work onto it
+ *    with an event recorded on `stream` and joins it back before returning, so all of a
+ *    call's work still completes in `stream` order.
  *  - Argument errors are detected on the host before anything is launched and are
  *    returned as a status; no exception crosses the ABI. A failed launch returns
  *    KDA_ERR_HIP.
