@@ -138,6 +138,34 @@ def test_split_resume_and_aliasing():
     assert_close(state.cpu().numpy(), s_full.cpu().numpy(), 1e-2, "split state")
 
 
+def test_split_resume_and_aliasing_segmented():
+    """The same with one long chain, so that every call is cut into segments: the first
+    segment reads the initial state and the segment chain writes the final state into the
+    same buffer; outputs and states match the one-call run and the oracle."""
+    import gated_delta_rule_13_amd as kda
+    cfg = CONFIGS[1].replace(B=1, H=1, T=5000, seed=22, random_s0=True)
+    x = make_chunk_inputs(cfg)
+    dt = torch.bfloat16
+    q, k, v, g, beta, s0 = (up(x.q, dt), up(x.k, dt), up(x.v, dt), up(x.g), up(x.beta),
+                            up(x.s0))
+    note("chunk split/resume, segmented")
+    o_full, s_full = kda.chunk_fwd(q, k, v, g, beta, initial_state=s0)
+    T1 = 2100
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()  # noqa: E731
+    state = s0.clone()
+    o1, _ = kda.chunk_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1),
+                          sl(beta, 0, T1), initial_state=state, final_state=state)
+    o2, _ = kda.chunk_fwd(sl(q, T1, 5000), sl(k, T1, 5000), sl(v, T1, 5000),
+                          sl(g, T1, 5000), sl(beta, T1, 5000), initial_state=state,
+                          final_state=state)
+    torch.cuda.synchronize()
+    o_split = torch.cat([o1, o2], dim=2).float().cpu().numpy()
+    assert_close(o_split, o_full.float().cpu().numpy(), 1e-2, "split outputs")
+    assert_close(state.cpu().numpy(), s_full.cpu().numpy(), 1e-2, "split state")
+    check_chains(x, o_split, state.cpu().numpy(), oracle_chains(x), TOL["bf16"],
+                 "split, segmented")
+
+
 def test_deterministic():
     cfg = CONFIGS[1].replace(B=2, H=4, T=1000, seed=8)
     x = make_chunk_inputs(cfg)
