@@ -273,3 +273,36 @@ def test_segmented_without_initial_or_final_state():
     got = [on[b, h, t0:t0 + ln] for (n, h) in ref for (b, t0, ln) in [x.chain_rows(n, h)]]
     assert_close(np.concatenate(got), np.concatenate([ro for ro, _ in ref.values()]),
                  TOL["bf16"], "segmented, no states: outputs")
+
+
+RANDOM_SHAPES = list(range(12))
+
+
+@pytest.mark.parametrize("case", RANDOM_SHAPES)
+def test_random_packed_shapes(case):
+    """Seeded random packed batches (1 to 12 sequences of 0 to 6000 tokens, 1 to 8 heads,
+    dv 64 or 128, per-channel or per-head decay, KDA or Gated Delta Rule-2 gates, with or
+    without an initial state) through the scheduled path: whatever the planner picks
+    (halves, segments, or neither), every chain matches the oracle."""
+    rng = np.random.default_rng(1000 + case)
+    n = int(rng.integers(1, 13))
+    lens = [int(v) for v in rng.integers(0, 6001, size=n)]
+    if sum(lens) == 0:
+        lens[0] = 1
+    H = int(rng.choice([1, 2, 3, 5, 8]))
+    dv = int(rng.choice([64, 128]))
+    gate = str(rng.choice(["channel", "head"]))
+    gates = str(rng.choice(["beta", "gdr2"]))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
+                             pin_frac=0.05, seed=2000 + case, gates=gates)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    if rng.random() < 0.5:
+        x.s0 = rng.standard_normal((n, H, 128, dv)).astype(np.float32) * np.float32(0.02)
+    else:
+        x.s0 = None
+    note(f"random packed case {case}: lens={lens} H={H} dv={dv} {gate} {gates}")
+    o, sT = run_chunk(x, "bf16", o_fill=float("nan"))
+    assert np.all(np.isfinite(o)), "some output position was not written"
+    check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], f"random case {case}")
