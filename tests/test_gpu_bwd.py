@@ -136,25 +136,53 @@ def test_bwd_b2_h16_t4096_full():
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
 
 
-def test_bwd_gdn_b1_h16_t8192_sampled_chains():
+def test_bwd_gdn_b1_h16_t8192_all_chains():
     cfg = CONFIGS[2]
-    note(f"bwd parity {cfg.name} (sampled chains)")
+    note(f"bwd parity {cfg.name} (all chains)")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
-    chains = [(0, 0), (0, 7), (0, 15)]
-    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct, chains), cfg.name)
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct), cfg.name)
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
 
 
 def test_bwd_varlen_t65536_sampled_chains():
+    """Every sequence of the packed T = 65536 workload on two heads each (16 of the 256
+    chains, the longest and the shortest sequence among them)."""
     cfg = CONFIGS[3]
-    note(f"bwd parity {cfg.name} (sampled chains)")
+    note(f"bwd parity {cfg.name} (two heads of every sequence)")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
-    lens = np.diff(x.cu_seqlens)
-    chains = sorted({(int(np.argmax(lens)), 3), (int(np.argmin(lens)), 30), (2, 17)})
+    chains = [(n, (5 * n + j * 17) % cfg.H) for n in range(x.n_seqs) for j in range(2)]
     errs = check(x, run_bwd(x, ct), oracle_grads(x, ct, chains), cfg.name)
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_bwd_random_packed_shapes(case):
+    """Seeded random packed batches (1 to 8 sequences of 0 to 2500 tokens, 1 to 4 heads, dv
+    64 or 128, per-channel or per-head decay, with or without an initial state and a
+    final-state cotangent): every chain's gradients match the oracle."""
+    rng = np.random.default_rng(3000 + case)
+    n = int(rng.integers(1, 9))
+    lens = [int(v) for v in rng.integers(0, 2501, size=n)]
+    if sum(lens) == 0:
+        lens[0] = 1
+    H = int(rng.integers(1, 5))
+    dv = int(rng.choice([64, 128]))
+    gate = str(rng.choice(["channel", "head"]))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
+                             pin_frac=0.05, seed=4000 + case)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = rng.standard_normal((n, H, 128, dv)).astype(np.float32) * np.float32(0.02)
+    ct = make_cotangents(cfg, n)
+    init, fin = bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+    note(f"bwd random case {case}: lens={lens} H={H} dv={dv} {gate} s0={init} dsT={fin}")
+    errs = check(x, run_bwd(x, ct, initial_state=init, final_cotangent=fin),
+                 oracle_grads(x, ct, initial_state=init, final_cotangent=fin),
+                 f"bwd random case {case}")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
 
 
 GDR2_NAMES = ("dq", "dk", "dv", "dg", "derase", "dwrite", "ds0")
