@@ -40,6 +40,10 @@
 // Global memory is read and written through buffer descriptors bounded by the chain's
 // rows: reads past the sequence's end return zero (q = k = 0, g = 0, beta = 0 is the
 // identity token) and writes past it are dropped, so partial chunks need no branches.
+//
+// Below the kernel: the work list of packed sequences (chunk_plan_kernel), the segment plan
+// that cuts long sequences (chunk_segplan_kernel, seg_chain_kernel, seg_correct_kernel), the
+// two-pass segmented scan of dv = 64 (seg_combine_kernel), and the host launchers.
 #include <stddef.h>
 
 #include <algorithm>
