@@ -417,20 +417,21 @@ def main() -> int:
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         return 2
 
     import torch
 
     import gated_delta_rule_13_amd as kda
-    from kda_workloads import CONFIGS, make_chunk_inputs
+    from kda_workloads import (GDN_B1_H16_T8192, KDA_B2_H16_T4096, KDA_DECODE_N256_H32,
+                               KDA_VARLEN_H32_T65536, make_chunk_inputs)
 
     kda.load_library()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    cfg = CONFIGS[3]
+    cfg = KDA_VARLEN_H32_T65536
     t0 = time.time()
     x = make_chunk_inputs(cfg)
     log(f"generated {cfg.name} in {time.time() - t0:.1f}s; lengths {np.diff(x.cu_seqlens)}")
@@ -462,7 +463,7 @@ def main() -> int:
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
     }
     if not args.no_decode:
-        dcfg = CONFIGS[4]
+        dcfg = KDA_DECODE_N256_H32
         sec, gsec = bench_decode(torch, kda, dcfg)
         per_step = decode_alg_bytes_per_step(dcfg.B, dcfg.H, dcfg.dk, dcfg.dv)
         dgbs = per_step * dcfg.T / sec / 1e9
@@ -495,7 +496,7 @@ def main() -> int:
             log(f"gdr2 chunk_bwd: {gbms:.3f} ms/step")
         del gx
         if not args.no_decode:
-            gd = CONFIGS[4].replace(name="gdr2_decode_n256_h32", T=64, gates="gdr2")
+            gd = KDA_DECODE_N256_H32.replace(name="gdr2_decode_n256_h32", T=64, gates="gdr2")
             sec, _ = bench_decode(torch, kda, gd)
             per_step = decode_alg_bytes_per_step(gd.B, gd.H, gd.dk, gd.dv, gdr2=True)
             dgbs = per_step * gd.T / sec / 1e9
@@ -505,8 +506,7 @@ def main() -> int:
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
     # the two smaller prefill workloads (parity-test shapes), scheduled as a caller would
     small = {}
-    for ci in (1, 2):
-        c = CONFIGS[ci]
+    for c in (KDA_B2_H16_T4096, GDN_B1_H16_T8192):
         sx = make_chunk_inputs(c)
         sms = bench_chunk(torch, kda, sx, args.steps, args.warmup)
         sb = chunk_alg_bytes(sx)

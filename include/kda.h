@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1,  /* NULL required pointer, non-positive size, inconsistent shape */
-  KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. dk = 96) */
+  KDA_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement (e.g. dk = 96) */
   KDA_ERR_HIP = 3           /* a HIP runtime error while launching */
 } kda_status;
 

@@ -8,7 +8,12 @@ the method's arithmetic: no decay, no state update, no chunking.
 """
 
 from .generate import (  # noqa: F401
-    CONFIGS,
+    GDN_B1_H16_T8192,
+    KDA_B2_H16_T4096,
+    KDA_DECODE_N256_H32,
+    KDA_VARLEN_H32_T65536,
+    TINY_KDA_F32,
+    WORKLOADS,
     ChunkInputs,
     Cotangents,
     DecodeInputs,

@@ -67,18 +67,20 @@ class WorkloadConfig:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = [
-    WorkloadConfig("tiny_kda_f32", "chunk", "f32", B=1, H=2, T=256, dk=64, dv=64, seed=0),
-    WorkloadConfig("kda_bf16_b2_h16_t4096", "chunk", "bf16", B=2, H=16, T=4096, dk=128, dv=128,
-                   random_s0=True, seed=1),
-    WorkloadConfig("gdn_bf16_b1_h16_t8192", "chunk", "bf16", B=1, H=16, T=8192, dk=128, dv=128,
-                   gate="head", seed=2),
-    WorkloadConfig("kda_bf16_varlen_h32_t65536", "chunk", "bf16", B=1, H=32, T=65536, dk=128,
-                   dv=128, num_seqs=8, pin_frac=0.05, seed=3),
-    # decode: B = independent sequences, T = consecutive single-token steps
-    WorkloadConfig("kda_decode_n256_h32", "decode", "bf16", B=256, H=32, T=512, dk=128, dv=128,
-                   random_s0=True, seed=4),
-]
+TINY_KDA_F32 = WorkloadConfig("tiny_kda_f32", "chunk", "f32", B=1, H=2, T=256, dk=64, dv=64,
+                              seed=0)
+KDA_B2_H16_T4096 = WorkloadConfig("kda_bf16_b2_h16_t4096", "chunk", "bf16", B=2, H=16, T=4096,
+                                  dk=128, dv=128, random_s0=True, seed=1)
+GDN_B1_H16_T8192 = WorkloadConfig("gdn_bf16_b1_h16_t8192", "chunk", "bf16", B=1, H=16, T=8192,
+                                  dk=128, dv=128, gate="head", seed=2)
+KDA_VARLEN_H32_T65536 = WorkloadConfig("kda_bf16_varlen_h32_t65536", "chunk", "bf16", B=1, H=32,
+                                       T=65536, dk=128, dv=128, num_seqs=8, pin_frac=0.05, seed=3)
+# decode: B = independent sequences, T = consecutive single-token steps
+KDA_DECODE_N256_H32 = WorkloadConfig("kda_decode_n256_h32", "decode", "bf16", B=256, H=32, T=512,
+                                     dk=128, dv=128, random_s0=True, seed=4)
+# every workload: the four chunked-forward shapes, then the decode workload
+WORKLOADS = (TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192, KDA_VARLEN_H32_T65536,
+             KDA_DECODE_N256_H32)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

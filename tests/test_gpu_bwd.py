@@ -17,7 +17,8 @@ import torch
 
 import gated_delta_rule_13_amd as kda
 import oracle
-from kda_workloads import CONFIGS, make_chunk_inputs, make_cotangents
+from kda_workloads import (GDN_B1_H16_T8192, KDA_B2_H16_T4096, KDA_VARLEN_H32_T65536,
+                           make_chunk_inputs, make_cotangents)
 from tests.gpu_util import TOL, assert_close, note, up
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +89,7 @@ def check(x, got, ref, what, tol=TOL["bf16"]):
 @pytest.mark.parametrize("gate", ["channel", "head"])
 @pytest.mark.parametrize("dv", [128, 64])
 def test_bwd_small_ragged(gate, dv):
-    cfg = CONFIGS[1].replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=81, random_s0=True)
+    cfg = KDA_B2_H16_T4096.replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=81, random_s0=True)
     note(f"bwd small {gate} dv={dv}")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
@@ -99,7 +100,7 @@ def test_bwd_small_ragged(gate, dv):
 @pytest.mark.parametrize("initial_state,final_cotangent", [(False, False), (True, False),
                                                             (False, True)])
 def test_bwd_optional_states(initial_state, final_cotangent):
-    cfg = CONFIGS[1].replace(B=1, H=2, T=150, seed=82, random_s0=True)
+    cfg = KDA_B2_H16_T4096.replace(B=1, H=2, T=150, seed=82, random_s0=True)
     note(f"bwd s0={initial_state} dsT={final_cotangent}")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
@@ -112,7 +113,7 @@ def test_bwd_optional_states(initial_state, final_cotangent):
 def test_bwd_varlen_edge_lengths(gate):
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(gate=gate, H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05,
+    cfg = KDA_VARLEN_H32_T65536.replace(gate=gate, H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05,
                              seed=83)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
@@ -128,7 +129,7 @@ def test_bwd_varlen_edge_lengths(gate):
 
 
 def test_bwd_b2_h16_t4096_full():
-    cfg = CONFIGS[1]
+    cfg = KDA_B2_H16_T4096
     note(f"bwd parity {cfg.name}")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
@@ -137,7 +138,7 @@ def test_bwd_b2_h16_t4096_full():
 
 
 def test_bwd_gdn_b1_h16_t8192_all_chains():
-    cfg = CONFIGS[2]
+    cfg = GDN_B1_H16_T8192
     note(f"bwd parity {cfg.name} (all chains)")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
@@ -148,7 +149,7 @@ def test_bwd_gdn_b1_h16_t8192_all_chains():
 def test_bwd_varlen_t65536_sampled_chains():
     """Every sequence of the packed T = 65536 workload on two heads each (16 of the 256
     chains, the longest and the shortest sequence among them)."""
-    cfg = CONFIGS[3]
+    cfg = KDA_VARLEN_H32_T65536
     note(f"bwd parity {cfg.name} (two heads of every sequence)")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
@@ -171,7 +172,7 @@ def test_bwd_random_packed_shapes(case):
     dv = int(rng.choice([64, 128]))
     gate = str(rng.choice(["channel", "head"]))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
+    cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
                              pin_frac=0.05, seed=4000 + case)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
@@ -219,7 +220,7 @@ def check_gdr2(x, got, ref, what):
 @pytest.mark.parametrize("gate", ["channel", "head"])
 @pytest.mark.parametrize("dv", [128, 64])
 def test_gdr2_bwd_small_ragged(gate, dv):
-    cfg = CONFIGS[1].replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=84, random_s0=True,
+    cfg = KDA_B2_H16_T4096.replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=84, random_s0=True,
                              gates="gdr2")
     note(f"gdr2 bwd small {gate} dv={dv}")
     x = make_chunk_inputs(cfg)
@@ -233,7 +234,7 @@ def test_gdr2_bwd_small_ragged(gate, dv):
 def test_gdr2_bwd_varlen_edges():
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05, seed=85,
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05, seed=85,
                              gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
@@ -247,7 +248,7 @@ def test_gdr2_bwd_varlen_edges():
 
 
 def test_gdr2_bwd_b2_h16_t4096_full():
-    cfg = CONFIGS[1].replace(name="gdr2_bf16_b2_h16_t4096", gates="gdr2")
+    cfg = KDA_B2_H16_T4096.replace(name="gdr2_bf16_b2_h16_t4096", gates="gdr2")
     note(f"gdr2 bwd parity {cfg.name}")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)

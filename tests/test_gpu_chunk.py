@@ -14,16 +14,17 @@ import pytest
 import torch
 
 import gated_delta_rule_13_amd as kda
-from kda_workloads import CONFIGS, make_chunk_inputs
+from kda_workloads import (GDN_B1_H16_T8192, KDA_B2_H16_T4096, KDA_VARLEN_H32_T65536,
+                           TINY_KDA_F32, make_chunk_inputs)
 from tests.gpu_util import (TOL, assert_close, check_chains, note, oracle_chains, run_chunk,
                             up)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2])
-def test_workload_full_parity(idx):
-    cfg = CONFIGS[idx]
+@pytest.mark.parametrize("cfg", [TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192],
+                         ids=lambda c: c.name)
+def test_workload_full_parity(cfg):
     note(f"chunk parity {cfg.name}")
     x = make_chunk_inputs(cfg)
     o, sT = run_chunk(x, cfg.dtype)
@@ -36,7 +37,7 @@ def test_varlen_t65536_all_chains():
     """The packed varlen T = 65536 workload in the benchmark's launch configuration (with
     its workspace: the segment plan): every output row is written, and all 256 chains
     match the oracle (checked eight heads at a time to bound the host memory)."""
-    cfg = CONFIGS[3]
+    cfg = KDA_VARLEN_H32_T65536
     note(f"chunk parity {cfg.name} (all chains)")
     x = make_chunk_inputs(cfg)
     o, sT = run_chunk(x, cfg.dtype, o_fill=float("nan"))
@@ -59,7 +60,7 @@ for dtype in ("f32", "bf16"):
 
 @pytest.mark.parametrize("dtype,gate,dk,dv", SMALL)
 def test_small_ragged(dtype, gate, dk, dv):
-    cfg = CONFIGS[1].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=77)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=77)
     note(f"chunk small {dtype} {gate} dk={dk} dv={dv}")
     x = make_chunk_inputs(cfg)
     o, sT = run_chunk(x, dtype)
@@ -71,7 +72,7 @@ def test_varlen_edge_lengths(dtype):
     lens = [0, 1, 63, 64, 65, 130, 0, 7, 129]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1]) + 5   # tokens past the last sequence must stay untouched
-    cfg = CONFIGS[3].replace(dtype=dtype, H=2, T=T, num_seqs=0, pin_frac=0.05, seed=5)
+    cfg = KDA_VARLEN_H32_T65536.replace(dtype=dtype, H=2, T=T, num_seqs=0, pin_frac=0.05, seed=5)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(3).standard_normal((len(lens), 2, 128, 128)).astype(
@@ -90,7 +91,7 @@ def test_varlen_edge_lengths(dtype):
 @pytest.mark.parametrize("case", ["floor", "no_decay", "beta0", "beta1"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_degenerate_gates(case, dtype):
-    cfg = CONFIGS[1].replace(dtype=dtype, B=1, H=2, T=300, seed=9)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, B=1, H=2, T=300, seed=9)
     x = make_chunk_inputs(cfg)
     if case == "floor":
         x.g[...] = -5.0
@@ -107,7 +108,7 @@ def test_degenerate_gates(case, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_token(dtype):
-    cfg = CONFIGS[1].replace(dtype=dtype, B=3, H=2, T=1, seed=4)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, B=3, H=2, T=1, seed=4)
     x = make_chunk_inputs(cfg)
     note(f"chunk T=1 {dtype}")
     o, sT = run_chunk(x, dtype)
@@ -118,7 +119,7 @@ def test_split_resume_and_aliasing():
     """[0, T) in one call equals [0, T1) then [T1, T) resumed from the returned state;
     the resumed call passes the same buffer as initial and final state."""
     import gated_delta_rule_13_amd as kda
-    cfg = CONFIGS[1].replace(B=2, H=4, T=640, seed=21)
+    cfg = KDA_B2_H16_T4096.replace(B=2, H=4, T=640, seed=21)
     x = make_chunk_inputs(cfg)
     dt = torch.bfloat16
     q, k, v, g, beta, s0 = (up(x.q, dt), up(x.k, dt), up(x.v, dt), up(x.g), up(x.beta),
@@ -143,7 +144,7 @@ def test_split_resume_and_aliasing_segmented():
     segment reads the initial state and the segment chain writes the final state into the
     same buffer; outputs and states match the one-call run and the oracle."""
     import gated_delta_rule_13_amd as kda
-    cfg = CONFIGS[1].replace(B=1, H=1, T=5000, seed=22, random_s0=True)
+    cfg = KDA_B2_H16_T4096.replace(B=1, H=1, T=5000, seed=22, random_s0=True)
     x = make_chunk_inputs(cfg)
     dt = torch.bfloat16
     q, k, v, g, beta, s0 = (up(x.q, dt), up(x.k, dt), up(x.v, dt), up(x.g), up(x.beta),
@@ -167,7 +168,7 @@ def test_split_resume_and_aliasing_segmented():
 
 
 def test_deterministic():
-    cfg = CONFIGS[1].replace(B=2, H=4, T=1000, seed=8)
+    cfg = KDA_B2_H16_T4096.replace(B=2, H=4, T=1000, seed=8)
     x = make_chunk_inputs(cfg)
     note("chunk determinism")
     o1, s1 = run_chunk(x, "bf16")
@@ -177,7 +178,7 @@ def test_deterministic():
 
 
 def test_gdn_equals_broadcast_kda():
-    cfg = CONFIGS[2].replace(H=4, T=700, seed=12)
+    cfg = GDN_B1_H16_T8192.replace(H=4, T=700, seed=12)
     x = make_chunk_inputs(cfg)
     note("chunk GDN vs broadcast KDA")
     o1, s1 = run_chunk(x, "bf16")
@@ -197,7 +198,7 @@ def test_schedule_is_bitwise_neutral(dv):
     lens = [957, 795, 643, 621, 513, 494]
     H = 48
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05, seed=21)
+    cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05, seed=21)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(8).standard_normal((len(lens), H, 128, dv)).astype(
@@ -230,10 +231,10 @@ def test_segmented_matches_oracle_and_whole_chains(case):
     name, lens, B, H, T, dv, gate = case
     if lens is not None:
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
+        cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
                                  pin_frac=0.05, seed=23)
     else:
-        cfg = CONFIGS[1].replace(B=B, H=H, T=T, dv=dv, gate=gate, seed=23, random_s0=True)
+        cfg = KDA_B2_H16_T4096.replace(B=B, H=H, T=T, dv=dv, gate=gate, seed=23, random_s0=True)
     x = make_chunk_inputs(cfg)
     if lens is not None:
         x.cu_seqlens = cu
@@ -256,7 +257,7 @@ def test_segmented_without_initial_or_final_state():
     final state requested (the segment chain writes none): outputs match the oracle."""
     lens = [6000, 2500, 700]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=31)
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=31)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = None
@@ -294,7 +295,7 @@ def test_random_packed_shapes(case):
     gate = str(rng.choice(["channel", "head"]))
     gates = str(rng.choice(["beta", "gdr2"]))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
+    cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
                              pin_frac=0.05, seed=2000 + case, gates=gates)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu

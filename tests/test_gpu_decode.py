@@ -12,14 +12,15 @@ import torch
 
 import gated_delta_rule_13_amd as kda
 import oracle
-from kda_workloads import CONFIGS, decode_initial_state, decode_step_inputs, make_chunk_inputs
+from kda_workloads import (KDA_B2_H16_T4096, KDA_DECODE_N256_H32, decode_initial_state,
+                           decode_step_inputs, make_chunk_inputs)
 from tests.gpu_util import DT, TOL, assert_close, note, up
 
 pytestmark = pytest.mark.gpu
 
 
 def test_decode_workload_all_chains():
-    cfg = CONFIGS[4]
+    cfg = KDA_DECODE_N256_H32
     note(f"decode parity {cfg.name}: {cfg.T} steps, all chains")
     N, H, T, dk, dv = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv
     S0 = decode_initial_state(cfg)
@@ -59,7 +60,7 @@ def test_decode_workload_all_chains():
 @pytest.mark.parametrize("gate", ["channel", "head"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
 def test_decode_small(dtype, gate, dk, dv):
-    cfg = CONFIGS[4].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=5, H=3, seed=31)
+    cfg = KDA_DECODE_N256_H32.replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=5, H=3, seed=31)
     note(f"decode small {dtype} {gate} {dk}x{dv}")
     S = decode_initial_state(cfg)
     state = up(S)
@@ -76,7 +77,7 @@ def test_decode_small(dtype, gate, dk, dv):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_steps_equal_chunk_forward(dtype):
     """T calls of the decode step equal one chunked forward over the same T tokens."""
-    cfg = CONFIGS[1].replace(dtype=dtype, B=2, H=3, T=70, seed=15)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, B=2, H=3, T=70, seed=15)
     x = make_chunk_inputs(cfg)
     dt = DT[dtype]
     note(f"decode steps vs chunk forward {dtype}")
@@ -99,7 +100,7 @@ def test_decode_steps_in_a_replayed_graph():
     """Eight decode steps captured once in a HIP graph and replayed three times, with eager
     work and synchronisations between the replays: every replay gives the eager outputs
     and final state bit for bit."""
-    cfg = CONFIGS[4].replace(B=16, H=4, T=8, seed=61)
+    cfg = KDA_DECODE_N256_H32.replace(B=16, H=4, T=8, seed=61)
     note("decode steps in a HIP graph")
     N, H, T = cfg.B, cfg.H, cfg.T
     S0 = up(decode_initial_state(cfg))

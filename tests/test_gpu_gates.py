@@ -19,7 +19,8 @@ import torch
 import gated_delta_rule_13_amd as kda
 import oracle
 from oracle import gates as G
-from kda_workloads import CONFIGS, bf16_round, make_chunk_inputs, make_gate_inputs
+from kda_workloads import (KDA_B2_H16_T4096, KDA_VARLEN_H32_T65536, bf16_round,
+                           make_chunk_inputs, make_gate_inputs)
 from tests.gpu_util import DT, TOL, assert_close, note, up
 
 pytestmark = pytest.mark.gpu
@@ -68,7 +69,7 @@ def check_prologue(x, dtype, got, what):
 
 
 def small_gates(dtype, dk, dv, B=2, H=3, T=77, seed=91):
-    cfg = CONFIGS[1].replace(dtype=dtype, dk=dk, dv=dv, B=B, H=H, T=T, seed=seed)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, dk=dk, dv=dv, B=B, H=H, T=T, seed=seed)
     return cfg, make_gate_inputs(cfg)
 
 
@@ -148,7 +149,7 @@ def test_epilogue_zero_rows_and_in_place(dtype):
 
 
 def test_gates_b2_h16_t4096_full():
-    cfg = CONFIGS[1]
+    cfg = KDA_B2_H16_T4096
     x = make_gate_inputs(cfg)
     note(f"prologue / epilogue in full on {cfg.name}")
     check_prologue(x, "bf16", run_prologue(x, "bf16"), cfg.name)
@@ -160,7 +161,7 @@ def test_gates_b2_h16_t4096_full():
 def test_gates_varlen_t65536_sampled_rows():
     """The benchmark's launch: H32 T65536 packed tokens (B = 1), dk = dv = 128, on 4096
     sampled rows (the grid strides over 2M rows, so every block runs many passes)."""
-    cfg = CONFIGS[3]
+    cfg = KDA_VARLEN_H32_T65536
     x = make_gate_inputs(cfg)
     note(f"prologue / epilogue on {cfg.name} (sampled rows)")
     bf = torch.bfloat16
@@ -196,7 +197,7 @@ def test_prologue_operator_epilogue_end_to_end(dtype):
     epilogue on the operator's output against its definition. (The composition is not
     compared in one piece: RMSNorm rescales every row to unit size, so a row with a
     small output would turn the bf16 rounding of q and k into a large relative error.)"""
-    cfg = CONFIGS[1].replace(dtype=dtype, B=1, H=2, T=150, seed=44)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, B=1, H=2, T=150, seed=44)
     x = make_gate_inputs(cfg)
     v = make_chunk_inputs(cfg).v
     note(f"prologue -> chunk_fwd -> epilogue {dtype}")

@@ -14,7 +14,8 @@ import torch
 
 import gated_delta_rule_13_amd as kda
 import oracle
-from kda_workloads import CONFIGS, decode_initial_state, decode_step_inputs, make_chunk_inputs
+from kda_workloads import (KDA_B2_H16_T4096, KDA_DECODE_N256_H32, KDA_VARLEN_H32_T65536,
+                           decode_initial_state, decode_step_inputs, make_chunk_inputs)
 from tests.gpu_util import (DT, TOL, assert_close, check_chains, note, oracle_chains, run_chunk,
                             up)
 
@@ -26,7 +27,7 @@ SMALL = [(dtype, gate, dk, dv) for dtype in ("f32", "bf16") for gate in ("channe
 
 @pytest.mark.parametrize("dtype,gate,dk,dv", SMALL)
 def test_gdr2_small_ragged(dtype, gate, dk, dv):
-    cfg = CONFIGS[1].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=78,
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=78,
                              gates="gdr2")
     note(f"gdr2 small {dtype} {gate} dk={dk} dv={dv}")
     x = make_chunk_inputs(cfg)
@@ -35,7 +36,7 @@ def test_gdr2_small_ragged(dtype, gate, dk, dv):
 
 
 def test_gdr2_b2_h16_t4096_full():
-    cfg = CONFIGS[1].replace(name="gdr2_bf16_b2_h16_t4096", gates="gdr2")
+    cfg = KDA_B2_H16_T4096.replace(name="gdr2_bf16_b2_h16_t4096", gates="gdr2")
     note(f"gdr2 parity {cfg.name}")
     x = make_chunk_inputs(cfg)
     o, sT = run_chunk(x, "bf16")
@@ -44,7 +45,7 @@ def test_gdr2_b2_h16_t4096_full():
 
 
 def test_gdr2_varlen_t65536_all_chains():
-    cfg = CONFIGS[3].replace(name="gdr2_bf16_varlen_h32_t65536", gates="gdr2")
+    cfg = KDA_VARLEN_H32_T65536.replace(name="gdr2_bf16_varlen_h32_t65536", gates="gdr2")
     note(f"gdr2 parity {cfg.name} (all chains)")
     x = make_chunk_inputs(cfg)
     o, sT = run_chunk(x, "bf16", o_fill=float("nan"))
@@ -64,7 +65,7 @@ def test_gdr2_segmented_matches_oracle_and_whole_chains():
     leaves them untouched) and their outputs are corrected."""
     lens = [5000, 3000, 800, 1]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=57,
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=57,
                              gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
@@ -82,7 +83,7 @@ def test_gdr2_segmented_matches_oracle_and_whole_chains():
 def test_gdr2_varlen_edge_lengths(dtype):
     lens = [0, 1, 63, 64, 65, 130, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = CONFIGS[3].replace(dtype=dtype, H=2, T=int(cu[-1]) + 3, num_seqs=0, pin_frac=0.05,
+    cfg = KDA_VARLEN_H32_T65536.replace(dtype=dtype, H=2, T=int(cu[-1]) + 3, num_seqs=0, pin_frac=0.05,
                              seed=6, gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
@@ -98,7 +99,7 @@ def test_gdr2_varlen_edge_lengths(dtype):
 def test_gdr2_with_beta_gates_matches_kda(dtype):
     """b = beta 1 and w = beta 1 reduce Gated Delta Rule-2 to KDA: both entry points agree
     (to the rounding of the bf16 operands, which the two paths form differently)."""
-    cfg = CONFIGS[1].replace(dtype=dtype, B=1, H=4, T=333, seed=13, random_s0=True)
+    cfg = KDA_B2_H16_T4096.replace(dtype=dtype, B=1, H=4, T=333, seed=13, random_s0=True)
     note(f"gdr2 = kda with beta gates {dtype}")
     x = make_chunk_inputs(cfg)
     o_kda, s_kda = run_chunk(x, dtype)
@@ -114,7 +115,7 @@ def test_gdr2_with_beta_gates_matches_kda(dtype):
 @pytest.mark.parametrize("gate", ["channel", "head"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
 def test_gdr2_decode_small(dtype, gate, dk, dv):
-    cfg = CONFIGS[4].replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=5, H=3, T=6, seed=31,
+    cfg = KDA_DECODE_N256_H32.replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=5, H=3, T=6, seed=31,
                              gates="gdr2")
     note(f"gdr2 decode {dtype} {gate} dk={dk} dv={dv}")
     S0 = decode_initial_state(cfg)
@@ -135,7 +136,7 @@ def test_gdr2_decode_steps_equal_chunk_forward():
     """T decode steps on the same tokens equal one chunked forward (the state is the
     whole context), for the bf16 matrix-core chunk path."""
     B, H, T, dk, dv = 2, 4, 70, 128, 128
-    cfg = CONFIGS[1].replace(B=B, H=H, T=T, seed=55, random_s0=True, gates="gdr2")
+    cfg = KDA_B2_H16_T4096.replace(B=B, H=H, T=T, seed=55, random_s0=True, gates="gdr2")
     note("gdr2 decode steps vs chunk forward")
     x = make_chunk_inputs(cfg)
     o_chunk, s_chunk = run_chunk(x, "bf16")

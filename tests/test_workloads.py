@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 import torch
 
-from kda_workloads import CONFIGS, bf16_round, decode_step_inputs, make_chunk_inputs, varlen_lengths
+from kda_workloads import (KDA_DECODE_N256_H32, KDA_VARLEN_H32_T65536, WORKLOADS, bf16_round,
+                           decode_step_inputs, make_chunk_inputs, varlen_lengths)
 
 
 def test_bf16_round_matches_torch():
@@ -16,7 +17,7 @@ def test_bf16_round_matches_torch():
 
 
 def test_small_cases_are_deterministic_and_shaped():
-    for cfg in CONFIGS[:4]:
+    for cfg in WORKLOADS[:4]:
         small = cfg.replace(T=192 if not cfg.num_seqs else 1000, H=2, B=min(cfg.B, 2))
         a, b = make_chunk_inputs(small), make_chunk_inputs(small)
         for x, y in zip((a.q, a.k, a.v, a.g, a.beta), (b.q, b.k, b.v, b.g, b.beta)):
@@ -42,7 +43,7 @@ def test_varlen_recipe():
 
 
 def test_pinned_rows_fraction():
-    cfg = CONFIGS[3].replace(T=20000)
+    cfg = KDA_VARLEN_H32_T65536.replace(T=20000)
     x = make_chunk_inputs(cfg)
     pinned = np.all(x.g == -5.0, axis=-1)
     assert 0.04 < pinned.mean() < 0.06
@@ -51,7 +52,7 @@ def test_pinned_rows_fraction():
 
 @pytest.mark.parametrize("step", [0, 7])
 def test_decode_steps_differ_and_repeat(step):
-    cfg = CONFIGS[4].replace(B=4, H=3)
+    cfg = KDA_DECODE_N256_H32.replace(B=4, H=3)
     a, b = decode_step_inputs(cfg, step), decode_step_inputs(cfg, step)
     c = decode_step_inputs(cfg, step + 1)
     np.testing.assert_array_equal(a.q, b.q)
