@@ -113,8 +113,8 @@ def test_bwd_optional_states(initial_state, final_cotangent):
 def test_bwd_varlen_edge_lengths(gate):
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = KDA_VARLEN_H32_T65536.replace(gate=gate, H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05,
-                             seed=83)
+    cfg = KDA_VARLEN_H32_T65536.replace(gate=gate, H=2, T=int(cu[-1]) + 5, num_seqs=0,
+                                        pin_frac=0.05, seed=83)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(8).standard_normal((len(lens), 2, 128, 128)).astype(
@@ -173,7 +173,7 @@ def test_bwd_random_packed_shapes(case):
     gate = str(rng.choice(["channel", "head"]))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
-                             pin_frac=0.05, seed=4000 + case)
+                                        pin_frac=0.05, seed=4000 + case)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = rng.standard_normal((n, H, 128, dv)).astype(np.float32) * np.float32(0.02)
@@ -221,7 +221,7 @@ def check_gdr2(x, got, ref, what):
 @pytest.mark.parametrize("dv", [128, 64])
 def test_gdr2_bwd_small_ragged(gate, dv):
     cfg = KDA_B2_H16_T4096.replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=84, random_s0=True,
-                             gates="gdr2")
+                                   gates="gdr2")
     note(f"gdr2 bwd small {gate} dv={dv}")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
@@ -235,7 +235,7 @@ def test_gdr2_bwd_varlen_edges():
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]) + 5, num_seqs=0, pin_frac=0.05, seed=85,
-                             gates="gdr2")
+                                        gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(10).standard_normal((len(lens), 2, 128, 128)).astype(

@@ -198,7 +198,8 @@ def test_schedule_is_bitwise_neutral(dv):
     lens = [957, 795, 643, 621, 513, 494]
     H = 48
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05, seed=21)
+    cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05,
+                                        seed=21)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(8).standard_normal((len(lens), H, 128, dv)).astype(
@@ -232,7 +233,7 @@ def test_segmented_matches_oracle_and_whole_chains(case):
     if lens is not None:
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
         cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
-                                 pin_frac=0.05, seed=23)
+                                            pin_frac=0.05, seed=23)
     else:
         cfg = KDA_B2_H16_T4096.replace(B=B, H=H, T=T, dv=dv, gate=gate, seed=23, random_s0=True)
     x = make_chunk_inputs(cfg)
@@ -296,7 +297,7 @@ def test_random_packed_shapes(case):
     gates = str(rng.choice(["beta", "gdr2"]))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cfg = KDA_VARLEN_H32_T65536.replace(H=H, T=int(cu[-1]), dv=dv, gate=gate, num_seqs=0,
-                             pin_frac=0.05, seed=2000 + case, gates=gates)
+                                        pin_frac=0.05, seed=2000 + case, gates=gates)
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     if rng.random() < 0.5:

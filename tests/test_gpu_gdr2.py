@@ -28,7 +28,7 @@ SMALL = [(dtype, gate, dk, dv) for dtype in ("f32", "bf16") for gate in ("channe
 @pytest.mark.parametrize("dtype,gate,dk,dv", SMALL)
 def test_gdr2_small_ragged(dtype, gate, dk, dv):
     cfg = KDA_B2_H16_T4096.replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=78,
-                             gates="gdr2")
+                                   gates="gdr2")
     note(f"gdr2 small {dtype} {gate} dk={dk} dv={dv}")
     x = make_chunk_inputs(cfg)
     o, sT = run_chunk(x, dtype)
@@ -66,7 +66,7 @@ def test_gdr2_segmented_matches_oracle_and_whole_chains():
     lens = [5000, 3000, 800, 1]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=57,
-                             gates="gdr2")
+                                        gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(5).standard_normal((len(lens), 2, 128, 128)).astype(
@@ -83,8 +83,8 @@ def test_gdr2_segmented_matches_oracle_and_whole_chains():
 def test_gdr2_varlen_edge_lengths(dtype):
     lens = [0, 1, 63, 64, 65, 130, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = KDA_VARLEN_H32_T65536.replace(dtype=dtype, H=2, T=int(cu[-1]) + 3, num_seqs=0, pin_frac=0.05,
-                             seed=6, gates="gdr2")
+    cfg = KDA_VARLEN_H32_T65536.replace(dtype=dtype, H=2, T=int(cu[-1]) + 3, num_seqs=0,
+                                        pin_frac=0.05, seed=6, gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
     x.s0 = np.random.default_rng(4).standard_normal((len(lens), 2, 128, 128)).astype(
@@ -116,7 +116,7 @@ def test_gdr2_with_beta_gates_matches_kda(dtype):
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
 def test_gdr2_decode_small(dtype, gate, dk, dv):
     cfg = KDA_DECODE_N256_H32.replace(dtype=dtype, gate=gate, dk=dk, dv=dv, B=5, H=3, T=6, seed=31,
-                             gates="gdr2")
+                                      gates="gdr2")
     note(f"gdr2 decode {dtype} {gate} dk={dk} dv={dv}")
     S0 = decode_initial_state(cfg)
     state = up(S0)
