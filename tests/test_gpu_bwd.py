@@ -158,7 +158,7 @@ def test_bwd_varlen_t65536_sampled_chains():
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(16))
 def test_bwd_random_packed_shapes(case):
     """Seeded random packed batches (1 to 8 sequences of 0 to 2500 tokens, 1 to 4 heads, dv
     64 or 128, per-channel or per-head decay, with or without an initial state and a

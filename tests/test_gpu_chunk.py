@@ -277,7 +277,7 @@ def test_segmented_without_initial_or_final_state():
                  TOL["bf16"], "segmented, no states: outputs")
 
 
-RANDOM_SHAPES = list(range(12))
+RANDOM_SHAPES = list(range(40))
 
 
 @pytest.mark.parametrize("case", RANDOM_SHAPES)
