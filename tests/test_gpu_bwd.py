@@ -186,6 +186,25 @@ def test_bwd_random_packed_shapes(case):
     print({k: f"{v:.2e}" for k, v in errs.items()})
 
 
+def test_bwd_more_sequences_than_one_plan_sorts():
+    """1,100 packed sequences of 0 to 30 tokens (more than one planning workgroup sorts):
+    the workspace holds the two histories only, the chain passes run in chain order, and
+    every chain's gradients match the oracle."""
+    rng = np.random.default_rng(79)
+    lens = [int(v) for v in rng.integers(0, 31, size=1100)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    one = kda.kda_chunk_bwd_workspace_size(1, 1, T, 128, 128, len(lens), kda.KDA_BF16)
+    cfg = KDA_VARLEN_H32_T65536.replace(H=1, T=T, num_seqs=0, pin_frac=0.05, seed=80)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = rng.standard_normal((len(lens), 1, 128, 128)).astype(np.float32) * np.float32(0.02)
+    ct = make_cotangents(cfg, len(lens))
+    note(f"bwd with 1100 packed sequences (workspace {one} bytes)")
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct), "bwd 1100 sequences")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+
+
 GDR2_NAMES = ("dq", "dk", "dv", "dg", "derase", "dwrite", "ds0")
 
 

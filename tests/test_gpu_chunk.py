@@ -308,3 +308,22 @@ def test_random_packed_shapes(case):
     o, sT = run_chunk(x, "bf16", o_fill=float("nan"))
     assert np.all(np.isfinite(o)), "some output position was not written"
     check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], f"random case {case}")
+
+
+def test_more_sequences_than_one_plan_sorts():
+    """1,100 packed sequences of 0 to 40 tokens (more than the 1,024 that one planning
+    workgroup sorts): no workspace is asked for, the chains run one workgroup each in chain
+    order, every output row is written and every chain matches the oracle."""
+    rng = np.random.default_rng(77)
+    lens = [int(v) for v in rng.integers(0, 41, size=1100)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    assert kda.kda_chunk_fwd_workspace_size(1, 2, T, 128, 128, len(lens), kda.KDA_BF16) == 0
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=T, num_seqs=0, pin_frac=0.05, seed=78)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = rng.standard_normal((len(lens), 2, 128, 128)).astype(np.float32) * np.float32(0.02)
+    note("chunk with 1100 packed sequences")
+    o, sT = run_chunk(x, "bf16", o_fill=float("nan"))
+    assert np.all(np.isfinite(o)), "some output position was not written"
+    check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], "1100 sequences")
