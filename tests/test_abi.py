@@ -240,6 +240,9 @@ def test_bwd_workspace_size():
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_F32) == 0
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 64, 128, 0, kda.KDA_BF16) == 0
     assert kda.kda_chunk_bwd_workspace_size(0, 16, 4096, 128, 128, 0, kda.KDA_BF16) == 0
+    # the longest T axis of the backward: (T + 64) 16 dv < 2^31
+    assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 20) - 65, 128, 128, 1, kda.KDA_BF16) > 0
+    assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 20) - 64, 128, 128, 1, kda.KDA_BF16) == 0
 
 
 def bwd_call(**over):
@@ -266,6 +269,9 @@ def bwd_call(**over):
     (dict(dt=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
     (dict(dv=96), kda.KDA_ERR_UNSUPPORTED),
+    # one chain's history must be addressable by a buffer descriptor: (T + 64) 16 dv < 2^31
+    (dict(T=(1 << 20) - 64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=(1 << 21) - 64, dv=64), kda.KDA_ERR_UNSUPPORTED),
 ])
 def test_bwd_rejects(over, code):
     assert bwd_call(**over) == code

@@ -205,6 +205,36 @@ def test_bwd_more_sequences_than_one_plan_sorts():
     print({k: f"{v:.2e}" for k, v in errs.items()})
 
 
+def test_bwd_longest_t_axis():
+    """The longest T axis the backward takes at dv = 128 (one chain's bf16 history,
+    (T + 64) x 16 x dv bytes, must stay under 2^31: T = 2^20 - 65), as packed sequences of
+    200 to 400 tokens: sampled sequences at the start, the middle and the end of the axis
+    match the oracle. The inputs are a 65,536-token draw repeated along T."""
+    T = (1 << 20) - 65
+    rng = np.random.default_rng(94)
+    lens = []
+    while sum(lens) < T:
+        lens.append(int(rng.integers(200, 401)))
+    lens[-1] -= sum(lens) - T
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = KDA_VARLEN_H32_T65536.replace(H=1, T=65536, num_seqs=0, pin_frac=0.05, seed=95)
+    x = make_chunk_inputs(cfg)
+    reps = -(-T // 65536)
+    for name in ("q", "k", "v", "g"):
+        tiled = np.tile(getattr(x, name), (1, 1, reps, 1))[:, :, :T]
+        setattr(x, name, np.ascontiguousarray(tiled))
+    x.beta = np.ascontiguousarray(np.tile(x.beta, (1, 1, reps))[:, :, :T])
+    x.cu_seqlens = cu
+    x.s0 = None
+    n = len(lens)
+    ct = make_cotangents(cfg.replace(T=T), n)
+    note(f"bwd longest T axis {T}: {n} sequences")
+    got = run_bwd(x, ct)
+    sample = [(i, 0) for i in (0, 1, n // 2, n // 2 + 1, n - 3, n - 2, n - 1)]
+    errs = check(x, got, oracle_grads(x, ct, chains=sample), f"bwd T = {T}")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+
+
 GDR2_NAMES = ("dq", "dk", "dv", "dg", "derase", "dwrite", "ds0")
 
 

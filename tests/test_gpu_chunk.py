@@ -327,3 +327,34 @@ def test_more_sequences_than_one_plan_sorts():
     o, sT = run_chunk(x, "bf16", o_fill=float("nan"))
     assert np.all(np.isfinite(o)), "some output position was not written"
     check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], "1100 sequences")
+
+
+@pytest.mark.parametrize("T", [(1 << 22) - 64, (1 << 22) + 64], ids=["matrix-core", "fp32"])
+def test_longest_t_axis(T):
+    """The longest T axis the matrix-core kernel takes (a chain's per-channel decay, T x dk
+    fp32, must stay under 2^31 bytes: T < 2^22) and one just past it, which the fp32 kernel
+    takes, as packed sequences of 200 to 400 tokens: sampled sequences at the start, the
+    middle and the end of the axis (byte offsets past 2^31) match the oracle. The inputs are
+    a 65,536-token draw repeated along T."""
+    rng = np.random.default_rng(92)
+    lens = []
+    while sum(lens) < T:
+        lens.append(int(rng.integers(200, 401)))
+    lens[-1] -= sum(lens) - T
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    base = make_chunk_inputs(KDA_VARLEN_H32_T65536.replace(H=1, T=65536, num_seqs=0,
+                                                           pin_frac=0.05, seed=93))
+    reps = -(-T // 65536)
+    x = base
+    for name in ("q", "k", "v", "g"):
+        tiled = np.tile(getattr(base, name), (1, 1, reps, 1))[:, :, :T]
+        setattr(x, name, np.ascontiguousarray(tiled))
+    x.beta = np.ascontiguousarray(np.tile(base.beta, (1, 1, reps))[:, :, :T])
+    x.cu_seqlens = cu
+    x.s0 = None
+    n = len(lens)
+    note(f"chunk longest T axis {T}: {n} sequences")
+    o, sT = run_chunk(x, "bf16")
+    sample = [0, 1, n // 2, n // 2 + 1, n - 3, n - 2, n - 1]
+    ref = oracle_chains(x, chains=[(i, 0) for i in sample], initial_state=False)
+    check_chains(x, o, sT, ref, TOL["bf16"], f"T = {T}")
