@@ -131,7 +131,9 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  *
  * Arithmetic: state and accumulation in float32. With dt = KDA_BF16 the dense
  * contractions take bf16 operands on the matrix cores (float32 accumulate); with
- * dt = KDA_F32 every operation is float32.
+ * dt = KDA_F32 every operation is float32. The matrix-core kernel serves dt = KDA_BF16
+ * with dk = 128 while a chain's per-channel decay, T * dk float32 values, stays under 2^31
+ * bytes (T < 2^22); dk = 64, dt = KDA_F32 and longer T axes run on the float32 kernel.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* initial_state, float* final_state,
@@ -233,7 +235,9 @@ kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, fl
 /*
  * Bytes of device workspace that kda_chunk_bwd needs for these shapes (0 when the call
  * would be rejected as unsupported): two bf16 state histories of dk * dv / 8 bytes per
- * token, sequences padded to whole 64-token steps.
+ * token, sequences padded to whole 64-token steps (each rounded up to 256 bytes), and for
+ * packed sequences (num_seqs at most 1024) the work list of kda_chunk_fwd_workspace_size's
+ * last case.
  */
 size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
                                     kda_dtype dt);
@@ -256,7 +260,9 @@ size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  *                    on one workspace race)
  * Gradients are written for every token of every sequence; tokens outside every
  * sequence are left untouched. Supported: dt = KDA_BF16, dk = 128, dv = 64 or 128, either
- * gate mode (anything else: KDA_ERR_UNSUPPORTED). A NULL required array, a workspace
+ * gate mode, and T with (T + 64) * 16 * dv < 2^31, so that one chain's history fits a
+ * buffer descriptor (T <= 1,048,511 at dv = 128; anything else: KDA_ERR_UNSUPPORTED).
+ * A NULL required array, a workspace
  * smaller than the size above, or the forward's argument errors: KDA_ERR_INVALID_ARG.
  * Arithmetic: bf16 operands on the matrix cores with float32 accumulation and float32
  * state gradients; the stored forward states are bf16.
