@@ -29,26 +29,50 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str, extra) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, host_sanitize: str = "", out: str = LIB) -> str:
+    """Compiles every csrc/*.hip and links ``out`` (the in-tree libkda.so by default).
+
+    ``host_sanitize`` ("address" or "undefined") instruments the host code only
+    (``-Xarch_host -fsanitize=...``; the GPU code is built as usual) for running the C-ABI
+    checks, which launch nothing, under the sanitizer: load ``out`` with
+    ``gated_delta_rule_13_amd.load_library(out)`` in a Python started with the sanitizer's
+    runtime (``libclang_rt.asan-x86_64.so`` or ``libclang_rt.ubsan_standalone-x86_64.so``
+    from ROCm's clang) in ``LD_PRELOAD``.
+    """
+    extra = []
+    build_dir = BUILD
+    if host_sanitize:
+        if host_sanitize not in ("address", "undefined"):
+            raise ValueError(f"unknown sanitizer {host_sanitize!r}")
+        extra = ["-Xarch_host", f"-fsanitize={host_sanitize}"]
+        if host_sanitize == "undefined":
+            extra += ["-Xarch_host", "-fno-sanitize-recover=undefined"]
+        build_dir = f"{BUILD}_{host_sanitize}"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libkda.so for gfx950")
+    ap.add_argument("-v", action="store_true", help="show the link step's output")
+    ap.add_argument("--host-sanitize", choices=["address", "undefined"], default="")
+    ap.add_argument("--out", default=LIB)
+    args = ap.parse_args()
+    print(build(verbose=args.v, host_sanitize=args.host_sanitize, out=args.out))

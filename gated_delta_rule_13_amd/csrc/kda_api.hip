@@ -2,6 +2,7 @@
 // then dispatch to the kernels on the caller's stream. Nothing here allocates,
 // synchronises or keeps state between calls.
 #include <cstdint>
+#include <cstring>
 
 #include <algorithm>
 
@@ -12,6 +13,18 @@ namespace {
 
 bool supported_dim(int d) { return d == 64 || d == 128; }
 
+// Enum arguments arrive from C, where any int is a valid value; a C++ enum without a fixed
+// underlying type holds only the values of its enumerators' bit width, so every entry point
+// reads its enum arguments as plain ints (a byte copy from the argument's address: no
+// enum-typed load or copy) and the code below compares ints.
+template <typename E>
+int enum_value(const E* e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, e, sizeof v);
+  return v;
+}
+
 // The row-streaming kernels access eight channels at a time (16 bytes in bf16).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -20,7 +33,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 extern "C" {
 
 const char* kda_status_string(kda_status s) {
-  switch (s) {
+  switch (enum_value(&s)) {
     case KDA_OK: return "KDA_OK";
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported shape or mode";
@@ -42,8 +55,7 @@ static int device_compute_units() {
   return n;
 }
 
-size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
-                                    kda_dtype dt) {
+static size_t chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int num_seqs, int dt) {
   // only the matrix-core path uses a workspace: its work list (every intermediate of the
   // method stays on chip)
   if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return 0;
@@ -65,13 +77,18 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
   return kda::chunk_plan_bytes(num_seqs, H, dv);
 }
 
+size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt) {
+  return chunk_fwd_workspace(B, H, T, dk, dv, num_seqs, enum_value(&dt));
+}
+
 // The two forward paths differ only in their gates: beta (KDA, Gated DeltaNet) or the
 // erase / write vectors of Gated Delta Rule-2 (erase != nullptr).
 static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, const float* erase, const float* write,
                                  const float* initial_state, float* final_state, void* o,
                                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
-                                 int dk, int dv, kda_dtype dt, kda_gate_mode gm, void* workspace,
+                                 int dk, int dv, int dt, int gm, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !g || !o) return KDA_ERR_INVALID_ARG;
   if (erase ? !write : !beta) return KDA_ERR_INVALID_ARG;
@@ -80,7 +97,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
   if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
   if (!cu_seqlens && num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARG;
-  const size_t need = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt);
+  const size_t need = chunk_fwd_workspace(B, H, T, dk, dv, num_seqs, dt);
   // workspace_bytes == 0: run without the schedule; otherwise it must hold the schedule
   if (workspace_bytes > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_INVALID_ARG;
   const bool scheduled = need > 0 && workspace_bytes > 0;
@@ -119,8 +136,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
 static kda_status recurrent_step_impl(const void* q, const void* k, const void* v,
                                       const float* g, const float* beta, const float* erase,
                                       const float* write, float* state, void* o, int N, int H,
-                                      int dk, int dv, kda_dtype dt, kda_gate_mode gm,
-                                      hipStream_t stream) {
+                                      int dk, int dv, int dt, int gm, hipStream_t stream) {
   if (!q || !k || !v || !g || !state || !o) return KDA_ERR_INVALID_ARG;
   if (erase ? !write : !beta) return KDA_ERR_INVALID_ARG;
   if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
@@ -144,16 +160,16 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!beta) return KDA_ERR_INVALID_ARG;
   return chunk_fwd_impl(q, k, v, g, beta, nullptr, nullptr, initial_state, final_state, o,
-                        cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm, workspace,
-                        workspace_bytes, stream);
+                        cu_seqlens, num_seqs, B, H, T, dk, dv, enum_value(&dt), enum_value(&gm),
+                        workspace, workspace_bytes, stream);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state, void* o, int N, int H, int dk,
                               int dv, kda_dtype dt, kda_gate_mode gm, hipStream_t stream) {
   if (!beta) return KDA_ERR_INVALID_ARG;
-  return recurrent_step_impl(q, k, v, g, beta, nullptr, nullptr, state, o, N, H, dk, dv, dt,
-                             gm, stream);
+  return recurrent_step_impl(q, k, v, g, beta, nullptr, nullptr, state, o, N, H, dk, dv,
+                             enum_value(&dt), enum_value(&gm), stream);
 }
 
 kda_status kda_gdr2_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -164,8 +180,8 @@ kda_status kda_gdr2_chunk_fwd(const void* q, const void* k, const void* v, const
                               size_t workspace_bytes, hipStream_t stream) {
   if (!erase || !write) return KDA_ERR_INVALID_ARG;
   return chunk_fwd_impl(q, k, v, g, nullptr, erase, write, initial_state, final_state, o,
-                        cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm, workspace,
-                        workspace_bytes, stream);
+                        cu_seqlens, num_seqs, B, H, T, dk, dv, enum_value(&dt), enum_value(&gm),
+                        workspace, workspace_bytes, stream);
 }
 
 kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, const float* g,
@@ -173,12 +189,11 @@ kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, 
                                    void* o, int N, int H, int dk, int dv, kda_dtype dt,
                                    kda_gate_mode gm, hipStream_t stream) {
   if (!erase || !write) return KDA_ERR_INVALID_ARG;
-  return recurrent_step_impl(q, k, v, g, nullptr, erase, write, state, o, N, H, dk, dv, dt,
-                             gm, stream);
+  return recurrent_step_impl(q, k, v, g, nullptr, erase, write, state, o, N, H, dk, dv,
+                             enum_value(&dt), enum_value(&gm), stream);
 }
 
-size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
-                                    kda_dtype dt) {
+static size_t chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int num_seqs, int dt) {
   if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0 || dt != KDA_BF16) return 0;
   if (!kda::chunk_bwd_supports(dk, dv, T)) return 0;
   const int N = num_seqs > 0 ? num_seqs : B;
@@ -186,6 +201,11 @@ size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num
   // the two histories, then the work list of packed sequences
   const size_t plan = num_seqs > 0 ? kda::chunk_plan_bytes(num_seqs, H, dv) : 0;
   return 2 * ((one + 255) / 256 * 256) + plan;
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
+                                    kda_dtype dt) {
+  return chunk_bwd_workspace(B, H, T, dk, dv, num_seqs, enum_value(&dt));
 }
 
 // The two backward paths differ only in their gates: beta (KDA, Gated DeltaNet) or the
@@ -197,9 +217,9 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
                                  void* grad_v, float* grad_g, float* grad_beta,
                                  float* grad_erase, float* grad_write,
                                  float* grad_initial_state, const int32_t* cu_seqlens,
-                                 int num_seqs, int B, int H, int T, int dk, int dv,
-                                 kda_dtype dt, kda_gate_mode gm, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+                                 int num_seqs, int B, int H, int T, int dk, int dv, int dt,
+                                 int gm, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
   if (!q || !k || !v || !g || !grad_o) return KDA_ERR_INVALID_ARG;
   if (erase ? (!write || !grad_erase || !grad_write) : (!beta || !grad_beta))
     return KDA_ERR_INVALID_ARG;
@@ -213,7 +233,7 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
   const long long N = cu_seqlens ? num_seqs : B;
   if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
   const size_t need =
-      kda_chunk_bwd_workspace_size(B, H, T, dk, dv, cu_seqlens ? num_seqs : 0, dt);
+      chunk_bwd_workspace(B, H, T, dk, dv, cu_seqlens ? num_seqs : 0, dt);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
 
   kda::BwdArgs b;
@@ -248,8 +268,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
   if (!beta) return KDA_ERR_INVALID_ARG;
   return chunk_bwd_impl(q, k, v, g, beta, nullptr, nullptr, initial_state, grad_o,
                         grad_final_state, grad_q, grad_k, grad_v, grad_g, grad_beta, nullptr,
-                        nullptr, grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv, dt,
-                        gm, workspace, workspace_bytes, stream);
+                        nullptr, grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv,
+                        enum_value(&dt), enum_value(&gm), workspace, workspace_bytes, stream);
 }
 
 kda_status kda_gdr2_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -265,7 +285,7 @@ kda_status kda_gdr2_chunk_bwd(const void* q, const void* k, const void* v, const
   return chunk_bwd_impl(q, k, v, g, nullptr, erase, write, initial_state, grad_o,
                         grad_final_state, grad_q, grad_k, grad_v, grad_g, nullptr, grad_erase,
                         grad_write, grad_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv,
-                        dt, gm, workspace, workspace_bytes, stream);
+                        enum_value(&dt), enum_value(&gm), workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, const float* A_log,
@@ -279,14 +299,15 @@ kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, cons
       !aligned16(q_out) || !aligned16(k_out) || !aligned16(g_out))
     return KDA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || dk <= 0) return KDA_ERR_INVALID_ARG;
-  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  const int dtype = enum_value(&dt);
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (!supported_dim(dk)) return KDA_ERR_UNSUPPORTED;
   if ((long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
   kda::PrologueArgs a;
   a.q_in = q_in; a.k_in = k_in; a.u = u; a.A_log = A_log; a.dt_bias = dt_bias;
   a.beta_in = beta_in; a.q_out = q_out; a.k_out = k_out; a.g_out = g_out; a.beta_out = beta_out;
   a.B = B; a.H = H; a.T = T;
-  const hipError_t err = kda::launch_prologue(a, dk, dt == KDA_BF16, stream);
+  const hipError_t err = kda::launch_prologue(a, dk, dtype == KDA_BF16, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -298,13 +319,14 @@ kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, fl
     return KDA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || !(eps < 1e30f)) return KDA_ERR_INVALID_ARG;  // also rejects NaN
   if (B <= 0 || H <= 0 || T <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
-  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  const int dtype = enum_value(&dt);
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (!supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
   if ((long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
   kda::EpilogueArgs a;
   a.o_in = o_in; a.z = z; a.weight = weight; a.eps = eps; a.o_out = o_out;
   a.B = B; a.H = H; a.T = T;
-  const hipError_t err = kda::launch_epilogue(a, dv, dt == KDA_BF16, stream);
+  const hipError_t err = kda::launch_epilogue(a, dv, dtype == KDA_BF16, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
