@@ -372,3 +372,39 @@ def test_longest_t_axis(T):
     sample = [0, 1, n // 2, n // 2 + 1, n - 3, n - 2, n - 1]
     ref = oracle_chains(x, chains=[(i, 0) for i in sample], initial_state=False)
     check_chains(x, o, sT, ref, TOL["bf16"], f"T = {T}")
+
+
+def test_forward_in_a_replayed_graph():
+    """The segment plan's launches (planner, items, chain, corrections) captured once in a
+    HIP graph and replayed three times, with eager work and synchronisations between the
+    replays: every replay gives the eager outputs and final states bit for bit."""
+    lens = [20000, 3000, 500]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=98)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(99).standard_normal((3, 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    ws = kda.kda_chunk_fwd_workspace_size(1, 2, int(cu[-1]), 128, 128, 3, kda.KDA_BF16)
+    assert ws > 128 * 128 * 4, "expected the segment plan"
+    note("chunk forward in a HIP graph")
+    bf = torch.bfloat16
+    q, k, v = up(x.q, bf), up(x.k, bf), up(x.v, bf)
+    g, beta, s0 = up(x.g), up(x.beta), up(x.s0)
+    cut = up(cu, torch.int32)
+    o = torch.empty(tuple(x.v.shape), dtype=bf, device=q.device)
+    sT = torch.empty((3, 2, 128, 128), dtype=torch.float32, device=q.device)
+    kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cut, o=o, final_state=sT)
+    torch.cuda.synchronize()
+    want_o, want_s = o.clone(), sT.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cut, o=o, final_state=sT)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        sT.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o), f"replay {rep}: outputs differ"
+        assert torch.equal(sT, want_s), f"replay {rep}: final states differ"
