@@ -285,6 +285,38 @@ def test_bwd_in_a_replayed_graph():
             assert torch.equal(got, w), f"replay {rep}: {name} differs"
 
 
+def test_bwd_on_two_streams_at_once():
+    """Two backward calls enqueued back to back on two streams of the device, which share
+    the library's second stream for their state histories: each gives the gradients of the
+    same call run alone, bit for bit."""
+    cases = []
+    for i, lens in enumerate(([2500, 700, 64], [1800, 1800, 5, 300])):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05,
+                                            seed=102 + i)
+        x = make_chunk_inputs(cfg)
+        ct = make_cotangents(cfg, len(lens))
+        bf = torch.bfloat16
+        args = (up(x.q, bf), up(x.k, bf), up(x.v, bf), up(x.g), up(x.beta), up(ct.do, bf))
+        kw = dict(grad_final_state=up(ct.dsT), cu_seqlens=up(cu, torch.int32))
+        cases.append((args, kw))
+    note("bwd on two streams")
+    alone = []
+    for args, kw in cases:
+        alone.append([t.clone() for t in kda.chunk_bwd(*args, **kw)])
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (args, kw), st in zip(cases, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            outs.append(kda.chunk_bwd(*args, **kw))
+    torch.cuda.synchronize()
+    for i, (got, want) in enumerate(zip(outs, alone)):
+        for name, a, b in zip(NAMES + ("ds0",), got, want):
+            assert torch.equal(a, b), f"call {i}: {name} differs"
+
+
 GDR2_NAMES = ("dq", "dk", "dv", "dg", "derase", "dwrite", "ds0")
 
 
