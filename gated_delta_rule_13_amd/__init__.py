@@ -26,6 +26,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_ERR_PRECONDITION = 4   # KDA_DEBUG builds (libkda_debug.so) only
+DEBUG_LIB_PATH = os.path.join(HERE, "libkda_debug.so")
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_PER_CHANNEL, KDA_GATE_PER_HEAD = 0, 1
 
@@ -44,12 +46,21 @@ class KDAError(RuntimeError):
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Loads libkda.so (built by ``gated_delta_rule_13_amd/build.py``); raises if missing."""
+    """Loads libkda.so (built by ``gated_delta_rule_13_amd/build.py``) as the library behind
+    every function of this module; raises if missing."""
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A separate handle on a build of the library (e.g. ``DEBUG_LIB_PATH``), with the C
+    signatures set; the module's functions keep using ``load_library``'s."""
     if not os.path.exists(path):
-        raise RuntimeError(f"libkda.so is not built ({path}); run __graft_entry__.build()")
+        raise RuntimeError(f"{os.path.basename(path)} is not built ({path}); "
+                           "run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
@@ -78,7 +89,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [I]
     lib.kda_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 
@@ -218,9 +228,13 @@ def _chunk(q, k, v, g, gates, initial_state, cu_seqlens, output_final_state, o, 
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
     _check(o, "o", q.dtype, dev)
+    if tuple(o.shape) != (B, H, T, dv):
+        raise ValueError(f"o must be {(B, H, T, dv)}, got {tuple(o.shape)}")
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, dev)
+    if final_state is not None and tuple(final_state.shape) != (N, H, dk, dv):
+        raise ValueError(f"final_state must be {(N, H, dk, dv)}, got {tuple(final_state.shape)}")
     num_seqs = 0 if cu_seqlens is None else N
     ws_bytes = kda_chunk_fwd_workspace_size(B, H, T, dk, dv, num_seqs, dt) if schedule else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -296,6 +310,8 @@ def _step(q, k, v, g, gates, state, o):
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _check(o, "o", q.dtype, dev)
+    if tuple(o.shape) != (N, H, dv):
+        raise ValueError(f"o must be {(N, H, dv)}, got {tuple(o.shape)}")
     if len(gates) == 1:
         st = kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gates[0]),
                                 _ptr(state), _ptr(o), N, H, dk, dv, dt, gm, _stream(dev))

@@ -38,8 +38,15 @@ def _compile(src: str, build_dir: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, host_sanitize: str = "", out: str = LIB) -> str:
+DEBUG_LIB = os.path.join(HERE, "libkda_debug.so")
+
+
+def build(verbose: bool = False, host_sanitize: str = "", out: str = LIB,
+          debug: bool = False) -> str:
     """Compiles every csrc/*.hip and links ``out`` (the in-tree libkda.so by default).
+
+    ``debug`` builds the KDA_DEBUG library (``libkda_debug.so`` unless ``out`` is given): every
+    operator entry point checks its value preconditions on the device first (kda.h).
 
     ``host_sanitize`` ("address" or "undefined") instruments the host code only
     (``-Xarch_host -fsanitize=...``; the GPU code is built as usual) for running the C-ABI
@@ -50,13 +57,19 @@ def build(verbose: bool = False, host_sanitize: str = "", out: str = LIB) -> str
     """
     extra = []
     build_dir = BUILD
+    if debug:
+        # the precondition checks of every operator entry point (kda_debug.hip)
+        extra = ["-DKDA_DEBUG=1"]
+        build_dir = f"{BUILD}_debug"
+        if out == LIB:
+            out = DEBUG_LIB
     if host_sanitize:
         if host_sanitize not in ("address", "undefined"):
             raise ValueError(f"unknown sanitizer {host_sanitize!r}")
-        extra = ["-Xarch_host", f"-fsanitize={host_sanitize}"]
+        extra += ["-Xarch_host", f"-fsanitize={host_sanitize}"]
         if host_sanitize == "undefined":
             extra += ["-Xarch_host", "-fno-sanitize-recover=undefined"]
-        build_dir = f"{BUILD}_{host_sanitize}"
+        build_dir = f"{build_dir}_{host_sanitize}"
     os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
@@ -74,5 +87,8 @@ if __name__ == "__main__":
     ap.add_argument("-v", action="store_true", help="show the link step's output")
     ap.add_argument("--host-sanitize", choices=["address", "undefined"], default="")
     ap.add_argument("--out", default=LIB)
+    ap.add_argument("--debug", action="store_true",
+                    help="build libkda_debug.so: device-side checks of the value preconditions")
     args = ap.parse_args()
-    print(build(verbose=args.v, host_sanitize=args.host_sanitize, out=args.out))
+    print(build(verbose=args.v, host_sanitize=args.host_sanitize, out=args.out,
+                debug=args.debug))

@@ -1,10 +1,12 @@
 // C ABI of libkda.so (declared in include/kda.h): argument validation on the host,
-// then dispatch to the kernels on the caller's stream. Nothing here allocates,
-// synchronises or keeps state between calls.
+// then dispatch to the kernels on the caller's stream. Nothing here allocates device memory
+// or synchronises the host; the state kept between calls is the per-device compute-unit
+// count below and the backward's per-device second stream (kda_chunk_bwd.hip).
 #include <cstdint>
 #include <cstring>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -38,42 +40,79 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported shape or mode";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+    case KDA_ERR_PRECONDITION:
+      return "KDA_ERR_PRECONDITION: an input value is outside the documented range";
   }
   return "KDA_ERR_UNKNOWN: unknown status code";
 }
 
-// Compute units of the current device, cached per device (sizes the chunk schedule).
+// Compute units of the current device, cached per device (sizes the chunk schedule). The
+// cache entries are atomics: concurrent first calls may both query the device, and both
+// store the same value.
 static int device_compute_units() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
+// KDA_DEBUG builds: the value preconditions of an operator call, checked on the device
+// before its work (the work is not launched when one fails).
+#if KDA_DEBUG
+static int debug_preconditions(const float* g, bool per_channel, const float* beta,
+                               const float* erase, const float* write,
+                               const int32_t* cu_seqlens, int num_seqs, long long rows, int T,
+                               int dk, int dv, hipStream_t stream) {
+  kda::DebugCheck c;
+  c.add(g, per_channel ? rows * dk : rows, -5.f, 0.f, kda::DebugCheck::kG);
+  if (erase) {
+    c.add(erase, rows * dk, 0.f, 1.f, kda::DebugCheck::kErase);
+    c.add(write, rows * dv, 0.f, 1.f, kda::DebugCheck::kWrite);
+  } else {
+    c.add(beta, rows, 0.f, 1.f, kda::DebugCheck::kBeta);
+  }
+  if (cu_seqlens) {
+    c.cu = cu_seqlens;
+    c.N = num_seqs;
+    c.T = T;
+  }
+  unsigned flags = 0;
+  if (kda::debug_check(c, stream, flags) != hipSuccess) return KDA_ERR_HIP;
+  return flags ? KDA_ERR_PRECONDITION : KDA_OK;
+}
+#endif
+
+// The workspace the forward recommends. A call is packed when it passes cu_seqlens (then B = 1
+// and num_seqs sequences); the size query takes num_seqs > 0 for such a call.
 static size_t chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int num_seqs, int dt) {
-  // only the matrix-core path uses a workspace: its work list (every intermediate of the
-  // method stays on chip)
+  // only the matrix-core path uses a workspace: its schedule (every intermediate of the
+  // method stays on chip) and, for the segment plan, the segments' states
   if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return 0;
   if (dt != KDA_BF16 || !kda::chunk_mfma_supports(dk, dv, T)) return 0;
-  const long long N = num_seqs > 0 ? num_seqs : B;
+  const bool packed = num_seqs > 0;
+  if (packed && B != 1) return 0;  // no such call is accepted
+  const long long N = packed ? num_seqs : B;
   if (N * H > (1ll << 24)) return 0;
   const int cus = device_compute_units();
   // dv = dk: the segment plan (packed sequences, or fewer equal-length chains than compute
-  // units); it also holds the work list that the Gated Delta Rule-2 gates use
-  if (dv == dk && (num_seqs > 0 || N * H < cus)) {
-    const size_t sp = kda::chunk_segplan_bytes((int)N, H, T, dv, num_seqs > 0);
-    if (sp > 0) return std::max(sp, num_seqs > 0 ? kda::chunk_plan_bytes(num_seqs, H, dv) : 0);
+  // units); its plan words also hold the work list that it falls back to
+  if (dv == dk && (packed || N * H < cus)) {
+    const size_t sp = kda::chunk_segplan_bytes((int)N, H, T, dv, packed, cus);
+    if (sp > 0) return sp;
   }
   // few chains for the device: segments and their states (this also covers the work list)
   const size_t seg = kda::chunk_seg_bytes((int)N, H, T, dv, cus);
   if (seg > 0) return seg;
   // equal-length batches are scheduled on the host: only packed sequences need a work list
-  if (num_seqs == 0) return 0;
+  if (!packed) return 0;
   return kda::chunk_plan_bytes(num_seqs, H, dv);
 }
 
@@ -97,19 +136,30 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
   if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
   if (!cu_seqlens && num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARG;
-  const size_t need = chunk_fwd_workspace(B, H, T, dk, dv, num_seqs, dt);
-  // workspace_bytes == 0: run without the schedule; otherwise it must hold the schedule
-  if (workspace_bytes > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_INVALID_ARG;
-  const bool scheduled = need > 0 && workspace_bytes > 0;
+  // packed exactly when cu_seqlens is given (num_seqs = B without it is B sequences of T)
+  const bool packed = cu_seqlens != nullptr;
+  const long long N = packed ? num_seqs : B;
+  const bool mfma = dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T);
+  // workspace_bytes == 0: run without a schedule. Otherwise packed sequences need at least
+  // their work list; every larger buffer is planned within (each path below checks that its
+  // own layout fits).
+  const size_t work_list = mfma && packed ? kda::chunk_plan_bytes((int)N, H, dv) : 0;
+  if (workspace_bytes > 0 && (!workspace || workspace_bytes < work_list))
+    return KDA_ERR_INVALID_ARG;
   if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
-  const long long N = cu_seqlens ? num_seqs : B;
   if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
 
+#if KDA_DEBUG
+  if (const int pre = debug_preconditions(g, gm == KDA_GATE_PER_CHANNEL, beta, erase, write,
+                                          cu_seqlens, num_seqs, (long long)B * H * T, T, dk,
+                                          dv, stream))
+    return static_cast<kda_status>(pre);
+#endif
   kda::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = erase; a.write = write;
   a.s0 = initial_state; a.sT = final_state; a.o = o; a.cu = cu_seqlens;
   a.N = (int)N; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
-  a.plan = scheduled ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.plan = nullptr;
   a.cus = device_compute_units();
   a.split_all = 0;
   a.hist = nullptr;
@@ -120,14 +170,21 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   a.qt = nullptr;
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
-  if (dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T)) {
-    const size_t sp = kda::chunk_segplan_bytes(a.N, H, T, dv, cu_seqlens != nullptr);
-    if (scheduled && sp > 0 && workspace_bytes >= sp)
-      err = kda::launch_chunk_mfma_segplan(a, per_channel, workspace, stream);
-    else if (scheduled && !erase && kda::chunk_seg_bytes(a.N, H, T, dv, a.cus) > 0)
+  if (mfma) {
+    const size_t sp_min = kda::chunk_segplan_min_bytes(a.N, H, T, dv);
+    const size_t seg = kda::chunk_seg_bytes(a.N, H, T, dv, a.cus);
+    if (workspace_bytes > 0 && (packed || N * H < a.cus) && sp_min > 0 &&
+        workspace_bytes >= sp_min) {
+      err = kda::launch_chunk_mfma_segplan(a, per_channel, workspace, workspace_bytes, stream);
+    } else if (workspace_bytes > 0 && !erase && seg > 0 && workspace_bytes >= seg) {
       err = kda::launch_chunk_mfma_segmented(a, per_channel, workspace, stream);
-    else
+    } else {
+      // the work list of packed sequences when it fits (chunk_plan_bytes is 0 past the
+      // sequences one planning workgroup sorts), else one workgroup per chain
+      if (packed && work_list > 0 && workspace_bytes >= work_list)
+        a.plan = static_cast<uint32_t*>(workspace);
       err = kda::launch_chunk_mfma(a, per_channel, stream);
+    }
   } else
     err = kda::launch_chunk_f32(a, dt == KDA_BF16, per_channel, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -144,6 +201,11 @@ static kda_status recurrent_step_impl(const void* q, const void* k, const void* 
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
   if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
   if ((long long)N * H > 0x7fffffffll) return KDA_ERR_UNSUPPORTED;
+#if KDA_DEBUG
+  if (const int pre = debug_preconditions(g, gm == KDA_GATE_PER_CHANNEL, beta, erase, write,
+                                          nullptr, 0, (long long)N * H, 1, dk, dv, stream))
+    return static_cast<kda_status>(pre);
+#endif
   kda::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = erase; a.write = write;
   a.state = state; a.o = o;
@@ -236,6 +298,12 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
       chunk_bwd_workspace(B, H, T, dk, dv, cu_seqlens ? num_seqs : 0, dt);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
 
+#if KDA_DEBUG
+  if (const int pre = debug_preconditions(g, gm == KDA_GATE_PER_CHANNEL, beta, erase, write,
+                                          cu_seqlens, num_seqs, (long long)B * H * T, T, dk,
+                                          dv, stream))
+    return static_cast<kda_status>(pre);
+#endif
   kda::BwdArgs b;
   kda::ChunkArgs& a = b.f;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.erase = erase; a.write = write;
@@ -317,7 +385,8 @@ kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, fl
   if (!o_in || !z || !o_out) return KDA_ERR_INVALID_ARG;
   if (!aligned16(o_in) || !aligned16(z) || !aligned16(o_out) || !aligned16(weight))
     return KDA_ERR_INVALID_ARG;
-  if (!(eps >= 0.f) || !(eps < 1e30f)) return KDA_ERR_INVALID_ARG;  // also rejects NaN
+  // eps > 0 keeps an all-zero row finite (0 / sqrt(eps) = 0); also rejects NaN and inf
+  if (!(eps > 0.f) || !(eps < 1e30f)) return KDA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
   const int dtype = enum_value(&dt);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;

@@ -882,24 +882,33 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
   ChunkArgs h = b.f;
   h.hist = b.hist_s;
   h.split_all = 0;  // the history launch decides its own split
+  // The fork and join events belong to this call (two calls enqueued from different host
+  // threads must not re-record each other's events); the guard destroys them on every path.
+  // Destroying an event that a stream still waits on is allowed: the wait keeps its target.
+  struct EventPair {
+    hipEvent_t forked = nullptr, joined = nullptr;
+    ~EventPair() {
+      if (forked) (void)hipEventDestroy(forked);
+      if (joined) (void)hipEventDestroy(joined);
+    }
+  } ev;
   hipStream_t side = side_stream();
-  hipEvent_t forked = nullptr, joined = nullptr;
-  if (side && (hipEventCreateWithFlags(&forked, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&joined, hipEventDisableTiming) != hipSuccess))
-    side = nullptr;
+  if (side && (hipEventCreateWithFlags(&ev.forked, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&ev.joined, hipEventDisableTiming) != hipSuccess))
+    side = nullptr;  // no events: run the history on the caller's stream instead
   if (side) {
-    if ((e = hipEventRecord(forked, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side, forked, 0)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev.forked, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side, ev.forked, 0)) != hipSuccess) return e;
   }
   e = launch_chunk_mfma_hist(h, per_channel, side ? side : stream, false);
   if (e == hipSuccess)
     e = a.erase ? launch_carry<true>(b, per_channel, chains, stream)
                 : launch_carry<false>(b, per_channel, chains, stream);
   if (side) {
-    hipError_t e2 = hipEventRecord(joined, side);
-    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, joined, 0);
-    hipEventDestroy(forked);
-    hipEventDestroy(joined);
+    // join even after a failed launch, so that the caller's stream never runs ahead of
+    // work already enqueued on the side stream
+    hipError_t e2 = hipEventRecord(ev.joined, side);
+    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, ev.joined, 0);
     if (e == hipSuccess) e = e2;
   }
   if (e != hipSuccess) return e;

@@ -66,20 +66,26 @@ constexpr int kModePair = 4;  // launch of both kModeState and kModeTrans items 
 constexpr int kModeSeg = 6;   // launch of a segment plan (see chunk_segplan_kernel)
 // Segment plan (chunk_segplan_kernel) in the workspace, as 32-bit words: a header of kSegHdr
 // words ([0] items, [1] segment length X in 64-token chunks or 0 without segments, [2]
-// segments over all sequences, [3] correction units per head), then segbase[N + 1] (the
-// first segment of sequence n: its segments are slots segbase[n] .. segbase[n + 1] - 1),
-// corr_off[slots + 1] (the first correction unit of slot s) and two words per item:
-// ((n * H + h) << 2) | part, and (segment << 2) | kind.
+// segments over all sequences, [3] correction units per head, [4] rows of carried-back
+// queries per head), then segbase[N + 1] (the first segment of sequence n: its segments are
+// slots segbase[n] .. segbase[n + 1] - 1), corr_off[cap + 1] (the first correction unit of
+// slot s), qoff[cap + 1] (the first carried-back-query row of slot s) and two words per
+// item: ((n * H + h) << 2) | part, and (segment << 2) | kind. cap is the slot capacity the
+// workspace was laid out for (ChunkArgs::seg_slots).
 constexpr int kSegWhole = 0, kSegFirst = 1, kSegZero = 2, kSegTrans = 3;  // item kinds
 constexpr int kSegHdr = 8;
 __host__ __device__ inline size_t segplan_corr_off(int N) { return kSegHdr + (size_t)N + 1; }
-__host__ __device__ inline size_t segplan_items_off(int N, int slots) {
-  return segplan_corr_off(N) + (size_t)slots + 1;
+__host__ __device__ inline size_t segplan_qoff_off(int N, int cap) {
+  return segplan_corr_off(N) + (size_t)cap + 1;
+}
+__host__ __device__ inline size_t segplan_items_off(int N, int cap) {
+  return segplan_qoff_off(N, cap) + (size_t)cap + 1;
 }
 
 #ifndef KDA_STATE_PRIO
 #define KDA_STATE_PRIO 3
 #endif
+
 
 
 // Operands of 64 tokens, written by the prep wavefronts and read by the state wavefronts.
@@ -104,6 +110,7 @@ static_assert(sizeof(Stage) % 16 == 0 && offsetof(Stage, kcT) % 16 == 0 &&
                   offsetof(Smem, ost) % 16 == 0,
               "vector LDS accesses need 16-byte aligned arrays");
 static_assert((kLDK * 2) % 16 == 0 && (kLDT * 2) % 16 == 0, "row pitch must keep alignment");
+
 
 
 
@@ -225,6 +232,27 @@ __device__ __forceinline__ void load_gates(float (&ww)[4], rsrc_t w, uint32_t of
   for (int e = 0; e < 4; ++e) ww[e] = ld_b32(w, off + e * DV * 4);
 }
 
+// Values of block I as the A operand of a 16x16x32 product: lane (r, p) holds token
+// 16 I + r, the VW = 32 / (4 / NT) value columns cbase + VW p .. of this wavefront (NT = 2:
+// 16 bytes; NT = 1: 8 bytes and four zeros). One row piece per lane instead of 4 NT
+// two-byte loads in the accumulator layout; the product with a -1 selector (vsel) turns it
+// into -V in the accumulator layout, onto which (K P) S accumulates.
+template <int NT, int DV>
+__device__ __forceinline__ bf16x8 load_vrow(rsrc_t v, uint32_t off) {
+  if constexpr (NT == 2) return __builtin_bit_cast(bf16x8, ld_b128(v, off));
+  else return cat8(ld_b64(v, off), bf16x4{});
+}
+// The selector of value tile c: B[8 p + i][r] = -1 where the lane's column VW p + i is the
+// tile's column 16 c + r.
+template <int NT>
+__device__ __forceinline__ bf16x8 vsel(int c, int rr, int p) {
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    b[i] = static_cast<bf16>(i < 4 * NT && 4 * NT * p + i == 16 * c + rr ? -1.f : 0.f);
+  return b;
+}
+
 // Stores the outputs of chunk `step` that this state wavefront staged in LDS (its 16 nt
 // columns from cbase, 64 token rows) as 16-byte row pieces; rows past the chain are dropped.
 template <int DV>
@@ -256,19 +284,19 @@ __device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int s
 //              is the query carried back to the segment start (M_t^T q_t, M_t the product of
 //              the token maps up to t), dk values per token, so that the output from any start
 //              state S is S^T M_t^T q_t plus the output from the zero state.
-// Outputs go to obase (rows of DV values laid out as o).
+// Outputs go to rows orow0 .. of obase (DV values per row).
 template <int NT, int DV, bool GDR2, int MODE>
 __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const TokenRange& tr,
                                            size_t row0, const float* s0p, float* sTp,
                                            size_t hist_off, int nsteps, int cbase, int lane,
-                                           int rr, int p, void* obase) {
+                                           int rr, int p, void* obase, size_t orow0) {
   constexpr bool HIST = MODE == kModeHist;
   constexpr bool OUT = MODE == kModeOut || MODE == kModeTransOut;
   constexpr bool TRANS = MODE == kModeTrans || MODE == kModeTransOut;
   // (the transition reads no values: a zero-sized view returns zeros)
   const rsrc_t vsrc = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV,
                                 TRANS ? 0u : (uint32_t)tr.len * DV * 2);
-  const rsrc_t odst = make_rsrc(static_cast<bf16*>(obase) + (OUT ? row0 * DV : 0),
+  const rsrc_t odst = make_rsrc(static_cast<bf16*>(obase) + (OUT ? orow0 * DV : 0),
                                 OUT ? (uint32_t)tr.len * DV * 2 : 0u);
   const rsrc_t hdst = make_rsrc(static_cast<char*>(a.hist) + (HIST ? hist_off : 0),
                                 HIST ? (uint32_t)nsteps * 4 * kDK * DV * 2 : 0);
@@ -291,16 +319,32 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
         S_acc[c][m][e] = TRANS ? (ch == col[c] ? 1.f : 0.f)
                                : (s0p ? s0p[(size_t)ch * DV + col[c]] : 0.f);
       }
-  bf16 vv[NT][4][4];
-  float ww[NT][4][4];  // write gate of the values (Gated Delta Rule-2 only)
   const rsrc_t wsrc = GDR2 ? make_rsrc(a.write + row0 * DV, (uint32_t)tr.len * DV * 4) : vsrc;
+  // KDA: value row pieces of the four blocks (token 16 I + rr at vrow + I * 16 DV * 2 bytes)
+  // and the selectors that turn them into -V; Gated Delta Rule-2: values and write gates in
+  // the accumulator layout (w * V is formed on the vector ALU)
+  constexpr bool VSEL = !GDR2;
+  const uint32_t vrow = (uint32_t)(rr * DV + cbase + 4 * NT * p) * 2;
+  bf16x8 va[4];
+  bf16x8 sel[NT];
+  bf16 vv[NT][4][4];
+  float ww[NT][4][4];
+  if constexpr (VSEL) {
 #pragma unroll
-  for (int c = 0; c < NT; ++c)
+    for (int c = 0; c < NT; ++c) sel[c] = vsel<NT>(c, rr, p);
+    if constexpr (!TRANS) {
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      load_values<DV>(vv[c][I], vsrc, voff[c] + I * 16 * DV * 2);
-      if (GDR2) load_gates<DV>(ww[c][I], wsrc, 2 * (voff[c] + I * 16 * DV * 2));
+      for (int I = 0; I < 4; ++I) va[I] = load_vrow<NT, DV>(vsrc, vrow + I * 16 * DV * 2);
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        load_values<DV>(vv[c][I], vsrc, voff[c] + I * 16 * DV * 2);
+        if (GDR2) load_gates<DV>(ww[c][I], wsrc, 2 * (voff[c] + I * 16 * DV * 2));
+      }
+  }
   // the initial state must be in registers before the loop, or the loop would wait
   // for these loads on every pass
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -318,6 +362,11 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
       f32x4 X[NT], Ot[NT];
 #pragma unroll
       for (int c = 0; c < NT; ++c) X[c] = Ot[c] = zero4();
+      // KDA: X starts as -V, so that the chain below leaves X - V
+      if constexpr (VSEL && !TRANS) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) X[c] = mfma32(va[I], sel[c], X[c]);
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][32 * ks + 8 * p]);
@@ -340,17 +389,30 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
       const bf16x4 aI = *reinterpret_cast<const bf16x4*>(&st.aqk[I][rr][4 * p]);
       // V' = Tm Diag(beta) (V - X)
       bf16x4 vp[NT];
+      if constexpr (VSEL) {
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        f32x4 R;
+        for (int c = 0; c < NT; ++c) {
+          f32x4 R;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          R[e] = GDR2 ? ww[c][I][e] * static_cast<float>(vv[c][I][e]) - X[c][e]
-                      : bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
-        vp[c] = pack4(R);
-        // the next 64 tokens' values of this block
-        load_values<DV>(vv[c][I], vsrc, voff[c] + cbyte + (I * 16 + kC) * DV * 2);
-        if (GDR2) load_gates<DV>(ww[c][I], wsrc, 2 * (voff[c] + cbyte + (I * 16 + kC) * DV * 2));
+          for (int e = 0; e < 4; ++e) R[e] = -bt[e] * X[c][e];
+          vp[c] = pack4(R);
+        }
+        if constexpr (!TRANS)  // the next 64 tokens' values of this block
+          va[I] = load_vrow<NT, DV>(vsrc, vrow + cbyte + (I * 16 + kC) * DV * 2);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          f32x4 R;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            R[e] = GDR2 ? ww[c][I][e] * static_cast<float>(vv[c][I][e]) - X[c][e]
+                        : bt[e] * (static_cast<float>(vv[c][I][e]) - X[c][e]);
+          vp[c] = pack4(R);
+          // the next 64 tokens' values of this block
+          load_values<DV>(vv[c][I], vsrc, voff[c] + cbyte + (I * 16 + kC) * DV * 2);
+          if (GDR2)
+            load_gates<DV>(ww[c][I], wsrc, 2 * (voff[c] + cbyte + (I * 16 + kC) * DV * 2));
+        }
       }
 #pragma unroll
       for (int c = 0; c < NT; ++c) vp[c] = pack4(mfma16(tI, vp[c], zero4()));
@@ -476,6 +538,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
   // twice, from the zero state (outputs and end state) and as its transition (carried-back
   // queries and the dk x dk transition), and its outputs are completed afterwards.
   void* obase = a.o;
+  size_t qrow = 0;  // transitions: the first row of the carried-back queries they write
   if constexpr (MODE == kModeSeg) {
     if (skind != kSegWhole) {
       const int xt = (int)a.plan[1] * kC;
@@ -494,11 +557,13 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
       } else {
         s0p = nullptr;
         sTp = a.seg_mats + per + (slot * a.H + h) * msz;         // A: the transition
-        obase = a.qt;
+        obase = a.qt;                                            // Qt: rows of head h
+        qrow = (size_t)h * a.plan[4] + a.plan[segplan_qoff_off(a.N, a.seg_slots) + slot];
       }
     }
   }
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
+  const size_t orow0 = obase == a.o ? row0 : qrow;
   const size_t hist_off = HIST ? hist_chain_offset(a, n, h, tr) : 0;
   const int nsteps = (tr.len + kC - 1) / kC;
 
@@ -534,10 +599,10 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     if constexpr (MODE == kModePair) {  // whole items only
       if (kind == kModeTrans)
         state_role<NT, DV, GDR2, kModeTrans>(sm, a, tr, row0, s0p, sTp, 0, nsteps, 16 * NT * j,
-                                             lane, rr, p, nullptr);
+                                             lane, rr, p, nullptr, 0);
       else
         state_role<NT, DV, GDR2, kModeState>(sm, a, tr, row0, s0p, sTp, 0, nsteps, 16 * NT * j,
-                                             lane, rr, p, nullptr);
+                                             lane, rr, p, nullptr, 0);
       return;
     }
     // segment plans: the transition items, then whole or half output items
@@ -545,7 +610,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     if constexpr (MODE == kModeSeg) {
       if (skind == kSegTrans) {
         state_role<NT, DV, GDR2, kModeTransOut>(sm, a, tr, row0, s0p, sTp, 0, nsteps,
-                                                16 * NT * j, lane, rr, p, obase);
+                                                16 * NT * j, lane, rr, p, obase, orow0);
         return;
       }
     }
@@ -553,12 +618,12 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
       if (part) {  // a half item: NT / 2 tiles per wavefront over one half of the columns
         state_role<NT / 2, DV, GDR2, RMODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps,
                                             (part == 2 ? DV / 2 : 0) + 16 * (NT / 2) * j, lane,
-                                            rr, p, obase);
+                                            rr, p, obase, orow0);
         return;
       }
     }
     state_role<NT, DV, GDR2, RMODE>(sm, a, tr, row0, s0p, sTp, hist_off, nsteps, 16 * NT * j,
-                                    lane, rr, p, obase);
+                                    lane, rr, p, obase, orow0);
   }
 }
 
@@ -728,8 +793,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* x
   return before + incl - v;
 }
 
+// The plan is laid out for slots_max slots (the workspace's capacity); a candidate segment
+// length is allowed only when its slots fit that capacity (and mats_ok: the workspace holds
+// the matrices of every slot) and its carried-back queries fit qt_rows rows per head.
 __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
-    const int32_t* cu, int N, int H, int T, int cus, int slots_max, int xc_min, uint32_t* plan) {
+    const int32_t* cu, int N, int H, int T, int cus, int slots_max, int mats_ok,
+    long long qt_rows, int xc_min, uint32_t* plan) {
   __shared__ int cl[kMaxPlanSeqs];     // chunks of sequence n
   __shared__ int ln[kMaxPlanSeqs];     // tokens of sequence n
   __shared__ int key[kMaxPlanSeqs];    // entries: chunks
@@ -743,6 +812,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
   const int t = threadIdx.x;
   uint32_t* segbase = plan + kSegHdr;
   uint32_t* corr_off = plan + segplan_corr_off(N);
+  uint32_t* qoff = plan + segplan_qoff_off(N, slots_max);
   uint32_t* items = plan + segplan_items_off(N, slots_max);
   int c = -1;
   if (t < N) {
@@ -764,8 +834,8 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
   {
     const int xc = xc_min + t * step;
     float b = 3.0e38f;
-    if (xc < maxc) {
-      long long total = 0, corr = 0, slots = 0;
+    if (mats_ok && xc < maxc) {
+      long long total = 0, corr = 0, slots = 0, later = 0;
       int longest = 0, most = 1;
       for (int i = 0; i < N; ++i) {
         const int ci = cl[i];
@@ -775,9 +845,10 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
         most = max(most, ns_i);
         total += ci + extra;
         corr += extra;
+        later += ci > xc ? ln[i] - xc * kC : 0;  // tokens past the first segment
         longest = max(longest, min(ci, xc));
       }
-      if (slots <= slots_max && slots <= kMaxPlanSeqs)
+      if (slots <= slots_max && slots <= kMaxPlanSeqs && later <= qt_rows)
         b = fmaxf((float)longest, kSegPacking * H * total / cus) +
             kSegCorrCost * H * corr / cus + kSegFixedCost + kSegChainCost * (most - 1);
     }
@@ -849,6 +920,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
       plan[0] = off;
       plan[2] = 0;
       plan[3] = 0;
+      plan[4] = 0;
     }
   }
   __syncthreads();
@@ -884,6 +956,18 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
       corr_off[slots] = ent_off[kMaxPlanSeqs];
       plan[2] = (uint32_t)slots;
       plan[3] = ent_off[kMaxPlanSeqs];
+    }
+    // rows of carried-back queries of every slot (later segments only), in slot order
+    uint32_t qrows = 0;
+    if (t < slots && eb[t] > 0) {
+      const int len = ln[ea[t]], k = eb[t];
+      qrows = (uint32_t)min(xc * kC, len - k * xc * kC);
+    }
+    const uint32_t qo = block_exclusive_scan(qrows, ent_off);
+    if (t < slots) qoff[t] = qo;
+    if (t == 0) {
+      qoff[slots] = ent_off[kMaxPlanSeqs];
+      plan[4] = ent_off[kMaxPlanSeqs];
     }
     __syncthreads();
     int m2 = 1;
@@ -1148,7 +1232,10 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
     if (k < 1 || g0 >= seg_end) continue;  // uniform over the workgroup
     const int len = min(kSegGroup, seg_end - g0);
     const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + g0;
-    const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.qt) + row0 * kDK, (uint32_t)len * kDK * 2);
+    // the unit's carried-back queries: rows of head h from the slot's first row
+    const size_t qrow0 = (size_t)h * plan[4] + plan[segplan_qoff_off(a.N, a.seg_slots) + sl] +
+                         (size_t)(g0 - k * xt);
+    const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.qt) + qrow0 * kDK, (uint32_t)len * kDK * 2);
     const rsrc_t os = make_rsrc(static_cast<bf16*>(a.o) + row0 * kDK, (uint32_t)len * kDK * 2);
     const float* S = a.seg_mats + ((size_t)sl * a.H + h) * msz;
     __syncthreads();  // the previous unit's reads of sa are done
@@ -1252,42 +1339,91 @@ size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus) {
 }
 
 // Segment plans: the shortest segment (64-token chunks), at least 512 tokens and at most 64
-// segments per T tokens, and the capacity in segments that covers every candidate length
-// of the planner for packed sequences (equal-length batches take only those that fit).
+// segments per T tokens, and the most slots any candidate of the planner can use.
 static int segplan_xc_min(int T) {
   const int ct = (T + kC - 1) / kC;
   return std::max(8, (ct + 63) / 64);
 }
 static int segplan_slots(int N, int T) {
   const int ct = (T + kC - 1) / kC;
-  return N + N / 8 + (ct + segplan_xc_min(T) - 1) / segplan_xc_min(T) + 1;
+  return std::min(kMaxPlanSeqs, N + N / 8 + (ct + segplan_xc_min(T) - 1) / segplan_xc_min(T) + 1);
 }
-static size_t segplan_plan_bytes(int N, int H, int T) {
-  const int sm = segplan_slots(N, T);
-  return (4 * (segplan_items_off(N, sm) + 4 * (size_t)H * sm) + 255) / 256 * 256;
+// Bytes of the plan words for a capacity of cap slots (up to 2 H items per slot).
+static size_t segplan_plan_bytes(int N, int H, int cap) {
+  return (4 * (segplan_items_off(N, cap) + 4 * (size_t)H * cap) + 255) / 256 * 256;
+}
+static size_t segplan_mats_bytes(int H, int cap) { return (size_t)3 * cap * H * kDK * kDK * 4; }
+
+// Slots worth planning for: every sequence plus about one extra segment per compute unit and
+// head (cutting beyond that only adds rounds of items).
+static int segplan_cap(int N, int H, int T, int cus) {
+  return std::max(N, std::min(segplan_slots(N, T), N + (cus + H - 1) / H + 1));
 }
 
-size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed) {
+// Layout of a segment plan in ws_bytes of workspace: the slot capacity (up to segplan_cap
+// slots whose plan words and matrices fit, at least N so that the halves work list always
+// fits), whether the matrices fit at all, and the rows of carried-back queries per head that
+// the rest holds.
+struct SegLayout {
+  int cap = 0;
+  bool mats_ok = false;
+  long long qt_rows = 0;
+};
+static bool segplan_layout(int N, int H, int T, int cus, size_t ws_bytes, SegLayout& L) {
+  if (N <= 0 || N > kMaxPlanSeqs || H <= 0 || ws_bytes < segplan_plan_bytes(N, H, N)) return false;
+  L = SegLayout{};
+  L.cap = N;
+  for (int cap = segplan_cap(N, H, T, cus); cap >= N; --cap) {
+    if (segplan_plan_bytes(N, H, cap) + segplan_mats_bytes(H, cap) <= ws_bytes) {
+      L.cap = cap;
+      L.mats_ok = true;
+      break;
+    }
+  }
+  if (L.mats_ok) {
+    const size_t used = segplan_plan_bytes(N, H, L.cap) + segplan_mats_bytes(H, L.cap);
+    L.qt_rows = (long long)((ws_bytes - used) / ((size_t)H * kDK * 2));
+  }
+  return true;
+}
+
+size_t chunk_segplan_min_bytes(int N, int H, int T, int dv) {
   if (dv != kDK || N <= 0 || N > kMaxPlanSeqs || H <= 0) return 0;
-  const size_t sm = (size_t)segplan_slots(N, T);
-  return segplan_plan_bytes(N, H, T) + 3 * sm * H * kDK * kDK * 4 +
-         (packed ? (size_t)1 : (size_t)N) * H * T * kDK * 2;
+  (void)T;
+  return segplan_plan_bytes(N, H, N);
+}
+
+// The workspace kda_chunk_fwd_workspace_size recommends: segplan_cap slots, and carried-back
+// queries for the whole T axis of every sequence when the chains are fewer than the compute
+// units (every sequence is then cut), else for a quarter of it (only the sequences much
+// longer than the average are cut).
+size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed, int cus) {
+  if (chunk_segplan_min_bytes(N, H, T, dv) == 0) return 0;
+  const int cap = segplan_cap(N, H, T, cus);
+  const long long chains = (long long)N * H;
+  const long long rows = chains < cus ? (packed ? (long long)T : (long long)N * T)
+                                      : ((long long)T + 3) / 4;
+  return segplan_plan_bytes(N, H, cap) + segplan_mats_bytes(H, cap) +
+         (size_t)rows * H * kDK * 2;
 }
 
 hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, void* ws,
-                                     hipStream_t stream) {
+                                     size_t ws_bytes, hipStream_t stream) {
   ChunkArgs a = args;
-  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.dv != kDK || !ws || a.N > kMaxPlanSeqs)
+  SegLayout L;
+  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.dv != kDK || !ws ||
+      !segplan_layout(a.N, a.H, a.T, a.cus, ws_bytes, L))
     return hipErrorInvalidValue;
-  const int sm = segplan_slots(a.N, a.T);
+  const int sm = L.cap;
   a.plan = static_cast<uint32_t*>(ws);
   a.seg_slots = sm;
-  a.seg_mats = reinterpret_cast<float*>(static_cast<char*>(ws) + segplan_plan_bytes(a.N, a.H, a.T));
+  a.seg_mats = reinterpret_cast<float*>(static_cast<char*>(ws) + segplan_plan_bytes(a.N, a.H, sm));
   a.qt = a.seg_mats + (size_t)3 * sm * a.H * kDK * kDK;
   a.seg_len = 0;
   a.nseg = 1;
   a.split_all = 0;
   chunk_segplan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, sm,
+                                                       L.mats_ok ? 1 : 0, L.qt_rows,
                                                        segplan_xc_min(a.T), a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -40,7 +40,8 @@ struct ChunkArgs {
   int nseg;
   // Segment plans (launch_chunk_mfma_segplan): capacity in segments, the start states,
   // transitions and zero-start end states of the segments (fp32, seg_slots x H matrices
-  // each), and the carried-back queries (bf16, laid out as q).
+  // each), and the carried-back queries (bf16 rows of dk values: per head, one row per token
+  // past the first segment of its sequence).
   int seg_slots;
   float* seg_mats;
   void* qt;
@@ -124,11 +125,14 @@ void chunk_seg_config(int N, int H, int T, int dv, int cus, int& seg_len, int& n
 size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus);
 hipError_t launch_chunk_mfma_segmented(const ChunkArgs& a, bool per_channel, void* ws,
                                        hipStream_t stream);
-// Segment plan of the forward (dv = dk = 128, any gates): its workspace
-// bytes (0 when not available) and the launches (planner, items, segment chain, corrections).
-size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed);
+// Segment plan of the forward (dv = dk = 128, any gates): the launches (planner, items,
+// segment chain, corrections). chunk_segplan_bytes is the recommended workspace,
+// chunk_segplan_min_bytes the smallest one the plan runs in (0 when not available: then only
+// its work list fits); launch_chunk_mfma_segplan plans within ws_bytes.
+size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed, int cus);
+size_t chunk_segplan_min_bytes(int N, int H, int T, int dv);
 hipError_t launch_chunk_mfma_segplan(const ChunkArgs& a, bool per_channel, void* ws,
-                                     hipStream_t stream);
+                                     size_t ws_bytes, hipStream_t stream);
 
 // Backward pass (bf16, dk = 128, dv in {64, 128}, one decay per channel or per head).
 bool chunk_bwd_supports(int dk, int dv, int T);
@@ -141,5 +145,26 @@ hipError_t launch_chunk_mfma_hist(const ChunkArgs& a, bool per_channel, hipStrea
 // first; a.plan, a.cu set).
 hipError_t launch_chunk_plan(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool per_channel, hipStream_t stream);
+
+// KDA_DEBUG builds: the value preconditions of one call (up to four float arrays, each with
+// its range and flag bit, and cu_seqlens), checked on the device before the work;
+// debug_check waits for the check on `stream` and returns the violated bits in `flags`.
+struct DebugCheck {
+  static constexpr unsigned kG = 1, kBeta = 2, kErase = 4, kWrite = 8, kCu = 16;
+  const float* arr[4] = {nullptr, nullptr, nullptr, nullptr};
+  long long n[4] = {0, 0, 0, 0};
+  float lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
+  unsigned bit[4] = {0, 0, 0, 0};
+  const int32_t* cu = nullptr;
+  int N = 0, T = 0;
+  void add(const float* p, long long count, float l, float h, unsigned b) {
+    for (int i = 0; i < 4; ++i)
+      if (!arr[i]) {
+        arr[i] = p; n[i] = count; lo[i] = l; hi[i] = h; bit[i] = b;
+        return;
+      }
+  }
+};
+hipError_t debug_check(const DebugCheck& c, hipStream_t stream, unsigned& flags);
 
 }  // namespace kda

@@ -21,17 +21,28 @@
  *    calls are asynchronous: a KDA_OK return means "enqueued". Its only global state is a
  *    per-device cache of the compute-unit count and, from the first kda_chunk_bwd /
  *    kda_gdr2_chunk_bwd call on a device, one more stream of that device (default
- *    priority, kept until the process ends): the backward forks part of its work onto it
- *    with an event recorded on `stream` and joins it back before returning, so all of a
- *    call's work still completes in `stream` order.
+ *    priority, non-blocking, created under a lock and kept until the process ends). The
+ *    backward's state-history pass and its reverse carry are independent, and running them
+ *    side by side shortens the call; the library keeps that stream rather than take a
+ *    second stream argument in every backward entry point for this one use. Each call forks
+ *    onto it with an event recorded on `stream` and joins back with a second event before
+ *    its last launch (both events belong to the call and are destroyed on every return
+ *    path), so all of a call's work still completes in `stream` order.
  *  - Argument errors are detected on the host before anything is launched and are
  *    returned as a status; no exception crosses the ABI. A failed launch returns
  *    KDA_ERR_HIP.
- *  - Preconditions that the host cannot see without reading device memory are not
- *    checked and are undefined if violated: g in [-5, 0] (the lower bound of the
- *    log-decay; the kernels rely on it for the exponent ranges of their scaled
- *    operands), beta in [0, 1], cu_seqlens non-decreasing from 0 to T. Out-of-range
- *    cu_seqlens entries are clamped to [0, T] so that no access leaves the buffers.
+ *  - Preconditions that the host cannot see without reading device memory: g in [-5, 0]
+ *    (the lower bound g_min = -5 of KDA's log-decay, page "【轻量化复刻大模型】线性注意力
+ *    （Linear Attention）", section 3.1; the kernels rely on it for the exponent ranges of
+ *    their scaled operands), beta and the Gated Delta Rule-2 erase / write gates in [0, 1],
+ *    cu_seqlens non-decreasing from 0 to T (cu_seqlens[0] = 0, cu_seqlens[num_seqs] = T).
+ *    Release builds (libkda.so) do not check them and the results are undefined if they are
+ *    violated; out-of-range cu_seqlens entries are clamped to [0, T] so that no access leaves
+ *    the buffers. KDA_DEBUG builds (libkda_debug.so, `build.py --debug`) check them in every
+ *    forward, decode and backward entry point: a kernel on `stream` scans g, beta or the
+ *    gates (every element of the arrays as passed) and cu_seqlens, the host waits for it
+ *    (the call synchronises `stream`, so it cannot be captured in a HIP graph), and a
+ *    violation returns KDA_ERR_PRECONDITION without launching the work.
  *  - Buffers may not alias each other, except initial_state with final_state.
  */
 #ifndef KDA_H
@@ -49,7 +60,8 @@ typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1,  /* NULL required pointer, non-positive size, inconsistent shape */
   KDA_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement (e.g. dk = 96) */
-  KDA_ERR_HIP = 3           /* a HIP runtime error while launching */
+  KDA_ERR_HIP = 3,          /* a HIP runtime error while launching */
+  KDA_ERR_PRECONDITION = 4  /* KDA_DEBUG builds only: an input value outside its stated range */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;   /* element type of q, k, v and o */
@@ -60,41 +72,51 @@ typedef enum {
 } kda_gate_mode;
 
 /*
- * Bytes of device workspace kda_chunk_fwd uses for this problem on the current device
- * (bf16 matrix-core path, dk = 128; every other case returns 0). Three uses:
+ * Bytes of device workspace that kda_chunk_fwd recommends for this problem on the current
+ * device (bf16 matrix-core path, dk = 128; every other case returns 0). num_seqs > 0 describes
+ * a packed call (cu_seqlens set, B = 1; any other B returns 0), num_seqs = 0 a batch of B
+ * sequences of T tokens. kda_chunk_fwd plans within whatever workspace it is given: any size
+ * from the work list's (below) up is accepted; the recommended size lets it cut long
+ * sequences as it sees fit, a smaller one may make it cut fewer or none. Three uses:
  *
  *  - dv = dk = 128 with packed sequences (num_seqs in 1 .. 1024), or equal-length batches
  *    with fewer chains (B * H) than compute units: the segment plan. A planning kernel
  *    reads the sequence lengths on the device and picks a segment length X (a multiple of
  *    64 tokens, at least max(512, 64 * ceil(T / 4096)) tokens) when cutting the longest
- *    sequences lowers the launch's critical path; otherwise it builds the work list
- *    described below. The first segment of a cut sequence runs from the initial state;
- *    every later segment runs twice at the same time, from the zero state (outputs O0, end
- *    state B) and from the identity (the dk x dk transition A of the segment, the product
- *    of its token maps, and the queries carried back to the segment start, Qt). The
- *    recurrence is linear in the state, so with S the segment's start state its outputs
- *    are O0 + Qt S and its end state A S + B: a chain over the segments gives every S and a
- *    correction pass adds Qt S. Results equal the whole-chain computation up to rounding.
- *    With C = ceil(T / 64), Xmin = max(8, ceil(C / 64)) and
- *    M = N + floor(N / 8) + ceil(C / Xmin) + 1 segments of capacity, the size is
- *    R(4 (N + M + 10 + 4 H M)) + 3 M H dk^2 * 4 + Q H T dk * 2 bytes, where R rounds up
- *    to a multiple of 256 and Q = 1 for packed sequences, B otherwise (the plan, the
- *    states and transitions, and Qt laid out as q). kda_gdr2_chunk_fwd takes the same
- *    plan (its recurrence is linear in the state too).
+ *    sequences lowers the launch's critical path and the segments fit the workspace;
+ *    otherwise it builds the work list described below. The first segment of a cut sequence
+ *    runs from the initial state; every later segment runs twice at the same time, from the
+ *    zero state (outputs O0, end state B) and from the identity (the dk x dk transition A of
+ *    the segment, the product of its token maps, and the queries carried back to the segment
+ *    start, Qt). The recurrence is linear in the state, so with S the segment's start state
+ *    its outputs are O0 + Qt S and its end state A S + B: a chain over the segments gives
+ *    every S and a correction pass adds Qt S. Results equal the whole-chain computation up
+ *    to rounding. The workspace holds the plan words, three fp32 dk x dk matrices per segment
+ *    slot and head, and one bf16 row of dk carried-back queries per head and token past the
+ *    first segment of its sequence. With C = ceil(T / 64), Xmin = max(8, ceil(C / 64)),
+ *    M = min(1024, N + floor(N / 8) + ceil(C / Xmin) + 1) and cus the compute units, the
+ *    recommendation is S = max(N, min(M, N + ceil(cus / H) + 1)) slots and Q rows per head,
+ *    Q = T for packed sequences and B T otherwise when N H < cus, else Q = ceil(T / 4):
+ *    R(4 (N + 2 S + 11 + 4 H S)) + 3 S H dk^2 * 4 + Q H dk * 2 bytes, R rounding up to a
+ *    multiple of 256 (230 MiB for 8 packed sequences, H = 32, T = 65536). Given another
+ *    size, the plan takes as many of the S slots as fit with their matrices, and the rest for
+ *    carried-back queries. kda_gdr2_chunk_fwd takes the same plan (its recurrence is linear
+ *    in the state too).
  *  - Otherwise, few chains for the device (N * H chains, two workgroups each at dv = 128,
  *    fewer than the compute units) and sequences of at least 1024 tokens: every sequence
  *    is cut into P segments of L tokens (P = CUs / (2 N H) or CUs / (N H) at dv = 64,
  *    L >= 512 a multiple of 64); each segment but the last gets B and A as above,
  *    S_{s+1} = A_s S_s + B_s gives every start state, then all segments compute their
- *    outputs in parallel. Workspace: N H P (2 dk dv + dk^2) * 4 bytes. Not used by
- *    kda_gdr2_chunk_fwd.
+ *    outputs in parallel. Workspace: N H P (2 dk dv + dk^2) * 4 bytes (a smaller workspace
+ *    runs without these segments). Not used by kda_gdr2_chunk_fwd.
  *  - Otherwise, packed sequences (num_seqs > 0, at most 1024): a work list of
  *    4 * (1 + 2 * num_seqs * H) bytes rounded up to 256, filled on the device by a small
  *    scheduling kernel: it splits the value columns of the longest sequences' chains over
  *    two workgroups and orders the work longest first, so that packed sequences of unequal
  *    length keep every compute unit busy. Work lists do not change results bit for bit:
- *    each value column is computed the same way. (Equal-length batches with enough chains
- *    need no workspace: their split is decided on the host.)
+ *    each value column is computed the same way. This is the smallest workspace a packed
+ *    call accepts. (Equal-length batches with enough chains need no workspace: their split
+ *    is decided on the host.)
  */
 size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num_seqs,
                                     kda_dtype dt);
@@ -122,12 +144,15 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  *                 axis (packed variable-length sequences); B must be 1 and N = num_seqs.
  *                 Tokens of o outside every sequence are left untouched.
  *   dk, dv        each 64 or 128 (anything else: KDA_ERR_UNSUPPORTED)
- *   workspace     device buffer of at least kda_chunk_fwd_workspace_size(...) bytes,
- *                 owned by the caller and not read before this call writes it; or
+ *   workspace     device buffer of workspace_bytes bytes, owned by the caller and not read
+ *                 before this call writes it (kda_chunk_fwd_workspace_size gives the
+ *                 recommended size; the call plans within any size it is given); or
  *                 workspace_bytes = 0 (workspace ignored) to run one workgroup per chain
- *                 in chain order. 0 < workspace_bytes < the size, or a NULL workspace
- *                 with workspace_bytes > 0: KDA_ERR_INVALID_ARG. Calls that overlap on
- *                 one workspace race.
+ *                 in chain order. With cu_seqlens, 0 < workspace_bytes < the work list's
+ *                 4 * (1 + 2 * num_seqs * H) bytes rounded up to 256 (num_seqs <= 1024), or
+ *                 a NULL workspace with workspace_bytes > 0: KDA_ERR_INVALID_ARG. Without
+ *                 cu_seqlens the batch rows are the sequences (num_seqs must be 0 or B).
+ *                 Calls that overlap on one workspace race.
  *
  * Arithmetic: state and accumulation in float32. With dt = KDA_BF16 the dense
  * contractions take bf16 operands on the matrix cores (float32 accumulate); with
@@ -224,7 +249,8 @@ kda_status kda_prologue(const void* q_in, const void* k_in, const float* u, cons
  *
  *   o_in, z, o_out  [B, H, T, dv], dtype dt; o_out may equal o_in
  *   weight          float32 [dv] (shared by the heads), or NULL for 1
- *   eps             finite, >= 0 (else KDA_ERR_INVALID_ARG)
+ *   eps             finite, > 0 (else KDA_ERR_INVALID_ARG): an all-zero row of o_in
+ *                   (a zero value or a token outside every packed sequence) maps to 0
  *   dv              64 or 128 (else KDA_ERR_UNSUPPORTED)
  * A NULL o_in, z or o_out, or any array not 16-byte aligned: KDA_ERR_INVALID_ARG.
  */

@@ -389,6 +389,9 @@ def pins_gates():
     _close(G.epilogue(o * 40.0, z, w, 0.0), G.epilogue(o, z, w, 0.0), 1e-12, "epilogue scale")
     y = G.epilogue(o, np.full_like(z, 50.0), np.ones(16), 0.0)
     _close(np.sqrt(np.mean(y * y, axis=-1)), np.ones(4), 1e-12, "epilogue unit RMS")
+    # an all-zero row with eps > 0 maps to exactly 0 (0 / sqrt(eps)), whatever the gate
+    y = G.epilogue(np.zeros((2, 16)), z[:2], w, 1e-6)
+    assert np.all(y == 0.0), "epilogue zero row"
 
 
 ALL_PINS = [

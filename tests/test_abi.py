@@ -35,26 +35,49 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(4):
+    for code in range(5):
         assert kda.kda_status_string(code).startswith("KDA_")
+    assert kda.kda_status_string(kda.KDA_ERR_PRECONDITION).startswith("KDA_ERR_PRECONDITION")
     assert "UNKNOWN" in kda.kda_status_string(99)
 
 
-def segment_plan_bytes(B, H, T, N, packed, dk=128):
-    """The segment plan's workspace as kda.h states it: plan words, the states and
-    transitions of M segments per head, and the carried-back queries laid out as q."""
+def test_debug_library_exports_every_declared_symbol():
+    """The KDA_DEBUG build (device-side precondition checks) has the same boundary."""
+    if not os.path.exists(kda.DEBUG_LIB_PATH):
+        from gated_delta_rule_13_amd.build import build
+        build(debug=True)
+    lib = kda.open_library(kda.DEBUG_LIB_PATH)
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.DEBUG_LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for sym in declared_symbols():
+        assert sym in exported, sym
+    assert lib.kda_status_string(kda.KDA_ERR_PRECONDITION).startswith(b"KDA_ERR_PRECONDITION")
+    # the host-side argument checks come first in the debug build too (nothing launches)
+    assert chunk_call_on(lib, q=None) == kda.KDA_ERR_INVALID_ARG
+    assert chunk_call_on(lib, dk=96) == kda.KDA_ERR_UNSUPPORTED
+
+
+def segment_plan_bytes(B, H, T, N, packed, dk=128, cus=256):
+    """The segment plan's recommended workspace as kda.h states it: plan words for a capacity
+    of S slots, the states and transitions of S segments per head, and rows of carried-back
+    queries per head (a whole T axis per sequence with fewer chains than compute units,
+    else a quarter of the T axis)."""
     C = -(-T // 64)
     xmin = max(8, -(-C // 64))
-    M = N + N // 8 + -(-C // xmin) + 1
-    plan = -(-4 * (N + M + 10 + 4 * H * M) // 256) * 256
-    return plan + 3 * M * H * dk * dk * 4 + (1 if packed else B) * H * T * dk * 2
+    S_all = min(1024, N + N // 8 + -(-C // xmin) + 1)
+    S = max(N, min(S_all, N + -(-cus // H) + 1))
+    words = 8 + (N + 1) + 2 * (S + 1) + 4 * H * S
+    plan = -(-4 * words // 256) * 256
+    rows = (T if packed else N * T) if N * H < cus else -(-T // 4)
+    return plan + 3 * S * H * dk * dk * 4 + rows * H * dk * 2
 
 
 def test_workspace_size():
     # (sizes for a 256-CU device; without a GPU the library assumes 256 compute units)
-    # dv = dk, packed sequences: the segment plan
+    # dv = dk, packed sequences: the segment plan (the T = 65536 workload: 230 MiB)
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 128, 128, 8, kda.KDA_BF16) == \
-        segment_plan_bytes(1, 32, 65536, 8, True) == 1002477056
+        segment_plan_bytes(1, 32, 65536, 8, True) == 241181440
     assert kda.kda_chunk_fwd_workspace_size(1, 4, 5000, 128, 128, 7, kda.KDA_BF16) == \
         segment_plan_bytes(1, 4, 5000, 7, True)
     # dv = dk, equal lengths with fewer chains than compute units: the segment plan
@@ -76,9 +99,21 @@ def test_workspace_size():
     assert kda.kda_chunk_fwd_workspace_size(1, 32, 65536, 64, 128, 8, kda.KDA_BF16) == 0
     assert kda.kda_chunk_fwd_workspace_size(1, 4, 65536, 128, 128, 1025, kda.KDA_BF16) == 0
     assert kda.kda_chunk_fwd_workspace_size(0, 4, 64, 128, 128, 0, kda.KDA_BF16) == 0
+    # num_seqs > 0 describes a packed call, which has B = 1: any other B gets no workspace
+    assert kda.kda_chunk_fwd_workspace_size(4, 1, 2048, 128, 128, 4, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_fwd_workspace_size(2, 4, 8192, 128, 128, 2, kda.KDA_BF16) == 0
 
 
 DUMMY = 0x1000  # never dereferenced: every call below is rejected on the host
+
+
+def chunk_call_on(lib, **over):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, beta=DUMMY, initial_state=None,
+                final_state=None, o=DUMMY, cu_seqlens=None, num_seqs=0, B=1, H=2, T=64,
+                dk=128, dv=128, dt=kda.KDA_BF16, gm=kda.KDA_GATE_PER_CHANNEL, workspace=None,
+                workspace_bytes=0, stream=None)
+    args.update(over)
+    return lib.kda_chunk_fwd(*args.values())
 
 
 def chunk_call(**over):
@@ -217,6 +252,7 @@ def epilogue_call(**over):
     (dict(z=None), kda.KDA_ERR_INVALID_ARG),
     (dict(o_out=None), kda.KDA_ERR_INVALID_ARG),
     (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=0.0), kda.KDA_ERR_INVALID_ARG),
     (dict(eps=float("nan")), kda.KDA_ERR_INVALID_ARG),
     (dict(eps=float("inf")), kda.KDA_ERR_INVALID_ARG),
     (dict(B=-1), kda.KDA_ERR_INVALID_ARG),

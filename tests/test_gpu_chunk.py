@@ -15,9 +15,9 @@ import torch
 
 import gated_delta_rule_13_amd as kda
 from kda_workloads import (GDN_B1_H16_T8192, KDA_B2_H16_T4096, KDA_VARLEN_H32_T65536,
-                           TINY_KDA_F32, make_chunk_inputs)
-from tests.gpu_util import (TOL, assert_close, check_chains, note, oracle_chains, run_chunk,
-                            up)
+                           TINY_KDA_F32, bf16_round, make_chunk_inputs)
+from tests.gpu_util import (TOL, assert_close, check_chains, dev, note, oracle_chains,
+                            run_chunk, up)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,58 @@ def test_varlen_t65536_all_chains():
                               f"{cfg.name} heads {h0}..{h0 + 7}")
         worst = (max(worst[0], eo), max(worst[1], es))
     print(f"{cfg.name}: all {x.n_seqs * cfg.H} chains, err o={worst[0]:.2e} S={worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("ws_kind", ["work_list", "64MiB", "recommended", "1GiB"])
+def test_varlen_t65536_within_given_workspace(ws_kind):
+    """The packed varlen T = 65536 workload through the C ABI with workspaces of several sizes:
+    the work list's size (the smallest accepted: no segments), 64 MiB (too small for the
+    segments' matrices: the halves work list), the recommended size and 1 GiB (segments).
+    Every call plans within what it is given; 8 heads of every sequence match the oracle."""
+    cfg = KDA_VARLEN_H32_T65536
+    x = make_chunk_inputs(cfg)
+    dt = torch.bfloat16
+    q, k, v, g, beta = up(x.q, dt), up(x.k, dt), up(x.v, dt), up(x.g), up(x.beta)
+    cu = up(x.cu_seqlens, torch.int32)
+    B, H, T, dk = x.q.shape
+    dv = x.v.shape[-1]
+    N = x.n_seqs
+    rec = kda.kda_chunk_fwd_workspace_size(B, H, T, dk, dv, N, kda.KDA_BF16)
+    sizes = {"work_list": 4 * (1 + 2 * N * H), "64MiB": 64 << 20, "recommended": rec,
+             "1GiB": 1 << 30}
+    nbytes = -(-sizes[ws_kind] // 256) * 256
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev())
+    o = torch.full(tuple(x.v.shape), float("nan"), dtype=dt, device=dev())
+    sT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev())
+    note(f"chunk varlen T65536 with a {ws_kind} workspace ({nbytes} bytes)")
+    st = kda.kda_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                           beta.data_ptr(), None, sT.data_ptr(), o.data_ptr(), cu.data_ptr(), N,
+                           B, H, T, dk, dv, kda.KDA_BF16, kda.KDA_GATE_PER_CHANNEL,
+                           ws.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+    assert st == kda.KDA_OK, kda.kda_status_string(st)
+    torch.cuda.synchronize()
+    of = o.float().cpu().numpy()
+    assert np.all(np.isfinite(of)), "some output position was not written"
+    chains = [(n, h) for n in range(N) for h in range(0, H, 4)]
+    check_chains(x, of, sT.cpu().numpy(), oracle_chains(x, chains, initial_state=False),
+                 TOL["bf16"], f"varlen T65536, {ws_kind} workspace")
+
+
+def test_workspace_below_the_work_list_is_rejected():
+    """A packed call with a workspace below its work list's size is an argument error."""
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=4096)
+    x = make_chunk_inputs(cfg)
+    dt = torch.bfloat16
+    q, k, v, g, beta = up(x.q, dt), up(x.k, dt), up(x.v, dt), up(x.g), up(x.beta)
+    cu = up(x.cu_seqlens, torch.int32)
+    B, H, T, dk = x.q.shape
+    o = torch.empty(tuple(x.v.shape), dtype=dt, device=dev())
+    ws = torch.empty(64, dtype=torch.uint8, device=dev())
+    st = kda.kda_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                           beta.data_ptr(), None, None, o.data_ptr(), cu.data_ptr(), x.n_seqs,
+                           B, H, T, dk, dk, kda.KDA_BF16, kda.KDA_GATE_PER_CHANNEL,
+                           ws.data_ptr(), 64, torch.cuda.current_stream().cuda_stream)
+    assert st == kda.KDA_ERR_INVALID_ARG
 
 
 SMALL = []
@@ -113,6 +165,29 @@ def test_single_token(dtype):
     note(f"chunk T=1 {dtype}")
     o, sT = run_chunk(x, dtype)
     check_chains(x, o, sT, oracle_chains(x), TOL[dtype], f"T=1 {dtype}")
+
+
+@pytest.mark.parametrize("mode", ["channel", "head", "gdr2"])
+def test_correlated_keys(mode, norm=1.0):
+    """Unit keys that point nearly the same way (a shared direction plus small noise) make
+    the strictly lower part N of a block's (I + N) large (up to about 0.9), so the terms of
+    the block inverse's product form grow and cancel; the results must still match the
+    oracle."""
+    cfg = KDA_B2_H16_T4096.replace(B=1, H=3, T=333, seed=31, gate="head" if mode == "head"
+                                   else "channel", gates="gdr2" if mode == "gdr2" else "beta")
+    x = make_chunk_inputs(cfg)
+    rng = np.random.default_rng(99)
+    base = rng.standard_normal((1, cfg.H, 1, cfg.dk))
+    kk = base + 0.25 * rng.standard_normal(x.k.shape)
+    kk = norm * kk / np.linalg.norm(kk, axis=-1, keepdims=True)
+    x.k[...] = bf16_round(kk.astype(np.float32))
+    if mode == "gdr2":
+        x.erase[...] = np.maximum(x.erase, 0.9)
+    else:
+        x.beta[...] = np.maximum(x.beta, 0.8)
+    note(f"chunk correlated keys |k| = {norm}, {mode}")
+    o, sT = run_chunk(x, "bf16")
+    check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], f"correlated keys {mode} {norm}")
 
 
 def test_split_resume_and_aliasing():
