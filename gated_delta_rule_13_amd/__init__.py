@@ -34,7 +34,8 @@ KDA_GATE_PER_CHANNEL, KDA_GATE_PER_HEAD = 0, 1
 EXPORTED_SYMBOLS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
                     "kda_status_string", "kda_gdr2_chunk_fwd", "kda_gdr2_recurrent_step",
                     "kda_prologue", "kda_epilogue", "kda_chunk_bwd",
-                    "kda_chunk_bwd_workspace_size", "kda_gdr2_chunk_bwd")
+                    "kda_chunk_bwd_workspace_size", "kda_gdr2_chunk_bwd",
+                    "kda_chunk_fwd_noalloc")
 
 _lib = None
 
@@ -66,6 +67,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
                                   ctypes.c_size_t, P]
     lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.kda_chunk_fwd_noalloc.restype = I
     lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.kda_recurrent_step.restype = I
     lib.kda_gdr2_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
@@ -106,6 +109,13 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, n
     return int(load_library().kda_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o,
                                             cu_seqlens, num_seqs, B, H, T, dk, dv, dt, gm,
                                             workspace, workspace_bytes, stream))
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens,
+                          num_seqs, B, H, T, dk, dv, dt, gm, stream) -> int:
+    return int(load_library().kda_chunk_fwd_noalloc(q, k, v, g, beta, initial_state,
+                                                    final_state, o, cu_seqlens, num_seqs, B, H,
+                                                    T, dk, dv, dt, gm, stream))
 
 
 def kda_recurrent_step(q, k, v, g, beta, state, o, N, H, dk, dv, dt, gm, stream) -> int:

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -224,6 +225,55 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   return chunk_fwd_impl(q, k, v, g, beta, nullptr, nullptr, initial_state, final_state, o,
                         cu_seqlens, num_seqs, B, H, T, dk, dv, enum_value(&dt), enum_value(&gm),
                         workspace, workspace_bytes, stream);
+}
+
+// Scratch memory of kda_chunk_fwd_noalloc: a file-scope device array, so that the call never
+// allocates. In host code the array's name is only a host-side stand-in; its device address
+// is looked up once per device (hipGetSymbolAddress, with that device current) and only that
+// address is handed to kernels. Every call on a device shares its array.
+static constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state,
+                                 float* final_state, void* o, const int32_t* cu_seqlens,
+                                 int num_seqs, int B, int H, int T, int dk, int dv,
+                                 kda_dtype dt, kda_gate_mode gm, hipStream_t stream) {
+  if (!beta) return KDA_ERR_INVALID_ARG;
+  const int dtype = enum_value(&dt);
+  if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARG;
+  if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
+  // the workspace kda_chunk_fwd would recommend, within the scratch array; packed sequences
+  // need at least their work list, which must fit
+  const long long N = cu_seqlens ? num_seqs : B;
+  const bool mfma = dtype == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T);
+  const size_t work_list = mfma && cu_seqlens ? kda::chunk_plan_bytes((int)N, H, dv) : 0;
+  if (work_list > kNoAllocScratchBytes) return KDA_ERR_UNSUPPORTED;
+  size_t bytes = chunk_fwd_workspace(B, H, T, dk, dv, cu_seqlens ? num_seqs : 0, dtype);
+  bytes = std::min(bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (bytes > 0 && noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+  return chunk_fwd_impl(q, k, v, g, beta, nullptr, nullptr, initial_state, final_state, o,
+                        cu_seqlens, num_seqs, B, H, T, dk, dv, dtype, enum_value(&gm),
+                        bytes > 0 ? ws : nullptr, bytes, stream);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,

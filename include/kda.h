@@ -167,6 +167,24 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Every other argument, layout, error and result is kda_chunk_fwd's. In place of the
+ * workspace the call uses a file-scope device array of the library, 64 MiB on every device
+ * the library runs on (held until the process ends), as the workspace kda_chunk_fwd would
+ * recommend, capped at that size: problems whose segment plan needs more simply cut fewer
+ * sequences. Packed calls whose work list (4 * (1 + 2 * num_seqs * H) bytes) exceeds the array
+ * return KDA_ERR_UNSUPPORTED. Nothing in the array needs clearing between calls (every call
+ * writes what it reads), but every call on one device shares that device's array: calls that
+ * overlap on one device (other streams or host threads) race.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state,
+                                 float* final_state, void* o, const int32_t* cu_seqlens,
+                                 int num_seqs, int B, int H, int T, int dk, int dv,
+                                 kda_dtype dt, kda_gate_mode gm, hipStream_t stream);
+
+/*
  * One single-token decode step for N sequences x H heads on a resident state.
  * Per chain: S~ = Diag(exp g) S; p = S~^T k; S = S~ + beta k (v - p)^T; o = S^T q —
  * the decay-then-delta form of the page "KDA 与 Gated DeltaNet：线性注意力怎样读写有限状态",
