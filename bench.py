@@ -7,7 +7,8 @@ transform, sequential state pass and chunk output, all in one fused kernel launc
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 
 Printed (one JSON line on stdout):
-  value          tokens/s of that step (65536 tokens per step)
+  value          tokens/s of that step (65536 tokens per step), from the mean over the
+                 timed steps; ms_per_step_median is the median of the per-call times
   roofline       the chunk kernel against the HBM roofline: algorithmic bytes per
                  launch / average launch time (HIP events on the launch stream),
                  and the HBM bytes measured by rocprofv3 counters when given
@@ -18,7 +19,8 @@ Printed (one JSON line on stdout):
   gates          the fused prologue (L2Norm, decay gate, sigmoid) and epilogue (gated
                  RMSNorm) on the chunk workload's rows, against the HBM roofline
   bwd            kda_chunk_bwd (all gradients) on the chunk workload
-  small_configs  kda_chunk_fwd on the B2 H16 T4096 and GDN B1 H16 T8192 workloads
+  small_configs  kda_chunk_fwd on the tiny fp32 (B1 H2 T256 dk=dv=64), B2 H16 T4096 and
+                 GDN B1 H16 T8192 workloads
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
 """
 
@@ -125,19 +127,25 @@ def epilogue_alg_bytes(B: int, H: int, T: int, dv: int, o_bytes: int = 2) -> flo
     return float(3 * o_bytes * dv * B * H * T + 4 * dv)
 
 
-def time_calls(torch, call, steps: int, warmup: int) -> float:
-    """Average milliseconds per call, HIP events on the launch stream."""
+def time_calls(torch, call, steps: int, warmup: int, per_call: bool = False):
+    """Milliseconds per call over ``steps`` back-to-back calls after ``warmup`` untimed ones,
+    HIP events on the launch stream, the timed region bracketed by device synchronisations.
+    Returns the mean (the bracket's time / steps); with ``per_call`` also the median of the
+    per-call times (one event pair around each call, recorded in the same stream)."""
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(torch.device("cuda:0"))
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         call()
-    ev1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    if not per_call:
+        return mean
+    return mean, statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
 
 
 def bench_gates(torch, kda, cfg, steps: int, warmup: int):
@@ -245,33 +253,45 @@ def bench_bwd(torch, kda, x, steps: int, warmup: int):
 
 
 def bench_chunk(torch, kda, x, steps: int, warmup: int):
+    """One chunk-forward call per step through the C ABI, with the workspace the library
+    recommends allocated once beforehand (as a caller would). Returns the mean and median
+    milliseconds per call and the workspace bytes."""
     dev = torch.device("cuda:0")
     up = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)  # noqa
-    q, k, v = (up(a, torch.bfloat16) for a in (x.q, x.k, x.v))
+    dt = torch.bfloat16 if x.cfg.dtype == "bf16" else torch.float32
+    code = kda.KDA_BF16 if dt == torch.bfloat16 else kda.KDA_F32
+    q, k, v = (up(a, dt) for a in (x.q, x.k, x.v))
     g, beta = up(x.g), up(x.beta)
     cu = up(x.cu_seqlens, torch.int32) if x.cu_seqlens is not None else None
     s0 = up(x.s0) if x.s0 is not None else None
-    o = torch.empty(tuple(x.v.shape), dtype=torch.bfloat16, device=dev)
+    o = torch.empty(tuple(x.v.shape), dtype=dt, device=dev)
     sT = torch.empty((x.n_seqs, x.q.shape[1], x.q.shape[3], x.v.shape[3]), dtype=torch.float32,
                      device=dev)
+    B, H, T, dk = x.q.shape
+    dv = x.v.shape[-1]
+    ns = x.n_seqs if cu is not None else 0
+    wsb = kda.kda_chunk_fwd_workspace_size(B, H, T, dk, dv, ns, code)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    gm = kda.KDA_GATE_PER_CHANNEL if x.g.ndim == 4 else kda.KDA_GATE_PER_HEAD
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ptr = lambda a: a.data_ptr() if a is not None else None  # noqa: E731
+    common = (ptr(s0), ptr(sT), ptr(o), ptr(cu), ns, B, H, T, dk, dv, code, gm, ptr(ws), wsb,
+              stream)
     if x.erase is not None:
         erase, write = up(x.erase), up(x.write)
-        call = lambda: kda.gdr2_chunk_fwd(q, k, v, g, erase, write, initial_state=s0,  # noqa
-                                          cu_seqlens=cu, o=o, final_state=sT)
+
+        def call():
+            rc = kda.kda_gdr2_chunk_fwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(erase),
+                                        ptr(write), *common)
+            if rc != kda.KDA_OK:
+                raise RuntimeError(f"kda_gdr2_chunk_fwd returned {rc}")
     else:
-        call = lambda: kda.chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu,  # noqa
-                                     o=o, final_state=sT)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
-        call()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
+        def call():
+            rc = kda.kda_chunk_fwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), *common)
+            if rc != kda.KDA_OK:
+                raise RuntimeError(f"kda_chunk_fwd returned {rc}")
+    mean, median = time_calls(torch, call, steps, warmup, per_call=True)
+    return mean, median, wsb
 
 
 def bench_decode(torch, kda, cfg, reps: int = 5):
@@ -425,7 +445,7 @@ def main() -> int:
 
     import gated_delta_rule_13_amd as kda
     from kda_workloads import (GDN_B1_H16_T8192, KDA_B2_H16_T4096, KDA_DECODE_N256_H32,
-                               KDA_VARLEN_H32_T65536, make_chunk_inputs)
+                               KDA_VARLEN_H32_T65536, TINY_KDA_F32, make_chunk_inputs)
 
     kda.load_library()
     if not torch.cuda.is_available():
@@ -437,18 +457,19 @@ def main() -> int:
     log(f"generated {cfg.name} in {time.time() - t0:.1f}s; lengths {np.diff(x.cu_seqlens)}")
     if args.copy_probe:
         copy_probe(torch)
-    ms = bench_chunk(torch, kda, x, args.steps, args.warmup)
+    ms, ms_median, ws_bytes = bench_chunk(torch, kda, x, args.steps, args.warmup)
     tokens = cfg.T
     value = tokens / (ms / 1e3)
     alg_bytes = chunk_alg_bytes(x)
     alg_flops = chunk_alg_flops_per_head_token(cfg.dk, cfg.dv) * cfg.H * cfg.T
     gbs = alg_bytes / (ms / 1e3) / 1e9
     tflops = alg_flops / (ms / 1e3) / 1e12
-    log(f"chunk_fwd: {ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s, {gbs:.0f} GB/s, "
-        f"{tflops:.1f} TFLOP/s")
+    log(f"chunk_fwd: {ms:.3f} ms/step (median {ms_median:.3f}), {value / 1e6:.2f} M tokens/s, "
+        f"{gbs:.0f} GB/s, {tflops:.1f} TFLOP/s, workspace {ws_bytes} bytes")
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "H": cfg.H, "dk": cfg.dk, "dv": cfg.dv,
@@ -458,7 +479,7 @@ def main() -> int:
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
                      "kernel": "kda chunk forward (segment plan: planner, items, segment chain, corrections)",
-                     "alg_bytes_per_launch": alg_bytes},
+                     "alg_bytes_per_launch": alg_bytes, "workspace_bytes": ws_bytes},
         "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
     }
@@ -479,11 +500,12 @@ def main() -> int:
         t0 = time.time()
         gx = make_chunk_inputs(gcfg)
         log(f"generated {gcfg.name} in {time.time() - t0:.1f}s")
-        gms = bench_chunk(torch, kda, gx, args.steps, args.warmup)
+        gms, gmed, _ = bench_chunk(torch, kda, gx, args.steps, args.warmup)
         gbytes = chunk_alg_bytes(gx)
         ggbs = gbytes / (gms / 1e3) / 1e9
         result["gdr2"] = {
-            "workload": gcfg.name, "ms_per_step": gms, "tokens_per_s": gcfg.T / (gms / 1e3),
+            "workload": gcfg.name, "ms_per_step": gms, "ms_per_step_median": gmed,
+            "tokens_per_s": gcfg.T / (gms / 1e3),
             "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic(MEASURED_TRAFFIC_GDR2),
@@ -496,7 +518,7 @@ def main() -> int:
             log(f"gdr2 chunk_bwd: {gbms:.3f} ms/step")
         del gx
         if not args.no_decode:
-            gd = KDA_DECODE_N256_H32.replace(name="gdr2_decode_n256_h32", T=64, gates="gdr2")
+            gd = KDA_DECODE_N256_H32.replace(name="gdr2_decode_n256_h32", gates="gdr2")
             sec, _ = bench_decode(torch, kda, gd)
             per_step = decode_alg_bytes_per_step(gd.B, gd.H, gd.dk, gd.dv, gdr2=True)
             dgbs = per_step * gd.T / sec / 1e9
@@ -506,13 +528,15 @@ def main() -> int:
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
     # the two smaller prefill workloads (parity-test shapes), scheduled as a caller would
     small = {}
-    for c in (KDA_B2_H16_T4096, GDN_B1_H16_T8192):
+    for c in (TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192):
         sx = make_chunk_inputs(c)
-        sms = bench_chunk(torch, kda, sx, args.steps, args.warmup)
+        sms, smed, _ = bench_chunk(torch, kda, sx, args.steps, args.warmup)
         sb = chunk_alg_bytes(sx)
-        small[c.name] = {"ms_per_step": sms, "tokens_per_s": c.B * c.T / (sms / 1e3),
+        small[c.name] = {"ms_per_step": sms, "ms_per_step_median": smed, "dtype": c.dtype,
+                         "tokens_per_s": c.B * c.T / (sms / 1e3),
                          "hbm_gbs": sb / (sms / 1e3) / 1e9}
-        log(f"{c.name}: {sms:.3f} ms/step, {c.B * c.T / sms / 1e3:.2f} M tokens/s")
+        log(f"{c.name}: {sms:.3f} ms/step (median {smed:.3f}), "
+            f"{c.B * c.T / sms / 1e3:.2f} M tokens/s")
     result["small_configs"] = small
     if not args.no_bwd:
         bms, wsb = bench_bwd(torch, kda, x, args.steps, args.warmup)
