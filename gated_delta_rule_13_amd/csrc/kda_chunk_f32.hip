@@ -10,8 +10,11 @@
 //   X  = Diag(beta) (V - (K ⊙ e^G) S)        V' = Tm X   (= U - W S of the pages)
 //   O  = (Q ⊙ e^G) S + A_qk V'
 //   S <- Diag(e^{G_C}) S + (K ⊙ e^{G_C - G})^T V'
-// Every exponent is a difference G_i - G_j with j <= i, or G itself, so no factor
-// exceeds 1 in magnitude and nothing is divided by a decay.
+// The decay factors of A_qk and A_kk are split at the middle of the chunk, R = G_15:
+// e^{G_i - G_j} = e^{G_i - R} e^{R - G_j}. Over 32 tokens with g >= -5 each factor lies in
+// [e^-80, e^80], inside the fp32 range, and their product is the exact weighting, so the
+// tiles are plain dot products of q e^{G - R} and k e^{R - G}; nothing is divided by a decay,
+// and every other exponent is G itself or G_C - G, at most 1.
 //
 // Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2"): the read side uses
 // the erase-gated keys B * K in place of Diag(beta) K (in A_kk and in the prediction), and
@@ -35,6 +38,8 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
   __shared__ float sQ[kC][DK];
   __shared__ float sK[kC][DK];
   __shared__ float sG[kC][DK];   // cumulative log-decay, later K ⊙ e^{G_C - G}
+  __shared__ float sQr[kC][DK + 1];  // q e^{G - R}, then (B *) k e^{G - R}
+  __shared__ float sKd[kC][DK + 1];  // k e^{R - G}
   __shared__ float sAqk[kC][kC + 1];
   __shared__ float sAkk[kC][kC + 1];
   __shared__ float sTm[kC][kC + 1];
@@ -97,31 +102,52 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(ChunkArgs a, int n_
       sGC[c] = run;
     }
     __syncthreads();
-    // -- A_qk (inclusive lower) and A_kk (strict lower, rows scaled by beta)
+    // -- the factors of the decay split at R = G_15 (q, k e^{G - R} and k e^{R - G})
+    for (int idx = tid; idx < kC * DK; idx += kThreads) {
+      const int t = idx / DK, c = idx % DK;
+      const float d = sG[t][c] - sG[kC / 2 - 1][c];
+      sQr[t][c] = sQ[t][c] * __expf(d);
+      sKd[t][c] = sK[t][c] * __expf(-d);
+    }
+    __syncthreads();
+    // -- A_qk (inclusive lower) and A_kk (strict lower, rows scaled by beta); the read-side
+    // key of A_kk, (B *) k e^{G - R}, is formed in place of q after A_qk
     for (int pidx = tid; pidx < kC * kC; pidx += kThreads) {
       const int i = pidx / kC, j = pidx % kC;
-      float aq = 0.f, ak = 0.f;
-      if (j <= i) {
-        for (int c = 0; c < DK; ++c) {
-          const float e = __expf(sG[i][c] - sG[j][c]);
-          const float kj = sK[j][c] * e;
-          aq += sQ[i][c] * kj;
-          ak += (GDR2 ? sE[i][c] : sK[i][c]) * kj;
-        }
-      }
+      float aq = 0.f;
+      if (j <= i)
+        for (int c = 0; c < DK; ++c) aq += sQr[i][c] * sKd[j][c];
       sAqk[i][j] = aq;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kC * DK; idx += kThreads) {
+      const int t = idx / DK, c = idx % DK;
+      sQr[t][c] = (GDR2 ? sE[t][c] : sK[t][c]) * __expf(sG[t][c] - sG[kC / 2 - 1][c]);
+    }
+    __syncthreads();
+    for (int pidx = tid; pidx < kC * kC; pidx += kThreads) {
+      const int i = pidx / kC, j = pidx % kC;
+      float ak = 0.f;
+      if (j < i)
+        for (int c = 0; c < DK; ++c) ak += sQr[i][c] * sKd[j][c];
       sAkk[i][j] = j < i ? sBeta[i] * ak : 0.f;
     }
     __syncthreads();
-    // -- Tm = (I + A_kk)^-1 by forward substitution, one column per thread
+    // -- Tm = (I + A_kk)^-1 by forward substitution, one column per thread, the column in
+    // registers (row i of column j is -sum_{m < i} A_kk[i][m] Tm[m][j]; Tm[m][j] = 0 for
+    // m < j and 1 at m = j)
     if (tid < kC) {
       const int j = tid;
-      for (int i = 0; i < kC; ++i) sTm[i][j] = i == j ? 1.f : 0.f;
-      for (int i = j + 1; i < kC; ++i) {
+      float tcol[kC];
+#pragma unroll
+      for (int i = 0; i < kC; ++i) {
         float acc = 0.f;
-        for (int m = j; m < i; ++m) acc += sAkk[i][m] * sTm[m][j];
-        sTm[i][j] = -acc;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc += sAkk[i][m] * tcol[m];
+        tcol[i] = i < j ? 0.f : (i == j ? 1.f : -acc);
       }
+#pragma unroll
+      for (int i = 0; i < kC; ++i) sTm[i][j] = tcol[i];
     }
     // -- decayed operands, in place: Q <- Q e^G, K <- K e^G, G <- K e^{G_C - G}
     for (int idx = tid; idx < kC * DK; idx += kThreads) {
