@@ -97,12 +97,16 @@ static size_t chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int num_s
   // only the matrix-core path uses a workspace: its schedule (every intermediate of the
   // method stays on chip) and, for the segment plan, the segments' states
   if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0) return 0;
-  if (dt != KDA_BF16 || !kda::chunk_mfma_supports(dk, dv, T)) return 0;
+  if (dt != KDA_BF16 || !kda::chunk_mfma_dims(dk, dv)) return 0;
   const bool packed = num_seqs > 0;
   if (packed && B != 1) return 0;  // no such call is accepted
   const long long N = packed ? num_seqs : B;
   if (N * H > (1ll << 24)) return 0;
   const int cus = device_compute_units();
+  // chains too long for whole-chain items: only the segment plan (dv = dk) runs them on the
+  // matrix cores; without it the call takes the fp32 path, which needs no workspace
+  if (!kda::chunk_mfma_supports(dk, dv, T))
+    return dv == dk ? kda::chunk_segplan_bytes((int)N, H, T, dv, packed, cus) : 0;
   // dv = dk: the segment plan (packed sequences, or fewer equal-length chains than compute
   // units); its plan words also hold the work list that it falls back to
   if (dv == dk && (packed || N * H < cus)) {
@@ -140,7 +144,15 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   // packed exactly when cu_seqlens is given (num_seqs = B without it is B sequences of T)
   const bool packed = cu_seqlens != nullptr;
   const long long N = packed ? num_seqs : B;
-  const bool mfma = dt == KDA_BF16 && kda::chunk_mfma_supports(dk, dv, T);
+  const bool dims = dt == KDA_BF16 && kda::chunk_mfma_dims(dk, dv);
+  const bool whole = dims && kda::chunk_mfma_supports(dk, dv, T);
+  // chains too long for whole-chain items run on the matrix cores only as a segment plan,
+  // which needs its matrices and carried-back queries in the workspace; else the fp32 path
+  const size_t long_min = dims && !whole && N <= (1ll << 24)
+                              ? kda::chunk_segplan_min_bytes((int)N, H, T, dv, packed)
+                              : 0;
+  const bool seg_long = long_min > 0 && workspace && workspace_bytes >= long_min;
+  const bool mfma = whole || seg_long;
   // workspace_bytes == 0: run without a schedule. Otherwise packed sequences need at least
   // their work list; every larger buffer is planned within (each path below checks that its
   // own layout fits).
@@ -172,10 +184,10 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
   const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
   hipError_t err;
   if (mfma) {
-    const size_t sp_min = kda::chunk_segplan_min_bytes(a.N, H, T, dv);
+    const size_t sp_min = kda::chunk_segplan_min_bytes(a.N, H, T, dv, packed);
     const size_t seg = kda::chunk_seg_bytes(a.N, H, T, dv, a.cus);
-    if (workspace_bytes > 0 && (packed || N * H < a.cus) && sp_min > 0 &&
-        workspace_bytes >= sp_min) {
+    if (seg_long || (workspace_bytes > 0 && (packed || N * H < a.cus) && sp_min > 0 &&
+                     workspace_bytes >= sp_min)) {
       err = kda::launch_chunk_mfma_segplan(a, per_channel, workspace, workspace_bytes, stream);
     } else if (workspace_bytes > 0 && !erase && seg > 0 && workspace_bytes >= seg) {
       err = kda::launch_chunk_mfma_segmented(a, per_channel, workspace, stream);

@@ -796,9 +796,11 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* x
 // The plan is laid out for slots_max slots (the workspace's capacity); a candidate segment
 // length is allowed only when its slots fit that capacity (and mats_ok: the workspace holds
 // the matrices of every slot) and its carried-back queries fit qt_rows rows per head.
+// xc_max > 0 bounds every item to xc_max chunks: sequences longer than that are always cut
+// (the host has checked that a candidate within the bound fits the workspace).
 __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
     const int32_t* cu, int N, int H, int T, int cus, int slots_max, int mats_ok,
-    long long qt_rows, int xc_min, uint32_t* plan) {
+    long long qt_rows, int xc_min, int xc_max, uint32_t* plan) {
   __shared__ int cl[kMaxPlanSeqs];     // chunks of sequence n
   __shared__ int ln[kMaxPlanSeqs];     // tokens of sequence n
   __shared__ int key[kMaxPlanSeqs];    // entries: chunks
@@ -829,12 +831,16 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
   while (n2 < N) n2 <<= 1;
   sort_entries(key, ea, eb, n2);
   const int maxc = key[0] > 0 ? key[0] : 0;
+  // sequences past the item bound must be cut
+  const bool must_cut = xc_max > 0 && maxc > xc_max;
   // candidate segment lengths xc_min + j * step (chunks), shorter than the longest sequence
-  const int step = maxc > xc_min ? (maxc - xc_min + kMaxPlanSeqs - 1) / kMaxPlanSeqs : 1;
+  // and within the item bound
+  const int hi = must_cut ? xc_max + 1 : maxc;
+  const int step = hi > xc_min ? (hi - xc_min + kMaxPlanSeqs - 1) / kMaxPlanSeqs : 1;
   {
     const int xc = xc_min + t * step;
     float b = 3.0e38f;
-    if (mats_ok && xc < maxc) {
+    if (mats_ok && xc < hi) {
       long long total = 0, corr = 0, slots = 0, later = 0;
       int longest = 0, most = 1;
       for (int i = 0; i < N; ++i) {
@@ -900,9 +906,15 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
       ++ns;
     }
     const double half_bound = fmax(fmax(ns < N ? key[ns] : 0.0, maxhalf), total / cus);
-    xc_sel = bnd[0] < kSegMinGain * half_bound ? xc_min + bix[0] * step : 0;
+    const bool any = bnd[0] < 3.0e38f;
+    xc_sel = any && (must_cut || bnd[0] < kSegMinGain * half_bound) ? xc_min + bix[0] * step : 0;
     plan[1] = (uint32_t)xc_sel;
-    if (xc_sel == 0) {
+    if (must_cut && xc_sel == 0) {
+      // no candidate fits (the host rules this out): an empty plan, no item runs
+      n_ent = 0;
+      ent_off[0] = 0;
+      plan[0] = plan[2] = plan[3] = plan[4] = 0;
+    } else if (xc_sel == 0) {
       // the halves schedule: sequences by chunk count, halves of the ns longest
       int a = 0, b = ns, e = 0;
       uint32_t off = 0;
@@ -1228,7 +1240,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
     const int k = (int)(sl - segbase[n]);
     const TokenRange tr = token_range(a.cu, n, a.T);
     const int g0 = k * xt + (int)(u - corr_off[sl]) * kSegGroup;  // first token of the unit
-    const int seg_end = min((k + 1) * xt, tr.len);
+    const int seg_end = (int)min((long long)(k + 1) * xt, (long long)tr.len);
     if (k < 1 || g0 >= seg_end) continue;  // uniform over the workgroup
     const int len = min(kSegGroup, seg_end - g0);
     const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + g0;
@@ -1299,10 +1311,16 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
 
 }  // namespace
 
+bool chunk_mfma_dims(int dk, int dv) { return dk == kDK && (dv == 64 || dv == 128); }
+
 // Buffer descriptors address at most 2^31 bytes: a chain's g rows (T x dk fp32) must fit.
 bool chunk_mfma_supports(int dk, int dv, int T) {
-  return dk == kDK && (dv == 64 || dv == 128) && (long long)T * kDK * 4 < (1ll << 31);
+  return chunk_mfma_dims(dk, dv) && (long long)T * kDK * 4 < (1ll << 31);
 }
+
+// Longer chains run only as segment plans whose items are at most kMaxItemTokens long.
+constexpr int kMaxItemTokens = 1 << 21;
+static bool segplan_long(int T) { return !chunk_mfma_supports(kDK, kDK, T); }
 
 size_t chunk_plan_bytes(int N, int H, int dv) {
   (void)dv;
@@ -1339,13 +1357,14 @@ size_t chunk_seg_bytes(int N, int H, int T, int dv, int cus) {
 }
 
 // Segment plans: the shortest segment (64-token chunks), at least 512 tokens and at most 64
-// segments per T tokens, and the most slots any candidate of the planner can use.
+// segments per T tokens (within the item bound), and the most slots any candidate of the
+// planner can use.
 static int segplan_xc_min(int T) {
-  const int ct = (T + kC - 1) / kC;
-  return std::max(8, (ct + 63) / 64);
+  const int ct = (int)(((long long)T + kC - 1) / kC);
+  return std::min(kMaxItemTokens / kC, std::max(8, (ct + 63) / 64));
 }
 static int segplan_slots(int N, int T) {
-  const int ct = (T + kC - 1) / kC;
+  const int ct = (int)(((long long)T + kC - 1) / kC);
   return std::min(kMaxPlanSeqs, N + N / 8 + (ct + segplan_xc_min(T) - 1) / segplan_xc_min(T) + 1);
 }
 // Bytes of the plan words for a capacity of cap slots (up to 2 H items per slot).
@@ -1354,10 +1373,27 @@ static size_t segplan_plan_bytes(int N, int H, int cap) {
 }
 static size_t segplan_mats_bytes(int H, int cap) { return (size_t)3 * cap * H * kDK * kDK * 4; }
 
+// Chains too long for whole-chain items: the slots and carried-back-query rows per head that
+// a plan needs at the least. The planner's largest candidate within the item bound is at
+// least 0.999 kMaxItemTokens long (its candidates are at most 32 chunks apart), so with
+// m = ceil(T / kMaxItemTokens) >= 2, N packed sequences of T tokens in all take at most
+// 2 N + 2 m slots and N sequences of T tokens each at most 2 m slots apiece; every token past
+// a first segment needs a row.
+static long long segplan_long_slots(int N, int T, bool packed) {
+  if (!segplan_long(T)) return 0;
+  const long long m = ((long long)T + kMaxItemTokens - 1) / kMaxItemTokens;
+  return (packed ? 2ll * N + 2 * m : 2 * m * N) + 1;
+}
+static long long segplan_long_rows(int N, int T, bool packed) {
+  return segplan_long(T) ? (packed ? (long long)T : (long long)N * T) : 0;
+}
+
 // Slots worth planning for: every sequence plus about one extra segment per compute unit and
-// head (cutting beyond that only adds rounds of items).
-static int segplan_cap(int N, int H, int T, int cus) {
-  return std::max(N, std::min(segplan_slots(N, T), N + (cus + H - 1) / H + 1));
+// head (cutting beyond that only adds rounds of items), and what long chains need.
+static int segplan_cap(int N, int H, int T, int cus, bool packed) {
+  const long long need = segplan_long_slots(N, T, packed);
+  return (int)std::max<long long>(
+      need, std::max(N, std::min(segplan_slots(N, T), N + (cus + H - 1) / H + 1)));
 }
 
 // Layout of a segment plan in ws_bytes of workspace: the slot capacity (up to segplan_cap
@@ -1369,12 +1405,18 @@ struct SegLayout {
   bool mats_ok = false;
   long long qt_rows = 0;
 };
-static bool segplan_layout(int N, int H, int T, int cus, size_t ws_bytes, SegLayout& L) {
+// Chains too long for whole-chain items need the matrices of at least segplan_long_slots
+// slots and segplan_long_rows rows, which are set aside first.
+static bool segplan_layout(int N, int H, int T, int cus, bool packed, size_t ws_bytes,
+                           SegLayout& L) {
   if (N <= 0 || N > kMaxPlanSeqs || H <= 0 || ws_bytes < segplan_plan_bytes(N, H, N)) return false;
+  const long long need = segplan_long_slots(N, T, packed);
+  if (need > kMaxPlanSeqs) return false;
+  const size_t rows = (size_t)segplan_long_rows(N, T, packed) * H * kDK * 2;
   L = SegLayout{};
   L.cap = N;
-  for (int cap = segplan_cap(N, H, T, cus); cap >= N; --cap) {
-    if (segplan_plan_bytes(N, H, cap) + segplan_mats_bytes(H, cap) <= ws_bytes) {
+  for (int cap = segplan_cap(N, H, T, cus, packed); cap >= std::max<long long>(N, need); --cap) {
+    if (segplan_plan_bytes(N, H, cap) + segplan_mats_bytes(H, cap) + rows <= ws_bytes) {
       L.cap = cap;
       L.mats_ok = true;
       break;
@@ -1384,13 +1426,16 @@ static bool segplan_layout(int N, int H, int T, int cus, size_t ws_bytes, SegLay
     const size_t used = segplan_plan_bytes(N, H, L.cap) + segplan_mats_bytes(H, L.cap);
     L.qt_rows = (long long)((ws_bytes - used) / ((size_t)H * kDK * 2));
   }
-  return true;
+  return L.mats_ok || need == 0;
 }
 
-size_t chunk_segplan_min_bytes(int N, int H, int T, int dv) {
+size_t chunk_segplan_min_bytes(int N, int H, int T, int dv, bool packed) {
   if (dv != kDK || N <= 0 || N > kMaxPlanSeqs || H <= 0) return 0;
-  (void)T;
-  return segplan_plan_bytes(N, H, N);
+  const long long need = segplan_long_slots(N, T, packed);
+  if (need == 0) return segplan_plan_bytes(N, H, N);
+  if (need > kMaxPlanSeqs) return 0;
+  return segplan_plan_bytes(N, H, (int)need) + segplan_mats_bytes(H, (int)need) +
+         (size_t)segplan_long_rows(N, T, packed) * H * kDK * 2;
 }
 
 // The workspace kda_chunk_fwd_workspace_size recommends: segplan_cap slots, and carried-back
@@ -1398,11 +1443,12 @@ size_t chunk_segplan_min_bytes(int N, int H, int T, int dv) {
 // units (every sequence is then cut), else for a quarter of it (only the sequences much
 // longer than the average are cut).
 size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed, int cus) {
-  if (chunk_segplan_min_bytes(N, H, T, dv) == 0) return 0;
-  const int cap = segplan_cap(N, H, T, cus);
+  if (chunk_segplan_min_bytes(N, H, T, dv, packed) == 0) return 0;
+  const int cap = segplan_cap(N, H, T, cus, packed);
   const long long chains = (long long)N * H;
-  const long long rows = chains < cus ? (packed ? (long long)T : (long long)N * T)
-                                      : ((long long)T + 3) / 4;
+  const long long rows = chains < cus || segplan_long(T)
+                             ? (packed ? (long long)T : (long long)N * T)
+                             : ((long long)T + 3) / 4;
   return segplan_plan_bytes(N, H, cap) + segplan_mats_bytes(H, cap) +
          (size_t)rows * H * kDK * 2;
 }
@@ -1411,8 +1457,8 @@ hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, vo
                                      size_t ws_bytes, hipStream_t stream) {
   ChunkArgs a = args;
   SegLayout L;
-  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.dv != kDK || !ws ||
-      !segplan_layout(a.N, a.H, a.T, a.cus, ws_bytes, L))
+  if (!chunk_mfma_dims(a.dk, a.dv) || a.dv != kDK || !ws ||
+      !segplan_layout(a.N, a.H, a.T, a.cus, a.cu != nullptr, ws_bytes, L))
     return hipErrorInvalidValue;
   const int sm = L.cap;
   a.plan = static_cast<uint32_t*>(ws);
@@ -1424,7 +1470,9 @@ hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, vo
   a.split_all = 0;
   chunk_segplan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, sm,
                                                        L.mats_ok ? 1 : 0, L.qt_rows,
-                                                       segplan_xc_min(a.T), a.plan);
+                                                       segplan_xc_min(a.T),
+                                                       segplan_long(a.T) ? kMaxItemTokens / kC : 0,
+                                                       a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(2 * (size_t)a.H * sm);  // the largest plan

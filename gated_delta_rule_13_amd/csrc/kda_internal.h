@@ -112,6 +112,9 @@ hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, bool pe
                          hipStream_t stream);
 hipError_t launch_chunk_f32(const ChunkArgs& a, bool bf16, bool per_channel, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool per_channel, hipStream_t stream);
+// Head sizes of the matrix-core path, and whether it runs whole chains of T tokens (longer
+// chains run only as segment plans, below).
+bool chunk_mfma_dims(int dk, int dv);
 bool chunk_mfma_supports(int dk, int dv, int T);
 hipError_t launch_prologue(const PrologueArgs& a, int dk, bool bf16, hipStream_t stream);
 hipError_t launch_epilogue(const EpilogueArgs& a, int dv, bool bf16, hipStream_t stream);
@@ -127,10 +130,12 @@ hipError_t launch_chunk_mfma_segmented(const ChunkArgs& a, bool per_channel, voi
                                        hipStream_t stream);
 // Segment plan of the forward (dv = dk = 128, any gates): the launches (planner, items,
 // segment chain, corrections). chunk_segplan_bytes is the recommended workspace,
-// chunk_segplan_min_bytes the smallest one the plan runs in (0 when not available: then only
-// its work list fits); launch_chunk_mfma_segplan plans within ws_bytes.
+// chunk_segplan_min_bytes the smallest one the plan runs in (0 when not available; for chains
+// that whole-chain items can hold, it is the work list the plan may fall back to);
+// launch_chunk_mfma_segplan plans within ws_bytes. Chains too long for whole-chain items
+// (chunk_mfma_supports false) are always cut into items of at most 2^21 tokens.
 size_t chunk_segplan_bytes(int N, int H, int T, int dv, bool packed, int cus);
-size_t chunk_segplan_min_bytes(int N, int H, int T, int dv);
+size_t chunk_segplan_min_bytes(int N, int H, int T, int dv, bool packed);
 hipError_t launch_chunk_mfma_segplan(const ChunkArgs& a, bool per_channel, void* ws,
                                      size_t ws_bytes, hipStream_t stream);
 

@@ -93,10 +93,11 @@ typedef enum {
  *    every S and a correction pass adds Qt S. Results equal the whole-chain computation up
  *    to rounding. The workspace holds the plan words, three fp32 dk x dk matrices per segment
  *    slot and head, and one bf16 row of dk carried-back queries per head and token past the
- *    first segment of its sequence. With C = ceil(T / 64), Xmin = max(8, ceil(C / 64)),
- *    M = min(1024, N + floor(N / 8) + ceil(C / Xmin) + 1) and cus the compute units, the
- *    recommendation is S = max(N, min(M, N + ceil(cus / H) + 1)) slots and Q rows per head,
- *    Q = T for packed sequences and B T otherwise when N H < cus, else Q = ceil(T / 4):
+ *    first segment of its sequence. With C = ceil(T / 64), Xmin = min(2^15, max(8,
+ *    ceil(C / 64))), M = min(1024, N + floor(N / 8) + ceil(C / Xmin) + 1) and cus the compute
+ *    units, the recommendation is S = max(N, min(M, N + ceil(cus / H) + 1)) slots and Q rows
+ *    per head, Q = T for packed sequences and B T otherwise when N H < cus, else
+ *    Q = ceil(T / 4) (for T >= 2^22, S at least and Q exactly as kda_chunk_fwd's minimum):
  *    R(4 (N + 2 S + 11 + 4 H S)) + 3 S H dk^2 * 4 + Q H dk * 2 bytes, R rounding up to a
  *    multiple of 256 (230 MiB for 8 packed sequences, H = 32, T = 65536). Given another
  *    size, the plan takes as many of the S slots as fit with their matrices, and the rest for
@@ -157,8 +158,15 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  * Arithmetic: state and accumulation in float32. With dt = KDA_BF16 the dense
  * contractions take bf16 operands on the matrix cores (float32 accumulate); with
  * dt = KDA_F32 every operation is float32. The matrix-core kernel serves dt = KDA_BF16
- * with dk = 128 while a chain's per-channel decay, T * dk float32 values, stays under 2^31
- * bytes (T < 2^22); dk = 64, dt = KDA_F32 and longer T axes run on the float32 kernel.
+ * with dk = 128. It runs a chain as one item while the chain's per-channel decay, T * dk
+ * float32 values, stays under 2^31 bytes (T < 2^22). Longer T axes run on the matrix cores
+ * with dv = 128 and a workspace of at least the minimum below: the call then cuts every
+ * sequence into segments of at most 2^21 tokens. The minimum is the plan words and three
+ * fp32 dk x dk matrices per head for each of S slots, plus dk bf16 values per head for
+ * every token of the T axis (N * T tokens without cu_seqlens), where, with
+ * m = ceil(T / 2^21), S = 2 N + 2 m + 1 with cu_seqlens and 2 m N + 1 without (S <= 1024;
+ * kda_chunk_fwd_workspace_size returns at least this). A smaller workspace, dv = 64,
+ * dk = 64 and dt = KDA_F32 run on the float32 kernel.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* initial_state, float* final_state,

@@ -18,6 +18,7 @@ from .generate import (  # noqa: F401
     Cotangents,
     DecodeInputs,
     GateInputs,
+    LongChainInputs,
     WorkloadConfig,
     bf16_round,
     decode_step_inputs,
@@ -25,5 +26,7 @@ from .generate import (  # noqa: F401
     make_chunk_inputs,
     make_cotangents,
     make_gate_inputs,
+    make_long_chain_inputs,
+    set_floor,
     varlen_lengths,
 )

@@ -319,3 +319,60 @@ def make_cotangents(cfg: WorkloadConfig, n_seqs: int) -> Cotangents:
         do = bf16_round(do)
     dsT = (np.float32(0.1) * _blocks(sd, 17, (n_seqs, H), (dk, dv), _normal)).astype(np.float32)
     return Cotangents(do, dsT)
+
+
+@dataclass
+class LongChainInputs:
+    """Device tensors of one packed axis of T tokens (B = 1): q, k, v bf16 [1, H, T, 128],
+    g float32 [1, H, T, 128], beta float32 [1, H, T] (KDA) or erase / write float32
+    [1, H, T, 128] (Gated Delta Rule-2), s0 float32 [N, H, 128, 128] or None."""
+    q: object
+    k: object
+    v: object
+    g: object
+    beta: object
+    erase: object
+    write: object
+    s0: object
+
+
+def make_long_chain_inputs(T: int, H: int, seed: int, device, gdr2: bool = False,
+                           n_seqs: int = 1, random_s0: bool = True) -> LongChainInputs:
+    """Inputs of the long-chain cases, drawn on ``device`` with torch's seeded generator (an
+    axis of millions of tokens takes too long to draw on the host). Same distributions as
+    ``make_chunk_inputs``: q and k unit-norm rows of normals, v normals (the three rounded to
+    bf16), beta and the Gated Delta Rule-2 gates sigmoids of normals, g the per-channel log
+    decay -exp(N(0, 1) - 3) floored at G_FLOOR, s0 normals times 0.02. Callers place runs of
+    g = G_FLOOR themselves (``set_floor``)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def normal(*shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit_rows():
+        x = normal(1, H, T, 128)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(torch.bfloat16)
+
+    q = unit_rows()
+    k = unit_rows()
+    v = normal(1, H, T, 128).to(torch.bfloat16)
+    g = normal(1, H, T, 128)
+    g -= 3.0
+    g.exp_().neg_().clamp_(min=G_FLOOR)
+    beta = erase = write = None
+    if gdr2:
+        erase = torch.sigmoid(normal(1, H, T, 128))
+        write = torch.sigmoid(normal(1, H, T, 128))
+    else:
+        beta = torch.sigmoid(normal(1, H, T))
+    s0 = normal(n_seqs, H, 128, 128) * 0.02 if random_s0 else None
+    return LongChainInputs(q, k, v, g, beta, erase, write, s0)
+
+
+def set_floor(g, start: int, length: int) -> None:
+    """Sets g = G_FLOOR on every head and channel of tokens start .. start + length - 1 of a
+    [1, H, T, dk] log-decay tensor (in place)."""
+    g[:, :, start:start + length] = G_FLOOR

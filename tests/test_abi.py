@@ -58,19 +58,37 @@ def test_debug_library_exports_every_declared_symbol():
     assert chunk_call_on(lib, dk=96) == kda.KDA_ERR_UNSUPPORTED
 
 
+def plan_words_bytes(N, H, S):
+    words = 8 + (N + 1) + 2 * (S + 1) + 4 * H * S
+    return -(-4 * words // 256) * 256
+
+
+def long_chain_slots(N, T, packed):
+    """Slots kda.h requires for T axes of 2^22 tokens or more (0 below)."""
+    if T < 1 << 22:
+        return 0
+    m = -(-T // (1 << 21))
+    return (2 * N + 2 * m if packed else 2 * m * N) + 1
+
+
 def segment_plan_bytes(B, H, T, N, packed, dk=128, cus=256):
     """The segment plan's recommended workspace as kda.h states it: plan words for a capacity
     of S slots, the states and transitions of S segments per head, and rows of carried-back
-    queries per head (a whole T axis per sequence with fewer chains than compute units,
-    else a quarter of the T axis)."""
+    queries per head (a whole T axis per sequence with fewer chains than compute units or
+    past 2^22 tokens, else a quarter of the T axis)."""
     C = -(-T // 64)
-    xmin = max(8, -(-C // 64))
+    xmin = min(1 << 15, max(8, -(-C // 64)))
     S_all = min(1024, N + N // 8 + -(-C // xmin) + 1)
-    S = max(N, min(S_all, N + -(-cus // H) + 1))
-    words = 8 + (N + 1) + 2 * (S + 1) + 4 * H * S
-    plan = -(-4 * words // 256) * 256
-    rows = (T if packed else N * T) if N * H < cus else -(-T // 4)
-    return plan + 3 * S * H * dk * dk * 4 + rows * H * dk * 2
+    S = max(long_chain_slots(N, T, packed), N, min(S_all, N + -(-cus // H) + 1))
+    rows = (T if packed else N * T) if N * H < cus or T >= 1 << 22 else -(-T // 4)
+    return plan_words_bytes(N, H, S) + 3 * S * H * dk * dk * 4 + rows * H * dk * 2
+
+
+def long_chain_min_bytes(H, T, N, packed, dk=128):
+    """The smallest workspace kda.h states for T axes of 2^22 tokens or more."""
+    S = long_chain_slots(N, T, packed)
+    rows = T if packed else N * T
+    return plan_words_bytes(N, H, S) + 3 * S * H * dk * dk * 4 + rows * H * dk * 2
 
 
 def test_workspace_size():
@@ -102,6 +120,33 @@ def test_workspace_size():
     # num_seqs > 0 describes a packed call, which has B = 1: any other B gets no workspace
     assert kda.kda_chunk_fwd_workspace_size(4, 1, 2048, 128, 128, 4, kda.KDA_BF16) == 0
     assert kda.kda_chunk_fwd_workspace_size(2, 4, 8192, 128, 128, 2, kda.KDA_BF16) == 0
+
+
+@pytest.mark.parametrize("B,H,T,N,packed", [
+    (1, 1, (1 << 22) + 5000, 1, True),      # one sequence past the whole-chain bound
+    (1, 32, (1 << 22) + 64, 8, True),       # packed: S = 2 N + 2 m + 1 exceeds the usual cap
+    (2, 4, (1 << 22) + 64, 2, False),       # equal lengths: S = 2 m N + 1, rows N T
+    (1, 2, 1 << 24, 3, True),               # Xmin at its bound of 2^15 chunks
+])
+def test_workspace_size_long_chains(B, H, T, N, packed):
+    """T axes of 2^22 tokens or more: the segment plan with items of at most 2^21 tokens;
+    the recommendation covers kda.h's minimum."""
+    got = kda.kda_chunk_fwd_workspace_size(B, H, T, 128, 128, N if packed else 0, kda.KDA_BF16)
+    assert got == segment_plan_bytes(B, H, T, N, packed)
+    assert got >= long_chain_min_bytes(H, T, N, packed)
+
+
+def test_workspace_size_long_chains_fp32_path():
+    """Long chains the segment plan cannot take get no workspace (the float32 path): dv = 64,
+    fp32, and plans whose minimum exceeds 1024 slots."""
+    T = (1 << 22) + 64
+    assert kda.kda_chunk_fwd_workspace_size(1, 4, T, 128, 64, 1, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_fwd_workspace_size(1, 4, T, 128, 128, 1, kda.KDA_F32) == 0
+    assert long_chain_slots(600, T, True) > 1024
+    assert kda.kda_chunk_fwd_workspace_size(1, 1, T, 128, 128, 600, kda.KDA_BF16) == 0
+    # just below the bound, whole chains as before
+    assert kda.kda_chunk_fwd_workspace_size(1, 1, (1 << 22) - 64, 128, 128, 1, kda.KDA_BF16) == \
+        segment_plan_bytes(1, 1, (1 << 22) - 64, 1, True)
 
 
 DUMMY = 0x1000  # never dereferenced: every call below is rejected on the host
