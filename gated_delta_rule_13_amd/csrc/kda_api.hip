@@ -189,7 +189,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     if (seg_long || (workspace_bytes > 0 && (packed || N * H < a.cus) && sp_min > 0 &&
                      workspace_bytes >= sp_min)) {
       err = kda::launch_chunk_mfma_segplan(a, per_channel, workspace, workspace_bytes, stream);
-    } else if (workspace_bytes > 0 && !erase && seg > 0 && workspace_bytes >= seg) {
+    } else if (workspace_bytes > 0 && (!erase || dv != dk) && seg > 0 && workspace_bytes >= seg) {
       err = kda::launch_chunk_mfma_segmented(a, per_channel, workspace, stream);
     } else {
       // the work list of packed sequences when it fits (chunk_plan_bytes is 0 past the

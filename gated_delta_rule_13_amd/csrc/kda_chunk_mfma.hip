@@ -319,7 +319,10 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
         S_acc[c][m][e] = TRANS ? (ch == col[c] ? 1.f : 0.f)
                                : (s0p ? s0p[(size_t)ch * DV + col[c]] : 0.f);
       }
-  const rsrc_t wsrc = GDR2 ? make_rsrc(a.write + row0 * DV, (uint32_t)tr.len * DV * 4) : vsrc;
+  // (the transition reads no write gates either: its DV = dk may differ from their width)
+  const rsrc_t wsrc = GDR2 ? make_rsrc(a.write + (TRANS ? 0 : row0 * DV),
+                                       TRANS ? 0u : (uint32_t)tr.len * DV * 4)
+                           : vsrc;
   // KDA: value row pieces of the four blocks (token 16 I + rr at vrow + I * 16 DV * 2 bytes)
   // and the selectors that turn them into -V; Gated Delta Rule-2: values and write gates in
   // the accumulator layout (w * V is formed on the vector ALU)
@@ -1030,7 +1033,8 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
 
 template <int NS, int NT, bool PER_CHANNEL, int MODE>
 hipError_t launch_ns(const ChunkArgs& a, unsigned grid, hipStream_t stream) {
-  if constexpr (MODE == kModeOut || MODE == kModeHist) {
+  if constexpr (MODE == kModeOut || MODE == kModeHist || MODE == kModeState ||
+                MODE == kModeTrans) {
     if (a.erase) {
       chunk_mfma_kernel<NS, NT, PER_CHANNEL, true, MODE>
           <<<dim3(grid), dim3(64 * (kPrepWaves + NS)), 0, stream>>>(a);
@@ -1521,7 +1525,9 @@ hipError_t launch_chunk_mfma(const ChunkArgs& args, bool per_channel, hipStream_
 hipError_t launch_chunk_mfma_segmented(const ChunkArgs& args, bool per_channel, void* ws,
                                        hipStream_t stream) {
   ChunkArgs a = args;
-  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || a.erase) return hipErrorInvalidValue;
+  // Gated Delta Rule-2 at dv = dk takes the segment plan instead (no kModePair variant)
+  if (!chunk_mfma_supports(a.dk, a.dv, a.T) || (a.erase && a.dv == kDK))
+    return hipErrorInvalidValue;
   int L, P;
   chunk_seg_config(a.N, a.H, a.T, a.dv, a.cus, L, P);
   if (L == 0) return hipErrorInvalidValue;

@@ -109,7 +109,7 @@ typedef enum {
  *    L >= 512 a multiple of 64); each segment but the last gets B and A as above,
  *    S_{s+1} = A_s S_s + B_s gives every start state, then all segments compute their
  *    outputs in parallel. Workspace: N H P (2 dk dv + dk^2) * 4 bytes (a smaller workspace
- *    runs without these segments). Not used by kda_gdr2_chunk_fwd.
+ *    runs without these segments). kda_gdr2_chunk_fwd takes it at dv = 64.
  *  - Otherwise, packed sequences (num_seqs > 0, at most 1024): a work list of
  *    4 * (1 + 2 * num_seqs * H) bytes rounded up to 256, filled on the device by a small
  *    scheduling kernel: it splits the value columns of the longest sequences' chains over

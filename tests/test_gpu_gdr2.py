@@ -59,19 +59,24 @@ def test_gdr2_varlen_t65536_all_chains():
     print(f"{cfg.name}: all {x.n_seqs * cfg.H} chains, err o={worst[0]:.2e} S={worst[1]:.2e}")
 
 
-def test_gdr2_segmented_matches_oracle_and_whole_chains():
-    """Few chains for the device: the segment plan cuts the long sequences; the later
-    segments run from the zero state and as transitions (zero values, so the write gate
-    leaves them untouched) and their outputs are corrected."""
+@pytest.mark.parametrize("dv", [128, 64])
+def test_gdr2_segmented_matches_oracle_and_whole_chains(dv):
+    """Few chains for the device: long sequences are cut into segments. dv = 128, the segment
+    plan: the later segments run from the zero state and as transitions (zero values, so the
+    write gate leaves them untouched) and their outputs are corrected. dv = 64: segments of
+    equal length get their end states from zero and their transitions, a chain over them
+    gives every start state, and every segment is re-run from it."""
     lens = [5000, 3000, 800, 1]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), num_seqs=0, pin_frac=0.05, seed=57,
-                                        gates="gdr2")
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=int(cu[-1]), dv=dv, num_seqs=0, pin_frac=0.05,
+                                        seed=57, gates="gdr2")
     x = make_chunk_inputs(cfg)
     x.cu_seqlens = cu
-    x.s0 = np.random.default_rng(5).standard_normal((len(lens), 2, 128, 128)).astype(
+    x.s0 = np.random.default_rng(5).standard_normal((len(lens), 2, 128, dv)).astype(
         np.float32) * np.float32(0.02)
-    note("gdr2 segmented")
+    ws = kda.kda_chunk_fwd_workspace_size(1, 2, int(cu[-1]), 128, dv, len(lens), kda.KDA_BF16)
+    assert ws > 128 * 128 * 4, "expected a segmented path"
+    note(f"gdr2 segmented dv={dv}")
     o1, s1 = run_chunk(x, "bf16", schedule=True)
     o0, s0 = run_chunk(x, "bf16", schedule=False)
     check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], "gdr2 segmented")
