@@ -20,7 +20,8 @@ Printed (one JSON line on stdout):
                  RMSNorm) on the chunk workload's rows, against the HBM roofline
   bwd            kda_chunk_bwd (all gradients) on the chunk workload
   small_configs  kda_chunk_fwd on the tiny fp32 (B1 H2 T256 dk=dv=64), B2 H16 T4096 and
-                 GDN B1 H16 T8192 workloads
+                 GDN B1 H16 T8192 workloads and the B2 H16 T4096 shape in fp32, each with its
+                 matrix-core rate (median time) against the peak of its arithmetic type
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
 """
 
@@ -42,21 +43,22 @@ if ROOT not in sys.path:
 METRIC = "KDA fwd tokens/s at H=32,dk=dv=128,T=64K; % MFMA peak; decode HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 (matrix cores)
 CHUNK = 64
 
-# HBM traffic of one chunk-forward call (for the packed KDA workload: the segment planner,
-# the items, the segment chain and the output corrections; for Gated Delta Rule-2 the one
-# chunk launch), from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch)
+# HBM traffic of one chunk-forward call (for the packed KDA and Gated Delta Rule-2 workloads:
+# the segment planner, the items, the segment chain and the output corrections), from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch)
 # each scaled by the counter/byte ratio measured on a plain 1 GiB copy kernel in the same
 # runs. It is reported only while the kernel source is the one the counters were taken on
 # (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3699508102,
-    "kernel_sha256": "bf201340b201f9c8195bc53f95247a41547de821e8815b626cfa5d9a4087cc0e",
+    "bytes": 3800356249,
+    "kernel_sha256": "675b4c17dbd7e91f9442ef847debebfd077d8cc5e5bbb6ad970b2db3b6fee534",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5956311052,
-    "kernel_sha256": "bf201340b201f9c8195bc53f95247a41547de821e8815b626cfa5d9a4087cc0e",
+    "bytes": 5937774431,
+    "kernel_sha256": "675b4c17dbd7e91f9442ef847debebfd077d8cc5e5bbb6ad970b2db3b6fee534",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,
@@ -526,17 +528,25 @@ def main() -> int:
                 "workload": gd.name, "steps": gd.T, "us_per_step": sec / gd.T * 1e6,
                 "hbm_gbs": dgbs, "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
-    # the two smaller prefill workloads (parity-test shapes), scheduled as a caller would
+    # the smaller prefill workloads (parity-test shapes), scheduled as a caller would, and
+    # the B2 H16 T4096 shape in fp32 (the fp32 matrix-core kernel at a size that fills it)
     small = {}
-    for c in (TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192):
+    for c in (TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192,
+              KDA_B2_H16_T4096.replace(name="kda_f32_b2_h16_t4096", dtype="f32")):
         sx = make_chunk_inputs(c)
         sms, smed, _ = bench_chunk(torch, kda, sx, args.steps, args.warmup)
         sb = chunk_alg_bytes(sx)
+        sflops = chunk_alg_flops_per_head_token(c.dk, c.dv) * c.B * c.H * c.T
+        speak = MFMA_F32_PEAK_TFLOPS if c.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        stf = sflops / (smed / 1e3) / 1e12
         small[c.name] = {"ms_per_step": sms, "ms_per_step_median": smed, "dtype": c.dtype,
                          "tokens_per_s": c.B * c.T / (sms / 1e3),
-                         "hbm_gbs": sb / (sms / 1e3) / 1e9}
+                         "hbm_gbs": sb / (sms / 1e3) / 1e9,
+                         "mfma": {"achieved": stf, "peak": speak, "unit": "TFLOP/s",
+                                  "frac": stf / speak, "alg_flops_per_launch": sflops,
+                                  "time": "median"}}
         log(f"{c.name}: {sms:.3f} ms/step (median {smed:.3f}), "
-            f"{c.B * c.T / sms / 1e3:.2f} M tokens/s")
+            f"{c.B * c.T / sms / 1e3:.2f} M tokens/s, {stf:.1f} TFLOP/s of {speak:.0f}")
     result["small_configs"] = small
     if not args.no_bwd:
         bms, wsb = bench_bwd(torch, kda, x, args.steps, args.warmup)
