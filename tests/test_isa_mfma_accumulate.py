@@ -20,7 +20,7 @@ import pytest
 
 from gated_delta_rule_13_amd import build as B
 
-SOURCES = ["kda_chunk_mfma.hip", "kda_chunk_bwd.hip"]
+SOURCES = ["kda_chunk_mfma.hip", "kda_chunk_bwd.hip", "kda_chunk_f32mma.hip"]
 REG = re.compile(r"^([va])(?:(\d+)|\[(\d+):(\d+)\])$")
 
 
