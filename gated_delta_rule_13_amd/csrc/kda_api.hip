@@ -1,7 +1,9 @@
 // C ABI of libkda.so (declared in include/kda.h): argument validation on the host,
 // then dispatch to the kernels on the caller's stream. Nothing here allocates device memory
-// or synchronises the host; the state kept between calls is the per-device compute-unit
-// count below and the backward's per-device second stream (kda_chunk_bwd.hip).
+// or synchronises the host (except the KDA_DEBUG build's precondition checks, which wait for
+// their result); the state kept between calls is the per-device compute-unit count below,
+// the no-allocation entry point's static scratch array and the backward's per-device second
+// stream (kda_chunk_bwd.hip).
 #include <cstdint>
 #include <cstring>
 

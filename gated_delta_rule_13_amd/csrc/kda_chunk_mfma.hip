@@ -769,10 +769,10 @@ __device__ __forceinline__ void sort_entries(int* key, int* ea, int* eb, int n2)
     }
 }
 
-// Exclusive prefix sum of v over the kMaxPlanSeqs threads (every thread calls it with its
-// value; x is kMaxPlanSeqs + 1 words of scratch): returns the sum over lower threads and
-// leaves the total in x[kMaxPlanSeqs]. Wavefront scans by lane shifts, then the wavefront
-// totals.
+// Exclusive prefix sum of v over the BS threads of the block (every thread calls it with its
+// value; x is BS + 1 words of scratch): returns the sum over lower threads and leaves the
+// total in x[BS]. Wavefront scans by lane shifts, then the wavefront totals.
+template <int BS>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* x) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   uint32_t incl = v;
@@ -785,13 +785,13 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* x
   if (lane == 63) x[wv] = incl;
   __syncthreads();
   uint32_t before = 0, total = 0;
-  for (int i = 0; i < kMaxPlanSeqs / 64; ++i) {
+  for (int i = 0; i < BS / 64; ++i) {
     const uint32_t wt = x[i];
     if (i < wv) before += wt;
     total += wt;
   }
   __syncthreads();
-  if (t == 0) x[kMaxPlanSeqs] = total;
+  if (t == 0) x[BS] = total;
   __syncthreads();
   return before + incl - v;
 }
@@ -801,18 +801,20 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* x
 // the matrices of every slot) and its carried-back queries fit qt_rows rows per head.
 // xc_max > 0 bounds every item to xc_max chunks: sequences longer than that are always cut
 // (the host has checked that a candidate within the bound fits the workspace).
-__global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
+// BS threads (256 or 1024) plan up to BS sequences into up to BS slots, with BS candidates.
+template <int BS>
+__global__ __launch_bounds__(BS) void chunk_segplan_kernel(
     const int32_t* cu, int N, int H, int T, int cus, int slots_max, int mats_ok,
     long long qt_rows, int xc_min, int xc_max, uint32_t* plan) {
-  __shared__ int cl[kMaxPlanSeqs];     // chunks of sequence n
-  __shared__ int ln[kMaxPlanSeqs];     // tokens of sequence n
-  __shared__ int key[kMaxPlanSeqs];    // entries: chunks
-  __shared__ int ea[kMaxPlanSeqs];     //          sequence
-  __shared__ int eb[kMaxPlanSeqs];     //          segment
-  __shared__ float bnd[kMaxPlanSeqs];  // bound of candidate segment length j
-  __shared__ int bix[kMaxPlanSeqs];
-  __shared__ int ent_parts[kMaxPlanSeqs];
-  __shared__ uint32_t ent_off[kMaxPlanSeqs + 1];
+  __shared__ int cl[BS];     // chunks of sequence n
+  __shared__ int ln[BS];     // tokens of sequence n
+  __shared__ int key[BS];    // entries: chunks
+  __shared__ int ea[BS];     //          sequence
+  __shared__ int eb[BS];     //          segment
+  __shared__ float bnd[BS];  // bound of candidate segment length j
+  __shared__ int bix[BS];
+  __shared__ int ent_parts[BS];
+  __shared__ uint32_t ent_off[BS + 1];
   __shared__ int n_ent, xc_sel;
   const int t = threadIdx.x;
   uint32_t* segbase = plan + kSegHdr;
@@ -839,7 +841,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
   // candidate segment lengths xc_min + j * step (chunks), shorter than the longest sequence
   // and within the item bound
   const int hi = must_cut ? xc_max + 1 : maxc;
-  const int step = hi > xc_min ? (hi - xc_min + kMaxPlanSeqs - 1) / kMaxPlanSeqs : 1;
+  const int step = hi > xc_min ? (hi - xc_min + BS - 1) / BS : 1;
   {
     const int xc = xc_min + t * step;
     float b = 3.0e38f;
@@ -857,7 +859,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
         later += ci > xc ? ln[i] - xc * kC : 0;  // tokens past the first segment
         longest = max(longest, min(ci, xc));
       }
-      if (slots <= slots_max && slots <= kMaxPlanSeqs && later <= qt_rows)
+      if (slots <= slots_max && slots <= BS && later <= qt_rows)
         b = fmaxf((float)longest, kSegPacking * H * total / cus) +
             kSegCorrCost * H * corr / cus + kSegFixedCost + kSegChainCost * (most - 1);
     }
@@ -884,7 +886,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
     }
     __syncthreads();
     if (t == 0) {
-      for (int i = 1; i < kMaxPlanSeqs / 64; ++i)
+      for (int i = 1; i < BS / 64; ++i)
         if (bnd[i] < bnd[0] || (bnd[i] == bnd[0] && bix[i] < bix[0])) {
           bnd[0] = bnd[i];
           bix[0] = bix[i];
@@ -893,22 +895,24 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
     __syncthreads();
   }
   if (t == 0) {
-    // the halves schedule (as chunk_plan_kernel) and its bound
-    double total = 0.0;
-    for (int i = 0; i < N; ++i) total += (double)key[i] * H;
+    // the halves schedule (as chunk_plan_kernel) and its bound, in fp32 (chunk counts times
+    // H stay far below 2^24 per sequence; the sums only rank schedules)
+    const float rcus = 1.f / (float)cus, hc = (float)kHalfCost;
+    float total = 0.f;
+    for (int i = 0; i < N; ++i) total += (float)key[i] * (float)H;
     int ns = 0;
-    double maxhalf = 0.0;
+    float maxhalf = 0.f;
     while (ns < N && key[ns] > 0) {
-      const double c0 = key[ns], next = ns + 1 < N ? key[ns + 1] : 0.0;
-      const double bound = fmax(fmax(c0, maxhalf), total / cus);
-      const double total2 = total + H * (2.0 * kHalfCost - 1.0) * c0;
-      const double maxhalf2 = fmax(maxhalf, kHalfCost * c0);
-      if (!(fmax(fmax(next, maxhalf2), total2 / cus) < 0.98 * bound)) break;
+      const float c0 = (float)key[ns], next = ns + 1 < N ? (float)key[ns + 1] : 0.f;
+      const float bound = fmaxf(fmaxf(c0, maxhalf), total * rcus);
+      const float total2 = total + (float)H * (2.f * hc - 1.f) * c0;
+      const float maxhalf2 = fmaxf(maxhalf, hc * c0);
+      if (!(fmaxf(fmaxf(next, maxhalf2), total2 * rcus) < 0.98f * bound)) break;
       total = total2;
       maxhalf = maxhalf2;
       ++ns;
     }
-    const double half_bound = fmax(fmax(ns < N ? key[ns] : 0.0, maxhalf), total / cus);
+    const float half_bound = fmaxf(fmaxf(ns < N ? (float)key[ns] : 0.f, maxhalf), total * rcus);
     const bool any = bnd[0] < 3.0e38f;
     xc_sel = any && (must_cut || bnd[0] < kSegMinGain * half_bound) ? xc_min + bix[0] * step : 0;
     plan[1] = (uint32_t)xc_sel;
@@ -946,8 +950,8 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
   } else {
     // segments of every sequence, in sequence order (slot = segbase[n] + k)
     const int ns_t = t < N ? (cl[t] > xc ? (cl[t] + xc - 1) / xc : 1) : 0;
-    const uint32_t base = block_exclusive_scan((uint32_t)ns_t, ent_off);
-    const int slots = (int)ent_off[kMaxPlanSeqs];
+    const uint32_t base = block_exclusive_scan<BS>((uint32_t)ns_t, ent_off);
+    const int slots = (int)ent_off[BS];
     if (t < N) {
       segbase[t] = base;
       for (int k = 0; k < ns_t; ++k) {
@@ -965,12 +969,12 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
       const int len = ln[ea[t]], k = eb[t];
       units = (uint32_t)(min(xc * kC, len - k * xc * kC) + kSegGroup - 1) / kSegGroup;
     }
-    const uint32_t uoff = block_exclusive_scan(units, ent_off);
+    const uint32_t uoff = block_exclusive_scan<BS>(units, ent_off);
     if (t < slots) corr_off[t] = uoff;
     if (t == 0) {
-      corr_off[slots] = ent_off[kMaxPlanSeqs];
+      corr_off[slots] = ent_off[BS];
       plan[2] = (uint32_t)slots;
-      plan[3] = ent_off[kMaxPlanSeqs];
+      plan[3] = ent_off[BS];
     }
     // rows of carried-back queries of every slot (later segments only), in slot order
     uint32_t qrows = 0;
@@ -978,11 +982,11 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
       const int len = ln[ea[t]], k = eb[t];
       qrows = (uint32_t)min(xc * kC, len - k * xc * kC);
     }
-    const uint32_t qo = block_exclusive_scan(qrows, ent_off);
+    const uint32_t qo = block_exclusive_scan<BS>(qrows, ent_off);
     if (t < slots) qoff[t] = qo;
     if (t == 0) {
-      qoff[slots] = ent_off[kMaxPlanSeqs];
-      plan[4] = ent_off[kMaxPlanSeqs];
+      qoff[slots] = ent_off[BS];
+      plan[4] = ent_off[BS];
     }
     __syncthreads();
     int m2 = 1;
@@ -996,9 +1000,9 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
       parts = !split ? 0 : eb[t] == 0 ? 1 : 2;
       ent_parts[t] = parts;
     }
-    const uint32_t eoff = block_exclusive_scan(t < slots ? (uint32_t)H * (parts == 2 ? 2 : 1) : 0u,
+    const uint32_t eoff = block_exclusive_scan<BS>(t < slots ? (uint32_t)H * (parts == 2 ? 2 : 1) : 0u,
                                                ent_off);
-    const uint32_t tot = ent_off[kMaxPlanSeqs];
+    const uint32_t tot = ent_off[BS];
     __syncthreads();
     if (t < slots) ent_off[t] = eoff;
     if (t == 0) {
@@ -1009,7 +1013,7 @@ __global__ __launch_bounds__(kMaxPlanSeqs) void chunk_segplan_kernel(
     __syncthreads();
   }
   const uint32_t n_items = ent_off[n_ent];
-  for (uint32_t i = t; i < n_items; i += kMaxPlanSeqs) {
+  for (uint32_t i = t; i < n_items; i += BS) {
     int lo = 0, hi = n_ent - 1;  // entry holding item i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -1379,7 +1383,7 @@ static size_t segplan_mats_bytes(int H, int cap) { return (size_t)3 * cap * H * 
 
 // Chains too long for whole-chain items: the slots and carried-back-query rows per head that
 // a plan needs at the least. The planner's largest candidate within the item bound is at
-// least 0.999 kMaxItemTokens long (its candidates are at most 32 chunks apart), so with
+// least 0.99 kMaxItemTokens long (its candidates are at most 129 chunks apart), so with
 // m = ceil(T / kMaxItemTokens) >= 2, N packed sequences of T tokens in all take at most
 // 2 N + 2 m slots and N sequences of T tokens each at most 2 m slots apiece; every token past
 // a first segment needs a row.
@@ -1472,11 +1476,17 @@ hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, vo
   a.seg_len = 0;
   a.nseg = 1;
   a.split_all = 0;
-  chunk_segplan_kernel<<<1, kMaxPlanSeqs, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, sm,
-                                                       L.mats_ok ? 1 : 0, L.qt_rows,
-                                                       segplan_xc_min(a.T),
-                                                       segplan_long(a.T) ? kMaxItemTokens / kC : 0,
-                                                       a.plan);
+  // a 256-thread planner when the sequences and the slot capacity fit it (fewer wavefronts
+  // at every barrier), else the 1024-thread one
+  const int xc_max = segplan_long(a.T) ? kMaxItemTokens / kC : 0;
+  if (a.N <= 256 && sm <= 256)
+    chunk_segplan_kernel<256><<<1, 256, 0, stream>>>(a.cu, a.N, a.H, a.T, a.cus, sm,
+                                                     L.mats_ok ? 1 : 0, L.qt_rows,
+                                                     segplan_xc_min(a.T), xc_max, a.plan);
+  else
+    chunk_segplan_kernel<kMaxPlanSeqs><<<1, kMaxPlanSeqs, 0, stream>>>(
+        a.cu, a.N, a.H, a.T, a.cus, sm, L.mats_ok ? 1 : 0, L.qt_rows, segplan_xc_min(a.T),
+        xc_max, a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(2 * (size_t)a.H * sm);  // the largest plan
