@@ -337,13 +337,15 @@ class LongChainInputs:
 
 
 def make_long_chain_inputs(T: int, H: int, seed: int, device, gdr2: bool = False,
-                           n_seqs: int = 1, random_s0: bool = True) -> LongChainInputs:
+                           n_seqs: int = 1, random_s0: bool = True,
+                           gate: str = "channel") -> LongChainInputs:
     """Inputs of the long-chain cases, drawn on ``device`` with torch's seeded generator (an
     axis of millions of tokens takes too long to draw on the host). Same distributions as
     ``make_chunk_inputs``: q and k unit-norm rows of normals, v normals (the three rounded to
     bf16), beta and the Gated Delta Rule-2 gates sigmoids of normals, g the per-channel log
-    decay -exp(N(0, 1) - 3) floored at G_FLOOR, s0 normals times 0.02. Callers place runs of
-    g = G_FLOOR themselves (``set_floor``)."""
+    decay -exp(N(0, 1) - 3) floored at G_FLOOR ([1, H, T, 128], or [1, H, T] with
+    gate="head"), s0 normals times 0.02. Callers place runs of g = G_FLOOR themselves
+    (``set_floor``)."""
     import torch
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -359,7 +361,7 @@ def make_long_chain_inputs(T: int, H: int, seed: int, device, gdr2: bool = False
     q = unit_rows()
     k = unit_rows()
     v = normal(1, H, T, 128).to(torch.bfloat16)
-    g = normal(1, H, T, 128)
+    g = normal(1, H, T, 128) if gate == "channel" else normal(1, H, T)
     g -= 3.0
     g.exp_().neg_().clamp_(min=G_FLOOR)
     beta = erase = write = None
@@ -373,6 +375,6 @@ def make_long_chain_inputs(T: int, H: int, seed: int, device, gdr2: bool = False
 
 
 def set_floor(g, start: int, length: int) -> None:
-    """Sets g = G_FLOOR on every head and channel of tokens start .. start + length - 1 of a
-    [1, H, T, dk] log-decay tensor (in place)."""
+    """Sets g = G_FLOOR on every head (and channel) of tokens start .. start + length - 1 of a
+    [1, H, T, dk] or [1, H, T] log-decay tensor (in place)."""
     g[:, :, start:start + length] = G_FLOOR

@@ -42,9 +42,10 @@ def call(x, cu, N, H, T):
     o = torch.full((1, H, T, DV), float("nan"), dtype=torch.bfloat16, device=dev())
     sT = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev())
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    gm = kda.KDA_GATE_PER_CHANNEL if x.g.dim() == 4 else kda.KDA_GATE_PER_HEAD
     head = (ptr(x.q), ptr(x.k), ptr(x.v), ptr(x.g))
     tail = (ptr(x.s0), ptr(sT), ptr(o), ptr(cu), num, 1, H, T, DK, DV, kda.KDA_BF16,
-            kda.KDA_GATE_PER_CHANNEL, ptr(ws), nbytes, torch.cuda.current_stream().cuda_stream)
+            gm, ptr(ws), nbytes, torch.cuda.current_stream().cuda_stream)
     if x.erase is not None:
         st = kda.kda_gdr2_chunk_fwd(*head, ptr(x.erase), ptr(x.write), *tail)
     else:
@@ -91,15 +92,16 @@ def windows(seq_start, seq_len, xt, extra=()):
     return sorted(set(out))
 
 
-@pytest.mark.parametrize("gdr2", [False, True], ids=["kda", "gdr2"])
-def test_long_single_sequence(gdr2):
-    """One sequence of 2^22 + 3000 tokens (two heads, random initial state): every output is
-    written, the plan cuts it into items within the bound, and windows across its segment
-    boundaries, the former whole-chain bound and its end match the oracle, as does the final
-    state."""
+@pytest.mark.parametrize("kind", ["kda", "gdr2", "gdn"])
+def test_long_single_sequence(kind):
+    """One sequence of 2^22 + 3000 tokens (two heads, random initial state), with KDA, Gated
+    Delta Rule-2 or one decay per head (Gated DeltaNet): every output is written, the plan
+    cuts it into items within the bound, and windows across its segment boundaries, the
+    former whole-chain bound and its end match the oracle, as does the final state."""
     H, T = 2, (1 << 22) + 3000
-    note(f"long chain: one sequence of {T} tokens, H={H}, {'gdr2' if gdr2 else 'kda'}")
-    x = make_long_chain_inputs(T, H, seed=4101 + gdr2, device=dev(), gdr2=gdr2)
+    note(f"long chain: one sequence of {T} tokens, H={H}, {kind}")
+    x = make_long_chain_inputs(T, H, seed=4101 + ["kda", "gdr2", "gdn"].index(kind), device=dev(),
+                               gdr2=kind == "gdr2", gate="head" if kind == "gdn" else "channel")
     # the plan's segment length depends on the lengths only: learn it from a first call, which
     # also checks the first tokens from the true initial state
     o, _, hdr = call(x, None, 1, H, T)

@@ -89,3 +89,28 @@ def test_decode_step_equals_one_token_forward():
 
 def test_gates_pins():
     pins.pins_gates()
+
+
+@pytest.mark.parametrize("kind", ["channel", "head", "gdr2"])
+def test_a_floor_run_forgets_the_state(kind):
+    """The premise of the long-chain GPU checks, on the oracle: after 32 tokens of the floor
+    decay g = -5 on every channel, the outputs no longer depend on the state that entered the
+    run (each token map has norm at most 2 e^-5 for unit keys and gates in [0, 1], so the
+    entering state is scaled by less than 1e-60), while before the run's end they still do.
+    The large initial state (Frobenius norm about 4000) makes any leak visible."""
+    q, k, v, g, beta, s0 = pins.case(260, 128, 128, seed=77, gate="channel" if kind != "head"
+                                     else "head")
+    s0 = s0 * 100.0
+    rng = np.random.default_rng(78)
+    ew = {} if kind != "gdr2" else {"erase": rng.random((260, 128)), "write": rng.random((260, 128))}
+    g = g.copy()
+    g[100:132] = -5.0
+    o_full, S_full = c_oracle(q, k, v, g, beta, s0=s0, **ew)
+    cut = {n: (a[100:] if a.ndim else a) for n, a in ew.items()}
+    o_cut, S_cut = c_oracle(q[100:], k[100:], v[100:], g[100:], beta[100:], **cut)
+    after, during = o_full[132:], o_full[100:132]
+    scale = float(np.max(np.abs(after)))
+    assert np.max(np.abs(after - o_cut[32:])) <= 1e-12 * scale
+    assert np.max(np.abs(S_full - S_cut)) <= 1e-12 * float(np.max(np.abs(S_full)))
+    # not vacuous: inside the run the entering state still shows
+    assert np.max(np.abs(during - o_cut[:32])) > 1e-6 * float(np.max(np.abs(during)))
