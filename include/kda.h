@@ -166,7 +166,8 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  * every token of the T axis (N * T tokens without cu_seqlens), where, with
  * m = ceil(T / 2^21), S = 2 N + 2 m + 1 with cu_seqlens and 2 m N + 1 without (S <= 1024;
  * kda_chunk_fwd_workspace_size returns at least this). A smaller workspace, dv = 64,
- * dk = 64 and dt = KDA_F32 run on the float32 kernel.
+ * dk = 64 and dt = KDA_F32 run on the fp32 matrix-core kernel (16x16x4 fp32 products, 64-bit
+ * addressing, no length limit).
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* initial_state, float* final_state,

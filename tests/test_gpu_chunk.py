@@ -418,13 +418,14 @@ def test_more_sequences_than_one_plan_sorts():
     check_chains(x, o, sT, oracle_chains(x), TOL["bf16"], "1100 sequences")
 
 
-@pytest.mark.parametrize("T", [(1 << 22) - 64, (1 << 22) + 64], ids=["matrix-core", "fp32"])
+@pytest.mark.parametrize("T", [(1 << 22) - 64, (1 << 22) + 64], ids=["bf16-whole-chains", "fp32"])
 def test_longest_t_axis(T):
-    """The longest T axis the matrix-core kernel takes (a chain's per-channel decay, T x dk
-    fp32, must stay under 2^31 bytes: T < 2^22) and one just past it, which the fp32 kernel
-    takes, as packed sequences of 200 to 400 tokens: sampled sequences at the start, the
-    middle and the end of the axis (byte offsets past 2^31) match the oracle. The inputs are
-    a 65,536-token draw repeated along T."""
+    """The longest T axis the bf16 kernel takes with whole-chain items (a chain's per-channel
+    decay, T x dk fp32, must stay under 2^31 bytes: T < 2^22) and one just past it, which
+    (about 14,000 packed sequences, more than one segment plan holds) the fp32 matrix-core
+    kernel takes, as packed sequences of 200 to 400 tokens: sampled sequences at the start,
+    the middle and the end of the axis (byte offsets past 2^31) match the oracle. The inputs
+    are a 65,536-token draw repeated along T."""
     rng = np.random.default_rng(92)
     lens = []
     while sum(lens) < T:
