@@ -138,6 +138,10 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !g || !o) return KDA_ERR_INVALID_ARG;
   if (erase ? !write : !beta) return KDA_ERR_INVALID_ARG;
+  // the kernels move token rows as 16-byte vectors
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+      (erase && (!aligned16(erase) || !aligned16(write))))
+    return KDA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;

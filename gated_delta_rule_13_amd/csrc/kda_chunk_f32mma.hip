@@ -6,27 +6,28 @@
 // The algorithm is the chunkwise form of "Token Mixer I", section "Kimi Delta Attention"
 // (WY representation, UT transform, inter-chunk state update, chunk output), taken over
 // blocks of 16 tokens. With G_t the block-local inclusive cumulative log decay per key
-// channel and R = G_7:
+// channel and G_15 its value at the block's end:
 //   A_qk[i][j] = sum_c q_i[c] k_j[c] e^{G_i[c] - G_j[c]}           (j <= i)
 //   A_kk[i][j] = sum_c k_i[c] k_j[c] e^{G_i[c] - G_j[c]}           (j <  i)
 //   Tm = (I + Diag(beta) A_kk)^-1,   V' = Tm Diag(beta) (V - (K e^G) S)
 //   O  = (Q e^G) S + A_qk V',        S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V'
-// The decay weights of A_qk and A_kk are split at the block's middle,
-// e^{G_i - G_j} = e^{G_i - R} e^{R - G_j}; with g >= -5 each factor lies in [e^-40, e^40]
-// and every other factor in [e^-80, 1], all inside the fp32 range, so nothing is divided by
-// a decay. Tm is the exact nilpotent product (I - N)(I + N^2)(I + N^4)(I + N^8) on the
-// matrix cores.
+// The decay weight of A_qk and A_kk is split at the block's end,
+// e^{G_i - G_j} = (e^{G_i} / e^{G_15}) e^{G_15 - G_j}: with g >= -5 the left factor lies in
+// [1, e^75] and every other factor in [e^-80, 1], all inside the fp32 range, so nothing is
+// divided by a decay smaller than e^-80. Tm is the exact nilpotent product
+// (I - N)(I + N^2)(I + N^4)(I + N^8) on the matrix cores.
 //
 // Gated Delta Rule-2 ("Token Mixer I", section "Gated DeltaNet-2"): the read side takes the
 // erase-gated keys b * k in A_kk and in the prediction, beta is 1, and the values are the
 // write-gated w * V.
 //
-// One 256-thread workgroup per (chain, 64 value columns); wavefront w owns value columns
-// 16 w .. 16 w + 15 of the workgroup's and their dk x 16 slice of S in accumulator registers.
-// Per block: the inputs (prefetched into registers during the previous block) go to LDS,
-// the cumulative decay and the decayed factors are formed there, wavefront 0 forms A_qk and
-// wavefront 1 A_kk and Tm while every wavefront forms its (K e^G) S and (Q e^G) S; then
-// V', the outputs and the state update. Plain 64-bit addressing: any T.
+// One workgroup per (chain, 64 value columns), six wavefronts in two roles:
+//  - two prep wavefronts, one per 16-token block of the next 32 tokens: each loads its block,
+//    forms the cumulative decay and the decayed operands in LDS, then A_qk and the inverse;
+//  - four state wavefronts, each owning 16 value columns and their dk x 16 slice of S in
+//    accumulator registers, run the two blocks of the current 32 tokens from those operands.
+// The operands of 32 tokens are double-buffered; one workgroup barrier per 32 tokens. Plain
+// 64-bit addressing: any T.
 //
 // Operand layouts of the 16x16x4 product D[i][j] += sum_k A[i][k] B[k][j]: lane 16 p + r
 // gives A[r][p] and B[p][r] and holds D[4 p + e][r]. A state tile S[16 m + 4 p + e][col r]
@@ -41,88 +42,197 @@
 namespace kda {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kB = 16;            // tokens per block
-constexpr int kCols = 64;         // value columns per workgroup (16 per wavefront)
+constexpr int kNB = 2;            // blocks per step (one per prep wavefront)
+constexpr int kStateWaves = 4;
+constexpr int kThreads = 64 * (kStateWaves + kNB);
+constexpr int kCols = 16 * kStateWaves;  // value columns per workgroup
 
-template <int DK, bool GDR2>
+// Operands of one step (kNB blocks), written by the prep wavefronts.
+template <int DK>
+struct F32Stage {
+  float qP[kNB][kB][DK + 4];      // q e^G
+  float kP[kB * kNB][DK + 4];     // (b *) k e^G, block-major rows
+  float kE[kNB][kB][DK + 1];      // k e^{G_15 - G}
+  float tot[kNB][DK];             // e^{G_15}
+  float aqk[kNB][kB][kB + 4];     // A_qk (lower, diagonal included)
+  float tm[kNB][kB][kB + 4];      // Tm
+  float v[kNB][kB][kCols + 1];    // V, or w * V, of the workgroup's columns
+  float beta[kNB][kB];
+};
+template <int DK>
 struct F32Smem {
-  float q[kB][DK];                // raw block inputs (fp32)
-  float k[kB][DK];
-  float g[kB][DK];                // log decay, then its cumulative sum G
-  float er[GDR2 ? kB : 1][GDR2 ? DK : 1];  // erase gates (Gated Delta Rule-2)
-  float v[kB][kCols + 1];         // V, or w * V, of the workgroup's columns
-  float beta[kB];
-  // (read as 16-byte vectors: aligned)
-  alignas(16) float qP[kB][DK + 4];   // q e^G
-  alignas(16) float kP[kB][DK + 4];   // (b *) k e^G
-  alignas(16) float qh[kB][DK + 4];   // q e^{G - R}
-  alignas(16) float kh[kB][DK + 4];   // (b *) k e^{G - R}
-  alignas(16) float kb[kB][DK + 4];   // k e^{R - G}
-  float kE[kB][DK + 1];               // k e^{G_15 - G}
-  alignas(16) float tot[DK];          // e^{G_15}
-  alignas(16) float aqk[kB][kB + 4];  // A_qk (lower, diagonal included)
-  alignas(16) float tm[kB][kB + 4];   // Tm
-  float nn[kB][kB + 1];               // Diag(beta) A_kk (strictly lower), for its transpose
+  F32Stage<DK> st[2];
+  float nn[kNB][kB][kB + 1];      // Diag(beta) A_kk of each prep wavefront, for its transpose
+};
+static_assert(sizeof(F32Smem<128>) <= 160 * 1024, "LDS budget of one CU");
+static_assert(offsetof(F32Stage<128>, kP) % 16 == 0 && offsetof(F32Stage<128>, kE) % 16 == 0 &&
+                  offsetof(F32Stage<128>, tot) % 16 == 0 &&
+                  offsetof(F32Stage<128>, aqk) % 16 == 0 &&
+                  offsetof(F32Stage<128>, tm) % 16 == 0 && sizeof(F32Stage<128>) % 16 == 0 &&
+                  offsetof(F32Stage<64>, kP) % 16 == 0 && offsetof(F32Stage<64>, kE) % 16 == 0 &&
+                  offsetof(F32Stage<64>, tot) % 16 == 0 &&
+                  offsetof(F32Stage<64>, aqk) % 16 == 0 &&
+                  offsetof(F32Stage<64>, tm) % 16 == 0 && sizeof(F32Stage<64>) % 16 == 0,
+              "16-byte LDS reads need aligned rows");
+
+// A prep lane holds four consecutive channels (4 cq .. 4 cq + 3) of kTPL consecutive tokens
+// (kTPL tg .. ), so that a token row's channels lie in consecutive lanes.
+template <int DK>
+struct PrepLayout {
+  static constexpr int kCL = DK / 4;      // lanes per token group
+  static constexpr int kTG = 64 / kCL;    // token groups
+  static constexpr int kTPL = kB / kTG;   // tokens per lane
 };
 
-// Registers of one block's inputs for this thread: elements [8 tid, 8 tid + 8) of the
-// block's q, k, g (and erase) rows, elements [4 tid, 4 tid + 4) of its value columns.
+// One prep wavefront's block inputs in registers.
 template <int DK, bool GDR2>
-struct F32Regs {
-  float q[8], k[8], g[8], e[GDR2 ? 8 : 1], v[4], w[GDR2 ? 4 : 1];
-  float beta;
+struct PrepRegs {
+  static constexpr int N = PrepLayout<DK>::kTPL;
+  f32x4 q[N], k[N], g[N], e[GDR2 ? N : 1];
+  f32x4 v[4], w[GDR2 ? 4 : 1];           // token lane / 4, columns 16 (lane % 4) ..
+  float beta;                            // token lane (lanes below 16)
 };
 
+template <typename TIn>
+__device__ __forceinline__ f32x4 ld4(const TIn* p) {
+  if constexpr (sizeof(TIn) == 4) {
+    return *reinterpret_cast<const f32x4*>(p);
+  } else {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                 static_cast<float>(x[3])};
+  }
+}
+
+// Loads the block of nt valid tokens starting at row `row` (tokens past nt read as identity
+// tokens: zero q, k, v, g and beta).
 template <int DK, typename TIn, bool PER_CHANNEL, bool GDR2>
-__device__ __forceinline__ void load_f32_block(F32Regs<DK, GDR2>& r, const ChunkArgs& a,
-                                               size_t row, int nt, int col0, int tid) {
-  constexpr int kPer = kB * DK / kThreads;  // 8 (dk = 128) or 4 (dk = 64)
+__device__ __forceinline__ void prep_load(PrepRegs<DK, GDR2>& r, const ChunkArgs& a,
+                                          size_t row, int nt, int col0, int lane) {
+  using L = PrepLayout<DK>;
+  const int cq = lane % L::kCL, tg = lane / L::kCL;
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
   const TIn* v = static_cast<const TIn*>(a.v);
-  const int idx = kPer * tid, t = idx / DK, c = idx % DK;
-  const bool ok = t < nt;
-  const size_t off = (row + t) * DK + c;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool in = ok && i < kPer;
-    r.q[i] = in ? to_f32(q[off + i]) : 0.f;
-    r.k[i] = in ? to_f32(k[off + i]) : 0.f;
-    r.g[i] = in ? (PER_CHANNEL ? a.g[off + i] : a.g[row + t]) : 0.f;
-    if constexpr (GDR2) r.e[i] = in ? a.erase[off + i] : 0.f;
+  for (int u = 0; u < L::kTPL; ++u) {
+    const int t = L::kTPL * tg + u;
+    const bool ok = t < nt;
+    const size_t off = (row + t) * DK + 4 * cq;
+    r.q[u] = ok ? ld4<TIn>(q + off) : zero4();
+    r.k[u] = ok ? ld4<TIn>(k + off) : zero4();
+    if constexpr (PER_CHANNEL) {
+      r.g[u] = ok ? *reinterpret_cast<const f32x4*>(a.g + off) : zero4();
+    } else {
+      const float gv = ok ? a.g[row + t] : 0.f;
+      r.g[u] = f32x4{gv, gv, gv, gv};
+    }
+    if constexpr (GDR2) r.e[u] = ok ? *reinterpret_cast<const f32x4*>(a.erase + off) : zero4();
   }
-  const int tv = tid / 16, cv = 4 * (tid % 16);
+  const int tv = lane / 4, cv = 16 * (lane % 4);
   const bool okv = tv < nt;
   const size_t offv = (row + tv) * a.dv + col0 + cv;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r.v[i] = okv ? to_f32(v[offv + i]) : 0.f;
-    if constexpr (GDR2) r.w[i] = okv ? a.write[offv + i] : 0.f;
+    r.v[i] = okv ? ld4<TIn>(v + offv + 4 * i) : zero4();
+    if constexpr (GDR2)
+      r.w[i] = okv ? *reinterpret_cast<const f32x4*>(a.write + offv + 4 * i) : zero4();
   }
-  r.beta = (!GDR2 && tid < nt) ? a.beta[row + tid] : 0.f;
+  r.beta = (!GDR2 && lane < nt) ? a.beta[row + lane] : 0.f;
 }
 
+// The cumulative decay and the decayed operands of block j of a stage (from registers).
 template <int DK, bool GDR2>
-__device__ __forceinline__ void store_f32_block(F32Smem<DK, GDR2>& sm, const F32Regs<DK, GDR2>& r,
-                                                int tid) {
-  constexpr int kPer = kB * DK / kThreads;
-  const int idx = kPer * tid, t = idx / DK, c = idx % DK;
+__device__ __forceinline__ void prep_operands(F32Stage<DK>& st, const PrepRegs<DK, GDR2>& r,
+                                              int j, int lane) {
+  using L = PrepLayout<DK>;
+  const int cq = lane % L::kCL, tg = lane / L::kCL;
+  // cumulative log decay: within the lane's tokens, then the lower token groups' totals
+  f32x4 G[L::kTPL];
+  G[0] = r.g[0];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    sm.q[t][c + i] = r.q[i];
-    sm.k[t][c + i] = r.k[i];
-    sm.g[t][c + i] = r.g[i];
-    if constexpr (GDR2) sm.er[t][c + i] = r.e[i];
+  for (int u = 1; u < L::kTPL; ++u) G[u] = G[u - 1] + r.g[u];
+  const f32x4 mine = G[L::kTPL - 1];
+  f32x4 before = zero4(), all = zero4();
+#pragma unroll
+  for (int gi = 0; gi < L::kTG; ++gi) {
+    f32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = __shfl(mine[c], cq + L::kCL * gi, 64);
+    if (gi < tg) before += o;
+    all += o;
   }
-  const int tv = tid / 16, cv = 4 * (tid % 16);
+  // e^{G_15} of the lane's channels
+  f32x4 tot;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sm.v[tv][cv + i] = GDR2 ? r.w[i] * r.v[i] : r.v[i];
-  if (tid < kB) sm.beta[tid] = GDR2 ? 1.f : r.beta;
+  for (int c = 0; c < 4; ++c) tot[c] = __expf(all[c]);
+  if (tg == 0) *reinterpret_cast<f32x4*>(&st.tot[j][4 * cq]) = tot;
+#pragma unroll
+  for (int u = 0; u < L::kTPL; ++u) {
+    const int t = L::kTPL * tg + u;
+    f32x4 qp, kp, ke;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float Gt = G[u][c] + before[c];
+      const float eG = __expf(Gt);
+      const float kr = GDR2 ? r.e[u][c] * r.k[u][c] : r.k[u][c];  // the read-side key
+      qp[c] = r.q[u][c] * eG;
+      kp[c] = kr * eG;
+      ke[c] = r.k[u][c] * __expf(all[c] - Gt);
+    }
+    *reinterpret_cast<f32x4*>(&st.qP[j][t][4 * cq]) = qp;
+    *reinterpret_cast<f32x4*>(&st.kP[kB * j + t][4 * cq]) = kp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) st.kE[j][t][4 * cq + c] = ke[c];
+  }
+  const int tv = lane / 4, cv = 16 * (lane % 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      st.v[j][tv][cv + 4 * i + c] = GDR2 ? r.w[i][c] * r.v[i][c] : r.v[i][c];
+  if (lane < kB) st.beta[j][lane] = GDR2 ? 1.f : r.beta;
 }
 
-// Row operand of lane (r, p) for the 16x16x4 products over channels 16 m + 4 p + e: the
-// four channels of row r as one vector.
+// A_qk and Tm of block j (the operands of the block are in LDS, written by this wavefront).
+// A_qk = (Q e^G / e^{G_15}) (K e^{G_15 - G})^T and A_kk likewise with the read-side key.
+template <int DK>
+__device__ __forceinline__ void prep_tiles(F32Stage<DK>& st, float (*nn)[kB + 1], int j,
+                                           int rr, int p) {
+  constexpr int NM = DK / 16;
+  f32x4 aq = zero4(), ak = zero4();
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int c0 = 16 * m + 4 * p;
+    const f32x4 ttc = *reinterpret_cast<const f32x4*>(&st.tot[j][c0]);
+    const f32x4 xq = *reinterpret_cast<const f32x4*>(&st.qP[j][rr][c0]);
+    const f32x4 xk = *reinterpret_cast<const f32x4*>(&st.kP[kB * j + rr][c0]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float rt = __builtin_amdgcn_rcpf(ttc[e]);
+      const float y = st.kE[j][rr][c0 + e];
+      aq = mfma_f32(xq[e] * rt, y, aq);
+      ak = mfma_f32(xk[e] * rt, y, ak);
+    }
+  }
+  // aq[e] = A_qk[4 p + e][rr], ak[e] = A_kk[4 p + e][rr]
+  f32x4 nc, nr;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * p + e;
+    st.aqk[j][i][rr] = rr <= i ? aq[e] : 0.f;
+    nc[e] = rr < i ? st.beta[j][i] * ak[e] : 0.f;  // N[i][rr]
+    nn[i][rr] = nc[e];
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) nr[e] = nn[rr][4 * p + e];  // N[rr][4 p + e]
+  const f32x4 inv = unit_lower_inverse(nc, nr, rr, p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st.tm[j][4 * p + e][rr] = inv[e];
+}
+
 template <int LD>
 __device__ __forceinline__ f32x4 row4(const float (*x)[LD], int r, int c) {
   return *reinterpret_cast<const f32x4*>(&x[r][c]);
@@ -131,18 +241,51 @@ __device__ __forceinline__ f32x4 row4(const float (*x)[LD], int r, int c) {
 template <int DK, typename TIn, bool PER_CHANNEL, bool GDR2>
 __global__ __launch_bounds__(kThreads) void chunk_f32mma_kernel(ChunkArgs a, int groups) {
   constexpr int NM = DK / 16;       // row tiles of S
-  __shared__ __align__(16) F32Smem<DK, GDR2> sm;
+  __shared__ __align__(16) F32Smem<DK> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rr = lane & 15, p = lane >> 4;
   const int chain = blockIdx.x / groups, grp = blockIdx.x % groups;
   const int n = chain / a.H, h = chain % a.H;
   const int DV = a.dv;
   const int col0 = grp * kCols;           // the workgroup's first value column
-  const int col = col0 + 16 * wave + rr;  // this lane's value column
   const TokenRange tr = token_range(a.cu, n, a.T);
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0;
-  const size_t mat = ((size_t)n * a.H + h) * DK * DV;
+  const int nblk = (tr.len + kB - 1) / kB;
+  const int nsteps = (nblk + kNB - 1) / kNB;
 
+  if (wave >= kStateWaves) {
+    // prep wavefront j: block kNB s + j of every step s, one step ahead of the state
+    const int j = wave - kStateWaves;
+    PrepRegs<DK, GDR2> r;
+    auto load = [&](int s) {
+      const int t0 = kB * (kNB * s + j);
+      prep_load<DK, TIn, PER_CHANNEL, GDR2>(r, a, row0 + t0, tr.len - t0, col0, lane);
+    };
+    if (nsteps > 0) {
+      load(0);
+      prep_operands<DK, GDR2>(sm.st[0], r, j, lane);
+      if (nsteps > 1) load(1);
+      wave_lds_fence();
+      prep_tiles<DK>(sm.st[0], sm.nn[j], j, rr, p);
+    }
+    lds_barrier();
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + 1 < nsteps) {
+        F32Stage<DK>& st = sm.st[(s + 1) & 1];
+        prep_operands<DK, GDR2>(st, r, j, lane);
+        if (s + 2 < nsteps) load(s + 2);  // in flight during the tiles and the barrier
+        wave_lds_fence();
+        prep_tiles<DK>(st, sm.nn[j], j, rr, p);
+      }
+      lds_barrier();
+    }
+    return;
+  }
+
+  // state wavefront: value columns col .. of the workgroup's
+  const int col = col0 + 16 * wave + rr;
+  const int vc = 16 * wave + rr;
+  const size_t mat = ((size_t)n * a.H + h) * DK * DV;
   // S_acc[m][e] = S[16 m + 4 p + e][col]
   f32x4 S_acc[NM];
 #pragma unroll
@@ -150,139 +293,56 @@ __global__ __launch_bounds__(kThreads) void chunk_f32mma_kernel(ChunkArgs a, int
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       S_acc[m][e] = a.s0 ? a.s0[mat + (size_t)(16 * m + 4 * p + e) * DV + col] : 0.f;
-
-  F32Regs<DK, GDR2> regs;
-  const int nblk = (tr.len + kB - 1) / kB;
-  if (nblk > 0) load_f32_block<DK, TIn, PER_CHANNEL, GDR2>(regs, a, row0, tr.len, col0, tid);
-  for (int b = 0; b < nblk; ++b) {
-    const int nt = min(kB, tr.len - kB * b);  // tokens of this block (later ones: identity)
-    // 1. the block's inputs to LDS (every wavefront has finished the previous block: the
-    // barrier after this step orders the overwrite of the factors below)
-    store_f32_block<DK, GDR2>(sm, regs, tid);
-    __syncthreads();
-    // 2. cumulative log decay per channel
-    if (tid < DK) {
-      float run = 0.f;
+  lds_barrier();  // the first step's operands are in LDS
+  TIn* o = static_cast<TIn*>(a.o);
+  for (int s = 0; s < nsteps; ++s) {
+    const F32Stage<DK>& st = sm.st[s & 1];
 #pragma unroll
-      for (int t = 0; t < kB; ++t) {
-        run += sm.g[t][tid];
-        sm.g[t][tid] = run;
-      }
-      sm.tot[tid] = __expf(run);
-    }
-    __syncthreads();
-    // 3. the decayed factors (identity tokens have q = k = 0 and g = 0)
-    for (int idx = tid; idx < kB * DK; idx += kThreads) {
-      const int t = idx / DK, c = idx % DK;
-      const float G = sm.g[t][c], R = sm.g[kB / 2 - 1][c], GC = sm.g[kB - 1][c];
-      const float eR = __expf(G - R);
-      const float qf = sm.q[t][c], kf = sm.k[t][c];
-      const float kr = GDR2 ? sm.er[t][c] * kf : kf;  // the read-side key
-      const float eG = __expf(G);
-      sm.qP[t][c] = qf * eG;
-      sm.kP[t][c] = kr * eG;
-      sm.qh[t][c] = qf * eR;
-      sm.kh[t][c] = kr * eR;
-      sm.kb[t][c] = kf * __expf(R - G);
-      sm.kE[t][c] = kf * __expf(GC - G);
-    }
-    __syncthreads();
-    // the next block's inputs, in flight during the products below
-    if (b + 1 < nblk)
-      load_f32_block<DK, TIn, PER_CHANNEL, GDR2>(regs, a, row0 + kB * (b + 1),
-                                                 tr.len - kB * (b + 1), col0, tid);
-    // 4. wavefront 0: A_qk; wavefront 1: A_kk and Tm (LDS)
-    if (wave == 0) {
-      f32x4 acc = zero4();
+    for (int j = 0; j < kNB; ++j) {
+      const int t0 = kB * (kNB * s + j);  // the block's first token
+      // X = ((b *) K e^G) S and (Q e^G) S
+      f32x4 X = zero4(), O = zero4();
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const f32x4 x = row4<DK + 4>(sm.qh, rr, 16 * m + 4 * p);
-        const f32x4 y = row4<DK + 4>(sm.kb, rr, 16 * m + 4 * p);
+        const f32x4 xk = row4<DK + 4>(st.kP, kB * j + rr, 16 * m + 4 * p);
+        const f32x4 xq = row4<DK + 4>(st.qP[j], rr, 16 * m + 4 * p);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(x[e], y[e], acc);
+        for (int e = 0; e < 4; ++e) {
+          X = mfma_f32(xk[e], S_acc[m][e], X);
+          O = mfma_f32(xq[e], S_acc[m][e], O);
+        }
       }
-      // acc[e] = A_qk[4 p + e][rr]
+      // V' = Tm Diag(beta) (V - X): the residual tile is the B operand over tokens 4 p + e
+      f32x4 Rb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.aqk[4 * p + e][rr] = rr <= 4 * p + e ? acc[e] : 0.f;
-    } else if (wave == 1) {
-      f32x4 acc = zero4();
+      for (int e = 0; e < 4; ++e)
+        Rb[e] = st.beta[j][4 * p + e] * (st.v[j][4 * p + e][vc] - X[e]);
+      const f32x4 tmr = row4<kB + 4>(st.tm[j], rr, 4 * p);
+      const f32x4 aqr = row4<kB + 4>(st.aqk[j], rr, 4 * p);
+      f32x4 Vp = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Vp = mfma_f32(tmr[e], Rb[e], Vp);
+      // O += A_qk V'
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O = mfma_f32(aqr[e], Vp[e], O);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 4 * p + e;
+        if (t < tr.len) o[(row0 + t) * DV + col] = from_f32<TIn>(O[e]);
+      }
+      // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V'
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const f32x4 x = row4<DK + 4>(sm.kh, rr, 16 * m + 4 * p);
-        const f32x4 y = row4<DK + 4>(sm.kb, rr, 16 * m + 4 * p);
+        f32x4 s_ = S_acc[m];
+        const f32x4 tt = *reinterpret_cast<const f32x4*>(&st.tot[j][16 * m + 4 * p]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(x[e], y[e], acc);
-      }
-      f32x4 nc, nr;
+        for (int e = 0; e < 4; ++e) s_[e] *= tt[e];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * p + e;
-        nc[e] = rr < i ? sm.beta[i] * acc[e] : 0.f;  // N[i][rr]
-        sm.nn[i][rr] = nc[e];
-      }
-      wave_lds_fence();
-#pragma unroll
-      for (int e = 0; e < 4; ++e) nr[e] = sm.nn[rr][4 * p + e];  // N[rr][4 p + e]
-      const f32x4 inv = unit_lower_inverse(nc, nr, rr, p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.tm[4 * p + e][rr] = inv[e];
-    }
-    // every wavefront: X = ((b *) K e^G) S and (Q e^G) S for its columns
-    f32x4 X = zero4(), O = zero4();
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const f32x4 xk = row4<DK + 4>(sm.kP, rr, 16 * m + 4 * p);
-      const f32x4 xq = row4<DK + 4>(sm.qP, rr, 16 * m + 4 * p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        X = mfma_f32(xk[e], S_acc[m][e], X);
-        O = mfma_f32(xq[e], S_acc[m][e], O);
+        for (int e = 0; e < 4; ++e) s_ = mfma_f32(st.kE[j][4 * p + e][16 * m + rr], Vp[e], s_);
+        S_acc[m] = s_;
       }
     }
-    // this lane's values and betas, read before the barrier: the next block's step 1
-    // rewrites them once every wavefront has passed it
-    const int vc = 16 * wave + rr;
-    f32x4 vv, bb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vv[e] = sm.v[4 * p + e][vc];
-      bb[e] = sm.beta[4 * p + e];
-    }
-    __syncthreads();  // A_qk and Tm are in LDS
-    // 5. V' = Tm Diag(beta) (V - X): the residual tile is the B operand over tokens 4 p + e
-    f32x4 Rb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Rb[e] = bb[e] * (vv[e] - X[e]);
-    const f32x4 tmr = row4<kB + 4>(sm.tm, rr, 4 * p);
-    const f32x4 aqr = row4<kB + 4>(sm.aqk, rr, 4 * p);
-    f32x4 Vp = zero4();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Vp = mfma_f32(tmr[e], Rb[e], Vp);
-    // O += A_qk V'
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O = mfma_f32(aqr[e], Vp[e], O);
-    if (a.o) {
-      TIn* o = static_cast<TIn*>(a.o);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * p + e;
-        if (t < nt) o[(row0 + kB * b + t) * DV + col] = from_f32<TIn>(O[e]);
-      }
-    }
-    // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V'
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      f32x4 s_ = S_acc[m];
-      const f32x4 tt = *reinterpret_cast<const f32x4*>(&sm.tot[16 * m + 4 * p]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_[e] *= tt[e];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_ = mfma_f32(sm.kE[4 * p + e][16 * m + rr], Vp[e], s_);
-      S_acc[m] = s_;
-    }
-    // the next block's step 1 overwrites only the raw inputs, which every wavefront has read
-    // before the barrier of step 4; its steps 2 to 4 rewrite the rest after a barrier that
-    // every wavefront passes only after this step
+    lds_barrier();  // this stage is read; the next one is written
   }
   if (a.sT) {
 #pragma unroll

@@ -140,6 +140,8 @@ size_t kda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  *   initial_state float32 [N, H, dk, dv] or NULL (= zero state)
  *   final_state   float32 [N, H, dk, dv] or NULL (= not written); may equal initial_state
  *   o             [B, H, T, dv], dtype dt; written for every token of every sequence
+ *                 q, k, v, g and o (and the Gated Delta Rule-2 gates below) must be 16-byte
+ *                 aligned, as every PyTorch allocation is (else KDA_ERR_INVALID_ARG).
  *   cu_seqlens    NULL: N = B sequences of length T (batch row b is sequence b).
  *                 Otherwise a DEVICE int32 array of num_seqs + 1 offsets into the T
  *                 axis (packed variable-length sequences); B must be 1 and N = num_seqs.

@@ -189,6 +189,11 @@ def chunk_call(**over):
     (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
     (dict(dv=32), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=256, dv=256), kda.KDA_ERR_UNSUPPORTED),
+    # row arrays must be 16-byte aligned
+    (dict(q=DUMMY + 8), kda.KDA_ERR_INVALID_ARG),
+    (dict(v=DUMMY + 2), kda.KDA_ERR_INVALID_ARG),
+    (dict(g=DUMMY + 4), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=DUMMY + 8, dt=kda.KDA_F32), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_chunk_fwd_rejects(over, code):
     assert chunk_call(**over) == code
@@ -217,6 +222,8 @@ def gdr2_step_call(**over):
     (dict(q=None), kda.KDA_ERR_INVALID_ARG),
     (dict(T=0), kda.KDA_ERR_INVALID_ARG),
     (dict(dv=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(erase=DUMMY + 4), kda.KDA_ERR_INVALID_ARG),
+    (dict(write=DUMMY + 8), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_gdr2_chunk_fwd_rejects(over, code):
     assert gdr2_chunk_call(**over) == code
