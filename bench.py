@@ -53,12 +53,12 @@ CHUNK = 64
 # runs. It is reported only while the kernel source is the one the counters were taken on
 # (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3800356249,
-    "kernel_sha256": "675b4c17dbd7e91f9442ef847debebfd077d8cc5e5bbb6ad970b2db3b6fee534",
+    "bytes": 3803042198,
+    "kernel_sha256": "8eab642ac5fa1903a455c0369ecbe98de5f514820ee3989d5a4fb38f544303f8",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5937774431,
-    "kernel_sha256": "675b4c17dbd7e91f9442ef847debebfd077d8cc5e5bbb6ad970b2db3b6fee534",
+    "bytes": 5945329537,
+    "kernel_sha256": "8eab642ac5fa1903a455c0369ecbe98de5f514820ee3989d5a4fb38f544303f8",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,
