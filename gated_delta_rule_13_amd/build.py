@@ -29,9 +29,20 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The backward's gradient kernel runs one wavefront per SIMD and may hold
+# more than 256 registers; its matrix-core products keep their operands and results in the
+# architectural vector registers (otherwise every product's result is moved out of the
+# accumulation registers before the vector ALU can use it), and the accumulation registers
+# serve only as spill space.
+SOURCE_FLAGS = {
+    "kda_chunk_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str, build_dir: str, extra) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -23,18 +23,21 @@
 //   dg_s = sum_{t >= s} d log P_t + d log Gam,   dq = dQh P,   dk = dKh P + dKb / P + dKt E.
 //
 // Three launches:
-//   1. the forward state pass with the state history (kda_chunk_mfma.hip): S at every
-//      block start, bf16, in the layout of hist_chain_offset;
+//   1. the forward state pass with the state history (kda_chunk_mfma.hip): S entering
+//      every pair of blocks (the even blocks), bf16, in the layout of hist_chain_offset;
 //   2. chunk_bwd_state_kernel: the carry above, one workgroup per chain, from the last
-//      block to the first; it records dS' of every block (same layout) and writes dS_0;
-//   3. chunk_bwd_grad_kernel: every block independently from (S, dS'), one wavefront per
-//      block: dq, dk, dv, dg, dbeta.
+//      block to the first; it records dS' at the end of every pair of blocks (the odd
+//      blocks; same layout) and writes dS_0;
+//   3. chunk_bwd_grad_kernel: every pair of blocks independently from its (S, dS'), one
+//      wavefront per block, the two exchanging the state and the gradient between their
+//      blocks: dq, dk, dv, dg, dbeta.
 // Launch 2 has the forward's structure: four "prep" wavefronts prepare the operands of
 // the next 64 tokens (in reverse) while four "state" wavefronts, holding dS in matrix-core
 // accumulators, run the carry of the current 64 tokens; one barrier per 64 tokens.
 #include <stddef.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -196,7 +199,7 @@ __device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const To
   const rsrc_t dosrc =
       make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, (uint32_t)tr.len * DV * 2);
   const rsrc_t hdst = make_rsrc(static_cast<char*>(b.hist_ds) + hist_off,
-                                (uint32_t)nsteps * 4 * kDK * DV * 2);
+                                (uint32_t)nsteps * 2 * kDK * DV * 2);
   int col[NT];
   uint32_t coff[NT];  // byte offset of (token 4 p, column col) within a 64-token step
 #pragma unroll
@@ -230,7 +233,8 @@ __device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const To
 #pragma unroll
     for (int I = 3; I >= 0; --I) {
       const uint32_t blk = 4 * (uint32_t)s + I;
-      // dS' of this block: record it, and Kt dS' (dS' as the B operand, bf16)
+      // dS' of this block (recorded at the end of each pair of blocks), and Kt dS' (dS' as
+      // the B operand, bf16)
       f32x4 dU[NT];
 #pragma unroll
       for (int c = 0; c < NT; ++c) dU[c] = zero4();
@@ -240,8 +244,10 @@ __device__ __forceinline__ void carry_role(RSmem& sm, const BwdArgs& b, const To
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
           const bf16x8 db = cat8(pack4(D_acc[c][2 * ks]), pack4(D_acc[c][2 * ks + 1]));
-          const uint32_t tile = blk * (DV / 16) + (cbase + 16 * c) / 16;
-          st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, db);
+          if (I & 1) {
+            const uint32_t tile = (blk / 2) * (DV / 16) + (cbase + 16 * c) / 16;
+            st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, db);
+          }
           dU[c] = mfma32(ak, db, dU[c]);
         }
       }
@@ -361,12 +367,19 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_bwd_state_kernel
 
 // ------------------------------------------------------------ launch 3: the gradients
 
-// One wavefront per 16-token block, no barriers. The block's S and dS' are read once, one
-// 16-column value tile at a time, as stored (lane-native B operands over 32-channel
-// slabs); for each tile the wavefront forms its columns of Kh S, U, dU, dY and adds the
-// tile's share of every contraction over the value columns (dO S^T, Diag(beta) dY S^T,
-// U dS'^T, dO U^T, dY U^T and rowsum(dS' * S)) for all channels, taking S and dS'
-// transposed by products with a 0/1 selector (exact in bf16).
+// One workgroup of two wavefronts per pair of 16-token blocks, one wavefront per block.
+// The history holds, per pair, the state S_e entering the even block and the gradient dS'_o
+// reaching the end of the odd block; the even wavefront reads S_e and the odd one dS'_o, one
+// 16-column value tile at a time as stored (lane-native B operands over 32-channel slabs).
+// Per tile each first forms, from its own block, the boundary tile the other needs:
+//   even: U_e = Tm_e Diag(beta_e) (V_e - Kh_e S_e),  then  S_o = Diag(Gam_e) S_e + Kt_e^T U_e
+//   odd:  dY_o = Tm_o^T (M_o^T dO_o + Kt_o dS'_o),
+//         then  dS'_e = Diag(Gam_o) dS'_o + Qh_o^T dO_o - Kh_o^T Diag(beta_o) dY_o
+// (the forward's state step and the carry across the boundary between the blocks); after
+// one barrier each takes the tile it received, finishes its block's columns of Kh S, U, dU
+// and dY, and adds the tile's share of every contraction over the value columns (dO S^T,
+// Diag(beta) dY S^T, U dS'^T, dO U^T, dY U^T and rowsum(dS' * S)) for all channels, taking
+// S and dS' transposed by products with a 0/1 selector (exact in bf16).
 
 template <int DV>
 struct GSmem {
@@ -390,15 +403,32 @@ struct GSmem {
   float dlgam[kDK];        // d log Gam
 };
 
-// Position of work item (16-token block) `slot` of head h: sequence n and block blk, or
-// false when the slot holds no block. Sequence n's blocks take slots from
-// floor(cu[n] / 16) + n on (consecutive sequences never overlap).
-__device__ __forceinline__ bool grad_item(const ChunkArgs& a, int slot, int& n, int& blk,
+// LDS of one pair: each block's scratch, its transposed operands for the boundary tile (in
+// lane order: lane l holds the entries of the 16x16x16 A operand that lane l supplies;
+// channel tile m has the rows of the state tiles, row r being channel
+// 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4), and the boundary tiles, by tile parity.
+template <int DV>
+struct GPair {
+  GSmem<DV> w[2];            // the even block's, the odd block's
+  bf16x4 kt[8][64];          // even: Kt_e^T
+  bf16x4 qh[8][64];          // odd: Qh_o^T
+  bf16x4 kh[8][64];          // odd: Kh_o^T
+  bf16x8 bnd[2][2][4][64];   // [parity][receiver]: dS'_e for the even, S_o for the odd
+  // per block, read back per value tile rather than held in registers: Tm, Tm^T and M^T
+  // (16x16x16 A operands) and the selectors of the transposes
+  bf16x4 tm[2][3][64];
+  bf16x8 sel[2][2][64];
+};
+
+// Position of work item (pair of 16-token blocks) `slot` of head h: sequence n and pair pr,
+// or false when the slot holds no pair. Sequence n's pairs take slots from
+// floor(cu[n] / 32) + n on (consecutive sequences never overlap).
+__device__ __forceinline__ bool grad_item(const ChunkArgs& a, int slot, int& n, int& pr,
                                           TokenRange& tr) {
   if (!a.cu) {
-    const int per = (a.T + 15) / 16;
+    const int per = (a.T + 31) / 32;
     n = slot / per;
-    blk = slot % per;
+    pr = slot % per;
     if (n >= a.N) return false;
     tr = token_range(nullptr, n, a.T);
     return true;
@@ -406,13 +436,13 @@ __device__ __forceinline__ bool grad_item(const ChunkArgs& a, int slot, int& n, 
   int lo = 0, hi = a.N - 1;  // last sequence whose first slot is <= slot
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int first = min(max(a.cu[mid], 0), a.T) / 16 + mid;
+    const int first = min(max(a.cu[mid], 0), a.T) / 32 + mid;
     if (first <= slot) lo = mid; else hi = mid - 1;
   }
   n = lo;
   tr = token_range(a.cu, n, a.T);
-  blk = slot - (tr.t0 / 16 + n);
-  return blk >= 0 && blk * 16 < tr.len;
+  pr = slot - (tr.t0 / 32 + n);
+  return pr >= 0 && pr * 32 < tr.len;
 }
 
 // Selector of channels 16 hh + n out of a 32-channel slab, as the B operand of a
@@ -430,42 +460,65 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
   return cat8(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
 }
 
+// Selector of the channels 8 (n / 4) + 4 hh + n % 4 (n < 16) of a 32-channel slab: with
+// token rows of an operand X as the A operand of a 16x16x32 product (lane 16 p + r holds
+// channels 8 p + i of token r), D[4p + e][n] = X[token 4p + e][that channel], which is, in
+// lane order, the A operand of X^T's channel tile 2 ks + hh for a 16x16x16 product.
+__device__ __forceinline__ bf16x8 tile_selector(int hh, int rr, int p) {
+  const int c = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = static_cast<bf16>(8 * p + i == c ? 1.f : 0.f);
+  return b;
+}
+
 // GDR2: the Gated Delta Rule-2 gates. The read-side key Kh is then (b * k) P, beta is 1,
 // R = w * V - Kh S, dV = w * dY, and the gradients of the gates are d erase = k P * dKh and
 // d write = V * dY (instead of dbeta).
-// Two wavefronts per SIMD (at most 256 registers; about 21 KB of LDS each): measured 10%
-// faster than the one that 300 registers would allow.
+// One wavefront per SIMD (the two blocks' LDS and the exchange, about 57 KB, allow two
+// workgroups per compute unit), so each may hold up to 512 registers.
 template <int DV, bool PER_CHANNEL, bool GDR2>
-__global__ __attribute__((amdgpu_waves_per_eu(2))) __launch_bounds__(64) void
+__global__ __attribute__((amdgpu_waves_per_eu(1))) __launch_bounds__(128) void
 chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   constexpr int NCT = DV / 16;   // value tiles of the block
-  __shared__ __align__(16) GSmem<DV> sm;
+  __shared__ __align__(16) GPair<DV> sp;
   const ChunkArgs& a = b.f;
-  const int lane = threadIdx.x;
+  // the wavefront's block within the pair (0: even, 1: odd), uniform across the wavefront
+  const int odd = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int rr = lane & 15, p = lane >> 4;
+  GSmem<DV>& sm = sp.w[odd];
+  const GSmem<DV>& so = sp.w[odd ^ 1];
   const int h = blockIdx.x / slots, slot = blockIdx.x % slots;
-  int n, blk;
+  int n, pr;
   TokenRange tr;
-  if (!grad_item(a, slot, n, blk, tr)) return;
+  if (!grad_item(a, slot, n, pr, tr)) return;   // both wavefronts leave together
+  const int blk = 2 * pr + odd;
+  // tokens of this block in the sequence: 0 for the odd block of a sequence's last pair when
+  // its block count is odd; every view of that block is then empty (zeros), which makes it
+  // the identity block, and the stored gradient is the one reaching the even block's end
+  // (made a scalar explicitly: the clamp is a vector instruction, and a vector operand in
+  // the buffer descriptors below would put each of their loads in a loop over lanes)
+  const int len = __builtin_amdgcn_readfirstlane(max(0, min(16, tr.len - 16 * blk)));
   const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + 16 * (size_t)blk;
-  const int len = min(16, tr.len - 16 * blk);  // tokens of this block in the sequence
-  const size_t hoff = hist_chain_offset(a, n, h, tr) + (size_t)blk * kDK * DV * 2;
+  const size_t hoff = hist_chain_offset(a, n, h, tr) + (size_t)pr * kDK * DV * 2;
   const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.q) + row0 * kDK, len * kDK * 2);
   const rsrc_t ks_ = make_rsrc(static_cast<const bf16*>(a.k) + row0 * kDK, len * kDK * 2);
   const rsrc_t vs = make_rsrc(static_cast<const bf16*>(a.v) + row0 * DV, len * DV * 2);
-  const rsrc_t hs = make_rsrc(static_cast<const char*>(b.hist_s) + hoff, kDK * DV * 2);
-  const rsrc_t hd = make_rsrc(static_cast<const char*>(b.hist_ds) + hoff, kDK * DV * 2);
+  // the stored matrix of this block: S_e (even) or dS'_o (odd)
+  const rsrc_t hm = make_rsrc(static_cast<const char*>(odd ? b.hist_ds : b.hist_s) + hoff,
+                              kDK * DV * 2);
   const rsrc_t es = make_rsrc(a.erase + (GDR2 ? row0 * kDK : 0), GDR2 ? len * kDK * 4 : 0);
   const rsrc_t ws_ = make_rsrc(a.write + (GDR2 ? row0 * DV : 0), GDR2 ? len * DV * 4 : 0);
 
-  // S and dS' of value tile 0 (prefetched one tile ahead in the loop below)
-  bf16x8 sb[4], db[4];
+  // the stored matrix's value tiles 0 and 1 (prefetched two tiles ahead in the loop below:
+  // with one wavefront per SIMD, the loads must cover the memory latency by themselves)
+  bf16x8 hb[4], hn[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    sb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, (uint32_t)((ks * 64 + lane) * 16)));
-    db[ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, (uint32_t)((ks * 64 + lane) * 16)));
-  }
-  // q and k of token rr, channels 32 ks + 8 p + i: the row operands
+    hb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)((ks * 64 + lane) * 16)));
+    hn[ks] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)(((4 + ks) * 64 + lane) * 16)));
+  }  // q and k of token rr, channels 32 ks + 8 p + i: the row operands
   bf16x8 q8[4], k8[4];
   f32x4 e8[4][2];   // erase gates of the same elements (Gated Delta Rule-2)
 #pragma unroll
@@ -541,6 +594,18 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     accq = mfma32(bq, bc, accq);        // (Qh Kb^T)[4p + e][rr]
     acck = mfma32(ah[ks], bc, acck);    // (Kh Kb^T)[4p + e][rr]
     acct = mfma32(bc, ah[ks], acct);    // (Kh Kb^T)[rr][4p + e]
+    // the transposed operands of channel tiles 2 ks and 2 ks + 1 for the boundary tile:
+    // Kt_e^T in the even block, Qh_o^T and Kh_o^T in the odd one
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 ts = tile_selector(hh, rr, p);
+      if (odd) {
+        sp.qh[2 * ks + hh][lane] = pack4(mfma32(bq, ts, zero4()));
+        sp.kh[2 * ks + hh][lane] = pack4(mfma32(ah[ks], ts, zero4()));
+      } else {
+        sp.kt[2 * ks + hh][lane] = pack4(mfma32(at[ks], ts, zero4()));
+      }
+    }
   }
   // ---- 2. M, A and Tm of the block
   {
@@ -559,16 +624,25 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     for (int e = 0; e < 4; ++e) sm.u.w.Tm[4 * p + e][rr] = inv[e];
   }
   wave_lds_fence();
-  bf16x4 tA, tT, mT;
+  {
+    bf16x4 tA, tT, mT;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tA[i] = static_cast<bf16>(sm.u.w.Tm[rr][4 * p + i]);   // Tm row rr
-    tT[i] = static_cast<bf16>(sm.u.w.Tm[4 * p + i][rr]);   // Tm^T row rr
-    mT[i] = static_cast<bf16>(sm.u.w.M[4 * p + i][rr]);    // M^T row rr
+    for (int i = 0; i < 4; ++i) {
+      tA[i] = static_cast<bf16>(sm.u.w.Tm[rr][4 * p + i]);   // Tm row rr
+      tT[i] = static_cast<bf16>(sm.u.w.Tm[4 * p + i][rr]);   // Tm^T row rr
+      mT[i] = static_cast<bf16>(sm.u.w.M[4 * p + i][rr]);    // M^T row rr
+    }
+    sp.tm[odd][0][lane] = tA;
+    sp.tm[odd][1][lane] = tT;
+    sp.tm[odd][2][lane] = mT;
+    sp.sel[odd][0][lane] = selector(0, rr, p);
+    sp.sel[odd][1][lane] = selector(1, rr, p);
   }
-  f32x4 btv;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) btv[e] = sm.beta[4 * p + e];
+  // beta of tokens 4 p + e
+#define KDA_BTV (*reinterpret_cast<const f32x4*>(&sm.beta[4 * p]))
+#define KDA_TA (sp.tm[ODD][0][lane])
+#define KDA_TT (sp.tm[ODD][1][lane])
+#define KDA_MT (sp.tm[ODD][2][lane])
 
   // ---- 3. the value tiles
   f32x4 C1[8], C2[8], C3[8], g1 = zero4(), g2 = zero4();
@@ -579,92 +653,171 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     r2[m] = 0.f;
   }
   f32x4 r1 = zero4();
-  const bf16x8 sel0 = selector(0, rr, p), sel1 = selector(1, rr, p);
   const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
+  wave_lds_fence();   // the transposed operands are written
+  // V and the write gates of value tile ct in the accumulator layout (token 4p + e)
+  bf16x4 vnext;
+  f32x4 wnext;
+  auto load_tile_values = [&](int ct) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t o = (uint32_t)((4 * p + e) * DV + 16 * ct + rr);
+      vnext[e] = ld_b16(vs, o * 2);
+      wnext[e] = GDR2 ? ld_b32(ws_, o * 4) : 1.f;
+    }
+  };
+  load_tile_values(0);
+  // the tile loop, compiled separately for each role (one loop per wavefront, no branch on
+  // the role inside it)
+  auto tiles = [&](auto role) {
+    constexpr int ODD = decltype(role)::value;
 #pragma unroll 1
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int col = 16 * ct + rr;
-    // V (and the write gates) of this tile (token 4p + e, column col)
-    f32x4 vcol, wcol;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int col = 16 * ct + rr, par = ct & 1;
+      // V (and the write gates) of this tile (token 4p + e, column col), loaded during the
+      // previous tile; then the next tile's
+      f32x4 vcol, wcol;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t o = (uint32_t)((4 * p + e) * DV + col);
-      vcol[e] = static_cast<float>(ld_b16(vs, o * 2));
-      wcol[e] = GDR2 ? ld_b32(ws_, o * 4) : 1.f;
-    }
-    // X = Kh S and dU2 = Kt dS' for this tile
-    f32x4 X = zero4(), dU2 = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      X = mfma32(ah[ks], sb[ks], X);
-      dU2 = mfma32(at[ks], db[ks], dU2);
-    }
-    f32x4 R, x;
-    bf16x4 dob;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      R[e] = wcol[e] * vcol[e] - X[e];
-      x[e] = btv[e] * R[e];
-      dob[e] = sm.dor[4 * p + e][col];
-    }
-    const f32x4 U = mfma16(tA, pack4(x), zero4());
-    const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
-    const f32x4 dY = mfma16(tT, pack4(dU), zero4());
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.u.w.ut[4 * p + e][rr] = static_cast<bf16>(U[e]);
-      sm.u.w.yt[4 * p + e][rr] = static_cast<bf16>(dY[e]);
-      sm.u.w.bt[4 * p + e][rr] = static_cast<bf16>((GDR2 ? wcol[e] : btv[e]) * dY[e]);
-      r1[e] += dY[e] * R[e];
-      if (GDR2 && 4 * p + e < len)   // d write = V * dY
-        b.dwrite[(row0 + 4 * p + e) * DV + col] = vcol[e] * dY[e];
-    }
-    // this tile's S and dS' as they arrived; then prefetch the next tile's
-    bf16x8 sc[4], dc[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      sc[ks] = sb[ks];
-      dc[ks] = db[ks];
-    }
-    if (ct + 1 < NCT) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t off = (uint32_t)((((ct + 1) * 4 + ks) * 64 + lane) * 16);
-        sb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hs, off));
-        db[ks] = __builtin_bit_cast(bf16x8, ld_b128(hd, off));
+      for (int e = 0; e < 4; ++e) {
+        vcol[e] = static_cast<float>(vnext[e]);
+        wcol[e] = GDR2 ? wnext[e] : 1.f;
       }
-    }
-    wave_lds_fence();
-    // dV = Diag(beta) dY (w * dY): this tile's 16 token rows of 16 columns
-    if (lane < 32) {
-      const int t = lane >> 1, c8 = 8 * (lane & 1);
-      st_b128(vd, (uint32_t)(t * DV + 16 * ct + c8) * 2,
-              *reinterpret_cast<const bf16x8*>(&sm.u.w.bt[t][c8]));
-    }
-    // the tile's share of the contractions over the value columns (k = column 16 ct + 4p + i)
-    const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][16 * ct + 4 * p]);
-    // beta = 1 with the Gated Delta Rule-2 gates: Diag(beta) dY is dY itself
-    const bf16x4 ay = *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.u.w.yt[rr][4 * p] : &sm.u.w.bt[rr][4 * p]);
-    const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.u.w.ut[rr][4 * p]);
-    const bf16x4 ayy = *reinterpret_cast<const bf16x4*>(&sm.u.w.yt[rr][4 * p]);
-    g1 = mfma16(ao, au, g1);     // (dO U^T)[4p + e][rr]
-    g2 = mfma16(ayy, au, g2);    // (dY U^T)[4p + e][rr]
+      if (ct + 1 < NCT) load_tile_values(ct + 1);
+      bf16x4 dob;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int e = 0; e < 4; ++e) dob[e] = sm.dor[4 * p + e][col];
+      // this block's S and dS' of the tile (sc, dc), R = w V - Kh S, U, dY
+      bf16x8 sc[4], dc[4];
+      f32x4 R, U, dY;
+      if constexpr (!ODD) {   // even: S_e is stored; U_e, then the odd block's entering state
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int m = 2 * ks + hh;   // channel tile: channels 16 m + n
-        const f32x4 st = mfma32(sc[ks], hh ? sel1 : sel0, zero4());   // S[16 m + rr][16 ct + 4p + e]
-        const f32x4 dt = mfma32(dc[ks], hh ? sel1 : sel0, zero4());
-        const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
-        C1[m] = mfma16(ao, sb4, C1[m]);   // (dO S^T)[4p + e][16 m + rr]
-        C2[m] = mfma16(ay, sb4, C2[m]);   // (Diag(beta) dY S^T)
-        C3[m] = mfma16(au, db4, C3[m]);   // (U dS'^T)
+        for (int ks = 0; ks < 4; ++ks) sc[ks] = hb[ks];
+        f32x4 X = zero4(), x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r2[m] += st[e] * dt[e];
+        for (int ks = 0; ks < 4; ++ks) X = mfma32(ah[ks], sc[ks], X);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          R[e] = wcol[e] * vcol[e] - X[e];
+          x[e] = KDA_BTV[e] * R[e];
+        }
+        U = mfma16(KDA_TA, pack4(x), zero4());
+        const bf16x4 ub = pack4(U);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {   // S_o = Diag(Gam_e) S_e + Kt_e^T U_e
+          f32x4 acc[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[32 * ks + 8 * p + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[hh][e] = gm[e] * static_cast<float>(sc[ks][4 * hh + e]);
+            acc[hh] = mfma16(sp.kt[2 * ks + hh][lane], ub, acc[hh]);
+          }
+          sp.bnd[par][1][ks][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
+        }
+      } else {      // odd: dS'_o is stored; dY_o, then the even block's leaving gradient
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dc[ks] = hb[ks];
+        f32x4 dU2 = zero4(), y;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dU2 = mfma32(at[ks], dc[ks], dU2);
+        const f32x4 dU = dU2 + mfma16(KDA_MT, dob, zero4());
+        dY = mfma16(KDA_TT, pack4(dU), zero4());
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = -KDA_BTV[e] * dY[e];
+        const bf16x4 yb = pack4(y);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {   // dS'_e = Diag(Gam_o) dS'_o + Qh_o^T dO_o - Kh_o^T Diag(beta_o) dY_o
+          f32x4 acc[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int m = 2 * ks + hh;
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[32 * ks + 8 * p + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[hh][e] = gm[e] * static_cast<float>(dc[ks][4 * hh + e]);
+            acc[hh] = mfma16(sp.qh[m][lane], dob, acc[hh]);
+            acc[hh] = mfma16(sp.kh[m][lane], yb, acc[hh]);
+          }
+          sp.bnd[par][0][ks][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
+        }
       }
-    wave_lds_fence();   // the tile rows are rewritten by the next tile
-  }
+      // the stored matrix two tiles ahead
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) hb[ks] = hn[ks];
+      if (ct + 2 < NCT) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          hn[ks] = __builtin_bit_cast(
+              bf16x8, ld_b128(hm, (uint32_t)((((ct + 2) * 4 + ks) * 64 + lane) * 16)));
+      }
+      lds_barrier();   // the boundary tiles of this value tile are written
+      if constexpr (!ODD) {   // even: its leaving gradient came from the odd block
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dc[ks] = sp.bnd[par][0][ks][lane];
+        f32x4 dU2 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dU2 = mfma32(at[ks], dc[ks], dU2);
+        const f32x4 dU = dU2 + mfma16(KDA_MT, dob, zero4());
+        dY = mfma16(KDA_TT, pack4(dU), zero4());
+      } else {      // odd: its entering state came from the even block
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) sc[ks] = sp.bnd[par][1][ks][lane];
+        f32x4 X = zero4(), x;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) X = mfma32(ah[ks], sc[ks], X);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          R[e] = wcol[e] * vcol[e] - X[e];
+          x[e] = KDA_BTV[e] * R[e];
+        }
+        U = mfma16(KDA_TA, pack4(x), zero4());
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.u.w.ut[4 * p + e][rr] = static_cast<bf16>(U[e]);
+        sm.u.w.yt[4 * p + e][rr] = static_cast<bf16>(dY[e]);
+        sm.u.w.bt[4 * p + e][rr] = static_cast<bf16>((GDR2 ? wcol[e] : KDA_BTV[e]) * dY[e]);
+        r1[e] += dY[e] * R[e];
+        if (GDR2 && 4 * p + e < len)   // d write = V * dY
+          b.dwrite[(row0 + 4 * p + e) * DV + col] = vcol[e] * dY[e];
+      }
+      wave_lds_fence();
+      // dV = Diag(beta) dY (w * dY): this tile's 16 token rows of 16 columns
+      if (lane < 32) {
+        const int t = lane >> 1, c8 = 8 * (lane & 1);
+        st_b128(vd, (uint32_t)(t * DV + 16 * ct + c8) * 2,
+                *reinterpret_cast<const bf16x8*>(&sm.u.w.bt[t][c8]));
+      }
+      // the tile's share of the contractions over the value columns (k = column 16 ct + 4p + i)
+      const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][16 * ct + 4 * p]);
+      // beta = 1 with the Gated Delta Rule-2 gates: Diag(beta) dY is dY itself
+      const bf16x4 ay = *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.u.w.yt[rr][4 * p] : &sm.u.w.bt[rr][4 * p]);
+      const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.u.w.ut[rr][4 * p]);
+      const bf16x4 ayy = *reinterpret_cast<const bf16x4*>(&sm.u.w.yt[rr][4 * p]);
+      g1 = mfma16(ao, au, g1);     // (dO U^T)[4p + e][rr]
+      g2 = mfma16(ayy, au, g2);    // (dY U^T)[4p + e][rr]
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int m = 2 * ks + hh;   // channel tile: channels 16 m + n
+          const f32x4 st = mfma32(sc[ks], sp.sel[ODD][hh][lane], zero4());   // S[16 m + rr][16 ct + 4p + e]
+          const f32x4 dt = mfma32(dc[ks], sp.sel[ODD][hh][lane], zero4());
+          const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
+          C1[m] = mfma16(ao, sb4, C1[m]);   // (dO S^T)[4p + e][16 m + rr]
+          C2[m] = mfma16(ay, sb4, C2[m]);   // (Diag(beta) dY S^T)
+          C3[m] = mfma16(au, db4, C3[m]);   // (U dS'^T)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r2[m] += st[e] * dt[e];
+        }
+      wave_lds_fence();   // the tile rows are rewritten by the next tile
+    }
+  };
+  if (odd) tiles(std::integral_constant<int, 1>{});
+  else tiles(std::integral_constant<int, 0>{});
+#undef KDA_BTV
+#undef KDA_TA
+#undef KDA_TT
+#undef KDA_MT
   // q and k rows again (token rr, channels 32 ks + 8 p + i) for the per-channel step below,
   // loaded now so that the reductions cover their latency
 #pragma unroll
@@ -711,7 +864,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     const int ch = 16 * m + rr;
     const float G = sm.gam[ch];
     // q and k of token 4 p + e, channel ch: the rows transposed by the selector (exact)
-    const bf16x8 sel = (m & 1) ? sel1 : sel0;
+    const bf16x8 sel = sp.sel[odd][m & 1][lane];
     const f32x4 qT = mfma32(q8[m >> 1], sel, zero4());
     const f32x4 kT = mfma32(k8[m >> 1], sel, zero4());
     float P[4], qf[4], kf[4], bf[4];
@@ -806,12 +959,12 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 
 bool chunk_bwd_supports(int dk, int dv, int T) {
   // the forward's bounds, and one chain's state history addressable by a buffer descriptor
-  return chunk_mfma_supports(dk, dv, T) && ((long long)T + 64) * 16 * dv < (1ll << 31);
+  return chunk_mfma_supports(dk, dv, T) && ((long long)T + 64) * 8 * dv < (1ll << 31);
 }
 
 size_t chunk_bwd_hist_bytes(int N, int H, int T, int dv, bool packed) {
   const size_t tokens = packed ? (size_t)T + 64 * (size_t)N : (size_t)N * (((size_t)T + 63) / 64 * 64);
-  return (size_t)H * tokens * (kDK / 16) * 2 * (size_t)dv;  // hist_chain_offset's layout
+  return (size_t)H * tokens * (kDK / 16) * (size_t)dv;  // hist_chain_offset's layout
 }
 
 namespace {
@@ -835,11 +988,11 @@ hipError_t launch_grad(BwdArgs& b, bool per_channel, int slots, hipStream_t stre
   const ChunkArgs& a = b.f;
   const unsigned grid = (unsigned)slots * a.H;
   if (a.dv == 128) {
-    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, 64, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, 64, 0, stream>>>(b, slots);
+    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, 128, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, 128, 0, stream>>>(b, slots);
   } else {
-    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, 64, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, 64, 0, stream>>>(b, slots);
+    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, 128, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, 128, 0, stream>>>(b, slots);
   }
   return hipGetLastError();
 }
@@ -876,9 +1029,10 @@ hipError_t launch_chunk_bwd(const BwdArgs& args, bool per_channel, hipStream_t s
     a.split_all = 1;
     chains *= 2;
   }
-  const int slots = a.cu ? a.T / 16 + a.N + 1 : a.N * ((a.T + 15) / 16);
-  // 1. the states at every block start, on the side stream, and 2. the carry, recording dS'
-  // of every block; then 3. the gradients of every block, after both
+  // one workgroup per pair of 16-token blocks (grad_item)
+  const int slots = a.cu ? a.T / 32 + a.N + 1 : a.N * ((a.T + 31) / 32);
+  // 1. the states entering every pair of blocks, on the side stream, and 2. the carry,
+  // recording dS' at the end of every pair; then 3. the gradients of every block, after both
   ChunkArgs h = b.f;
   h.hist = b.hist_s;
   h.split_all = 0;  // the history launch decides its own split

@@ -275,8 +275,8 @@ __device__ __forceinline__ void flush_outputs(const Smem& sm, rsrc_t odst, int s
 // MODE selects what the wavefront produces besides the final state (written to sTp, the
 // dk x dv row-major matrix of this item, when not null; s0p likewise for the initial state):
 //   kModeOut   the outputs o (the forward itself);
-//   kModeHist  the state at every block start in a.hist (at byte hist_off, the layout of
-//              hist_chain_offset), for the backward pass; no outputs;
+//   kModeHist  the state entering every pair of blocks in a.hist (at byte hist_off, the
+//              layout of hist_chain_offset), for the backward pass; no outputs;
 //   kModeState nothing else (the end state of a segment started from zero);
 //   kModeTrans the transition of the segment: the identity as initial state and zero values,
 //              so that the final state is the dk x dk product of the segment's token maps;
@@ -299,7 +299,7 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
   const rsrc_t odst = make_rsrc(static_cast<bf16*>(obase) + (OUT ? orow0 * DV : 0),
                                 OUT ? (uint32_t)tr.len * DV * 2 : 0u);
   const rsrc_t hdst = make_rsrc(static_cast<char*>(a.hist) + (HIST ? hist_off : 0),
-                                HIST ? (uint32_t)nsteps * 4 * kDK * DV * 2 : 0);
+                                HIST ? (uint32_t)nsteps * 2 * kDK * DV * 2 : 0);
   int col[NT];
   uint32_t voff[NT];  // byte offset of (token 4 p, column col) within a 64-token chunk
 #pragma unroll
@@ -378,8 +378,10 @@ __device__ __forceinline__ void state_role(Smem& sm, const ChunkArgs& a, const T
           const bf16x8 sb = cat8(pack4(S_acc[c][2 * ks]), pack4(S_acc[c][2 * ks + 1]));
           X[c] = mfma32(ak, sb, X[c]);
           if constexpr (HIST) {
-            const uint32_t tile = (uint32_t)(4 * s + I) * (DV / 16) + (cbase + 16 * c) / 16;
-            st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, sb);
+            if ((I & 1) == 0) {  // the state entering each pair of blocks
+              const uint32_t tile = (uint32_t)(2 * s + I / 2) * (DV / 16) + (cbase + 16 * c) / 16;
+              st_b128(hdst, ((tile * 4 + ks) * 64 + lane) * 16, sb);
+            }
           } else if constexpr (OUT) {
             const bf16x8 aq =
                 *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][32 * ks + 8 * p]);

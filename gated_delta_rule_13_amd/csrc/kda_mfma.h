@@ -225,21 +225,24 @@ __host__ __device__ inline void split_item(uint32_t local, uint32_t n, uint32_t&
 }
 
 // State history of the backward pass. For every chain (sequence n, head h) the kernels
-// keep one dk x dv bf16 matrix per 16-token block of the chain (its 64-token steps
-// padded with identity tokens), stored as the 16x16x32 B operands of the state tiles:
-// for value tile ct and channel slab ks, lane l = 16 p + r holds the 8 channels
-// 32 ks + 8 p + i (i < 8) of column 16 ct + r, 16 bytes at ((ct * 4 + ks) * 64 + l) * 16.
-// One block's matrix is dk * dv * 2 bytes, i.e. dk * dv / 8 bytes per token, and the
-// chains of head h are laid out along the padded token axis: sequence n starts at padded
-// token cu[n] + 64 n with packed sequences (B = 1), at n * ceil64(T) otherwise; no two
-// sequences' padded ranges overlap.
+// keep one dk x dv bf16 matrix per pair of 16-token blocks of the chain (its 64-token
+// steps padded with identity tokens): the history of states holds the state entering the
+// pair's first (even) block, the history of state gradients the gradient reaching the end
+// of its second (odd) block; the state between the two blocks and the gradient between
+// them follow from these within the pair. A matrix is stored as the 16x16x32 B operands of
+// the state tiles: for value tile ct and channel slab ks, lane l = 16 p + r holds the 8
+// channels 32 ks + 8 p + i (i < 8) of column 16 ct + r, 16 bytes at
+// ((ct * 4 + ks) * 64 + l) * 16. One matrix is dk * dv * 2 bytes, i.e. dk * dv / 16 bytes
+// per token, and the chains of head h are laid out along the padded token axis: sequence n
+// starts at padded token cu[n] + 64 n with packed sequences (B = 1), at n * ceil64(T)
+// otherwise; no two sequences' padded ranges overlap.
 __device__ __forceinline__ size_t hist_tokens(const ChunkArgs& a) {
   return a.cu ? (size_t)a.T + 64 * (size_t)a.N : (size_t)a.N * (((size_t)a.T + 63) / 64 * 64);
 }
 __device__ __forceinline__ size_t hist_chain_offset(const ChunkArgs& a, int n, int h,
                                                     const TokenRange& tr) {
   const size_t start = a.cu ? (size_t)tr.t0 + 64 * (size_t)n : (size_t)n * (((size_t)a.T + 63) / 64 * 64);
-  return ((size_t)h * hist_tokens(a) + start) * (kDK / 16) * 2 * (size_t)a.dv;
+  return ((size_t)h * hist_tokens(a) + start) * (kDK / 16) * (size_t)a.dv;
 }
 
 }  // namespace kda

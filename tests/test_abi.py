@@ -317,20 +317,21 @@ def test_epilogue_rejects(over, code):
 
 
 def test_bwd_workspace_size():
-    # two bf16 histories of dk * dv / 8 bytes per padded token: 2 x 32 x (4096 + 64 * 2) x 2048
+    # two bf16 histories of dk * dv / 16 bytes per padded token (one matrix per pair of
+    # 16-token blocks): 2 x 32 x (4096 + 64 * 2) x 1024
     # (packed sequences: plus the 768-byte work list of 2 x 32 chains)
-    one = 32 * (4096 + 64 * 2) * 2048
+    one = 32 * (4096 + 64 * 2) * 1024
     assert kda.kda_chunk_bwd_workspace_size(1, 32, 4096, 128, 128, 2, kda.KDA_BF16) == \
         2 * one + 768
     # equal lengths: B sequences padded to 64 tokens each
-    one = 16 * 2 * 4096 * 1024
+    one = 16 * 2 * 4096 * 512
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 64, 0, kda.KDA_BF16) == 2 * one
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_F32) == 0
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 64, 128, 0, kda.KDA_BF16) == 0
     assert kda.kda_chunk_bwd_workspace_size(0, 16, 4096, 128, 128, 0, kda.KDA_BF16) == 0
-    # the longest T axis of the backward: (T + 64) 16 dv < 2^31
-    assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 20) - 65, 128, 128, 1, kda.KDA_BF16) > 0
-    assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 20) - 64, 128, 128, 1, kda.KDA_BF16) == 0
+    # the longest T axis of the backward: (T + 64) 8 dv < 2^31
+    assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 21) - 65, 128, 128, 1, kda.KDA_BF16) > 0
+    assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 21) - 64, 128, 128, 1, kda.KDA_BF16) == 0
 
 
 def bwd_call(**over):
@@ -357,9 +358,9 @@ def bwd_call(**over):
     (dict(dt=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
     (dict(dv=96), kda.KDA_ERR_UNSUPPORTED),
-    # one chain's history must be addressable by a buffer descriptor: (T + 64) 16 dv < 2^31
-    (dict(T=(1 << 20) - 64), kda.KDA_ERR_UNSUPPORTED),
-    (dict(T=(1 << 21) - 64, dv=64), kda.KDA_ERR_UNSUPPORTED),
+    # one chain's history must be addressable by a buffer descriptor: (T + 64) 8 dv < 2^31
+    (dict(T=(1 << 21) - 64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=(1 << 22) - 64, dv=64), kda.KDA_ERR_UNSUPPORTED),
 ])
 def test_bwd_rejects(over, code):
     assert bwd_call(**over) == code
