@@ -386,6 +386,7 @@ struct GSmem {
   float P[16][kDK];        // decay from the block start through token t; later d log P_t
   float gam[kDK];
   bf16 dor[16][kLDK];      // token rows of dO (dv <= dk columns); later of dq (dk columns)
+  bf16 vr[16][kLDK];       // token rows of V (dv columns)
   union {
     struct {               // phases 2-4
       bf16 ut[16][24];     // U, dY, Diag(beta) dY of the current value tile (token rows)
@@ -414,10 +415,6 @@ struct GPair {
   bf16x4 qh[8][64];          // odd: Qh_o^T
   bf16x4 kh[8][64];          // odd: Kh_o^T
   bf16x8 bnd[2][2][4][64];   // [parity][receiver]: dS'_e for the even, S_o for the odd
-  // per block, read back per value tile rather than held in registers: Tm, Tm^T and M^T
-  // (16x16x16 A operands) and the selectors of the transposes
-  bf16x4 tm[2][3][64];
-  bf16x8 sel[2][2][64];
 };
 
 // Position of work item (pair of 16-token blocks) `slot` of head h: sequence n and pair pr,
@@ -532,17 +529,18 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     }
   }
 
-  // ---- 0. decay of every channel (two per lane), dO rows, beta. Every load is issued
+  // ---- 0. decay of every channel (two per lane), dO and V rows, beta. Every load is issued
   // before the first use: bounded reads past the block's last token return g = 0.
   {
     const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
     const rsrc_t gs = make_rsrc(a.g + row0 * (PER_CHANNEL ? kDK : 1),
                                 len * (PER_CHANNEL ? kDK : 1) * 4);
-    f32x4 dov[16 * DV / 8 / 64];
+    f32x4 dov[16 * DV / 8 / 64], vov[16 * DV / 8 / 64];
 #pragma unroll
     for (int j = 0; j < 16 * DV / 8 / 64; ++j) {
       const int i = lane + 64 * j, tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
       dov[j] = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
+      vov[j] = ld_b128(vs, (uint32_t)(tt * DV + cc) * 2);
     }
     const float bv = GDR2 ? 1.f : ld_b32(make_rsrc(a.beta + row0, len * 4), (lane & 15) * 4);
     float gv[2][16];
@@ -555,6 +553,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     for (int j = 0; j < 16 * DV / 8 / 64; ++j) {
       const int i = lane + 64 * j, tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
       *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = dov[j];
+      *reinterpret_cast<f32x4*>(&sm.vr[tt][cc]) = vov[j];
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -624,25 +623,6 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     for (int e = 0; e < 4; ++e) sm.u.w.Tm[4 * p + e][rr] = inv[e];
   }
   wave_lds_fence();
-  {
-    bf16x4 tA, tT, mT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tA[i] = static_cast<bf16>(sm.u.w.Tm[rr][4 * p + i]);   // Tm row rr
-      tT[i] = static_cast<bf16>(sm.u.w.Tm[4 * p + i][rr]);   // Tm^T row rr
-      mT[i] = static_cast<bf16>(sm.u.w.M[4 * p + i][rr]);    // M^T row rr
-    }
-    sp.tm[odd][0][lane] = tA;
-    sp.tm[odd][1][lane] = tT;
-    sp.tm[odd][2][lane] = mT;
-    sp.sel[odd][0][lane] = selector(0, rr, p);
-    sp.sel[odd][1][lane] = selector(1, rr, p);
-  }
-  // beta of tokens 4 p + e
-#define KDA_BTV (*reinterpret_cast<const f32x4*>(&sm.beta[4 * p]))
-#define KDA_TA (sp.tm[ODD][0][lane])
-#define KDA_TT (sp.tm[ODD][1][lane])
-#define KDA_MT (sp.tm[ODD][2][lane])
 
   // ---- 3. the value tiles
   f32x4 C1[8], C2[8], C3[8], g1 = zero4(), g2 = zero4();
@@ -655,34 +635,51 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   f32x4 r1 = zero4();
   const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
   wave_lds_fence();   // the transposed operands are written
-  // V and the write gates of value tile ct in the accumulator layout (token 4p + e)
-  bf16x4 vnext;
+  // the write gates of value tile ct in the accumulator layout (token 4p + e), loaded one
+  // tile ahead (Gated Delta Rule-2)
   f32x4 wnext;
-  auto load_tile_values = [&](int ct) {
+  auto load_write_gates = [&](int ct) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t o = (uint32_t)((4 * p + e) * DV + 16 * ct + rr);
-      vnext[e] = ld_b16(vs, o * 2);
-      wnext[e] = GDR2 ? ld_b32(ws_, o * 4) : 1.f;
-    }
+    for (int e = 0; e < 4; ++e)
+      wnext[e] = GDR2 ? ld_b32(ws_, (uint32_t)((4 * p + e) * DV + 16 * ct + rr) * 4) : 1.f;
   };
-  load_tile_values(0);
+  load_write_gates(0);
   // the tile loop, compiled separately for each role (one loop per wavefront, no branch on
   // the role inside it)
   auto tiles = [&](auto role) {
     constexpr int ODD = decltype(role)::value;
+    // the block's operands that every tile uses, held in registers across the tiles: Tm,
+    // Tm^T, M^T, beta, the transposes' selectors, the decay Gam of the state tiles' rows
+    // (channel tile m: 32 (m / 2) + 8 p + 4 (m % 2) + e) and the transposed operands of the
+    // boundary tile (even: Kt_e^T; odd: Qh_o^T, Kh_o^T)
+    bf16x4 tA, tT, mT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tA[i] = static_cast<bf16>(sm.u.w.Tm[rr][4 * p + i]);   // Tm row rr
+      tT[i] = static_cast<bf16>(sm.u.w.Tm[4 * p + i][rr]);   // Tm^T row rr
+      mT[i] = static_cast<bf16>(sm.u.w.M[4 * p + i][rr]);    // M^T row rr
+    }
+    const f32x4 btv = *reinterpret_cast<const f32x4*>(&sm.beta[4 * p]);
+    const bf16x8 sel[2] = {selector(0, rr, p), selector(1, rr, p)};
+    f32x4 gmr[8];
+    bf16x4 tr1[8], tr2[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      gmr[m] = *reinterpret_cast<const f32x4*>(&sm.gam[32 * (m >> 1) + 8 * p + 4 * (m & 1)]);
+      tr1[m] = ODD ? sp.qh[m][lane] : sp.kt[m][lane];
+      tr2[m] = ODD ? sp.kh[m][lane] : bf16x4{};
+    }
 #pragma unroll 1
     for (int ct = 0; ct < NCT; ++ct) {
       const int col = 16 * ct + rr, par = ct & 1;
-      // V (and the write gates) of this tile (token 4p + e, column col), loaded during the
-      // previous tile; then the next tile's
+      // V and the write gates of this tile (token 4p + e, column col)
       f32x4 vcol, wcol;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vcol[e] = static_cast<float>(vnext[e]);
+        vcol[e] = static_cast<float>(sm.vr[4 * p + e][col]);
         wcol[e] = GDR2 ? wnext[e] : 1.f;
       }
-      if (ct + 1 < NCT) load_tile_values(ct + 1);
+      if (GDR2 && ct + 1 < NCT) load_write_gates(ct + 1);
       bf16x4 dob;
 #pragma unroll
       for (int e = 0; e < 4; ++e) dob[e] = sm.dor[4 * p + e][col];
@@ -698,19 +695,19 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           R[e] = wcol[e] * vcol[e] - X[e];
-          x[e] = KDA_BTV[e] * R[e];
+          x[e] = btv[e] * R[e];
         }
-        U = mfma16(KDA_TA, pack4(x), zero4());
+        U = mfma16(tA, pack4(x), zero4());
         const bf16x4 ub = pack4(U);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {   // S_o = Diag(Gam_e) S_e + Kt_e^T U_e
           f32x4 acc[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[32 * ks + 8 * p + 4 * hh]);
+            const f32x4 gm = gmr[2 * ks + hh];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[hh][e] = gm[e] * static_cast<float>(sc[ks][4 * hh + e]);
-            acc[hh] = mfma16(sp.kt[2 * ks + hh][lane], ub, acc[hh]);
+            acc[hh] = mfma16(tr1[2 * ks + hh], ub, acc[hh]);
           }
           sp.bnd[par][1][ks][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
         }
@@ -720,10 +717,10 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
         f32x4 dU2 = zero4(), y;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) dU2 = mfma32(at[ks], dc[ks], dU2);
-        const f32x4 dU = dU2 + mfma16(KDA_MT, dob, zero4());
-        dY = mfma16(KDA_TT, pack4(dU), zero4());
+        const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
+        dY = mfma16(tT, pack4(dU), zero4());
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = -KDA_BTV[e] * dY[e];
+        for (int e = 0; e < 4; ++e) y[e] = -btv[e] * dY[e];
         const bf16x4 yb = pack4(y);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {   // dS'_e = Diag(Gam_o) dS'_o + Qh_o^T dO_o - Kh_o^T Diag(beta_o) dY_o
@@ -731,23 +728,21 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int m = 2 * ks + hh;
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[32 * ks + 8 * p + 4 * hh]);
+            const f32x4 gm = gmr[2 * ks + hh];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[hh][e] = gm[e] * static_cast<float>(dc[ks][4 * hh + e]);
-            acc[hh] = mfma16(sp.qh[m][lane], dob, acc[hh]);
-            acc[hh] = mfma16(sp.kh[m][lane], yb, acc[hh]);
+            acc[hh] = mfma16(tr1[m], dob, acc[hh]);
+            acc[hh] = mfma16(tr2[m], yb, acc[hh]);
           }
           sp.bnd[par][0][ks][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
         }
       }
-      // the stored matrix two tiles ahead
+      // the stored matrix two tiles ahead (past the last tile the loads read zeros)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) hb[ks] = hn[ks];
-      if (ct + 2 < NCT) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          hn[ks] = __builtin_bit_cast(
-              bf16x8, ld_b128(hm, (uint32_t)((((ct + 2) * 4 + ks) * 64 + lane) * 16)));
+      for (int ks = 0; ks < 4; ++ks) {
+        hb[ks] = hn[ks];
+        hn[ks] = __builtin_bit_cast(
+            bf16x8, ld_b128(hm, (uint32_t)((((ct + 2) * 4 + ks) * 64 + lane) * 16)));
       }
       lds_barrier();   // the boundary tiles of this value tile are written
       if constexpr (!ODD) {   // even: its leaving gradient came from the odd block
@@ -756,8 +751,8 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
         f32x4 dU2 = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) dU2 = mfma32(at[ks], dc[ks], dU2);
-        const f32x4 dU = dU2 + mfma16(KDA_MT, dob, zero4());
-        dY = mfma16(KDA_TT, pack4(dU), zero4());
+        const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
+        dY = mfma16(tT, pack4(dU), zero4());
       } else {      // odd: its entering state came from the even block
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sc[ks] = sp.bnd[par][1][ks][lane];
@@ -767,15 +762,15 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           R[e] = wcol[e] * vcol[e] - X[e];
-          x[e] = KDA_BTV[e] * R[e];
+          x[e] = btv[e] * R[e];
         }
-        U = mfma16(KDA_TA, pack4(x), zero4());
+        U = mfma16(tA, pack4(x), zero4());
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sm.u.w.ut[4 * p + e][rr] = static_cast<bf16>(U[e]);
         sm.u.w.yt[4 * p + e][rr] = static_cast<bf16>(dY[e]);
-        sm.u.w.bt[4 * p + e][rr] = static_cast<bf16>((GDR2 ? wcol[e] : KDA_BTV[e]) * dY[e]);
+        sm.u.w.bt[4 * p + e][rr] = static_cast<bf16>((GDR2 ? wcol[e] : btv[e]) * dY[e]);
         r1[e] += dY[e] * R[e];
         if (GDR2 && 4 * p + e < len)   // d write = V * dY
           b.dwrite[(row0 + 4 * p + e) * DV + col] = vcol[e] * dY[e];
@@ -800,8 +795,8 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int m = 2 * ks + hh;   // channel tile: channels 16 m + n
-          const f32x4 st = mfma32(sc[ks], sp.sel[ODD][hh][lane], zero4());   // S[16 m + rr][16 ct + 4p + e]
-          const f32x4 dt = mfma32(dc[ks], sp.sel[ODD][hh][lane], zero4());
+          const f32x4 st = mfma32(sc[ks], sel[hh], zero4());   // S[16 m + rr][16 ct + 4p + e]
+          const f32x4 dt = mfma32(dc[ks], sel[hh], zero4());
           const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
           C1[m] = mfma16(ao, sb4, C1[m]);   // (dO S^T)[4p + e][16 m + rr]
           C2[m] = mfma16(ay, sb4, C2[m]);   // (Diag(beta) dY S^T)
@@ -814,10 +809,6 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   };
   if (odd) tiles(std::integral_constant<int, 1>{});
   else tiles(std::integral_constant<int, 0>{});
-#undef KDA_BTV
-#undef KDA_TA
-#undef KDA_TT
-#undef KDA_MT
   // q and k rows again (token rr, channels 32 ks + 8 p + i) for the per-channel step below,
   // loaded now so that the reductions cover their latency
 #pragma unroll
@@ -864,7 +855,7 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     const int ch = 16 * m + rr;
     const float G = sm.gam[ch];
     // q and k of token 4 p + e, channel ch: the rows transposed by the selector (exact)
-    const bf16x8 sel = sp.sel[odd][m & 1][lane];
+    const bf16x8 sel = selector(m & 1, rr, p);
     const f32x4 qT = mfma32(q8[m >> 1], sel, zero4());
     const f32x4 kT = mfma32(k8[m >> 1], sel, zero4());
     float P[4], qf[4], kf[4], bf[4];
