@@ -515,7 +515,9 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   for (int ks = 0; ks < 4; ++ks) {
     hb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)((ks * 64 + lane) * 16)));
     hn[ks] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)(((4 + ks) * 64 + lane) * 16)));
-  }  // q and k of token rr, channels 32 ks + 8 p + i: the row operands
+  }
+  // q and k of token rr, channels 32 ks + 8 p + i: the row operands (kept for the
+  // per-channel step after the tiles)
   bf16x8 q8[4], k8[4];
   f32x4 e8[4][2];   // erase gates of the same elements (Gated Delta Rule-2)
 #pragma unroll
@@ -644,6 +646,14 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       wnext[e] = GDR2 ? ld_b32(ws_, (uint32_t)((4 * p + e) * DV + 16 * ct + rr) * 4) : 1.f;
   };
   load_write_gates(0);
+  // Gated Delta Rule-2: the erase gates of token 4 p + e, channel 16 m + rr for the
+  // per-channel step after the tiles (loaded now, so that the tiles cover their latency)
+  float e4[8][4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      e4[m][e] = GDR2 ? ld_b32(es, (uint32_t)((4 * p + e) * kDK + 16 * m + rr) * 4) : 1.f;
   // the tile loop, compiled separately for each role (one loop per wavefront, no branch on
   // the role inside it)
   auto tiles = [&](auto role) {
@@ -809,14 +819,6 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   };
   if (odd) tiles(std::integral_constant<int, 1>{});
   else tiles(std::integral_constant<int, 0>{});
-  // q and k rows again (token rr, channels 32 ks + 8 p + i) for the per-channel step below,
-  // loaded now so that the reductions cover their latency
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const uint32_t off = (uint32_t)(rr * kDK + 32 * ks + 8 * p);
-    q8[ks] = __builtin_bit_cast(bf16x8, ld_b128(qs, off * 2));
-    k8[ks] = __builtin_bit_cast(bf16x8, ld_b128(ks_, off * 2));
-  }
   // reductions: r1 over the 16 columns of each lane group, r2 over the lane groups
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -861,11 +863,10 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     float P[4], qf[4], kf[4], bf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t off = (uint32_t)((4 * p + e) * kDK + ch);
       P[e] = sm.P[4 * p + e][ch];
       qf[e] = qT[e];
       kf[e] = kT[e];
-      bf[e] = GDR2 ? ld_b32(es, off * 4) : 1.f;
+      bf[e] = e4[m][e];
     }
     // operands with k = token (4p + i) and n = this channel
     bf16x4 bkb, bkh, bqh;
