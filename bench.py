@@ -53,12 +53,19 @@ CHUNK = 64
 # runs. It is reported only while the kernel source is the one the counters were taken on
 # (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3803042198,
-    "kernel_sha256": "8eab642ac5fa1903a455c0369ecbe98de5f514820ee3989d5a4fb38f544303f8",
+    "bytes": 3803640862,
+    "kernel_sha256": "7dc592aea77832c74519dc5aca8fe732cbf2ee91065e504e50082b947296400e",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5945329537,
-    "kernel_sha256": "8eab642ac5fa1903a455c0369ecbe98de5f514820ee3989d5a4fb38f544303f8",
+    "bytes": 5936227725,
+    "kernel_sha256": "7dc592aea77832c74519dc5aca8fe732cbf2ee91065e504e50082b947296400e",
+}
+# one kda_chunk_bwd call (state history, reverse carry, gradients): its own source and that of
+# the forward kernel whose history mode it runs
+MEASURED_TRAFFIC_BWD = {  # profiles/kda_chunk_bwd_varlen_h32_t65536.md
+    "bytes": 20037801569,
+    "kernel_sha256": "76f39b31263246852e9bdded5bf0f5ec7c86dc5577bfd219a96b2ddd35deac3b",
+    "hist_sha256": "7dc592aea77832c74519dc5aca8fe732cbf2ee91065e504e50082b947296400e",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,
@@ -70,6 +77,7 @@ MEASURED_TRAFFIC_EPILOGUE = {  # profiles/kda_epilogue_h32_t65536.md
 }
 CSRC = os.path.join(ROOT, "gated_delta_rule_13_amd", "csrc")
 CHUNK_KERNEL_SRC = os.path.join(CSRC, "kda_chunk_mfma.hip")
+BWD_KERNEL_SRC = os.path.join(CSRC, "kda_chunk_bwd.hip")
 GATES_KERNEL_SRC = os.path.join(CSRC, "kda_gates.hip")
 
 
@@ -80,9 +88,14 @@ def measured_traffic(record=None, src=CHUNK_KERNEL_SRC):
     record = MEASURED_TRAFFIC if record is None else record
     if not record:
         return None
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    return record["bytes"] if digest == record["kernel_sha256"] else None
+    def digest(path):
+        with open(path, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    if digest(src) != record["kernel_sha256"]:
+        return None
+    if "hist_sha256" in record and digest(CHUNK_KERNEL_SRC) != record["hist_sha256"]:
+        return None
+    return record["bytes"]
 
 
 def log(msg: str) -> None:
@@ -556,7 +569,8 @@ def main() -> int:
             "workload": cfg.name, "ms_per_step": bms, "tokens_per_s": cfg.T / (bms / 1e3),
             "workspace_bytes": wsb,
             "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bgbs / HBM_PEAK_GBS, "alg_bytes_per_launch": bbytes}}
+                         "frac": bgbs / HBM_PEAK_GBS, "alg_bytes_per_launch": bbytes,
+                         "traffic": measured_traffic(MEASURED_TRAFFIC_BWD, BWD_KERNEL_SRC)}}
         log(f"chunk_bwd: {bms:.3f} ms/step, {cfg.T / bms / 1e3:.2f} M tokens/s, {bgbs:.0f} GB/s")
     if not args.no_gates:
         result["gates"] = dict(workload=cfg.name, **bench_gates(torch, kda, cfg, args.steps,
