@@ -360,7 +360,7 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               cu_seqlens: Optional[torch.Tensor] = None, grad_initial_state: bool = True):
     """Backward of ``chunk_fwd`` (see ``kda_chunk_bwd``): returns (dq, dk, dv, dg, dbeta,
     dS0 or None) for the loss gradients grad_o [B, H, T, dv] and grad_final_state
-    [N, H, dk, dv] (None = 0). bf16 q/k/v/grad_o, dk = 128, dv in {64, 128}."""
+    [N, H, dk, dv] (None = 0). bf16 q/k/v/grad_o, dk in {64, 128}, dv in {64, 128}."""
     return _bwd(q, k, v, g, (beta,), grad_o, initial_state, grad_final_state, cu_seqlens,
                 grad_initial_state)
 

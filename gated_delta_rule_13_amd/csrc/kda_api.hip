@@ -323,8 +323,44 @@ kda_status kda_gdr2_recurrent_step(const void* q, const void* k, const void* v, 
                              enum_value(&dt), enum_value(&gm), stream);
 }
 
+// dk = 64 runs the dk = 128 kernels on copies of the key-side arrays padded with zero
+// channels (q, k; g with g = 0, the identity decay, per channel; the erase gates), the states
+// padded with zero rows: a zero key channel never enters the state and a zero query channel
+// reads nothing, so every other gradient is that of the dk = 64 problem, and the padded
+// channels' gradients are dropped. The copies sit at the front of the workspace.
+struct Pad64 {
+  size_t q, k, g, e, s0, dsT, dq, dk, dg, de, ds0, inner;
+};
+static Pad64 pad64_layout(int B, int H, int T, int dv, int N) {
+  const size_t rows = (size_t)B * H * T, nh = (size_t)N * H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  Pad64 L;
+  L.q = take(rows * 128 * 2);
+  L.k = take(rows * 128 * 2);
+  L.g = take(rows * 128 * 4);
+  L.e = take(rows * 128 * 4);
+  L.s0 = take(nh * 128 * dv * 4);
+  L.dsT = take(nh * 128 * dv * 4);
+  L.dq = take(rows * 128 * 2);
+  L.dk = take(rows * 128 * 2);
+  L.dg = take(rows * 128 * 4);
+  L.de = take(rows * 128 * 4);
+  L.ds0 = take(nh * 128 * dv * 4);
+  L.inner = off;
+  return L;
+}
+
 static size_t chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int num_seqs, int dt) {
   if (B <= 0 || H <= 0 || T <= 0 || num_seqs < 0 || dt != KDA_BF16) return 0;
+  if (dk == 64) {
+    const size_t inner = chunk_bwd_workspace(B, H, T, 128, dv, num_seqs, dt);
+    return inner ? pad64_layout(B, H, T, dv, num_seqs > 0 ? num_seqs : B).inner + inner : 0;
+  }
   if (!kda::chunk_bwd_supports(dk, dv, T)) return 0;
   const int N = num_seqs > 0 ? num_seqs : B;
   const size_t one = kda::chunk_bwd_hist_bytes(N, H, T, dv, num_seqs > 0);
@@ -359,12 +395,54 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
   if (gm != KDA_GATE_PER_CHANNEL && gm != KDA_GATE_PER_HEAD) return KDA_ERR_INVALID_ARG;
   if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_INVALID_ARG;
   if (!cu_seqlens && num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARG;
-  if (dt != KDA_BF16 || !kda::chunk_bwd_supports(dk, dv, T)) return KDA_ERR_UNSUPPORTED;
+  if (dt != KDA_BF16 || !kda::chunk_bwd_supports(dk == 64 ? 128 : dk, dv, T))
+    return KDA_ERR_UNSUPPORTED;
   const long long N = cu_seqlens ? num_seqs : B;
   if (N * H > (1ll << 24) || (long long)B * H * T > (1ll << 40)) return KDA_ERR_UNSUPPORTED;
   const size_t need =
       chunk_bwd_workspace(B, H, T, dk, dv, cu_seqlens ? num_seqs : 0, dt);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+  if (dk == 64) {
+    const Pad64 L = pad64_layout(B, H, T, dv, (int)N);
+    char* w = static_cast<char*>(workspace);
+    const long long rows = (long long)B * H * T, nh = N * H;
+    const bool per_channel = gm == KDA_GATE_PER_CHANNEL;
+    hipError_t e = hipSuccess;
+    auto pad = [&](const void* src, size_t off, long long n, int ws, int wd, int eb) {
+      if (e == hipSuccess) e = kda::launch_pad_rows(src, w + off, n, ws, wd, eb, stream);
+    };
+    auto unpad = [&](size_t off, void* dst, long long n, int ws, int wd, int eb) {
+      if (e == hipSuccess) e = kda::launch_pad_rows(w + off, dst, n, ws, wd, eb, stream);
+    };
+    pad(q, L.q, rows, 64, 128, 2);
+    pad(k, L.k, rows, 64, 128, 2);
+    if (per_channel) pad(g, L.g, rows, 64, 128, 4);
+    if (erase) pad(erase, L.e, rows, 64, 128, 4);
+    if (initial_state) pad(initial_state, L.s0, nh, 64 * dv, 128 * dv, 4);
+    if (grad_final_state) pad(grad_final_state, L.dsT, nh, 64 * dv, 128 * dv, 4);
+    // the outputs start as the caller's arrays, so that tokens outside every sequence keep
+    // their values through the copies back
+    pad(grad_q, L.dq, rows, 64, 128, 2);
+    pad(grad_k, L.dk, rows, 64, 128, 2);
+    if (per_channel) pad(grad_g, L.dg, rows, 64, 128, 4);
+    if (erase) pad(grad_erase, L.de, rows, 64, 128, 4);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    auto at = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    const kda_status st = chunk_bwd_impl(
+        w + L.q, w + L.k, v, per_channel ? at(L.g) : g, beta, erase ? at(L.e) : nullptr, write,
+        initial_state ? at(L.s0) : nullptr, grad_o, grad_final_state ? at(L.dsT) : nullptr,
+        w + L.dq, w + L.dk, grad_v, per_channel ? at(L.dg) : grad_g, grad_beta,
+        erase ? at(L.de) : nullptr, grad_write, grad_initial_state ? at(L.ds0) : nullptr,
+        cu_seqlens, num_seqs, B, H, T, 128, dv, dt, gm, w + L.inner, workspace_bytes - L.inner,
+        stream);
+    if (st != KDA_OK) return st;
+    unpad(L.dq, grad_q, rows, 128, 64, 2);
+    unpad(L.dk, grad_k, rows, 128, 64, 2);
+    if (per_channel) unpad(L.dg, grad_g, rows, 128, 64, 4);
+    if (erase) unpad(L.de, grad_erase, rows, 128, 64, 4);
+    if (grad_initial_state) unpad(L.ds0, grad_initial_state, nh, 128 * dv, 64 * dv, 4);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
 
 #if KDA_DEBUG
   if (const int pre = debug_preconditions(g, gm == KDA_GATE_PER_CHANNEL, beta, erase, write,

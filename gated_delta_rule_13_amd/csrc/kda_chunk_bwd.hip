@@ -36,6 +36,7 @@
 // accumulators, run the carry of the current 64 tokens; one barrier per 64 tokens.
 #include <stddef.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -948,6 +949,38 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 }
 
 }  // namespace
+
+// Row copies for the dk = 64 backward, which runs the dk = 128 kernels on key-side arrays
+// padded with zero channels: destination row r takes the first min(w_src, w_dst) elements of
+// source row r, then zeros up to w_dst (the elements are moved as raw bits; zero bits are a
+// zero of either element type).
+template <typename E>
+__global__ void pad_rows_kernel(const E* __restrict__ src, E* __restrict__ dst, long long rows,
+                                int w_src, int w_dst) {
+  const long long n = rows * w_dst;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long r = i / w_dst;
+    const int c = (int)(i - r * w_dst);
+    dst[i] = c < w_src ? src[r * w_src + c] : E(0);
+  }
+}
+
+hipError_t launch_pad_rows(const void* src, void* dst, long long rows, int w_src, int w_dst,
+                           int elem_bytes, hipStream_t stream) {
+  if (rows <= 0 || w_dst <= 0) return hipSuccess;
+  const long long n = rows * w_dst;
+  const unsigned blocks = (unsigned)std::min<long long>((n + 255) / 256, 1 << 16);
+  if (elem_bytes == 2)
+    pad_rows_kernel<uint16_t><<<blocks, 256, 0, stream>>>(static_cast<const uint16_t*>(src),
+                                                         static_cast<uint16_t*>(dst), rows,
+                                                         w_src, w_dst);
+  else
+    pad_rows_kernel<uint32_t><<<blocks, 256, 0, stream>>>(static_cast<const uint32_t*>(src),
+                                                         static_cast<uint32_t*>(dst), rows,
+                                                         w_src, w_dst);
+  return hipGetLastError();
+}
 
 bool chunk_bwd_supports(int dk, int dv, int T) {
   // the forward's bounds, and one chain's state history addressable by a buffer descriptor

@@ -150,6 +150,10 @@ hipError_t launch_chunk_mfma_hist(const ChunkArgs& a, bool per_channel, hipStrea
 // first; a.plan, a.cu set).
 hipError_t launch_chunk_plan(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool per_channel, hipStream_t stream);
+// Row copies with a zero tail (kda_chunk_bwd.hip): dst[r][c] = src[r][c] for c < min(w_src,
+// w_dst), 0 for the rest of the w_dst elements; elem_bytes 2 or 4.
+hipError_t launch_pad_rows(const void* src, void* dst, long long rows, int w_src, int w_dst,
+                           int elem_bytes, hipStream_t stream);
 
 // KDA_DEBUG builds: the value preconditions of one call (up to four float arrays, each with
 // its range and flag bit, and cu_seqlens), checked on the device before the work;

@@ -292,7 +292,10 @@ kda_status kda_epilogue(const void* o_in, const void* z, const float* weight, fl
  * would be rejected as unsupported): two bf16 state histories of dk * dv / 16 bytes per
  * token (one dk x dv matrix per pair of 16-token blocks: the states entering the pairs and
  * the state gradients at their ends), sequences padded to whole 64-token steps (each
- * rounded up to 256 bytes), and for
+ * rounded up to 256 bytes), at dk = 64 preceded by copies of the key-side arrays and states
+ * padded to 128 channels (q, k, dq, dk bf16 and g, erase, dg, d erase float32 of
+ * B * H * T rows; initial state, final-state gradient and initial-state gradient of N * H
+ * chains), and for
  * packed sequences (num_seqs at most 1024) the work list of kda_chunk_fwd_workspace_size's
  * last case.
  */
@@ -316,9 +319,11 @@ size_t kda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int num
  *                    owned by the caller (contents on entry ignored; calls that overlap
  *                    on one workspace race)
  * Gradients are written for every token of every sequence; tokens outside every
- * sequence are left untouched. Supported: dt = KDA_BF16, dk = 128, dv = 64 or 128, either
- * gate mode, and T with (T + 64) * 8 * dv < 2^31, so that one chain's history fits a
- * buffer descriptor (T <= 2,097,087 at dv = 128; anything else: KDA_ERR_UNSUPPORTED).
+ * sequence are left untouched. Supported: dt = KDA_BF16, dk = 64 or 128, dv = 64 or 128,
+ * either gate mode, and T with (T + 64) * 8 * dv < 2^31, so that one chain's history fits
+ * a buffer descriptor (T <= 2,097,087 at dv = 128; anything else: KDA_ERR_UNSUPPORTED).
+ * dk = 64 runs the dk = 128 kernels on copies padded with zero key channels (a zero key
+ * channel never enters the state, so the other gradients are those of the dk = 64 problem).
  * A NULL required array, a workspace
  * smaller than the size above, or the forward's argument errors: KDA_ERR_INVALID_ARG.
  * Arithmetic: bf16 operands on the matrix cores with float32 accumulation and float32

@@ -327,7 +327,14 @@ def test_bwd_workspace_size():
     one = 16 * 2 * 4096 * 512
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 64, 0, kda.KDA_BF16) == 2 * one
     assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_F32) == 0
-    assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 64, 128, 0, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 96, 128, 0, kda.KDA_BF16) == 0
+    # dk = 64: the dk = 128 workspace behind padded copies of the key-side arrays and states
+    # (q, k, dq, dk bf16 and g, erase, dg, d erase fp32 of 128 channels per row; s0, dS_T,
+    # dS_0 of 128 x dv fp32 per chain)
+    rows, nh = 2 * 16 * 4096, 2 * 16
+    pads = rows * 128 * (4 * 2 + 4 * 4) + 3 * nh * 128 * 128 * 4
+    assert kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 64, 128, 0, kda.KDA_BF16) == \
+        pads + kda.kda_chunk_bwd_workspace_size(2, 16, 4096, 128, 128, 0, kda.KDA_BF16)
     assert kda.kda_chunk_bwd_workspace_size(0, 16, 4096, 128, 128, 0, kda.KDA_BF16) == 0
     # the longest T axis of the backward: (T + 64) 8 dv < 2^31
     assert kda.kda_chunk_bwd_workspace_size(1, 1, (1 << 21) - 65, 128, 128, 1, kda.KDA_BF16) > 0
@@ -356,7 +363,8 @@ def bwd_call(**over):
     (dict(workspace_bytes=100), kda.KDA_ERR_INVALID_ARG),     # smaller than the size
     (dict(workspace=None, workspace_bytes=1 << 30), kda.KDA_ERR_INVALID_ARG),
     (dict(dt=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),
-    (dict(dk=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=64), kda.KDA_ERR_INVALID_ARG),   # supported, but the workspace is too small
     (dict(dv=96), kda.KDA_ERR_UNSUPPORTED),
     # one chain's history must be addressable by a buffer descriptor: (T + 64) 8 dv < 2^31
     (dict(T=(1 << 21) - 64), kda.KDA_ERR_UNSUPPORTED),

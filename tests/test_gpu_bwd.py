@@ -5,7 +5,8 @@ the C ABI.
 Every gradient (dq, dk, dv, dg, dbeta, dS0) is compared chain by chain with the normwise
 bound max |got - want| <= 2e-2 max |want| of bf16 inputs with fp32 accumulation, each
 tensor separately. Checked: both gate modes and value head sizes on ragged sequences with
-and without an initial state and a final-state cotangent; sequence lengths around the
+and without an initial state and a final-state cotangent; key head size 64 (the dk = 128
+kernels on zero-padded key channels); sequence lengths around the
 16- and 64-token block edges (packed); the B2 H16 T4096 workload in full; the packed
 H32 T65536 workload on all 256 chains; tokens outside every sequence left untouched; and
 the Gated Delta Rule-2 backward (erase and write gates: their gradients replace dbeta), on
@@ -129,6 +130,53 @@ def test_bwd_varlen_edge_lengths(gate):
     check(x, got, oracle_grads(x, ct), f"bwd varlen edges {gate}")
 
 
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("dv", [128, 64])
+def test_bwd_dk64_small_ragged(gate, dv):
+    """dk = 64 (the dk = 128 kernels on copies padded with zero key channels): every gradient
+    of ragged sequences with an initial state and a final-state cotangent matches the oracle,
+    which runs at dk = 64."""
+    cfg = KDA_B2_H16_T4096.replace(gate=gate, dk=64, dv=dv, B=2, H=3, T=200, seed=86,
+                                   random_s0=True)
+    note(f"bwd dk=64 small {gate} dv={dv}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct), f"bwd dk=64 {gate} dv={dv}")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+def test_bwd_dk64_varlen_edge_lengths(gate):
+    """dk = 64, packed sequences around the block edges, through the raw entry point with
+    pre-filled outputs: tokens outside every sequence keep their values through the padded
+    copies, and every chain matches the oracle."""
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 130, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = KDA_VARLEN_H32_T65536.replace(gate=gate, dk=64, dv=128, H=2, T=int(cu[-1]) + 5,
+                                        num_seqs=0, pin_frac=0.05, seed=87)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(11).standard_normal((len(lens), 2, 64, 128)).astype(
+        np.float32) * np.float32(0.02)
+    ct = make_cotangents(cfg, len(lens))
+    note(f"bwd dk=64 varlen edges {gate}")
+    got = run_bwd(x, ct, fill=float("nan"))
+    for name in NAMES:
+        tail = got[name][0, :, cu[-1]:]
+        assert np.all(np.isnan(tail)), f"{name}: tokens outside every sequence were written"
+    check(x, got, oracle_grads(x, ct), f"bwd dk=64 varlen edges {gate}")
+
+
+def test_bwd_dk64_b2_h16_t4096():
+    """dk = 64 at B2 H16 T4096 (dv = 128): every chain matches the oracle."""
+    cfg = KDA_B2_H16_T4096.replace(name="kda_bf16_dk64_b2_h16_t4096", dk=64, seed=88)
+    note(f"bwd parity {cfg.name}")
+    x = make_chunk_inputs(cfg)
+    ct = make_cotangents(cfg, x.n_seqs)
+    errs = check(x, run_bwd(x, ct), oracle_grads(x, ct), cfg.name)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
 def test_bwd_b2_h16_t4096_full():
     cfg = KDA_B2_H16_T4096
     note(f"bwd parity {cfg.name}")
@@ -211,11 +259,12 @@ def test_bwd_more_sequences_than_one_plan_sorts():
 
 
 def test_bwd_longest_t_axis():
-    """The longest T axis the backward takes at dv = 128 (one chain's bf16 history,
-    (T + 64) x 16 x dv bytes, must stay under 2^31: T = 2^20 - 65), as packed sequences of
-    200 to 400 tokens: sampled sequences at the start, the middle and the end of the axis
-    match the oracle. The inputs are a 65,536-token draw repeated along T."""
-    T = (1 << 20) - 65
+    """The longest T axis the backward takes at dv = 128 (one chain's bf16 history, one
+    matrix per pair of blocks, (T + 64) x 8 x dv bytes, must stay under 2^31: T = 2^21 - 65),
+    as packed sequences of 200 to 400 tokens: sampled sequences at the start, the middle and
+    the end of the axis match the oracle. The inputs are a 65,536-token draw repeated
+    along T."""
+    T = (1 << 21) - 65
     rng = np.random.default_rng(94)
     lens = []
     while sum(lens) < T:
@@ -353,17 +402,18 @@ def check_gdr2(x, got, ref, what):
     return errs
 
 
+@pytest.mark.parametrize("dk", [128, 64])
 @pytest.mark.parametrize("gate", ["channel", "head"])
 @pytest.mark.parametrize("dv", [128, 64])
-def test_gdr2_bwd_small_ragged(gate, dv):
-    cfg = KDA_B2_H16_T4096.replace(gate=gate, dv=dv, B=2, H=3, T=200, seed=84, random_s0=True,
-                                   gates="gdr2")
-    note(f"gdr2 bwd small {gate} dv={dv}")
+def test_gdr2_bwd_small_ragged(gate, dv, dk):
+    cfg = KDA_B2_H16_T4096.replace(gate=gate, dk=dk, dv=dv, B=2, H=3, T=200, seed=84,
+                                   random_s0=True, gates="gdr2")
+    note(f"gdr2 bwd small {gate} dk={dk} dv={dv}")
     x = make_chunk_inputs(cfg)
     ct = make_cotangents(cfg, x.n_seqs)
     ref = oracle.kda_backward(x.q, x.k, x.v, x.g, x.beta, ct.do, s0=x.s0, dsT=ct.dsT,
                               erase=x.erase, write=x.write)
-    errs = check_gdr2(x, run_gdr2_bwd(x, ct), ref, f"gdr2 bwd {gate} dv={dv}")
+    errs = check_gdr2(x, run_gdr2_bwd(x, ct), ref, f"gdr2 bwd {gate} dk={dk} dv={dv}")
     print({k: f"{v:.2e}" for k, v in errs.items()})
 
 
