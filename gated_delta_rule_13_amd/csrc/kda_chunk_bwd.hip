@@ -405,16 +405,23 @@ struct GSmem {
   float dlgam[kDK];        // d log Gam
 };
 
-// LDS of one pair: each block's scratch, its transposed operands for the boundary tile (in
-// lane order: lane l holds the entries of the 16x16x16 A operand that lane l supplies;
-// channel tile m has the rows of the state tiles, row r being channel
-// 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4), and the boundary tiles, by tile parity.
+// LDS of one pair: each block's scratch; per block, the two channel halves' shares of the
+// sums over the channels (the 16 x 16 products of phase 1, and Kh S or Kt dS' of a value
+// tile before and after the boundary tiles, by tile parity) and of one decay per head; and
+// the boundary tiles, by tile parity and receiver.
+struct GHalf {
+  union {
+    f32x4 mq[2][3][64];     // [half]: Qh Kb^T, Kh Kb^T (column layout), Kh Kb^T (row layout)
+    // [parity][half]: Kh S or Kt dS' of the tile, before the boundary tiles and again after
+    // them (the second use begins once every wavefront has read the first)
+    f32x4 xp[2][2][64];
+  };
+  float dgh[2][16];         // [half]: the per-token sums of dg (one decay per head)
+};
 template <int DV>
-struct GPair {
+struct GQuad {
   GSmem<DV> w[2];            // the even block's, the odd block's
-  bf16x4 kt[8][64];          // even: Kt_e^T
-  bf16x4 qh[8][64];          // odd: Qh_o^T
-  bf16x4 kh[8][64];          // odd: Kh_o^T
+  GHalf x[2];
   bf16x8 bnd[2][2][4][64];   // [parity][receiver]: dS'_e for the even, S_o for the odd
 };
 
@@ -473,24 +480,30 @@ __device__ __forceinline__ bf16x8 tile_selector(int hh, int rr, int p) {
 // GDR2: the Gated Delta Rule-2 gates. The read-side key Kh is then (b * k) P, beta is 1,
 // R = w * V - Kh S, dV = w * dY, and the gradients of the gates are d erase = k P * dKh and
 // d write = V * dY (instead of dbeta).
-// One wavefront per SIMD (the two blocks' LDS and the exchange, about 57 KB, allow two
-// workgroups per compute unit), so each may hold up to 512 registers.
+// Four wavefronts per workgroup: the pair's even and odd block (odd = wave / 2), each split
+// over two halves of the key channels (hc = wave % 2: slabs 2 hc and 2 hc + 1, channel tiles
+// 4 hc .. 4 hc + 3, channels 64 hc .. 64 hc + 63). A half holds its slabs of the stored tile,
+// the row operands and the contraction sums; contractions over the channels (Kh S, Kt dS'
+// and the 16 x 16 products of the row operands) are summed over the two halves through LDS,
+// and the 16 x 16 steps that follow them (U, dY, the block inverse) run in both halves.
+// About 76 KB of LDS: two workgroups, two wavefronts per SIMD, at most 256 registers each.
 template <int DV, bool PER_CHANNEL, bool GDR2>
-__global__ __attribute__((amdgpu_waves_per_eu(1))) __launch_bounds__(128) void
+__global__ __attribute__((amdgpu_waves_per_eu(2))) __launch_bounds__(256) void
 chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   constexpr int NCT = DV / 16;   // value tiles of the block
-  __shared__ __align__(16) GPair<DV> sp;
+  __shared__ __align__(16) GQuad<DV> sp;
   const ChunkArgs& a = b.f;
-  // the wavefront's block within the pair (0: even, 1: odd), uniform across the wavefront
-  const int odd = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // the wavefront's block within the pair and channel half, uniform across the wavefront
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int odd = wave >> 1, hc = wave & 1;
   const int lane = threadIdx.x & 63;
   const int rr = lane & 15, p = lane >> 4;
   GSmem<DV>& sm = sp.w[odd];
-  const GSmem<DV>& so = sp.w[odd ^ 1];
+  GHalf& xs = sp.x[odd];
   const int h = blockIdx.x / slots, slot = blockIdx.x % slots;
   int n, pr;
   TokenRange tr;
-  if (!grad_item(a, slot, n, pr, tr)) return;   // both wavefronts leave together
+  if (!grad_item(a, slot, n, pr, tr)) return;   // all four wavefronts leave together
   const int blk = 2 * pr + odd;
   // tokens of this block in the sequence: 0 for the odd block of a sequence's last pair when
   // its block count is odd; every view of that block is then empty (zeros), which makes it
@@ -509,108 +522,122 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   const rsrc_t es = make_rsrc(a.erase + (GDR2 ? row0 * kDK : 0), GDR2 ? len * kDK * 4 : 0);
   const rsrc_t ws_ = make_rsrc(a.write + (GDR2 ? row0 * DV : 0), GDR2 ? len * DV * 4 : 0);
 
-  // the stored matrix's value tiles 0 and 1 (prefetched two tiles ahead in the loop below:
-  // with one wavefront per SIMD, the loads must cover the memory latency by themselves)
-  bf16x8 hb[4], hn[4];
+  // this half's slabs of the stored matrix's value tiles 0 and 1 (prefetched two tiles
+  // ahead in the loop below)
+  bf16x8 hb[2], hn[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    hb[ks] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)((ks * 64 + lane) * 16)));
-    hn[ks] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)(((4 + ks) * 64 + lane) * 16)));
+  for (int j = 0; j < 2; ++j) {
+    const int ks = 2 * hc + j;
+    hb[j] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)((ks * 64 + lane) * 16)));
+    hn[j] = __builtin_bit_cast(bf16x8, ld_b128(hm, (uint32_t)(((4 + ks) * 64 + lane) * 16)));
   }
-  // q and k of token rr, channels 32 ks + 8 p + i: the row operands (kept for the
-  // per-channel step after the tiles)
-  bf16x8 q8[4], k8[4];
-  f32x4 e8[4][2];   // erase gates of the same elements (Gated Delta Rule-2)
+  // q and k of token rr, channels 32 ks + 8 p + i of this half's slabs: the row operands
+  // (kept for the per-channel step after the tiles)
+  bf16x8 q8[2], k8[2];
+  f32x4 e8[2][2];   // erase gates of the same elements (Gated Delta Rule-2)
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const uint32_t off = (uint32_t)(rr * kDK + 32 * ks + 8 * p);
-    q8[ks] = __builtin_bit_cast(bf16x8, ld_b128(qs, off * 2));
-    k8[ks] = __builtin_bit_cast(bf16x8, ld_b128(ks_, off * 2));
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t off = (uint32_t)(rr * kDK + 32 * (2 * hc + j) + 8 * p);
+    q8[j] = __builtin_bit_cast(bf16x8, ld_b128(qs, off * 2));
+    k8[j] = __builtin_bit_cast(bf16x8, ld_b128(ks_, off * 2));
     if (GDR2) {
-      e8[ks][0] = ld_b128(es, off * 4);
-      e8[ks][1] = ld_b128(es, off * 4 + 16);
+      e8[j][0] = ld_b128(es, off * 4);
+      e8[j][1] = ld_b128(es, off * 4 + 16);
     }
   }
 
-  // ---- 0. decay of every channel (two per lane), dO and V rows, beta. Every load is issued
-  // before the first use: bounded reads past the block's last token return g = 0.
+  // ---- 0. decay of this half's channels (one per lane), half of the dO and V rows, beta.
+  // Every load is issued before the first use: bounded reads past the block's last token
+  // return g = 0.
   {
     const rsrc_t ds = make_rsrc(static_cast<const bf16*>(b.dout) + row0 * DV, len * DV * 2);
     const rsrc_t gs = make_rsrc(a.g + row0 * (PER_CHANNEL ? kDK : 1),
                                 len * (PER_CHANNEL ? kDK : 1) * 4);
-    f32x4 dov[16 * DV / 8 / 64], vov[16 * DV / 8 / 64];
+    constexpr int NV = 16 * DV / 8 / 128;   // 16-byte row pieces per lane (half the rows)
+    f32x4 dov[NV], vov[NV];
 #pragma unroll
-    for (int j = 0; j < 16 * DV / 8 / 64; ++j) {
-      const int i = lane + 64 * j, tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+    for (int j = 0; j < NV; ++j) {
+      const int i = lane + 64 * (2 * j + hc), tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
       dov[j] = ld_b128(ds, (uint32_t)(tt * DV + cc) * 2);
       vov[j] = ld_b128(vs, (uint32_t)(tt * DV + cc) * 2);
     }
     const float bv = GDR2 ? 1.f : ld_b32(make_rsrc(a.beta + row0, len * 4), (lane & 15) * 4);
-    float gv[2][16];
+    float gv[16];
+    const int c = 64 * hc + lane;
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
+    for (int t = 0; t < 16; ++t)
+      gv[t] = ld_b32(gs, (uint32_t)(PER_CHANNEL ? t * kDK + c : t) * 4);
 #pragma unroll
-      for (int t = 0; t < 16; ++t)
-        gv[half][t] = ld_b32(gs, (uint32_t)(PER_CHANNEL ? t * kDK + lane + 64 * half : t) * 4);
-#pragma unroll
-    for (int j = 0; j < 16 * DV / 8 / 64; ++j) {
-      const int i = lane + 64 * j, tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
+    for (int j = 0; j < NV; ++j) {
+      const int i = lane + 64 * (2 * j + hc), tt = i / (DV / 8), cc = 8 * (i % (DV / 8));
       *reinterpret_cast<f32x4*>(&sm.dor[tt][cc]) = dov[j];
       *reinterpret_cast<f32x4*>(&sm.vr[tt][cc]) = vov[j];
     }
+    float run = 1.f;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int c = lane + 64 * half;
-      float run = 1.f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        run *= __expf(gv[half][t]);
-        sm.P[t][c] = run;
-      }
-      sm.gam[c] = run;
+    for (int t = 0; t < 16; ++t) {
+      run *= __expf(gv[t]);
+      sm.P[t][c] = run;
     }
-    if (lane < 16) sm.beta[lane] = bv;
+    sm.gam[c] = run;
+    if (hc == 0 && lane < 16) sm.beta[lane] = bv;
   }
   wave_lds_fence();
 
-  // ---- 1. row operands of token rr (bf16): Qh, Kh (the read-side key), Kb = k / P, Kt
-  bf16x8 ah[4], at[4];
-  f32x4 accq = zero4(), acck = zero4(), acct = zero4();
+  // ---- 1. row operands of token rr (bf16) on this half's slabs: Qh, Kh (the read-side
+  // key), Kb = k / P, Kt; this half's share of the 16 x 16 products over the channels; the
+  // transposed operands of this half's channel tiles for the boundary tile (Kt_e^T in the
+  // even block, Qh_o^T and Kh_o^T in the odd one)
+  bf16x8 ah[2], at[2];
+  bf16x4 tr1[4], tr2[4];
+  {
+    f32x4 accq = zero4(), acck = zero4(), acct = zero4();
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int c0 = 32 * ks + 8 * p;
-    float qh[8], kh[8], kb[8], kt[8];
+    for (int j = 0; j < 2; ++j) {
+      const int c0 = 32 * (2 * hc + j) + 8 * p;
+      float qh[8], kh[8], kb[8], kt[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float P = sm.P[rr][c0 + i], G = sm.gam[c0 + i];
-      const float rp = __builtin_amdgcn_rcpf(P);
-      const float kf = static_cast<float>(k8[ks][i]);
-      qh[i] = static_cast<float>(q8[ks][i]) * P;
-      kh[i] = kf * P * (GDR2 ? e8[ks][i >> 2][i & 3] : 1.f);
-      kb[i] = kf * rp;
-      kt[i] = kb[i] * G;
-    }
-    const bf16x8 bq = to_bf16x8(qh), bc = to_bf16x8(kb);
-    ah[ks] = to_bf16x8(kh);
-    at[ks] = to_bf16x8(kt);
-    accq = mfma32(bq, bc, accq);        // (Qh Kb^T)[4p + e][rr]
-    acck = mfma32(ah[ks], bc, acck);    // (Kh Kb^T)[4p + e][rr]
-    acct = mfma32(bc, ah[ks], acct);    // (Kh Kb^T)[rr][4p + e]
-    // the transposed operands of channel tiles 2 ks and 2 ks + 1 for the boundary tile:
-    // Kt_e^T in the even block, Qh_o^T and Kh_o^T in the odd one
+      for (int i = 0; i < 8; ++i) {
+        const float P = sm.P[rr][c0 + i], G = sm.gam[c0 + i];
+        const float rp = __builtin_amdgcn_rcpf(P);
+        const float kf = static_cast<float>(k8[j][i]);
+        qh[i] = static_cast<float>(q8[j][i]) * P;
+        kh[i] = kf * P * (GDR2 ? e8[j][i >> 2][i & 3] : 1.f);
+        kb[i] = kf * rp;
+        kt[i] = kb[i] * G;
+      }
+      const bf16x8 bq = to_bf16x8(qh), bc = to_bf16x8(kb);
+      ah[j] = to_bf16x8(kh);
+      at[j] = to_bf16x8(kt);
+      accq = mfma32(bq, bc, accq);        // (Qh Kb^T)[4p + e][rr], this half's channels
+      acck = mfma32(ah[j], bc, acck);     // (Kh Kb^T)[4p + e][rr]
+      acct = mfma32(bc, ah[j], acct);     // (Kh Kb^T)[rr][4p + e]
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8 ts = tile_selector(hh, rr, p);
-      if (odd) {
-        sp.qh[2 * ks + hh][lane] = pack4(mfma32(bq, ts, zero4()));
-        sp.kh[2 * ks + hh][lane] = pack4(mfma32(ah[ks], ts, zero4()));
-      } else {
-        sp.kt[2 * ks + hh][lane] = pack4(mfma32(at[ks], ts, zero4()));
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8 ts = tile_selector(hh, rr, p);
+        if (odd) {
+          tr1[2 * j + hh] = pack4(mfma32(bq, ts, zero4()));
+          tr2[2 * j + hh] = pack4(mfma32(ah[j], ts, zero4()));
+        } else {
+          tr1[2 * j + hh] = pack4(mfma32(at[j], ts, zero4()));
+          tr2[2 * j + hh] = bf16x4{};
+        }
       }
     }
+    xs.mq[hc][0][lane] = accq;
+    xs.mq[hc][1][lane] = acck;
+    xs.mq[hc][2][lane] = acct;
   }
-  // ---- 2. M, A and Tm of the block
+  lds_barrier();   // both halves' shares, the dO and V rows and beta are written
+  // ---- 2. M, A and Tm of the block (in both halves; both write the same values)
   {
+    f32x4 accq, acck, acct;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      accq[e] = xs.mq[0][0][lane][e] + xs.mq[1][0][lane][e];
+      acck[e] = xs.mq[0][1][lane][e] + xs.mq[1][1][lane][e];
+      acct[e] = xs.mq[0][2][lane][e] + xs.mq[1][2][lane][e];
+    }
     f32x4 nc, nr;
     const float brr = sm.beta[rr];
 #pragma unroll
@@ -625,19 +652,18 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.u.w.Tm[4 * p + e][rr] = inv[e];
   }
-  wave_lds_fence();
+  lds_barrier();   // every half has read the shares (their storage holds the tiles' sums next)
 
   // ---- 3. the value tiles
-  f32x4 C1[8], C2[8], C3[8], g1 = zero4(), g2 = zero4();
-  float r2[8];
+  f32x4 C1[4], C2[4], C3[4], g1 = zero4(), g2 = zero4();
+  float r2[4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < 4; ++m) {
     C1[m] = C2[m] = C3[m] = zero4();
     r2[m] = 0.f;
   }
   f32x4 r1 = zero4();
   const rsrc_t vd = make_rsrc(static_cast<bf16*>(b.dv) + row0 * DV, len * DV * 2);
-  wave_lds_fence();   // the transposed operands are written
   // the write gates of value tile ct in the accumulator layout (token 4p + e), loaded one
   // tile ahead (Gated Delta Rule-2)
   f32x4 wnext;
@@ -647,22 +673,22 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       wnext[e] = GDR2 ? ld_b32(ws_, (uint32_t)((4 * p + e) * DV + 16 * ct + rr) * 4) : 1.f;
   };
   load_write_gates(0);
-  // Gated Delta Rule-2: the erase gates of token 4 p + e, channel 16 m + rr for the
+  // Gated Delta Rule-2: the erase gates of token 4 p + e, channel 16 (4 hc + m) + rr for the
   // per-channel step after the tiles (loaded now, so that the tiles cover their latency)
-  float e4[8][4];
+  float e4[4][4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      e4[m][e] = GDR2 ? ld_b32(es, (uint32_t)((4 * p + e) * kDK + 16 * m + rr) * 4) : 1.f;
-  // the tile loop, compiled separately for each role (one loop per wavefront, no branch on
-  // the role inside it)
+      e4[m][e] = GDR2 ? ld_b32(es, (uint32_t)((4 * p + e) * kDK + 16 * (4 * hc + m) + rr) * 4)
+                      : 1.f;
+  // the tile loop, compiled separately for each block of the pair (one loop per wavefront,
+  // no branch on the block inside it)
   auto tiles = [&](auto role) {
     constexpr int ODD = decltype(role)::value;
     // the block's operands that every tile uses, held in registers across the tiles: Tm,
-    // Tm^T, M^T, beta, the transposes' selectors, the decay Gam of the state tiles' rows
-    // (channel tile m: 32 (m / 2) + 8 p + 4 (m % 2) + e) and the transposed operands of the
-    // boundary tile (even: Kt_e^T; odd: Qh_o^T, Kh_o^T)
+    // Tm^T, M^T, beta, the transposes' selectors and the decay Gam of this half's state tile
+    // rows (channel tile 2 j + hh: 32 (2 hc + j) + 8 p + 4 hh + e)
     bf16x4 tA, tT, mT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -672,14 +698,11 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     }
     const f32x4 btv = *reinterpret_cast<const f32x4*>(&sm.beta[4 * p]);
     const bf16x8 sel[2] = {selector(0, rr, p), selector(1, rr, p)};
-    f32x4 gmr[8];
-    bf16x4 tr1[8], tr2[8];
+    f32x4 gmr[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      gmr[m] = *reinterpret_cast<const f32x4*>(&sm.gam[32 * (m >> 1) + 8 * p + 4 * (m & 1)]);
-      tr1[m] = ODD ? sp.qh[m][lane] : sp.kt[m][lane];
-      tr2[m] = ODD ? sp.kh[m][lane] : bf16x4{};
-    }
+    for (int m = 0; m < 4; ++m)
+      gmr[m] = *reinterpret_cast<const f32x4*>(
+          &sm.gam[32 * (2 * hc + (m >> 1)) + 8 * p + 4 * (m & 1)]);
 #pragma unroll 1
     for (int ct = 0; ct < NCT; ++ct) {
       const int col = 16 * ct + rr, par = ct & 1;
@@ -694,128 +717,153 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
       bf16x4 dob;
 #pragma unroll
       for (int e = 0; e < 4; ++e) dob[e] = sm.dor[4 * p + e][col];
-      // this block's S and dS' of the tile (sc, dc), R = w V - Kh S, U, dY
-      bf16x8 sc[4], dc[4];
+      // this half's slabs of the block's S and dS' of the tile (sc, dc)
+      bf16x8 sc[2], dc[2];
       f32x4 R, U, dY;
-      if constexpr (!ODD) {   // even: S_e is stored; U_e, then the odd block's entering state
+      // A: this half's share of Kh S_e (even) or Kt dS'_o (odd), from the stored slabs
+      {
+        f32x4 part = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sc[ks] = hb[ks];
-        f32x4 X = zero4(), x;
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (!ODD) {
+            sc[j] = hb[j];
+            part = mfma32(ah[j], sc[j], part);
+          } else {
+            dc[j] = hb[j];
+            part = mfma32(at[j], dc[j], part);
+          }
+        }
+        xs.xp[par][hc][lane] = part;
+      }
+      // the stored slabs two tiles ahead (past the last tile the loads read zeros)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) X = mfma32(ah[ks], sc[ks], X);
+      for (int j = 0; j < 2; ++j) {
+        hb[j] = hn[j];
+        hn[j] = __builtin_bit_cast(
+            bf16x8, ld_b128(hm, (uint32_t)((((ct + 2) * 4 + 2 * hc + j) * 64 + lane) * 16)));
+      }
+      lds_barrier();   // both halves' shares are written
+      f32x4 whole;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) whole[e] = xs.xp[par][0][lane][e] + xs.xp[par][1][lane][e];
+      if constexpr (!ODD) {   // U_e, then this half's rows of the odd block's entering state
+        f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          R[e] = wcol[e] * vcol[e] - X[e];
+          R[e] = wcol[e] * vcol[e] - whole[e];
           x[e] = btv[e] * R[e];
         }
         U = mfma16(tA, pack4(x), zero4());
         const bf16x4 ub = pack4(U);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {   // S_o = Diag(Gam_e) S_e + Kt_e^T U_e
+        for (int j = 0; j < 2; ++j) {   // S_o = Diag(Gam_e) S_e + Kt_e^T U_e
           f32x4 acc[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const f32x4 gm = gmr[2 * ks + hh];
+            const f32x4 gm = gmr[2 * j + hh];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[hh][e] = gm[e] * static_cast<float>(sc[ks][4 * hh + e]);
-            acc[hh] = mfma16(tr1[2 * ks + hh], ub, acc[hh]);
+            for (int e = 0; e < 4; ++e)
+              acc[hh][e] = gm[e] * static_cast<float>(sc[j][4 * hh + e]);
+            acc[hh] = mfma16(tr1[2 * j + hh], ub, acc[hh]);
           }
-          sp.bnd[par][1][ks][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
+          sp.bnd[par][1][2 * hc + j][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
         }
-      } else {      // odd: dS'_o is stored; dY_o, then the even block's leaving gradient
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) dc[ks] = hb[ks];
-        f32x4 dU2 = zero4(), y;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) dU2 = mfma32(at[ks], dc[ks], dU2);
-        const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
+      } else {      // dY_o, then this half's rows of the even block's leaving gradient
+        const f32x4 dU = whole + mfma16(mT, dob, zero4());
         dY = mfma16(tT, pack4(dU), zero4());
+        f32x4 y;
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = -btv[e] * dY[e];
         const bf16x4 yb = pack4(y);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {   // dS'_e = Diag(Gam_o) dS'_o + Qh_o^T dO_o - Kh_o^T Diag(beta_o) dY_o
+        for (int j = 0; j < 2; ++j) {
+          // dS'_e = Diag(Gam_o) dS'_o + Qh_o^T dO_o - Kh_o^T Diag(beta_o) dY_o
           f32x4 acc[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int m = 2 * ks + hh;
-            const f32x4 gm = gmr[2 * ks + hh];
+            const f32x4 gm = gmr[2 * j + hh];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[hh][e] = gm[e] * static_cast<float>(dc[ks][4 * hh + e]);
-            acc[hh] = mfma16(tr1[m], dob, acc[hh]);
-            acc[hh] = mfma16(tr2[m], yb, acc[hh]);
+            for (int e = 0; e < 4; ++e)
+              acc[hh][e] = gm[e] * static_cast<float>(dc[j][4 * hh + e]);
+            acc[hh] = mfma16(tr1[2 * j + hh], dob, acc[hh]);
+            acc[hh] = mfma16(tr2[2 * j + hh], yb, acc[hh]);
           }
-          sp.bnd[par][0][ks][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
+          sp.bnd[par][0][2 * hc + j][lane] = cat8(pack4(acc[0]), pack4(acc[1]));
         }
       }
-      // the stored matrix two tiles ahead (past the last tile the loads read zeros)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        hb[ks] = hn[ks];
-        hn[ks] = __builtin_bit_cast(
-            bf16x8, ld_b128(hm, (uint32_t)((((ct + 2) * 4 + ks) * 64 + lane) * 16)));
-      }
       lds_barrier();   // the boundary tiles of this value tile are written
-      if constexpr (!ODD) {   // even: its leaving gradient came from the odd block
+      // B: this half's share of Kt dS'_e (even) or Kh S_o (odd), from the received slabs
+      {
+        f32x4 part = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) dc[ks] = sp.bnd[par][0][ks][lane];
-        f32x4 dU2 = zero4();
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (!ODD) {
+            dc[j] = sp.bnd[par][0][2 * hc + j][lane];
+            part = mfma32(at[j], dc[j], part);
+          } else {
+            sc[j] = sp.bnd[par][1][2 * hc + j][lane];
+            part = mfma32(ah[j], sc[j], part);
+          }
+        }
+        xs.xp[par][hc][lane] = part;
+      }
+      lds_barrier();   // both halves' shares are written
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) dU2 = mfma32(at[ks], dc[ks], dU2);
-        const f32x4 dU = dU2 + mfma16(mT, dob, zero4());
+      for (int e = 0; e < 4; ++e) whole[e] = xs.xp[par][0][lane][e] + xs.xp[par][1][lane][e];
+      if constexpr (!ODD) {   // dY_e
+        const f32x4 dU = whole + mfma16(mT, dob, zero4());
         dY = mfma16(tT, pack4(dU), zero4());
-      } else {      // odd: its entering state came from the even block
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sc[ks] = sp.bnd[par][1][ks][lane];
-        f32x4 X = zero4(), x;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) X = mfma32(ah[ks], sc[ks], X);
+      } else {      // U_o
+        f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          R[e] = wcol[e] * vcol[e] - X[e];
+          R[e] = wcol[e] * vcol[e] - whole[e];
           x[e] = btv[e] * R[e];
         }
         U = mfma16(tA, pack4(x), zero4());
       }
+      // the tile rows of U, dY and Diag(beta) dY (both halves write the same values, each
+      // then reads back what it wrote)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sm.u.w.ut[4 * p + e][rr] = static_cast<bf16>(U[e]);
         sm.u.w.yt[4 * p + e][rr] = static_cast<bf16>(dY[e]);
         sm.u.w.bt[4 * p + e][rr] = static_cast<bf16>((GDR2 ? wcol[e] : btv[e]) * dY[e]);
         r1[e] += dY[e] * R[e];
-        if (GDR2 && 4 * p + e < len)   // d write = V * dY
+        if (GDR2 && hc == 0 && 4 * p + e < len)   // d write = V * dY
           b.dwrite[(row0 + 4 * p + e) * DV + col] = vcol[e] * dY[e];
       }
       wave_lds_fence();
       // dV = Diag(beta) dY (w * dY): this tile's 16 token rows of 16 columns
-      if (lane < 32) {
+      if (hc == 0 && lane < 32) {
         const int t = lane >> 1, c8 = 8 * (lane & 1);
         st_b128(vd, (uint32_t)(t * DV + 16 * ct + c8) * 2,
                 *reinterpret_cast<const bf16x8*>(&sm.u.w.bt[t][c8]));
       }
-      // the tile's share of the contractions over the value columns (k = column 16 ct + 4p + i)
+      // the tile's share of the contractions over the value columns (k = column
+      // 16 ct + 4p + i), for this half's channel tiles
       const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.dor[rr][16 * ct + 4 * p]);
       // beta = 1 with the Gated Delta Rule-2 gates: Diag(beta) dY is dY itself
-      const bf16x4 ay = *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.u.w.yt[rr][4 * p] : &sm.u.w.bt[rr][4 * p]);
+      const bf16x4 ay =
+          *reinterpret_cast<const bf16x4*>(GDR2 ? &sm.u.w.yt[rr][4 * p] : &sm.u.w.bt[rr][4 * p]);
       const bf16x4 au = *reinterpret_cast<const bf16x4*>(&sm.u.w.ut[rr][4 * p]);
       const bf16x4 ayy = *reinterpret_cast<const bf16x4*>(&sm.u.w.yt[rr][4 * p]);
-      g1 = mfma16(ao, au, g1);     // (dO U^T)[4p + e][rr]
+      g1 = mfma16(ao, au, g1);     // (dO U^T)[4p + e][rr] (used from half 0)
       g2 = mfma16(ayy, au, g2);    // (dY U^T)[4p + e][rr]
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int m = 2 * ks + hh;   // channel tile: channels 16 m + n
-          const f32x4 st = mfma32(sc[ks], sel[hh], zero4());   // S[16 m + rr][16 ct + 4p + e]
-          const f32x4 dt = mfma32(dc[ks], sel[hh], zero4());
+          const int m = 2 * j + hh;   // channel tile 4 hc + m: channels 16 (4 hc + m) + n
+          const f32x4 st = mfma32(sc[j], sel[hh], zero4());   // S[16 (4 hc + m) + rr][16 ct + 4p + e]
+          const f32x4 dt = mfma32(dc[j], sel[hh], zero4());
           const bf16x4 sb4 = pack4(st), db4 = pack4(dt);
-          C1[m] = mfma16(ao, sb4, C1[m]);   // (dO S^T)[4p + e][16 m + rr]
+          C1[m] = mfma16(ao, sb4, C1[m]);   // (dO S^T)[4p + e][16 (4 hc + m) + rr]
           C2[m] = mfma16(ay, sb4, C2[m]);   // (Diag(beta) dY S^T)
           C3[m] = mfma16(au, db4, C3[m]);   // (U dS'^T)
 #pragma unroll
           for (int e = 0; e < 4; ++e) r2[m] += st[e] * dt[e];
         }
-      wave_lds_fence();   // the tile rows are rewritten by the next tile
     }
   };
   if (odd) tiles(std::integral_constant<int, 1>{});
@@ -831,16 +879,19 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     r1[e] = v;   // lane 16 p + r: token 4 p + e
   }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < 4; ++m) {
     r2[m] += __shfl_xor(r2[m], 16, 64);
     r2[m] += __shfl_xor(r2[m], 32, 64);
   }
+  lds_barrier();   // both halves are done with the last tile's rows (G1 shares their storage)
+  if (hc == 0) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    sm.u.w.G1[4 * p + e][rr] = g1[e];
-    sm.G2[4 * p + e][rr] = g2[e];
+    for (int e = 0; e < 4; ++e) {
+      sm.u.w.G1[4 * p + e][rr] = g1[e];
+      sm.G2[4 * p + e][rr] = g2[e];
+    }
   }
-  wave_lds_fence();
+  lds_barrier();   // G1 and G2 are written
 
   // ---- 4. the 16 x 16 corrections and the chain rule through the decay, per channel tile
   bf16x4 dmr, dar, dmT, daT;   // dM, dA rows rr and columns rr
@@ -852,10 +903,10 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
     dmT[i] = static_cast<bf16>(rr <= s_ ? sm.u.w.G1[s_][rr] : 0.f);
     daT[i] = static_cast<bf16>(rr < s_ ? -sm.beta[s_] * sm.G2[s_][rr] : 0.f);
   }
-  wave_lds_fence();   // G1 is read before dk overwrites it (same storage)
+  lds_barrier();   // G1 is read by both halves before dk overwrites it (same storage)
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int ch = 16 * m + rr;
+  for (int m = 0; m < 4; ++m) {
+    const int ch = 16 * (4 * hc + m) + rr;
     const float G = sm.gam[ch];
     // q and k of token 4 p + e, channel ch: the rows transposed by the selector (exact)
     const bf16x8 sel = selector(m & 1, rr, p);
@@ -900,41 +951,47 @@ chunk_bwd_grad_kernel(BwdArgs b, int slots) {
   }
   wave_lds_fence();
 
-  // ---- 5. outputs: dq, dk rows; dg (suffix sums); dbeta
+  // ---- 5. outputs: this half's channels of the dq, dk rows; dg (suffix sums); dbeta
   {
     const rsrc_t qd = make_rsrc(static_cast<bf16*>(b.dq) + row0 * kDK, len * kDK * 2);
     const rsrc_t kd = make_rsrc(static_cast<bf16*>(b.dk) + row0 * kDK, len * kDK * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = lane + 64 * i;   // 256 pieces of 8 channels
-      const int t = idx >> 4, c8 = 8 * (idx & 15);
+    for (int i = 0; i < 2; ++i) {
+      const int idx = lane + 64 * i;   // 128 pieces of 8 channels (16 tokens x 8 pieces)
+      const int t = idx >> 3, c8 = 64 * hc + 8 * (idx & 7);
       const uint32_t off = (uint32_t)(t * kDK + c8) * 2;
       st_b128(qd, off, *reinterpret_cast<const bf16x8*>(&sm.dor[t][c8]));
       st_b128(kd, off, *reinterpret_cast<const bf16x8*>(&sm.u.dkr[t][c8]));
     }
   }
-  float dgs[2][16];   // per-channel suffix sums (lane's two channels)
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int c = lane + 64 * half;
+  float dgs[16];   // the suffix sums of this lane's channel 64 hc + lane
+  {
+    const int c = 64 * hc + lane;
     float acc = sm.dlgam[c];
 #pragma unroll
     for (int t = 15; t >= 0; --t) {
       acc += sm.P[t][c];
-      dgs[half][t] = acc;
+      dgs[t] = acc;
       if (PER_CHANNEL && t < len) b.dg[(row0 + t) * kDK + c] = acc;
     }
   }
-  if (!PER_CHANNEL) {   // one decay per head: the sum over the channels
+  if (!PER_CHANNEL) {   // one decay per head: the sum over the channels of both halves
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      float v = dgs[0][t] + dgs[1][t];
+      float v = dgs[t];
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      if (lane == 0 && t < len) b.dg[row0 + t] = v;
+      dgs[t] = v;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) xs.dgh[hc][t] = dgs[t];
     }
   }
-  if (!GDR2) {
+  lds_barrier();   // (one decay per head) both halves' sums are written
+  if (!PER_CHANNEL && hc == 0 && lane < 16 && lane < len)
+    b.dg[row0 + lane] = xs.dgh[0][lane] + xs.dgh[1][lane];
+  if (!GDR2 && hc == 0) {
     // dbeta_t = sum_j dY_tj R_tj - sum_s A_ts (dY U^T)_ts; lane 16 p holds token 4 p + e
     if (rr == 0) {
 #pragma unroll
@@ -1013,11 +1070,11 @@ hipError_t launch_grad(BwdArgs& b, bool per_channel, int slots, hipStream_t stre
   const ChunkArgs& a = b.f;
   const unsigned grid = (unsigned)slots * a.H;
   if (a.dv == 128) {
-    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, 128, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, 128, 0, stream>>>(b, slots);
+    if (per_channel) chunk_bwd_grad_kernel<128, true, GDR2><<<grid, 256, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<128, false, GDR2><<<grid, 256, 0, stream>>>(b, slots);
   } else {
-    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, 128, 0, stream>>>(b, slots);
-    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, 128, 0, stream>>>(b, slots);
+    if (per_channel) chunk_bwd_grad_kernel<64, true, GDR2><<<grid, 256, 0, stream>>>(b, slots);
+    else chunk_bwd_grad_kernel<64, false, GDR2><<<grid, 256, 0, stream>>>(b, slots);
   }
   return hipGetLastError();
 }
