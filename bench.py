@@ -63,8 +63,8 @@ MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
 # one kda_chunk_bwd call (state history, reverse carry, gradients): its own source and that of
 # the forward kernel whose history mode it runs
 MEASURED_TRAFFIC_BWD = {  # profiles/kda_chunk_bwd_varlen_h32_t65536.md
-    "bytes": 20037801569,
-    "kernel_sha256": "76f39b31263246852e9bdded5bf0f5ec7c86dc5577bfd219a96b2ddd35deac3b",
+    "bytes": 20040202992,
+    "kernel_sha256": "2286d7707f2052a2ae67b1e87ac3eda8181d747c71ccfc3ae43561b2ffc0ceee",
     "hist_sha256": "7dc592aea77832c74519dc5aca8fe732cbf2ee91065e504e50082b947296400e",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
