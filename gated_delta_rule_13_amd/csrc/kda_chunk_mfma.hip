@@ -120,7 +120,8 @@ static_assert((kLDK * 2) % 16 == 0 && (kLDT * 2) % 16 == 0, "row pitch must keep
 // A lane holds 8 tokens of one half block; the halves exchange their products.
 // For Gated Delta Rule-2 the read-side operand is (b * k) P, b the erase gate: it serves
 // both the prediction (b * k)^T S and the strictly lower (b * k) (k / P)^T of the solve.
-template <bool GDR2>
+// Without NEEDQ (a pass that writes no outputs) the query operand is not formed.
+template <bool GDR2, bool NEEDQ = true>
 __device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const BlockRegs& r,
                                            int I, int lane) {
   const int cq = lane & 31, hf = lane >> 5;
@@ -151,10 +152,10 @@ __device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const Bl
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       run[j] *= al[u][j];
-      qr[j] = static_cast<float>(r.q[u][j]) * run[j];
+      qr[j] = NEEDQ ? static_cast<float>(r.q[u][j]) * run[j] : 0.f;
       kr[j] = static_cast<float>(r.k[u][j]) * (GDR2 ? r.b[u][j] * run[j] : run[j]);
     }
-    *reinterpret_cast<bf16x4*>(&st.qr[t][4 * cq]) = pack4(qr);
+    if (NEEDQ) *reinterpret_cast<bf16x4*>(&st.qr[t][4 * cq]) = pack4(qr);
     *reinterpret_cast<bf16x4*>(&st.kr[t][4 * cq]) = pack4(kr);
   }
 #pragma unroll
@@ -183,21 +184,22 @@ __device__ __forceinline__ void prep_block(Stage& st, bf16 (*kd)[kLDK], const Bl
 
 
 // The A_qk / A_kk tile of block I and the inverse of its (I + N), N = Diag(beta) A_kk
-// strictly lower (unit_lower_inverse).
+// strictly lower (unit_lower_inverse); A_qk only when NEEDQ.
+template <bool NEEDQ = true>
 __device__ __forceinline__ void block_tiles(Stage& st, const bf16 (*kd)[kLDK], int I, int rr,
                                             int p) {
   bf16x8 bq[4], bk[4], bc[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int ch = 32 * ks + 8 * p;
-    bq[ks] = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][ch]);
+    if (NEEDQ) bq[ks] = *reinterpret_cast<const bf16x8*>(&st.qr[16 * I + rr][ch]);
     bk[ks] = *reinterpret_cast<const bf16x8*>(&st.kr[16 * I + rr][ch]);
     bc[ks] = *reinterpret_cast<const bf16x8*>(&kd[16 * I + rr][ch]);
   }
   f32x4 accq = zero4(), acck = zero4(), acct = zero4();
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    accq = mfma32(bq[ks], bc[ks], accq);   // A_qk[i][j], lane holds i = 4p + e, j = rr
+    if (NEEDQ) accq = mfma32(bq[ks], bc[ks], accq);   // A_qk[i][j], lane holds i = 4p + e, j = rr
     acck = mfma32(bk[ks], bc[ks], acck);   // A_kk[i][j]
     acct = mfma32(bc[ks], bk[ks], acct);   // A_kk[j][i]: lane holds A_kk[rr][4p + e]
   }
@@ -206,7 +208,7 @@ __device__ __forceinline__ void block_tiles(Stage& st, const bf16 (*kd)[kLDK], i
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 4 * p + e;
-    st.aqk[I][i][rr] = static_cast<bf16>(rr <= i ? accq[e] : 0.f);
+    if (NEEDQ) st.aqk[I][i][rr] = static_cast<bf16>(rr <= i ? accq[e] : 0.f);
     nc[e] = rr < i ? st.beta[16 * I + i] * acck[e] : 0.f;   // N[i][rr]
     nr[e] = i < rr ? brr * acct[e] : 0.f;                    // N[rr][i]
   }
@@ -573,25 +575,27 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
   const int nsteps = (tr.len + kC - 1) / kC;
 
   if (prep_wave) {
-    // ---------------- prep wavefront: block I of every 64 tokens
+    // ---------------- prep wavefront: block I of every 64 tokens (the state history pass
+    // writes no outputs and forms no query operands)
+    constexpr bool NEEDQ = MODE != kModeHist;
     const int I = wave;
     const PrepSrc src = prep_src<PER_CHANNEL, GDR2>(a, row0, tr.len, I, lane);
     BlockRegs r;
     if (nsteps > 0) {
-      load_block<PER_CHANNEL, GDR2>(r, src, 0);
-      prep_block<GDR2>(sm.st[0], sm.kd, r, I, lane);
+      load_block<PER_CHANNEL, GDR2, NEEDQ>(r, src, 0);
+      prep_block<GDR2, NEEDQ>(sm.st[0], sm.kd, r, I, lane);
       wave_lds_fence();
-      block_tiles(sm.st[0], sm.kd, I, rr, p);
-      if (nsteps > 1) load_block<PER_CHANNEL, GDR2>(r, src, kC);
+      block_tiles<NEEDQ>(sm.st[0], sm.kd, I, rr, p);
+      if (nsteps > 1) load_block<PER_CHANNEL, GDR2, NEEDQ>(r, src, kC);
     }
     lds_barrier();
     for (int s = 0; s < nsteps; ++s) {
       if (s + 1 < nsteps) {
         Stage& st = sm.st[(s + 1) & 1];
-        prep_block<GDR2>(st, sm.kd, r, I, lane);
+        prep_block<GDR2, NEEDQ>(st, sm.kd, r, I, lane);
         wave_lds_fence();
-        block_tiles(st, sm.kd, I, rr, p);
-        if (s + 2 < nsteps) load_block<PER_CHANNEL, GDR2>(r, src, (s + 2) * kC);
+        block_tiles<NEEDQ>(st, sm.kd, I, rr, p);
+        if (s + 2 < nsteps) load_block<PER_CHANNEL, GDR2, NEEDQ>(r, src, (s + 2) * kC);
       }
       lds_barrier();
     }

@@ -147,14 +147,15 @@ __device__ __forceinline__ PrepSrc prep_src(const ChunkArgs& a, size_t row0, int
   return s;
 }
 
-// Loads block I of the 64 tokens starting at c0 (rows past the chain read as zero).
-template <bool PER_CHANNEL, bool GDR2>
+// Loads block I of the 64 tokens starting at c0 (rows past the chain read as zero); the
+// queries only when NEEDQ (a pass that writes no outputs does not read them).
+template <bool PER_CHANNEL, bool GDR2, bool NEEDQ = true>
 __device__ __forceinline__ void load_block(BlockRegs& r, const PrepSrc& s, int c0) {
   const uint32_t qk = s.qk_off + (uint32_t)c0 * kDK * 2;
   const uint32_t go = s.g_off + (uint32_t)c0 * (PER_CHANNEL ? kDK * 4 : 4);
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    r.q[u] = ld_b64(s.q, qk + u * kDK * 2);
+    if (NEEDQ) r.q[u] = ld_b64(s.q, qk + u * kDK * 2);
     r.k[u] = ld_b64(s.k, qk + u * kDK * 2);
     if (PER_CHANNEL) {
       r.g[u] = ld_b128(s.g, go + u * kDK * 4);
