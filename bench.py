@@ -487,6 +487,13 @@ def main() -> int:
     log(f"generated {cfg.name} in {time.time() - t0:.1f}s; lengths {np.diff(x.cu_seqlens)}")
     if args.copy_probe:
         copy_probe(torch)
+    # the smaller prefill workloads (parity-test shapes), scheduled as a caller would, and the
+    # B2 H16 T4096 shape in fp32 (the fp32 matrix-core kernel at a size that fills it): made
+    # and uploaded here, timed right after the headline forward
+    small_cfgs = (TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192,
+                  KDA_B2_H16_T4096.replace(name="kda_f32_b2_h16_t4096", dtype="f32"))
+    small_x = [make_chunk_inputs(c) for c in small_cfgs]
+    small_d = [device_inputs(torch, sx) for sx in small_x]
     d = device_inputs(torch, x, cotangents=not args.no_bwd)
     # The backward is timed first, on the same device inputs, and the forward right after it:
     # the host-side input generation leaves the GPU idle for seconds, and a forward timed
@@ -496,6 +503,22 @@ def main() -> int:
         bms, bwsb = bench_bwd(torch, kda, x, d, args.steps, args.warmup)
     ms, ms_median, ws_bytes = bench_chunk(torch, kda, x, args.steps, args.warmup, d)
     del d
+    small = {}
+    for c, sx, sd in zip(small_cfgs, small_x, small_d):
+        sms, smed, _ = bench_chunk(torch, kda, sx, args.steps, args.warmup, sd)
+        sb = chunk_alg_bytes(sx)
+        sflops = chunk_alg_flops_per_head_token(c.dk, c.dv) * c.B * c.H * c.T
+        speak = MFMA_F32_PEAK_TFLOPS if c.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        stf = sflops / (smed / 1e3) / 1e12
+        small[c.name] = {"ms_per_step": sms, "ms_per_step_median": smed, "dtype": c.dtype,
+                         "tokens_per_s": c.B * c.T / (sms / 1e3),
+                         "hbm_gbs": sb / (sms / 1e3) / 1e9,
+                         "mfma": {"achieved": stf, "peak": speak, "unit": "TFLOP/s",
+                                  "frac": stf / speak, "alg_flops_per_launch": sflops,
+                                  "time": "median"}}
+        log(f"{c.name}: {sms:.3f} ms/step (median {smed:.3f}), "
+            f"{c.B * c.T / sms / 1e3:.2f} M tokens/s, {stf:.1f} TFLOP/s of {speak:.0f}")
+    del small_d
     tokens = cfg.T
     value = tokens / (ms / 1e3)
     alg_bytes = chunk_alg_bytes(x)
@@ -567,25 +590,6 @@ def main() -> int:
                 "workload": gd.name, "steps": gd.T, "us_per_step": sec / gd.T * 1e6,
                 "hbm_gbs": dgbs, "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_step": per_step}
             log(f"gdr2 decode: {sec / gd.T * 1e6:.1f} us/step, {dgbs:.0f} GB/s")
-    # the smaller prefill workloads (parity-test shapes), scheduled as a caller would, and
-    # the B2 H16 T4096 shape in fp32 (the fp32 matrix-core kernel at a size that fills it)
-    small = {}
-    for c in (TINY_KDA_F32, KDA_B2_H16_T4096, GDN_B1_H16_T8192,
-              KDA_B2_H16_T4096.replace(name="kda_f32_b2_h16_t4096", dtype="f32")):
-        sx = make_chunk_inputs(c)
-        sms, smed, _ = bench_chunk(torch, kda, sx, args.steps, args.warmup)
-        sb = chunk_alg_bytes(sx)
-        sflops = chunk_alg_flops_per_head_token(c.dk, c.dv) * c.B * c.H * c.T
-        speak = MFMA_F32_PEAK_TFLOPS if c.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
-        stf = sflops / (smed / 1e3) / 1e12
-        small[c.name] = {"ms_per_step": sms, "ms_per_step_median": smed, "dtype": c.dtype,
-                         "tokens_per_s": c.B * c.T / (sms / 1e3),
-                         "hbm_gbs": sb / (sms / 1e3) / 1e9,
-                         "mfma": {"achieved": stf, "peak": speak, "unit": "TFLOP/s",
-                                  "frac": stf / speak, "alg_flops_per_launch": sflops,
-                                  "time": "median"}}
-        log(f"{c.name}: {sms:.3f} ms/step (median {smed:.3f}), "
-            f"{c.B * c.T / sms / 1e3:.2f} M tokens/s, {stf:.1f} TFLOP/s of {speak:.0f}")
     result["small_configs"] = small
     if not args.no_bwd:
         bbytes = bwd_alg_bytes(x)
