@@ -1134,76 +1134,68 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const int32_t* cu, int
   }
 }
 
-// Start states of the later segments of a segment plan and the chain's final state:
-// S_{k+1} = A_k S_k + B_k from S_1 (left by the first segment), on the fp32 matrix cores,
-// dv = dk. One workgroup per (chain, 16 value columns): S's 16 columns in LDS; wavefront w
-// owns row tiles 2 w and 2 w + 1 and prefetches the next step's A rows and B tile.
-__global__ __launch_bounds__(256) void seg_chain_kernel(ChunkArgs a) {
-  __shared__ float S[kDK][17];
+// S_{k+1} = A_k S_k + B_k over the segments of every cut sequence (fp32 matrix cores), from
+// the second segment's start state (which the first segment's item writes): the start state
+// of every later segment and, from the last, the final state. One workgroup of eight
+// wavefronts per (chain, 16 value columns), so that chains with many segments spread each
+// step over many compute units; wavefront w owns rows 16 w .. 16 w + 15. A lane holds the
+// operands of two steps, the current one and the next one in flight (90 registers, two
+// workgroups per compute unit). Most workgroups belong to uncut chains and leave after one
+// load; with few of them resident at once they would pass through the device in rounds.
+__global__ __launch_bounds__(512) void seg_chain_kernel(ChunkArgs a) {
+  __shared__ __align__(16) float St[16][kDK + 4];  // S^T: [column][row]
   const uint32_t* plan = a.plan;
-  if (plan[1] == 0) return;
   const int chain = blockIdx.x, cb = 16 * blockIdx.y;
   const int n = chain / a.H, h = chain % a.H;
-  const uint32_t s0 = plan[kSegHdr + n], ns = plan[kSegHdr + n + 1] - s0;
-  if (ns < 2 || s0 + ns > (uint32_t)a.seg_slots) return;
+  // the plan's flag and the sequence's slots, loaded together
+  const uint32_t on = plan[1], s0 = plan[kSegHdr + n], s1 = plan[kSegHdr + n + 1];
+  const uint32_t ns = s1 - s0;
+  if (on == 0 || s1 < s0 || ns < 2 || s1 > (uint32_t)a.seg_slots) return;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, rr = lane & 15, p = lane >> 4;
   const size_t msz = (size_t)kDK * kDK, per = (size_t)a.seg_slots * a.H * msz;
   const float* first = a.seg_mats + ((size_t)(s0 + 1) * a.H + h) * msz;
-  for (int i = threadIdx.x; i < kDK * 16; i += 256) S[i >> 4][i & 15] = first[(size_t)(i >> 4) * kDK + cb + (i & 15)];
-  // operands of step k: A[16 (2 wv + ti) + rr][4 p + 16 j .. + 3] (16-byte loads) and
-  // B[16 (2 wv + ti) + 4 p + e][cb + rr]; product (j, e) contracts channel 4 p + 16 j + e of
-  // lane group p. Three steps' operands are in flight (a ring of three register buffers),
-  // so that a step waits for loads issued three steps earlier.
-  f32x4 a0[2][8], a1[2][8], a2[2][8];
-  f32x4 b0[2], b1[2], b2[2];
-  auto load = [&](uint32_t k, f32x4 (&x)[2][8], f32x4 (&y)[2]) {
+  for (int i = threadIdx.x; i < kDK * 16; i += 512)
+    St[i & 15][i >> 4] = first[(size_t)(i >> 4) * kDK + cb + (i & 15)];
+  // operands of step k: A[16 wv + rr][4 p + 16 j .. + 3] (16-byte loads) and
+  // B[16 wv + 4 p + e][cb + rr]; product (j, e) contracts channel 4 p + 16 j + e of lane
+  // group p, whose S entries for e = 0 .. 3 are one 16-byte read of the transposed tile
+  f32x4 x0[8], x1[8], y0, y1;
+  auto load = [&](uint32_t k, f32x4 (&x)[8], f32x4& y) {
     const size_t m = ((size_t)(s0 + k) * a.H + h) * msz;
+    const float* Ar = a.seg_mats + per + m + (size_t)(16 * wv + rr) * kDK + 4 * p;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int r0 = 16 * (2 * wv + ti);
-      const float* Ar = a.seg_mats + per + m + (size_t)(r0 + rr) * kDK + 4 * p;
+    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const f32x4*>(Ar + 16 * j);
+    const float* Br = a.seg_mats + 2 * per + m + (size_t)(16 * wv + 4 * p) * kDK + cb + rr;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[ti][j] = *reinterpret_cast<const f32x4*>(Ar + 16 * j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[ti][e] = a.seg_mats[2 * per + m + (size_t)(r0 + 4 * p + e) * kDK + cb + rr];
-    }
+    for (int e = 0; e < 4; ++e) y[e] = Br[(size_t)e * kDK];
   };
-  auto step = [&](uint32_t k, const f32x4 (&x)[2][8], const f32x4 (&y)[2]) {
+  auto step = [&](uint32_t k, const f32x4 (&x)[8], const f32x4& y) {
     __syncthreads();  // S of step k is in LDS
-    f32x4 acc[2] = {y[0], y[1]};
+    f32x4 acc = y;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 sb = *reinterpret_cast<const f32x4*>(&St[rr][4 * p + 16 * j]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float bs = S[4 * p + 16 * j + e][rr];
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) acc[ti] = mfma_f32(x[ti][j][e], bs, acc[ti]);
-      }
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(x[j][e], sb[e], acc);
+    }
     __syncthreads();  // every read of S is done
     float* dst = k + 1 < ns ? a.seg_mats + ((size_t)(s0 + k + 1) * a.H + h) * msz
                             : (a.sT ? a.sT + (size_t)chain * msz : nullptr);
+    *reinterpret_cast<f32x4*>(&St[rr][16 * wv + 4 * p]) = acc;  // rows 16 wv + 4 p + e
+    if (dst) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * (2 * wv + ti) + 4 * p + e;
-        S[row][rr] = acc[ti][e];
-        if (dst) dst[(size_t)row * kDK + cb + rr] = acc[ti][e];
-      }
-  };
-  load(1, a0, b0);
-  if (2 < ns) load(2, a1, b1);
-  if (3 < ns) load(3, a2, b2);
-  for (uint32_t k = 1; k < ns; k += 3) {
-    step(k, a0, b0);
-    if (k + 3 < ns) load(k + 3, a0, b0);
-    if (k + 1 < ns) {
-      step(k + 1, a1, b1);
-      if (k + 4 < ns) load(k + 4, a1, b1);
+      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * wv + 4 * p + e) * kDK + cb + rr] = acc[e];
     }
-    if (k + 2 < ns) {
-      step(k + 2, a2, b2);
-      if (k + 5 < ns) load(k + 5, a2, b2);
+  };
+  // two register sets: step k + 1's operands are in flight during step k
+  load(1, x0, y0);
+  if (2 < ns) load(2, x1, y1);
+  for (uint32_t k = 1; k < ns; k += 2) {
+    step(k, x0, y0);
+    if (k + 2 < ns) load(k + 2, x0, y0);
+    if (k + 1 < ns) {
+      step(k + 1, x1, y1);
+      if (k + 3 < ns) load(k + 3, x1, y1);
     }
   }
 }
@@ -1506,7 +1498,7 @@ hipError_t launch_chunk_mfma_segplan(const ChunkArgs& args, bool per_channel, vo
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  seg_chain_kernel<<<dim3((unsigned)(a.N * a.H), kDK / 16), 256, 0, stream>>>(a);
+  seg_chain_kernel<<<dim3((unsigned)(a.N * a.H), kDK / 16), 512, 0, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   seg_correct_kernel<<<dim3(1024), 256, 0, stream>>>(a);
