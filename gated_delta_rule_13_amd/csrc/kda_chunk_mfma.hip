@@ -1228,6 +1228,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
   const int rr = lane & 15, p = lane >> 4;
   const size_t msz = (size_t)kDK * kDK;
   float (*cw)[kCorrLd] = ct_[wv];
+  const uint32_t qt_per_head = plan[4];  // rows of carried-back queries per head
   for (uint32_t w = blockIdx.x; w < units * (uint32_t)a.H; w += gridDim.x) {
     const int h = (int)(w % (uint32_t)a.H);
     const uint32_t u = w / (uint32_t)a.H;
@@ -1236,34 +1237,43 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
       const uint32_t mid = (lo + hi + 1) >> 1;
       if (corr_off[mid] <= u) lo = mid; else hi = mid - 1;
     }
-    const uint32_t sl = lo;
+    // the searches read LDS, so their results sit in vector registers; they are the same in
+    // every lane, and as scalars the unit's buffer descriptors need no loop over lanes
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lo);
     int nlo = 0, nhi = a.N - 1;  // the sequence of slot sl
     while (nlo < nhi) {
       const int mid = (nlo + nhi + 1) >> 1;
       if (segbase[mid] <= sl) nlo = mid; else nhi = mid - 1;
     }
-    const int n = nlo;
-    const int k = (int)(sl - segbase[n]);
+    const int n = __builtin_amdgcn_readfirstlane(nlo);
+    const int k = (int)(sl - __builtin_amdgcn_readfirstlane(segbase[n]));
     const TokenRange tr = token_range(a.cu, n, a.T);
-    const int g0 = k * xt + (int)(u - corr_off[sl]) * kSegGroup;  // first token of the unit
+    const int g0 = k * xt + (int)(u - __builtin_amdgcn_readfirstlane(corr_off[sl])) *
+                                kSegGroup;  // first token of the unit
     const int seg_end = (int)min((long long)(k + 1) * xt, (long long)tr.len);
     if (k < 1 || g0 >= seg_end) continue;  // uniform over the workgroup
     const int len = min(kSegGroup, seg_end - g0);
     const size_t row0 = ((size_t)tr.b * a.H + h) * a.T + tr.t0 + g0;
     // the unit's carried-back queries: rows of head h from the slot's first row
-    const size_t qrow0 = (size_t)h * plan[4] + plan[segplan_qoff_off(a.N, a.seg_slots) + sl] +
-                         (size_t)(g0 - k * xt);
+    const size_t qrow0 =
+        (size_t)h * qt_per_head +
+        __builtin_amdgcn_readfirstlane(plan[segplan_qoff_off(a.N, a.seg_slots) + sl]) +
+        (size_t)(g0 - k * xt);
     const rsrc_t qs = make_rsrc(static_cast<const bf16*>(a.qt) + qrow0 * kDK, (uint32_t)len * kDK * 2);
     const rsrc_t os = make_rsrc(static_cast<bf16*>(a.o) + row0 * kDK, (uint32_t)len * kDK * 2);
     const float* S = a.seg_mats + ((size_t)sl * a.H + h) * msz;
-    __syncthreads();  // the previous unit's reads of sa are done
-    for (int i = threadIdx.x; i < 8 * 4 * 64; i += 256) {
-      const int ct = i >> 8, ks = (i >> 6) & 3, l = i & 63, r = l & 15, q = l >> 4;
-      float x[8];
+    // S^T staged as bf16: wavefront wv stages slab wv of every column tile; all 64 loads are
+    // issued before the first wait
+    float x[8][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = S[(size_t)(32 * ks + 8 * q + j) * kDK + 16 * ct + r];
-      sa[ct][ks][l] = cat8(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
-    }
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[ct][j] = S[(size_t)(32 * wv + 8 * p + j) * kDK + 16 * ct + rr];
+    __syncthreads();  // the previous unit's reads of sa are done
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      sa[ct][wv][lane] = cat8(pack4(x[ct][0], x[ct][1], x[ct][2], x[ct][3]),
+                              pack4(x[ct][4], x[ct][5], x[ct][6], x[ct][7]));
     __syncthreads();
     // block b0: queries of token b0 + rr (B operands), O rows as 16-byte pieces
     // (piece lane + 64 i: token b0 + piece / 16, columns 8 (piece % 16) ..)
