@@ -1134,12 +1134,14 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const int32_t* cu, int
   }
 }
 
-// S_{k+1} = A_k S_k + B_k over the segments of every cut sequence (fp32 matrix cores), from
-// the second segment's start state (which the first segment's item writes): the start state
-// of every later segment and, from the last, the final state. One workgroup of eight
+// S_{k+1} = A_k S_k + B_k over the segments of every sequence cut into three or more (fp32
+// matrix cores), from the second segment's start state (which the first segment's item
+// writes): the start state of every later segment. The last step, to the final state, is
+// taken by seg_correct_kernel beside the output corrections, so that sequences cut in two
+// (the common case) need no step here. One workgroup of eight
 // wavefronts per (chain, 16 value columns), so that chains with many segments spread each
 // step over many compute units; wavefront w owns rows 16 w .. 16 w + 15. A lane holds the
-// operands of two steps, the current one and the next one in flight (90 registers, two
+// operands of two steps, the current one and the next one in flight (92 registers, two
 // workgroups per compute unit). Most workgroups belong to uncut chains and leave after one
 // load; with few of them resident at once they would pass through the device in rounds.
 __global__ __launch_bounds__(512) void seg_chain_kernel(ChunkArgs a) {
@@ -1150,7 +1152,8 @@ __global__ __launch_bounds__(512) void seg_chain_kernel(ChunkArgs a) {
   // the plan's flag and the sequence's slots, loaded together
   const uint32_t on = plan[1], s0 = plan[kSegHdr + n], s1 = plan[kSegHdr + n + 1];
   const uint32_t ns = s1 - s0;
-  if (on == 0 || s1 < s0 || ns < 2 || s1 > (uint32_t)a.seg_slots) return;
+  if (on == 0 || s1 < s0 || ns < 3 || s1 > (uint32_t)a.seg_slots) return;
+  const uint32_t kend = ns - 1;  // steps 1 .. kend - 1 write the start states 2 .. kend
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, rr = lane & 15, p = lane >> 4;
   const size_t msz = (size_t)kDK * kDK, per = (size_t)a.seg_slots * a.H * msz;
   const float* first = a.seg_mats + ((size_t)(s0 + 1) * a.H + h) * msz;
@@ -1179,23 +1182,20 @@ __global__ __launch_bounds__(512) void seg_chain_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) acc = mfma_f32(x[j][e], sb[e], acc);
     }
     __syncthreads();  // every read of S is done
-    float* dst = k + 1 < ns ? a.seg_mats + ((size_t)(s0 + k + 1) * a.H + h) * msz
-                            : (a.sT ? a.sT + (size_t)chain * msz : nullptr);
+    float* dst = a.seg_mats + ((size_t)(s0 + k + 1) * a.H + h) * msz;
     *reinterpret_cast<f32x4*>(&St[rr][16 * wv + 4 * p]) = acc;  // rows 16 wv + 4 p + e
-    if (dst) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * wv + 4 * p + e) * kDK + cb + rr] = acc[e];
-    }
+    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * wv + 4 * p + e) * kDK + cb + rr] = acc[e];
   };
   // two register sets: step k + 1's operands are in flight during step k
   load(1, x0, y0);
-  if (2 < ns) load(2, x1, y1);
-  for (uint32_t k = 1; k < ns; k += 2) {
+  if (2 < kend) load(2, x1, y1);
+  for (uint32_t k = 1; k < kend; k += 2) {
     step(k, x0, y0);
-    if (k + 2 < ns) load(k + 2, x0, y0);
-    if (k + 1 < ns) {
+    if (k + 2 < kend) load(k + 2, x0, y0);
+    if (k + 1 < kend) {
       step(k + 1, x1, y1);
-      if (k + 3 < ns) load(k + 3, x1, y1);
+      if (k + 3 < kend) load(k + 3, x1, y1);
     }
   }
 }
@@ -1206,15 +1206,19 @@ __global__ __launch_bounds__(512) void seg_chain_kernel(ChunkArgs a) {
 // with the queries as the B operand, so that each product is a tile of O^T. The fp32 sums
 // go through a wavefront-private LDS tile, and O is read and written as whole 256-byte
 // rows (16 bytes per lane). The next block's loads are issued before the current block's
-// products.
+// products. The same launch takes the last step of every cut sequence's segment chain,
+// S_T = A S + B from the last segment's start state, one unit per (sequence, 16 value
+// columns, head), after the corrections: small matrix-core products in the tail of their
+// memory-bound passes, instead of a launch of their own.
 constexpr int kCorrLd = kDK + 4;  // padded row (floats) of the correction tile
 __device__ __forceinline__ bf16x8 to_bf16x8_(const float (&x)[8]) {
   return cat8(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
 }
 __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
   __shared__ bf16x8 sa[8][4][64];            // [column tile][32-channel slab][lane]
-  __shared__ float ct_[4][16][kCorrLd];      // per wavefront: 16 tokens x 128 columns
+  __shared__ __align__(16) float ct_[4][16][kCorrLd];  // per wavefront: 16 tokens x 128 columns
   __shared__ uint32_t segbase[kMaxPlanSeqs + 1], corr_off[kMaxPlanSeqs + 1];
+  __shared__ uint32_t cut[kMaxPlanSeqs], scan_x[257];  // the sequences cut in two or more
   const uint32_t* plan = a.plan;
   const uint32_t units = plan[3], slots = plan[2];
   if (plan[1] == 0 || units == 0 || slots == 0 || slots > (uint32_t)a.seg_slots ||
@@ -1223,15 +1227,85 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(ChunkArgs a) {
   for (int i = threadIdx.x; i <= a.N; i += 256) segbase[i] = plan[kSegHdr + i];
   for (uint32_t i = threadIdx.x; i <= slots; i += 256) corr_off[i] = plan[segplan_corr_off(a.N) + i];
   __syncthreads();
+  // the cut sequences in order (thread t looks at sequences 4 t .. 4 t + 3)
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = 4 * (int)threadIdx.x + i;
+    if (n < a.N && segbase[n + 1] >= segbase[n] + 2) ++mine;
+  }
+  uint32_t at = block_exclusive_scan<256>(mine, scan_x);
+  const uint32_t ncut = scan_x[256];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = 4 * (int)threadIdx.x + i;
+    if (n < a.N && segbase[n + 1] >= segbase[n] + 2) cut[at++] = (uint32_t)n;
+  }
+  __syncthreads();
   const int xt = (int)plan[1] * kC;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rr = lane & 15, p = lane >> 4;
   const size_t msz = (size_t)kDK * kDK;
   float (*cw)[kCorrLd] = ct_[wv];
   const uint32_t qt_per_head = plan[4];  // rows of carried-back queries per head
-  for (uint32_t w = blockIdx.x; w < units * (uint32_t)a.H; w += gridDim.x) {
-    const int h = (int)(w % (uint32_t)a.H);
-    const uint32_t u = w / (uint32_t)a.H;
+  // units: the corrections, then the final states (when requested)
+  const uint32_t nfin = a.sT ? ncut * 8u * (uint32_t)a.H : 0u;
+  const uint32_t ncorr = units * (uint32_t)a.H;
+  for (uint32_t w0 = blockIdx.x; w0 < nfin + ncorr; w0 += gridDim.x) {
+    if (w0 >= ncorr) {
+      const uint32_t w = w0 - ncorr;
+      // S_T = A S + B for 16 value columns of one chain, from the start state of its
+      // sequence's last segment; wavefront wv owns row tiles 2 wv and 2 wv + 1, A rows in
+      // registers (16-byte loads), S^T of the columns through LDS (ct_[0], free between units)
+      const int h = (int)(w % (uint32_t)a.H);
+      const int cb = 16 * (int)((w / (uint32_t)a.H) % 8u);
+      const uint32_t n = cut[w / (8u * (uint32_t)a.H)];
+      const uint32_t sl = segbase[n + 1] - 1;  // the last segment's slot
+      const size_t pm = (size_t)a.seg_slots * a.H * msz;
+      const float* Sk = a.seg_mats + ((size_t)sl * a.H + h) * msz;
+      f32x4 xa[2][8], acc[2];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int r0 = 16 * (2 * wv + ti);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          xa[ti][j] = *reinterpret_cast<const f32x4*>(Sk + pm + (size_t)(r0 + rr) * kDK + 4 * p +
+                                                      16 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ti][e] = Sk[2 * pm + (size_t)(r0 + 4 * p + e) * kDK + cb + rr];
+      }
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = (int)threadIdx.x + 256 * i;
+        sv[i] = Sk[(size_t)(idx >> 4) * kDK + cb + (idx & 15)];
+      }
+      float (*St)[kCorrLd] = ct_[0];  // St[c][r] = S[r][cb + c]
+      __syncthreads();  // earlier readers of ct_ are done
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = (int)threadIdx.x + 256 * i;
+        St[idx & 15][idx >> 4] = sv[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 sb = *reinterpret_cast<const f32x4*>(&St[rr][4 * p + 16 * j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int ti = 0; ti < 2; ++ti) acc[ti] = mfma_f32(xa[ti][j][e], sb[e], acc[ti]);
+      }
+      float* dst = a.sT + ((size_t)n * a.H + h) * msz;
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(size_t)(16 * (2 * wv + ti) + 4 * p + e) * kDK + cb + rr] = acc[ti][e];
+      continue;
+    }
+    const int h = (int)(w0 % (uint32_t)a.H);
+    const uint32_t u = w0 / (uint32_t)a.H;
     uint32_t lo = 0, hi = slots - 1;  // the last slot whose first unit is <= u
     while (lo < hi) {
       const uint32_t mid = (lo + hi + 1) >> 1;
