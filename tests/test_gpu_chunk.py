@@ -366,6 +366,32 @@ def test_segmented_without_initial_or_final_state():
                  TOL["bf16"], "segmented, no states: outputs")
 
 
+def test_segmented_one_long_among_many():
+    """300 packed sequences, 299 of 64 tokens and at index 287 one of 20,000 tokens, which the
+    planner cuts into many segments: the 1024-thread planner, a segment chain of many steps,
+    and the final-state step of the corrections launch, which finds the one cut sequence
+    among hundreds. Every chain matches the oracle and the whole-chain run."""
+    lens = [64] * 300
+    lens[287] = 20000
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    ws = kda.kda_chunk_fwd_workspace_size(1, 2, T, 128, 128, len(lens), kda.KDA_BF16)
+    assert ws > kda.kda_chunk_fwd_workspace_size(1, 2, T, 128, 64, len(lens), kda.KDA_BF16), \
+        "expected the segment plan"
+    cfg = KDA_VARLEN_H32_T65536.replace(H=2, T=T, num_seqs=0, pin_frac=0.05, seed=41)
+    x = make_chunk_inputs(cfg)
+    x.cu_seqlens = cu
+    x.s0 = np.random.default_rng(42).standard_normal((len(lens), 2, 128, 128)).astype(
+        np.float32) * np.float32(0.02)
+    note("segmented chunk: one long sequence among 300")
+    o1, s1 = run_chunk(x, "bf16", o_fill=float("nan"))
+    assert np.all(np.isfinite(o1)), "some output position was not written"
+    o0, s0 = run_chunk(x, "bf16", schedule=False)
+    check_chains(x, o1, s1, oracle_chains(x), TOL["bf16"], "one long among 300")
+    assert_close(o1, o0, TOL["bf16"], "one long among 300: segmented vs whole outputs")
+    assert_close(s1, s0, TOL["bf16"], "one long among 300: segmented vs whole states")
+
+
 RANDOM_SHAPES = list(range(40))
 
 
