@@ -56,19 +56,19 @@ CHUNK = 64
 # runs. It is reported only while the kernel source is the one the counters were taken on
 # (its SHA-256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {      # profiles/kda_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 3804461204,
-    "kernel_sha256": "f0fc216c0749c3da02830168fa94dee9d75310078138073f5e58562291dde992",
+    "bytes": 3792918794,
+    "kernel_sha256": "c3ba2b158da694e96aabb8bb8d51a22ac73eeb9da47893f28d0fc58c7c2bd8cd",
 }
 MEASURED_TRAFFIC_GDR2 = {  # profiles/kda_gdr2_chunk_fwd_varlen_h32_t65536.md
-    "bytes": 5930530680,
-    "kernel_sha256": "f0fc216c0749c3da02830168fa94dee9d75310078138073f5e58562291dde992",
+    "bytes": 5926890387,
+    "kernel_sha256": "c3ba2b158da694e96aabb8bb8d51a22ac73eeb9da47893f28d0fc58c7c2bd8cd",
 }
 # one kda_chunk_bwd call (state history, reverse carry, gradients): its own source and that of
 # the forward kernel whose history mode it runs
 MEASURED_TRAFFIC_BWD = {  # profiles/kda_chunk_bwd_varlen_h32_t65536.md
-    "bytes": 19504202137,
+    "bytes": 19504313182,
     "kernel_sha256": "2286d7707f2052a2ae67b1e87ac3eda8181d747c71ccfc3ae43561b2ffc0ceee",
-    "hist_sha256": "f0fc216c0749c3da02830168fa94dee9d75310078138073f5e58562291dde992",
+    "hist_sha256": "c3ba2b158da694e96aabb8bb8d51a22ac73eeb9da47893f28d0fc58c7c2bd8cd",
 }
 MEASURED_TRAFFIC_PROLOGUE = {  # profiles/kda_prologue_h32_t65536.md
     "bytes": 4320464550,

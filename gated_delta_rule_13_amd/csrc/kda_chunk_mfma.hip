@@ -82,8 +82,16 @@ __host__ __device__ inline size_t segplan_items_off(int N, int cap) {
   return segplan_qoff_off(N, cap) + (size_t)cap + 1;
 }
 
+// Issue priority (s_setprio) of the state wavefronts relative to the prep wavefronts
+// (priority 0) on the same SIMD, by gate kind, as measured on the packed T = 65536 workloads:
+// with one decay per key channel and the beta gate (KDA) equal priority was up to 3% faster
+// than priority 1, 2 or 3 and never slower; with the Gated Delta Rule-2 gates or one decay
+// per head, priority 3 was 3-7% faster than equal priority.
 #ifndef KDA_STATE_PRIO
 #define KDA_STATE_PRIO 3
+#endif
+#ifndef KDA_STATE_PRIO_KDA
+#define KDA_STATE_PRIO_KDA 0
 #endif
 
 
@@ -601,9 +609,11 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NS)) void chunk_mfma_kernel(Chun
     }
   } else {
     // ---------------- state wavefront
-    // The state steps are the sequential critical path; the prep wavefronts sharing a
-    // SIMD have slack, so the state wavefronts take issue priority.
-    __builtin_amdgcn_s_setprio(KDA_STATE_PRIO);
+    // The state steps are the sequential critical path; with the Gated Delta Rule-2 gates
+    // or one decay per head they take issue priority over the prep wavefronts sharing a
+    // SIMD (the KDA gates measured fastest at equal priority, see KDA_STATE_PRIO_KDA).
+    constexpr short kStatePrio = PER_CHANNEL && !GDR2 ? KDA_STATE_PRIO_KDA : KDA_STATE_PRIO;
+    __builtin_amdgcn_s_setprio(kStatePrio);
     const int j = wave - kPrepWaves;
     if constexpr (MODE == kModePair) {  // whole items only
       if (kind == kModeTrans)
